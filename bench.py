@@ -1,0 +1,179 @@
+#!/usr/bin/env python
+"""Throughput of the Video Swin window-attention block on one MI355X.
+
+A step is one regular + shifted block pair (eq. 1) of the Swin-T stage-1
+workload: bf16 tokens (B=1, T'=16, H'=56, W'=56, C=96) from a 32x224x224
+clip with 2x4x4 patches, 3 heads of 32, window (8,7,7), shift (4,3,3), MLP
+ratio 4, seeded synthetic inputs and weights (no dataset).  Inputs, weights,
+outputs and workspace are resident in HBM before the timed region.
+
+Prints one JSON line: tokens/s through a block (tokens x blocks per second),
+TFLOP/s and the fraction of the bf16 MFMA peak, the roofline of the dominant
+kernel (the fused window attention, timed alone with HIP events on the
+stream it is launched on) and the fp64 CPU oracle's rate on the same
+workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "window-attention block tokens/s + TFLOP/s (% of MFMA peak) at Swin-T stage 1"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def block_flops(plan: dict, C: int, hid: int) -> dict:
+    """Closed-form FLOPs (2 per multiply-accumulate) of one block on dense
+    padded windows: qkv and proj on padded tokens, QK^T and AV per window,
+    MLP on real tokens."""
+    Lp = plan["num_windows"] * plan["tokens_per_window"]
+    L = plan["tokens"]
+    N = plan["tokens_per_window"]
+    f = {"qkv": 2 * Lp * C * 3 * C, "attn": 2 * 2 * Lp * N * C, "proj": 2 * Lp * C * C,
+         "fc1": 2 * L * C * hid, "fc2": 2 * L * hid * C}
+    f["total"] = sum(f.values())
+    return f
+
+
+def cpu_baseline(x, params, shape, min_seconds=10.0, max_reps=5):
+    """The fp64 oracle, untouched, on the same workload: full block pairs
+    repeated until about `min_seconds` of CPU work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    x64 = x.astype(np.float64)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        _, y = oracle.block(x64, params[0], shape.heads, shape.window, (0, 0, 0))
+        oracle.block(y, params[1], shape.heads, shape.window, shape.shift)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    return {"value": 2 * shape.tokens * reps / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} full block pair(s) of the same workload in fp64 numpy "
+                      f"({el:.1f} s, BLAS threads={cores})"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--kernel-launches", type=int, default=50,
+                    help="attention-kernel launches timed for the roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with the attention kernel's counter-derived HBM bytes per launch")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the block shards by clip with no exchange, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import shifted_window_attention_amd as vs
+
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[2]
+    s = wl.shape
+    x_np, params = synth.gen_workload(2)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).cuda()
+    x = dev(x_np)
+    w = [{k: dev(v) for k, v in p.items()} for p in params]
+    hid = s.mlp_ratio * s.C
+    shifts = [(0, 0, 0), s.shift]
+    descs = [vs.make_desc(s.B, s.T, s.H, s.W, s.C, s.heads, s.window, sh, mlp_hidden=hid,
+                          dtype=torch.bfloat16) for sh in shifts]
+    plans = [vs.vswin_plan_query(d) for d in descs]
+    ws = torch.empty(max(p["workspace_bytes"] for p in plans), dtype=torch.uint8, device="cuda")
+    y1 = torch.empty_like(x)
+    y2 = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        vs.vswin_block_fwd(x, w[0], s.heads, s.window, shifts[0], out=y1, workspace=ws, stream=stream)
+        vs.vswin_block_fwd(y1, w[1], s.heads, s.window, shifts[1], out=y2, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = [block_flops(p, s.C, hid) for p in plans]
+    step_flops = sum(f["total"] for f in flops)
+    tokens_per_step = s.tokens * len(shifts)
+    tflops = step_flops / (ms * 1e-3) / 1e12
+
+    # ---- dominant kernel: the fused window attention, alone, on the same stream
+    Lp = plans[0]["num_windows"] * plans[0]["tokens_per_window"]
+    d = s.C // s.heads
+    g = torch.Generator(device="cuda").manual_seed(2)
+    qkv = [torch.randn((plans[0]["num_windows"], s.heads, plans[0]["tokens_per_window"], d),
+                       generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
+    o = torch.empty((plans[0]["num_windows"], plans[0]["tokens_per_window"], s.C), dtype=torch.bfloat16,
+                    device="cuda")
+    kern_us = []
+    for i, dsc in enumerate(descs):
+        for _ in range(5):
+            vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, stream=stream)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(args.kernel_launches):
+            vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, stream=stream)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        kern_us.append(a0.elapsed_time(a1) * 1e3 / args.kernel_launches)
+    attn_flops = flops[0]["attn"]
+    attn_us = sum(kern_us) / len(kern_us)
+    achieved = attn_flops / (attn_us * 1e-6) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "attn_mfma_kernel", "avg_us": round(attn_us, 3),
+                "avg_us_regular": round(kern_us[0], 3), "avg_us_shifted": round(kern_us[1], 3),
+                "flops_per_launch": attn_flops}
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_step / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Swin-T stage-1 regular+shifted block pair: bf16 tokens (1,16,56,56,96), "
+                               "3 heads x 32, window (8,7,7), shift (4,3,3), MLP ratio 4, seeded synthetic",
+                   "global_batch": s.B, "tokens_per_block": s.tokens, "blocks_per_step": len(shifts),
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "step_gflop": round(step_flops / 1e9, 3), "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x_np, params, s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * vswin.h -- C ABI of the MI355X (gfx950) Video Swin 3D (shifted-)window
+ * attention block library (libvswin.so).
+ *
+ * Every entry point takes plain pointers and sizes.  Device pointers point to
+ * HIP device memory owned by the caller; the library never allocates, frees
+ * or keeps a reference to caller memory.  Work is enqueued asynchronously on
+ * the given HIP stream (`stream` is a hipStream_t; NULL = the null stream).
+ *
+ * Errors: argument errors are detected on the host before anything is
+ * enqueued and leave every output untouched.  A call on an empty input
+ * (B = 0, or zero rows) is a no-op that succeeds without looking at its
+ * pointers.  Launch failures come back as
+ * VSWIN_ERR_HIP.  No C++ exception crosses this boundary.  vswin_last_error()
+ * returns a thread-local description of the last failing call on the calling
+ * thread.  Calls keep no state between invocations and may be made from
+ * several threads at once (with distinct output and workspace buffers).
+ *
+ * Method (Video Swin Transformer pages):
+ *   block      = pre-norm block of eq. 1 (§3.1): z^ = x + MSA(LN1(x)),
+ *                y = z^ + MLP(LN2(z^));
+ *   MSA        = 3D window multi-head self-attention of §3.2 / eq. 2:
+ *                pad -> roll(-shift) -> partition into P x Mh x Mw windows
+ *                -> qkv Linear -> softmax(q k^T / sqrt(d) + B + mask) v
+ *                -> proj Linear -> reverse partition -> roll(+shift) -> crop;
+ *   B          = relative position bias read from a (2P-1)(2Mh-1)(2Mw-1) x
+ *                heads table (§3.2, eq. 2);
+ *   mask       = pairs of tokens that were not neighbours before the roll
+ *                (§3.2, fig. 3) are excluded.
+ * Conventions for points the pages leave open are stated at each entry point.
+ */
+#ifndef VSWIN_H_
+#define VSWIN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VSWIN_ABI_VERSION 1
+
+typedef enum {
+  VSWIN_OK = 0,
+  VSWIN_ERR_INVALID_ARG = -1,   /* bad descriptor, null or misaligned pointer    */
+  VSWIN_ERR_UNSUPPORTED = -2,   /* valid but not implemented (e.g. head_dim > 64) */
+  VSWIN_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required    */
+  VSWIN_ERR_HIP = -4            /* a HIP call or kernel launch failed            */
+} vswin_status;
+
+typedef enum { VSWIN_FP32 = 0, VSWIN_BF16 = 1 } vswin_dtype;
+
+/* Descriptor flags: readings of points the pages leave open.              */
+enum {
+  /* Pad tokens keep the region label of their grid position instead of
+   * forming a region of their own (the published code's behaviour: pads are
+   * visible in regular blocks).  Default off: pads are masked.            */
+  VSWIN_F_PAD_VISIBLE = 1u,
+  /* Clamp an axis's window to its size only when size < window (the pages'
+   * literal "smaller").  Default: clamp when size <= window, shift 0.       */
+  VSWIN_F_CLAMP_STRICT = 2u,
+  /* Add -100 to masked scores (the published code's value) instead of
+   * excluding the pair.  Default off: masked pairs get weight exactly 0.   */
+  VSWIN_F_MASK_M100 = 4u
+};
+
+/* One block's geometry.  Tokens are (B, T, H, W, C), contiguous, channels
+ * last.  window/shift are the requested values (P, Mh, Mw) and (sP, sMh, sMw)
+ * with 0 <= shift < window; the library applies the clamp itself and reports
+ * the effective values through vswin_plan_query.  The relative-position
+ * table is sized by the requested window.                                  */
+typedef struct {
+  int32_t B, T, H, W, C;
+  int32_t heads;          /* C % heads == 0; head_dim = C / heads            */
+  int32_t window[3];      /* requested window (P, Mh, Mw), all >= 1          */
+  int32_t shift[3];       /* requested shift, 0 <= shift[i] < window[i]      */
+  int32_t mlp_hidden;     /* MLP hidden width (4 * C for the pages' ratio)   */
+  vswin_dtype dtype;      /* storage type of tokens, weights and outputs     */
+  float ln_eps;           /* LayerNorm epsilon (1e-5)                        */
+  uint32_t flags;         /* VSWIN_F_* bits                                  */
+} vswin_desc;
+
+/* Block weights: device pointers, element type = desc.dtype, PyTorch layouts
+ * (Linear weight = (out, in), row-major).  All must be 16-byte aligned.
+ * qkv output rows are [q | k | v], channel = head * head_dim + e.
+ * rpb_table is (rows, heads) row-major, rows = (2P-1)(2Mh-1)(2Mw-1); the row
+ * of a (query, key) pair with in-window offset (dt, dh, dw) = query - key is
+ * (dt+P-1)(2Mh-1)(2Mw-1) + (dh+Mh-1)(2Mw-1) + (dw+Mw-1) (temporal outermost,
+ * so that the §3.4 inflation tiling makes the bias frame independent).      */
+typedef struct {
+  const void *ln1_g, *ln1_b;     /* (C), (C)                                  */
+  const void *qkv_w, *qkv_b;     /* (3C, C), (3C); qkv_b may be NULL          */
+  const void *proj_w, *proj_b;   /* (C, C), (C); proj_b may be NULL           */
+  const void *rpb_table;         /* (rows, heads)                             */
+  const void *ln2_g, *ln2_b;     /* (C), (C)                                  */
+  const void *fc1_w, *fc1_b;     /* (hidden, C), (hidden); fc1_b may be NULL  */
+  const void *fc2_w, *fc2_b;     /* (C, hidden), (C); fc2_b may be NULL       */
+} vswin_block_weights;
+
+/* Result of planning one block.                                            */
+typedef struct {
+  int32_t eff_window[3];   /* window after the clamp                          */
+  int32_t eff_shift[3];    /* shift after the clamp                           */
+  int32_t padded[3];       /* (Tp, Hp, Wp): sizes rounded up to the window    */
+  int32_t tokens_per_window; /* N = P * Mh * Mw                               */
+  int64_t num_windows;     /* B * prod(padded / window)                      */
+  int64_t tokens;          /* B * T * H * W                                  */
+  int32_t masked;          /* 1 if any window needs the region mask          */
+  int32_t fast_attention;  /* 1 if the MFMA attention kernel serves it       */
+  size_t workspace_bytes;  /* device workspace needed by vswin_block_fwd     */
+  size_t msa_workspace_bytes; /* ... and by vswin_window_msa_fwd             */
+} vswin_plan;
+
+/* Validate `desc` and report the clamped geometry and workspace sizes.
+ * Host only: makes no HIP call.  Returns VSWIN_ERR_INVALID_ARG for a bad
+ * descriptor (plan untouched), VSWIN_ERR_UNSUPPORTED when the geometry is
+ * valid but vswin_block_fwd / vswin_window_msa_fwd cannot serve it (plan is
+ * still filled in: the permutation entry points accept such descriptors).  Window/shift clamp (pages: Pitfalls and the
+ * paper-vs-code notes): an axis whose size is <= its window (< with
+ * VSWIN_F_CLAMP_STRICT) takes window = size and shift = 0.                  */
+vswin_status vswin_plan_query(const vswin_desc* desc, vswin_plan* plan);
+
+/* One Video Swin block (eq. 1):  y = z^ + MLP(LN2(z^)),
+ * z^ = x + MSA(LN1(x)).  x, y: (B,T,H,W,C) of desc.dtype, must not alias.
+ * MSA as in vswin_window_msa_fwd; MLP = Linear(C, hidden) -> exact erf GELU
+ * -> Linear(hidden, C); LayerNorm with biased variance and desc.ln_eps.
+ * In the bf16 path z^ is kept in fp32 inside the workspace; softmax runs in
+ * fp32 and the attention weights are rounded to bf16 for the AV product.
+ * A regular/shifted pair (eq. 1) is two calls: shift 0, then window // 2.
+ * workspace: >= plan.workspace_bytes bytes of device memory, 256-byte
+ * aligned, used as scratch for the duration of the call on `stream`.        */
+vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x,
+                             const vswin_block_weights* w, void* y,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* The window attention branch alone (the pages' window_msa, §3.2 / eq. 2):
+ * x_norm (B,T,H,W,C) is the LayerNorm output; y (same shape) receives the
+ * projected attention output with no residual.  Zero padding is appended at
+ * the end of each axis, then the padded grid is rolled by -shift; masked
+ * pairs are those whose tokens carry different region labels, where along
+ * every shifted axis of padded length n the rolled positions [0, n-w),
+ * [n-w, n-s) and [n-s, n) form separate regions and pad tokens form their
+ * own region (see VSWIN_F_PAD_VISIBLE).  The ln1_*, ln2_* and fc* fields of
+ * `w` are ignored.  workspace >= plan.msa_workspace_bytes.                          */
+vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm,
+                                  const vswin_block_weights* w, void* y,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* The attention core alone (eq. 2) on projected windows: per window w and
+ * head h, q/k/v[((w * heads + h) * N + n) * head_dim + e] (bf16 or fp32 of
+ * desc.dtype; N = tokens per window, windows and slots ordered as for
+ * vswin_index_map), o[(w * N + n) * C + h * head_dim + e] receives
+ * softmax(q k^T / sqrt(head_dim) + B + mask) v.  rpb_table as in
+ * vswin_block_weights.  No workspace.                                         */
+vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const void* k,
+                                 const void* v, const void* rpb_table, void* o, void* stream);
+
+/* Index map of the pad + roll + partition permutation (§3.2):
+ * map[w * N + n] = flat source token index b*T*H*W + (t*H + h)*W + w of
+ * window slot n of window w (windows ordered (b, wt, wh, ww), slots
+ * (pt, ph, pw), row-major), or -1 for a pad slot.  region (nullable) gets the
+ * slot's region label 9*lt + 3*lh + lw, or 255 for a pad that forms its own
+ * region.  map, region: device buffers of num_windows * N entries.           */
+vswin_status vswin_index_map(const vswin_desc* desc, int32_t* map, uint8_t* region,
+                             void* stream);
+
+/* Pad + roll(-shift) + partition of x (B,T,H,W,C) into windows
+ * (num_windows, N, C), pad slots zero.  Bit-exact permutation.              */
+vswin_status vswin_partition_fwd(const vswin_desc* desc, const void* x, void* windows,
+                                 void* stream);
+
+/* Inverse: reverse partition + roll(+shift) + crop of windows
+ * (num_windows, N, C) into y (B,T,H,W,C); with residual != NULL,
+ * y = residual + unpartitioned windows.  Pad slots are dropped.             */
+vswin_status vswin_reverse_fwd(const vswin_desc* desc, const void* windows,
+                               const void* residual, void* y, void* stream);
+
+/* LayerNorm over the last axis of `rows` rows of width C (biased variance):
+ * y = (x - mean) / sqrt(var + eps) * g + b.  x of in_dtype, y of out_dtype,
+ * g and b of out_dtype.                                                      */
+vswin_status vswin_layernorm_fwd(int64_t rows, int32_t C, vswin_dtype in_dtype,
+                                 vswin_dtype out_dtype, const void* x, const void* g,
+                                 const void* b, float eps, void* y, void* stream);
+
+/* 3D patch embedding (§3.1 step 1; the Conv3d of the mmaction2 code with
+ * kernel = stride = patch):  video (B, Cin, T, H, W) -> tokens
+ * (B, ceil(T/pt), ceil(H/ph), ceil(W/pw), C); each patch's values in
+ * (c, kt, kh, kw) order (zero beyond the video's end) times w^T + b.
+ * w is (C, Cin, pt, ph, pw), b (C) nullable.  Needs a workspace of
+ * vswin_patch_embed_workspace() bytes.                                       */
+size_t vswin_patch_embed_workspace(int32_t B, int32_t Cin, int32_t T, int32_t H, int32_t W,
+                                   const int32_t patch[3], vswin_dtype dtype);
+vswin_status vswin_patch_embed_fwd(int32_t B, int32_t Cin, int32_t T, int32_t H, int32_t W,
+                                   const int32_t patch[3], int32_t C, vswin_dtype dtype,
+                                   const void* video, const void* w, const void* b,
+                                   void* y, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Patch merging between stages (§3.1 step 2): x (B,T,H,W,C) ->
+ * y (B, T, ceil(H/2), ceil(W/2), Cout): the 2x2 spatial group concatenated in
+ * (h, w) offset order (0,0), (1,0), (0,1), (1,1) (zero beyond the grid),
+ * LayerNorm over 4C (g, b of 4C), then Linear(4C -> Cout) with w (Cout, 4C)
+ * and b (Cout) nullable.  Workspace: vswin_patch_merge_workspace() bytes.     */
+size_t vswin_patch_merge_workspace(int32_t B, int32_t T, int32_t H, int32_t W, int32_t C,
+                                   vswin_dtype dtype);
+vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, int32_t C,
+                                   int32_t Cout, vswin_dtype dtype, const void* x,
+                                   const void* ln_g, const void* ln_b, const void* w,
+                                   const void* b, float eps, void* y, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+const char* vswin_status_string(vswin_status s);
+const char* vswin_last_error(void);
+int32_t vswin_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSWIN_H_ */

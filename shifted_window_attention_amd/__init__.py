@@ -1,0 +1,319 @@
+"""Python binding of libvswin.so -- the MI355X (gfx950) Video Swin 3D
+(shifted-)window attention block.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/vswin.h.  PyTorch provides device
+memory and the current HIP stream.  There is no CPU fallback: if the library
+is missing or fails to load, every call raises.
+
+The functions carry the C entry points' names (``vswin_block_fwd`` ...).
+Tensors must be contiguous, on the current HIP device, float32 or bfloat16
+(all of one dtype per call), and 16-byte aligned (fresh torch allocations are).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+__all__ = [
+    "VswinError", "lib", "Desc", "BlockWeights", "PlanInfo", "make_desc",
+    "vswin_plan_query", "vswin_block_fwd", "vswin_window_msa_fwd", "vswin_attention_fwd",
+    "vswin_index_map",
+    "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
+    "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd",
+    "F_PAD_VISIBLE", "F_CLAMP_STRICT", "F_MASK_M100", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvswin.so")
+
+F_PAD_VISIBLE = 1
+F_CLAMP_STRICT = 2
+F_MASK_M100 = 4
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP error"}
+
+
+class VswinError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"vswin status {status} ({_STATUS.get(status, '?')}): {msg}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("C", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("window", ctypes.c_int32 * 3), ("shift", ctypes.c_int32 * 3),
+                ("mlp_hidden", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "ln1_g", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b", "rpb_table",
+        "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("eff_window", ctypes.c_int32 * 3), ("eff_shift", ctypes.c_int32 * 3),
+                ("padded", ctypes.c_int32 * 3), ("tokens_per_window", ctypes.c_int32),
+                ("num_windows", ctypes.c_int64), ("tokens", ctypes.c_int64),
+                ("masked", ctypes.c_int32), ("fast_attention", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t), ("msa_workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvswin.so (built in-tree by shifted_window_attention_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m shifted_window_attention_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    pdesc = ctypes.POINTER(Desc)
+    pw = ctypes.POINTER(BlockWeights)
+    i3 = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "vswin_plan_query": (i32, [pdesc, ctypes.POINTER(PlanInfo)]),
+        "vswin_block_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
+        "vswin_window_msa_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
+        "vswin_attention_fwd": (i32, [pdesc, vp, vp, vp, vp, vp, vp]),
+        "vswin_index_map": (i32, [pdesc, vp, vp, vp]),
+        "vswin_partition_fwd": (i32, [pdesc, vp, vp, vp]),
+        "vswin_reverse_fwd": (i32, [pdesc, vp, vp, vp, vp]),
+        "vswin_layernorm_fwd": (i32, [i64, i32, i32, i32, vp, vp, vp, f32, vp, vp]),
+        "vswin_patch_embed_workspace": (sz, [i32, i32, i32, i32, i32, i3, i32]),
+        "vswin_patch_embed_fwd": (i32, [i32, i32, i32, i32, i32, i3, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "vswin_patch_merge_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
+        "vswin_patch_merge_fwd": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp,
+                                        vp, sz, vp]),
+        "vswin_status_string": (ctypes.c_char_p, [i32]),
+        "vswin_last_error": (ctypes.c_char_p, []),
+        "vswin_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise VswinError(status, lib().vswin_last_error().decode())
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return 0
+    if t == torch.bfloat16:
+        return 1
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on the HIP device")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def make_desc(B: int, T: int, H: int, W: int, C: int, heads: int, window: Sequence[int],
+              shift: Sequence[int], *, mlp_hidden: Optional[int] = None, dtype=torch.bfloat16,
+              eps: float = 1e-5, flags: int = 0) -> Desc:
+    d = Desc()
+    d.B, d.T, d.H, d.W, d.C, d.heads = B, T, H, W, C, heads
+    for i in range(3):
+        d.window[i], d.shift[i] = int(window[i]), int(shift[i])
+    d.mlp_hidden = 4 * C if mlp_hidden is None else mlp_hidden
+    d.dtype = _dt(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    d.ln_eps, d.flags = eps, flags
+    return d
+
+
+def vswin_plan_query(desc: Desc, geometry_only: bool = False) -> dict:
+    """Host-only planning: clamped window/shift, padded grid, counts, workspace.
+
+    With geometry_only, a descriptor the compute entry points cannot serve
+    (status unsupported) still returns its geometry."""
+    p = PlanInfo()
+    st = lib().vswin_plan_query(ctypes.byref(desc), ctypes.byref(p))
+    if not (geometry_only and st == -2):
+        _check(st)
+    return dict(eff_window=tuple(p.eff_window), eff_shift=tuple(p.eff_shift), padded=tuple(p.padded),
+                tokens_per_window=p.tokens_per_window, num_windows=p.num_windows, tokens=p.tokens,
+                masked=bool(p.masked), fast_attention=bool(p.fast_attention),
+                workspace_bytes=p.workspace_bytes, msa_workspace_bytes=p.msa_workspace_bytes)
+
+
+def _desc_for(x: torch.Tensor, heads, window, shift, eps, flags, mlp_hidden) -> Desc:
+    B, T, H, W, C = x.shape
+    return make_desc(B, T, H, W, C, heads, window, shift, mlp_hidden=mlp_hidden, dtype=x.dtype,
+                     eps=eps, flags=flags)
+
+
+def _weights(w: Dict[str, torch.Tensor]) -> BlockWeights:
+    bw = BlockWeights()
+    for name, _ in BlockWeights._fields_:
+        t = w.get(name)
+        setattr(bw, name, _ptr(t) if t is not None else None)
+    return bw
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def vswin_block_fwd(x: torch.Tensor, w: Dict[str, torch.Tensor], heads: int, window: Sequence[int],
+                    shift: Sequence[int], *, eps: float = 1e-5, flags: int = 0,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """One Video Swin block (eq. 1) on x (B, T, H, W, C); returns y of x's shape."""
+    hid = w["fc1_w"].shape[0]
+    d = _desc_for(x, heads, window, shift, eps, flags, hid)
+    plan = vswin_plan_query(d)
+    y = torch.empty_like(x) if out is None else out
+    ws = _workspace(plan["workspace_bytes"], x.device, workspace)
+    bw = _weights(w)
+    _check(lib().vswin_block_fwd(ctypes.byref(d), _ptr(x), ctypes.byref(bw), _ptr(y), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+def vswin_window_msa_fwd(x_norm: torch.Tensor, w: Dict[str, torch.Tensor], heads: int,
+                         window: Sequence[int], shift: Sequence[int], *, eps: float = 1e-5,
+                         flags: int = 0, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The (S)W-MSA branch (§3.2) on the LayerNorm output; no residual."""
+    d = _desc_for(x_norm, heads, window, shift, eps, flags, 4 * x_norm.shape[-1])
+    plan = vswin_plan_query(d)
+    y = torch.empty_like(x_norm) if out is None else out
+    ws = _workspace(plan["msa_workspace_bytes"], x_norm.device, workspace)
+    bw = _weights(w)
+    _check(lib().vswin_window_msa_fwd(ctypes.byref(d), _ptr(x_norm), ctypes.byref(bw), _ptr(y),
+                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+def vswin_attention_fwd(desc: Desc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        table: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention core on projected windows: q/k/v (nW, heads, N, head_dim) ->
+    o (nW, N, C), heads concatenated."""
+    plan = vswin_plan_query(desc)
+    o = out if out is not None else torch.empty((plan["num_windows"], plan["tokens_per_window"], desc.C),
+                                                 dtype=q.dtype, device=q.device)
+    _check(lib().vswin_attention_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(table), _ptr(o),
+                                     _stream(stream)))
+    return o
+
+
+def vswin_index_map(desc: Desc, device="cuda", stream=None):
+    """(map int32 (nW*N,), region uint8 (nW*N,)) of the pad+roll+partition permutation."""
+    plan = vswin_plan_query(desc, geometry_only=True)
+    n = plan["num_windows"] * plan["tokens_per_window"]
+    m = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+    r = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    _check(lib().vswin_index_map(ctypes.byref(desc), _ptr(m), _ptr(r), _stream(stream)))
+    return m[:n], r[:n]
+
+
+def vswin_partition_fwd(x: torch.Tensor, window, shift, *, flags: int = 0, stream=None) -> torch.Tensor:
+    B, T, H, W, C = x.shape
+    d = make_desc(B, T, H, W, C, 1, window, shift, dtype=x.dtype, flags=flags)
+    plan = vswin_plan_query(d, geometry_only=True)
+    out = torch.empty((plan["num_windows"], plan["tokens_per_window"], C), dtype=x.dtype, device=x.device)
+    _check(lib().vswin_partition_fwd(ctypes.byref(d), _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def vswin_reverse_fwd(windows: torch.Tensor, shape, window, shift, *, residual=None, flags: int = 0,
+                      stream=None) -> torch.Tensor:
+    B, T, H, W, C = shape
+    d = make_desc(B, T, H, W, C, 1, window, shift, dtype=windows.dtype, flags=flags)
+    y = torch.empty(tuple(shape), dtype=windows.dtype, device=windows.device)
+    _check(lib().vswin_reverse_fwd(ctypes.byref(d), _ptr(windows), _ptr(residual), _ptr(y),
+                                   _stream(stream)))
+    return y
+
+
+def vswin_layernorm_fwd(x: torch.Tensor, g: torch.Tensor, b: torch.Tensor, eps: float = 1e-5,
+                        out_dtype=None, stream=None) -> torch.Tensor:
+    C = x.shape[-1]
+    out_dtype = g.dtype if out_dtype is None else out_dtype
+    y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    _check(lib().vswin_layernorm_fwd(x.numel() // C, C, _dt(x.dtype), _dt(out_dtype), _ptr(x), _ptr(g),
+                                     _ptr(b), eps, _ptr(y), _stream(stream)))
+    return y
+
+
+def vswin_patch_embed_fwd(video: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor],
+                          stream=None) -> torch.Tensor:
+    """video (B, Cin, T, H, W), w (C, Cin, pt, ph, pw) -> tokens (B, T', H', W', C)."""
+    B, Cin, T, H, W = video.shape
+    C, _, pt, ph, pw = w.shape
+    patch = (ctypes.c_int32 * 3)(pt, ph, pw)
+    dt = _dt(video.dtype)
+    nbytes = lib().vswin_patch_embed_workspace(B, Cin, T, H, W, patch, dt)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=video.device)
+    y = torch.empty((B, -(-T // pt), -(-H // ph), -(-W // pw), C), dtype=video.dtype, device=video.device)
+    _check(lib().vswin_patch_embed_fwd(B, Cin, T, H, W, patch, C, dt, _ptr(video), _ptr(w), _ptr(b),
+                                       _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def vswin_patch_merge_fwd(x: torch.Tensor, ln_g, ln_b, w, b=None, eps: float = 1e-5,
+                          stream=None) -> torch.Tensor:
+    """x (B, T, H, W, C) -> (B, T, ceil(H/2), ceil(W/2), Cout)."""
+    B, T, H, W, C = x.shape
+    Cout = w.shape[0]
+    dt = _dt(x.dtype)
+    nbytes = lib().vswin_patch_merge_workspace(B, T, H, W, C, dt)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+    y = torch.empty((B, T, -(-H // 2), -(-W // 2), Cout), dtype=x.dtype, device=x.device)
+    _check(lib().vswin_patch_merge_fwd(B, T, H, W, C, Cout, dt, _ptr(x), _ptr(ln_g), _ptr(ln_b), _ptr(w),
+                                       _ptr(b), eps, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def vswin_backbone_fwd(video: torch.Tensor, params: dict, cfg: dict, *, eps: float = 1e-5,
+                       collect: bool = False, stream=None):
+    """Video Swin backbone forward as a sequence of library calls: patch
+    embedding -> stages of blocks (shift 0 / half window alternating) with
+    patch merging between stages -> final LayerNorm (§3.1)."""
+    x = vswin_patch_embed_fwd(video, params["embed_w"], params.get("embed_b"), stream=stream)
+    window = tuple(cfg["window"])
+    half = tuple(v // 2 for v in window)
+    trace = []
+    n_st = len(cfg["depths"])
+    for i in range(n_st):
+        for j, p in enumerate(params["stages"][i]):
+            shift = (0, 0, 0) if j % 2 == 0 else half
+            y = vswin_block_fwd(x, p, cfg["heads"][i], window, shift, eps=eps, stream=stream)
+            if collect:
+                trace.append((x, y))
+            x = y
+        if i < n_st - 1:
+            m = params["merges"][i]
+            x = vswin_patch_merge_fwd(x, m["ln_g"], m["ln_b"], m["w"], m.get("b"), eps=eps, stream=stream)
+    out = vswin_layernorm_fwd(x, params["norm_g"], params["norm_b"], eps=eps, stream=stream)
+    return (out, trace) if collect else out

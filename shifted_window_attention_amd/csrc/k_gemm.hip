@@ -1,0 +1,263 @@
+// Linear layers of the Video Swin block (qkv, proj, fc1, fc2, patch embed,
+// patch merge): out = A (M x K) * W^T + bias with a fused epilogue.
+//
+// bf16 path: v_mfma_f32_16x16x32_bf16 (fp32 accumulate).  The kernel
+// computes C^T tiles -- MFMA operand A = 16 weight rows (features), operand
+// B = 16 activation rows (tokens), both K-contiguous in global memory and in
+// LDS -- so each lane ends with 4 consecutive output features of one token
+// and the epilogue writes 8- or 16-byte vectors.  Block tile 128 tokens x BN
+// features, 4 waves as 2 x 2, K staged 32 at a time through double-buffered
+// LDS with an 80-byte row pitch (conflict-free 16-byte fragment reads).
+// fp32 path: a plain LDS-tiled FMA kernel (it serves the small fp32
+// workload; throughput is not its purpose).
+#include "vswin_kernels.h"
+
+namespace vswin {
+
+__device__ __forceinline__ float gelu_erf(float x) {
+  // exact GELU: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+template <typename T, Epi KIND>
+struct EpiDev {
+  EpiArgs a;
+  __device__ __forceinline__ int64_t row_ctx(int64_t m) const {
+    if constexpr (KIND == Epi::kProjRes || KIND == Epi::kProjOut) {
+      int lab;
+      const int64_t w = m / a.N;
+      return slot_source(a.geo, w, (int)(m - w * a.N), lab);
+    } else {
+      return m;
+    }
+  }
+  __device__ __forceinline__ void store(int64_t m, int64_t rc, int n0, float v[4]) const {
+    if (a.bias) {
+      float bb[4];
+      load4((const T*)a.bias, n0, bb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += bb[i];
+    }
+    if constexpr (KIND == Epi::kBias) {
+      store4((T*)a.out, m * a.ld_out + n0, v);
+    } else if constexpr (KIND == Epi::kGelu) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
+      store4((T*)a.out, m * a.ld_out + n0, v);
+    } else if constexpr (KIND == Epi::kRes) {
+      float r[4];
+      load4((const float*)a.res, m * a.ld_out + n0, r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += r[i];
+      store4((T*)a.out, m * a.ld_out + n0, v);
+    } else if constexpr (KIND == Epi::kQKV) {
+      const int which = n0 / a.C;
+      const int c = n0 - which * a.C;
+      const int h = c / a.d;
+      const int e = c - h * a.d;
+      const int64_t w = m / a.N;
+      const int t = (int)(m - w * a.N);
+      T* base = (T*)(which == 0 ? a.out : (which == 1 ? a.out2 : a.out3));
+      store4(base, ((w * a.heads + h) * a.N + t) * a.d + e, v);
+    } else if constexpr (KIND == Epi::kProjRes) {
+      if (rc < 0) return;
+      float r[4];
+      load4((const T*)a.res, rc * a.C + n0, r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += r[i];
+      store4((float*)a.out, rc * a.C + n0, v);
+    } else {  // kProjOut
+      if (rc < 0) return;
+      store4((T*)a.out, rc * a.C + n0, v);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMM
+// ---------------------------------------------------------------------------
+constexpr int kBM = 128, kBK = 32, kLDK = 40;
+
+template <int BN, class E>
+__global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
+                                                        int64_t M, int N, int K, E epi) {
+  constexpr int WN = BN / 2;
+  constexpr int NT = WN / 16;
+  constexpr int MT = 4;
+  constexpr int WCH = (BN * 4 + 255) / 256;   // 16-byte weight chunks per thread
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][kBM * kLDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Ws[2][BN * kLDK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nb = N / BN;
+  const int64_t bm = blockIdx.x / nb;
+  const int bn = (int)(blockIdx.x - bm * nb);
+  const int64_t m0 = bm * kBM;
+  const int n0 = bn * BN;
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t ra[2], rw[WCH];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c >> 2, kc = (c & 3) * 8;
+      const int64_t m = m0 + r;
+      if (m < M) ra[i] = *reinterpret_cast<const u32x4_t*>(A + m * K + kt * kBK + kc);
+      else ra[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int c = tid + 256 * i;
+      if (c < BN * 4) {
+        const int r = c >> 2, kc = (c & 3) * 8;
+        rw[i] = *reinterpret_cast<const u32x4_t*>(W + (int64_t)(n0 + r) * K + kt * kBK + kc);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c >> 2, kc = (c & 3) * 8;
+      *reinterpret_cast<u32x4_t*>(&As[buf][r * kLDK + kc]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int c = tid + 256 * i;
+      if (c < BN * 4) {
+        const int r = c >> 2, kc = (c & 3) * 8;
+        *reinterpret_cast<u32x4_t*>(&Ws[buf][r * kLDK + kc]) = rw[i];
+      }
+    }
+  };
+
+  const int nk = K / kBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    bf16x8_t af[MT], wf[NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(wm * 64 + mt * 16 + fr) * kLDK + fk]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      wf[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][(wn * WN + nt * 16 + fr) * kLDK + fk]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], af[mt], acc[mt][nt], 0, 0, 0);
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t m = m0 + wm * 64 + mt * 16 + fr;
+    if (m >= M) continue;
+    const int64_t rc = epi.row_ctx(m);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + wn * WN + nt * 16 + (lane >> 4) * 4;
+      float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+      epi.store(m, rc, n, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 FMA GEMM (64 x 64 tile, 4 x 4 outputs per thread)
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
+                                                       int64_t M, int N, int K, E epi) {
+  __shared__ float As[16][68];
+  __shared__ float Ws[16][68];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int nb = (N + 63) / 64;
+  const int64_t bm = blockIdx.x / nb;
+  const int bn = (int)(blockIdx.x - bm * nb);
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 4, kk = idx & 15;
+      const int64_t m = bm * 64 + r;
+      const int n = bn * 64 + r;
+      As[kk][r] = (m < M && k0 + kk < K) ? A[m * K + k0 + kk] : 0.f;
+      Ws[kk][r] = (n < N && k0 + kk < K) ? W[(int64_t)n * K + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = As[kk][ty * 4 + i]; w[i] = Ws[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = bm * 64 + ty * 4 + i;
+    const int n = bn * 64 + tx * 4;
+    if (m < M && n < N) {
+      const int64_t rc = epi.row_ctx(m);
+      float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+      epi.store(m, rc, n, v);
+    }
+  }
+}
+
+template <Epi KIND>
+static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K,
+                              const EpiArgs& e, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (dt == VSWIN_BF16) {
+    EpiDev<bf16_t, KIND> epi{e};
+    const int64_t mb = (M + kBM - 1) / kBM;
+    auto go = [&](auto kern, int bn) {
+      const int64_t blocks = mb * (N / bn);
+      kern<<<dim3((unsigned)blocks), dim3(256), 0, st>>>((const bf16_t*)A, (const bf16_t*)W, M, N, K, epi);
+    };
+    if (N % 128 == 0) go(gemm_bf16_kernel<128, EpiDev<bf16_t, KIND>>, 128);
+    else if (N % 96 == 0) go(gemm_bf16_kernel<96, EpiDev<bf16_t, KIND>>, 96);
+    else if (N % 64 == 0) go(gemm_bf16_kernel<64, EpiDev<bf16_t, KIND>>, 64);
+    else go(gemm_bf16_kernel<32, EpiDev<bf16_t, KIND>>, 32);
+  } else {
+    EpiDev<float, KIND> epi{e};
+    const int64_t blocks = ((M + 63) / 64) * ((N + 63) / 64);
+    gemm_f32_kernel<EpiDev<float, KIND>><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+        (const float*)A, (const float*)W, M, N, K, epi);
+  }
+  return hipGetLastError();
+}
+
+hipError_t gemm(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K, const EpiArgs& e,
+                hipStream_t st) {
+  switch (e.kind) {
+    case Epi::kBias: return launch_kind<Epi::kBias>(dt, A, W, M, N, K, e, st);
+    case Epi::kQKV: return launch_kind<Epi::kQKV>(dt, A, W, M, N, K, e, st);
+    case Epi::kProjRes: return launch_kind<Epi::kProjRes>(dt, A, W, M, N, K, e, st);
+    case Epi::kProjOut: return launch_kind<Epi::kProjOut>(dt, A, W, M, N, K, e, st);
+    case Epi::kGelu: return launch_kind<Epi::kGelu>(dt, A, W, M, N, K, e, st);
+    case Epi::kRes: return launch_kind<Epi::kRes>(dt, A, W, M, N, K, e, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vswin

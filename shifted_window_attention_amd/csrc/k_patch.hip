@@ -1,0 +1,89 @@
+// Gathers of the backbone's patch embedding and patch merging (§3.1 steps
+// 1-2): exact permutations (with zero fill beyond the grid) that turn both
+// layers into plain Linear layers on the MFMA GEMM.
+#include "vswin_kernels.h"
+
+namespace vswin {
+
+// video (B, Cin, T, H, W) -> rows (B*T'*H'*W', Cin*pt*ph*pw), patch values in
+// (c, kt, kh, kw) order, zeros beyond the video's end.
+template <typename T>
+__global__ void __launch_bounds__(256) patch_gather_kernel(const T* __restrict__ v, T* __restrict__ out, int B,
+                                                           int Cin, int Tv, int Hv, int Wv, int pt, int ph,
+                                                           int pw, int To, int Ho, int Wo) {
+  const int K = Cin * pt * ph * pw;
+  const int64_t total = (int64_t)B * To * Ho * Wo * K;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t row = i / K;
+  int k = (int)(i - row * K);
+  const int kw = k % pw; k /= pw;
+  const int kh = k % ph; k /= ph;
+  const int kt = k % pt;
+  const int c = k / pt;
+  int64_t r = row;
+  const int wo = (int)(r % Wo); r /= Wo;
+  const int ho = (int)(r % Ho); r /= Ho;
+  const int to = (int)(r % To);
+  const int b = (int)(r / To);
+  const int t = to * pt + kt, h = ho * ph + kh, w = wo * pw + kw;
+  float val = 0.f;
+  if (t < Tv && h < Hv && w < Wv)
+    val = Elem<T>::load(v, ((((int64_t)b * Cin + c) * Tv + t) * Hv + h) * Wv + w);
+  Elem<T>::store(out, i, val);
+}
+
+hipError_t patch_gather(vswin_dtype dt, const void* video, void* out, int B, int Cin, int T, int H, int W,
+                        int pt, int ph, int pw, hipStream_t st) {
+  const int To = (T + pt - 1) / pt, Ho = (H + ph - 1) / ph, Wo = (W + pw - 1) / pw;
+  const int64_t total = (int64_t)B * To * Ho * Wo * Cin * pt * ph * pw;
+  if (total <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (dt == VSWIN_BF16)
+    hipLaunchKernelGGL(patch_gather_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)video,
+                       (bf16_t*)out, B, Cin, T, H, W, pt, ph, pw, To, Ho, Wo);
+  else
+    hipLaunchKernelGGL(patch_gather_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)video,
+                       (float*)out, B, Cin, T, H, W, pt, ph, pw, To, Ho, Wo);
+  return hipGetLastError();
+}
+
+// x (B, T, H, W, C) -> (B, T, H2, W2, 4C): the 2x2 group in (h, w) offset
+// order (0,0), (1,0), (0,1), (1,1); zeros beyond the grid.  4 channels per
+// thread.
+template <typename T>
+__global__ void __launch_bounds__(256) merge_gather_kernel(const T* __restrict__ x, T* __restrict__ out, int B,
+                                                           int Tn, int H, int W, int C, int H2, int W2) {
+  const int c4 = C / 4;
+  const int64_t total = (int64_t)B * Tn * H2 * W2 * 4 * c4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  int64_t r = i;
+  const int cc = (int)(r % c4); r /= c4;
+  const int q = (int)(r % 4); r /= 4;
+  const int j = (int)(r % W2); r /= W2;
+  const int ii = (int)(r % H2); r /= H2;
+  const int t = (int)(r % Tn);
+  const int b = (int)(r / Tn);
+  const int h = 2 * ii + (q & 1), w = 2 * j + (q >> 1);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (h < H && w < W) load4(x, ((((int64_t)b * Tn + t) * H + h) * W + w) * C + 4 * cc, v);
+  store4(out, i * 4, v);
+}
+
+hipError_t merge_gather(vswin_dtype dt, const void* x, void* out, int B, int T, int H, int W, int C,
+                        hipStream_t st) {
+  const int H2 = (H + 1) / 2, W2 = (W + 1) / 2;
+  const int64_t total = (int64_t)B * T * H2 * W2 * C;
+  if (total <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (dt == VSWIN_BF16)
+    hipLaunchKernelGGL(merge_gather_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)x,
+                       (bf16_t*)out, B, T, H, W, C, H2, W2);
+  else
+    hipLaunchKernelGGL(merge_gather_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)x,
+                       (float*)out, B, T, H, W, C, H2, W2);
+  return hipGetLastError();
+}
+
+}  // namespace vswin

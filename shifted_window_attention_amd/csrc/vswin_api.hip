@@ -1,0 +1,462 @@
+// C ABI of libvswin.so: argument validation, the block plan (clamp, padding,
+// window counts, workspace layout) and the launch sequence on one stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "vswin_kernels.h"
+
+using namespace vswin;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+vswin_status fail(vswin_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+vswin_status fail(vswin_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+vswin_status hip_fail(hipError_t e, const char* where) {
+  return fail(VSWIN_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Test hook: VSWIN_FAULT=launch makes every compute call fail as if a launch
+// had failed, after validation and before anything is enqueued.
+bool fault_injected() {
+  const char* f = getenv("VSWIN_FAULT");
+  return f && strcmp(f, "launch") == 0;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t elem_size(vswin_dtype d) { return d == VSWIN_BF16 ? 2 : 4; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Plan {
+  WinGeo geo;
+  RelTab rel;
+  int B, C, heads, d, hid;
+  int64_t L, Lp, nW;
+  int N;
+  bool use_mask;
+  bool fast;
+  vswin_dtype dt;
+  // workspace offsets (bytes)
+  size_t off_xw, off_q, off_k, off_v, off_zh, off_h, ws_block, ws_msa;
+};
+
+AttnArgs attn_args(const Plan& p, const void* q, const void* k, const void* v, const void* table, void* o,
+                   uint32_t flags) {
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.table = table; a.o = o;
+  a.nW = p.nW; a.heads = p.heads; a.d = p.d; a.C = p.C; a.N = p.N;
+  a.rel = p.rel; a.geo = p.geo;
+  a.use_mask = p.use_mask ? 1 : 0;
+  a.mask_m100 = (flags & VSWIN_F_MASK_M100) ? 1 : 0;
+  return a;
+}
+
+vswin_status make_plan(const vswin_desc* d, Plan& p, bool compute = true) {
+  if (!d) return fail(VSWIN_ERR_INVALID_ARG, "desc is NULL");
+  if (d->dtype != VSWIN_FP32 && d->dtype != VSWIN_BF16)
+    return fail(VSWIN_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
+  if (d->B < 0 || d->T < 1 || d->H < 1 || d->W < 1 || d->C < 1)
+    return fail(VSWIN_ERR_INVALID_ARG, "bad token shape B=%d T=%d H=%d W=%d C=%d", d->B, d->T, d->H, d->W, d->C);
+  if (d->heads < 1 || d->C % d->heads != 0)
+    return fail(VSWIN_ERR_INVALID_ARG, "C=%d is not a multiple of heads=%d", d->C, d->heads);
+  if (d->mlp_hidden < 1) return fail(VSWIN_ERR_INVALID_ARG, "mlp_hidden=%d", d->mlp_hidden);
+  if (!(d->ln_eps > 0.f)) return fail(VSWIN_ERR_INVALID_ARG, "ln_eps must be > 0");
+  if (d->flags & ~(uint32_t)(VSWIN_F_PAD_VISIBLE | VSWIN_F_CLAMP_STRICT | VSWIN_F_MASK_M100))
+    return fail(VSWIN_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
+  const int size[3] = {d->T, d->H, d->W};
+  int win[3], sh[3], pad[3];
+  for (int i = 0; i < 3; ++i) {
+    if (d->window[i] < 1) return fail(VSWIN_ERR_INVALID_ARG, "window[%d]=%d", i, d->window[i]);
+    if (d->shift[i] < 0 || d->shift[i] >= d->window[i])
+      return fail(VSWIN_ERR_INVALID_ARG, "shift[%d]=%d not in [0, window)", i, d->shift[i]);
+    const bool small = (d->flags & VSWIN_F_CLAMP_STRICT) ? size[i] < d->window[i] : size[i] <= d->window[i];
+    win[i] = small ? size[i] : d->window[i];
+    sh[i] = small ? 0 : d->shift[i];
+    pad[i] = (size[i] + win[i] - 1) / win[i] * win[i];
+  }
+  const int dh = d->C / d->heads;
+  const int N = win[0] * win[1] * win[2];
+  if (!compute) {
+    // permutation-only entry points: 4-channel vectors
+    if (d->C % 4) return fail(VSWIN_ERR_UNSUPPORTED, "C=%d not a multiple of 4", d->C);
+  } else if (dh > 64) {
+    return fail(VSWIN_ERR_UNSUPPORTED, "head_dim %d > 64", dh);
+  } else if (dh % 4 != 0) {
+    return fail(VSWIN_ERR_UNSUPPORTED, "head_dim %d not a multiple of 4", dh);
+  } else if (N > 2048) {
+    return fail(VSWIN_ERR_UNSUPPORTED, "window of %d tokens > 2048", N);
+  } else if (d->dtype == VSWIN_BF16) {
+    if (d->C % 32 || d->mlp_hidden % 32)
+      return fail(VSWIN_ERR_UNSUPPORTED, "bf16 path needs C and mlp_hidden multiples of 32 (C=%d hidden=%d)",
+                  d->C, d->mlp_hidden);
+  } else if (d->C % 4 || d->mlp_hidden % 4) {
+    return fail(VSWIN_ERR_UNSUPPORTED, "C and mlp_hidden must be multiples of 4");
+  }
+  WinGeo& g = p.geo;
+  g.T = d->T; g.H = d->H; g.W = d->W;
+  g.Tp = pad[0]; g.Hp = pad[1]; g.Wp = pad[2];
+  g.P = win[0]; g.Mh = win[1]; g.Mw = win[2];
+  g.st = sh[0]; g.sh = sh[1]; g.sw = sh[2];
+  g.nwh = pad[1] / win[1]; g.nww = pad[2] / win[2];
+  g.N = N;
+  g.nws = (pad[0] / win[0]) * g.nwh * g.nww;
+  g.pad_visible = (d->flags & VSWIN_F_PAD_VISIBLE) ? 1 : 0;
+  const int R = (2 * d->window[1] - 1) * (2 * d->window[2] - 1);
+  p.rel.R = R;
+  p.rel.Rw = 2 * d->window[2] - 1;
+  p.rel.rows = (2 * d->window[0] - 1) * R;
+  p.rel.centre = (d->window[0] - 1) * R + (d->window[1] - 1) * p.rel.Rw + (d->window[2] - 1);
+  p.B = d->B; p.C = d->C; p.heads = d->heads; p.d = dh; p.hid = d->mlp_hidden; p.dt = d->dtype;
+  p.N = N;
+  p.nW = (int64_t)d->B * g.nws;
+  p.Lp = p.nW * N;
+  p.L = (int64_t)d->B * d->T * d->H * d->W;
+  const bool shifted = sh[0] || sh[1] || sh[2];
+  const bool has_pad = pad[0] != d->T || pad[1] != d->H || pad[2] != d->W;
+  p.use_mask = shifted || (has_pad && !g.pad_visible);
+  p.fast = attention_mfma_supported(p.dt, attn_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, d->flags));
+  const size_t es = elem_size(d->dtype);
+  const size_t act = align256((size_t)p.Lp * p.C * es);
+  p.off_xw = 0;
+  p.off_q = act;
+  p.off_k = 2 * act;
+  p.off_v = 3 * act;
+  p.ws_msa = 4 * act;
+  p.off_zh = 4 * act;
+  p.off_h = p.off_zh + align256((size_t)p.L * p.C * 4);
+  p.ws_block = p.off_h + align256((size_t)p.L * p.hid * es);
+  return VSWIN_OK;
+}
+
+vswin_status check_ptr(const void* ptr, const char* name, bool nullable = false) {
+  if (!ptr) return nullable ? VSWIN_OK : fail(VSWIN_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(ptr, 16)) return fail(VSWIN_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return VSWIN_OK;
+}
+
+#define CHECK(expr)                     \
+  do {                                  \
+    const vswin_status s_ = (expr);     \
+    if (s_ != VSWIN_OK) return s_;      \
+  } while (0)
+
+#define HIPCHECK(expr, where)                          \
+  do {                                                 \
+    const hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, where);  \
+  } while (0)
+
+vswin_status check_msa_weights(const vswin_block_weights* w) {
+  if (!w) return fail(VSWIN_ERR_INVALID_ARG, "weights is NULL");
+  CHECK(check_ptr(w->qkv_w, "qkv_w"));
+  CHECK(check_ptr(w->qkv_b, "qkv_b", true));
+  CHECK(check_ptr(w->proj_w, "proj_w"));
+  CHECK(check_ptr(w->proj_b, "proj_b", true));
+  CHECK(check_ptr(w->rpb_table, "rpb_table"));
+  return VSWIN_OK;
+}
+
+// qkv -> attention -> proj (+ scatter); `xw` holds the gathered window rows.
+vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weights* w, char* ws,
+                     const void* residual, void* out, bool to_zh, hipStream_t st) {
+  void* xw = ws + p.off_xw;
+  void* q = ws + p.off_q;
+  void* k = ws + p.off_k;
+  void* v = ws + p.off_v;
+  EpiArgs e{};
+  e.kind = Epi::kQKV;
+  e.bias = w->qkv_b;
+  e.out = q; e.out2 = k; e.out3 = v;
+  e.C = p.C; e.heads = p.heads; e.d = p.d; e.N = p.N; e.geo = p.geo;
+  HIPCHECK(gemm(p.dt, xw, w->qkv_w, p.Lp, 3 * p.C, p.C, e, st), "qkv gemm");
+  const AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags);
+  if (p.fast) HIPCHECK(attention_mfma(a, st), "attention (mfma)");
+  else HIPCHECK(attention_generic(p.dt, a, st), "attention (generic)");
+  EpiArgs e2{};
+  e2.kind = to_zh ? Epi::kProjRes : Epi::kProjOut;
+  e2.bias = w->proj_b;
+  e2.out = out;
+  e2.res = residual;
+  e2.C = p.C; e2.heads = p.heads; e2.d = p.d; e2.N = p.N; e2.geo = p.geo;
+  HIPCHECK(gemm(p.dt, xw, w->proj_w, p.Lp, p.C, p.C, e2, st), "proj gemm");
+  return VSWIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vswin_last_error(void) { return g_err; }
+int32_t vswin_abi_version(void) { return VSWIN_ABI_VERSION; }
+
+const char* vswin_status_string(vswin_status s) {
+  switch (s) {
+    case VSWIN_OK: return "ok";
+    case VSWIN_ERR_INVALID_ARG: return "invalid argument";
+    case VSWIN_ERR_UNSUPPORTED: return "unsupported";
+    case VSWIN_ERR_WORKSPACE: return "workspace too small";
+    case VSWIN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+vswin_status vswin_plan_query(const vswin_desc* desc, vswin_plan* plan) {
+  if (!plan) return fail(VSWIN_ERR_INVALID_ARG, "plan is NULL");
+  Plan p{};
+  CHECK(make_plan(desc, p, false));
+  plan->eff_window[0] = p.geo.P; plan->eff_window[1] = p.geo.Mh; plan->eff_window[2] = p.geo.Mw;
+  plan->eff_shift[0] = p.geo.st; plan->eff_shift[1] = p.geo.sh; plan->eff_shift[2] = p.geo.sw;
+  plan->padded[0] = p.geo.Tp; plan->padded[1] = p.geo.Hp; plan->padded[2] = p.geo.Wp;
+  plan->tokens_per_window = p.N;
+  plan->num_windows = p.nW;
+  plan->tokens = p.L;
+  plan->masked = p.use_mask ? 1 : 0;
+  plan->fast_attention = p.fast ? 1 : 0;
+  plan->workspace_bytes = p.ws_block;
+  plan->msa_workspace_bytes = p.ws_msa;
+  // geometry is filled in; now the constraints of the compute entry points
+  Plan q{};
+  return make_plan(desc, q, true);
+}
+
+vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.L == 0) return VSWIN_OK;   // empty batch: nothing to read or write
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(y, "y"));
+  if (x == y) return fail(VSWIN_ERR_INVALID_ARG, "x and y must not alias");
+  CHECK(check_msa_weights(w));
+  CHECK(check_ptr(w->ln1_g, "ln1_g"));
+  CHECK(check_ptr(w->ln1_b, "ln1_b"));
+  CHECK(check_ptr(w->ln2_g, "ln2_g"));
+  CHECK(check_ptr(w->ln2_b, "ln2_b"));
+  CHECK(check_ptr(w->fc1_w, "fc1_w"));
+  CHECK(check_ptr(w->fc1_b, "fc1_b", true));
+  CHECK(check_ptr(w->fc2_w, "fc2_w"));
+  CHECK(check_ptr(w->fc2_b, "fc2_b", true));
+  if (p.L == 0) return VSWIN_OK;
+  if (!workspace || !aligned(workspace, 256))
+    return fail(VSWIN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.ws_block)
+    return fail(VSWIN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, p.ws_block);
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  // LN1 + pad + roll + partition
+  HIPCHECK(ln_gather(p.dt, x, w->ln1_g, w->ln1_b, ws + p.off_xw, p.Lp, p.C, desc->ln_eps, p.geo, 1, st),
+           "ln1 gather");
+  // attention branch; z^ = x + MSA (fp32)
+  CHECK(run_msa(p, desc, w, ws, x, ws + p.off_zh, true, st));
+  // LN2 -> xw region (free after proj)
+  HIPCHECK(ln_rows(VSWIN_FP32, p.dt, ws + p.off_zh, w->ln2_g, w->ln2_b, ws + p.off_xw, p.L, p.C, desc->ln_eps,
+                   st),
+           "ln2");
+  EpiArgs e{};
+  e.kind = Epi::kGelu;
+  e.bias = w->fc1_b;
+  e.out = ws + p.off_h;
+  e.ld_out = p.hid;
+  HIPCHECK(gemm(p.dt, ws + p.off_xw, w->fc1_w, p.L, p.hid, p.C, e, st), "fc1 gemm");
+  EpiArgs e2{};
+  e2.kind = Epi::kRes;
+  e2.bias = w->fc2_b;
+  e2.out = y;
+  e2.res = ws + p.off_zh;
+  e2.ld_out = p.C;
+  HIPCHECK(gemm(p.dt, ws + p.off_h, w->fc2_w, p.L, p.C, p.hid, e2, st), "fc2 gemm");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm, const vswin_block_weights* w,
+                                  void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.L == 0) return VSWIN_OK;
+  CHECK(check_ptr(x_norm, "x_norm"));
+  CHECK(check_ptr(y, "y"));
+  if (x_norm == y) return fail(VSWIN_ERR_INVALID_ARG, "x_norm and y must not alias");
+  CHECK(check_msa_weights(w));
+  if (p.L == 0) return VSWIN_OK;
+  if (!workspace || !aligned(workspace, 256))
+    return fail(VSWIN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.ws_msa)
+    return fail(VSWIN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, p.ws_msa);
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  HIPCHECK(ln_gather(p.dt, x_norm, nullptr, nullptr, ws + p.off_xw, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
+           "partition");
+  return run_msa(p, desc, w, ws, nullptr, y, false, st);
+}
+
+vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const void* k, const void* v,
+                                 const void* rpb_table, void* o, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.Lp == 0) return VSWIN_OK;
+  CHECK(check_ptr(q, "q"));
+  CHECK(check_ptr(k, "k"));
+  CHECK(check_ptr(v, "v"));
+  CHECK(check_ptr(rpb_table, "rpb_table"));
+  CHECK(check_ptr(o, "o"));
+  if (p.Lp == 0) return VSWIN_OK;
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  const AttnArgs a = attn_args(p, q, k, v, rpb_table, o, desc->flags);
+  if (p.fast) HIPCHECK(attention_mfma(a, (hipStream_t)stream), "attention (mfma)");
+  else HIPCHECK(attention_generic(p.dt, a, (hipStream_t)stream), "attention (generic)");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_index_map(const vswin_desc* desc, int32_t* map, uint8_t* region, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p, false));
+  if (p.Lp == 0) return VSWIN_OK;
+  if (!map) return fail(VSWIN_ERR_INVALID_ARG, "map is NULL");
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  HIPCHECK(index_map(map, region, p.Lp, p.geo, (hipStream_t)stream), "index map");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_partition_fwd(const vswin_desc* desc, const void* x, void* windows, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p, false));
+  if (p.Lp == 0) return VSWIN_OK;
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(windows, "windows"));
+  if (p.Lp == 0) return VSWIN_OK;
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  HIPCHECK(ln_gather(p.dt, x, nullptr, nullptr, windows, p.Lp, p.C, desc->ln_eps, p.geo, 0, (hipStream_t)stream),
+           "partition");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_reverse_fwd(const vswin_desc* desc, const void* windows, const void* residual, void* y,
+                               void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p, false));
+  if (p.Lp == 0) return VSWIN_OK;
+  CHECK(check_ptr(windows, "windows"));
+  CHECK(check_ptr(residual, "residual", true));
+  CHECK(check_ptr(y, "y"));
+  if (p.Lp == 0) return VSWIN_OK;
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  HIPCHECK(reverse_scatter(p.dt, windows, residual, y, p.Lp, p.C, p.geo, (hipStream_t)stream), "reverse");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_layernorm_fwd(int64_t rows, int32_t C, vswin_dtype in_dtype, vswin_dtype out_dtype,
+                                 const void* x, const void* g, const void* b, float eps, void* y, void* stream) {
+  if (rows < 0 || C < 2 || C % 2 || C > 4096) return fail(VSWIN_ERR_INVALID_ARG, "rows=%lld C=%d", (long long)rows, C);
+  if ((in_dtype != VSWIN_FP32 && in_dtype != VSWIN_BF16) || (out_dtype != VSWIN_FP32 && out_dtype != VSWIN_BF16))
+    return fail(VSWIN_ERR_INVALID_ARG, "bad dtype");
+  if (!(eps > 0.f)) return fail(VSWIN_ERR_INVALID_ARG, "eps must be > 0");
+  if (rows == 0) return VSWIN_OK;
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(g, "g"));
+  CHECK(check_ptr(b, "b"));
+  CHECK(check_ptr(y, "y"));
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  HIPCHECK(ln_rows(in_dtype, out_dtype, x, g, b, y, rows, C, eps, (hipStream_t)stream), "layernorm");
+  return VSWIN_OK;
+}
+
+size_t vswin_patch_embed_workspace(int32_t B, int32_t Cin, int32_t T, int32_t H, int32_t W, const int32_t patch[3],
+                                   vswin_dtype dtype) {
+  if (!patch || patch[0] < 1 || patch[1] < 1 || patch[2] < 1 || B < 0 || Cin < 1) return 0;
+  const int64_t rows = (int64_t)B * ((T + patch[0] - 1) / patch[0]) * ((H + patch[1] - 1) / patch[1]) *
+                       ((W + patch[2] - 1) / patch[2]);
+  return align256((size_t)rows * Cin * patch[0] * patch[1] * patch[2] * elem_size(dtype));
+}
+
+vswin_status vswin_patch_embed_fwd(int32_t B, int32_t Cin, int32_t T, int32_t H, int32_t W, const int32_t patch[3],
+                                   int32_t C, vswin_dtype dtype, const void* video, const void* w, const void* b,
+                                   void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!patch || patch[0] < 1 || patch[1] < 1 || patch[2] < 1)
+    return fail(VSWIN_ERR_INVALID_ARG, "bad patch size");
+  if (B < 0 || Cin < 1 || T < 1 || H < 1 || W < 1 || C < 1)
+    return fail(VSWIN_ERR_INVALID_ARG, "bad video shape");
+  if (dtype != VSWIN_FP32 && dtype != VSWIN_BF16) return fail(VSWIN_ERR_INVALID_ARG, "bad dtype");
+  const int K = Cin * patch[0] * patch[1] * patch[2];
+  if (dtype == VSWIN_BF16 && (K % 32 || C % 32))
+    return fail(VSWIN_ERR_UNSUPPORTED, "bf16 patch embed needs Cin*patch and C multiples of 32");
+  if (dtype == VSWIN_FP32 && C % 4) return fail(VSWIN_ERR_UNSUPPORTED, "C must be a multiple of 4");
+  if (B == 0) return VSWIN_OK;
+  CHECK(check_ptr(video, "video"));
+  CHECK(check_ptr(w, "w"));
+  CHECK(check_ptr(b, "b", true));
+  CHECK(check_ptr(y, "y"));
+  const size_t need = vswin_patch_embed_workspace(B, Cin, T, H, W, patch, dtype);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(VSWIN_ERR_WORKSPACE, "patch embed needs %zu workspace bytes", need);
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHECK(patch_gather(dtype, video, workspace, B, Cin, T, H, W, patch[0], patch[1], patch[2], st), "patch gather");
+  const int64_t rows = (int64_t)B * ((T + patch[0] - 1) / patch[0]) * ((H + patch[1] - 1) / patch[1]) *
+                       ((W + patch[2] - 1) / patch[2]);
+  EpiArgs e{};
+  e.kind = Epi::kBias;
+  e.bias = b;
+  e.out = y;
+  e.ld_out = C;
+  HIPCHECK(gemm(dtype, workspace, w, rows, C, K, e, st), "patch embed gemm");
+  return VSWIN_OK;
+}
+
+size_t vswin_patch_merge_workspace(int32_t B, int32_t T, int32_t H, int32_t W, int32_t C, vswin_dtype dtype) {
+  if (B < 0 || T < 1 || H < 1 || W < 1 || C < 1) return 0;
+  const int64_t rows = (int64_t)B * T * ((H + 1) / 2) * ((W + 1) / 2);
+  return 2 * align256((size_t)rows * 4 * C * elem_size(dtype));
+}
+
+vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, int32_t C, int32_t Cout,
+                                   vswin_dtype dtype, const void* x, const void* ln_g, const void* ln_b,
+                                   const void* w, const void* b, float eps, void* y, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 1 || H < 1 || W < 1 || C < 1 || Cout < 1) return fail(VSWIN_ERR_INVALID_ARG, "bad shape");
+  if (dtype != VSWIN_FP32 && dtype != VSWIN_BF16) return fail(VSWIN_ERR_INVALID_ARG, "bad dtype");
+  if (!(eps > 0.f)) return fail(VSWIN_ERR_INVALID_ARG, "eps must be > 0");
+  if (C % 8) return fail(VSWIN_ERR_UNSUPPORTED, "C must be a multiple of 8");
+  if (4 * C > 4096) return fail(VSWIN_ERR_UNSUPPORTED, "4C > 4096");
+  if (dtype == VSWIN_BF16 && Cout % 32) return fail(VSWIN_ERR_UNSUPPORTED, "bf16 merge needs Cout % 32 == 0");
+  if (dtype == VSWIN_FP32 && Cout % 4) return fail(VSWIN_ERR_UNSUPPORTED, "Cout must be a multiple of 4");
+  if (B == 0) return VSWIN_OK;
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(ln_g, "ln_g"));
+  CHECK(check_ptr(ln_b, "ln_b"));
+  CHECK(check_ptr(w, "w"));
+  CHECK(check_ptr(b, "b", true));
+  CHECK(check_ptr(y, "y"));
+  const size_t need = vswin_patch_merge_workspace(B, T, H, W, C, dtype);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(VSWIN_ERR_WORKSPACE, "patch merge needs %zu workspace bytes", need);
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t rows = (int64_t)B * T * ((H + 1) / 2) * ((W + 1) / 2);
+  char* g4 = (char*)workspace;
+  char* n4 = g4 + need / 2;
+  HIPCHECK(merge_gather(dtype, x, g4, B, T, H, W, C, st), "merge gather");
+  HIPCHECK(ln_rows(dtype, dtype, g4, ln_g, ln_b, n4, rows, 4 * C, eps, st), "merge layernorm");
+  EpiArgs e{};
+  e.kind = Epi::kBias;
+  e.bias = b;
+  e.out = y;
+  e.ld_out = Cout;
+  HIPCHECK(gemm(dtype, n4, w, rows, Cout, 4 * C, e, st), "merge gemm");
+  return VSWIN_OK;
+}
+
+}  // extern "C"

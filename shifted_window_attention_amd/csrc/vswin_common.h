@@ -1,0 +1,146 @@
+// Shared host/device definitions of the vswin HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vswin.h"
+
+namespace vswin {
+
+// ---------------------------------------------------------------------------
+// Window geometry of one block after the clamp, as the kernels see it.
+// The permutation it encodes (pages: §3.2, fig. 3; the mmaction2 walk-through
+// op order LN -> pad -> roll -> partition):
+//   padded grid (Tp, Hp, Wp) = sizes rounded up to the window, zeros appended
+//   at the end; the padded grid is rolled by -shift, so rolled position r
+//   holds padded coordinate (r + s) mod n; windows (b, wt, wh, ww) and slots
+//   (pt, ph, pw) are row-major.
+// ---------------------------------------------------------------------------
+struct WinGeo {
+  int T, H, W;        // real token grid
+  int Tp, Hp, Wp;     // padded grid
+  int P, Mh, Mw;      // effective window
+  int st, sh, sw;     // effective shift
+  int nwh, nww;       // windows along H and W (nwt = Tp / P)
+  int N;              // tokens per window
+  int nws;            // windows per clip
+  int pad_visible;    // pads keep their positional label
+};
+
+// Region label of one axis (rolled position r, padded length n, window w,
+// shift s): slices [0, n-w), [n-w, n-s), [n-s, n) of the rolled grid.
+__host__ __device__ inline int axis_label(int r, int n, int w, int s) {
+  return s == 0 ? 0 : (r < n - w ? 0 : (r < n - s ? 1 : 2));
+}
+
+constexpr int kPadLabel = 255;
+
+// Source token (flat b,t,h,w) of window slot (w, n), or -1 for a pad slot;
+// `label` receives the slot's region label.
+__host__ __device__ inline int64_t slot_source(const WinGeo& g, int64_t w, int n, int& label) {
+  const int b = (int)(w / g.nws);
+  const int wr = (int)(w - (int64_t)b * g.nws);
+  const int wpl = g.nwh * g.nww;
+  const int wt = wr / wpl;
+  const int rem = wr - wt * wpl;
+  const int wh = rem / g.nww;
+  const int ww = rem - wh * g.nww;
+  const int mhw = g.Mh * g.Mw;
+  const int pt = n / mhw;
+  const int r2 = n - pt * mhw;
+  const int ph = r2 / g.Mw;
+  const int pw = r2 - ph * g.Mw;
+  const int rt = wt * g.P + pt, rh = wh * g.Mh + ph, rw = ww * g.Mw + pw;
+  int ot = rt + g.st; if (ot >= g.Tp) ot -= g.Tp;
+  int oh = rh + g.sh; if (oh >= g.Hp) oh -= g.Hp;
+  int ow = rw + g.sw; if (ow >= g.Wp) ow -= g.Wp;
+  const bool pad = ot >= g.T || oh >= g.H || ow >= g.W;
+  const int lab = 9 * axis_label(rt, g.Tp, g.P, g.st) + 3 * axis_label(rh, g.Hp, g.Mh, g.sh) +
+                  axis_label(rw, g.Wp, g.Mw, g.sw);
+  label = (pad && !g.pad_visible) ? kPadLabel : lab;
+  return pad ? (int64_t)-1 : (((int64_t)b * g.T + ot) * g.H + oh) * g.W + ow;
+}
+
+// Rolled-grid label of a slot given the window's rolled origin (rt0, rh0, rw0)
+// and in-window coordinates; used by the attention kernels, which already know
+// the window origin.
+__host__ __device__ inline int slot_label_at(const WinGeo& g, int rt, int rh, int rw) {
+  int ot = rt + g.st; if (ot >= g.Tp) ot -= g.Tp;
+  int oh = rh + g.sh; if (oh >= g.Hp) oh -= g.Hp;
+  int ow = rw + g.sw; if (ow >= g.Wp) ow -= g.Wp;
+  const bool pad = ot >= g.T || oh >= g.H || ow >= g.W;
+  const int lab = 9 * axis_label(rt, g.Tp, g.P, g.st) + 3 * axis_label(rh, g.Hp, g.Mh, g.sh) +
+                  axis_label(rw, g.Wp, g.Mw, g.sw);
+  return (pad && !g.pad_visible) ? kPadLabel : lab;
+}
+
+// Relative-position table geometry (configured window; eq. 2): the row of a
+// pair with offset (dt, dh, dw) = query - key is
+//   (dt + P0 - 1) * R + (dh + Mh0 - 1) * Rw + (dw + Mw0 - 1),
+// R = (2Mh0-1)(2Mw0-1), Rw = 2Mw0-1.  With f(t,h,w) = t*R + h*Rw + w the row
+// is f(query) - f(key) + centre, centre = f(P0-1, Mh0-1, Mw0-1).
+struct RelTab {
+  int rows;     // (2P0-1) * R
+  int R, Rw;
+  int centre;
+};
+
+#if defined(__HIPCC__)
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+__device__ __forceinline__ float bflo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bfhi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// round-to-nearest-even float -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t p;
+  p[0] = (__bf16)a;
+  p[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ uint16_t f2bf(float a) {
+  __bf16 h = (__bf16)a;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p, int64_t i) { return bf2f(p[i]); }
+  __device__ __forceinline__ static void store(bf16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+};
+
+// four consecutive elements (16-byte aligned for float, 8-byte for bf16)
+__device__ __forceinline__ void load4(const float* p, int64_t i, float v[4]) {
+  const float4 t = *reinterpret_cast<const float4*>(p + i);
+  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, int64_t i, float v[4]) {
+  const u32x2_t t = *reinterpret_cast<const u32x2_t*>(p + i);
+  v[0] = bflo(t[0]); v[1] = bfhi(t[0]); v[2] = bflo(t[1]); v[3] = bfhi(t[1]);
+}
+__device__ __forceinline__ void store4(float* p, int64_t i, const float v[4]) {
+  *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16_t* p, int64_t i, const float v[4]) {
+  u32x2_t t;
+  t[0] = pack_bf16x2(v[0], v[1]);
+  t[1] = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2_t*>(p + i) = t;
+}
+#endif
+
+}  // namespace vswin

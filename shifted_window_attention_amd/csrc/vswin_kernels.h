@@ -1,0 +1,69 @@
+// Host-side launchers of the vswin kernels (internal to libvswin.so).
+#pragma once
+
+#include "vswin_common.h"
+
+namespace vswin {
+
+// --- permutation / normalisation (k_layout.hip) ---------------------------
+hipError_t ln_gather(vswin_dtype dt, const void* x, const void* g, const void* b, void* y, int64_t slots,
+                     int C, float eps, const WinGeo& geo, int apply_ln, hipStream_t st);
+hipError_t ln_rows(vswin_dtype in_dt, vswin_dtype out_dt, const void* x, const void* g, const void* b,
+                   void* y, int64_t rows, int C, float eps, hipStream_t st);
+hipError_t reverse_scatter(vswin_dtype dt, const void* win, const void* res, void* y, int64_t slots, int C,
+                           const WinGeo& geo, hipStream_t st);
+hipError_t index_map(int32_t* map, uint8_t* region, int64_t slots, const WinGeo& geo, hipStream_t st);
+
+// --- GEMMs (k_gemm.hip): out = A (M x K) * W^T (W: N x K) + epilogue -------
+enum class Epi : int {
+  kBias = 0,     // out[m, n] = acc + bias                      (out: dtype)
+  kQKV = 1,      // acc + bias scattered to q/k/v (nW, heads, N, d)
+  kProjRes = 2,  // zh[src(m), n] = x[src(m), n] + acc + bias   (zh fp32)
+  kProjOut = 3,  // y[src(m), n] = acc + bias                   (y: dtype)
+  kGelu = 4,     // out[m, n] = gelu(acc + bias)                (out: dtype)
+  kRes = 5,      // out[m, n] = res32[m, n] + acc + bias        (out: dtype)
+};
+
+struct EpiArgs {
+  Epi kind;
+  const void* bias;   // (N) of dtype, nullable
+  void* out;          // primary output
+  void* out2;         // kQKV: k, out3: v
+  void* out3;
+  const void* res;    // kProjRes: x (dtype); kRes: zh (fp32)
+  int64_t ld_out;     // row pitch of out (elements) for kBias/kGelu/kRes
+  // kQKV / kProj*: geometry
+  int C, heads, d, N;
+  WinGeo geo;
+};
+
+hipError_t gemm(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K, const EpiArgs& e,
+                hipStream_t st);
+
+// --- attention (k_attention.hip) ------------------------------------------
+struct AttnArgs {
+  const void *q, *k, *v;   // (nW, heads, N, d) of dtype
+  const void* table;       // (rows, heads) of dtype
+  void* o;                 // (nW, N, C) of dtype
+  int64_t nW;
+  int heads, d, C, N;
+  RelTab rel;
+  WinGeo geo;
+  int use_mask;            // some window may need the region mask
+  int mask_m100;           // additive -100 instead of exclusion
+  int force_max;           // MFMA kernel: always take the exact row-max pass
+};
+hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st);
+hipError_t attention_mfma(const AttnArgs& a, hipStream_t st);
+// shapes the MFMA kernel serves (bf16, d = 32, temporal window % 4 == 0 with
+// group-uniform temporal labels, N <= kMfmaMaxN, no additive -100 mask)
+constexpr int kMfmaMaxN = 1024;
+bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a);
+
+// --- patch embedding / merging gathers (k_patch.hip) ----------------------
+hipError_t patch_gather(vswin_dtype dt, const void* video, void* out, int B, int Cin, int T, int H, int W,
+                        int pt, int ph, int pw, hipStream_t st);
+hipError_t merge_gather(vswin_dtype dt, const void* x, void* out, int B, int T, int H, int W, int C,
+                        hipStream_t st);
+
+}  // namespace vswin

@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+entry point include/vswin.h declares, the host plan matches the oracle's
+geometry exactly, and every argument error is reported before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import vswin as ov
+import shifted_window_attention_amd as vs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vswin.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vswin_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = vs.lib()
+    names = _declared()
+    assert "vswin_block_fwd" in names and "vswin_window_msa_fwd" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.vswin_abi_version() == 1
+
+
+def test_status_strings():
+    L = vs.lib()
+    for s, txt in [(0, b"ok"), (-1, b"invalid argument"), (-2, b"unsupported"),
+                   (-3, b"workspace too small"), (-4, b"HIP error")]:
+        assert L.vswin_status_string(s) == txt
+
+
+GEOMS = [
+    (1, (4, 14, 14), 32, 2, (2, 7, 7), (1, 3, 3), "fp32"),
+    (1, (16, 56, 56), 96, 3, (8, 7, 7), (0, 0, 0), "bf16"),
+    (1, (16, 56, 56), 96, 3, (8, 7, 7), (4, 3, 3), "bf16"),
+    (4, (16, 14, 14), 384, 12, (8, 7, 7), (4, 3, 3), "bf16"),
+    (8, (16, 60, 60), 128, 4, (8, 7, 7), (0, 0, 0), "bf16"),
+    (8, (16, 60, 60), 128, 4, (8, 7, 7), (4, 3, 3), "bf16"),
+    (2, (16, 7, 7), 768, 24, (8, 7, 7), (4, 3, 3), "bf16"),       # backbone stage 4: clamp
+    (2, (5, 9, 11), 32, 2, (2, 4, 3), (1, 2, 1), "bf16"),
+    (1, (3, 5, 5), 64, 2, (8, 7, 7), (4, 3, 3), "fp32"),
+]
+
+
+@pytest.mark.parametrize("g", GEOMS)
+@pytest.mark.parametrize("strict", [False, True])
+def test_plan_matches_oracle_geometry(g, strict):
+    B, size, C, heads, window, shift, dt = g
+    d = vs.make_desc(B, *size, C, heads, window, shift, dtype=0 if dt == "fp32" else 1,
+                     flags=vs.F_CLAMP_STRICT if strict else 0)
+    p = vs.vswin_plan_query(d)
+    o = ov.Geometry(B, size, window, shift, clamp_strict=strict)
+    assert p["eff_window"] == o.window
+    assert p["eff_shift"] == o.shift
+    assert p["padded"] == o.padded
+    assert p["tokens_per_window"] == o.N
+    assert p["num_windows"] == o.nW
+    assert p["tokens"] == B * int(np.prod(size))
+    assert p["masked"] == o.use_mask
+    assert p["workspace_bytes"] >= p["msa_workspace_bytes"] > 0
+
+
+def test_fast_path_selection():
+    for wid in (2, 3, 4):
+        s = synth.WORKLOADS[wid].shape
+        for shift in ((0, 0, 0), s.shift):
+            d = vs.make_desc(s.B, s.T, s.H, s.W, s.C, s.heads, s.window, shift, dtype=1)
+            assert vs.vswin_plan_query(d)["fast_attention"], (wid, shift)
+    # fp32 and windows whose temporal extent is not a multiple of 4 use the generic kernel
+    assert not vs.vswin_plan_query(vs.make_desc(1, 4, 14, 14, 32, 2, (2, 7, 7), (1, 3, 3), dtype=0))["fast_attention"]
+    assert not vs.vswin_plan_query(vs.make_desc(1, 6, 14, 14, 64, 2, (6, 7, 7), (3, 3, 3), dtype=1))["fast_attention"]
+    # code-compat -100 mask is only in the generic kernel
+    assert not vs.vswin_plan_query(vs.make_desc(1, 16, 14, 14, 64, 2, (8, 7, 7), (4, 3, 3), dtype=1,
+                                                flags=vs.F_MASK_M100))["fast_attention"]
+
+
+BAD = [
+    dict(C=96, heads=5),                       # C % heads
+    dict(shift=(8, 3, 3)),                     # shift >= window
+    dict(shift=(-1, 0, 0)),
+    dict(window=(0, 7, 7)),
+    dict(T=0),
+    dict(eps=0.0),
+    dict(flags=64),
+]
+
+
+@pytest.mark.parametrize("bad", BAD)
+def test_plan_rejects_bad_descriptors(bad):
+    kw = dict(B=1, T=16, H=14, W=14, C=96, heads=3, window=(8, 7, 7), shift=(4, 3, 3), eps=1e-5, flags=0)
+    kw.update(bad)
+    d = vs.make_desc(kw["B"], kw["T"], kw["H"], kw["W"], kw["C"], kw["heads"], kw["window"], kw["shift"],
+                     dtype=1, eps=kw["eps"], flags=kw["flags"])
+    with pytest.raises(vs.VswinError) as e:
+        vs.vswin_plan_query(d)
+    assert e.value.status == -1
+
+
+def test_unsupported_head_dim():
+    d = vs.make_desc(1, 16, 14, 14, 256, 2, (8, 7, 7), (0, 0, 0), dtype=1)   # head_dim 128
+    with pytest.raises(vs.VswinError) as e:
+        vs.vswin_plan_query(d)
+    assert e.value.status == -2
+
+
+def _fake_weights(base=0x10000):
+    w = vs.BlockWeights()
+    for i, (n, _) in enumerate(vs.BlockWeights._fields_):
+        setattr(w, n, base + 256 * i)
+    return w
+
+
+def _call_block(d, x, w, y, ws, nbytes, fn="vswin_block_fwd"):
+    return getattr(vs.lib(), fn)(ctypes.byref(d), x, ctypes.byref(w) if w is not None else None, y, ws,
+                                 nbytes, None)
+
+
+def test_block_argument_errors_before_launch():
+    d = vs.make_desc(1, 16, 14, 14, 96, 3, (8, 7, 7), (4, 3, 3), dtype=1)
+    need = vs.vswin_plan_query(d)["workspace_bytes"]
+    w = _fake_weights()
+    X, Y, WS = 0x100000, 0x200000, 0x300000
+    L = vs.lib()
+    assert _call_block(d, None, w, Y, WS, need) == -1                 # null x
+    assert _call_block(d, X + 8, w, Y, WS, need) == -1                # misaligned x
+    assert _call_block(d, X, w, X, WS, need) == -1                    # aliasing
+    assert _call_block(d, X, None, Y, WS, need) == -1                 # null weights
+    w2 = _fake_weights(); w2.rpb_table = None
+    assert _call_block(d, X, w2, Y, WS, need) == -1
+    assert b"rpb_table" in L.vswin_last_error()
+    assert _call_block(d, X, w, Y, WS, need - 1) == -3                # workspace too small
+    assert _call_block(d, X, w, Y, WS + 16, need) == -3               # workspace misaligned
+    need_msa = vs.vswin_plan_query(d)["msa_workspace_bytes"]
+    assert _call_block(d, X, w, Y, WS, need_msa - 1, "vswin_window_msa_fwd") == -3
+
+
+def test_fault_hook_reports_hip_error(monkeypatch):
+    monkeypatch.setenv("VSWIN_FAULT", "launch")
+    d = vs.make_desc(1, 16, 14, 14, 96, 3, (8, 7, 7), (4, 3, 3), dtype=1)
+    need = vs.vswin_plan_query(d)["workspace_bytes"]
+    assert _call_block(d, 0x100000, _fake_weights(), 0x200000, 0x300000, need) == -4
+    assert b"injected" in vs.lib().vswin_last_error()
+
+
+def test_empty_batch_is_a_no_op():
+    d = vs.make_desc(0, 16, 14, 14, 96, 3, (8, 7, 7), (4, 3, 3), dtype=1)
+    p = vs.vswin_plan_query(d)
+    assert p["num_windows"] == 0 and p["tokens"] == 0
+    # nothing is enqueued, so this runs without a GPU
+    assert _call_block(d, 0x100000, _fake_weights(), 0x200000, None, 0) == 0
