@@ -133,15 +133,17 @@ def main():
                        generator=g, device="cuda").to(torch.bfloat16) for _ in range(3)]
     o = torch.empty((plans[0]["num_windows"], plans[0]["tokens_per_window"], s.C), dtype=torch.bfloat16,
                     device="cuda")
+    attn_ws = torch.empty(max(256, max(p["attention_workspace_bytes"] for p in plans)), dtype=torch.uint8,
+                          device="cuda")
     kern_us = []
     for i, dsc in enumerate(descs):
         for _ in range(5):
-            vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, stream=stream)
+            vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, workspace=attn_ws, stream=stream)
         torch.cuda.synchronize()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record(stream)
         for _ in range(args.kernel_launches):
-            vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, stream=stream)
+            vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, workspace=attn_ws, stream=stream)
         a1.record(stream)
         torch.cuda.synchronize()
         kern_us.append(a0.elapsed_time(a1) * 1e3 / args.kernel_launches)

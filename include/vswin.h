@@ -110,6 +110,7 @@ typedef struct {
   int32_t fast_attention;  /* 1 if the MFMA attention kernel serves it       */
   size_t workspace_bytes;  /* device workspace needed by vswin_block_fwd     */
   size_t msa_workspace_bytes; /* ... and by vswin_window_msa_fwd             */
+  size_t attention_workspace_bytes; /* ... and by vswin_attention_fwd        */
 } vswin_plan;
 
 /* Validate `desc` and report the clamped geometry and workspace sizes.
@@ -149,14 +150,20 @@ vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm,
                                   void* workspace, size_t workspace_bytes,
                                   void* stream);
 
-/* The attention core alone (eq. 2) on projected windows: per window w and
- * head h, q/k/v[((w * heads + h) * N + n) * head_dim + e] (bf16 or fp32 of
- * desc.dtype; N = tokens per window, windows and slots ordered as for
- * vswin_index_map), o[(w * N + n) * C + h * head_dim + e] receives
- * softmax(q k^T / sqrt(head_dim) + B + mask) v.  rpb_table as in
- * vswin_block_weights.  No workspace.                                         */
+/* The attention core alone (eq. 2) on projected windows, in the layout
+ * vswin_block_fwd keeps internally:
+ *   q, k: [((w * heads + h) * N + s) * head_dim + e], o: [(w * N + s) * C +
+ *   h * head_dim + e]; v: as q when plan.fast_attention == 0, else transposed
+ *   [((w * heads + h) * head_dim + e) * N + s].
+ * s is the row of a window slot: natural (pt, ph, pw) order when
+ * plan.fast_attention == 0; otherwise the MFMA slot order s = 4 m + i for
+ * the token (pt = 4 a + i, ph, pw), m = (a * Mh + ph) * Mw + pw.
+ * o receives softmax(q k^T / sqrt(head_dim) + B + mask) v per window and head
+ * (rows of pad slots are unspecified).  rpb_table as in vswin_block_weights.
+ * workspace >= plan.attention_workspace_bytes (may be NULL when 0).        */
 vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const void* k,
-                                 const void* v, const void* rpb_table, void* o, void* stream);
+                                 const void* v, const void* rpb_table, void* o,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Index map of the pad + roll + partition permutation (§3.2):
  * map[w * N + n] = flat source token index b*T*H*W + (t*H + h)*W + w of

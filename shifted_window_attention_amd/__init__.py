@@ -61,7 +61,8 @@ class PlanInfo(ctypes.Structure):
                 ("padded", ctypes.c_int32 * 3), ("tokens_per_window", ctypes.c_int32),
                 ("num_windows", ctypes.c_int64), ("tokens", ctypes.c_int64),
                 ("masked", ctypes.c_int32), ("fast_attention", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t), ("msa_workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("msa_workspace_bytes", ctypes.c_size_t),
+                ("attention_workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -84,7 +85,7 @@ def lib() -> ctypes.CDLL:
         "vswin_plan_query": (i32, [pdesc, ctypes.POINTER(PlanInfo)]),
         "vswin_block_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
         "vswin_window_msa_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
-        "vswin_attention_fwd": (i32, [pdesc, vp, vp, vp, vp, vp, vp]),
+        "vswin_attention_fwd": (i32, [pdesc, vp, vp, vp, vp, vp, vp, sz, vp]),
         "vswin_index_map": (i32, [pdesc, vp, vp, vp]),
         "vswin_partition_fwd": (i32, [pdesc, vp, vp, vp]),
         "vswin_reverse_fwd": (i32, [pdesc, vp, vp, vp, vp]),
@@ -159,7 +160,8 @@ def vswin_plan_query(desc: Desc, geometry_only: bool = False) -> dict:
     return dict(eff_window=tuple(p.eff_window), eff_shift=tuple(p.eff_shift), padded=tuple(p.padded),
                 tokens_per_window=p.tokens_per_window, num_windows=p.num_windows, tokens=p.tokens,
                 masked=bool(p.masked), fast_attention=bool(p.fast_attention),
-                workspace_bytes=p.workspace_bytes, msa_workspace_bytes=p.msa_workspace_bytes)
+                workspace_bytes=p.workspace_bytes, msa_workspace_bytes=p.msa_workspace_bytes,
+                attention_workspace_bytes=p.attention_workspace_bytes)
 
 
 def _desc_for(x: torch.Tensor, heads, window, shift, eps, flags, mlp_hidden) -> Desc:
@@ -216,14 +218,16 @@ def vswin_window_msa_fwd(x_norm: torch.Tensor, w: Dict[str, torch.Tensor], heads
 
 
 def vswin_attention_fwd(desc: Desc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                        table: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Attention core on projected windows: q/k/v (nW, heads, N, head_dim) ->
-    o (nW, N, C), heads concatenated."""
+                        table: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention core on projected windows in the block's internal layout (see
+    vswin_attention_fwd in include/vswin.h): o (nW, N, C), heads concatenated."""
     plan = vswin_plan_query(desc)
     o = out if out is not None else torch.empty((plan["num_windows"], plan["tokens_per_window"], desc.C),
                                                  dtype=q.dtype, device=q.device)
+    ws = _workspace(plan["attention_workspace_bytes"], q.device, workspace)
     _check(lib().vswin_attention_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(table), _ptr(o),
-                                     _stream(stream)))
+                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return o
 
 

@@ -29,9 +29,14 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# per-file extras: the attention kernel keeps MFMA operands/results in VGPRs
+# (no accumulation-register round trips between score tiles and VALU work)
+EXTRA = {"k_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -122,47 +122,66 @@ hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st) 
 // ---------------------------------------------------------------------------
 // MFMA kernel
 // ---------------------------------------------------------------------------
-constexpr int kQT = 4;            // query tiles per wave
+constexpr int kQT = 4;            // query tiles of 16 a wave carries at once
 constexpr int kWaves = 4;
 constexpr int kKLD = 40;          // K row pitch in LDS (elements): 80 bytes
 constexpr int kDummyLab = 0x7fff0000;
 constexpr int kNoQueryLab = 0x7ffe0000;
 
+int attention_table_stride(const RelTab& rel) { return (rel.rows + 3 * rel.R + 8 + 7) & ~7; }
+
+size_t attention_workspace_bytes(const RelTab& rel, int heads) {
+  return ((size_t)heads * attention_table_stride(rel) * 2 + 255) / 256 * 256 + ((size_t)heads * 4 + 255) / 256 * 256;
+}
+
+// Per head: fp16 table reversed and scaled by log2(e), followed by a -inf zone
+// of 3R + 8 entries; tmax[h] = log2(e) * max |T|.
+__global__ void __launch_bounds__(256) attn_prep_kernel(const bf16_t* __restrict__ table, _Float16* __restrict__ tab16,
+                                                        float* __restrict__ tmax, int rows, int heads, int stride) {
+  __shared__ float red[4];
+  const int h = blockIdx.x;
+  float m = 0.f;
+  for (int x = threadIdx.x; x < stride; x += 256) {
+    if (x < rows) {
+      const float t = bf2f(table[(int64_t)(rows - 1 - x) * heads + h]);
+      m = fmaxf(m, fabsf(t));
+      tab16[(int64_t)h * stride + x] = (_Float16)(t * kLog2e);
+    } else {
+      tab16[(int64_t)h * stride + x] = (_Float16)(-INFINITY);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) tmax[h] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) * kLog2e;
+}
+
 struct MfmaLaunch {
-  int NT;        // key tiles of 16 (slots padded to NT*16)
-  int VST;       // V^T row pitch (elements)
-  int QTT;       // query tiles of 16
-  int qsplit;    // workgroups per (window, head)
-  int tps;       // query tiles per workgroup
-  int tab_n;     // fp16 entries of table + -inf zone
-  size_t lds;    // dynamic LDS bytes
-  size_t off_vt, off_tab, off_kaddr, off_klab, off_red;
+  int NT;         // key tiles of 16 (slots padded to NT*16)
+  int NVS;        // V^T columns staged (NT rounded up to even, *16)
+  int VST;        // V^T row pitch in LDS (elements): (VST/2) mod 32 = 2*odd
+  int QTT;        // query tiles of 16
+  int tstride;    // fp16 table entries per head
+  size_t lds, off_vt, off_tab, off_kaddr, off_klab, off_red;
 };
 
 static MfmaLaunch mfma_launch(const AttnArgs& a) {
   MfmaLaunch L{};
   L.NT = (a.N + 15) / 16;
-  const int nt2 = (L.NT + 1) & ~1;
-  L.VST = nt2 * 16 + 4;          // (VST/2) mod 32 = 2 * odd: conflict-free 8-byte column reads
+  L.NVS = ((L.NT + 1) & ~1) * 16;
+  L.VST = L.NVS + 4;
   L.QTT = L.NT;
-  const int per_wg = kWaves * kQT;
-  int qs = (L.QTT + per_wg - 1) / per_wg;
-  if (const char* s = getenv("VSWIN_ATTN_QSPLIT")) {
-    const int v = atoi(s);
-    if (v >= qs && v <= L.QTT) qs = v;
-  }
-  L.qsplit = qs;
-  L.tps = (L.QTT + qs - 1) / qs;
-  L.tab_n = a.rel.rows + 3 * a.rel.R + 8;
+  L.tstride = attention_table_stride(a.rel);
   size_t off = (size_t)L.NT * 16 * kKLD * 2;
   L.off_vt = off;
   off += (size_t)32 * L.VST * 2;
+  off = (off + 15) & ~(size_t)15;
   L.off_tab = off;
-  off += ((size_t)L.tab_n * 2 + 15) & ~(size_t)15;
+  off += (size_t)L.tstride * 2;
   L.off_kaddr = off;
-  off += (size_t)L.NT * 4 * 4;
+  off += (size_t)(L.NT * 4 + 4) * 4;
   L.off_klab = off;
-  off += (size_t)L.NT * 4 * 4;
+  off += (size_t)(L.NT * 4 + 4) * 4;
   L.off_red = off;
   off += 16;
   L.lds = off;
@@ -187,95 +206,198 @@ bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
   return mfma_launch(a).lds <= 160 * 1024;
 }
 
-template <int MODE>   // 0: exp2(x)  1: row max only  2: exp2(x - rowmax)
-__device__ __forceinline__ void attn_pass(const bf16_t* __restrict__ Ks, const bf16_t* __restrict__ Vt,
+template <int QT>
+struct QState {
+  bf16x8_t q[QT];       // B operand: 8 head-dim values of this lane's query
+  int qaddr[QT];        // byte offset of the query's reversed-table base
+  int qlab[QT];         // region label of the query
+  float mrow[QT];       // row max (two-pass mode)
+  f32x4_t o0[QT], o1[QT], os[QT];   // O^T (d 0-15, d 16-31) and row sums
+};
+
+// One pair of key tiles (32 slots) for the QT query tiles of the wave, all in
+// one basic block so the tiles' MFMA, LDS and VALU work interleave.
+//   MODE 0: P = exp2(x); 1: track the row max of x; 2: P = exp2(x - max).
+//   SEL: per key group, point masked / dummy groups at the -inf zone.
+//   TAIL: the pair may end in dummy slots or lack its second tile.
+//   R2C: byte stride of one temporal offset in the table (0 = runtime R2).
+template <int MODE, bool SEL, bool TAIL, int QT, int R2C>
+__device__ __forceinline__ void attn_pair(int tp, int NT, const bf16_t* __restrict__ Ks,
+                                          const bf16_t* __restrict__ Vt, int VST,
                                           const unsigned char* __restrict__ tabb, const int* __restrict__ kaddr,
-                                          const int* __restrict__ klab, int NT, int N, int VST, int R2,
-                                          int zone, bool wmasked, float alpha, const bool vq[kQT],
-                                          const bf16x8_t qreg[kQT], const int qaddr[kQT], const int qlab[kQT],
-                                          float mrow[kQT], f32x4_t acc0[kQT], f32x4_t acc1[kQT],
-                                          f32x4_t accs[kQT]) {
+                                          const int* __restrict__ klab, int R2r, int zone, float alpha,
+                                          const bf16x8_t& ones, QState<QT>& st) {
+  const int R2 = R2C ? R2C : R2r;
   const int lane = threadIdx.x & 63;
   const int fr = lane & 15, g4 = lane >> 4;
-  bf16x8_t ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  for (int tp = 0; tp < NT; tp += 2) {
-    const bool hasB = tp + 1 < NT;
-    const bool sel = wmasked || (tp + 2) * 16 > N;
-    const bf16x8_t kA = *reinterpret_cast<const bf16x8_t*>(Ks + (16 * tp + fr) * kKLD + g4 * 8);
-    bf16x8_t kB;
-    if (hasB) kB = *reinterpret_cast<const bf16x8_t*>(Ks + (16 * tp + 16 + fr) * kKLD + g4 * 8);
-    else kB = bf16x8_t{};
-    const int gA = kaddr[4 * tp + g4];
-    const int gB = hasB ? kaddr[4 * tp + 4 + g4] : 0;
-    int lA = 0, lB = 0;
-    if (sel) {
-      lA = klab[4 * tp + g4];
-      lB = hasB ? klab[4 * tp + 4 + g4] : kDummyLab;
-    }
-    bf16x8_t vA0, vA1;
-    if (MODE != 1) {
-      const u32x2_t* p0 = reinterpret_cast<const u32x2_t*>(Vt + fr * VST + 16 * tp + 4 * g4);
-      const u32x2_t* p1 = reinterpret_cast<const u32x2_t*>(Vt + (fr + 16) * VST + 16 * tp + 4 * g4);
-      u32x4_t t0, t1;
-      const u32x2_t a0 = p0[0], b0 = p0[4], a1 = p1[0], b1 = p1[4];   // +16 slots = +32 bytes
-      t0[0] = a0[0]; t0[1] = a0[1]; t0[2] = b0[0]; t0[3] = b0[1];
-      t1[0] = a1[0]; t1[1] = a1[1]; t1[2] = b1[0]; t1[3] = b1[1];
-      vA0 = __builtin_bit_cast(bf16x8_t, t0);
-      vA1 = __builtin_bit_cast(bf16x8_t, t1);
-    }
+  const bool hasB = !TAIL || tp + 1 < NT;
+  const bf16x8_t kA = *reinterpret_cast<const bf16x8_t*>(Ks + (16 * tp + fr) * kKLD + g4 * 8);
+  bf16x8_t kB = bf16x8_t{};
+  if (hasB) kB = *reinterpret_cast<const bf16x8_t*>(Ks + (16 * tp + 16 + fr) * kKLD + g4 * 8);
+  const int gA = kaddr[4 * tp + g4];
+  const int gB = kaddr[4 * tp + 4 + g4];
+  int lA = 0, lB = 0;
+  if (SEL) {
+    lA = klab[4 * tp + g4];
+    lB = hasB ? klab[4 * tp + 4 + g4] : kDummyLab;
+  }
+  bf16x8_t vA0 = bf16x8_t{}, vA1 = bf16x8_t{};
+  if (MODE != 1) {
+    const u32x2_t* p0 = reinterpret_cast<const u32x2_t*>(Vt + fr * VST + 16 * tp + 4 * g4);
+    const u32x2_t* p1 = reinterpret_cast<const u32x2_t*>(Vt + (fr + 16) * VST + 16 * tp + 4 * g4);
+    const u32x2_t a0 = p0[0], b0 = p0[4], a1 = p1[0], b1 = p1[4];   // +16 slots = +32 bytes
+    u32x4_t t0, t1;
+    t0[0] = a0[0]; t0[1] = a0[1]; t0[2] = b0[0]; t0[3] = b0[1];
+    t1[0] = a1[0]; t1[1] = a1[1]; t1[2] = b1[0]; t1[3] = b1[1];
+    vA0 = __builtin_bit_cast(bf16x8_t, t0);
+    vA1 = __builtin_bit_cast(bf16x8_t, t1);
+  }
+  f32x4_t sA[QT], sB[QT];
 #pragma unroll
-    for (int u = 0; u < kQT; ++u) {
-      if (!vq[u]) continue;
-      const f32x4_t sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, qreg[u], zero4, 0, 0, 0);
-      f32x4_t sB = zero4;
-      if (hasB) sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, qreg[u], zero4, 0, 0, 0);
-      int adA = qaddr[u] + gA, adB = qaddr[u] + gB;
-      if (sel) {
-        adA = (lA == qlab[u]) ? adA : zone;
-        adB = (lB == qlab[u]) ? adB : zone;
-      }
-      float xA[4], xB[4];
+  for (int u = 0; u < QT; ++u) {
+    sA[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, st.q[u], zero4, 0, 0, 0);
+    sB[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, st.q[u], zero4, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    int adA = st.qaddr[u] + gA, adB = st.qaddr[u] + gB;
+    if (SEL) {
+      adA = (lA == st.qlab[u]) ? adA : zone;
+      adB = (lB == st.qlab[u]) ? adB : zone;
+    }
+    float xA[4], xB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xA[i] = __builtin_fmaf(sA[u][i], alpha, (float)*reinterpret_cast<const _Float16*>(tabb + adA + i * R2));
+      xB[i] = __builtin_fmaf(sB[u][i], alpha, (float)*reinterpret_cast<const _Float16*>(tabb + adB + i * R2));
+    }
+    if (MODE == 1) {
+      float m = st.mrow[u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(xA[i], xB[i]));
+      st.mrow[u] = m;
+    } else {
+      float pA[4], pB[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float bA = (float)*reinterpret_cast<const _Float16*>(tabb + adA + i * R2);
-        const float bB = (float)*reinterpret_cast<const _Float16*>(tabb + adB + i * R2);
-        xA[i] = __builtin_fmaf(sA[i], alpha, bA);
-        xB[i] = __builtin_fmaf(sB[i], alpha, bB);
+        pA[i] = __builtin_amdgcn_exp2f(MODE == 2 ? xA[i] - st.mrow[u] : xA[i]);
+        pB[i] = __builtin_amdgcn_exp2f(MODE == 2 ? xB[i] - st.mrow[u] : xB[i]);
       }
-      if (MODE == 1) {
-        float m = mrow[u];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(xA[i], xB[i]));
-        mrow[u] = m;
-      } else {
-        float pA[4], pB[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (MODE == 2) {
-            pA[i] = __builtin_amdgcn_exp2f(xA[i] - mrow[u]);
-            pB[i] = __builtin_amdgcn_exp2f(xB[i] - mrow[u]);
-          } else {
-            pA[i] = __builtin_amdgcn_exp2f(xA[i]);
-            pB[i] = __builtin_amdgcn_exp2f(xB[i]);
-          }
-        }
-        u32x4_t pk;
-        pk[0] = pack_bf16x2(pA[0], pA[1]);
-        pk[1] = pack_bf16x2(pA[2], pA[3]);
-        pk[2] = pack_bf16x2(pB[0], pB[1]);
-        pk[3] = pack_bf16x2(pB[2], pB[3]);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
-        acc0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA0, pb, acc0[u], 0, 0, 0);
-        acc1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA1, pb, acc1[u], 0, 0, 0);
-        accs[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, accs[u], 0, 0, 0);
-      }
+      u32x4_t pk;
+      pk[0] = pack_bf16x2(pA[0], pA[1]);
+      pk[1] = pack_bf16x2(pA[2], pA[3]);
+      pk[2] = pack_bf16x2(pB[0], pB[1]);
+      pk[3] = pack_bf16x2(pB[2], pB[3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+      st.o0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA0, pb, st.o0[u], 0, 0, 0);
+      st.o1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA1, pb, st.o1[u], 0, 0, 0);
+      st.os[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, st.os[u], 0, 0, 0);
     }
   }
 }
 
+struct AttnCtx {
+  const bf16_t* Ks;
+  const bf16_t* Vt;
+  const unsigned char* tabb;
+  const int* kaddr;
+  const int* klab;
+  int N, NT, VST, R2, zone;
+  float alpha;
+};
+
+template <int MODE, bool MASKED, int QT, int R2C>
+__device__ __forceinline__ void attn_pass(const AttnCtx& c, const bf16x8_t& ones, QState<QT>& st) {
+  const int nclean = c.N / 32;   // pairs whose 32 slots are all real keys
+  for (int pi = 0; pi < nclean; ++pi)
+    attn_pair<MODE, MASKED, false, QT, R2C>(2 * pi, c.NT, c.Ks, c.Vt, c.VST, c.tabb, c.kaddr, c.klab, c.R2,
+                                            c.zone, c.alpha, ones, st);
+  if (2 * nclean < c.NT)
+    attn_pair<MODE, true, true, QT, R2C>(2 * nclean, c.NT, c.Ks, c.Vt, c.VST, c.tabb, c.kaddr, c.klab, c.R2,
+                                         c.zone, c.alpha, ones, st);
+}
+
+// Process query tiles j0, j0 + step, ... (QT of them) of one wave.
+template <int QT, int R2C>
+__device__ __forceinline__ void attn_tiles(const AttnArgs& a, const AttnCtx& c, int j0, int step, int64_t w, int h,
+                                           int rt0, int rh0, int rw0, float kmax, float tmx, bool wmasked,
+                                           const bf16_t* Qg, bf16_t* Og) {
+  const int lane = threadIdx.x & 63;
+  const int fr = lane & 15, g4 = lane >> 4;
+  const WinGeo& g = a.geo;
+  const int mhw = g.Mh * g.Mw;
+  const int R = a.rel.R, Rw = a.rel.Rw;
+  const int cq = a.rel.rows - 1 - a.rel.centre;
+  QState<QT> st;
+  bool need_max = false;
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int qs = 16 * (j0 + step * u) + fr;
+    const bool valid = qs < c.N;
+    u32x4_t qv = {0u, 0u, 0u, 0u};
+    int fq = 0;
+    st.qlab[u] = kNoQueryLab;
+    if (valid) {
+      qv = *reinterpret_cast<const u32x4_t*>(Qg + qs * 32 + g4 * 8);
+      const int m = qs >> 2, i = qs & 3;
+      const int aa = m / mhw, r2 = m - aa * mhw, kh = r2 / g.Mw, kw = r2 - kh * g.Mw;
+      fq = (4 * aa + i) * R + kh * Rw + kw;
+      st.qlab[u] = slot_label_at(g, rt0 + 4 * aa + i, rh0 + kh, rw0 + kw);
+    }
+    st.q[u] = __builtin_bit_cast(bf16x8_t, qv);
+    st.qaddr[u] = 2 * (cq - fq);
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bflo(qv[e]), hi = bfhi(qv[e]);
+      sq += lo * lo + hi * hi;
+    }
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    need_max |= valid && !(c.alpha * sqrtf(sq) * kmax + tmx <= 90.f);
+    st.mrow[u] = -INFINITY;
+    st.o0[u] = st.o1[u] = st.os[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  const bool wave_max = a.force_max || __ballot(need_max) != 0;
+  if (wave_max) {
+    if (wmasked) attn_pass<1, true, QT, R2C>(c, ones, st);
+    else attn_pass<1, false, QT, R2C>(c, ones, st);
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      float m = st.mrow[u];
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      st.mrow[u] = (m == -INFINITY) ? 0.f : m;
+    }
+    if (wmasked) attn_pass<2, true, QT, R2C>(c, ones, st);
+    else attn_pass<2, false, QT, R2C>(c, ones, st);
+  } else {
+    if (wmasked) attn_pass<0, true, QT, R2C>(c, ones, st);
+    else attn_pass<0, false, QT, R2C>(c, ones, st);
+  }
+  // normalise and write O^T fragments (rows in slot order)
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int qs = 16 * (j0 + step * u) + fr;
+    if (qs >= c.N) continue;
+    const float inv = 1.0f / st.os[u][0];
+    float o0[4], o1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o0[i] = st.o0[u][i] * inv; o1[i] = st.o1[u][i] * inv; }
+    const int64_t base = (w * c.N + qs) * (int64_t)a.C + h * 32;
+    store4(Og, base + 4 * g4, o0);
+    store4(Og, base + 16 + 4 * g4, o1);
+  }
+}
+
+// One workgroup per (window, head).  Inputs (slot order, see slot_to_natural):
+// q, k (item, N, 32); v transposed (item, 32, N); tab16 / tmax from the prep
+// kernel.  Output rows of o in slot order.  R2C: compile-time table stride.
+template <int R2C>
 __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnArgs a, const MfmaLaunch L, const float alpha) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
@@ -285,15 +407,13 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnArgs a, const 
   int* klab = reinterpret_cast<int*>(smem + L.off_klab);
   int* red = reinterpret_cast<int*>(smem + L.off_red);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int fr = lane & 15, g4 = lane >> 4;
-  // XCD-aware order: consecutive logical blocks (the query splits of one
-  // window-head, then neighbouring heads) land on the same XCD and L2.
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-aware order: consecutive logical blocks (neighbouring heads of one
+  // window, then neighbouring windows) land on the same XCD.
   const int64_t nblk = gridDim.x;
-  int64_t bid = blockIdx.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int64_t item = bid / L.qsplit;
-  const int split = (int)(bid - item * L.qsplit);
+  int64_t item = blockIdx.x;
+  if ((nblk & 7) == 0) item = (item & 7) * (nblk >> 3) + (item >> 3);
   const int64_t w = item / a.heads;
   const int h = (int)(item - w * a.heads);
   const WinGeo& g = a.geo;
@@ -306,66 +426,73 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnArgs a, const 
   const bf16_t* Qg = reinterpret_cast<const bf16_t*>(a.q) + item * N * 32;
   const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + item * N * 32;
   const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + item * N * 32;
-  const bf16_t* Tg = reinterpret_cast<const bf16_t*>(a.table);
-  const int rows = a.rel.rows, R = a.rel.R, Rw = a.rel.Rw;
+  const _Float16* Tg = reinterpret_cast<const _Float16*>(a.tab16) + (int64_t)h * L.tstride;
+  const int R = a.rel.R, Rw = a.rel.Rw;
 
   if (tid < 4) red[tid] = 0;
   __syncthreads();
 
-  // ---- stage the head's table: reversed, * log2(e), fp16; then -inf zone
-  float tmax = 0.f;
-  for (int x = tid; x < L.tab_n; x += 256) {
-    if (x < rows) {
-      const float t = bf2f(Tg[(int64_t)(rows - 1 - x) * a.heads + h]);
-      tmax = fmaxf(tmax, fabsf(t));
-      tab[x] = (_Float16)(t * kLog2e);
-    } else {
-      tab[x] = (_Float16)(-INFINITY);
+  // ---- stage: table (16-byte copies), K rows, V^T rows, key-group info.
+  // Loads are issued in batches before their LDS stores so that each thread
+  // has several global requests in flight.
+  for (int c0 = 0; c0 < L.tstride / 8; c0 += 256 * 4) {
+    u32x4_t buf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + tid + 256 * i;
+      if (c < L.tstride / 8) buf[i] = reinterpret_cast<const u32x4_t*>(Tg)[c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + tid + 256 * i;
+      if (c < L.tstride / 8) reinterpret_cast<u32x4_t*>(tab)[c] = buf[i];
     }
   }
-  // ---- K rows in slot order (slot k = 4m + i -> token (kt = 4a+i, kh, kw))
   float kmax2 = 0.f;
-  for (int c = tid; c < L.NT * 64; c += 256) {
-    const int kap = c >> 2, ch = c & 3;
-    u32x4_t val = {0u, 0u, 0u, 0u};
-    float sq = 0.f;
-    if (kap < N) {
-      const int m = kap >> 2, i = kap & 3;
-      const int aa = m / mhw, r2 = m - aa * mhw, kh = r2 / g.Mw, kw = r2 - kh * g.Mw;
-      const int n = ((4 * aa + i) * g.Mh + kh) * g.Mw + kw;
-      val = *reinterpret_cast<const u32x4_t*>(Kg + n * 32 + ch * 8);
+  for (int c0 = 0; c0 < L.NT * 64; c0 += 256 * 8) {
+    u32x4_t buf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = c0 + tid + 256 * i;
+      buf[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if ((c >> 2) < N) buf[i] = *reinterpret_cast<const u32x4_t*>(Kg + (c >> 2) * 32 + (c & 3) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = c0 + tid + 256 * i;
+      if (c0 + 256 * i >= L.NT * 64) break;      // depends on the batch index only: wave uniform
+      float sq = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = bflo(val[e]), hi = bfhi(val[e]);
+        const float lo = bflo(buf[i][e]), hi = bfhi(buf[i][e]);
         sq += lo * lo + hi * hi;
       }
+      if (c < L.NT * 64) *reinterpret_cast<u32x4_t*>(Ks + (c >> 2) * kKLD + (c & 3) * 8) = buf[i];
+      sq += __shfl_xor(sq, 1);
+      sq += __shfl_xor(sq, 2);
+      kmax2 = fmaxf(kmax2, sq);
     }
-    *reinterpret_cast<u32x4_t*>(Ks + kap * kKLD + ch * 8) = val;
-    sq += __shfl_xor(sq, 1);
-    sq += __shfl_xor(sq, 2);
-    kmax2 = fmaxf(kmax2, sq);
   }
-  // ---- V^T in slot order, zero beyond N
-  const int nslot_v = ((L.NT + 1) & ~1) * 16;
-  for (int c = tid; c < nslot_v * 4; c += 256) {
-    const int kap = c >> 2, ch = c & 3;
-    u32x4_t val = {0u, 0u, 0u, 0u};
-    if (kap < N) {
-      const int m = kap >> 2, i = kap & 3;
-      const int aa = m / mhw, r2 = m - aa * mhw, kh = r2 / g.Mw, kw = r2 - kh * g.Mw;
-      const int n = ((4 * aa + i) * g.Mh + kh) * g.Mw + kw;
-      val = *reinterpret_cast<const u32x4_t*>(Vg + n * 32 + ch * 8);
+  const int c4 = L.NVS / 4;
+  for (int c0 = 0; c0 < 32 * c4; c0 += 256 * 16) {
+    u32x2_t buf[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = c0 + tid + 256 * i;
+      const int d = c / c4, k4 = (c - d * c4) * 4;
+      buf[i] = u32x2_t{0u, 0u};
+      if (c < 32 * c4 && k4 < N) buf[i] = *reinterpret_cast<const u32x2_t*>(Vg + d * N + k4);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Vt[(ch * 8 + 2 * e) * L.VST + kap] = (bf16_t)(val[e] & 0xffffu);
-      Vt[(ch * 8 + 2 * e + 1) * L.VST + kap] = (bf16_t)(val[e] >> 16);
+    for (int i = 0; i < 16; ++i) {
+      const int c = c0 + tid + 256 * i;
+      const int d = c / c4, k4 = (c - d * c4) * 4;
+      if (c < 32 * c4) *reinterpret_cast<u32x2_t*>(Vt + d * L.VST + k4) = buf[i];
     }
   }
-  // ---- key groups: table byte offset of the group's first key, region label
-  const int lab0 = slot_label_at(g, rt0, rh0, rw0);
   int anymask = 0;
-  for (int m = tid; m < L.NT * 4; m += 256) {
+  const int lab0 = slot_label_at(g, rt0, rh0, rw0);
+  for (int m = tid; m < L.NT * 4 + 4; m += 256) {
     if (m < N / 4) {
       const int aa = m / mhw, r2 = m - aa * mhw, kh = r2 / g.Mw, kw = r2 - kh * g.Mw;
       kaddr[m] = 2 * (4 * aa * R + kh * Rw + kw);
@@ -378,88 +505,28 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnArgs a, const 
     }
   }
   atomicMax(&red[0], __float_as_int(kmax2));
-  atomicMax(&red[1], __float_as_int(tmax));
-  if (anymask) atomicOr(&red[2], 1);
+  if (anymask) atomicOr(&red[1], 1);
   __syncthreads();
   const float kmax = sqrtf(__int_as_float(red[0]));
-  const float tmx = __int_as_float(red[1]);
-  const bool wmasked = a.use_mask && red[2] != 0;
-
-  // ---- this wave's query tiles
-  const int j0 = split * L.tps;
-  const int j1 = min(L.QTT, j0 + L.tps);
-  bool vq[kQT];
-  bf16x8_t qreg[kQT];
-  int qaddr[kQT], qlab[kQT];
-  float mrow[kQT];
-  f32x4_t acc0[kQT], acc1[kQT], accs[kQT];
-  bool need_max = false;
-  const int zone = 2 * rows;
-  const int cq = rows - 1 - a.rel.centre;
-#pragma unroll
-  for (int u = 0; u < kQT; ++u) {
-    const int j = j0 + wv + kWaves * u;
-    vq[u] = j < j1;
-    const int qn = 16 * j + fr;
-    const bool valid = vq[u] && qn < N;
-    u32x4_t qv = {0u, 0u, 0u, 0u};
-    int fq = 0;
-    qlab[u] = kNoQueryLab;
-    if (valid) {
-      qv = *reinterpret_cast<const u32x4_t*>(Qg + qn * 32 + g4 * 8);
-      const int pt = qn / mhw, r2 = qn - pt * mhw, ph = r2 / g.Mw, pw = r2 - ph * g.Mw;
-      fq = pt * R + ph * Rw + pw;
-      qlab[u] = slot_label_at(g, rt0 + pt, rh0 + ph, rw0 + pw);
-    }
-    qreg[u] = __builtin_bit_cast(bf16x8_t, qv);
-    qaddr[u] = 2 * (cq - fq);
-    float sq = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bflo(qv[e]), hi = bfhi(qv[e]);
-      sq += lo * lo + hi * hi;
-    }
-    sq += __shfl_xor(sq, 16);
-    sq += __shfl_xor(sq, 32);
-    const float bound = alpha * sqrtf(sq) * kmax + kLog2e * tmx;
-    need_max |= valid && !(bound <= 90.f);
-    mrow[u] = -INFINITY;
-    acc0[u] = acc1[u] = accs[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  const bool wave_max = a.force_max || __ballot(need_max) != 0;
-  const unsigned char* tabb = reinterpret_cast<const unsigned char*>(tab);
-  const int R2 = 2 * R;
-  if (!wave_max) {
-    attn_pass<0>(Ks, Vt, tabb, kaddr, klab, L.NT, N, L.VST, R2, zone, wmasked, alpha, vq, qreg, qaddr, qlab,
-                 mrow, acc0, acc1, accs);
-  } else {
-    attn_pass<1>(Ks, Vt, tabb, kaddr, klab, L.NT, N, L.VST, R2, zone, wmasked, alpha, vq, qreg, qaddr, qlab,
-                 mrow, acc0, acc1, accs);
-#pragma unroll
-    for (int u = 0; u < kQT; ++u) {
-      float m = mrow[u];
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      mrow[u] = (m == -INFINITY) ? 0.f : m;
-    }
-    attn_pass<2>(Ks, Vt, tabb, kaddr, klab, L.NT, N, L.VST, R2, zone, wmasked, alpha, vq, qreg, qaddr, qlab,
-                 mrow, acc0, acc1, accs);
-  }
-
-  // ---- normalise and write O (window order, head h at columns h*32)
+  const float tmx = a.tmax[h];
+  const bool wmasked = a.use_mask && red[1] != 0;
+  AttnCtx c;
+  c.Ks = Ks; c.Vt = Vt; c.tabb = reinterpret_cast<const unsigned char*>(tab);
+  c.kaddr = kaddr; c.klab = klab;
+  c.N = N; c.NT = L.NT; c.VST = L.VST; c.R2 = 2 * R; c.zone = 2 * a.rel.rows; c.alpha = alpha;
   bf16_t* Og = reinterpret_cast<bf16_t*>(a.o);
-#pragma unroll
-  for (int u = 0; u < kQT; ++u) {
-    if (!vq[u]) continue;
-    const int qn = 16 * (j0 + wv + kWaves * u) + fr;
-    if (qn >= N) continue;
-    const float inv = 1.0f / accs[u][0];
-    float o0[4], o1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { o0[i] = acc0[u][i] * inv; o1[i] = acc1[u][i] * inv; }
-    const int64_t base = (w * N + qn) * (int64_t)a.C + h * 32;
-    store4(Og, base + 4 * g4, o0);
-    store4(Og, base + 16 + 4 * g4, o1);
+
+  // ---- query tiles wv, wv + 4, wv + 8, ... in chunks of at most 4
+  const int mine = (L.QTT - wv + kWaves - 1) / kWaves;
+  for (int u0 = 0; u0 < mine; u0 += kQT) {
+    const int n = min(kQT, mine - u0);
+    const int j0 = wv + kWaves * u0;
+    switch (n) {
+      case 4: attn_tiles<4, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
+      case 3: attn_tiles<3, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
+      case 2: attn_tiles<2, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
+      default: attn_tiles<1, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
+    }
   }
 }
 
@@ -469,15 +536,22 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
   const MfmaLaunch L = mfma_launch(a);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipFuncSetAttribute((const void*)attn_mfma_kernel<338>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipFuncSetAttribute((const void*)attn_mfma_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
+  hipLaunchKernelGGL(attn_prep_kernel, dim3(a.heads), dim3(256), 0, st, (const bf16_t*)a.table,
+                     (_Float16*)a.tab16, (float*)a.tmax, a.rel.rows, a.heads, L.tstride);
   const float alpha = kLog2e / sqrtf((float)a.d);
   AttnArgs ak = a;
   // VSWIN_ATTN_MAXPASS=1 makes every wave take the exact row-max pass (test
   // hook for the path that otherwise runs only for very large logits).
   if (const char* f = getenv("VSWIN_ATTN_MAXPASS")) ak.force_max = atoi(f) != 0;
-  hipLaunchKernelGGL(attn_mfma_kernel, dim3((unsigned)(items * L.qsplit)), dim3(256), L.lds, st, ak, L, alpha);
+  // the (8,7,7) window's table (R = 13 * 13) gets compile-time read offsets
+  if (2 * a.rel.R == 338)
+    hipLaunchKernelGGL(attn_mfma_kernel<338>, dim3((unsigned)items), dim3(256), L.lds, st, ak, L, alpha);
+  else
+    hipLaunchKernelGGL(attn_mfma_kernel<0>, dim3((unsigned)items), dim3(256), L.lds, st, ak, L, alpha);
   return hipGetLastError();
 }
 

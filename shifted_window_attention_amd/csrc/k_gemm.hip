@@ -12,6 +12,8 @@
 // workload; throughput is not its purpose).
 #include "vswin_kernels.h"
 
+#include <type_traits>
+
 namespace vswin {
 
 __device__ __forceinline__ float gelu_erf(float x) {
@@ -22,6 +24,25 @@ __device__ __forceinline__ float gelu_erf(float x) {
 template <typename T, Epi KIND>
 struct EpiDev {
   EpiArgs a;
+  // block computes token-major fragments (V^T output of the qkv projection)
+  __device__ __forceinline__ bool swapped(int n0) const {
+    if constexpr (KIND == Epi::kQKV) return a.vt && n0 >= 2 * a.C;
+    else return false;
+  }
+  // four consecutive window rows m4..m4+3 (same window) of feature n
+  __device__ __forceinline__ void store_t(int64_t m4, int n, float v[4]) const {
+    if constexpr (KIND == Epi::kQKV) {
+      const float b = a.bias ? Elem<T>::load((const T*)a.bias, n) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += b;
+      const int c = n - 2 * a.C;
+      const int h = c / a.d;
+      const int e = c - h * a.d;
+      const int64_t w = m4 / a.N;
+      const int t = (int)(m4 - w * a.N);
+      store4((T*)a.out3, ((w * a.heads + h) * a.d + e) * (int64_t)a.N + t, v);
+    }
+  }
   __device__ __forceinline__ int64_t row_ctx(int64_t m) const {
     if constexpr (KIND == Epi::kProjRes || KIND == Epi::kProjOut) {
       int lab;
@@ -138,41 +159,63 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict
   };
 
   const int nk = K / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    bf16x8_t af[MT], wf[NT];
+  auto mainloop = [&](auto swap_tag) {
+    constexpr bool SWAP = decltype(swap_tag)::value;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      bf16x8_t af[MT], wf[NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(wm * 64 + mt * 16 + fr) * kLDK + fk]);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      wf[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][(wn * WN + nt * 16 + fr) * kLDK + fk]);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
+        af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(wm * 64 + mt * 16 + fr) * kLDK + fk]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], af[mt], acc[mt][nt], 0, 0, 0);
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
+        wf[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][(wn * WN + nt * 16 + fr) * kLDK + fk]);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t m = m0 + wm * 64 + mt * 16 + fr;
-    if (m >= M) continue;
-    const int64_t rc = epi.row_ctx(m);
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = n0 + wn * WN + nt * 16 + (lane >> 4) * 4;
-      float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
-      epi.store(m, rc, n, v);
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (SWAP)   // rows = tokens, cols = features
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], wf[nt], acc[mt][nt], 0, 0, 0);
+          else                  // rows = features, cols = tokens
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], af[mt], acc[mt][nt], 0, 0, 0);
+        }
+      if (kt + 1 < nk) sstore(buf ^ 1);
+      __syncthreads();
     }
-  }
+    if constexpr (SWAP) {
+      // lane: feature column fr, tokens 4*(lane>>4) .. +3 of each 16-row tile
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m4 = m0 + wm * 64 + mt * 16 + (lane >> 4) * 4;
+        if (m4 >= M) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+          epi.store_t(m4, n0 + wn * WN + nt * 16 + fr, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = m0 + wm * 64 + mt * 16 + fr;
+        if (m >= M) continue;
+        const int64_t rc = epi.row_ctx(m);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = n0 + wn * WN + nt * 16 + (lane >> 4) * 4;
+          float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+          epi.store(m, rc, n, v);
+        }
+      }
+    }
+  };
+  if (epi.swapped(n0)) mainloop(std::true_type{});
+  else mainloop(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -234,9 +277,11 @@ static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int6
       const int64_t blocks = mb * (N / bn);
       kern<<<dim3((unsigned)blocks), dim3(256), 0, st>>>((const bf16_t*)A, (const bf16_t*)W, M, N, K, epi);
     };
-    if (N % 128 == 0) go(gemm_bf16_kernel<128, EpiDev<bf16_t, KIND>>, 128);
-    else if (N % 96 == 0) go(gemm_bf16_kernel<96, EpiDev<bf16_t, KIND>>, 96);
-    else if (N % 64 == 0) go(gemm_bf16_kernel<64, EpiDev<bf16_t, KIND>>, 64);
+    // the qkv projection needs every feature tile inside one of q, k, v
+    const int F = KIND == Epi::kQKV ? e.C : N;
+    if (N % 128 == 0 && F % 128 == 0) go(gemm_bf16_kernel<128, EpiDev<bf16_t, KIND>>, 128);
+    else if (N % 96 == 0 && F % 96 == 0) go(gemm_bf16_kernel<96, EpiDev<bf16_t, KIND>>, 96);
+    else if (N % 64 == 0 && F % 64 == 0) go(gemm_bf16_kernel<64, EpiDev<bf16_t, KIND>>, 64);
     else go(gemm_bf16_kernel<32, EpiDev<bf16_t, KIND>>, 32);
   } else {
     EpiDev<float, KIND> epi{e};

@@ -49,12 +49,16 @@ struct Plan {
   bool fast;
   vswin_dtype dt;
   // workspace offsets (bytes)
-  size_t off_xw, off_q, off_k, off_v, off_zh, off_h, ws_block, ws_msa;
+  size_t off_xw, off_q, off_k, off_v, off_tab, off_zh, off_h, ws_block, ws_msa, ws_attn;
 };
 
 AttnArgs attn_args(const Plan& p, const void* q, const void* k, const void* v, const void* table, void* o,
-                   uint32_t flags) {
+                   uint32_t flags, char* scratch = nullptr) {
   AttnArgs a{};
+  if (scratch) {
+    a.tab16 = scratch;
+    a.tmax = (float*)(scratch + (p.ws_attn - align256((size_t)p.heads * 4)));
+  }
   a.q = q; a.k = k; a.v = v; a.table = table; a.o = o;
   a.nW = p.nW; a.heads = p.heads; a.d = p.d; a.C = p.C; a.N = p.N;
   a.rel = p.rel; a.geo = p.geo;
@@ -127,14 +131,17 @@ vswin_status make_plan(const vswin_desc* d, Plan& p, bool compute = true) {
   const bool has_pad = pad[0] != d->T || pad[1] != d->H || pad[2] != d->W;
   p.use_mask = shifted || (has_pad && !g.pad_visible);
   p.fast = attention_mfma_supported(p.dt, attn_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, d->flags));
+  g.slot_perm = p.fast ? 1 : 0;     // window rows in the MFMA kernel's slot order
   const size_t es = elem_size(d->dtype);
   const size_t act = align256((size_t)p.Lp * p.C * es);
+  p.ws_attn = p.fast ? attention_workspace_bytes(p.rel, p.heads) : 0;
   p.off_xw = 0;
   p.off_q = act;
   p.off_k = 2 * act;
   p.off_v = 3 * act;
-  p.ws_msa = 4 * act;
-  p.off_zh = 4 * act;
+  p.off_tab = 4 * act;
+  p.ws_msa = 4 * act + p.ws_attn;
+  p.off_zh = p.ws_msa;
   p.off_h = p.off_zh + align256((size_t)p.L * p.C * 4);
   p.ws_block = p.off_h + align256((size_t)p.L * p.hid * es);
   return VSWIN_OK;
@@ -180,8 +187,9 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
   e.bias = w->qkv_b;
   e.out = q; e.out2 = k; e.out3 = v;
   e.C = p.C; e.heads = p.heads; e.d = p.d; e.N = p.N; e.geo = p.geo;
+  e.vt = p.fast ? 1 : 0;
   HIPCHECK(gemm(p.dt, xw, w->qkv_w, p.Lp, 3 * p.C, p.C, e, st), "qkv gemm");
-  const AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags);
+  const AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags, ws + p.off_tab);
   if (p.fast) HIPCHECK(attention_mfma(a, st), "attention (mfma)");
   else HIPCHECK(attention_generic(p.dt, a, st), "attention (generic)");
   EpiArgs e2{};
@@ -226,6 +234,7 @@ vswin_status vswin_plan_query(const vswin_desc* desc, vswin_plan* plan) {
   plan->fast_attention = p.fast ? 1 : 0;
   plan->workspace_bytes = p.ws_block;
   plan->msa_workspace_bytes = p.ws_msa;
+  plan->attention_workspace_bytes = p.ws_attn;
   // geometry is filled in; now the constraints of the compute entry points
   Plan q{};
   return make_plan(desc, q, true);
@@ -304,10 +313,13 @@ vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm, co
 }
 
 vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const void* k, const void* v,
-                                 const void* rpb_table, void* o, void* stream) {
+                                 const void* rpb_table, void* o, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   Plan p{};
   CHECK(make_plan(desc, p));
   if (p.Lp == 0) return VSWIN_OK;
+  if (p.ws_attn && (!workspace || !aligned(workspace, 256) || workspace_bytes < p.ws_attn))
+    return fail(VSWIN_ERR_WORKSPACE, "attention needs %zu workspace bytes", p.ws_attn);
   CHECK(check_ptr(q, "q"));
   CHECK(check_ptr(k, "k"));
   CHECK(check_ptr(v, "v"));
@@ -315,7 +327,7 @@ vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const vo
   CHECK(check_ptr(o, "o"));
   if (p.Lp == 0) return VSWIN_OK;
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
-  const AttnArgs a = attn_args(p, q, k, v, rpb_table, o, desc->flags);
+  const AttnArgs a = attn_args(p, q, k, v, rpb_table, o, desc->flags, (char*)workspace);
   if (p.fast) HIPCHECK(attention_mfma(a, (hipStream_t)stream), "attention (mfma)");
   else HIPCHECK(attention_generic(p.dt, a, (hipStream_t)stream), "attention (generic)");
   return VSWIN_OK;
@@ -327,7 +339,9 @@ vswin_status vswin_index_map(const vswin_desc* desc, int32_t* map, uint8_t* regi
   if (p.Lp == 0) return VSWIN_OK;
   if (!map) return fail(VSWIN_ERR_INVALID_ARG, "map is NULL");
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
-  HIPCHECK(index_map(map, region, p.Lp, p.geo, (hipStream_t)stream), "index map");
+  WinGeo g = p.geo;
+  g.slot_perm = 0;   // the export reports natural (pt, ph, pw) order
+  HIPCHECK(index_map(map, region, p.Lp, g, (hipStream_t)stream), "index map");
   return VSWIN_OK;
 }
 
@@ -339,7 +353,9 @@ vswin_status vswin_partition_fwd(const vswin_desc* desc, const void* x, void* wi
   CHECK(check_ptr(windows, "windows"));
   if (p.Lp == 0) return VSWIN_OK;
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
-  HIPCHECK(ln_gather(p.dt, x, nullptr, nullptr, windows, p.Lp, p.C, desc->ln_eps, p.geo, 0, (hipStream_t)stream),
+  WinGeo g = p.geo;
+  g.slot_perm = 0;
+  HIPCHECK(ln_gather(p.dt, x, nullptr, nullptr, windows, p.Lp, p.C, desc->ln_eps, g, 0, (hipStream_t)stream),
            "partition");
   return VSWIN_OK;
 }
@@ -354,7 +370,9 @@ vswin_status vswin_reverse_fwd(const vswin_desc* desc, const void* windows, cons
   CHECK(check_ptr(y, "y"));
   if (p.Lp == 0) return VSWIN_OK;
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
-  HIPCHECK(reverse_scatter(p.dt, windows, residual, y, p.Lp, p.C, p.geo, (hipStream_t)stream), "reverse");
+  WinGeo g = p.geo;
+  g.slot_perm = 0;
+  HIPCHECK(reverse_scatter(p.dt, windows, residual, y, p.Lp, p.C, g, (hipStream_t)stream), "reverse");
   return VSWIN_OK;
 }
 

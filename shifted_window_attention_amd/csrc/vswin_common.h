@@ -26,7 +26,21 @@ struct WinGeo {
   int N;              // tokens per window
   int nws;            // windows per clip
   int pad_visible;    // pads keep their positional label
+  int slot_perm;      // window rows in attention slot order (see slot_to_natural)
 };
+
+// Order of the rows of one window inside the block's buffers.  Natural order
+// is (pt, ph, pw) row-major.  The MFMA attention path (P % 4 == 0) stores
+// slot k = 4 m + i for the token (pt = 4 a + i, ph, pw) with m = (a, ph, pw)
+// row-major: four consecutive slots differ only in their temporal coordinate,
+// so their relative-position rows are r, r + R, r + 2R, r + 3R.
+__host__ __device__ inline int slot_to_natural(const WinGeo& g, int k) {
+  if (!g.slot_perm) return k;
+  const int m = k >> 2, i = k & 3;
+  const int mhw = g.Mh * g.Mw;
+  const int a = m / mhw;
+  return (4 * a + i) * mhw + (m - a * mhw);
+}
 
 // Region label of one axis (rolled position r, padded length n, window w,
 // shift s): slices [0, n-w), [n-w, n-s), [n-s, n) of the rolled grid.
@@ -38,7 +52,8 @@ constexpr int kPadLabel = 255;
 
 // Source token (flat b,t,h,w) of window slot (w, n), or -1 for a pad slot;
 // `label` receives the slot's region label.
-__host__ __device__ inline int64_t slot_source(const WinGeo& g, int64_t w, int n, int& label) {
+__host__ __device__ inline int64_t slot_source(const WinGeo& g, int64_t w, int slot, int& label) {
+  const int n = slot_to_natural(g, slot);
   const int b = (int)(w / g.nws);
   const int wr = (int)(w - (int64_t)b * g.nws);
   const int wpl = g.nwh * g.nww;

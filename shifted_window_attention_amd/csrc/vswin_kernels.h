@@ -35,6 +35,7 @@ struct EpiArgs {
   // kQKV / kProj*: geometry
   int C, heads, d, N;
   WinGeo geo;
+  int vt;             // kQKV: write v transposed (item, d, N) (MFMA attention layout)
 };
 
 hipError_t gemm(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K, const EpiArgs& e,
@@ -42,7 +43,7 @@ hipError_t gemm(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, 
 
 // --- attention (k_attention.hip) ------------------------------------------
 struct AttnArgs {
-  const void *q, *k, *v;   // (nW, heads, N, d) of dtype
+  const void *q, *k, *v;   // (nW, heads, N, d) of dtype; MFMA path: v is (nW, heads, d, N)
   const void* table;       // (rows, heads) of dtype
   void* o;                 // (nW, N, C) of dtype
   int64_t nW;
@@ -52,7 +53,11 @@ struct AttnArgs {
   int use_mask;            // some window may need the region mask
   int mask_m100;           // additive -100 instead of exclusion
   int force_max;           // MFMA kernel: always take the exact row-max pass
+  void* tab16;             // MFMA kernel scratch: prepared fp16 tables (heads x stride)
+  float* tmax;             // MFMA kernel scratch: log2(e) * max|table| per head
 };
+// bytes of scratch the MFMA kernel needs for its prepared tables
+size_t attention_workspace_bytes(const RelTab& rel, int heads);
 hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st);
 hipError_t attention_mfma(const AttnArgs& a, hipStream_t st);
 // shapes the MFMA kernel serves (bf16, d = 32, temporal window % 4 == 0 with

@@ -284,6 +284,18 @@ def test_empty_batch_on_gpu():
     assert y.shape == x.shape
 
 
+def _slot_to_natural(N, P, Mh, Mw, fast):
+    """Row order of the block's internal window buffers, as documented for
+    vswin_attention_fwd: slot s = 4 m + i holds token (pt = 4 a + i, ph, pw)
+    with m = (a * Mh + ph) * Mw + pw when the MFMA path serves the shape."""
+    s = np.arange(N)
+    if not fast:
+        return s
+    m, i = s // 4, s % 4
+    a, r = m // (Mh * Mw), m % (Mh * Mw)
+    return (4 * a + i) * (Mh * Mw) + r
+
+
 @pytest.mark.parametrize("shift", [(0, 0, 0), (4, 3, 3)])
 @pytest.mark.parametrize("size", [(16, 14, 14), (16, 12, 13)])
 def test_attention_core_alone(shift, size):
@@ -296,11 +308,18 @@ def test_attention_core_alone(shift, size):
     desc = vs.make_desc(B, *size, C, heads, window, shift)
     plan = vs.vswin_plan_query(desc)
     nW, N = plan["num_windows"], plan["tokens_per_window"]
+    perm = _slot_to_natural(N, *plan["eff_window"], plan["fast_attention"])
     rng = np.random.default_rng(17)
     q, k, v = (synth.round_bf16((1.5 * rng.standard_normal((nW, heads, N, d))).astype(np.float32))
                for _ in range(3))
     table = synth.round_bf16(rng.standard_normal((15 * 13 * 13, heads)).astype(np.float32))
-    o = host64(vs.vswin_attention_fwd(desc, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(table, "bf16")))
+    qs, ks, vs_ = q[:, :, perm], k[:, :, perm], v[:, :, perm]
+    if plan["fast_attention"]:
+        vs_ = np.ascontiguousarray(vs_.transpose(0, 1, 3, 2))
+    o = host64(vs.vswin_attention_fwd(desc, dev(qs, "bf16"), dev(ks, "bf16"), dev(vs_, "bf16"),
+                                      dev(table, "bf16")))
+    o_nat = np.empty_like(o)
+    o_nat[:, perm] = o
     g = ov.Geometry(B, size, window, shift)
     bias = table.astype(np.float64)[g.rel]
     ref = np.zeros((nW, N, C))
@@ -316,4 +335,4 @@ def test_attention_core_alone(shift, size):
             ref[w, :, h * d:(h + 1) * d] = (e / e.sum(1, keepdims=True)) @ v[w, h].astype(np.float64)
     # pad query rows are not outputs of the block; compare the real ones
     real = g.index_map() >= 0
-    check(o[real], ref[real], "bf16", "attention core")
+    check(o_nat[real], ref[real], "bf16", "attention core")
