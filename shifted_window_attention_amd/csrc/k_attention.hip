@@ -41,12 +41,12 @@ template <typename T, int DMAX>
 __global__ void __launch_bounds__(256) attn_generic_kernel(const AttnArgs a) {
   __shared__ int kf[kGenMaxN];
   __shared__ int klab[kGenMaxN];
-  const int64_t item = blockIdx.x;
-  const int64_t w = item / a.heads;
-  const int h = (int)(item - w * a.heads);
+  const int item = blockIdx.x;
+  const int w = item / a.heads;
+  const int h = item - w * a.heads;
   const WinGeo& g = a.geo;
   const int N = a.N, d = a.d;
-  const int wr = (int)(w % g.nws);
+  const int wr = w % g.nws;
   const int wpl = g.nwh * g.nww;
   const int wt = wr / wpl, rem = wr - wt * wpl, wh = rem / g.nww, ww = rem - (rem / g.nww) * g.nww;
   const int rt0 = wt * g.P, rh0 = wh * g.Mh, rw0 = ww * g.Mw;
@@ -57,9 +57,9 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(const AttnArgs a) {
     klab[n] = slot_label_at(g, rt0 + pt, rh0 + ph, rw0 + pw);
   }
   __syncthreads();
-  const T* Q = (const T*)a.q + item * N * d;
-  const T* K = (const T*)a.k + item * N * d;
-  const T* V = (const T*)a.v + item * N * d;
+  const T* Q = (const T*)a.q + (int64_t)item * N * d;
+  const T* K = (const T*)a.k + (int64_t)item * N * d;
+  const T* V = (const T*)a.v + (int64_t)item * N * d;
   const T* tab = (const T*)a.table;
   T* O = (T*)a.o;
   const float scale = 1.0f / sqrtf((float)d);
@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(const AttnArgs a) {
       if (pass == 1) {
         const float inv = 1.0f / sum;
         for (int e = 0; e < d; ++e)
-          Elem<T>::store(O, (w * N + qi) * (int64_t)a.C + h * d + e, acc[e] * inv);
+          Elem<T>::store(O, ((int64_t)w * N + qi) * a.C + h * d + e, acc[e] * inv);
       }
     }
   }
@@ -123,65 +123,42 @@ hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st) 
 // MFMA kernel
 // ---------------------------------------------------------------------------
 constexpr int kQT = 4;            // query tiles of 16 a wave carries at once
-constexpr int kWaves = 4;
-constexpr int kKLD = 40;          // K row pitch in LDS (elements): 80 bytes
+constexpr int kWaves = 4;         // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQSplit = 2;        // workgroups per (window, head): query tiles split in halves
+constexpr int kKLD = 40;          // K row pitch in the LDS ring (elements): 80 bytes
+constexpr int kVLD = 36;          // V^T row pitch in the LDS ring (elements): 72 bytes
+constexpr int kRing = 32 * kKLD + 32 * kVLD;   // one 32-key step: K rows + V^T columns
+constexpr int kTabPer = 12;       // table entries staged per thread
+constexpr int kKNorm = 8;         // 16-byte K chunks per thread for the key norms (N <= 512)
 constexpr int kDummyLab = 0x7fff0000;
 constexpr int kNoQueryLab = 0x7ffe0000;
 
 int attention_table_stride(const RelTab& rel) { return (rel.rows + 3 * rel.R + 8 + 7) & ~7; }
 
-size_t attention_workspace_bytes(const RelTab& rel, int heads) {
-  return ((size_t)heads * attention_table_stride(rel) * 2 + 255) / 256 * 256 + ((size_t)heads * 4 + 255) / 256 * 256;
-}
-
-// Per head: fp16 table reversed and scaled by log2(e), followed by a -inf zone
-// of 3R + 8 entries; tmax[h] = log2(e) * max |T|.
-__global__ void __launch_bounds__(256) attn_prep_kernel(const bf16_t* __restrict__ table, _Float16* __restrict__ tab16,
-                                                        float* __restrict__ tmax, int rows, int heads, int stride) {
-  __shared__ float red[4];
-  const int h = blockIdx.x;
-  float m = 0.f;
-  for (int x = threadIdx.x; x < stride; x += 256) {
-    if (x < rows) {
-      const float t = bf2f(table[(int64_t)(rows - 1 - x) * heads + h]);
-      m = fmaxf(m, fabsf(t));
-      tab16[(int64_t)h * stride + x] = (_Float16)(t * kLog2e);
-    } else {
-      tab16[(int64_t)h * stride + x] = (_Float16)(-INFINITY);
-    }
-  }
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) tmax[h] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) * kLog2e;
-}
+size_t attention_workspace_bytes(const RelTab&, int) { return 0; }
 
 struct MfmaLaunch {
-  int NT;         // key tiles of 16 (slots padded to NT*16)
-  int NVS;        // V^T columns staged (NT rounded up to even, *16)
-  int VST;        // V^T row pitch in LDS (elements): (VST/2) mod 32 = 2*odd
+  int NT;         // key tiles of 16
+  int NP;         // 32-key steps (pairs of tiles), padded with dummy slots
   int QTT;        // query tiles of 16
-  int tstride;    // fp16 table entries per head
-  size_t lds, off_vt, off_tab, off_kaddr, off_klab, off_red;
+  int tstride;    // fp16 table entries per head (table + -inf zone)
+  size_t lds, off_ring, off_kaddr, off_klab, off_red;
 };
 
 static MfmaLaunch mfma_launch(const AttnArgs& a) {
   MfmaLaunch L{};
   L.NT = (a.N + 15) / 16;
-  L.NVS = ((L.NT + 1) & ~1) * 16;
-  L.VST = L.NVS + 4;
+  L.NP = (L.NT + 1) / 2;
   L.QTT = L.NT;
   L.tstride = attention_table_stride(a.rel);
-  size_t off = (size_t)L.NT * 16 * kKLD * 2;
-  L.off_vt = off;
-  off += (size_t)32 * L.VST * 2;
-  off = (off + 15) & ~(size_t)15;
-  L.off_tab = off;
-  off += (size_t)L.tstride * 2;
+  size_t off = ((size_t)L.tstride * 2 + 15) & ~(size_t)15;
+  L.off_ring = off;
+  off += (size_t)2 * kRing * 2;
   L.off_kaddr = off;
-  off += (size_t)(L.NT * 4 + 4) * 4;
+  off += (size_t)(L.NP * 8) * 4;
   L.off_klab = off;
-  off += (size_t)(L.NT * 4 + 4) * 4;
+  off += (size_t)(L.NP * 8) * 4;
   L.off_red = off;
   off += 16;
   L.lds = off;
@@ -203,7 +180,8 @@ bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
   for (int rt = 0; rt < g.Tp; rt += 4)
     for (int i = 1; i < 4; ++i)
       if (tkey(rt + i) != tkey(rt)) return false;
-  return mfma_launch(a).lds <= 160 * 1024;
+  if (attention_table_stride(a.rel) > kTabPer * kThreads) return false;
+  return mfma_launch(a).lds <= 64 * 1024;
 }
 
 template <int QT>
@@ -215,15 +193,13 @@ struct QState {
   f32x4_t o0[QT], o1[QT], os[QT];   // O^T (d 0-15, d 16-31) and row sums
 };
 
-// One pair of key tiles (32 slots) for the QT query tiles of the wave, all in
-// one basic block so the tiles' MFMA, LDS and VALU work interleave.
+// One 32-key step from ring buffer `rb` for the QT query tiles of the wave,
+// in one basic block so the tiles' MFMA, LDS and VALU work interleave.
 //   MODE 0: P = exp2(x); 1: track the row max of x; 2: P = exp2(x - max).
 //   SEL: per key group, point masked / dummy groups at the -inf zone.
-//   TAIL: the pair may end in dummy slots or lack its second tile.
 //   R2C: byte stride of one temporal offset in the table (0 = runtime R2).
-template <int MODE, bool SEL, bool TAIL, int QT, int R2C>
-__device__ __forceinline__ void attn_pair(int tp, int NT, const bf16_t* __restrict__ Ks,
-                                          const bf16_t* __restrict__ Vt, int VST,
+template <int MODE, bool SEL, int QT, int R2C>
+__device__ __forceinline__ void attn_step(int p, const bf16_t* __restrict__ rb,
                                           const unsigned char* __restrict__ tabb, const int* __restrict__ kaddr,
                                           const int* __restrict__ klab, int R2r, int zone, float alpha,
                                           const bf16x8_t& ones, QState<QT>& st) {
@@ -231,21 +207,21 @@ __device__ __forceinline__ void attn_pair(int tp, int NT, const bf16_t* __restri
   const int lane = threadIdx.x & 63;
   const int fr = lane & 15, g4 = lane >> 4;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const bool hasB = !TAIL || tp + 1 < NT;
-  const bf16x8_t kA = *reinterpret_cast<const bf16x8_t*>(Ks + (16 * tp + fr) * kKLD + g4 * 8);
-  bf16x8_t kB = bf16x8_t{};
-  if (hasB) kB = *reinterpret_cast<const bf16x8_t*>(Ks + (16 * tp + 16 + fr) * kKLD + g4 * 8);
-  const int gA = kaddr[4 * tp + g4];
-  const int gB = kaddr[4 * tp + 4 + g4];
+  const bf16_t* Kb = rb;
+  const bf16_t* Vb = rb + 32 * kKLD;
+  const bf16x8_t kA = *reinterpret_cast<const bf16x8_t*>(Kb + fr * kKLD + g4 * 8);
+  const bf16x8_t kB = *reinterpret_cast<const bf16x8_t*>(Kb + (16 + fr) * kKLD + g4 * 8);
+  const int gA = kaddr[8 * p + g4];
+  const int gB = kaddr[8 * p + 4 + g4];
   int lA = 0, lB = 0;
   if (SEL) {
-    lA = klab[4 * tp + g4];
-    lB = hasB ? klab[4 * tp + 4 + g4] : kDummyLab;
+    lA = klab[8 * p + g4];
+    lB = klab[8 * p + 4 + g4];
   }
   bf16x8_t vA0 = bf16x8_t{}, vA1 = bf16x8_t{};
   if (MODE != 1) {
-    const u32x2_t* p0 = reinterpret_cast<const u32x2_t*>(Vt + fr * VST + 16 * tp + 4 * g4);
-    const u32x2_t* p1 = reinterpret_cast<const u32x2_t*>(Vt + (fr + 16) * VST + 16 * tp + 4 * g4);
+    const u32x2_t* p0 = reinterpret_cast<const u32x2_t*>(Vb + fr * kVLD + 4 * g4);
+    const u32x2_t* p1 = reinterpret_cast<const u32x2_t*>(Vb + (fr + 16) * kVLD + 4 * g4);
     const u32x2_t a0 = p0[0], b0 = p0[4], a1 = p1[0], b1 = p1[4];   // +16 slots = +32 bytes
     u32x4_t t0, t1;
     t0[0] = a0[0]; t0[1] = a0[1]; t0[2] = b0[0]; t0[3] = b0[1];
@@ -297,44 +273,210 @@ __device__ __forceinline__ void attn_pair(int tp, int NT, const bf16_t* __restri
   }
 }
 
-struct AttnCtx {
-  const bf16_t* Ks;
-  const bf16_t* Vt;
+// Per-thread share of one 32-key step: threads 0-127 one 16-byte chunk of the
+// K rows, threads 128-255 one of the V^T columns (two 8-byte halves).
+struct StepChunk {
+  u32x4_t v;
+};
+
+struct StreamCtx {
+  const bf16_t* Kg;     // (N, 32) slot order
+  const bf16_t* Vg;     // (32, N) slot order
+  bf16_t* ring;         // 2 x kRing elements
   const unsigned char* tabb;
   const int* kaddr;
   const int* klab;
-  int N, NT, VST, R2, zone;
+  int N, NP, R2, zone;
   float alpha;
 };
 
-template <int MODE, bool MASKED, int QT, int R2C>
-__device__ __forceinline__ void attn_pass(const AttnCtx& c, const bf16x8_t& ones, QState<QT>& st) {
-  const int nclean = c.N / 32;   // pairs whose 32 slots are all real keys
-  for (int pi = 0; pi < nclean; ++pi)
-    attn_pair<MODE, MASKED, false, QT, R2C>(2 * pi, c.NT, c.Ks, c.Vt, c.VST, c.tabb, c.kaddr, c.klab, c.R2,
-                                            c.zone, c.alpha, ones, st);
-  if (2 * nclean < c.NT)
-    attn_pair<MODE, true, true, QT, R2C>(2 * nclean, c.NT, c.Ks, c.Vt, c.VST, c.tabb, c.kaddr, c.klab, c.R2,
-                                         c.zone, c.alpha, ones, st);
+__device__ __forceinline__ StepChunk load_step(const StreamCtx& c, int p) {
+  const int t = threadIdx.x;
+  StepChunk r;
+  r.v = u32x4_t{0u, 0u, 0u, 0u};
+  if (p >= c.NP) return r;
+  if (t < 128) {
+    const int row = 32 * p + (t >> 2);
+    if (row < c.N) r.v = *reinterpret_cast<const u32x4_t*>(c.Kg + row * 32 + (t & 3) * 8);
+  } else {
+    const int d = (t - 128) >> 2, k0 = 32 * p + ((t - 128) & 3) * 8;
+    const bf16_t* src = c.Vg + d * c.N + k0;
+    if (k0 < c.N) {
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
+      r.v[0] = lo[0]; r.v[1] = lo[1];
+    }
+    if (k0 + 4 < c.N) {
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 4);
+      r.v[2] = hi[0]; r.v[3] = hi[1];
+    }
+  }
+  return r;
 }
 
-// Process query tiles j0, j0 + step, ... (QT of them) of one wave.
-template <int QT, int R2C>
-__device__ __forceinline__ void attn_tiles(const AttnArgs& a, const AttnCtx& c, int j0, int step, int64_t w, int h,
-                                           int rt0, int rh0, int rw0, float kmax, float tmx, bool wmasked,
-                                           const bf16_t* Qg, bf16_t* Og) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void store_step(const StreamCtx& c, int buf, const StepChunk& r) {
+  const int t = threadIdx.x;
+  bf16_t* rb = c.ring + buf * kRing;
+  if (t < 128) {
+    *reinterpret_cast<u32x4_t*>(rb + (t >> 2) * kKLD + (t & 3) * 8) = r.v;
+  } else {
+    const int d = (t - 128) >> 2, k0 = ((t - 128) & 3) * 8;
+    u32x2_t lo, hi;
+    lo[0] = r.v[0]; lo[1] = r.v[1]; hi[0] = r.v[2]; hi[1] = r.v[3];
+    *reinterpret_cast<u32x2_t*>(rb + 32 * kKLD + d * kVLD + k0) = lo;
+    *reinterpret_cast<u32x2_t*>(rb + 32 * kKLD + d * kVLD + k0 + 4) = hi;
+  }
+}
+
+// One pass over all keys.  Step p computes from ring buffer p % 2 while the
+// chunk of step p + 1 waits in registers and step p + 2 is being fetched.
+// Entry: step 0 in ring buffer 0 (visible to all waves), step 1 in `next`.
+template <int MODE, bool MASKED, int QT, int R2C>
+__device__ __forceinline__ void attn_stream(const StreamCtx& c, StepChunk next, const bf16x8_t& ones,
+                                            QState<QT>& st) {
+  const int nclean = c.N / 32;   // steps whose 32 slots are all real keys
+  for (int p = 0; p < c.NP; ++p) {
+    const StepChunk fut = load_step(c, p + 2);
+    const bf16_t* rb = c.ring + (p & 1) * kRing;
+    if (p < nclean)
+      attn_step<MODE, MASKED, QT, R2C>(p, rb, c.tabb, c.kaddr, c.klab, c.R2, c.zone, c.alpha, ones, st);
+    else
+      attn_step<MODE, true, QT, R2C>(p, rb, c.tabb, c.kaddr, c.klab, c.R2, c.zone, c.alpha, ones, st);
+    if (p + 1 < c.NP) store_step(c, (p + 1) & 1, next);
+    next = fut;
+    __syncthreads();
+  }
+}
+
+// One workgroup per (window, head, query half).  Inputs (slot order, see
+// slot_to_natural): q, k (item, N, 32); v transposed (item, 32, N); table
+// (rows, heads) bf16.  Output rows of o in slot order.  R2C: compile-time
+// table stride (0 = runtime).
+template <int R2C>
+__global__ void __launch_bounds__(kThreads)
+attn_mfma_kernel(const AttnArgs a, const MfmaLaunch L, const float alpha) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  _Float16* tab = reinterpret_cast<_Float16*>(smem);
+  bf16_t* ring = reinterpret_cast<bf16_t*>(smem + L.off_ring);
+  int* kaddr = reinterpret_cast<int*>(smem + L.off_kaddr);
+  int* klab = reinterpret_cast<int*>(smem + L.off_klab);
+  int* red = reinterpret_cast<int*>(smem + L.off_red);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, g4 = lane >> 4;
+  // XCD-aware order: consecutive logical blocks (the halves of one window-head,
+  // then neighbouring heads and windows) land on the same XCD and its L2.
+  const int64_t nblk = gridDim.x;
+  int64_t bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int item = (int)(bid / kQSplit);
+  const int split = (int)(bid - (int64_t)item * kQSplit);
+  const int w = item / a.heads;
+  const int h = item - w * a.heads;
   const WinGeo& g = a.geo;
+  const int N = a.N;
   const int mhw = g.Mh * g.Mw;
+  const int wr = w % g.nws;
+  const int wpl = g.nwh * g.nww;
+  const int wt = wr / wpl, rem = wr - wt * wpl, wh = rem / g.nww, ww = rem - (rem / g.nww) * g.nww;
+  const int rt0 = wt * g.P, rh0 = wh * g.Mh, rw0 = ww * g.Mw;
+  const bf16_t* Qg = reinterpret_cast<const bf16_t*>(a.q) + (int64_t)item * N * 32;
+  const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)item * N * 32;
+  const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)item * N * 32;
+  const bf16_t* Tg = reinterpret_cast<const bf16_t*>(a.table);
   const int R = a.rel.R, Rw = a.rel.Rw;
-  const int cq = a.rel.rows - 1 - a.rel.centre;
-  QState<QT> st;
-  bool need_max = false;
+
+  StreamCtx c;
+  c.Kg = Kg; c.Vg = Vg; c.ring = ring;
+  c.tabb = reinterpret_cast<const unsigned char*>(tab);
+  c.kaddr = kaddr; c.klab = klab;
+  c.N = N; c.NP = L.NP; c.R2 = 2 * R; c.zone = 2 * a.rel.rows; c.alpha = alpha;
+
+  if (tid < 4) red[tid] = 0;
+
+  // ---- one batch of global loads: table column, K rows (norms), the first
+  // two key steps and this wave's query tiles
+  uint16_t tv[kTabPer];
 #pragma unroll
-  for (int u = 0; u < QT; ++u) {
-    const int qs = 16 * (j0 + step * u) + fr;
-    const bool valid = qs < c.N;
+  for (int i = 0; i < kTabPer; ++i) {
+    const int x = tid + kThreads * i;
+    tv[i] = 0;
+    if (x < a.rel.rows) tv[i] = Tg[(int64_t)(a.rel.rows - 1 - x) * a.heads + h];
+  }
+  float kmax2 = 0.f;
+  {
+    u32x4_t kv[kKNorm];
+#pragma unroll
+    for (int i = 0; i < kKNorm; ++i) {
+      const int cc = tid + kThreads * i;
+      kv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if ((cc >> 2) < N) kv[i] = *reinterpret_cast<const u32x4_t*>(Kg + (cc >> 2) * 32 + (cc & 3) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kKNorm; ++i) {
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bflo(kv[i][e]), hi = bfhi(kv[i][e]);
+        sq += lo * lo + hi * hi;
+      }
+      sq += __shfl_xor(sq, 1);
+      sq += __shfl_xor(sq, 2);
+      kmax2 = fmaxf(kmax2, sq);
+    }
+  }
+  const StepChunk s0 = load_step(c, 0);
+  const StepChunk s1 = load_step(c, 1);
+  const int tps = (L.QTT + kQSplit - 1) / kQSplit;
+  const int jb = split * tps;                          // first query tile of this workgroup
+  const int jn = min(L.QTT, jb + tps) - jb;            // query tiles of this workgroup
+  const int mine = max(0, (jn - wv + kWaves - 1) / kWaves);   // <= kQT for N <= 512
+
+  // ---- geometry of the key groups (no memory traffic)
+  int anymask = 0;
+  const int lab0 = slot_label_at(g, rt0, rh0, rw0);
+  for (int m = tid; m < L.NP * 8; m += kThreads) {
+    if (m < N / 4) {
+      const int aa = m / mhw, r2 = m - aa * mhw, kh = r2 / g.Mw, kw = r2 - kh * g.Mw;
+      kaddr[m] = 2 * (4 * aa * R + kh * Rw + kw);
+      const int lab = slot_label_at(g, rt0 + 4 * aa, rh0 + kh, rw0 + kw);
+      klab[m] = lab;
+      anymask |= (lab != lab0);
+    } else {
+      kaddr[m] = 0;
+      klab[m] = kDummyLab;
+    }
+  }
+  // ---- LDS stores: table reversed and scaled by log2(e) (fp16), -inf zone
+  float tmaxl = 0.f;
+#pragma unroll
+  for (int i = 0; i < kTabPer; ++i) {
+    const int x = tid + kThreads * i;
+    if (x < L.tstride) {
+      const bool real = x < a.rel.rows;
+      const float t = bf2f(tv[i]);
+      tmaxl = real ? fmaxf(tmaxl, fabsf(t)) : tmaxl;
+      tab[x] = real ? (_Float16)(t * kLog2e) : (_Float16)(-INFINITY);
+    }
+  }
+  store_step(c, 0, s0);
+  __syncthreads();      // red[] cleared before the atomics below
+  atomicMax(&red[0], __float_as_int(kmax2));
+  atomicMax(&red[2], __float_as_int(tmaxl * kLog2e));
+  if (anymask) atomicOr(&red[1], 1);
+  __syncthreads();
+  const float kmax = sqrtf(__int_as_float(red[0]));
+  const float tmx = __int_as_float(red[2]);
+  const bool wmasked = a.use_mask && red[1] != 0;
+
+  // ---- this wave's query tiles jb + wv, jb + wv + 4, ... (at most kQT)
+  QState<kQT> st;
+  bool need_max = false;
+  const int cq = a.rel.rows - 1 - a.rel.centre;
+#pragma unroll
+  for (int u = 0; u < kQT; ++u) {
+    const int qs = 16 * (jb + wv + kWaves * u) + fr;
+    const bool valid = u < mine && qs < N;
     u32x4_t qv = {0u, 0u, 0u, 0u};
     int fq = 0;
     st.qlab[u] = kNoQueryLab;
@@ -355,178 +497,49 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const AttnCtx& c, 
     }
     sq += __shfl_xor(sq, 16);
     sq += __shfl_xor(sq, 32);
-    need_max |= valid && !(c.alpha * sqrtf(sq) * kmax + tmx <= 90.f);
+    need_max |= valid && !(alpha * sqrtf(sq) * kmax + tmx <= 90.f);
     st.mrow[u] = -INFINITY;
     st.o0[u] = st.o1[u] = st.os[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   bf16x8_t ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
-  const bool wave_max = a.force_max || __ballot(need_max) != 0;
-  if (wave_max) {
-    if (wmasked) attn_pass<1, true, QT, R2C>(c, ones, st);
-    else attn_pass<1, false, QT, R2C>(c, ones, st);
+  // the whole workgroup takes the same passes (they share the ring barriers)
+  const bool wg_max = a.force_max || __syncthreads_or(need_max ? 1 : 0);
+  if (!wg_max) {
+    if (wmasked) attn_stream<0, true, kQT, R2C>(c, s1, ones, st);
+    else attn_stream<0, false, kQT, R2C>(c, s1, ones, st);
+  } else {
+    if (wmasked) attn_stream<1, true, kQT, R2C>(c, s1, ones, st);
+    else attn_stream<1, false, kQT, R2C>(c, s1, ones, st);
 #pragma unroll
-    for (int u = 0; u < QT; ++u) {
+    for (int u = 0; u < kQT; ++u) {
       float m = st.mrow[u];
       m = fmaxf(m, __shfl_xor(m, 16));
       m = fmaxf(m, __shfl_xor(m, 32));
       st.mrow[u] = (m == -INFINITY) ? 0.f : m;
     }
-    if (wmasked) attn_pass<2, true, QT, R2C>(c, ones, st);
-    else attn_pass<2, false, QT, R2C>(c, ones, st);
-  } else {
-    if (wmasked) attn_pass<0, true, QT, R2C>(c, ones, st);
-    else attn_pass<0, false, QT, R2C>(c, ones, st);
+    const StepChunk t0 = load_step(c, 0);
+    const StepChunk t1 = load_step(c, 1);
+    store_step(c, 0, t0);
+    __syncthreads();
+    if (wmasked) attn_stream<2, true, kQT, R2C>(c, t1, ones, st);
+    else attn_stream<2, false, kQT, R2C>(c, t1, ones, st);
   }
-  // normalise and write O^T fragments (rows in slot order)
+
+  // ---- normalise and write O^T fragments (rows in slot order)
+  bf16_t* Og = reinterpret_cast<bf16_t*>(a.o);
 #pragma unroll
-  for (int u = 0; u < QT; ++u) {
-    const int qs = 16 * (j0 + step * u) + fr;
-    if (qs >= c.N) continue;
+  for (int u = 0; u < kQT; ++u) {
+    const int qs = 16 * (jb + wv + kWaves * u) + fr;
+    if (u >= mine || qs >= N) continue;
     const float inv = 1.0f / st.os[u][0];
     float o0[4], o1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { o0[i] = st.o0[u][i] * inv; o1[i] = st.o1[u][i] * inv; }
-    const int64_t base = (w * c.N + qs) * (int64_t)a.C + h * 32;
+    const int64_t base = ((int64_t)w * N + qs) * a.C + h * 32;
     store4(Og, base + 4 * g4, o0);
     store4(Og, base + 16 + 4 * g4, o1);
-  }
-}
-
-// One workgroup per (window, head).  Inputs (slot order, see slot_to_natural):
-// q, k (item, N, 32); v transposed (item, 32, N); tab16 / tmax from the prep
-// kernel.  Output rows of o in slot order.  R2C: compile-time table stride.
-template <int R2C>
-__global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnArgs a, const MfmaLaunch L, const float alpha) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* Vt = reinterpret_cast<bf16_t*>(smem + L.off_vt);
-  _Float16* tab = reinterpret_cast<_Float16*>(smem + L.off_tab);
-  int* kaddr = reinterpret_cast<int*>(smem + L.off_kaddr);
-  int* klab = reinterpret_cast<int*>(smem + L.off_klab);
-  int* red = reinterpret_cast<int*>(smem + L.off_red);
-
-  const int tid = threadIdx.x;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // XCD-aware order: consecutive logical blocks (neighbouring heads of one
-  // window, then neighbouring windows) land on the same XCD.
-  const int64_t nblk = gridDim.x;
-  int64_t item = blockIdx.x;
-  if ((nblk & 7) == 0) item = (item & 7) * (nblk >> 3) + (item >> 3);
-  const int64_t w = item / a.heads;
-  const int h = (int)(item - w * a.heads);
-  const WinGeo& g = a.geo;
-  const int N = a.N;
-  const int mhw = g.Mh * g.Mw;
-  const int wr = (int)(w % g.nws);
-  const int wpl = g.nwh * g.nww;
-  const int wt = wr / wpl, rem = wr - wt * wpl, wh = rem / g.nww, ww = rem - (rem / g.nww) * g.nww;
-  const int rt0 = wt * g.P, rh0 = wh * g.Mh, rw0 = ww * g.Mw;
-  const bf16_t* Qg = reinterpret_cast<const bf16_t*>(a.q) + item * N * 32;
-  const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + item * N * 32;
-  const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + item * N * 32;
-  const _Float16* Tg = reinterpret_cast<const _Float16*>(a.tab16) + (int64_t)h * L.tstride;
-  const int R = a.rel.R, Rw = a.rel.Rw;
-
-  if (tid < 4) red[tid] = 0;
-  __syncthreads();
-
-  // ---- stage: table (16-byte copies), K rows, V^T rows, key-group info.
-  // Loads are issued in batches before their LDS stores so that each thread
-  // has several global requests in flight.
-  for (int c0 = 0; c0 < L.tstride / 8; c0 += 256 * 4) {
-    u32x4_t buf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = c0 + tid + 256 * i;
-      if (c < L.tstride / 8) buf[i] = reinterpret_cast<const u32x4_t*>(Tg)[c];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = c0 + tid + 256 * i;
-      if (c < L.tstride / 8) reinterpret_cast<u32x4_t*>(tab)[c] = buf[i];
-    }
-  }
-  float kmax2 = 0.f;
-  for (int c0 = 0; c0 < L.NT * 64; c0 += 256 * 8) {
-    u32x4_t buf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = c0 + tid + 256 * i;
-      buf[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if ((c >> 2) < N) buf[i] = *reinterpret_cast<const u32x4_t*>(Kg + (c >> 2) * 32 + (c & 3) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = c0 + tid + 256 * i;
-      if (c0 + 256 * i >= L.NT * 64) break;      // depends on the batch index only: wave uniform
-      float sq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bflo(buf[i][e]), hi = bfhi(buf[i][e]);
-        sq += lo * lo + hi * hi;
-      }
-      if (c < L.NT * 64) *reinterpret_cast<u32x4_t*>(Ks + (c >> 2) * kKLD + (c & 3) * 8) = buf[i];
-      sq += __shfl_xor(sq, 1);
-      sq += __shfl_xor(sq, 2);
-      kmax2 = fmaxf(kmax2, sq);
-    }
-  }
-  const int c4 = L.NVS / 4;
-  for (int c0 = 0; c0 < 32 * c4; c0 += 256 * 16) {
-    u32x2_t buf[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = c0 + tid + 256 * i;
-      const int d = c / c4, k4 = (c - d * c4) * 4;
-      buf[i] = u32x2_t{0u, 0u};
-      if (c < 32 * c4 && k4 < N) buf[i] = *reinterpret_cast<const u32x2_t*>(Vg + d * N + k4);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = c0 + tid + 256 * i;
-      const int d = c / c4, k4 = (c - d * c4) * 4;
-      if (c < 32 * c4) *reinterpret_cast<u32x2_t*>(Vt + d * L.VST + k4) = buf[i];
-    }
-  }
-  int anymask = 0;
-  const int lab0 = slot_label_at(g, rt0, rh0, rw0);
-  for (int m = tid; m < L.NT * 4 + 4; m += 256) {
-    if (m < N / 4) {
-      const int aa = m / mhw, r2 = m - aa * mhw, kh = r2 / g.Mw, kw = r2 - kh * g.Mw;
-      kaddr[m] = 2 * (4 * aa * R + kh * Rw + kw);
-      const int lab = slot_label_at(g, rt0 + 4 * aa, rh0 + kh, rw0 + kw);
-      klab[m] = lab;
-      anymask |= (lab != lab0);
-    } else {
-      kaddr[m] = 0;
-      klab[m] = kDummyLab;
-    }
-  }
-  atomicMax(&red[0], __float_as_int(kmax2));
-  if (anymask) atomicOr(&red[1], 1);
-  __syncthreads();
-  const float kmax = sqrtf(__int_as_float(red[0]));
-  const float tmx = a.tmax[h];
-  const bool wmasked = a.use_mask && red[1] != 0;
-  AttnCtx c;
-  c.Ks = Ks; c.Vt = Vt; c.tabb = reinterpret_cast<const unsigned char*>(tab);
-  c.kaddr = kaddr; c.klab = klab;
-  c.N = N; c.NT = L.NT; c.VST = L.VST; c.R2 = 2 * R; c.zone = 2 * a.rel.rows; c.alpha = alpha;
-  bf16_t* Og = reinterpret_cast<bf16_t*>(a.o);
-
-  // ---- query tiles wv, wv + 4, wv + 8, ... in chunks of at most 4
-  const int mine = (L.QTT - wv + kWaves - 1) / kWaves;
-  for (int u0 = 0; u0 < mine; u0 += kQT) {
-    const int n = min(kQT, mine - u0);
-    const int j0 = wv + kWaves * u0;
-    switch (n) {
-      case 4: attn_tiles<4, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
-      case 3: attn_tiles<3, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
-      case 2: attn_tiles<2, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
-      default: attn_tiles<1, R2C>(a, c, j0, kWaves, w, h, rt0, rh0, rw0, kmax, tmx, wmasked, Qg, Og); break;
-    }
   }
 }
 
@@ -534,24 +547,17 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
   const int64_t items = a.nW * a.heads;
   if (items <= 0) return hipSuccess;
   const MfmaLaunch L = mfma_launch(a);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_mfma_kernel<338>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    hipFuncSetAttribute((const void*)attn_mfma_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(attn_prep_kernel, dim3(a.heads), dim3(256), 0, st, (const bf16_t*)a.table,
-                     (_Float16*)a.tab16, (float*)a.tmax, a.rel.rows, a.heads, L.tstride);
   const float alpha = kLog2e / sqrtf((float)a.d);
   AttnArgs ak = a;
-  // VSWIN_ATTN_MAXPASS=1 makes every wave take the exact row-max pass (test
-  // hook for the path that otherwise runs only for very large logits).
+  // VSWIN_ATTN_MAXPASS=1 makes every workgroup take the exact row-max pass
+  // (test hook for the path that otherwise runs only for very large logits).
   if (const char* f = getenv("VSWIN_ATTN_MAXPASS")) ak.force_max = atoi(f) != 0;
+  const dim3 grid((unsigned)(items * kQSplit));
   // the (8,7,7) window's table (R = 13 * 13) gets compile-time read offsets
   if (2 * a.rel.R == 338)
-    hipLaunchKernelGGL(attn_mfma_kernel<338>, dim3((unsigned)items), dim3(256), L.lds, st, ak, L, alpha);
+    hipLaunchKernelGGL(attn_mfma_kernel<338>, grid, dim3(kThreads), L.lds, st, ak, L, alpha);
   else
-    hipLaunchKernelGGL(attn_mfma_kernel<0>, dim3((unsigned)items), dim3(256), L.lds, st, ak, L, alpha);
+    hipLaunchKernelGGL(attn_mfma_kernel<0>, grid, dim3(kThreads), L.lds, st, ak, L, alpha);
   return hipGetLastError();
 }
 

@@ -38,16 +38,16 @@ struct EpiDev {
       const int c = n - 2 * a.C;
       const int h = c / a.d;
       const int e = c - h * a.d;
-      const int64_t w = m4 / a.N;
-      const int t = (int)(m4 - w * a.N);
-      store4((T*)a.out3, ((w * a.heads + h) * a.d + e) * (int64_t)a.N + t, v);
+      const int w = (int)m4 / a.N;
+      const int t = (int)m4 - w * a.N;
+      store4((T*)a.out3, ((int64_t)(w * a.heads + h) * a.d + e) * a.N + t, v);
     }
   }
   __device__ __forceinline__ int64_t row_ctx(int64_t m) const {
     if constexpr (KIND == Epi::kProjRes || KIND == Epi::kProjOut) {
       int lab;
-      const int64_t w = m / a.N;
-      return slot_source(a.geo, w, (int)(m - w * a.N), lab);
+      const int w = (int)m / a.N;
+      return slot_source(a.geo, w, (int)m - w * a.N, lab);
     } else {
       return m;
     }
@@ -76,10 +76,10 @@ struct EpiDev {
       const int c = n0 - which * a.C;
       const int h = c / a.d;
       const int e = c - h * a.d;
-      const int64_t w = m / a.N;
-      const int t = (int)(m - w * a.N);
+      const int w = (int)m / a.N;
+      const int t = (int)m - w * a.N;
       T* base = (T*)(which == 0 ? a.out : (which == 1 ? a.out2 : a.out3));
-      store4(base, ((w * a.heads + h) * a.N + t) * a.d + e, v);
+      store4(base, ((int64_t)(w * a.heads + h) * a.N + t) * a.d + e, v);
     } else if constexpr (KIND == Epi::kProjRes) {
       if (rc < 0) return;
       float r[4];
@@ -219,6 +219,173 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA GEMM with the whole K extent (K <= 128) staged in one batch:
+// one global round trip and one barrier per workgroup.  The A rows can be
+// gathered through the window map and layer-normalised on the way into LDS
+// (LN1 + pad + roll + partition fused into the qkv projection).
+// ---------------------------------------------------------------------------
+struct APrologue {
+  int mode;              // 0: rows of A; 1: gather x rows by slot; 2: gather + LayerNorm
+  const bf16_t* x;       // modes 1, 2: token rows (B*T*H*W, K)
+  const bf16_t* g;       // mode 2: LN gamma, beta (K)
+  const bf16_t* b;
+  float eps;
+  WinGeo geo;
+};
+
+template <int BN, int KK, class E>
+__global__ void __launch_bounds__(256) gemm_bf16_fullk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
+                                                              int64_t M, int N, E epi, APrologue pro) {
+  constexpr int WN = BN / 2;
+  constexpr int NT = WN / 16;
+  constexpr int MT = 4;
+  constexpr int LD = KK + 8;                 // row pitch (elements): 16-byte multiple, rows spread over banks
+  constexpr int HALF = KK / 2;               // elements per thread of one A row (2 threads per row)
+  constexpr int ACH = HALF / 8;              // 16-byte chunks per thread of one A row
+  constexpr int WCH = (BN * KK / 8 + 255) / 256;
+  __shared__ __attribute__((aligned(16))) bf16_t As[kBM * LD];
+  __shared__ __attribute__((aligned(16))) bf16_t Ws[BN * LD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nb = N / BN;
+  const int64_t bm = blockIdx.x / nb;
+  const int bn = (int)(blockIdx.x - bm * nb);
+  const int64_t m0 = bm * kBM;
+  const int n0 = bn * BN;
+
+  // ---- issue all global loads: this thread's half of one A row, its W chunks
+  const int arow = tid >> 1, ahalf = tid & 1;
+  const int64_t am = m0 + arow;
+  const bf16_t* asrc = nullptr;
+  if (am < M) {
+    if (pro.mode == 0) {
+      asrc = A + am * KK;
+    } else {
+      int lab;
+      const int w = (int)am / pro.geo.N;
+      const int64_t src = slot_source(pro.geo, w, (int)am - w * pro.geo.N, lab);
+      if (src >= 0) asrc = pro.x + src * KK;
+    }
+  }
+  u32x4_t av[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i)
+    av[i] = asrc ? *reinterpret_cast<const u32x4_t*>(asrc + ahalf * HALF + i * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  u32x4_t wv[WCH];
+#pragma unroll
+  for (int i = 0; i < WCH; ++i) {
+    const int c = tid + 256 * i;
+    if (c < BN * KK / 8) {
+      const int r = c / (KK / 8), k = (c % (KK / 8)) * 8;
+      wv[i] = *reinterpret_cast<const u32x4_t*>(W + (int64_t)(n0 + r) * KK + k);
+    }
+  }
+  // ---- optional LayerNorm of the A row (two threads per row)
+  if (pro.mode == 2) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += bflo(av[i][e]) + bfhi(av[i][e]);
+    s += __shfl_xor(s, 1);
+    const float mean = s * (1.0f / KK);
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d0 = bflo(av[i][e]) - mean, d1 = bfhi(av[i][e]) - mean;
+        q += d0 * d0 + d1 * d1;
+      }
+    q += __shfl_xor(q, 1);
+    const float rstd = 1.0f / sqrtf(q * (1.0f / KK) + pro.eps);
+    if (asrc) {
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) {
+        const int k0 = ahalf * HALF + i * 8;
+        const u32x4_t gg = *reinterpret_cast<const u32x4_t*>(pro.g + k0);
+        const u32x4_t bb = *reinterpret_cast<const u32x4_t*>(pro.b + k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = (bflo(av[i][e]) - mean) * rstd * bflo(gg[e]) + bflo(bb[e]);
+          const float hi = (bfhi(av[i][e]) - mean) * rstd * bfhi(gg[e]) + bfhi(bb[e]);
+          av[i][e] = pack_bf16x2(lo, hi);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ACH; ++i)
+    *reinterpret_cast<u32x4_t*>(&As[arow * LD + ahalf * HALF + i * 8]) = av[i];
+#pragma unroll
+  for (int i = 0; i < WCH; ++i) {
+    const int c = tid + 256 * i;
+    if (c < BN * KK / 8) {
+      const int r = c / (KK / 8), k = (c % (KK / 8)) * 8;
+      *reinterpret_cast<u32x4_t*>(&Ws[r * LD + k]) = wv[i];
+    }
+  }
+  __syncthreads();
+
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto run = [&](auto swap_tag) {
+    constexpr bool SWAP = decltype(swap_tag)::value;
+#pragma unroll
+    for (int k = 0; k < KK; k += 32) {
+      bf16x8_t af[MT], wf[NT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[(wm * 64 + mt * 16 + fr) * LD + k + fk]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        wf[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[(wn * WN + nt * 16 + fr) * LD + k + fk]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (SWAP)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], wf[nt], acc[mt][nt], 0, 0, 0);
+          else
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], af[mt], acc[mt][nt], 0, 0, 0);
+        }
+    }
+    if constexpr (SWAP) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m4 = m0 + wm * 64 + mt * 16 + (lane >> 4) * 4;
+        if (m4 >= M) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+          epi.store_t(m4, n0 + wn * WN + nt * 16 + fr, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = m0 + wm * 64 + mt * 16 + fr;
+        if (m >= M) continue;
+        const int64_t rc = epi.row_ctx(m);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = n0 + wn * WN + nt * 16 + (lane >> 4) * 4;
+          float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+          epi.store(m, rc, n, v);
+        }
+      }
+    }
+  };
+  if (epi.swapped(n0)) run(std::true_type{});
+  else run(std::false_type{});
+}
+
+// ---------------------------------------------------------------------------
 // fp32 FMA GEMM (64 x 64 tile, 4 x 4 outputs per thread)
 // ---------------------------------------------------------------------------
 template <class E>
@@ -268,9 +435,26 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 
 template <Epi KIND>
 static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K,
-                              const EpiArgs& e, hipStream_t st) {
+                              const EpiArgs& e, const APrologue& pro, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  if (dt == VSWIN_BF16) {
+  if (dt == VSWIN_BF16 && (K == 96 || K == 128)) {
+    EpiDev<bf16_t, KIND> epi{e};
+    const int64_t mb = (M + kBM - 1) / kBM;
+    const int F = KIND == Epi::kQKV ? e.C : N;
+    auto go = [&](auto kern, int bn) {
+      kern<<<dim3((unsigned)(mb * (N / bn))), dim3(256), 0, st>>>((const bf16_t*)A, (const bf16_t*)W, M, N, epi, pro);
+    };
+    if (K == 96) {
+      if (N % 96 == 0 && F % 96 == 0) go(gemm_bf16_fullk_kernel<96, 96, EpiDev<bf16_t, KIND>>, 96);
+      else if (N % 64 == 0 && F % 64 == 0) go(gemm_bf16_fullk_kernel<64, 96, EpiDev<bf16_t, KIND>>, 64);
+      else go(gemm_bf16_fullk_kernel<32, 96, EpiDev<bf16_t, KIND>>, 32);
+    } else {
+      if (N % 128 == 0 && F % 128 == 0) go(gemm_bf16_fullk_kernel<128, 128, EpiDev<bf16_t, KIND>>, 128);
+      else if (N % 64 == 0 && F % 64 == 0) go(gemm_bf16_fullk_kernel<64, 128, EpiDev<bf16_t, KIND>>, 64);
+      else go(gemm_bf16_fullk_kernel<32, 128, EpiDev<bf16_t, KIND>>, 32);
+    }
+  } else if (dt == VSWIN_BF16) {
+    if (pro.mode != 0) return hipErrorInvalidValue;   // gathered A rows need the full-K kernel
     EpiDev<bf16_t, KIND> epi{e};
     const int64_t mb = (M + kBM - 1) / kBM;
     auto go = [&](auto kern, int bn) {
@@ -284,6 +468,7 @@ static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int6
     else if (N % 64 == 0 && F % 64 == 0) go(gemm_bf16_kernel<64, EpiDev<bf16_t, KIND>>, 64);
     else go(gemm_bf16_kernel<32, EpiDev<bf16_t, KIND>>, 32);
   } else {
+    if (pro.mode != 0) return hipErrorInvalidValue;
     EpiDev<float, KIND> epi{e};
     const int64_t blocks = ((M + 63) / 64) * ((N + 63) / 64);
     gemm_f32_kernel<EpiDev<float, KIND>><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
@@ -292,15 +477,26 @@ static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int6
   return hipGetLastError();
 }
 
+bool gemm_can_gather(vswin_dtype dt, int K) { return dt == VSWIN_BF16 && (K == 96 || K == 128); }
+
 hipError_t gemm(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K, const EpiArgs& e,
-                hipStream_t st) {
+                hipStream_t st, const GatherA* ga) {
+  APrologue pro{};
+  if (ga) {
+    pro.mode = ga->ln ? 2 : 1;
+    pro.x = (const bf16_t*)ga->x;
+    pro.g = (const bf16_t*)ga->g;
+    pro.b = (const bf16_t*)ga->b;
+    pro.eps = ga->eps;
+    pro.geo = ga->geo;
+  }
   switch (e.kind) {
-    case Epi::kBias: return launch_kind<Epi::kBias>(dt, A, W, M, N, K, e, st);
-    case Epi::kQKV: return launch_kind<Epi::kQKV>(dt, A, W, M, N, K, e, st);
-    case Epi::kProjRes: return launch_kind<Epi::kProjRes>(dt, A, W, M, N, K, e, st);
-    case Epi::kProjOut: return launch_kind<Epi::kProjOut>(dt, A, W, M, N, K, e, st);
-    case Epi::kGelu: return launch_kind<Epi::kGelu>(dt, A, W, M, N, K, e, st);
-    case Epi::kRes: return launch_kind<Epi::kRes>(dt, A, W, M, N, K, e, st);
+    case Epi::kBias: return launch_kind<Epi::kBias>(dt, A, W, M, N, K, e, pro, st);
+    case Epi::kQKV: return launch_kind<Epi::kQKV>(dt, A, W, M, N, K, e, pro, st);
+    case Epi::kProjRes: return launch_kind<Epi::kProjRes>(dt, A, W, M, N, K, e, pro, st);
+    case Epi::kProjOut: return launch_kind<Epi::kProjOut>(dt, A, W, M, N, K, e, pro, st);
+    case Epi::kGelu: return launch_kind<Epi::kGelu>(dt, A, W, M, N, K, e, pro, st);
+    case Epi::kRes: return launch_kind<Epi::kRes>(dt, A, W, M, N, K, e, pro, st);
   }
   return hipErrorInvalidValue;
 }

@@ -42,8 +42,9 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(const TIN* __restrict__ x,
   int64_t src = row;
   if (gather) {
     int lab;
-    const int64_t w = row / geo.N;
-    src = slot_source(geo, w, (int)(row - w * geo.N), lab);
+    const int r = (int)row;
+    const int w = r / geo.N;
+    src = slot_source(geo, w, r - w * geo.N, lab);
   }
   const int npairs = C >> 1;
   TOUT* yr = y + row * C;
@@ -178,8 +179,8 @@ __global__ void __launch_bounds__(256) reverse_kernel(const T* __restrict__ win,
   const int64_t s = i / c4;
   const int c = (int)(i - s * c4) * 4;
   int lab;
-  const int64_t w = s / geo.N;
-  const int64_t src = slot_source(geo, w, (int)(s - w * geo.N), lab);
+  const int w = (int)s / geo.N;
+  const int64_t src = slot_source(geo, w, (int)s - w * geo.N, lab);
   if (src < 0) return;
   float v[4];
   load4(win, s * C + c, v);
@@ -210,8 +211,8 @@ __global__ void __launch_bounds__(256) index_map_kernel(int32_t* __restrict__ ma
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (s >= slots) return;
   int lab;
-  const int64_t w = s / geo.N;
-  const int64_t src = slot_source(geo, w, (int)(s - w * geo.N), lab);
+  const int w = (int)s / geo.N;
+  const int64_t src = slot_source(geo, w, (int)s - w * geo.N, lab);
   map[s] = (int32_t)src;
   if (region) region[s] = (uint8_t)lab;
 }

@@ -55,10 +55,7 @@ struct Plan {
 AttnArgs attn_args(const Plan& p, const void* q, const void* k, const void* v, const void* table, void* o,
                    uint32_t flags, char* scratch = nullptr) {
   AttnArgs a{};
-  if (scratch) {
-    a.tab16 = scratch;
-    a.tmax = (float*)(scratch + (p.ws_attn - align256((size_t)p.heads * 4)));
-  }
+  (void)scratch;
   a.q = q; a.k = k; a.v = v; a.table = table; a.o = o;
   a.nW = p.nW; a.heads = p.heads; a.d = p.d; a.C = p.C; a.N = p.N;
   a.rel = p.rel; a.geo = p.geo;
@@ -127,6 +124,8 @@ vswin_status make_plan(const vswin_desc* d, Plan& p, bool compute = true) {
   p.nW = (int64_t)d->B * g.nws;
   p.Lp = p.nW * N;
   p.L = (int64_t)d->B * d->T * d->H * d->W;
+  if (p.Lp >= ((int64_t)1 << 31) - 4096 || p.L * p.C >= ((int64_t)1 << 40))
+    return fail(VSWIN_ERR_UNSUPPORTED, "grid of %lld window slots is too large", (long long)p.Lp);
   const bool shifted = sh[0] || sh[1] || sh[2];
   const bool has_pad = pad[0] != d->T || pad[1] != d->H || pad[2] != d->W;
   p.use_mask = shifted || (has_pad && !g.pad_visible);
@@ -175,9 +174,11 @@ vswin_status check_msa_weights(const vswin_block_weights* w) {
   return VSWIN_OK;
 }
 
-// qkv -> attention -> proj (+ scatter); `xw` holds the gathered window rows.
+// qkv -> attention -> proj (+ scatter).  `ga` (nullable) makes the qkv
+// projection gather (and normalise) its rows itself; otherwise `xw` holds the
+// gathered window rows.
 vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weights* w, char* ws,
-                     const void* residual, void* out, bool to_zh, hipStream_t st) {
+                     const void* residual, void* out, bool to_zh, hipStream_t st, const GatherA* ga = nullptr) {
   void* xw = ws + p.off_xw;
   void* q = ws + p.off_q;
   void* k = ws + p.off_k;
@@ -188,7 +189,7 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
   e.out = q; e.out2 = k; e.out3 = v;
   e.C = p.C; e.heads = p.heads; e.d = p.d; e.N = p.N; e.geo = p.geo;
   e.vt = p.fast ? 1 : 0;
-  HIPCHECK(gemm(p.dt, xw, w->qkv_w, p.Lp, 3 * p.C, p.C, e, st), "qkv gemm");
+  HIPCHECK(gemm(p.dt, xw, w->qkv_w, p.Lp, 3 * p.C, p.C, e, st, ga), "qkv gemm");
   const AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags, ws + p.off_tab);
   if (p.fast) HIPCHECK(attention_mfma(a, st), "attention (mfma)");
   else HIPCHECK(attention_generic(p.dt, a, st), "attention (generic)");
@@ -265,11 +266,22 @@ vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x, const vswin_
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  // LN1 + pad + roll + partition
-  HIPCHECK(ln_gather(p.dt, x, w->ln1_g, w->ln1_b, ws + p.off_xw, p.Lp, p.C, desc->ln_eps, p.geo, 1, st),
-           "ln1 gather");
-  // attention branch; z^ = x + MSA (fp32)
-  CHECK(run_msa(p, desc, w, ws, x, ws + p.off_zh, true, st));
+  // LN1 + pad + roll + partition: fused into the qkv projection when it can
+  // stage whole rows, else a separate gather kernel
+  if (gemm_can_gather(p.dt, p.C)) {
+    const GatherA ga{x, w->ln1_g, w->ln1_b, desc->ln_eps, 1, p.geo};
+    CHECK(run_msa(p, desc, w, ws, x, ws + p.off_zh, true, st, &ga));
+  } else {
+    HIPCHECK(ln_gather(p.dt, x, w->ln1_g, w->ln1_b, ws + p.off_xw, p.Lp, p.C, desc->ln_eps, p.geo, 1, st),
+             "ln1 gather");
+    CHECK(run_msa(p, desc, w, ws, x, ws + p.off_zh, true, st));
+  }
+  if (mlp_fused_supported(p.dt, p.C, p.hid)) {
+    HIPCHECK(mlp_fused((const float*)(ws + p.off_zh), w->ln2_g, w->ln2_b, w->fc1_w, w->fc1_b, w->fc2_w, w->fc2_b,
+                       y, p.L, p.C, desc->ln_eps, st),
+             "fused mlp");
+    return VSWIN_OK;
+  }
   // LN2 -> xw region (free after proj)
   HIPCHECK(ln_rows(VSWIN_FP32, p.dt, ws + p.off_zh, w->ln2_g, w->ln2_b, ws + p.off_xw, p.L, p.C, desc->ln_eps,
                    st),
@@ -307,6 +319,10 @@ vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm, co
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
+  if (gemm_can_gather(p.dt, p.C)) {
+    const GatherA ga{x_norm, nullptr, nullptr, desc->ln_eps, 0, p.geo};
+    return run_msa(p, desc, w, ws, nullptr, y, false, st, &ga);
+  }
   HIPCHECK(ln_gather(p.dt, x_norm, nullptr, nullptr, ws + p.off_xw, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
            "partition");
   return run_msa(p, desc, w, ws, nullptr, y, false, st);

@@ -52,10 +52,11 @@ constexpr int kPadLabel = 255;
 
 // Source token (flat b,t,h,w) of window slot (w, n), or -1 for a pad slot;
 // `label` receives the slot's region label.
-__host__ __device__ inline int64_t slot_source(const WinGeo& g, int64_t w, int slot, int& label) {
+// 32-bit index math: the plan rejects grids with 2^31 or more window slots.
+__host__ __device__ inline int64_t slot_source(const WinGeo& g, int w, int slot, int& label) {
   const int n = slot_to_natural(g, slot);
-  const int b = (int)(w / g.nws);
-  const int wr = (int)(w - (int64_t)b * g.nws);
+  const int b = w / g.nws;
+  const int wr = w - b * g.nws;
   const int wpl = g.nwh * g.nww;
   const int wt = wr / wpl;
   const int rem = wr - wt * wpl;

@@ -38,8 +38,19 @@ struct EpiArgs {
   int vt;             // kQKV: write v transposed (item, d, N) (MFMA attention layout)
 };
 
+// Optional A-row gather: row m of A = token row src(m) of x (zeros for pad
+// slots), layer-normalised with g, b when `ln` (bf16, K in {96, 128} only).
+struct GatherA {
+  const void* x;
+  const void* g;
+  const void* b;
+  float eps;
+  int ln;
+  WinGeo geo;
+};
 hipError_t gemm(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K, const EpiArgs& e,
-                hipStream_t st);
+                hipStream_t st, const GatherA* ga = nullptr);
+bool gemm_can_gather(vswin_dtype dt, int K);
 
 // --- attention (k_attention.hip) ------------------------------------------
 struct AttnArgs {
@@ -53,8 +64,6 @@ struct AttnArgs {
   int use_mask;            // some window may need the region mask
   int mask_m100;           // additive -100 instead of exclusion
   int force_max;           // MFMA kernel: always take the exact row-max pass
-  void* tab16;             // MFMA kernel scratch: prepared fp16 tables (heads x stride)
-  float* tmax;             // MFMA kernel scratch: log2(e) * max|table| per head
 };
 // bytes of scratch the MFMA kernel needs for its prepared tables
 size_t attention_workspace_bytes(const RelTab& rel, int heads);
@@ -62,8 +71,13 @@ hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st);
 hipError_t attention_mfma(const AttnArgs& a, hipStream_t st);
 // shapes the MFMA kernel serves (bf16, d = 32, temporal window % 4 == 0 with
 // group-uniform temporal labels, N <= kMfmaMaxN, no additive -100 mask)
-constexpr int kMfmaMaxN = 1024;
+constexpr int kMfmaMaxN = 512;
 bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a);
+
+// --- fused LN2 -> fc1 -> GELU -> fc2 -> residual (k_mlp.hip) --------------
+bool mlp_fused_supported(vswin_dtype dt, int C, int hid);
+hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const void* W1, const void* b1,
+                     const void* W2, const void* bo, void* y, int64_t L, int C, float eps, hipStream_t st);
 
 // --- patch embedding / merging gathers (k_patch.hip) ----------------------
 hipError_t patch_gather(vswin_dtype dt, const void* video, void* out, int B, int Cin, int T, int H, int W,
