@@ -114,6 +114,7 @@ vswin_status make_plan(const vswin_desc* d, Plan& p, bool compute = true) {
   g.N = N;
   g.nws = (pad[0] / win[0]) * g.nwh * g.nww;
   g.pad_visible = (d->flags & VSWIN_F_PAD_VISIBLE) ? 1 : 0;
+  geo_divisors(g);
   const int R = (2 * d->window[1] - 1) * (2 * d->window[2] - 1);
   p.rel.R = R;
   p.rel.Rw = 2 * d->window[2] - 1;
@@ -183,6 +184,18 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
   void* q = ws + p.off_q;
   void* k = ws + p.off_k;
   void* v = ws + p.off_v;
+  const int vt = p.fast ? 1 : 0;
+  if (ga && winproj_supported(p.dt, p.C, p.d, p.N, vt)) {
+    HIPCHECK(qkv_proj(ga->x, ga->g, ga->b, ga->eps, ga->ln, w->qkv_w, w->qkv_b, q, k, v, vt, p.Lp, p.C, p.heads,
+                      p.d, p.geo, st),
+             "qkv projection");
+    const AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags, ws + p.off_tab);
+    if (p.fast) HIPCHECK(attention_mfma(a, st), "attention (mfma)");
+    else HIPCHECK(attention_generic(p.dt, a, st), "attention (generic)");
+    HIPCHECK(out_proj(xw, w->proj_w, w->proj_b, to_zh ? residual : nullptr, out, p.Lp, p.C, p.geo, st),
+             "output projection");
+    return VSWIN_OK;
+  }
   EpiArgs e{};
   e.kind = Epi::kQKV;
   e.bias = w->qkv_b;
@@ -465,7 +478,7 @@ vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, i
   if (!(eps > 0.f)) return fail(VSWIN_ERR_INVALID_ARG, "eps must be > 0");
   if (C % 8) return fail(VSWIN_ERR_UNSUPPORTED, "C must be a multiple of 8");
   if (4 * C > 4096) return fail(VSWIN_ERR_UNSUPPORTED, "4C > 4096");
-  if (dtype == VSWIN_BF16 && Cout % 32) return fail(VSWIN_ERR_UNSUPPORTED, "bf16 merge needs Cout % 32 == 0");
+  if (dtype == VSWIN_BF16 && Cout % 32) return fail(VSWIN_ERR_UNSUPPORTED, "bf16 merge needs Cout %% 32 == 0");
   if (dtype == VSWIN_FP32 && Cout % 4) return fail(VSWIN_ERR_UNSUPPORTED, "Cout must be a multiple of 4");
   if (B == 0) return VSWIN_OK;
   CHECK(check_ptr(x, "x"));

@@ -9,6 +9,27 @@
 namespace vswin {
 
 // ---------------------------------------------------------------------------
+// Division by a run-time invariant 1 <= d < 2^31 of dividends 0 <= n < 2^31
+// with one multiply-high, an add and a shift (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", PLDI 1994, sec. 4):
+// s = ceil(log2 d), mul = floor(2^32 (2^s - d) / d) + 1, and then
+// n / d = (mulhi(n, mul) + n) >> s.  With n < 2^31 the sum stays below 2^32.
+// ---------------------------------------------------------------------------
+struct FastDiv {
+  uint32_t d, mul, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while (((uint64_t)1 << s) < d) ++s;
+  const uint64_t mul = ((((uint64_t)1 << s) - d) << 32) / d + 1;
+  return FastDiv{d, (uint32_t)mul, s};
+}
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  const uint32_t hi = (uint32_t)(((uint64_t)n * f.mul) >> 32);
+  return (hi + n) >> f.s;
+}
+
+// ---------------------------------------------------------------------------
 // Window geometry of one block after the clamp, as the kernels see it.
 // The permutation it encodes (pages: §3.2, fig. 3; the mmaction2 walk-through
 // op order LN -> pad -> roll -> partition):
@@ -27,7 +48,18 @@ struct WinGeo {
   int nws;            // windows per clip
   int pad_visible;    // pads keep their positional label
   int slot_perm;      // window rows in attention slot order (see slot_to_natural)
+  // divisors of the slot -> token map (set by geo_divisors)
+  FastDiv fN, fnws, fwpl, fnww, fmhw, fMw;
 };
+
+inline void geo_divisors(WinGeo& g) {
+  g.fN = make_fastdiv((uint32_t)g.N);
+  g.fnws = make_fastdiv((uint32_t)g.nws);
+  g.fwpl = make_fastdiv((uint32_t)(g.nwh * g.nww));
+  g.fnww = make_fastdiv((uint32_t)g.nww);
+  g.fmhw = make_fastdiv((uint32_t)(g.Mh * g.Mw));
+  g.fMw = make_fastdiv((uint32_t)g.Mw);
+}
 
 // Order of the rows of one window inside the block's buffers.  Natural order
 // is (pt, ph, pw) row-major.  The MFMA attention path (P % 4 == 0) stores
@@ -38,7 +70,7 @@ __host__ __device__ inline int slot_to_natural(const WinGeo& g, int k) {
   if (!g.slot_perm) return k;
   const int m = k >> 2, i = k & 3;
   const int mhw = g.Mh * g.Mw;
-  const int a = m / mhw;
+  const int a = (int)fdiv((uint32_t)m, g.fmhw);
   return (4 * a + i) * mhw + (m - a * mhw);
 }
 
@@ -55,17 +87,17 @@ constexpr int kPadLabel = 255;
 // 32-bit index math: the plan rejects grids with 2^31 or more window slots.
 __host__ __device__ inline int64_t slot_source(const WinGeo& g, int w, int slot, int& label) {
   const int n = slot_to_natural(g, slot);
-  const int b = w / g.nws;
+  const int b = (int)fdiv((uint32_t)w, g.fnws);
   const int wr = w - b * g.nws;
   const int wpl = g.nwh * g.nww;
-  const int wt = wr / wpl;
+  const int wt = (int)fdiv((uint32_t)wr, g.fwpl);
   const int rem = wr - wt * wpl;
-  const int wh = rem / g.nww;
+  const int wh = (int)fdiv((uint32_t)rem, g.fnww);
   const int ww = rem - wh * g.nww;
   const int mhw = g.Mh * g.Mw;
-  const int pt = n / mhw;
+  const int pt = (int)fdiv((uint32_t)n, g.fmhw);
   const int r2 = n - pt * mhw;
-  const int ph = r2 / g.Mw;
+  const int ph = (int)fdiv((uint32_t)r2, g.fMw);
   const int pw = r2 - ph * g.Mw;
   const int rt = wt * g.P + pt, rh = wh * g.Mh + ph, rw = ww * g.Mw + pw;
   int ot = rt + g.st; if (ot >= g.Tp) ot -= g.Tp;
@@ -76,6 +108,13 @@ __host__ __device__ inline int64_t slot_source(const WinGeo& g, int w, int slot,
                   axis_label(rw, g.Wp, g.Mw, g.sw);
   label = (pad && !g.pad_visible) ? kPadLabel : lab;
   return pad ? (int64_t)-1 : (((int64_t)b * g.T + ot) * g.H + oh) * g.W + ow;
+}
+
+// Source token of window row m (slot order of the geometry) of the whole
+// batch of windows, or -1 for a pad slot.
+__host__ __device__ inline int64_t row_source(const WinGeo& g, int m, int& label) {
+  const int w = (int)fdiv((uint32_t)m, g.fN);
+  return slot_source(g, w, m - w * g.N, label);
 }
 
 // Rolled-grid label of a slot given the window's rolled origin (rt0, rh0, rw0)

@@ -52,6 +52,18 @@ hipError_t gemm(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, 
                 hipStream_t st, const GatherA* ga = nullptr);
 bool gemm_can_gather(vswin_dtype dt, int K);
 
+// --- window projections for C in {96, 128}, bf16 (k_winproj.hip) ----------
+// qkv: gather (+ LN1 when ln) window rows of x, project, split by head into
+// q, k (nW*heads, N, d) and v (same, or transposed (nW*heads, d, N) when vt).
+// out: o rows * W^T + bias scattered to token rows; with `res` the output is
+// fp32 z = res + ..., else bf16.
+bool winproj_supported(vswin_dtype dt, int C, int d, int N, int vt);
+hipError_t qkv_proj(const void* x, const void* ln_g, const void* ln_b, float eps, int ln, const void* W,
+                    const void* bias, void* q, void* k, void* v, int vt, int64_t M, int C, int heads, int d,
+                    const WinGeo& geo, hipStream_t st);
+hipError_t out_proj(const void* o, const void* W, const void* bias, const void* res, void* out, int64_t M, int C,
+                    const WinGeo& geo, hipStream_t st);
+
 // --- attention (k_attention.hip) ------------------------------------------
 struct AttnArgs {
   const void *q, *k, *v;   // (nW, heads, N, d) of dtype; MFMA path: v is (nW, heads, d, N)
