@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvswin.so")
-SOURCES = ["vswin_api.hip", "k_layout.hip", "k_gemm.hip", "k_winproj.hip", "k_attention.hip", "k_mlp.hip",
-           "k_patch.hip"]
+SOURCES = ["vswin_api.hip", "k_layout.hip", "k_gemm.hip", "k_winproj.hip", "k_attention.hip", "k_attn_mfma.hip",
+           "k_mlp.hip", "k_patch.hip"]
 ARCH = os.environ.get("VSWIN_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
@@ -32,7 +32,7 @@ def _hipcc() -> str:
 
 # per-file extras: the attention kernel keeps MFMA operands/results in VGPRs
 # (no accumulation-register round trips between score tiles and VALU work)
-EXTRA = {"k_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"k_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -1,0 +1,595 @@
+// Window attention on MFMA for bf16, head_dim 32 (§3.2, eq. 2):
+//   per (window, head): S = q k^T / sqrt(d) + B[idx(i, j)], masked pairs
+//   excluded, P = softmax_j(S), O = P v, heads concatenated as h*32 + e.
+//
+// Work split.  The query tiles (16 queries) of all (head, window) items form
+// one list, head-major; each workgroup (8 waves, one per CU) takes an equal
+// contiguous run of it and walks the items in that run.  A window's K and
+// V^T are staged once in LDS for all of the run's tiles of that window, and
+// the next window's K/V is fetched into registers while the current one is
+// computed (two LDS buffers when they fit, else one), so staging latency
+// hides behind compute.  Waves own tiles, not steps: inside a window no
+// barrier is needed.
+//
+// Scores.  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (k = head_dim): a lane
+// holds 4 keys of one query, so all per-query state stays in the lane.
+//   * Keys are in slot order (slot 4m + i holds temporal position 4a + i of
+//     spatial cell m), so the 4 keys of a lane differ only in their temporal
+//     offset.  The bias table is stored in LDS as fp32 4-tuples
+//     (B[r], B[r + R'], B[r + 2R'], B[r + 3R']) * log2(e) indexed by the
+//     query's and the key group's offsets, and enters as the MFMA's C operand:
+//     the bias costs one 16-byte LDS read per 4 scores and no VALU.  Masked
+//     and dummy key groups read a 4-tuple of -inf instead.
+//   * q arrives multiplied by log2(e) / sqrt(d), so the MFMA result is the
+//     exponent of 2 directly.  P = exp2(x) with no running max when a
+//     Cauchy-Schwarz bound |x| <= |q| max|k| + max|B log2 e| <= 90 shows
+//     exp2 cannot overflow (softmax is shift invariant); otherwise the wave
+//     first takes an exact row-max pass.
+//   * O^T = V^T P^T on MFMA with P^T already in B-operand layout; the row
+//     sums come from a third MFMA against a ones operand.  V^T rows are read
+//     in pair order (d = 8g + 4p + i), so a lane ends with 8 consecutive
+//     output features and writes one 16-byte vector per query.
+//
+// LDS layouts (bank-conflict free 16-byte fragment reads):
+//   K      key rows of 64 bytes; chunk c of row r at chunk c ^ ((r >> 2) & 3).
+//   V^T    32 rows of the padded key count; inside each 32-key block the keys
+//          are permuted so lane group g's 8 keys {4g..4g+3, 16+4g..16+4g+3}
+//          are one 16-byte chunk; chunk c of row d at c ^ ((d >> 3) & 3); the
+//          row pitch is 4 mod 16 chunks.
+//   table  4-tuples with a temporal stride R' = 4 mod 16 entries (R' >= R).
+#include "vswin_kernels.h"
+
+#include <math.h>
+#include <stdlib.h>
+
+namespace vswin {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPref = 4;          // K and V^T 16-byte chunks per thread and window (N <= 512)
+constexpr int kTabIter = 8;       // table 4-tuples per thread (<= 4096 entries)
+constexpr int kDummyLab = 0x7fff0000;
+constexpr int kNoQueryLab = 0x7ffe0000;
+constexpr size_t kLdsMax = 160 * 1024;
+
+struct A5 {
+  int N, NPAD, NP, QTT, NB;
+  int pitch_v;                // V^T row pitch (16-byte chunks)
+  int Rp, Rw, R, TD, TH, A;   // table: temporal stride R', row stride, true R, extents, query base
+  int TS4;                    // 4-tuples incl. the -inf one at the end
+  int nW, heads;
+  FastDiv fdRp, fdRw, fdnW, fdKC;
+  int64_t TT;                 // tiles in the whole list
+  float qscale;               // multiplier applied to q on load (1 when pre-scaled)
+  int force_max;
+  uint32_t off_kp, off_tab, off_redt, off_buf, buf_bytes, off_v, off_lp, off_red;
+};
+
+struct Pref {
+  u32x4_t k[kPref], v[kPref];
+};
+
+template <int QT>
+struct QState {
+  bf16x8_t q[QT];
+  int qaddr[QT];      // byte offset of the query's table base
+  int qlab[QT];
+  float mrow[QT];
+  f32x4_t o0[QT], o1[QT], os[QT];
+};
+
+struct Win {          // one (head, window) item
+  int h, w, mem;      // head, window, item index in q/k/v (w * heads + h)
+  int rt0, rh0, rw0;  // rolled origin of the window
+};
+
+__device__ __forceinline__ Win window_of(const AttnArgs& a, const A5& L, int it) {
+  const WinGeo& g = a.geo;
+  Win r;
+  r.h = (int)fdiv((uint32_t)it, L.fdnW);
+  r.w = it - r.h * L.nW;
+  r.mem = r.w * L.heads + r.h;
+  const int wr = r.w - (int)fdiv((uint32_t)r.w, g.fnws) * g.nws;
+  const int wt = (int)fdiv((uint32_t)wr, g.fwpl);
+  const int rem = wr - wt * g.nwh * g.nww;
+  const int wh = (int)fdiv((uint32_t)rem, g.fnww);
+  r.rt0 = wt * g.P;
+  r.rh0 = wh * g.Mh;
+  r.rw0 = (rem - wh * g.nww) * g.Mw;
+  return r;
+}
+
+// threadIdx.x behind an empty asm: keeps the compiler from hoisting the
+// per-lane address math of the staging helpers out of the window loop (it
+// would hold those values in registers across the compute)
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  return v;
+}
+
+// ---- staging -------------------------------------------------------------
+__device__ __forceinline__ void pref_load(Pref& pf, const AttnArgs& a, const A5& L, int mem) {
+  const int tid = opaque_tid();
+  const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)mem * L.N * 32;
+  const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)mem * L.N * 32;
+  const int kcpr = L.NPAD >> 3;
+#pragma unroll
+  for (int j = 0; j < kPref; ++j) {
+    const int c = tid + kThreads * j;
+    const int r = c >> 2;
+    pf.k[j] = r < L.N ? *reinterpret_cast<const u32x4_t*>(Kg + r * 32 + (c & 3) * 8) : u32x4_t{0u, 0u, 0u, 0u};
+    const int d = (int)fdiv((uint32_t)c, L.fdKC);
+    const int key0 = 8 * (c - d * kcpr);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (d < 32) {
+      const bf16_t* src = Vg + d * L.N + key0;
+      if ((L.N & 7) == 0) {
+        if (key0 < L.N) v = *reinterpret_cast<const u32x4_t*>(src);
+      } else {
+        if (key0 < L.N) {
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
+          v[0] = lo[0]; v[1] = lo[1];
+        }
+        if (key0 + 4 < L.N) {
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 4);
+          v[2] = hi[0]; v[3] = hi[1];
+        }
+      }
+    }
+    pf.v[j] = v;
+  }
+}
+
+__device__ __forceinline__ void pref_store(const Pref& pf, const A5& L, unsigned char* B) {
+  const int tid = opaque_tid();
+  const int kcpr = L.NPAD >> 3;
+  float km = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPref; ++j) {
+    const int c = tid + kThreads * j;
+    const int r = c >> 2, q = c & 3;
+    if (r < L.NPAD) *reinterpret_cast<u32x4_t*>(B + r * 64 + ((q ^ ((r >> 2) & 3)) << 4)) = pf.k[j];
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bflo(pf.k[j][e]), hi = bfhi(pf.k[j][e]);
+      sq += lo * lo + hi * hi;
+    }
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    km = fmaxf(km, sq);
+    const int d = (int)fdiv((uint32_t)c, L.fdKC);
+    if (d < 32) {
+      const int kc = c - d * kcpr;
+      const int p = kc >> 2, cb = kc & 3;
+      const int lc0 = 2 * (cb & 1), sw = (d >> 3) & 3;
+      unsigned char* row = B + L.off_v + d * L.pitch_v * 16 + p * 64 + 8 * (cb >> 1);
+      u32x2_t lo, hi;
+      lo[0] = pf.v[j][0]; lo[1] = pf.v[j][1];
+      hi[0] = pf.v[j][2]; hi[1] = pf.v[j][3];
+      *reinterpret_cast<u32x2_t*>(row + ((lc0 ^ sw) << 4)) = lo;
+      *reinterpret_cast<u32x2_t*>(row + (((lc0 + 1) ^ sw) << 4)) = hi;
+    }
+  }
+  km = wave_max(km);
+  if ((tid & 63) == 0) reinterpret_cast<float*>(B + L.off_red)[tid >> 6] = km;
+}
+
+// region labels of the window's key groups and whether they differ
+__device__ __forceinline__ void stage_labels(const AttnArgs& a, const A5& L, const Win& wi, unsigned char* B) {
+  const WinGeo& g = a.geo;
+  const int tid = opaque_tid();
+  const int mhw = g.Mh * g.Mw;
+  const int lab0 = slot_label_at(g, wi.rt0, wi.rh0, wi.rw0);
+  int* lp = reinterpret_cast<int*>(B + L.off_lp);
+  bool differs = false;
+  for (int m = tid; m < L.NP * 8; m += kThreads) {
+    int lab = kDummyLab;
+    if (m < L.N / 4) {
+      const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
+      const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
+      lab = slot_label_at(g, wi.rt0 + 4 * aa, wi.rh0 + kh, wi.rw0 + kw);
+      differs |= lab != lab0;
+    }
+    const int p = m >> 3, s = m & 7;
+    lp[2 * (4 * p + (s & 3)) + (s >> 2)] = lab;
+  }
+  const uint64_t any = __builtin_amdgcn_ballot_w64(differs);
+  if ((tid & 63) == 0) reinterpret_cast<int*>(B + L.off_red)[8 + (tid >> 6)] = any != 0;
+}
+
+// fp32 4-tuples of the head's column of the table, scaled by log2(e)
+__device__ __forceinline__ void build_table(const AttnArgs& a, const A5& L, int h, unsigned char* smem) {
+  const int tid = opaque_tid();
+  const bf16_t* T = reinterpret_cast<const bf16_t*>(a.table);
+  uint16_t raw[kTabIter][4];
+#pragma unroll
+  for (int j = 0; j < kTabIter; ++j) {
+    const int x = tid + kThreads * j;
+    const int dtr = (int)fdiv((uint32_t)x, L.fdRp);
+    const int rem = x - dtr * L.Rp;
+    const int dhr = (int)fdiv((uint32_t)rem, L.fdRw);
+    const int dwr = rem - dhr * L.Rw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dt = dtr + i;
+      const bool ok = x < L.TS4 - 1 && rem < L.R && dt < L.TD;
+      const int row = (L.TD - 1 - dt) * L.R + (L.TH - 1 - dhr) * L.Rw + (L.Rw - 1 - dwr);
+      raw[j][i] = ok ? T[row * L.heads + h] : (uint16_t)0;
+    }
+  }
+  f32x4_t* tab = reinterpret_cast<f32x4_t*>(smem + L.off_tab);
+  float tm = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTabIter; ++j) {
+    const int x = tid + kThreads * j;
+    if (x < L.TS4) {
+      f32x4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = bf2f(raw[j][i]) * kLog2e;
+        tm = fmaxf(tm, fabsf(v[i]));
+      }
+      if (x == L.TS4 - 1) v = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      tab[x] = v;
+    }
+  }
+  tm = wave_max(tm);
+  if ((tid & 63) == 0) reinterpret_cast<float*>(smem + L.off_redt)[tid >> 6] = tm;
+}
+
+// ---- one 32-key step for the wave's QT tiles --------------------------------
+//   MODE 0: P = exp2(x); 1: row max of x only; 2: P = exp2(x - max).
+//   SEL: per key group, masked / dummy groups read the -inf 4-tuple.
+template <int MODE, bool SEL, int QT>
+__device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict__ B, const A5& L,
+                                          const unsigned char* __restrict__ tabb, const int* __restrict__ kp,
+                                          int zone, const bf16x8_t& ones, QState<QT>& st) {
+  const int lane = threadIdx.x & 63;
+  const int fr = lane & 15, g4 = lane >> 4;
+  const int sw = (fr >> 2) & 3;
+  const bf16x8_t kA = *reinterpret_cast<const bf16x8_t*>(B + (32 * p + fr) * 64 + ((g4 ^ sw) << 4));
+  const bf16x8_t kB = *reinterpret_cast<const bf16x8_t*>(B + (32 * p + 16 + fr) * 64 + ((g4 ^ sw) << 4));
+  bf16x8_t vA0 = bf16x8_t{}, vA1 = bf16x8_t{};
+  if (MODE != 1) {
+    const int d0 = 8 * (fr >> 2) + (fr & 3);
+    const unsigned char* vb = B + L.off_v + p * 64 + ((g4 ^ sw) << 4);
+    vA0 = *reinterpret_cast<const bf16x8_t*>(vb + d0 * L.pitch_v * 16);
+    vA1 = *reinterpret_cast<const bf16x8_t*>(vb + (d0 + 4) * L.pitch_v * 16);
+  }
+  const int2 gk = reinterpret_cast<const int2*>(kp)[4 * p + g4];
+  int2 lk = {0, 0};
+  if (SEL) lk = reinterpret_cast<const int2*>(B + L.off_lp)[4 * p + g4];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    int adA = st.qaddr[u] + gk.x, adB = st.qaddr[u] + gk.y;
+    if (SEL) {
+      adA = (lk.x == st.qlab[u]) ? adA : zone;
+      adB = (lk.y == st.qlab[u]) ? adB : zone;
+    }
+    const f32x4_t tA = *reinterpret_cast<const f32x4_t*>(tabb + adA);
+    const f32x4_t tB = *reinterpret_cast<const f32x4_t*>(tabb + adB);
+    const f32x4_t sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, st.q[u], tA, 0, 0, 0);
+    const f32x4_t sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, st.q[u], tB, 0, 0, 0);
+    if (MODE == 1) {
+      float m = st.mrow[u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(sA[i], sB[i]));
+      st.mrow[u] = m;
+    } else {
+      float pA[4], pB[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pA[i] = __builtin_amdgcn_exp2f(MODE == 2 ? sA[i] - st.mrow[u] : sA[i]);
+        pB[i] = __builtin_amdgcn_exp2f(MODE == 2 ? sB[i] - st.mrow[u] : sB[i]);
+      }
+      u32x4_t pk;
+      pk[0] = pack_bf16x2(pA[0], pA[1]);
+      pk[1] = pack_bf16x2(pA[2], pA[3]);
+      pk[2] = pack_bf16x2(pB[0], pB[1]);
+      pk[3] = pack_bf16x2(pB[2], pB[3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+      st.o0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA0, pb, st.o0[u], 0, 0, 0);
+      st.o1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA1, pb, st.o1[u], 0, 0, 0);
+      st.os[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, st.os[u], 0, 0, 0);
+    }
+  }
+}
+
+template <int MODE, bool MASKED, int QT>
+__device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, const unsigned char* tabb,
+                                          const int* kp, int zone, const bf16x8_t& ones, QState<QT>& st) {
+  const int nclean = L.N >> 5;   // steps whose 32 keys are all real
+  for (int p = 0; p < L.NP; ++p) {
+    if (MASKED || p >= nclean) attn_step<MODE, true, QT>(p, B, L, tabb, kp, zone, ones, st);
+    else attn_step<MODE, false, QT>(p, B, L, tabb, kp, zone, ones, st);
+  }
+}
+
+// The wave's QT query tiles jt, jt + 8, ... of one window.
+template <int QT>
+__device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const Win& wi, int jt,
+                                           const unsigned char* B, const unsigned char* smem, const int* kp) {
+  const WinGeo& g = a.geo;
+  const int lane = threadIdx.x & 63;
+  const int fr = lane & 15, g4 = lane >> 4;
+  const int mhw = g.Mh * g.Mw;
+  const int N = L.N;
+  const unsigned char* tabb = smem + L.off_tab;
+  const int zone = 16 * (L.TS4 - 1);
+  float kmax2 = 0.f, tmx = 0.f;
+  int masked = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    kmax2 = fmaxf(kmax2, reinterpret_cast<const float*>(B + L.off_red)[i]);
+    masked |= reinterpret_cast<const int*>(B + L.off_red)[8 + i];
+    tmx = fmaxf(tmx, reinterpret_cast<const float*>(smem + L.off_redt)[i]);
+  }
+  const float kmax = sqrtf(kmax2);
+  const bf16_t* Qg = reinterpret_cast<const bf16_t*>(a.q) + (int64_t)wi.mem * N * 32;
+
+  QState<QT> st;
+  bool need = false;
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int qs = 16 * (jt + 8 * u) + fr;
+    const bool valid = qs < N;
+    u32x4_t qv = {0u, 0u, 0u, 0u};
+    st.qlab[u] = kNoQueryLab;
+    int f = 0;
+    if (valid) {
+      qv = *reinterpret_cast<const u32x4_t*>(Qg + qs * 32 + g4 * 8);
+      const int m = qs >> 2, i = qs & 3;
+      const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
+      const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
+      f = (4 * aa + i) * L.Rp + kh * L.Rw + kw;
+      st.qlab[u] = slot_label_at(g, wi.rt0 + 4 * aa + i, wi.rh0 + kh, wi.rw0 + kw);
+    }
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float lo = bflo(qv[e]), hi = bfhi(qv[e]);
+      if (L.qscale != 1.0f) {
+        lo *= L.qscale;
+        hi *= L.qscale;
+        qv[e] = pack_bf16x2(lo, hi);
+        lo = bflo(qv[e]);
+        hi = bfhi(qv[e]);
+      }
+      sq += lo * lo + hi * hi;
+    }
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    need |= valid && !(sqrtf(sq) * kmax + tmx <= 90.f);
+    st.q[u] = __builtin_bit_cast(bf16x8_t, qv);
+    st.qaddr[u] = 16 * (L.A - f);
+    st.mrow[u] = -INFINITY;
+    st.o0[u] = st.o1[u] = st.os[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  const bool wave_max_pass = L.force_max || __builtin_amdgcn_ballot_w64(need) != 0;
+  if (!wave_max_pass) {
+    if (masked) attn_pass<0, true, QT>(B, L, tabb, kp, zone, ones, st);
+    else attn_pass<0, false, QT>(B, L, tabb, kp, zone, ones, st);
+  } else {
+    if (masked) attn_pass<1, true, QT>(B, L, tabb, kp, zone, ones, st);
+    else attn_pass<1, false, QT>(B, L, tabb, kp, zone, ones, st);
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      float m = st.mrow[u];
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      st.mrow[u] = (m == -INFINITY) ? 0.f : m;
+    }
+    if (masked) attn_pass<2, true, QT>(B, L, tabb, kp, zone, ones, st);
+    else attn_pass<2, false, QT>(B, L, tabb, kp, zone, ones, st);
+  }
+
+  // lane: query fr, output features 8 g4 .. + 7 of head h
+  bf16_t* Og = reinterpret_cast<bf16_t*>(a.o);
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int qs = 16 * (jt + 8 * u) + fr;
+    if (qs >= N) continue;
+    const float inv = 1.0f / st.os[u][0];
+    u32x4_t pk;
+    pk[0] = pack_bf16x2(st.o0[u][0] * inv, st.o0[u][1] * inv);
+    pk[1] = pack_bf16x2(st.o0[u][2] * inv, st.o0[u][3] * inv);
+    pk[2] = pack_bf16x2(st.o1[u][0] * inv, st.o1[u][1] * inv);
+    pk[3] = pack_bf16x2(st.o1[u][2] * inv, st.o1[u][3] * inv);
+    *reinterpret_cast<u32x4_t*>(Og + ((int64_t)wi.w * N + qs) * a.C + wi.h * 32 + 8 * g4) = pk;
+  }
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(kThreads) attn_mfma_kernel(const AttnArgs a, const A5 L) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-aware order: consecutive runs (which share boundary windows) go to
+  // workgroups on the same XCD and its L2.
+  int b = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int64_t t0 = (int64_t)b * L.TT / G, t1 = (int64_t)(b + 1) * L.TT / G;
+  if (t0 >= t1) return;
+  const int it0 = (int)(t0 / L.QTT), it1 = (int)((t1 - 1) / L.QTT);
+
+  // key-group table offsets (the same for every window), as (A, B) pairs per step and lane group
+  int* kp = reinterpret_cast<int*>(smem + L.off_kp);
+  {
+    const WinGeo& g = a.geo;
+    const int mhw = g.Mh * g.Mw;
+    for (int m = tid; m < L.NP * 8; m += kThreads) {
+      int off = 0;
+      if (m < L.N / 4) {
+        const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
+        const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
+        off = 16 * (4 * aa * L.Rp + kh * L.Rw + kw);
+      }
+      const int p = m >> 3, s = m & 7;
+      kp[2 * (4 * p + (s & 3)) + (s >> 2)] = off;
+    }
+  }
+  Pref pf;
+  Win cur = window_of(a, L, it0);
+  pref_load(pf, a, L, cur.mem);
+  build_table(a, L, cur.h, smem);
+  int h_tab = cur.h;
+  pref_store(pf, L, smem + L.off_buf);
+  stage_labels(a, L, cur, smem + L.off_buf);
+  __syncthreads();
+
+  for (int it = it0; it <= it1; ++it) {
+    const int buf = L.NB == 2 ? ((it - it0) & 1) : 0;
+    const unsigned char* B = smem + L.off_buf + (size_t)buf * L.buf_bytes;
+    const bool more = it < it1;
+    Win nxt{};
+    if (more) {
+      nxt = window_of(a, L, it + 1);
+      pref_load(pf, a, L, nxt.mem);
+    }
+    // this workgroup's tiles of the window: [j0, j1); wave wv takes the ones
+    // congruent to wv + it (mod 8), rotating the remainder over the waves
+    const int64_t base = (int64_t)it * L.QTT;
+    const int j0 = (int)((t0 > base ? t0 : base) - base);
+    const int j1 = (int)((t1 < base + L.QTT ? t1 : base + L.QTT) - base);
+    const int k0 = (wv - it) & 7;
+    const int cnt = j0 + k0 < j1 ? (j1 - j0 - k0 + 7) >> 3 : 0;
+    switch (cnt) {
+      case 1: attn_tiles<1>(a, L, cur, j0 + k0, B, smem, kp); break;
+      case 2: attn_tiles<2>(a, L, cur, j0 + k0, B, smem, kp); break;
+      case 3: attn_tiles<3>(a, L, cur, j0 + k0, B, smem, kp); break;
+      case 4: attn_tiles<4>(a, L, cur, j0 + k0, B, smem, kp); break;
+      default: break;
+    }
+    if (more) {
+      const bool new_head = nxt.h != h_tab;
+      if (L.NB == 1 || new_head) __syncthreads();
+      if (new_head) {
+        build_table(a, L, nxt.h, smem);
+        h_tab = nxt.h;
+      }
+      unsigned char* Bn = smem + L.off_buf + (size_t)(L.NB == 2 ? (buf ^ 1) : 0) * L.buf_bytes;
+      pref_store(pf, L, Bn);
+      stage_labels(a, L, nxt, Bn);
+      cur = nxt;
+    }
+    __syncthreads();
+  }
+}
+
+namespace {
+
+bool plan_a5(const AttnArgs& a, A5& L) {
+  L = A5{};
+  L.N = a.N;
+  L.NP = (a.N + 31) / 32;
+  L.NPAD = 32 * L.NP;
+  L.QTT = (a.N + 15) / 16;
+  const int kc = L.NPAD / 8;                 // V^T chunks per row
+  L.pitch_v = kc + ((4 - kc) % 16 + 16) % 16;
+  L.R = a.rel.R;
+  L.Rw = a.rel.Rw;
+  L.TD = a.rel.rows / a.rel.R;               // 2 P0 - 1
+  L.TH = a.rel.R / a.rel.Rw;                 // 2 Mh0 - 1
+  L.Rp = L.R + ((4 - L.R) % 16 + 16) % 16;
+  L.A = (L.TD / 2) * L.Rp + (L.TH / 2) * L.Rw + L.Rw / 2;
+  L.TS4 = L.TD * L.Rp + 1;
+  L.nW = (int)a.nW;
+  L.heads = a.heads;
+  L.fdRp = make_fastdiv((uint32_t)L.Rp);
+  L.fdRw = make_fastdiv((uint32_t)L.Rw);
+  L.fdnW = make_fastdiv((uint32_t)L.nW);
+  L.fdKC = make_fastdiv((uint32_t)kc);
+  L.TT = a.nW * a.heads * (int64_t)L.QTT;
+  L.qscale = a.q_scaled ? 1.0f : kLog2e / sqrtf((float)a.d);
+  L.force_max = a.force_max;
+  if (L.TS4 > kTabIter * kThreads) return false;
+  size_t off = 0;
+  L.off_kp = (uint32_t)off;
+  off += (size_t)L.NP * 8 * 4;
+  L.off_redt = (uint32_t)off;
+  off += 64;
+  off = (off + 15) & ~(size_t)15;
+  L.off_tab = (uint32_t)off;
+  off += (size_t)L.TS4 * 16;
+  L.off_buf = (uint32_t)off;
+  size_t bb = (size_t)L.NPAD * 64;
+  L.off_v = (uint32_t)bb;
+  bb += (size_t)32 * L.pitch_v * 16;
+  L.off_lp = (uint32_t)bb;
+  bb += (size_t)L.NP * 8 * 4;
+  L.off_red = (uint32_t)bb;
+  bb += 64;
+  L.buf_bytes = (uint32_t)((bb + 15) & ~(size_t)15);
+  L.NB = off + 2 * (size_t)L.buf_bytes <= kLdsMax ? 2 : 1;
+  return off + (size_t)L.NB * L.buf_bytes <= kLdsMax;
+}
+
+size_t a5_lds(const A5& L) { return (size_t)L.off_buf + (size_t)L.NB * L.buf_bytes; }
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+}  // namespace
+
+size_t attention_workspace_bytes(const RelTab&, int) { return 0; }
+
+bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
+  if (dt != VSWIN_BF16 || a.d != 32 || a.mask_m100) return false;
+  if (a.geo.P % 4 != 0 || a.N > kMfmaMaxN) return false;
+  // every group of 4 temporal positions (kt = 4a .. 4a+3) of every window
+  // must share its temporal label and temporal pad status
+  const WinGeo& g = a.geo;
+  auto tkey = [&](int rt) {
+    int ot = rt + g.st;
+    if (ot >= g.Tp) ot -= g.Tp;
+    const int pad = (ot >= g.T && !g.pad_visible) ? 1 : 0;
+    return axis_label(rt, g.Tp, g.P, g.st) * 2 + pad;
+  };
+  for (int rt = 0; rt < g.Tp; rt += 4)
+    for (int i = 1; i < 4; ++i)
+      if (tkey(rt + i) != tkey(rt)) return false;
+  A5 L;
+  return plan_a5(a, L);
+}
+
+hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
+  const int64_t items = a.nW * a.heads;
+  if (items <= 0) return hipSuccess;
+  AttnArgs ak = a;
+  // VSWIN_ATTN_MAXPASS=1 makes every wave take the exact row-max pass (test
+  // hook for the path that otherwise runs only for very large logits).
+  if (const char* f = getenv("VSWIN_ATTN_MAXPASS")) ak.force_max = atoi(f) != 0;
+  A5 L;
+  if (!plan_a5(ak, L)) return hipErrorInvalidValue;
+  const size_t lds = a5_lds(L);
+  const int per_cu = lds <= kLdsMax / 2 ? 2 : 1;
+  const int64_t cap = (int64_t)cu_count() * per_cu;
+  const int64_t G = cap < L.TT ? cap : L.TT;
+  hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  attn_mfma_kernel<<<dim3((unsigned)G), dim3(kThreads), lds, st>>>(ak, L);
+  return hipGetLastError();
+}
+
+}  // namespace vswin

@@ -91,6 +91,7 @@ struct QkvParams {
   const bf16_t* bias;   // (3C) or NULL
   bf16_t *q, *k, *v;    // (nW*heads, N, d); v transposed (nW*heads, d, N) when vt
   int vt;
+  float qscale;         // multiplier of q after the bias
   int M;                // window rows (nW * N)
   int heads, d;
   FastDiv fd;           // division by d
@@ -229,6 +230,7 @@ __global__ void __launch_bounds__(kQkvThreads) qkv_proj_kernel(QkvParams pr) {
     // lane: token row wm*32 + mt*16 + fr, features 32 j + 8 g .. + 7 of q/k/v,
     // stored at ((w*heads + h)*N + t)*d + e = w*N*C + (h*N*d + e) + t*d
     bf16_t* out = wn == 0 ? pr.q : (wn == 1 ? pr.k : pr.v);
+    const float osc = wn == 0 ? pr.qscale : 1.0f;
     int coff[NT / 2];
 #pragma unroll
     for (int j = 0; j < NT / 2; ++j) {
@@ -248,8 +250,8 @@ __global__ void __launch_bounds__(kQkvThreads) qkv_proj_kernel(QkvParams pr) {
         unpack8(bq[j], b8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v8[i] = acc[mt][2 * j][i] + b8[i];
-          v8[4 + i] = acc[mt][2 * j + 1][i] + b8[4 + i];
+          v8[i] = (acc[mt][2 * j][i] + b8[i]) * osc;
+          v8[4 + i] = (acc[mt][2 * j + 1][i] + b8[4 + i]) * osc;
         }
         *reinterpret_cast<u32x4_t*>(row + coff[j]) = pack8(v8);
       }
@@ -424,11 +426,11 @@ bool winproj_supported(vswin_dtype dt, int C, int d, int N, int vt) {
 }
 
 hipError_t qkv_proj(const void* x, const void* ln_g, const void* ln_b, float eps, int ln, const void* W,
-                    const void* bias, void* q, void* k, void* v, int vt, int64_t M, int C, int heads, int d,
-                    const WinGeo& geo, hipStream_t st) {
+                    const void* bias, void* q, void* k, void* v, int vt, float qscale, int64_t M, int C, int heads,
+                    int d, const WinGeo& geo, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   QkvParams pr{(const bf16_t*)x, (const bf16_t*)ln_g, (const bf16_t*)ln_b, eps, ln, (const bf16_t*)W,
-               (const bf16_t*)bias, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v, vt, (int)M, heads, d, make_fastdiv((uint32_t)d), geo};
+               (const bf16_t*)bias, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v, vt, qscale, (int)M, heads, d, make_fastdiv((uint32_t)d), geo};
   const unsigned grid = (unsigned)((M + kQkvBM - 1) / kQkvBM);
   auto go = [&](auto kern, size_t lds) -> hipError_t {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

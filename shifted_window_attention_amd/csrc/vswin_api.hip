@@ -186,10 +186,13 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
   void* v = ws + p.off_v;
   const int vt = p.fast ? 1 : 0;
   if (ga && winproj_supported(p.dt, p.C, p.d, p.N, vt)) {
-    HIPCHECK(qkv_proj(ga->x, ga->g, ga->b, ga->eps, ga->ln, w->qkv_w, w->qkv_b, q, k, v, vt, p.Lp, p.C, p.heads,
-                      p.d, p.geo, st),
+    // the MFMA attention takes q pre-multiplied by log2(e) / sqrt(d)
+    const float qscale = p.fast ? 1.4426950408889634f / sqrtf((float)p.d) : 1.0f;
+    HIPCHECK(qkv_proj(ga->x, ga->g, ga->b, ga->eps, ga->ln, w->qkv_w, w->qkv_b, q, k, v, vt, qscale, p.Lp, p.C,
+                      p.heads, p.d, p.geo, st),
              "qkv projection");
-    const AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags, ws + p.off_tab);
+    AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags, ws + p.off_tab);
+    a.q_scaled = p.fast ? 1 : 0;
     if (p.fast) HIPCHECK(attention_mfma(a, st), "attention (mfma)");
     else HIPCHECK(attention_generic(p.dt, a, st), "attention (generic)");
     HIPCHECK(out_proj(xw, w->proj_w, w->proj_b, to_zh ? residual : nullptr, out, p.Lp, p.C, p.geo, st),

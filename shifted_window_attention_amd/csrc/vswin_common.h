@@ -19,6 +19,7 @@ struct FastDiv {
   uint32_t d, mul, s;
 };
 inline FastDiv make_fastdiv(uint32_t d) {
+  if (d == 0) return FastDiv{0u, 0u, 0u};   // placeholder for an empty extent; never divided by
   uint32_t s = 0;
   while (((uint64_t)1 << s) < d) ++s;
   const uint64_t mul = ((((uint64_t)1 << s) - d) << 32) / d + 1;

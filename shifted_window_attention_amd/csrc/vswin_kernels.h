@@ -58,13 +58,14 @@ bool gemm_can_gather(vswin_dtype dt, int K);
 // out: o rows * W^T + bias scattered to token rows; with `res` the output is
 // fp32 z = res + ..., else bf16.
 bool winproj_supported(vswin_dtype dt, int C, int d, int N, int vt);
+// q is multiplied by qscale after the bias (1 for plain q).
 hipError_t qkv_proj(const void* x, const void* ln_g, const void* ln_b, float eps, int ln, const void* W,
-                    const void* bias, void* q, void* k, void* v, int vt, int64_t M, int C, int heads, int d,
-                    const WinGeo& geo, hipStream_t st);
+                    const void* bias, void* q, void* k, void* v, int vt, float qscale, int64_t M, int C, int heads,
+                    int d, const WinGeo& geo, hipStream_t st);
 hipError_t out_proj(const void* o, const void* W, const void* bias, const void* res, void* out, int64_t M, int C,
                     const WinGeo& geo, hipStream_t st);
 
-// --- attention (k_attention.hip) ------------------------------------------
+// --- attention (k_attention.hip: generic; k_attn_mfma.hip: MFMA) -----------
 struct AttnArgs {
   const void *q, *k, *v;   // (nW, heads, N, d) of dtype; MFMA path: v is (nW, heads, d, N)
   const void* table;       // (rows, heads) of dtype
@@ -76,6 +77,7 @@ struct AttnArgs {
   int use_mask;            // some window may need the region mask
   int mask_m100;           // additive -100 instead of exclusion
   int force_max;           // MFMA kernel: always take the exact row-max pass
+  int q_scaled;            // MFMA kernel: q already multiplied by log2(e) / sqrt(d)
 };
 // bytes of scratch the MFMA kernel needs for its prepared tables
 size_t attention_workspace_bytes(const RelTab& rel, int heads);
