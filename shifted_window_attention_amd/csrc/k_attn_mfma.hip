@@ -2,14 +2,14 @@
 //   per (window, head): S = q k^T / sqrt(d) + B[idx(i, j)], masked pairs
 //   excluded, P = softmax_j(S), O = P v, heads concatenated as h*32 + e.
 //
-// Work split.  The query tiles (16 queries) of all (head, window) items form
-// one list, head-major; each workgroup (8 waves, one per CU) takes an equal
-// contiguous run of it and walks the items in that run.  A window's K and
-// V^T are staged once in LDS for all of the run's tiles of that window, and
-// the next window's K/V is fetched into registers while the current one is
-// computed (two LDS buffers when they fit, else one), so staging latency
-// hides behind compute.  Waves own tiles, not steps: inside a window no
-// barrier is needed.
+// Work split.  The workgroups (W waves, one per CU) are divided among the
+// heads; the query tiles (16 queries) of one head's windows form a list and
+// each of that head's workgroups takes an equal contiguous run of it, so a
+// workgroup builds its head's bias table once.  A window's K and V^T are
+// staged once in LDS for all of the run's tiles of that window, and the next
+// window's K/V is fetched into registers while the current one is computed
+// (two LDS buffers when they fit, else one), so staging latency hides behind
+// compute.  Waves own tiles, not steps: inside a window no barrier is needed.
 //
 // Scores.  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (k = head_dim): a lane
 // holds 4 keys of one query, so all per-query state stays in the lane.
@@ -29,6 +29,8 @@
 //     sums come from a third MFMA against a ones operand.  V^T rows are read
 //     in pair order (d = 8g + 4p + i), so a lane ends with 8 consecutive
 //     output features and writes one 16-byte vector per query.
+//   * A query slot's table offset and region label are those of its key
+//     group (the same 4 temporal positions), read from the per-window tables.
 //
 // LDS layouts (bank-conflict free 16-byte fragment reads):
 //   K      key rows of 64 bytes; chunk c of row r at chunk c ^ ((r >> 2) & 3).
@@ -47,13 +49,22 @@ namespace vswin {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kPref = 4;          // K and V^T 16-byte chunks per thread and window (N <= 512)
-constexpr int kTabIter = 8;       // table 4-tuples per thread (<= 4096 entries)
+constexpr int kMaxWaves = 16;
+constexpr int kMaxTab = 4096;     // table 4-tuples held in LDS at most
 constexpr int kDummyLab = 0x7fff0000;
-constexpr int kNoQueryLab = 0x7ffe0000;
 constexpr size_t kLdsMax = 160 * 1024;
+
+// W waves per workgroup; a wave carries at most QTM query tiles of a window.
+template <int W, int QTM>
+struct Cfg {
+  static constexpr int kWaves = W;
+  static constexpr int kQTM = QTM;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kPref = (4 * kMfmaMaxN + kThreads - 1) / kThreads;   // 16-byte K (and V^T) chunks per thread
+  static constexpr int kTabIter = (kMaxTab + kThreads - 1) / kThreads;
+  static_assert((kMfmaMaxN / 16 + W - 1) / W <= QTM, "a wave's tiles of one window exceed QTM");
+  static_assert(W <= kMaxWaves, "too many waves");
+};
 
 struct A5 {
   int N, NPAD, NP, QTT, NB;
@@ -61,15 +72,15 @@ struct A5 {
   int Rp, Rw, R, TD, TH, A;   // table: temporal stride R', row stride, true R, extents, query base
   int TS4;                    // 4-tuples incl. the -inf one at the end
   int nW, heads;
-  FastDiv fdRp, fdRw, fdnW, fdKC;
-  int64_t TT;                 // tiles in the whole list
+  FastDiv fdRp, fdRw, fdKC;
   float qscale;               // multiplier applied to q on load (1 when pre-scaled)
   int force_max;
   uint32_t off_kp, off_tab, off_redt, off_buf, buf_bytes, off_v, off_lp, off_red;
 };
 
+template <class CF>
 struct Pref {
-  u32x4_t k[kPref], v[kPref];
+  u32x4_t k[CF::kPref], v[CF::kPref];
 };
 
 template <int QT>
@@ -82,17 +93,16 @@ struct QState {
 };
 
 struct Win {          // one (head, window) item
-  int h, w, mem;      // head, window, item index in q/k/v (w * heads + h)
+  int w, mem;         // window, item index in q/k/v (w * heads + h)
   int rt0, rh0, rw0;  // rolled origin of the window
 };
 
-__device__ __forceinline__ Win window_of(const AttnArgs& a, const A5& L, int it) {
+__device__ __forceinline__ Win window_of(const AttnArgs& a, const A5& L, int h, int w) {
   const WinGeo& g = a.geo;
   Win r;
-  r.h = (int)fdiv((uint32_t)it, L.fdnW);
-  r.w = it - r.h * L.nW;
-  r.mem = r.w * L.heads + r.h;
-  const int wr = r.w - (int)fdiv((uint32_t)r.w, g.fnws) * g.nws;
+  r.w = w;
+  r.mem = w * L.heads + h;
+  const int wr = w - (int)fdiv((uint32_t)w, g.fnws) * g.nws;
   const int wt = (int)fdiv((uint32_t)wr, g.fwpl);
   const int rem = wr - wt * g.nwh * g.nww;
   const int wh = (int)fdiv((uint32_t)rem, g.fnww);
@@ -117,15 +127,19 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// index of key group m's entry in the (step, lane group) pair layout
+__device__ __forceinline__ int pair_slot(int m) { return 2 * (4 * (m >> 3) + (m & 3)) + ((m >> 2) & 1); }
+
 // ---- staging -------------------------------------------------------------
-__device__ __forceinline__ void pref_load(Pref& pf, const AttnArgs& a, const A5& L, int mem) {
+template <class CF>
+__device__ __forceinline__ void pref_load(Pref<CF>& pf, const AttnArgs& a, const A5& L, int mem) {
   const int tid = opaque_tid();
   const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)mem * L.N * 32;
   const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)mem * L.N * 32;
   const int kcpr = L.NPAD >> 3;
 #pragma unroll
-  for (int j = 0; j < kPref; ++j) {
-    const int c = tid + kThreads * j;
+  for (int j = 0; j < CF::kPref; ++j) {
+    const int c = tid + CF::kThreads * j;
     const int r = c >> 2;
     pf.k[j] = r < L.N ? *reinterpret_cast<const u32x4_t*>(Kg + r * 32 + (c & 3) * 8) : u32x4_t{0u, 0u, 0u, 0u};
     const int d = (int)fdiv((uint32_t)c, L.fdKC);
@@ -150,13 +164,14 @@ __device__ __forceinline__ void pref_load(Pref& pf, const AttnArgs& a, const A5&
   }
 }
 
-__device__ __forceinline__ void pref_store(const Pref& pf, const A5& L, unsigned char* B) {
+template <class CF>
+__device__ __forceinline__ void pref_store(const Pref<CF>& pf, const A5& L, unsigned char* B) {
   const int tid = opaque_tid();
   const int kcpr = L.NPAD >> 3;
   float km = 0.f;
 #pragma unroll
-  for (int j = 0; j < kPref; ++j) {
-    const int c = tid + kThreads * j;
+  for (int j = 0; j < CF::kPref; ++j) {
+    const int c = tid + CF::kThreads * j;
     const int r = c >> 2, q = c & 3;
     if (r < L.NPAD) *reinterpret_cast<u32x4_t*>(B + r * 64 + ((q ^ ((r >> 2) & 3)) << 4)) = pf.k[j];
     float sq = 0.f;
@@ -186,6 +201,7 @@ __device__ __forceinline__ void pref_store(const Pref& pf, const A5& L, unsigned
 }
 
 // region labels of the window's key groups and whether they differ
+template <class CF>
 __device__ __forceinline__ void stage_labels(const AttnArgs& a, const A5& L, const Win& wi, unsigned char* B) {
   const WinGeo& g = a.geo;
   const int tid = opaque_tid();
@@ -193,7 +209,7 @@ __device__ __forceinline__ void stage_labels(const AttnArgs& a, const A5& L, con
   const int lab0 = slot_label_at(g, wi.rt0, wi.rh0, wi.rw0);
   int* lp = reinterpret_cast<int*>(B + L.off_lp);
   bool differs = false;
-  for (int m = tid; m < L.NP * 8; m += kThreads) {
+  for (int m = tid; m < L.NP * 8; m += CF::kThreads) {
     int lab = kDummyLab;
     if (m < L.N / 4) {
       const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
@@ -201,21 +217,37 @@ __device__ __forceinline__ void stage_labels(const AttnArgs& a, const A5& L, con
       lab = slot_label_at(g, wi.rt0 + 4 * aa, wi.rh0 + kh, wi.rw0 + kw);
       differs |= lab != lab0;
     }
-    const int p = m >> 3, s = m & 7;
-    lp[2 * (4 * p + (s & 3)) + (s >> 2)] = lab;
+    lp[pair_slot(m)] = lab;
   }
   const uint64_t any = __builtin_amdgcn_ballot_w64(differs);
-  if ((tid & 63) == 0) reinterpret_cast<int*>(B + L.off_red)[8 + (tid >> 6)] = any != 0;
+  if ((tid & 63) == 0) reinterpret_cast<int*>(B + L.off_red)[kMaxWaves + (tid >> 6)] = any != 0;
+}
+
+// key-group table offsets (bytes; the same for every window)
+template <class CF>
+__device__ __forceinline__ void stage_offsets(const AttnArgs& a, const A5& L, int* kp) {
+  const WinGeo& g = a.geo;
+  const int mhw = g.Mh * g.Mw;
+  for (int m = (int)threadIdx.x; m < L.NP * 8; m += CF::kThreads) {
+    int off = 0;
+    if (m < L.N / 4) {
+      const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
+      const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
+      off = 16 * (4 * aa * L.Rp + kh * L.Rw + kw);
+    }
+    kp[pair_slot(m)] = off;
+  }
 }
 
 // fp32 4-tuples of the head's column of the table, scaled by log2(e)
+template <class CF>
 __device__ __forceinline__ void build_table(const AttnArgs& a, const A5& L, int h, unsigned char* smem) {
   const int tid = opaque_tid();
   const bf16_t* T = reinterpret_cast<const bf16_t*>(a.table);
-  uint16_t raw[kTabIter][4];
+  uint16_t raw[CF::kTabIter][4];
 #pragma unroll
-  for (int j = 0; j < kTabIter; ++j) {
-    const int x = tid + kThreads * j;
+  for (int j = 0; j < CF::kTabIter; ++j) {
+    const int x = tid + CF::kThreads * j;
     const int dtr = (int)fdiv((uint32_t)x, L.fdRp);
     const int rem = x - dtr * L.Rp;
     const int dhr = (int)fdiv((uint32_t)rem, L.fdRw);
@@ -231,8 +263,8 @@ __device__ __forceinline__ void build_table(const AttnArgs& a, const A5& L, int 
   f32x4_t* tab = reinterpret_cast<f32x4_t*>(smem + L.off_tab);
   float tm = 0.f;
 #pragma unroll
-  for (int j = 0; j < kTabIter; ++j) {
-    const int x = tid + kThreads * j;
+  for (int j = 0; j < CF::kTabIter; ++j) {
+    const int x = tid + CF::kThreads * j;
     if (x < L.TS4) {
       f32x4_t v;
 #pragma unroll
@@ -251,10 +283,11 @@ __device__ __forceinline__ void build_table(const AttnArgs& a, const A5& L, int 
 // ---- one 32-key step for the wave's QT tiles --------------------------------
 //   MODE 0: P = exp2(x); 1: row max of x only; 2: P = exp2(x - max).
 //   SEL: per key group, masked / dummy groups read the -inf 4-tuple.
+//   gk / lk: this step's key-group offsets / labels for lane group g4.
 template <int MODE, bool SEL, int QT>
 __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict__ B, const A5& L,
-                                          const unsigned char* __restrict__ tabb, const int* __restrict__ kp,
-                                          int zone, const bf16x8_t& ones, QState<QT>& st) {
+                                          const unsigned char* __restrict__ tabb, int2 gk, int2 lk, int zone,
+                                          const bf16x8_t& ones, QState<QT>& st) {
   const int lane = threadIdx.x & 63;
   const int fr = lane & 15, g4 = lane >> 4;
   const int sw = (fr >> 2) & 3;
@@ -267,9 +300,7 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
     vA0 = *reinterpret_cast<const bf16x8_t*>(vb + d0 * L.pitch_v * 16);
     vA1 = *reinterpret_cast<const bf16x8_t*>(vb + (d0 + 4) * L.pitch_v * 16);
   }
-  const int2 gk = reinterpret_cast<const int2*>(kp)[4 * p + g4];
-  int2 lk = {0, 0};
-  if (SEL) lk = reinterpret_cast<const int2*>(B + L.off_lp)[4 * p + g4];
+  f32x4_t tA[QT], tB[QT];
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     int adA = st.qaddr[u] + gk.x, adB = st.qaddr[u] + gk.y;
@@ -277,10 +308,15 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
       adA = (lk.x == st.qlab[u]) ? adA : zone;
       adB = (lk.y == st.qlab[u]) ? adB : zone;
     }
-    const f32x4_t tA = *reinterpret_cast<const f32x4_t*>(tabb + adA);
-    const f32x4_t tB = *reinterpret_cast<const f32x4_t*>(tabb + adB);
-    const f32x4_t sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, st.q[u], tA, 0, 0, 0);
-    const f32x4_t sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, st.q[u], tB, 0, 0, 0);
+    tA[u] = *reinterpret_cast<const f32x4_t*>(tabb + adA);
+    tB[u] = *reinterpret_cast<const f32x4_t*>(tabb + adB);
+  }
+  // every LDS read of the step is in flight before the first MFMA waits on one
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const f32x4_t sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, st.q[u], tA[u], 0, 0, 0);
+    const f32x4_t sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, st.q[u], tB[u], 0, 0, 0);
     if (MODE == 1) {
       float m = st.mrow[u];
 #pragma unroll
@@ -306,63 +342,83 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
   }
 }
 
+// One pass over the keys; the next step's offsets and labels are read a step ahead.
 template <int MODE, bool MASKED, int QT>
 __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, const unsigned char* tabb,
-                                          const int* kp, int zone, const bf16x8_t& ones, QState<QT>& st) {
+                                          const int2* kp2, int zone, const bf16x8_t& ones, QState<QT>& st) {
+  const int g4 = (threadIdx.x & 63) >> 4;
+  const int2* lp2 = reinterpret_cast<const int2*>(B + L.off_lp);
   const int nclean = L.N >> 5;   // steps whose 32 keys are all real
+  int2 gk = kp2[g4];
+  int2 lk = lp2[g4];
   for (int p = 0; p < L.NP; ++p) {
-    if (MASKED || p >= nclean) attn_step<MODE, true, QT>(p, B, L, tabb, kp, zone, ones, st);
-    else attn_step<MODE, false, QT>(p, B, L, tabb, kp, zone, ones, st);
+    const int pn = p + 1 < L.NP ? p + 1 : p;
+    const int2 gkn = kp2[4 * pn + g4];
+    const int2 lkn = lp2[4 * pn + g4];
+    if (MASKED || p >= nclean) attn_step<MODE, true, QT>(p, B, L, tabb, gk, lk, zone, ones, st);
+    else attn_step<MODE, false, QT>(p, B, L, tabb, gk, lk, zone, ones, st);
+    gk = gkn;
+    lk = lkn;
   }
 }
 
-// The wave's QT query tiles jt, jt + 8, ... of one window.
-template <int QT>
-__device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const Win& wi, int jt,
-                                           const unsigned char* B, const unsigned char* smem, const int* kp) {
-  const WinGeo& g = a.geo;
+// The wave's QT query tiles jt, jt + W, ... of one window.
+// q rows of a wave's tiles of one window (loaded a window ahead)
+template <class CF>
+struct QPre {
+  u32x4_t q[CF::kQTM];
+};
+
+template <class CF>
+__device__ __forceinline__ void q_load(QPre<CF>& qp, const AttnArgs& a, const A5& L, int mem, int jt, int cnt) {
   const int lane = threadIdx.x & 63;
   const int fr = lane & 15, g4 = lane >> 4;
-  const int mhw = g.Mh * g.Mw;
+  const bf16_t* Qg = reinterpret_cast<const bf16_t*>(a.q) + (int64_t)mem * L.N * 32;
+#pragma unroll
+  for (int u = 0; u < CF::kQTM; ++u) {
+    const int qs = 16 * (jt + CF::kWaves * u) + fr;
+    qp.q[u] = (u < cnt && qs < L.N) ? *reinterpret_cast<const u32x4_t*>(Qg + qs * 32 + g4 * 8)
+                                    : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+template <class CF, int QT>
+__device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const Win& wi, int h, int jt,
+                                           const QPre<CF>& qp, const unsigned char* B, const unsigned char* smem,
+                                           const int* kp) {
+  const int lane = threadIdx.x & 63;
+  const int fr = lane & 15, g4 = lane >> 4;
   const int N = L.N;
   const unsigned char* tabb = smem + L.off_tab;
   const int zone = 16 * (L.TS4 - 1);
+  const int* lp = reinterpret_cast<const int*>(B + L.off_lp);
   float kmax2 = 0.f, tmx = 0.f;
   int masked = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < CF::kWaves; ++i) {
     kmax2 = fmaxf(kmax2, reinterpret_cast<const float*>(B + L.off_red)[i]);
-    masked |= reinterpret_cast<const int*>(B + L.off_red)[8 + i];
+    masked |= reinterpret_cast<const int*>(B + L.off_red)[kMaxWaves + i];
     tmx = fmaxf(tmx, reinterpret_cast<const float*>(smem + L.off_redt)[i]);
   }
   const float kmax = sqrtf(kmax2);
-  const bf16_t* Qg = reinterpret_cast<const bf16_t*>(a.q) + (int64_t)wi.mem * N * 32;
 
   QState<QT> st;
   bool need = false;
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
-    const int qs = 16 * (jt + 8 * u) + fr;
+    const int qs = 16 * (jt + CF::kWaves * u) + fr;
     const bool valid = qs < N;
-    u32x4_t qv = {0u, 0u, 0u, 0u};
-    st.qlab[u] = kNoQueryLab;
-    int f = 0;
-    if (valid) {
-      qv = *reinterpret_cast<const u32x4_t*>(Qg + qs * 32 + g4 * 8);
-      const int m = qs >> 2, i = qs & 3;
-      const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
-      const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
-      f = (4 * aa + i) * L.Rp + kh * L.Rw + kw;
-      st.qlab[u] = slot_label_at(g, wi.rt0 + 4 * aa + i, wi.rh0 + kh, wi.rw0 + kw);
-    }
+    // the query's key group: same table base (plus its temporal index) and label
+    const int ps = pair_slot(qs >> 2);
+    st.qaddr[u] = 16 * L.A - kp[ps] - 16 * (qs & 3) * L.Rp;
+    st.qlab[u] = lp[ps];
+    u32x4_t qv = qp.q[u];
     float sq = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float lo = bflo(qv[e]), hi = bfhi(qv[e]);
       if (L.qscale != 1.0f) {
-        lo *= L.qscale;
-        hi *= L.qscale;
-        qv[e] = pack_bf16x2(lo, hi);
+        qv[e] = pack_bf16x2(lo * L.qscale, hi * L.qscale);
         lo = bflo(qv[e]);
         hi = bfhi(qv[e]);
       }
@@ -372,20 +428,20 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
     sq += __shfl_xor(sq, 32);
     need |= valid && !(sqrtf(sq) * kmax + tmx <= 90.f);
     st.q[u] = __builtin_bit_cast(bf16x8_t, qv);
-    st.qaddr[u] = 16 * (L.A - f);
     st.mrow[u] = -INFINITY;
     st.o0[u] = st.o1[u] = st.os[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   bf16x8_t ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  const int2* kp2 = reinterpret_cast<const int2*>(kp);
   const bool wave_max_pass = L.force_max || __builtin_amdgcn_ballot_w64(need) != 0;
   if (!wave_max_pass) {
-    if (masked) attn_pass<0, true, QT>(B, L, tabb, kp, zone, ones, st);
-    else attn_pass<0, false, QT>(B, L, tabb, kp, zone, ones, st);
+    if (masked) attn_pass<0, true, QT>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<0, false, QT>(B, L, tabb, kp2, zone, ones, st);
   } else {
-    if (masked) attn_pass<1, true, QT>(B, L, tabb, kp, zone, ones, st);
-    else attn_pass<1, false, QT>(B, L, tabb, kp, zone, ones, st);
+    if (masked) attn_pass<1, true, QT>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<1, false, QT>(B, L, tabb, kp2, zone, ones, st);
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       float m = st.mrow[u];
@@ -393,15 +449,15 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
       m = fmaxf(m, __shfl_xor(m, 32));
       st.mrow[u] = (m == -INFINITY) ? 0.f : m;
     }
-    if (masked) attn_pass<2, true, QT>(B, L, tabb, kp, zone, ones, st);
-    else attn_pass<2, false, QT>(B, L, tabb, kp, zone, ones, st);
+    if (masked) attn_pass<2, true, QT>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<2, false, QT>(B, L, tabb, kp2, zone, ones, st);
   }
 
   // lane: query fr, output features 8 g4 .. + 7 of head h
   bf16_t* Og = reinterpret_cast<bf16_t*>(a.o);
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
-    const int qs = 16 * (jt + 8 * u) + fr;
+    const int qs = 16 * (jt + CF::kWaves * u) + fr;
     if (qs >= N) continue;
     const float inv = 1.0f / st.os[u][0];
     u32x4_t pk;
@@ -409,84 +465,95 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
     pk[1] = pack_bf16x2(st.o0[u][2] * inv, st.o0[u][3] * inv);
     pk[2] = pack_bf16x2(st.o1[u][0] * inv, st.o1[u][1] * inv);
     pk[3] = pack_bf16x2(st.o1[u][2] * inv, st.o1[u][3] * inv);
-    *reinterpret_cast<u32x4_t*>(Og + ((int64_t)wi.w * N + qs) * a.C + wi.h * 32 + 8 * g4) = pk;
+    *reinterpret_cast<u32x4_t*>(Og + ((int64_t)wi.w * N + qs) * a.C + h * 32 + 8 * g4) = pk;
   }
+}
+
+template <class CF>
+__device__ __forceinline__ void tiles_dispatch(int cnt, const AttnArgs& a, const A5& L, const Win& wi, int h, int jt,
+                                               const QPre<CF>& qp, const unsigned char* B, const unsigned char* smem,
+                                               const int* kp) {
+  if constexpr (CF::kQTM >= 4) {
+    if (cnt == 4) { attn_tiles<CF, 4>(a, L, wi, h, jt, qp, B, smem, kp); return; }
+  }
+  if constexpr (CF::kQTM >= 3) {
+    if (cnt == 3) { attn_tiles<CF, 3>(a, L, wi, h, jt, qp, B, smem, kp); return; }
+  }
+  if (cnt == 2) { attn_tiles<CF, 2>(a, L, wi, h, jt, qp, B, smem, kp); return; }
+  if (cnt == 1) attn_tiles<CF, 1>(a, L, wi, h, jt, qp, B, smem, kp);
+}
+
+// this workgroup's tiles of window w are [j0, j1) of the window's list; wave
+// wv takes the ones congruent to wv + w (mod W), rotating the remainder
+struct TileRun {
+  int jt, cnt;
+};
+template <class CF>
+__device__ __forceinline__ TileRun tile_run(int wv, int w, int64_t t0, int64_t t1, int QTT) {
+  const int64_t base = (int64_t)w * QTT;
+  const int j0 = (int)((t0 > base ? t0 : base) - base);
+  const int j1 = (int)((t1 < base + QTT ? t1 : base + QTT) - base);
+  const int k0 = (wv - w % CF::kWaves + CF::kWaves) % CF::kWaves;
+  TileRun r;
+  r.jt = j0 + k0;
+  r.cnt = j0 + k0 < j1 ? (j1 - j0 - k0 + CF::kWaves - 1) / CF::kWaves : 0;
+  return r;
 }
 
 }  // namespace
 
-__global__ void __launch_bounds__(kThreads) attn_mfma_kernel(const AttnArgs a, const A5 L) {
+template <class CF>
+__global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs a, const A5 L) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int tid = threadIdx.x;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // XCD-aware order: consecutive runs (which share boundary windows) go to
-  // workgroups on the same XCD and its L2.
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  // XCD-aware order: consecutive runs (same head, neighbouring windows) go
+  // to workgroups on the same XCD and its L2.
   int b = blockIdx.x;
   const int G = gridDim.x;
   if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
-  const int64_t t0 = (int64_t)b * L.TT / G, t1 = (int64_t)(b + 1) * L.TT / G;
+  // this workgroup's head and its run of the head's tile list
+  const int h = (int)(((int64_t)(b + 1) * L.heads - 1) / G);
+  const int gb = (int)((int64_t)h * G / L.heads);
+  const int gh = (int)((int64_t)(h + 1) * G / L.heads) - gb;
+  const int64_t th = (int64_t)L.nW * L.QTT;
+  const int64_t t0 = (int64_t)(b - gb) * th / gh, t1 = (int64_t)(b - gb + 1) * th / gh;
   if (t0 >= t1) return;
-  const int it0 = (int)(t0 / L.QTT), it1 = (int)((t1 - 1) / L.QTT);
+  const int w0 = (int)(t0 / L.QTT), w1 = (int)((t1 - 1) / L.QTT);
 
-  // key-group table offsets (the same for every window), as (A, B) pairs per step and lane group
   int* kp = reinterpret_cast<int*>(smem + L.off_kp);
-  {
-    const WinGeo& g = a.geo;
-    const int mhw = g.Mh * g.Mw;
-    for (int m = tid; m < L.NP * 8; m += kThreads) {
-      int off = 0;
-      if (m < L.N / 4) {
-        const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
-        const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
-        off = 16 * (4 * aa * L.Rp + kh * L.Rw + kw);
-      }
-      const int p = m >> 3, s = m & 7;
-      kp[2 * (4 * p + (s & 3)) + (s >> 2)] = off;
-    }
-  }
-  Pref pf;
-  Win cur = window_of(a, L, it0);
-  pref_load(pf, a, L, cur.mem);
-  build_table(a, L, cur.h, smem);
-  int h_tab = cur.h;
-  pref_store(pf, L, smem + L.off_buf);
-  stage_labels(a, L, cur, smem + L.off_buf);
+  stage_offsets<CF>(a, L, kp);
+  Pref<CF> pf;
+  QPre<CF> qcur, qnext;
+  Win cur = window_of(a, L, h, w0);
+  TileRun run = tile_run<CF>(wv, w0, t0, t1, L.QTT);
+  q_load<CF>(qcur, a, L, cur.mem, run.jt, run.cnt);
+  pref_load<CF>(pf, a, L, cur.mem);
+  build_table<CF>(a, L, h, smem);
+  pref_store<CF>(pf, L, smem + L.off_buf);
+  stage_labels<CF>(a, L, cur, smem + L.off_buf);
   __syncthreads();
 
-  for (int it = it0; it <= it1; ++it) {
-    const int buf = L.NB == 2 ? ((it - it0) & 1) : 0;
+  for (int w = w0; w <= w1; ++w) {
+    const int buf = L.NB == 2 ? ((w - w0) & 1) : 0;
     const unsigned char* B = smem + L.off_buf + (size_t)buf * L.buf_bytes;
-    const bool more = it < it1;
+    const bool more = w < w1;
     Win nxt{};
+    TileRun rnext{};
     if (more) {
-      nxt = window_of(a, L, it + 1);
-      pref_load(pf, a, L, nxt.mem);
+      nxt = window_of(a, L, h, w + 1);
+      rnext = tile_run<CF>(wv, w + 1, t0, t1, L.QTT);
+      q_load<CF>(qnext, a, L, nxt.mem, rnext.jt, rnext.cnt);
+      pref_load<CF>(pf, a, L, nxt.mem);
     }
-    // this workgroup's tiles of the window: [j0, j1); wave wv takes the ones
-    // congruent to wv + it (mod 8), rotating the remainder over the waves
-    const int64_t base = (int64_t)it * L.QTT;
-    const int j0 = (int)((t0 > base ? t0 : base) - base);
-    const int j1 = (int)((t1 < base + L.QTT ? t1 : base + L.QTT) - base);
-    const int k0 = (wv - it) & 7;
-    const int cnt = j0 + k0 < j1 ? (j1 - j0 - k0 + 7) >> 3 : 0;
-    switch (cnt) {
-      case 1: attn_tiles<1>(a, L, cur, j0 + k0, B, smem, kp); break;
-      case 2: attn_tiles<2>(a, L, cur, j0 + k0, B, smem, kp); break;
-      case 3: attn_tiles<3>(a, L, cur, j0 + k0, B, smem, kp); break;
-      case 4: attn_tiles<4>(a, L, cur, j0 + k0, B, smem, kp); break;
-      default: break;
-    }
+    tiles_dispatch<CF>(run.cnt, a, L, cur, h, run.jt, qcur, B, smem, kp);
     if (more) {
-      const bool new_head = nxt.h != h_tab;
-      if (L.NB == 1 || new_head) __syncthreads();
-      if (new_head) {
-        build_table(a, L, nxt.h, smem);
-        h_tab = nxt.h;
-      }
+      if (L.NB == 1) __syncthreads();
       unsigned char* Bn = smem + L.off_buf + (size_t)(L.NB == 2 ? (buf ^ 1) : 0) * L.buf_bytes;
-      pref_store(pf, L, Bn);
-      stage_labels(a, L, nxt, Bn);
+      pref_store<CF>(pf, L, Bn);
+      stage_labels<CF>(a, L, nxt, Bn);
       cur = nxt;
+      run = rnext;
+      qcur = qnext;
     }
     __syncthreads();
   }
@@ -513,17 +580,15 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.heads = a.heads;
   L.fdRp = make_fastdiv((uint32_t)L.Rp);
   L.fdRw = make_fastdiv((uint32_t)L.Rw);
-  L.fdnW = make_fastdiv((uint32_t)L.nW);
   L.fdKC = make_fastdiv((uint32_t)kc);
-  L.TT = a.nW * a.heads * (int64_t)L.QTT;
   L.qscale = a.q_scaled ? 1.0f : kLog2e / sqrtf((float)a.d);
   L.force_max = a.force_max;
-  if (L.TS4 > kTabIter * kThreads) return false;
+  if (L.TS4 > kMaxTab || a.heads > 256) return false;
   size_t off = 0;
   L.off_kp = (uint32_t)off;
   off += (size_t)L.NP * 8 * 4;
   L.off_redt = (uint32_t)off;
-  off += 64;
+  off += 4 * kMaxWaves;
   off = (off + 15) & ~(size_t)15;
   L.off_tab = (uint32_t)off;
   off += (size_t)L.TS4 * 16;
@@ -534,7 +599,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.off_lp = (uint32_t)bb;
   bb += (size_t)L.NP * 8 * 4;
   L.off_red = (uint32_t)bb;
-  bb += 64;
+  bb += 8 * kMaxWaves;
   L.buf_bytes = (uint32_t)((bb + 15) & ~(size_t)15);
   L.NB = off + 2 * (size_t)L.buf_bytes <= kLdsMax ? 2 : 1;
   return off + (size_t)L.NB * L.buf_bytes <= kLdsMax;
@@ -547,6 +612,21 @@ int cu_count() {
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
   return n;
+}
+
+template <class CF>
+hipError_t launch_cfg(const AttnArgs& ak, const A5& L, hipStream_t st) {
+  const size_t lds = a5_lds(L);
+  const int per_cu = lds <= kLdsMax / 2 ? 2 : 1;
+  const int64_t tiles = ak.nW * ak.heads * (int64_t)L.QTT;
+  const int64_t cap = (int64_t)cu_count() * per_cu;
+  int64_t G = cap < tiles ? cap : tiles;
+  if (G < ak.heads) G = ak.heads;   // every head gets a workgroup
+  hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<CF>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  attn_mfma_kernel<CF><<<dim3((unsigned)G), dim3(CF::kThreads), lds, st>>>(ak, L);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -572,6 +652,10 @@ bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
   return plan_a5(a, L);
 }
 
+#ifndef VSWIN_ATTN_WAVES
+#define VSWIN_ATTN_WAVES 8
+#endif
+
 hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
   const int64_t items = a.nW * a.heads;
   if (items <= 0) return hipSuccess;
@@ -581,15 +665,13 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
   if (const char* f = getenv("VSWIN_ATTN_MAXPASS")) ak.force_max = atoi(f) != 0;
   A5 L;
   if (!plan_a5(ak, L)) return hipErrorInvalidValue;
-  const size_t lds = a5_lds(L);
-  const int per_cu = lds <= kLdsMax / 2 ? 2 : 1;
-  const int64_t cap = (int64_t)cu_count() * per_cu;
-  const int64_t G = cap < L.TT ? cap : L.TT;
-  hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
-  attn_mfma_kernel<<<dim3((unsigned)G), dim3(kThreads), lds, st>>>(ak, L);
-  return hipGetLastError();
+#if VSWIN_ATTN_WAVES == 16
+  return launch_cfg<Cfg<16, 2>>(ak, L, st);
+#elif VSWIN_ATTN_WAVES == 12
+  return launch_cfg<Cfg<12, 3>>(ak, L, st);
+#else
+  return launch_cfg<Cfg<8, 4>>(ak, L, st);
+#endif
 }
 
 }  // namespace vswin
