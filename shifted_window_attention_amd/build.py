@@ -32,7 +32,7 @@ def _hipcc() -> str:
 
 # per-file extras: the attention kernel keeps MFMA operands/results in VGPRs
 # (no accumulation-register round trips between score tiles and VALU work)
-EXTRA = {"k_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"k_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "k_mlp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

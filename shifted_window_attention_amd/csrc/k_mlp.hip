@@ -226,6 +226,231 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const float* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// C = 96: the whole MLP weight set (W1 384x96 and W2 96x384, 147 KB) stays in
+// LDS for the kernel's lifetime; one workgroup per CU, and each wave owns
+// 16-token tiles from start to end with no barrier after the weight load.
+//   * LN2 in registers: lane (token fr, group g) holds z^ columns
+//     32j + 8g .. +7 (j = 0..2), which are at once its k-chunks of the fc1
+//     operand and its output columns of the residual.
+//   * fc1 runs on 32 hidden units at a time as a pair of 16-row MFMA tiles
+//     whose W1 rows are read in pair order (hidden 8g + 4p + i at tile row
+//     4g + i), so a lane ends with hidden units 8g .. 8g + 7 of its token:
+//     after bias and GELU that is exactly the lane's k-chunk of the fc2
+//     operand, and the hidden activations never leave registers.
+//   * fc2 accumulates 6 output tiles (W2 rows in pair order too), so the
+//     lane's 8 consecutive output columns go out as one 16-byte store.
+// LDS: W1 rows of 192 B with chunk q of row r at q ^ ((r >> 2) & 3); W2 rows
+// of 768 B with chunk q at q ^ (r & 15): conflict-free 16-byte reads.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ int pair_row(int f) {
+  return (f & ~31) | (((f >> 2) & 1) << 4) | (((f >> 3) & 3) << 2) | (f & 3);
+}
+__device__ __forceinline__ void unpack8(const u32x4_t& v, float f[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bflo(v[e]);
+    f[2 * e + 1] = bfhi(v[e]);
+  }
+}
+__device__ __forceinline__ u32x4_t pack8(const float f[8]) {
+  u32x4_t v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+  return v;
+}
+
+constexpr int kMlpWaves = 8;
+constexpr int kMlpThreads = 64 * kMlpWaves;
+constexpr int kMlpC = 96, kMlpHid = 4 * kMlpC;
+constexpr size_t kMlpW1 = (size_t)kMlpHid * kMlpC * 2;
+// Phi(x) = (1 + erf(x / sqrt 2)) / 2 by linear interpolation in a table of
+// kPhiN points over [-kPhiX, kPhiX): h = 2 kPhiX / kPhiN = 0.0176, error
+// <= max|Phi''| h^2 / 8 = 0.242 * 3.1e-4 / 8 < 1e-5 inside the range and
+// < 3.4e-6 (the tail mass) outside it, where the index is clamped.
+constexpr int kPhiN = 512;
+constexpr float kPhiX = 4.5f;
+constexpr size_t kMlpVec = kMlpHid * 2 + 3 * kMlpC * 2;                 // b1, LN2 gamma / beta, fc2 bias
+constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + kPhiN * 8;
+
+struct ZTile {
+  float z[3][8];     // columns 32j + 8g .. + 7 of token fr
+};
+
+__device__ __forceinline__ void ztile_load(ZTile& zt, const float* __restrict__ zh, int64_t L, int64_t t) {
+  const int lane = threadIdx.x & 63, fr = lane & 15, g = lane >> 4;
+  const int64_t tok = t * 16 + fr;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    if (tok < L) {
+      const float4 a = *reinterpret_cast<const float4*>(zh + tok * kMlpC + 32 * j + 8 * g);
+      const float4 b = *reinterpret_cast<const float4*>(zh + tok * kMlpC + 32 * j + 8 * g + 4);
+      zt.z[j][0] = a.x; zt.z[j][1] = a.y; zt.z[j][2] = a.z; zt.z[j][3] = a.w;
+      zt.z[j][4] = b.x; zt.z[j][5] = b.y; zt.z[j][6] = b.z; zt.z[j][7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zt.z[j][e] = 0.f;
+    }
+  }
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __restrict__ zh, const bf16_t* __restrict__ g2,
+                                                               const bf16_t* __restrict__ b2ln,
+                                                               const bf16_t* __restrict__ W1, const bf16_t* __restrict__ b1,
+                                                               const bf16_t* __restrict__ W2, const bf16_t* __restrict__ bo,
+                                                               bf16_t* __restrict__ y, int64_t L, float eps) {
+  constexpr int C = kMlpC, HID = kMlpHid;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* W1s = lds;                 // HID rows x 192 B
+  unsigned char* W2s = lds + kMlpW1;        // C rows x 768 B
+  bf16_t* b1s = reinterpret_cast<bf16_t*>(lds + 2 * kMlpW1);
+  bf16_t* vecs = b1s + HID;                 // LN2 gamma, beta, fc2 bias (C each)
+  float2* phi = reinterpret_cast<float2*>(lds + 2 * kMlpW1 + kMlpVec);   // (Phi(x_i), Phi(x_i+1) - Phi(x_i))
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15, g = lane >> 4;
+  const int64_t ntiles = (L + 15) / 16;
+  const int64_t nw = (int64_t)gridDim.x * kMlpWaves;
+  int64_t t = (int64_t)blockIdx.x * kMlpWaves + wave;
+
+  // first tile's z^ rows, then the weights (one pass, all threads)
+  ZTile cur;
+  ztile_load(cur, zh, L, t);
+  {
+    // all 16-byte chunks of W1 and W2 in flight at once, then into LDS
+    constexpr int NCH = HID * (C / 8) / kMlpThreads;   // 9 chunks of each matrix per thread
+    static_assert(NCH * kMlpThreads == HID * (C / 8), "weight staging shape");
+    u32x4_t w1v[NCH], w2v[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * kMlpThreads;
+      w1v[i] = *reinterpret_cast<const u32x4_t*>(W1 + (int64_t)c * 8);
+      w2v[i] = *reinterpret_cast<const u32x4_t*>(W2 + (int64_t)c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * kMlpThreads;
+      const int f1 = c / (C / 8), q1 = c - f1 * (C / 8), r1 = pair_row(f1);
+      *reinterpret_cast<u32x4_t*>(W1s + r1 * (C * 2) + ((q1 ^ ((r1 >> 2) & 3)) << 4)) = w1v[i];
+      const int f2 = c / (HID / 8), q2 = c - f2 * (HID / 8), r2 = pair_row(f2);
+      *reinterpret_cast<u32x4_t*>(W2s + r2 * (HID * 2) + ((q2 ^ (r2 & 15)) << 4)) = w2v[i];
+    }
+  }
+  for (int c = tid; c < HID / 8; c += kMlpThreads)
+    *reinterpret_cast<u32x4_t*>(b1s + c * 8) =
+        b1 ? *reinterpret_cast<const u32x4_t*>(b1 + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  for (int i = tid; i < kPhiN; i += kMlpThreads) {
+    const float h = 2.0f * kPhiX / kPhiN;
+    const float x0 = -kPhiX + h * i, x1 = x0 + h;
+    const float p0 = 0.5f * (1.0f + erff(x0 * 0.70710678118654752f));
+    const float p1 = 0.5f * (1.0f + erff(x1 * 0.70710678118654752f));
+    phi[i] = make_float2(p0, p1 - p0);
+  }
+  for (int c = tid; c < 3 * (C / 8); c += kMlpThreads) {
+    const int which = c / (C / 8), q = c - which * (C / 8);
+    const bf16_t* src = which == 0 ? g2 : (which == 1 ? b2ln : bo);
+    *reinterpret_cast<u32x4_t*>(vecs + which * C + q * 8) =
+        src ? *reinterpret_cast<const u32x4_t*>(src + q * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+
+  const int swz1 = (fr >> 2) & 3;   // W1 rows 32c + 16p + fr: ((row >> 2) & 3) = (fr >> 2) & 3
+  for (; t < ntiles; t += nw) {
+    ZTile nxt;
+    if (t + nw < ntiles) ztile_load(nxt, zh, L, t + nw);
+    // ---- LN2 of the lane's token (4 lanes share a token: xor 16, 32)
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += cur.z[j][e];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    const float mean = s * (1.0f / C);
+    float q2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float dd = cur.z[j][e] - mean;
+        q2 += dd * dd;
+      }
+    q2 += __shfl_xor(q2, 16);
+    q2 += __shfl_xor(q2, 32);
+    const float rstd = 1.0f / sqrtf(q2 * (1.0f / C) + eps);
+    bf16x8_t af[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      float gg[8], bb[8], a[8];
+      unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 32 * j + 8 * g), gg);
+      unpack8(*reinterpret_cast<const u32x4_t*>(vecs + C + 32 * j + 8 * g), bb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = (cur.z[j][e] - mean) * rstd * gg[e] + bb[e];
+      af[j] = __builtin_bit_cast(bf16x8_t, pack8(a));
+    }
+    // ---- fc1 -> GELU -> fc2 over 12 chunks of 32 hidden units
+    f32x4_t acc2[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) acc2[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int ch = 0; ch < HID / 32; ++ch) {
+      bf16x8_t w1f[2][3], w2f[6];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const unsigned char* row = W1s + (32 * ch + 16 * p + fr) * (C * 2);
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk) w1f[p][kk] = *reinterpret_cast<const bf16x8_t*>(row + (((4 * kk + g) ^ swz1) << 4));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 6; ++nt) {
+        const int r = 16 * nt + fr;
+        w2f[nt] = *reinterpret_cast<const bf16x8_t*>(W2s + r * (HID * 2) + (((4 * ch + g) ^ (r & 15)) << 4));
+      }
+      const u32x4_t hb = *reinterpret_cast<const u32x4_t*>(b1s + 32 * ch + 8 * g);
+      f32x4_t a1[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) a1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1f[p][kk], af[kk], a1[p], 0, 0, 0);
+      float hbf[8], h[8];
+      unpack8(hb, hbf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // GELU(x) = x Phi(x), Phi from the table
+        const float x = (i < 4 ? a1[0][i] : a1[1][i - 4]) + hbf[i];
+        const float u = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f), 0.0f,
+                                                (float)kPhiN - 0.5f);
+        const int k = (int)u;
+        const float2 e = phi[k];
+        h[i] = x * __builtin_fmaf(__builtin_amdgcn_fractf(u), e.y, e.x);
+      }
+      const bf16x8_t hf = __builtin_bit_cast(bf16x8_t, pack8(h));
+#pragma unroll
+      for (int nt = 0; nt < 6; ++nt) acc2[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[nt], hf, acc2[nt], 0, 0, 0);
+    }
+    // ---- y = z^ + fc2 + b2: lane holds columns 32j + 8g .. + 7 of token fr
+    const int64_t tok = t * 16 + fr;
+    if (tok < L) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        float ob[8], o[8];
+        unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 2 * C + 32 * j + 8 * g), ob);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] = cur.z[j][i] + acc2[2 * j][i] + ob[i];
+          o[4 + i] = cur.z[j][4 + i] + acc2[2 * j + 1][i] + ob[4 + i];
+        }
+        *reinterpret_cast<u32x4_t*>(y + tok * C + 32 * j + 8 * g) = pack8(o);
+      }
+    }
+    cur = nxt;
+  }
+}
+
 bool mlp_fused_supported(vswin_dtype dt, int C, int hid) {
   return dt == VSWIN_BF16 && hid == 4 * C && (C == 96 || C == 128);
 }
@@ -234,11 +459,21 @@ hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const vo
                      const void* W2, const void* bo, void* y, int64_t L, int C, float eps, hipStream_t st) {
   if (L <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((L + 63) / 64);
-  if (C == 96)
-    hipLaunchKernelGGL(mlp_fused_kernel<96>, dim3(blocks), dim3(256), 0, st, zh, (const bf16_t*)g2,
-                       (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1, (const bf16_t*)W2,
-                       (const bf16_t*)bo, (bf16_t*)y, L, eps);
-  else if (C == 128)
+  if (C == 96) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+      ncu = 256;
+    const int64_t tiles = (L + 15) / 16;
+    int64_t grid = (tiles + kMlpWaves - 1) / kMlpWaves;
+    if (grid > ncu) grid = ncu;
+    hipError_t e = hipFuncSetAttribute((const void*)mlp_wave_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kMlpLds);
+    if (e != hipSuccess) return e;
+    mlp_wave_kernel<<<dim3((unsigned)grid), dim3(kMlpThreads), kMlpLds, st>>>(
+        zh, (const bf16_t*)g2, (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1, (const bf16_t*)W2,
+        (const bf16_t*)bo, (bf16_t*)y, L, eps);
+  } else if (C == 128)
     hipLaunchKernelGGL(mlp_fused_kernel<128>, dim3(blocks), dim3(256), 0, st, zh, (const bf16_t*)g2,
                        (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1, (const bf16_t*)W2,
                        (const bf16_t*)bo, (bf16_t*)y, L, eps);
