@@ -32,7 +32,9 @@ def _hipcc() -> str:
 
 # per-file extras: the attention kernel keeps MFMA operands/results in VGPRs
 # (no accumulation-register round trips between score tiles and VALU work)
-EXTRA = {"k_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "k_mlp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# MFMA accumulators in ordinary VGPRs (no AGPR copies) for the MFMA kernels
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"k_attn_mfma.hip": _VGPR_FORM, "k_mlp.hip": _VGPR_FORM, "k_winproj.hip": _VGPR_FORM}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -72,7 +72,7 @@ struct A5 {
   int Rp, Rw, R, TD, TH, A;   // table: temporal stride R', row stride, true R, extents, query base
   int TS4;                    // 4-tuples incl. the -inf one at the end
   int nW, heads;
-  FastDiv fdRp, fdRw, fdKC;
+  FastDiv fdRp, fdRw, fdKC, fdH;
   float qscale;               // multiplier applied to q on load (1 when pre-scaled)
   int force_max;
   uint32_t off_kp, off_tab, off_redt, off_buf, buf_bytes, off_v, off_lp, off_red;
@@ -239,45 +239,71 @@ __device__ __forceinline__ void stage_offsets(const AttnArgs& a, const A5& L, in
   }
 }
 
-// fp32 4-tuples of the head's column of the table, scaled by log2(e)
+// fp32 4-tuples of the head's column of the table, scaled by log2(e).
+// The raw (rows, heads) table is read with coalesced 16-byte loads; this
+// head's column goes to an LDS scratch (the K/V buffer region, still free
+// in the prologue), and the 4-tuples are built from there.  Two barriers.
 template <class CF>
 __device__ __forceinline__ void build_table(const AttnArgs& a, const A5& L, int h, unsigned char* smem) {
   const int tid = opaque_tid();
   const bf16_t* T = reinterpret_cast<const bf16_t*>(a.table);
-  uint16_t raw[CF::kTabIter][4];
+  float* col = reinterpret_cast<float*>(smem + L.off_buf);
+  const int E = L.TD * L.R * L.heads;
+  const int nch = (E + 7) / 8;
+  constexpr int BATCH = 8;
+  for (int c0 = 0; c0 < nch; c0 += BATCH * CF::kThreads) {
+    u32x4_t v[BATCH];
 #pragma unroll
-  for (int j = 0; j < CF::kTabIter; ++j) {
-    const int x = tid + CF::kThreads * j;
-    const int dtr = (int)fdiv((uint32_t)x, L.fdRp);
-    const int rem = x - dtr * L.Rp;
-    const int dhr = (int)fdiv((uint32_t)rem, L.fdRw);
-    const int dwr = rem - dhr * L.Rw;
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = c0 + i * CF::kThreads + tid;
+      v[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (8 * c + 8 <= E) {
+        v[i] = *reinterpret_cast<const u32x4_t*>(T + 8 * c);
+      } else if (c < nch) {
+        for (int e = 0; e < 8 && 8 * c + e < E; ++e) {
+          const uint32_t x = T[8 * c + e];
+          v[i][e >> 1] |= (e & 1) ? (x << 16) : x;
+        }
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int dt = dtr + i;
-      const bool ok = x < L.TS4 - 1 && rem < L.R && dt < L.TD;
-      const int row = (L.TD - 1 - dt) * L.R + (L.TH - 1 - dhr) * L.Rw + (L.Rw - 1 - dwr);
-      raw[j][i] = ok ? T[row * L.heads + h] : (uint16_t)0;
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = c0 + i * CF::kThreads + tid;
+      if (c < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = 8 * c + e;
+          const int r = (int)fdiv((uint32_t)idx, L.fdH);
+          if (idx < E && idx - r * L.heads == h)
+            col[r] = ((e & 1) ? bfhi(v[i][e >> 1]) : bflo(v[i][e >> 1])) * kLog2e;
+        }
+      }
     }
   }
+  __syncthreads();
   f32x4_t* tab = reinterpret_cast<f32x4_t*>(smem + L.off_tab);
   float tm = 0.f;
-#pragma unroll
-  for (int j = 0; j < CF::kTabIter; ++j) {
-    const int x = tid + CF::kThreads * j;
-    if (x < L.TS4) {
-      f32x4_t v;
+  for (int x = tid; x < L.TS4; x += CF::kThreads) {
+    f32x4_t v = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (x < L.TS4 - 1) {
+      const int dtr = (int)fdiv((uint32_t)x, L.fdRp);
+      const int rem = x - dtr * L.Rp;
+      const int dhr = (int)fdiv((uint32_t)rem, L.fdRw);
+      const int dwr = rem - dhr * L.Rw;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[i] = bf2f(raw[j][i]) * kLog2e;
+        const int dt = dtr + i;
+        const bool ok = rem < L.R && dt < L.TD;
+        const int row = ok ? (L.TD - 1 - dt) * L.R + (L.TH - 1 - dhr) * L.Rw + (L.Rw - 1 - dwr) : 0;
+        v[i] = ok ? col[row] : 0.f;
         tm = fmaxf(tm, fabsf(v[i]));
       }
-      if (x == L.TS4 - 1) v = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      tab[x] = v;
     }
+    tab[x] = v;
   }
   tm = wave_max(tm);
   if ((tid & 63) == 0) reinterpret_cast<float*>(smem + L.off_redt)[tid >> 6] = tm;
+  __syncthreads();   // the scratch column is overwritten by the first window's K/V
 }
 
 // ---- one 32-key step for the wave's QT tiles --------------------------------
@@ -561,6 +587,12 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
 
 namespace {
 
+// the K/V buffers, which also hold the table column scratch in the prologue
+size_t a5_lds(const A5& L) {
+  const size_t bufs = (size_t)L.NB * L.buf_bytes, col = (size_t)L.TD * L.R * 4;
+  return (size_t)L.off_buf + (bufs > col ? bufs : col);
+}
+
 bool plan_a5(const AttnArgs& a, A5& L) {
   L = A5{};
   L.N = a.N;
@@ -581,6 +613,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.fdRp = make_fastdiv((uint32_t)L.Rp);
   L.fdRw = make_fastdiv((uint32_t)L.Rw);
   L.fdKC = make_fastdiv((uint32_t)kc);
+  L.fdH = make_fastdiv((uint32_t)a.heads);
   L.qscale = a.q_scaled ? 1.0f : kLog2e / sqrtf((float)a.d);
   L.force_max = a.force_max;
   if (L.TS4 > kMaxTab || a.heads > 256) return false;
@@ -602,16 +635,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   bb += 8 * kMaxWaves;
   L.buf_bytes = (uint32_t)((bb + 15) & ~(size_t)15);
   L.NB = off + 2 * (size_t)L.buf_bytes <= kLdsMax ? 2 : 1;
-  return off + (size_t)L.NB * L.buf_bytes <= kLdsMax;
-}
-
-size_t a5_lds(const A5& L) { return (size_t)L.off_buf + (size_t)L.NB * L.buf_bytes; }
-
-int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
-  return n;
+  return a5_lds(L) <= kLdsMax;
 }
 
 template <class CF>
@@ -619,11 +643,10 @@ hipError_t launch_cfg(const AttnArgs& ak, const A5& L, hipStream_t st) {
   const size_t lds = a5_lds(L);
   const int per_cu = lds <= kLdsMax / 2 ? 2 : 1;
   const int64_t tiles = ak.nW * ak.heads * (int64_t)L.QTT;
-  const int64_t cap = (int64_t)cu_count() * per_cu;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
   int64_t G = cap < tiles ? cap : tiles;
   if (G < ak.heads) G = ak.heads;   // every head gets a workgroup
-  hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<CF>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = ensure_dynamic_lds((const void*)attn_mfma_kernel<CF>, lds);
   if (e != hipSuccess) return e;
   attn_mfma_kernel<CF><<<dim3((unsigned)G), dim3(CF::kThreads), lds, st>>>(ak, L);
   return hipGetLastError();

@@ -460,15 +460,11 @@ hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const vo
   if (L <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((L + 63) / 64);
   if (C == 96) {
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-      ncu = 256;
+    const int ncu = device_cu_count();
     const int64_t tiles = (L + 15) / 16;
     int64_t grid = (tiles + kMlpWaves - 1) / kMlpWaves;
     if (grid > ncu) grid = ncu;
-    hipError_t e = hipFuncSetAttribute((const void*)mlp_wave_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kMlpLds);
+    hipError_t e = ensure_dynamic_lds((const void*)mlp_wave_kernel, kMlpLds);
     if (e != hipSuccess) return e;
     mlp_wave_kernel<<<dim3((unsigned)grid), dim3(kMlpThreads), kMlpLds, st>>>(
         zh, (const bf16_t*)g2, (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1, (const bf16_t*)W2,

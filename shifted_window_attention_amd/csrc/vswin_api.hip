@@ -5,9 +5,46 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <new>
+#include <unordered_map>
+#include <utility>
 
 #include "vswin_kernels.h"
+
+namespace vswin {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::unordered_map<int, int> counts;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = counts.find(dev);
+  if (it != counts.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  counts[dev] = n;
+  return n;
+}
+
+hipError_t ensure_dynamic_lds(const void* kern, size_t bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kern, dev);
+  auto it = done.find(key);
+  if (it != done.end() && it->second >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[key] = bytes;
+  return e;
+}
+
+}  // namespace vswin
 
 using namespace vswin;
 

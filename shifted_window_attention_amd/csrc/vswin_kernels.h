@@ -5,6 +5,12 @@
 
 namespace vswin {
 
+// --- launch helpers (vswin_api.hip) ---------------------------------------
+// compute units of the current device (queried once per device)
+int device_cu_count();
+// raise `kern`'s dynamic LDS limit to `bytes` once per (kernel, device, size)
+hipError_t ensure_dynamic_lds(const void* kern, size_t bytes);
+
 // --- permutation / normalisation (k_layout.hip) ---------------------------
 hipError_t ln_gather(vswin_dtype dt, const void* x, const void* g, const void* b, void* y, int64_t slots,
                      int C, float eps, const WinGeo& geo, int apply_ln, hipStream_t st);

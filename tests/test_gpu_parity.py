@@ -276,6 +276,41 @@ def test_block_is_deterministic():
     assert torch.equal(a, b)
 
 
+def test_block_pair_graph_replay_matches_eager():
+    """The block pair captured in a HIP graph gives, on every replay, the
+    bits of the eager calls (the library records only kernel launches)."""
+    say("graph replay of the stage-1 block pair vs eager")
+    x, params = synth.gen_workload(2)
+    s = synth.WORKLOADS[2].shape
+    xt = dev(x, "bf16")
+    p = [dev_params(q, "bf16") for q in params]
+    plan = vs.vswin_plan_query(vs.make_desc(s.B, s.T, s.H, s.W, s.C, s.heads, s.window, s.shift))
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    y1, y2 = torch.empty_like(xt), torch.empty_like(xt)
+
+    def pair(st):
+        vs.vswin_block_fwd(xt, p[0], s.heads, s.window, (0, 0, 0), out=y1, workspace=ws, stream=st)
+        vs.vswin_block_fwd(y1, p[1], s.heads, s.window, s.shift, out=y2, workspace=ws, stream=st)
+
+    pair(None)
+    torch.cuda.synchronize()
+    ref1, ref2 = y1.clone(), y2.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pair(torch.cuda.current_stream())
+    other = dev(np.random.default_rng(5).standard_normal(x.shape).astype(np.float32), "bf16")
+    for r in range(3):
+        y1.zero_()
+        y2.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y1, ref1) and torch.equal(y2, ref2), f"replay {r} differs from the eager result"
+        # eager work between replays, on the same workspace
+        vs.vswin_block_fwd(other, p[1], s.heads, s.window, s.shift, workspace=ws)
+        torch.cuda.synchronize()
+
+
 def test_empty_batch_on_gpu():
     say("empty batch")
     x = torch.empty((0, 16, 14, 14, 96), dtype=torch.bfloat16, device="cuda")
