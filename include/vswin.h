@@ -62,7 +62,13 @@ enum {
   VSWIN_F_CLAMP_STRICT = 2u,
   /* Add -100 to masked scores (the published code's value) instead of
    * excluding the pair.  Default off: masked pairs get weight exactly 0.   */
-  VSWIN_F_MASK_M100 = 4u
+  VSWIN_F_MASK_M100 = 4u,
+  /* vswin_attention_fwd only (other entry points ignore it): the workspace
+   * already holds the prepared bias tables of this rpb_table and geometry,
+   * left there by an earlier vswin_attention_fwd call on the same workspace,
+   * so they are not rebuilt.  For repeated calls with fixed weights; the
+   * result is undefined if the table or the workspace changed since.      */
+  VSWIN_F_TABLES_READY = 8u
 };
 
 /* One block's geometry.  Tokens are (B, T, H, W, C), contiguous, channels
@@ -160,7 +166,10 @@ vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm,
  * the token (pt = 4 a + i, ph, pw), m = (a * Mh + ph) * Mw + pw.
  * o receives softmax(q k^T / sqrt(head_dim) + B + mask) v per window and head
  * (rows of pad slots are unspecified).  rpb_table as in vswin_block_weights.
- * workspace >= plan.attention_workspace_bytes (may be NULL when 0).        */
+ * workspace >= plan.attention_workspace_bytes (may be NULL when 0); when
+ * plan.fast_attention == 1 it receives the fp32 prepared form of rpb_table
+ * (heads x about 2.7K 16-byte 4-tuples for a (8,7,7) window) that the
+ * kernel stages in LDS; see VSWIN_F_TABLES_READY.                          */
 vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const void* k,
                                  const void* v, const void* rpb_table, void* o,
                                  void* workspace, size_t workspace_bytes, void* stream);

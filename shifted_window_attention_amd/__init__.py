@@ -24,7 +24,7 @@ __all__ = [
     "vswin_index_map",
     "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
     "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd",
-    "F_PAD_VISIBLE", "F_CLAMP_STRICT", "F_MASK_M100", "LIB_PATH",
+    "F_PAD_VISIBLE", "F_CLAMP_STRICT", "F_MASK_M100", "F_TABLES_READY", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvswin.so")
@@ -32,6 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvswin.so
 F_PAD_VISIBLE = 1
 F_CLAMP_STRICT = 2
 F_MASK_M100 = 4
+F_TABLES_READY = 8
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP error"}
 

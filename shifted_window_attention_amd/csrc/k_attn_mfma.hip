@@ -73,6 +73,7 @@ struct A5 {
   int TS4;                    // 4-tuples incl. the -inf one at the end
   int nW, heads;
   FastDiv fdRp, fdRw, fdKC, fdH;
+  Tab4Geo tg;                 // the prepared table (same extents as above)
   float qscale;               // multiplier applied to q on load (1 when pre-scaled)
   int force_max;
   uint32_t off_kp, off_tab, off_redt, off_buf, buf_bytes, off_v, off_lp, off_red;
@@ -239,71 +240,50 @@ __device__ __forceinline__ void stage_offsets(const AttnArgs& a, const A5& L, in
   }
 }
 
-// fp32 4-tuples of the head's column of the table, scaled by log2(e).
-// The raw (rows, heads) table is read with coalesced 16-byte loads; this
-// head's column goes to an LDS scratch (the K/V buffer region, still free
-// in the prologue), and the 4-tuples are built from there.  Two barriers.
+// The prepared tables of every head, (heads, TS4) 4-tuples, built once per
+// call and copied to LDS by each workgroup.
+__global__ void __launch_bounds__(256) attn_table_kernel(const bf16_t* __restrict__ T, f32x4_t* __restrict__ out,
+                                                         const A5 L) {
+  const int x = blockIdx.x * 256 + (int)threadIdx.x;
+  const int h = blockIdx.y;
+  if (x < L.TS4) out[(size_t)h * L.TS4 + x] = t4_entry(T, L.tg, h, x);
+}
+
+// head h's prepared table: loads issued here, stored by tab_store
 template <class CF>
-__device__ __forceinline__ void build_table(const AttnArgs& a, const A5& L, int h, unsigned char* smem) {
+struct TabPre {
+  f32x4_t t[CF::kTabIter];
+};
+
+template <class CF>
+__device__ __forceinline__ void tab_load(TabPre<CF>& tp, const AttnArgs& a, const A5& L, int h) {
   const int tid = opaque_tid();
-  const bf16_t* T = reinterpret_cast<const bf16_t*>(a.table);
-  float* col = reinterpret_cast<float*>(smem + L.off_buf);
-  const int E = L.TD * L.R * L.heads;
-  const int nch = (E + 7) / 8;
-  constexpr int BATCH = 8;
-  for (int c0 = 0; c0 < nch; c0 += BATCH * CF::kThreads) {
-    u32x4_t v[BATCH];
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.tab4) + (size_t)h * L.TS4;
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) {
-      const int c = c0 + i * CF::kThreads + tid;
-      v[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (8 * c + 8 <= E) {
-        v[i] = *reinterpret_cast<const u32x4_t*>(T + 8 * c);
-      } else if (c < nch) {
-        for (int e = 0; e < 8 && 8 * c + e < E; ++e) {
-          const uint32_t x = T[8 * c + e];
-          v[i][e >> 1] |= (e & 1) ? (x << 16) : x;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i) {
-      const int c = c0 + i * CF::kThreads + tid;
-      if (c < nch) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int idx = 8 * c + e;
-          const int r = (int)fdiv((uint32_t)idx, L.fdH);
-          if (idx < E && idx - r * L.heads == h)
-            col[r] = ((e & 1) ? bfhi(v[i][e >> 1]) : bflo(v[i][e >> 1])) * kLog2e;
-        }
-      }
-    }
+  for (int i = 0; i < CF::kTabIter; ++i) {
+    const int x = tid + i * CF::kThreads;
+    if (x < L.TS4) tp.t[i] = src[x];
   }
-  __syncthreads();
+}
+
+// to LDS, with each wave's max |entry| (the -inf tuple excluded) for the
+// overflow bound
+template <class CF>
+__device__ __forceinline__ void tab_store(const TabPre<CF>& tp, const A5& L, unsigned char* smem) {
+  const int tid = opaque_tid();
   f32x4_t* tab = reinterpret_cast<f32x4_t*>(smem + L.off_tab);
   float tm = 0.f;
-  for (int x = tid; x < L.TS4; x += CF::kThreads) {
-    f32x4_t v = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (x < L.TS4 - 1) {
-      const int dtr = (int)fdiv((uint32_t)x, L.fdRp);
-      const int rem = x - dtr * L.Rp;
-      const int dhr = (int)fdiv((uint32_t)rem, L.fdRw);
-      const int dwr = rem - dhr * L.Rw;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dt = dtr + i;
-        const bool ok = rem < L.R && dt < L.TD;
-        const int row = ok ? (L.TD - 1 - dt) * L.R + (L.TH - 1 - dhr) * L.Rw + (L.Rw - 1 - dwr) : 0;
-        v[i] = ok ? col[row] : 0.f;
-        tm = fmaxf(tm, fabsf(v[i]));
-      }
+  for (int i = 0; i < CF::kTabIter; ++i) {
+    const int x = tid + i * CF::kThreads;
+    if (x < L.TS4) {
+      tab[x] = tp.t[i];
+      if (x < L.TS4 - 1)
+        tm = fmaxf(tm, fmaxf(fmaxf(fabsf(tp.t[i][0]), fabsf(tp.t[i][1])), fmaxf(fabsf(tp.t[i][2]), fabsf(tp.t[i][3]))));
     }
-    tab[x] = v;
   }
   tm = wave_max(tm);
   if ((tid & 63) == 0) reinterpret_cast<float*>(smem + L.off_redt)[tid >> 6] = tm;
-  __syncthreads();   // the scratch column is overwritten by the first window's K/V
 }
 
 // ---- one 32-key step for the wave's QT tiles --------------------------------
@@ -554,8 +534,12 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
   TileRun run = tile_run<CF>(wv, w0, t0, t1, L.QTT);
   q_load<CF>(qcur, a, L, cur.mem, run.jt, run.cnt);
   pref_load<CF>(pf, a, L, cur.mem);
-  build_table<CF>(a, L, h, smem);
-  pref_store<CF>(pf, L, smem + L.off_buf);
+  {
+    TabPre<CF> tp;
+    tab_load<CF>(tp, a, L, h);
+    pref_store<CF>(pf, L, smem + L.off_buf);
+    tab_store<CF>(tp, L, smem);
+  }
   stage_labels<CF>(a, L, cur, smem + L.off_buf);
   __syncthreads();
 
@@ -587,11 +571,10 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
 
 namespace {
 
-// the K/V buffers, which also hold the table column scratch in the prologue
-size_t a5_lds(const A5& L) {
-  const size_t bufs = (size_t)L.NB * L.buf_bytes, col = (size_t)L.TD * L.R * 4;
-  return (size_t)L.off_buf + (bufs > col ? bufs : col);
-}
+size_t a5_lds(const A5& L) { return (size_t)L.off_buf + (size_t)L.NB * L.buf_bytes; }
+
+// temporal stride R' of the 4-tuple table: >= R and 4 mod 16 (conflict-free reads)
+int tab_rp(int R) { return R + ((4 - R) % 16 + 16) % 16; }
 
 bool plan_a5(const AttnArgs& a, A5& L) {
   L = A5{};
@@ -605,7 +588,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.Rw = a.rel.Rw;
   L.TD = a.rel.rows / a.rel.R;               // 2 P0 - 1
   L.TH = a.rel.R / a.rel.Rw;                 // 2 Mh0 - 1
-  L.Rp = L.R + ((4 - L.R) % 16 + 16) % 16;
+  L.Rp = tab_rp(L.R);
   L.A = (L.TD / 2) * L.Rp + (L.TH / 2) * L.Rw + L.Rw / 2;
   L.TS4 = L.TD * L.Rp + 1;
   L.nW = (int)a.nW;
@@ -614,6 +597,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.fdRw = make_fastdiv((uint32_t)L.Rw);
   L.fdKC = make_fastdiv((uint32_t)kc);
   L.fdH = make_fastdiv((uint32_t)a.heads);
+  L.tg = tab4_geo(a.rel, a.heads);
   L.qscale = a.q_scaled ? 1.0f : kLog2e / sqrtf((float)a.d);
   L.force_max = a.force_max;
   if (L.TS4 > kMaxTab || a.heads > 256) return false;
@@ -654,7 +638,24 @@ hipError_t launch_cfg(const AttnArgs& ak, const A5& L, hipStream_t st) {
 
 }  // namespace
 
-size_t attention_workspace_bytes(const RelTab&, int) { return 0; }
+Tab4Geo tab4_geo(const RelTab& rel, int heads) {
+  Tab4Geo t{};
+  t.R = rel.R;
+  t.Rw = rel.Rw;
+  t.TD = rel.rows / rel.R;
+  t.TH = rel.R / rel.Rw;
+  t.Rp = tab_rp(rel.R);
+  t.TS4 = t.TD * t.Rp + 1;
+  t.heads = heads;
+  t.fdRp = make_fastdiv((uint32_t)t.Rp);
+  t.fdRw = make_fastdiv((uint32_t)t.Rw);
+  return t;
+}
+
+size_t attention_workspace_bytes(const RelTab& rel, int heads) {
+  const Tab4Geo t = tab4_geo(rel, heads);
+  return ((size_t)heads * t.TS4 * 16 + 255) & ~(size_t)255;
+}
 
 bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
   if (dt != VSWIN_BF16 || a.d != 32 || a.mask_m100) return false;
@@ -687,7 +688,13 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
   // hook for the path that otherwise runs only for very large logits).
   if (const char* f = getenv("VSWIN_ATTN_MAXPASS")) ak.force_max = atoi(f) != 0;
   A5 L;
-  if (!plan_a5(ak, L)) return hipErrorInvalidValue;
+  if (!plan_a5(ak, L) || !ak.tab4) return hipErrorInvalidValue;
+  if (!ak.tab_ready) {
+    attn_table_kernel<<<dim3((unsigned)((L.TS4 + 255) / 256), (unsigned)L.heads), dim3(256), 0, st>>>(
+        reinterpret_cast<const bf16_t*>(ak.table), reinterpret_cast<f32x4_t*>(ak.tab4), L);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 #if VSWIN_ATTN_WAVES == 16
   return launch_cfg<Cfg<16, 2>>(ak, L, st);
 #elif VSWIN_ATTN_WAVES == 12

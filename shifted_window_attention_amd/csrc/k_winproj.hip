@@ -106,6 +106,12 @@ struct QkvParams {
   int heads, d;
   FastDiv fd;           // division by d
   WinGeo geo;
+  // workgroups from tile_blocks on write the attention's prepared tables
+  // (tg) of `table` to tab4 instead (none when tab4 is NULL)
+  int tile_blocks;
+  const bf16_t* table;
+  f32x4_t* tab4;
+  Tab4Geo tg;
 };
 
 namespace {
@@ -147,13 +153,22 @@ __global__ void __launch_bounds__(kWpThreads, C == 96 ? 4 : 2) qkv_wave_kernel(Q
   using L = QkvLds<C>;
   constexpr int KS = C / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  if ((int)blockIdx.x >= pr.tile_blocks) {
+    const int n = pr.tg.TS4 * pr.tg.heads;
+    for (int e = ((int)blockIdx.x - pr.tile_blocks) * kWpThreads + (int)threadIdx.x; e < n;
+         e += ((int)gridDim.x - pr.tile_blocks) * kWpThreads) {
+      const int h = e / pr.tg.TS4;
+      pr.tab4[e] = t4_entry(pr.table, pr.tg, h, e - h * pr.tg.TS4);
+    }
+    return;
+  }
   unsigned char* Ws = lds;
   bf16_t* bias_s = reinterpret_cast<bf16_t*>(lds + L::w);   // 3C bias, then LN gamma (C), beta (C)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, g = lane >> 4;
   const int64_t ntiles = ((int64_t)pr.M + 15) / 16;
-  const int64_t nw = (int64_t)gridDim.x * kWpWaves;
+  const int64_t nw = (int64_t)pr.tile_blocks * kWpWaves;
   int64_t t = (int64_t)blockIdx.x * kWpWaves + wave;
   const int vt = pr.vt;
 
@@ -404,16 +419,26 @@ bool winproj_supported(vswin_dtype dt, int C, int d, int N, int vt) {
 
 hipError_t qkv_proj(const void* x, const void* ln_g, const void* ln_b, float eps, int ln, const void* W,
                     const void* bias, void* q, void* k, void* v, int vt, float qscale, int64_t M, int C, int heads,
-                    int d, const WinGeo& geo, hipStream_t st) {
+                    int d, const WinGeo& geo, const void* table, void* tab4, const Tab4Geo& tg, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   QkvParams pr{(const bf16_t*)x, (const bf16_t*)ln_g, (const bf16_t*)ln_b, eps, ln, (const bf16_t*)W,
                (const bf16_t*)bias, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v, vt, qscale, (int)M, heads, d,
                make_fastdiv((uint32_t)d), geo};
+  // two workgroups per CU for C = 96 (LDS and the 4-waves-per-SIMD register bound allow it)
+  pr.tile_blocks = (int)wave_grid(M, C == 96 ? 2 : 1);
+  int extra = 0;
+  if (tab4 && table) {
+    pr.table = (const bf16_t*)table;
+    pr.tab4 = (f32x4_t*)tab4;
+    pr.tg = tg;
+    const int64_t n = (int64_t)tg.TS4 * tg.heads;
+    extra = (int)((n + kWpThreads - 1) / kWpThreads);
+    if (extra > 64) extra = 64;
+  }
   auto go = [&](auto kern, size_t lds) -> hipError_t {
     hipError_t e = ensure_dynamic_lds((const void*)kern, lds);
     if (e != hipSuccess) return e;
-    // two workgroups per CU for C = 96 (LDS and the 4-waves-per-SIMD register bound allow it)
-    kern<<<dim3(wave_grid(M, C == 96 ? 2 : 1)), dim3(kWpThreads), lds, st>>>(pr);
+    kern<<<dim3((unsigned)(pr.tile_blocks + extra)), dim3(kWpThreads), lds, st>>>(pr);
     return hipGetLastError();
   };
   if (C == 96) return go(qkv_wave_kernel<96>, QkvLds<96>::bytes);

@@ -92,7 +92,7 @@ struct Plan {
 AttnArgs attn_args(const Plan& p, const void* q, const void* k, const void* v, const void* table, void* o,
                    uint32_t flags, char* scratch = nullptr) {
   AttnArgs a{};
-  (void)scratch;
+  a.tab4 = scratch;
   a.q = q; a.k = k; a.v = v; a.table = table; a.o = o;
   a.nW = p.nW; a.heads = p.heads; a.d = p.d; a.C = p.C; a.N = p.N;
   a.rel = p.rel; a.geo = p.geo;
@@ -111,7 +111,7 @@ vswin_status make_plan(const vswin_desc* d, Plan& p, bool compute = true) {
     return fail(VSWIN_ERR_INVALID_ARG, "C=%d is not a multiple of heads=%d", d->C, d->heads);
   if (d->mlp_hidden < 1) return fail(VSWIN_ERR_INVALID_ARG, "mlp_hidden=%d", d->mlp_hidden);
   if (!(d->ln_eps > 0.f)) return fail(VSWIN_ERR_INVALID_ARG, "ln_eps must be > 0");
-  if (d->flags & ~(uint32_t)(VSWIN_F_PAD_VISIBLE | VSWIN_F_CLAMP_STRICT | VSWIN_F_MASK_M100))
+  if (d->flags & ~(uint32_t)(VSWIN_F_PAD_VISIBLE | VSWIN_F_CLAMP_STRICT | VSWIN_F_MASK_M100 | VSWIN_F_TABLES_READY))
     return fail(VSWIN_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   const int size[3] = {d->T, d->H, d->W};
   int win[3], sh[3], pad[3];
@@ -225,11 +225,14 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
   if (ga && winproj_supported(p.dt, p.C, p.d, p.N, vt)) {
     // the MFMA attention takes q pre-multiplied by log2(e) / sqrt(d)
     const float qscale = p.fast ? 1.4426950408889634f / sqrtf((float)p.d) : 1.0f;
+    // the MFMA attention's prepared bias tables are written by the qkv launch
     HIPCHECK(qkv_proj(ga->x, ga->g, ga->b, ga->eps, ga->ln, w->qkv_w, w->qkv_b, q, k, v, vt, qscale, p.Lp, p.C,
-                      p.heads, p.d, p.geo, st),
+                      p.heads, p.d, p.geo, p.fast ? w->rpb_table : nullptr, p.fast ? ws + p.off_tab : nullptr,
+                      tab4_geo(p.rel, p.heads), st),
              "qkv projection");
     AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags, ws + p.off_tab);
     a.q_scaled = p.fast ? 1 : 0;
+    a.tab_ready = p.fast ? 1 : 0;
     if (p.fast) HIPCHECK(attention_mfma(a, st), "attention (mfma)");
     else HIPCHECK(attention_generic(p.dt, a, st), "attention (generic)");
     HIPCHECK(out_proj(xw, w->proj_w, w->proj_b, to_zh ? residual : nullptr, out, p.Lp, p.C, p.geo, st),
@@ -396,7 +399,8 @@ vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const vo
   CHECK(check_ptr(o, "o"));
   if (p.Lp == 0) return VSWIN_OK;
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
-  const AttnArgs a = attn_args(p, q, k, v, rpb_table, o, desc->flags, (char*)workspace);
+  AttnArgs a = attn_args(p, q, k, v, rpb_table, o, desc->flags, (char*)workspace);
+  a.tab_ready = (desc->flags & VSWIN_F_TABLES_READY) ? 1 : 0;
   if (p.fast) HIPCHECK(attention_mfma(a, (hipStream_t)stream), "attention (mfma)");
   else HIPCHECK(attention_generic(p.dt, a, (hipStream_t)stream), "attention (generic)");
   return VSWIN_OK;

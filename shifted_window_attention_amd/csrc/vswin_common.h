@@ -142,6 +142,16 @@ struct RelTab {
   int centre;
 };
 
+// The MFMA attention's prepared form of one head's table column: fp32
+// 4-tuples (B[r], B[r + Rp], B[r + 2 Rp], B[r + 3 Rp]) * log2(e), entry
+// x = dtr * Rp + rem for the offset from the query base (dtr + i, rem / Rw,
+// rem % Rw), i = 0..3; Rp >= R is the temporal stride (4 mod 16 for
+// conflict-free LDS reads); the last entry TS4 - 1 is a tuple of -inf.
+struct Tab4Geo {
+  int TD, TH, R, Rw, Rp, TS4, heads;
+  FastDiv fdRp, fdRw;
+};
+
 #if defined(__HIPCC__)
 // ---------------------------------------------------------------------------
 // device helpers
@@ -167,6 +177,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ uint16_t f2bf(float a) {
   __bf16 h = (__bf16)a;
   return __builtin_bit_cast(uint16_t, h);
+}
+
+// entry x of head h's prepared table, from the (rows, heads) bf16 table T:
+// offsets outside the table give 0
+__device__ __forceinline__ f32x4_t t4_entry(const bf16_t* __restrict__ T, const Tab4Geo& tg, int h, int x) {
+  f32x4_t v = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (x < tg.TS4 - 1) {
+    const int dtr = (int)fdiv((uint32_t)x, tg.fdRp);
+    const int rem = x - dtr * tg.Rp;
+    const int dhr = (int)fdiv((uint32_t)rem, tg.fdRw);
+    const int dwr = rem - dhr * tg.Rw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dt = dtr + i;
+      const bool ok = rem < tg.R && dt < tg.TD;
+      const int row = ok ? (tg.TD - 1 - dt) * tg.R + (tg.TH - 1 - dhr) * tg.Rw + (tg.Rw - 1 - dwr) : 0;
+      v[i] = ok ? bf2f(T[(size_t)row * tg.heads + h]) * 1.4426950408889634f : 0.f;
+    }
+  }
+  return v;
 }
 
 template <typename T> struct Elem;

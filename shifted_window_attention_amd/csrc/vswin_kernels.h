@@ -64,10 +64,12 @@ bool gemm_can_gather(vswin_dtype dt, int K);
 // out: o rows * W^T + bias scattered to token rows; with `res` the output is
 // fp32 z = res + ..., else bf16.
 bool winproj_supported(vswin_dtype dt, int C, int d, int N, int vt);
-// q is multiplied by qscale after the bias (1 for plain q).
+// q is multiplied by qscale after the bias (1 for plain q).  With tab4
+// non-null, extra workgroups also write the attention's prepared tables
+// (tg) of `table` there.
 hipError_t qkv_proj(const void* x, const void* ln_g, const void* ln_b, float eps, int ln, const void* W,
                     const void* bias, void* q, void* k, void* v, int vt, float qscale, int64_t M, int C, int heads,
-                    int d, const WinGeo& geo, hipStream_t st);
+                    int d, const WinGeo& geo, const void* table, void* tab4, const Tab4Geo& tg, hipStream_t st);
 hipError_t out_proj(const void* o, const void* W, const void* bias, const void* res, void* out, int64_t M, int C,
                     const WinGeo& geo, hipStream_t st);
 
@@ -84,9 +86,13 @@ struct AttnArgs {
   int mask_m100;           // additive -100 instead of exclusion
   int force_max;           // MFMA kernel: always take the exact row-max pass
   int q_scaled;            // MFMA kernel: q already multiplied by log2(e) / sqrt(d)
+  void* tab4;              // MFMA kernel: workspace of attention_workspace_bytes for the prepared tables
+  int tab_ready;           // MFMA kernel: tab4 already holds this call's tables
 };
-// bytes of scratch the MFMA kernel needs for its prepared tables
+// bytes of workspace the MFMA kernel needs for its prepared bias tables
+// (heads * TS4 fp32 4-tuples) and their extents
 size_t attention_workspace_bytes(const RelTab& rel, int heads);
+Tab4Geo tab4_geo(const RelTab& rel, int heads);
 hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st);
 hipError_t attention_mfma(const AttnArgs& a, hipStream_t st);
 // shapes the MFMA kernel serves (bf16, d = 32, temporal window % 4 == 0 with

@@ -371,3 +371,31 @@ def test_attention_core_alone(shift, size):
     # pad query rows are not outputs of the block; compare the real ones
     real = g.index_map() >= 0
     check(o_nat[real], ref[real], "bf16", "attention core")
+
+
+def test_attention_prepared_tables_reuse():
+    """The prepared bias tables live in the attention workspace: a call with
+    F_TABLES_READY reuses them (same result, bit for bit), a call without it
+    rebuilds them from the table it is given."""
+    say("attention prepared-table reuse")
+    B, C, heads, window, shift, size = 1, 96, 3, (8, 7, 7), (4, 3, 3), (16, 14, 14)
+    d = C // heads
+    desc = vs.make_desc(B, *size, C, heads, window, shift)
+    ready = vs.make_desc(B, *size, C, heads, window, shift, flags=vs.F_TABLES_READY)
+    plan = vs.vswin_plan_query(desc)
+    assert plan["fast_attention"] == 1 and plan["attention_workspace_bytes"] > 0
+    nW, N = plan["num_windows"], plan["tokens_per_window"]
+    g = torch.Generator(device="cuda").manual_seed(5)
+    q, k, vt = (torch.randn((nW, heads, *s), generator=g, device="cuda").to(torch.bfloat16)
+                for s in ((N, d), (N, d), (d, N)))
+    t1, t2 = (torch.randn((15 * 13 * 13, heads), generator=g, device="cuda").to(torch.bfloat16) for _ in range(2))
+    ws = torch.empty(plan["attention_workspace_bytes"], dtype=torch.uint8, device="cuda")
+    o1 = vs.vswin_attention_fwd(desc, q, k, vt, t1, workspace=ws).clone()
+    o1r = vs.vswin_attention_fwd(ready, q, k, vt, t1, workspace=ws).clone()
+    o2 = vs.vswin_attention_fwd(desc, q, k, vt, t2, workspace=ws).clone()
+    ws2 = torch.empty_like(ws)
+    o2f = vs.vswin_attention_fwd(desc, q, k, vt, t2, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o1r)
+    assert torch.equal(o2, o2f)
+    assert not torch.equal(o1, o2)
