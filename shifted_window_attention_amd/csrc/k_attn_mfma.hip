@@ -5,11 +5,12 @@
 // Work split.  The workgroups (W waves, one per CU) are divided among the
 // heads; the query tiles (16 queries) of one head's windows form a list and
 // each of that head's workgroups takes an equal contiguous run of it, so a
-// workgroup builds its head's bias table once.  A window's K and V^T are
-// staged once in LDS for all of the run's tiles of that window, and the next
-// window's K/V is fetched into registers while the current one is computed
-// (two LDS buffers when they fit, else one), so staging latency hides behind
-// compute.  Waves own tiles, not steps: inside a window no barrier is needed.
+// workgroup copies its head's prepared bias table (built once per call) to
+// LDS once.  A window's K and V^T are staged once in LDS for all of the run's
+// tiles of that window by direct global-to-LDS loads, and the next window's
+// are in flight while the current one is computed (two LDS buffers when they
+// fit, else one).  Waves own tiles, not steps: inside a window no barrier is
+// needed.
 //
 // Scores.  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (k = head_dim): a lane
 // holds 4 keys of one query, so all per-query state stays in the lane.
@@ -21,10 +22,10 @@
 //     the bias costs one 16-byte LDS read per 4 scores and no VALU.  Masked
 //     and dummy key groups read a 4-tuple of -inf instead.
 //   * q arrives multiplied by log2(e) / sqrt(d), so the MFMA result is the
-//     exponent of 2 directly.  P = exp2(x) with no running max when a
-//     Cauchy-Schwarz bound |x| <= |q| max|k| + max|B log2 e| <= 90 shows
-//     exp2 cannot overflow (softmax is shift invariant); otherwise the wave
-//     first takes an exact row-max pass.
+//     exponent of 2 directly.  P = exp2(x) with no running max (softmax is
+//     shift invariant); a row whose sum leaves [2^-100, 2^100] or whose
+//     accumulators are not finite sends its wave through an exact pass that
+//     subtracts the row max first.
 //   * O^T = V^T P^T on MFMA with P^T already in B-operand layout; the row
 //     sums come from a third MFMA against a ones operand.  V^T rows are read
 //     in pair order (d = 8g + 4p + i), so a lane ends with 8 consecutive
@@ -60,7 +61,6 @@ struct Cfg {
   static constexpr int kWaves = W;
   static constexpr int kQTM = QTM;
   static constexpr int kThreads = 64 * W;
-  static constexpr int kPref = (4 * kMfmaMaxN + kThreads - 1) / kThreads;   // 16-byte K (and V^T) chunks per thread
   static constexpr int kTabIter = (kMaxTab + kThreads - 1) / kThreads;
   static_assert((kMfmaMaxN / 16 + W - 1) / W <= QTM, "a wave's tiles of one window exceed QTM");
   static_assert(W <= kMaxWaves, "too many waves");
@@ -76,12 +76,7 @@ struct A5 {
   Tab4Geo tg;                 // the prepared table (same extents as above)
   float qscale;               // multiplier applied to q on load (1 when pre-scaled)
   int force_max;
-  uint32_t off_kp, off_tab, off_redt, off_buf, buf_bytes, off_v, off_lp, off_red;
-};
-
-template <class CF>
-struct Pref {
-  u32x4_t k[CF::kPref], v[CF::kPref];
+  uint32_t off_kp, off_tab, off_buf, buf_bytes, off_v, off_lp, off_red;
 };
 
 template <int QT>
@@ -132,73 +127,63 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ int pair_slot(int m) { return 2 * (4 * (m >> 3) + (m & 3)) + ((m >> 2) & 1); }
 
 // ---- staging -------------------------------------------------------------
+// One window's K and V^T go from global memory straight into LDS
+// (global_load_lds: a wave instruction fills 1 KB, or 256 B for 4-byte
+// elements, at a uniform LDS address, from per-lane global addresses), so no
+// registers or VALU work carry them.  Lanes whose key is past N stay off; their
+// LDS slots hold the zeros written once by zero_pads.
+//   K: instruction b covers key rows 16b .. 16b + 15; lane i takes row
+//      16b + i/4, LDS chunk i%4, i.e. global chunk (i%4) ^ ((i>>4)&3).
+//   V^T: instruction (d, q) covers chunk slots 16q .. 16q + 15 of row d; lane i
+//      takes slot 16q + i/4, dword i%4: keys 2 apart pairs of its 8 keys.
+//      Wave wv owns rows 8 (wv>>1) + 4 (wv&1) .. + 3, so the row swizzle
+//      (d >> 3) & 3 = wv >> 1 is the same for all of its rows.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <class CF>
-__device__ __forceinline__ void pref_load(Pref<CF>& pf, const AttnArgs& a, const A5& L, int mem) {
-  const int tid = opaque_tid();
+__device__ __forceinline__ void stage_kv(const AttnArgs& a, const A5& L, int mem, unsigned char* B, int wv) {
+  static_assert(CF::kWaves == 8, "V^T rows are split as 4 per wave");
+  const int lane = threadIdx.x & 63;
   const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)mem * L.N * 32;
   const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)mem * L.N * 32;
-  const int kcpr = L.NPAD >> 3;
-#pragma unroll
-  for (int j = 0; j < CF::kPref; ++j) {
-    const int c = tid + CF::kThreads * j;
-    const int r = c >> 2;
-    pf.k[j] = r < L.N ? *reinterpret_cast<const u32x4_t*>(Kg + r * 32 + (c & 3) * 8) : u32x4_t{0u, 0u, 0u, 0u};
-    const int d = (int)fdiv((uint32_t)c, L.fdKC);
-    const int key0 = 8 * (c - d * kcpr);
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (d < 32) {
-      const bf16_t* src = Vg + d * L.N + key0;
-      if ((L.N & 7) == 0) {
-        if (key0 < L.N) v = *reinterpret_cast<const u32x4_t*>(src);
-      } else {
-        if (key0 < L.N) {
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
-          v[0] = lo[0]; v[1] = lo[1];
-        }
-        if (key0 + 4 < L.N) {
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 4);
-          v[2] = hi[0]; v[3] = hi[1];
-        }
-      }
+  const int kr = lane >> 2;
+  const int koff = kr * 32 + (((lane & 3) ^ ((lane >> 4) & 3)) << 3);
+  const int nkb = (L.N + 15) >> 4;
+  for (int b = wv; b < nkb; b += CF::kWaves) {
+    if (16 * b + kr < L.N)
+      __builtin_amdgcn_global_load_lds(Kg + b * 512 + koff, (lds_ptr_t)(B + b * 1024), 16, 0, 0);
+  }
+  const int sw = wv >> 1;
+  const int key = 32 * (lane >> 4) + 4 * (((lane >> 2) & 3) ^ sw) + 16 * ((lane >> 1) & 1) + 2 * (lane & 1);
+  const int nq = (4 * L.NP + 15) >> 4;
+  for (int r = 0; r < 4; ++r) {
+    const int d = 8 * sw + 4 * (wv & 1) + r;
+    for (int q = 0; q < nq; ++q) {
+      if (key + 128 * q < L.N)
+        __builtin_amdgcn_global_load_lds(Vg + d * L.N + 128 * q + key,
+                                         (lds_ptr_t)(B + L.off_v + (d * L.pitch_v + 16 * q) * 16), 4, 0, 0);
     }
-    pf.v[j] = v;
   }
 }
 
+// zeros in every LDS slot of the K / V^T buffers that stage_kv never writes
+// and the steps read: key rows N .. NPAD - 1 of K, and in V^T the keys >= N of
+// the last 32-key block
 template <class CF>
-__device__ __forceinline__ void pref_store(const Pref<CF>& pf, const A5& L, unsigned char* B) {
-  const int tid = opaque_tid();
-  const int kcpr = L.NPAD >> 3;
-  float km = 0.f;
-#pragma unroll
-  for (int j = 0; j < CF::kPref; ++j) {
-    const int c = tid + CF::kThreads * j;
-    const int r = c >> 2, q = c & 3;
-    if (r < L.NPAD) *reinterpret_cast<u32x4_t*>(B + r * 64 + ((q ^ ((r >> 2) & 3)) << 4)) = pf.k[j];
-    float sq = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bflo(pf.k[j][e]), hi = bfhi(pf.k[j][e]);
-      sq += lo * lo + hi * hi;
-    }
-    sq += __shfl_xor(sq, 1);
-    sq += __shfl_xor(sq, 2);
-    km = fmaxf(km, sq);
-    const int d = (int)fdiv((uint32_t)c, L.fdKC);
-    if (d < 32) {
-      const int kc = c - d * kcpr;
-      const int p = kc >> 2, cb = kc & 3;
-      const int lc0 = 2 * (cb & 1), sw = (d >> 3) & 3;
-      unsigned char* row = B + L.off_v + d * L.pitch_v * 16 + p * 64 + 8 * (cb >> 1);
-      u32x2_t lo, hi;
-      lo[0] = pf.v[j][0]; lo[1] = pf.v[j][1];
-      hi[0] = pf.v[j][2]; hi[1] = pf.v[j][3];
-      *reinterpret_cast<u32x2_t*>(row + ((lc0 ^ sw) << 4)) = lo;
-      *reinterpret_cast<u32x2_t*>(row + (((lc0 + 1) ^ sw) << 4)) = hi;
+__device__ __forceinline__ void zero_pads(const A5& L, unsigned char* smem) {
+  const int tid = threadIdx.x;
+  for (int nb = 0; nb < L.NB; ++nb) {
+    unsigned char* B = smem + L.off_buf + (size_t)nb * L.buf_bytes;
+    for (int x = tid; x < (L.NPAD - L.N) * 16; x += CF::kThreads)
+      reinterpret_cast<uint32_t*>(B + L.N * 64)[x] = 0u;
+    for (int x = tid; x < 32 * 16; x += CF::kThreads) {
+      const int d = x >> 4, jp = (x >> 2) & 3, e = x & 3;
+      const int j = jp ^ ((d >> 3) & 3);
+      const int key = 32 * (L.NP - 1) + 4 * j + 16 * (e >> 1) + 2 * (e & 1);
+      if (key >= L.N)
+        *reinterpret_cast<uint32_t*>(B + L.off_v + (d * L.pitch_v + 4 * (L.NP - 1) + jp) * 16 + 4 * e) = 0u;
     }
   }
-  km = wave_max(km);
-  if ((tid & 63) == 0) reinterpret_cast<float*>(B + L.off_red)[tid >> 6] = km;
 }
 
 // region labels of the window's key groups and whether they differ
@@ -221,7 +206,7 @@ __device__ __forceinline__ void stage_labels(const AttnArgs& a, const A5& L, con
     lp[pair_slot(m)] = lab;
   }
   const uint64_t any = __builtin_amdgcn_ballot_w64(differs);
-  if ((tid & 63) == 0) reinterpret_cast<int*>(B + L.off_red)[kMaxWaves + (tid >> 6)] = any != 0;
+  if ((tid & 63) == 0) reinterpret_cast<int*>(B + L.off_red)[tid >> 6] = any != 0;
 }
 
 // key-group table offsets (bytes; the same for every window)
@@ -266,24 +251,15 @@ __device__ __forceinline__ void tab_load(TabPre<CF>& tp, const AttnArgs& a, cons
   }
 }
 
-// to LDS, with each wave's max |entry| (the -inf tuple excluded) for the
-// overflow bound
 template <class CF>
 __device__ __forceinline__ void tab_store(const TabPre<CF>& tp, const A5& L, unsigned char* smem) {
   const int tid = opaque_tid();
   f32x4_t* tab = reinterpret_cast<f32x4_t*>(smem + L.off_tab);
-  float tm = 0.f;
 #pragma unroll
   for (int i = 0; i < CF::kTabIter; ++i) {
     const int x = tid + i * CF::kThreads;
-    if (x < L.TS4) {
-      tab[x] = tp.t[i];
-      if (x < L.TS4 - 1)
-        tm = fmaxf(tm, fmaxf(fmaxf(fabsf(tp.t[i][0]), fabsf(tp.t[i][1])), fmaxf(fabsf(tp.t[i][2]), fabsf(tp.t[i][3]))));
-    }
+    if (x < L.TS4) tab[x] = tp.t[i];
   }
-  tm = wave_max(tm);
-  if ((tid & 63) == 0) reinterpret_cast<float*>(smem + L.off_redt)[tid >> 6] = tm;
 }
 
 // ---- one 32-key step for the wave's QT tiles --------------------------------
@@ -398,54 +374,60 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   const unsigned char* tabb = smem + L.off_tab;
   const int zone = 16 * (L.TS4 - 1);
   const int* lp = reinterpret_cast<const int*>(B + L.off_lp);
-  float kmax2 = 0.f, tmx = 0.f;
   int masked = 0;
 #pragma unroll
-  for (int i = 0; i < CF::kWaves; ++i) {
-    kmax2 = fmaxf(kmax2, reinterpret_cast<const float*>(B + L.off_red)[i]);
-    masked |= reinterpret_cast<const int*>(B + L.off_red)[kMaxWaves + i];
-    tmx = fmaxf(tmx, reinterpret_cast<const float*>(smem + L.off_redt)[i]);
-  }
-  const float kmax = sqrtf(kmax2);
+  for (int i = 0; i < CF::kWaves; ++i) masked |= reinterpret_cast<const int*>(B + L.off_red)[i];
 
   QState<QT> st;
-  bool need = false;
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     const int qs = 16 * (jt + CF::kWaves * u) + fr;
-    const bool valid = qs < N;
     // the query's key group: same table base (plus its temporal index) and label
     const int ps = pair_slot(qs >> 2);
     st.qaddr[u] = 16 * L.A - kp[ps] - 16 * (qs & 3) * L.Rp;
     st.qlab[u] = lp[ps];
     u32x4_t qv = qp.q[u];
-    float sq = 0.f;
+    if (L.qscale != 1.0f) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float lo = bflo(qv[e]), hi = bfhi(qv[e]);
-      if (L.qscale != 1.0f) {
-        qv[e] = pack_bf16x2(lo * L.qscale, hi * L.qscale);
-        lo = bflo(qv[e]);
-        hi = bfhi(qv[e]);
-      }
-      sq += lo * lo + hi * hi;
+      for (int e = 0; e < 4; ++e) qv[e] = pack_bf16x2(bflo(qv[e]) * L.qscale, bfhi(qv[e]) * L.qscale);
     }
-    sq += __shfl_xor(sq, 16);
-    sq += __shfl_xor(sq, 32);
-    need |= valid && !(sqrtf(sq) * kmax + tmx <= 90.f);
     st.q[u] = __builtin_bit_cast(bf16x8_t, qv);
-    st.mrow[u] = -INFINITY;
-    st.o0[u] = st.o1[u] = st.os[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   bf16x8_t ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
   const int2* kp2 = reinterpret_cast<const int2*>(kp);
-  const bool wave_max_pass = L.force_max || __builtin_amdgcn_ballot_w64(need) != 0;
-  if (!wave_max_pass) {
+  auto clear = [&]() {
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      st.mrow[u] = -INFINITY;
+      st.o0[u] = st.o1[u] = st.os[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // P = exp2(x) with no max first; softmax is shift invariant, so the result
+  // stands unless some row left the safe range: its sum outside
+  // [2^-100, 2^100] (overflow, or all of the row's terms tiny) or a
+  // non-finite accumulator.  Then the wave redoes its tiles with the exact
+  // row max subtracted.
+  bool exact = L.force_max != 0;
+  if (!exact) {
+    clear();
     if (masked) attn_pass<0, true, QT>(B, L, tabb, kp2, zone, ones, st);
     else attn_pass<0, false, QT>(B, L, tabb, kp2, zone, ones, st);
-  } else {
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      const int qs = 16 * (jt + CF::kWaves * u) + fr;
+      const float sum = st.os[u][0];
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t += st.o0[u][i] + st.o1[u][i];
+      bad |= qs < N && !(sum >= 0x1p-100f && sum <= 0x1p100f && t - t == 0.f);
+    }
+    exact = __builtin_amdgcn_ballot_w64(bad) != 0;
+  }
+  if (exact) {
+    clear();
     if (masked) attn_pass<1, true, QT>(B, L, tabb, kp2, zone, ones, st);
     else attn_pass<1, false, QT>(B, L, tabb, kp2, zone, ones, st);
 #pragma unroll
@@ -465,7 +447,7 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   for (int u = 0; u < QT; ++u) {
     const int qs = 16 * (jt + CF::kWaves * u) + fr;
     if (qs >= N) continue;
-    const float inv = 1.0f / st.os[u][0];
+    const float inv = __builtin_amdgcn_rcpf(st.os[u][0]);
     u32x4_t pk;
     pk[0] = pack_bf16x2(st.o0[u][0] * inv, st.o0[u][1] * inv);
     pk[1] = pack_bf16x2(st.o0[u][2] * inv, st.o0[u][3] * inv);
@@ -489,20 +471,20 @@ __device__ __forceinline__ void tiles_dispatch(int cnt, const AttnArgs& a, const
   if (cnt == 1) attn_tiles<CF, 1>(a, L, wi, h, jt, qp, B, smem, kp);
 }
 
-// this workgroup's tiles of window w are [j0, j1) of the window's list; wave
-// wv takes the ones congruent to wv + w (mod W), rotating the remainder
+// Tile t of the workgroup's run [t0, t1) belongs to wave (t - t0) mod W, so
+// the waves' totals over the run differ by at most one tile.  Wave wv's
+// tiles of window w: jt, jt + W, ... (cnt of them) of the window's list.
 struct TileRun {
   int jt, cnt;
 };
 template <class CF>
 __device__ __forceinline__ TileRun tile_run(int wv, int w, int64_t t0, int64_t t1, int QTT) {
   const int64_t base = (int64_t)w * QTT;
-  const int j0 = (int)((t0 > base ? t0 : base) - base);
-  const int j1 = (int)((t1 < base + QTT ? t1 : base + QTT) - base);
-  const int k0 = (wv - w % CF::kWaves + CF::kWaves) % CF::kWaves;
+  const int64_t lo = t0 > base ? t0 : base, hi = t1 < base + QTT ? t1 : base + QTT;
+  const int64_t first = lo + ((wv - (int)((lo - t0) % CF::kWaves)) + CF::kWaves) % CF::kWaves;
   TileRun r;
-  r.jt = j0 + k0;
-  r.cnt = j0 + k0 < j1 ? (j1 - j0 - k0 + CF::kWaves - 1) / CF::kWaves : 0;
+  r.jt = (int)(first - base);
+  r.cnt = first < hi ? (int)((hi - first + CF::kWaves - 1) / CF::kWaves) : 0;
   return r;
 }
 
@@ -528,44 +510,55 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
 
   int* kp = reinterpret_cast<int*>(smem + L.off_kp);
   stage_offsets<CF>(a, L, kp);
-  Pref<CF> pf;
+  zero_pads<CF>(L, smem);
   QPre<CF> qcur, qnext;
   Win cur = window_of(a, L, h, w0);
   TileRun run = tile_run<CF>(wv, w0, t0, t1, L.QTT);
   q_load<CF>(qcur, a, L, cur.mem, run.jt, run.cnt);
-  pref_load<CF>(pf, a, L, cur.mem);
+  stage_kv<CF>(a, L, cur.mem, smem + L.off_buf, wv);
   {
     TabPre<CF> tp;
     tab_load<CF>(tp, a, L, h);
-    pref_store<CF>(pf, L, smem + L.off_buf);
     tab_store<CF>(tp, L, smem);
   }
   stage_labels<CF>(a, L, cur, smem + L.off_buf);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's direct loads are in LDS
   __syncthreads();
 
-  for (int w = w0; w <= w1; ++w) {
-    const int buf = L.NB == 2 ? ((w - w0) & 1) : 0;
+  // Window k of the run sits in buffer k & 1 (two buffers) or 0; the next
+  // window is staged while this one is computed (after it, with one buffer).
+  const int nwin = w1 - w0 + 1;
+  for (int k = 0; k < nwin; ++k) {
+    const int w = w0 + k;
+    const int buf = L.NB == 2 ? (k & 1) : 0;
     const unsigned char* B = smem + L.off_buf + (size_t)buf * L.buf_bytes;
-    const bool more = w < w1;
+    const bool more = k + 1 < nwin;
     Win nxt{};
     TileRun rnext{};
     if (more) {
       nxt = window_of(a, L, h, w + 1);
       rnext = tile_run<CF>(wv, w + 1, t0, t1, L.QTT);
       q_load<CF>(qnext, a, L, nxt.mem, rnext.jt, rnext.cnt);
-      pref_load<CF>(pf, a, L, nxt.mem);
+      if (L.NB == 2) {
+        unsigned char* Bn = smem + L.off_buf + (size_t)(buf ^ 1) * L.buf_bytes;
+        stage_kv<CF>(a, L, nxt.mem, Bn, wv);
+        stage_labels<CF>(a, L, nxt, Bn);
+      }
     }
     tiles_dispatch<CF>(run.cnt, a, L, cur, h, run.jt, qcur, B, smem, kp);
     if (more) {
-      if (L.NB == 1) __syncthreads();
-      unsigned char* Bn = smem + L.off_buf + (size_t)(L.NB == 2 ? (buf ^ 1) : 0) * L.buf_bytes;
-      pref_store<CF>(pf, L, Bn);
-      stage_labels<CF>(a, L, nxt, Bn);
+      if (L.NB == 1) {
+        __syncthreads();
+        unsigned char* Bn = smem + L.off_buf;
+        stage_kv<CF>(a, L, nxt.mem, Bn, wv);
+        stage_labels<CF>(a, L, nxt, Bn);
+      }
       cur = nxt;
       run = rnext;
       qcur = qnext;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -604,8 +597,6 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   size_t off = 0;
   L.off_kp = (uint32_t)off;
   off += (size_t)L.NP * 8 * 4;
-  L.off_redt = (uint32_t)off;
-  off += 4 * kMaxWaves;
   off = (off + 15) & ~(size_t)15;
   L.off_tab = (uint32_t)off;
   off += (size_t)L.TS4 * 16;
@@ -616,7 +607,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.off_lp = (uint32_t)bb;
   bb += (size_t)L.NP * 8 * 4;
   L.off_red = (uint32_t)bb;
-  bb += 8 * kMaxWaves;
+  bb += 4 * kMaxWaves;
   L.buf_bytes = (uint32_t)((bb + 15) & ~(size_t)15);
   L.NB = off + 2 * (size_t)L.buf_bytes <= kLdsMax ? 2 : 1;
   return a5_lds(L) <= kLdsMax;
@@ -676,10 +667,6 @@ bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
   return plan_a5(a, L);
 }
 
-#ifndef VSWIN_ATTN_WAVES
-#define VSWIN_ATTN_WAVES 8
-#endif
-
 hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
   const int64_t items = a.nW * a.heads;
   if (items <= 0) return hipSuccess;
@@ -695,13 +682,7 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#if VSWIN_ATTN_WAVES == 16
-  return launch_cfg<Cfg<16, 2>>(ak, L, st);
-#elif VSWIN_ATTN_WAVES == 12
-  return launch_cfg<Cfg<12, 3>>(ak, L, st);
-#else
   return launch_cfg<Cfg<8, 4>>(ak, L, st);
-#endif
 }
 
 }  // namespace vswin
