@@ -272,7 +272,7 @@ constexpr size_t kMlpW1 = (size_t)kMlpHid * kMlpC * 2;
 // < 3.4e-6 (the tail mass) outside it, where the index is clamped.
 constexpr int kPhiN = 512;
 constexpr float kPhiX = 4.5f;
-constexpr size_t kMlpVec = kMlpHid * 2 + 3 * kMlpC * 2;                 // b1, LN2 gamma / beta, fc2 bias
+constexpr size_t kMlpVec = kMlpHid * 4 + kMlpC * 4 + 3 * kMlpC * 2;     // b1, proj bias (fp32), LN2 gamma / beta, fc2 bias
 constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + kPhiN * 8;
 
 struct ZTile {
@@ -296,20 +296,64 @@ __device__ __forceinline__ void ztile_load(ZTile& zt, const float* __restrict__ 
   }
 }
 
+// With the output projection in front (PROJ): a token tile's inputs are its
+// attention output rows o (gathered from window-row space) and its residual
+// rows x, both bf16.
+struct ProjTileIn {
+  u32x4_t o[3], x[3];   // k-chunk g of o's 32-column block kk; x columns 32j + 8g .. + 7
+};
+
 }  // namespace
 
-__global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __restrict__ zh, const bf16_t* __restrict__ g2,
-                                                               const bf16_t* __restrict__ b2ln,
-                                                               const bf16_t* __restrict__ W1, const bf16_t* __restrict__ b1,
-                                                               const bf16_t* __restrict__ W2, const bf16_t* __restrict__ bo,
-                                                               bf16_t* __restrict__ y, int64_t L, float eps) {
+struct MlpArgs {
+  const float* zh;       // !PROJ: z^ token rows (L, C), fp32
+  const bf16_t* o;       // PROJ: attention output, window rows (Lp, C)
+  const bf16_t* x;       // PROJ: block input token rows (L, C): the residual
+  const bf16_t* wp;      // PROJ: (C, C) projection weight, bias bp (C) or NULL
+  const bf16_t* bp;
+  WinGeo geo;            // PROJ: token -> window row
+  const bf16_t *g2, *b2ln, *W1, *b1, *W2, *bo;
+  bf16_t* y;
+  int64_t L;
+  float eps;
+};
+
+namespace {
+
+__device__ __forceinline__ void proj_tile_load(ProjTileIn& pt, const MlpArgs& a, int64_t t) {
+  const int lane = threadIdx.x & 63, fr = lane & 15, g = lane >> 4;
+  const int64_t tok = t * 16 + fr;
+  const bool ok = tok < a.L;
+  const int64_t m = ok ? token_row(a.geo, (int)tok) : 0;
+  const int64_t tx = ok ? tok : 0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    pt.o[j] = *reinterpret_cast<const u32x4_t*>(a.o + m * kMlpC + 32 * j + 8 * g);
+    pt.x[j] = *reinterpret_cast<const u32x4_t*>(a.x + tx * kMlpC + 32 * j + 8 * g);
+  }
+}
+
+__device__ __forceinline__ int pair_row_inv(int r) {
+  return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
+}
+
+}  // namespace
+
+template <bool PROJ>
+__global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) {
   constexpr int C = kMlpC, HID = kMlpHid;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* W1s = lds;                 // HID rows x 192 B
   unsigned char* W2s = lds + kMlpW1;        // C rows x 768 B
-  bf16_t* b1s = reinterpret_cast<bf16_t*>(lds + 2 * kMlpW1);
-  bf16_t* vecs = b1s + HID;                 // LN2 gamma, beta, fc2 bias (C each)
+  float* b1s = reinterpret_cast<float*>(lds + 2 * kMlpW1);   // fc1 bias, fp32
+  float* bps = b1s + HID;                                    // projection bias, fp32
+  bf16_t* vecs = reinterpret_cast<bf16_t*>(bps + C);         // LN2 gamma, beta, fc2 bias (C each)
   float2* phi = reinterpret_cast<float2*>(lds + 2 * kMlpW1 + kMlpVec);   // (Phi(x_i), Phi(x_i+1) - Phi(x_i))
+  const bf16_t* __restrict__ W1 = a.W1;
+  const bf16_t* __restrict__ W2 = a.W2;
+  const bf16_t* __restrict__ b1 = a.b1;
+  const int64_t L = a.L;
+  const float eps = a.eps;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, g = lane >> 4;
@@ -317,9 +361,23 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __re
   const int64_t nw = (int64_t)gridDim.x * kMlpWaves;
   int64_t t = (int64_t)blockIdx.x * kMlpWaves + wave;
 
-  // first tile's z^ rows, then the weights (one pass, all threads)
+  // first tile's inputs, then the weights (one pass, all threads)
   ZTile cur;
-  ztile_load(cur, zh, L, t);
+  ProjTileIn pcur;
+  // PROJ: the projection weight as 18 MFMA A fragments, held in registers for
+  // the whole launch; output tile nt covers pair-order rows 16 nt .. + 15
+  bf16x8_t wpf[PROJ ? 6 : 1][3];
+  if constexpr (PROJ) {
+    proj_tile_load(pcur, a, t);
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk)
+        wpf[nt][kk] =
+            *reinterpret_cast<const bf16x8_t*>(a.wp + pair_row_inv(16 * nt + fr) * C + 32 * kk + 8 * g);
+  } else {
+    ztile_load(cur, a.zh, L, t);
+  }
   {
     // all 16-byte chunks of W1 and W2 in flight at once, then into LDS
     constexpr int NCH = HID * (C / 8) / kMlpThreads;   // 9 chunks of each matrix per thread
@@ -340,9 +398,9 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __re
       *reinterpret_cast<u32x4_t*>(W2s + r2 * (HID * 2) + ((q2 ^ (r2 & 15)) << 4)) = w2v[i];
     }
   }
-  for (int c = tid; c < HID / 8; c += kMlpThreads)
-    *reinterpret_cast<u32x4_t*>(b1s + c * 8) =
-        b1 ? *reinterpret_cast<const u32x4_t*>(b1 + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  for (int c = tid; c < HID; c += kMlpThreads) b1s[c] = b1 ? bf2f(b1[c]) : 0.f;
+  if constexpr (PROJ)
+    for (int c = tid; c < C; c += kMlpThreads) bps[c] = a.bp ? bf2f(a.bp[c]) : 0.f;
   for (int i = tid; i < kPhiN; i += kMlpThreads) {
     const float h = 2.0f * kPhiX / kPhiN;
     const float x0 = -kPhiX + h * i, x1 = x0 + h;
@@ -352,7 +410,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __re
   }
   for (int c = tid; c < 3 * (C / 8); c += kMlpThreads) {
     const int which = c / (C / 8), q = c - which * (C / 8);
-    const bf16_t* src = which == 0 ? g2 : (which == 1 ? b2ln : bo);
+    const bf16_t* src = which == 0 ? a.g2 : (which == 1 ? a.b2ln : a.bo);
     *reinterpret_cast<u32x4_t*>(vecs + which * C + q * 8) =
         src ? *reinterpret_cast<const u32x4_t*>(src + q * 8) : u32x4_t{0u, 0u, 0u, 0u};
   }
@@ -361,7 +419,37 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __re
   const int swz1 = (fr >> 2) & 3;   // W1 rows 32c + 16p + fr: ((row >> 2) & 3) = (fr >> 2) & 3
   for (; t < ntiles; t += nw) {
     ZTile nxt;
-    if (t + nw < ntiles) ztile_load(nxt, zh, L, t + nw);
+    ProjTileIn pnxt = pcur;
+    if constexpr (PROJ) {
+      if (t + nw < ntiles) proj_tile_load(pnxt, a, t + nw);
+      // z^ = x + o Wp^T + bp: 6 output tiles (pair order) of 16 tokens, the
+      // accumulators starting at the bias; lane ends with columns
+      // 32j + 8g .. + 7 of token fr, as a ZTile
+      f32x4_t acc[6];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        acc[2 * j] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g);
+        acc[2 * j + 1] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g + 4);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < 6; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wpf[nt][kk], __builtin_bit_cast(bf16x8_t, pcur.o[kk]),
+                                                            acc[nt], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        float xv[8];
+        unpack8(pcur.x[j], xv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cur.z[j][i] = xv[i] + acc[2 * j][i];
+          cur.z[j][4 + i] = xv[4 + i] + acc[2 * j + 1][i];
+        }
+      }
+    } else {
+      if (t + nw < ntiles) ztile_load(nxt, a.zh, L, t + nw);
+    }
     // ---- LN2 of the lane's token (4 lanes share a token: xor 16, 32)
     float s = 0.f;
 #pragma unroll
@@ -398,6 +486,8 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __re
     for (int i = 0; i < 6; ++i) acc2[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int ch = 0; ch < HID / 32; ++ch) {
+      // every LDS read of the chunk (weights of both layers, fc1 bias as the
+      // fc1 accumulator's start) is in flight before the first MFMA
       bf16x8_t w1f[2][3], w2f[6];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -410,18 +500,19 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __re
         const int r = 16 * nt + fr;
         w2f[nt] = *reinterpret_cast<const bf16x8_t*>(W2s + r * (HID * 2) + (((4 * ch + g) ^ (r & 15)) << 4));
       }
-      const u32x4_t hb = *reinterpret_cast<const u32x4_t*>(b1s + 32 * ch + 8 * g);
-      f32x4_t a1[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      f32x4_t a1[2];
+      a1[0] = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g);
+      a1[1] = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g + 4);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < 3; ++kk)
 #pragma unroll
         for (int p = 0; p < 2; ++p) a1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1f[p][kk], af[kk], a1[p], 0, 0, 0);
-      float hbf[8], h[8];
-      unpack8(hb, hbf);
+      float h[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // GELU(x) = x Phi(x), Phi from the table
-        const float x = (i < 4 ? a1[0][i] : a1[1][i - 4]) + hbf[i];
+        const float x = i < 4 ? a1[0][i] : a1[1][i - 4];
         const float u = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f), 0.0f,
                                                 (float)kPhiN - 0.5f);
         const int k = (int)u;
@@ -444,11 +535,42 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const float* __re
           o[i] = cur.z[j][i] + acc2[2 * j][i] + ob[i];
           o[4 + i] = cur.z[j][4 + i] + acc2[2 * j + 1][i] + ob[4 + i];
         }
-        *reinterpret_cast<u32x4_t*>(y + tok * C + 32 * j + 8 * g) = pack8(o);
+        *reinterpret_cast<u32x4_t*>(a.y + tok * C + 32 * j + 8 * g) = pack8(o);
       }
     }
-    cur = nxt;
+    if constexpr (PROJ) pcur = pnxt;
+    else cur = nxt;
   }
+}
+
+namespace {
+template <bool PROJ>
+hipError_t launch_mlp_wave(const MlpArgs& a, hipStream_t st) {
+  const int ncu = device_cu_count();
+  const int64_t tiles = (a.L + 15) / 16;
+  int64_t grid = (tiles + kMlpWaves - 1) / kMlpWaves;
+  if (grid > ncu) grid = ncu;
+  hipError_t e = ensure_dynamic_lds((const void*)mlp_wave_kernel<PROJ>, kMlpLds);
+  if (e != hipSuccess) return e;
+  mlp_wave_kernel<PROJ><<<dim3((unsigned)grid), dim3(kMlpThreads), kMlpLds, st>>>(a);
+  return hipGetLastError();
+}
+}  // namespace
+
+bool proj_mlp_supported(vswin_dtype dt, int C, int hid) { return dt == VSWIN_BF16 && C == 96 && hid == 4 * C; }
+
+hipError_t proj_mlp(const void* o, const void* x, const void* wp, const void* bp, const void* g2, const void* b2ln,
+                    const void* W1, const void* b1, const void* W2, const void* bo, void* y, int64_t L, int C,
+                    float eps, const WinGeo& geo, hipStream_t st) {
+  if (L <= 0) return hipSuccess;
+  if (C != 96) return hipErrorInvalidValue;
+  MlpArgs a{};
+  a.o = (const bf16_t*)o; a.x = (const bf16_t*)x; a.wp = (const bf16_t*)wp; a.bp = (const bf16_t*)bp;
+  a.geo = geo;
+  a.g2 = (const bf16_t*)g2; a.b2ln = (const bf16_t*)b2ln;
+  a.W1 = (const bf16_t*)W1; a.b1 = (const bf16_t*)b1; a.W2 = (const bf16_t*)W2; a.bo = (const bf16_t*)bo;
+  a.y = (bf16_t*)y; a.L = L; a.eps = eps;
+  return launch_mlp_wave<true>(a, st);
 }
 
 bool mlp_fused_supported(vswin_dtype dt, int C, int hid) {
@@ -460,15 +582,12 @@ hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const vo
   if (L <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((L + 63) / 64);
   if (C == 96) {
-    const int ncu = device_cu_count();
-    const int64_t tiles = (L + 15) / 16;
-    int64_t grid = (tiles + kMlpWaves - 1) / kMlpWaves;
-    if (grid > ncu) grid = ncu;
-    hipError_t e = ensure_dynamic_lds((const void*)mlp_wave_kernel, kMlpLds);
-    if (e != hipSuccess) return e;
-    mlp_wave_kernel<<<dim3((unsigned)grid), dim3(kMlpThreads), kMlpLds, st>>>(
-        zh, (const bf16_t*)g2, (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1, (const bf16_t*)W2,
-        (const bf16_t*)bo, (bf16_t*)y, L, eps);
+    MlpArgs a{};
+    a.zh = zh;
+    a.g2 = (const bf16_t*)g2; a.b2ln = (const bf16_t*)b2ln;
+    a.W1 = (const bf16_t*)W1; a.b1 = (const bf16_t*)b1; a.W2 = (const bf16_t*)W2; a.bo = (const bf16_t*)bo;
+    a.y = (bf16_t*)y; a.L = L; a.eps = eps;
+    return launch_mlp_wave<false>(a, st);
   } else if (C == 128)
     hipLaunchKernelGGL(mlp_fused_kernel<128>, dim3(blocks), dim3(256), 0, st, zh, (const bf16_t*)g2,
                        (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1, (const bf16_t*)W2,

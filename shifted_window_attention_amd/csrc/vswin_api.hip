@@ -212,11 +212,20 @@ vswin_status check_msa_weights(const vswin_block_weights* w) {
   return VSWIN_OK;
 }
 
+// Can the block run as qkv (gathering LN1) -> attention -> proj_mlp, the
+// projection fused into the MLP kernel?
+bool block_proj_fused(const Plan& p) {
+  return p.fast && gemm_can_gather(p.dt, p.C) && winproj_supported(p.dt, p.C, p.d, p.N, 1) &&
+         proj_mlp_supported(p.dt, p.C, p.hid);
+}
+
 // qkv -> attention -> proj (+ scatter).  `ga` (nullable) makes the qkv
 // projection gather (and normalise) its rows itself; otherwise `xw` holds the
-// gathered window rows.
+// gathered window rows.  With `no_proj` (gathering fast path only) it stops
+// after the attention, whose output rows are left in `xw`.
 vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weights* w, char* ws,
-                     const void* residual, void* out, bool to_zh, hipStream_t st, const GatherA* ga = nullptr) {
+                     const void* residual, void* out, bool to_zh, hipStream_t st, const GatherA* ga = nullptr,
+                     bool no_proj = false) {
   void* xw = ws + p.off_xw;
   void* q = ws + p.off_q;
   void* k = ws + p.off_k;
@@ -235,10 +244,12 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
     a.tab_ready = p.fast ? 1 : 0;
     if (p.fast) HIPCHECK(attention_mfma(a, st), "attention (mfma)");
     else HIPCHECK(attention_generic(p.dt, a, st), "attention (generic)");
+    if (no_proj) return VSWIN_OK;
     HIPCHECK(out_proj(xw, w->proj_w, w->proj_b, to_zh ? residual : nullptr, out, p.Lp, p.C, p.geo, st),
              "output projection");
     return VSWIN_OK;
   }
+  if (no_proj) return fail(VSWIN_ERR_UNSUPPORTED, "internal: fused projection path not available");
   EpiArgs e{};
   e.kind = Epi::kQKV;
   e.bias = w->qkv_b;
@@ -324,6 +335,15 @@ vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x, const vswin_
   char* ws = (char*)workspace;
   // LN1 + pad + roll + partition: fused into the qkv projection when it can
   // stage whole rows, else a separate gather kernel
+  if (block_proj_fused(p)) {
+    // qkv -> attention -> (proj + residual + LN2 + MLP + residual) in one kernel
+    const GatherA ga{x, w->ln1_g, w->ln1_b, desc->ln_eps, 1, p.geo};
+    CHECK(run_msa(p, desc, w, ws, x, nullptr, true, st, &ga, true));
+    HIPCHECK(proj_mlp(ws + p.off_xw, x, w->proj_w, w->proj_b, w->ln2_g, w->ln2_b, w->fc1_w, w->fc1_b, w->fc2_w,
+                      w->fc2_b, y, p.L, p.C, desc->ln_eps, p.geo, st),
+             "projection + mlp");
+    return VSWIN_OK;
+  }
   if (gemm_can_gather(p.dt, p.C)) {
     const GatherA ga{x, w->ln1_g, w->ln1_b, desc->ln_eps, 1, p.geo};
     CHECK(run_msa(p, desc, w, ws, x, ws + p.off_zh, true, st, &ga));

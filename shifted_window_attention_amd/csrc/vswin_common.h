@@ -49,8 +49,9 @@ struct WinGeo {
   int nws;            // windows per clip
   int pad_visible;    // pads keep their positional label
   int slot_perm;      // window rows in attention slot order (see slot_to_natural)
-  // divisors of the slot -> token map (set by geo_divisors)
+  // divisors of the slot <-> token maps (set by geo_divisors)
   FastDiv fN, fnws, fwpl, fnww, fmhw, fMw;
+  FastDiv fT, fH, fW, fP, fMh;
 };
 
 inline void geo_divisors(WinGeo& g) {
@@ -60,6 +61,11 @@ inline void geo_divisors(WinGeo& g) {
   g.fnww = make_fastdiv((uint32_t)g.nww);
   g.fmhw = make_fastdiv((uint32_t)(g.Mh * g.Mw));
   g.fMw = make_fastdiv((uint32_t)g.Mw);
+  g.fT = make_fastdiv((uint32_t)g.T);
+  g.fH = make_fastdiv((uint32_t)g.H);
+  g.fW = make_fastdiv((uint32_t)g.W);
+  g.fP = make_fastdiv((uint32_t)g.P);
+  g.fMh = make_fastdiv((uint32_t)g.Mh);
 }
 
 // Order of the rows of one window inside the block's buffers.  Natural order
@@ -116,6 +122,24 @@ __host__ __device__ inline int64_t slot_source(const WinGeo& g, int w, int slot,
 __host__ __device__ inline int64_t row_source(const WinGeo& g, int m, int& label) {
   const int w = (int)fdiv((uint32_t)m, g.fN);
   return slot_source(g, w, m - w * g.N, label);
+}
+
+// Window row (slot order of the geometry) that holds token `tok` (flat
+// b,t,h,w): the inverse of row_source on real tokens.  The token sits at the
+// rolled position (o - s) mod n of each padded axis.
+__host__ __device__ inline int token_row(const WinGeo& g, int tok) {
+  const int r1 = (int)fdiv((uint32_t)tok, g.fW), ow = tok - r1 * g.W;
+  const int r2 = (int)fdiv((uint32_t)r1, g.fH), oh = r1 - r2 * g.H;
+  const int b = (int)fdiv((uint32_t)r2, g.fT), ot = r2 - b * g.T;
+  int rt = ot - g.st; if (rt < 0) rt += g.Tp;
+  int rh = oh - g.sh; if (rh < 0) rh += g.Hp;
+  int rw = ow - g.sw; if (rw < 0) rw += g.Wp;
+  const int wt = (int)fdiv((uint32_t)rt, g.fP), pt = rt - wt * g.P;
+  const int wh = (int)fdiv((uint32_t)rh, g.fMh), ph = rh - wh * g.Mh;
+  const int ww = (int)fdiv((uint32_t)rw, g.fMw), pw = rw - ww * g.Mw;
+  const int w = b * g.nws + (wt * g.nwh + wh) * g.nww + ww;
+  const int k = g.slot_perm ? 4 * (((pt >> 2) * g.Mh + ph) * g.Mw + pw) + (pt & 3) : (pt * g.Mh + ph) * g.Mw + pw;
+  return w * g.N + k;
 }
 
 // Rolled-grid label of a slot given the window's rolled origin (rt0, rh0, rw0)

@@ -101,6 +101,13 @@ constexpr int kMfmaMaxN = 512;
 bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a);
 
 // --- fused LN2 -> fc1 -> GELU -> fc2 -> residual (k_mlp.hip) --------------
+// proj_mlp (bf16, C = 96, hid = 4C): the output projection in front as well,
+// y = z^ + MLP(LN2(z^)), z^ = x + o Wp^T + bp with o the attention output in
+// window-row space (gathered per token) and z^ kept in fp32 registers.
+bool proj_mlp_supported(vswin_dtype dt, int C, int hid);
+hipError_t proj_mlp(const void* o, const void* x, const void* wp, const void* bp, const void* g2, const void* b2ln,
+                    const void* W1, const void* b1, const void* W2, const void* bo, void* y, int64_t L, int C,
+                    float eps, const WinGeo& geo, hipStream_t st);
 bool mlp_fused_supported(vswin_dtype dt, int C, int hid);
 hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const void* W1, const void* b1,
                      const void* W2, const void* bo, void* y, int64_t L, int C, float eps, hipStream_t st);
