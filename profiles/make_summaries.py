@@ -82,7 +82,7 @@ Calibration against the copy of known size (262144 KiB read and written): FETCH_
 - kernel source sha256: `{src}`
 
 The kernel fetches {fb / alg_r:.2f}x the algorithmic q/k/V^T bytes (a window shared by two workgroups' runs is read
-by both; each workgroup gathers its head's column of the bias table) and writes the output exactly once.
+by both; each workgroup also copies its head's prepared bias table, built once per call, from L2) and writes the output exactly once.
 """
 
 
