@@ -61,7 +61,6 @@ struct Cfg {
   static constexpr int kWaves = W;
   static constexpr int kQTM = QTM;
   static constexpr int kThreads = 64 * W;
-  static constexpr int kTabIter = (kMaxTab + kThreads - 1) / kThreads;
   static_assert((kMfmaMaxN / 16 + W - 1) / W <= QTM, "a wave's tiles of one window exceed QTM");
   static_assert(W <= kMaxWaves, "too many waves");
 };
@@ -234,31 +233,16 @@ __global__ void __launch_bounds__(256) attn_table_kernel(const bf16_t* __restric
   if (x < L.TS4) out[(size_t)h * L.TS4 + x] = t4_entry(T, L.tg, h, x);
 }
 
-// head h's prepared table: loads issued here, stored by tab_store
+// head h's prepared table into LDS by direct global-to-LDS loads (1 KB per
+// wave instruction); the last instruction's lanes past TS4 stay off
 template <class CF>
-struct TabPre {
-  f32x4_t t[CF::kTabIter];
-};
-
-template <class CF>
-__device__ __forceinline__ void tab_load(TabPre<CF>& tp, const AttnArgs& a, const A5& L, int h) {
-  const int tid = opaque_tid();
+__device__ __forceinline__ void tab_copy(const AttnArgs& a, const A5& L, int h, unsigned char* smem, int wv) {
+  const int lane = threadIdx.x & 63;
   const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.tab4) + (size_t)h * L.TS4;
-#pragma unroll
-  for (int i = 0; i < CF::kTabIter; ++i) {
-    const int x = tid + i * CF::kThreads;
-    if (x < L.TS4) tp.t[i] = src[x];
-  }
-}
-
-template <class CF>
-__device__ __forceinline__ void tab_store(const TabPre<CF>& tp, const A5& L, unsigned char* smem) {
-  const int tid = opaque_tid();
-  f32x4_t* tab = reinterpret_cast<f32x4_t*>(smem + L.off_tab);
-#pragma unroll
-  for (int i = 0; i < CF::kTabIter; ++i) {
-    const int x = tid + i * CF::kThreads;
-    if (x < L.TS4) tab[x] = tp.t[i];
+  const int nb = (L.TS4 + 63) >> 6;
+  for (int b = wv; b < nb; b += CF::kWaves) {
+    if (64 * b + lane < L.TS4)
+      __builtin_amdgcn_global_load_lds(src + 64 * b + lane, (lds_ptr_t)(smem + L.off_tab + 1024 * b), 16, 0, 0);
   }
 }
 
@@ -371,8 +355,10 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   const int lane = threadIdx.x & 63;
   const int fr = lane & 15, g4 = lane >> 4;
   const int N = L.N;
-  const unsigned char* tabb = smem + L.off_tab;
-  const int zone = 16 * (L.TS4 - 1);
+  // table addresses are taken from the LDS base: the query offsets and the
+  // -inf slot carry the table's own offset
+  const unsigned char* tabb = smem;
+  const int zone = (int)L.off_tab + 16 * (L.TS4 - 1);
   const int* lp = reinterpret_cast<const int*>(B + L.off_lp);
   int masked = 0;
 #pragma unroll
@@ -384,7 +370,7 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
     const int qs = 16 * (jt + CF::kWaves * u) + fr;
     // the query's key group: same table base (plus its temporal index) and label
     const int ps = pair_slot(qs >> 2);
-    st.qaddr[u] = 16 * L.A - kp[ps] - 16 * (qs & 3) * L.Rp;
+    st.qaddr[u] = (int)L.off_tab + 16 * L.A - kp[ps] - 16 * (qs & 3) * L.Rp;
     st.qlab[u] = lp[ps];
     u32x4_t qv = qp.q[u];
     if (L.qscale != 1.0f) {
@@ -516,11 +502,7 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
   TileRun run = tile_run<CF>(wv, w0, t0, t1, L.QTT);
   q_load<CF>(qcur, a, L, cur.mem, run.jt, run.cnt);
   stage_kv<CF>(a, L, cur.mem, smem + L.off_buf, wv);
-  {
-    TabPre<CF> tp;
-    tab_load<CF>(tp, a, L, h);
-    tab_store<CF>(tp, L, smem);
-  }
+  tab_copy<CF>(a, L, h, smem, wv);
   stage_labels<CF>(a, L, cur, smem + L.off_buf);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's direct loads are in LDS
   __syncthreads();
