@@ -262,6 +262,8 @@ __device__ __forceinline__ u32x4_t pack8(const float f[8]) {
   return v;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 constexpr int kMlpWaves = 8;
 constexpr int kMlpThreads = 64 * kMlpWaves;
 constexpr int kMlpC = 96, kMlpHid = 4 * kMlpC;
@@ -378,24 +380,22 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
   } else {
     ztile_load(cur, a.zh, L, t);
   }
+  // W1 and W2 go straight from global memory into their swizzled LDS layouts
+  // (global_load_lds: a wave instruction fills 1 KB of consecutive LDS chunks
+  // from per-lane addresses), still in flight while the first tile's
+  // projection and LN2 run; LDS chunk (r, qp) holds global row
+  // pair_row_inv(r), chunk qp ^ swizzle(r)
   {
-    // all 16-byte chunks of W1 and W2 in flight at once, then into LDS
-    constexpr int NCH = HID * (C / 8) / kMlpThreads;   // 9 chunks of each matrix per thread
-    static_assert(NCH * kMlpThreads == HID * (C / 8), "weight staging shape");
-    u32x4_t w1v[NCH], w2v[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * kMlpThreads;
-      w1v[i] = *reinterpret_cast<const u32x4_t*>(W1 + (int64_t)c * 8);
-      w2v[i] = *reinterpret_cast<const u32x4_t*>(W2 + (int64_t)c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * kMlpThreads;
-      const int f1 = c / (C / 8), q1 = c - f1 * (C / 8), r1 = pair_row(f1);
-      *reinterpret_cast<u32x4_t*>(W1s + r1 * (C * 2) + ((q1 ^ ((r1 >> 2) & 3)) << 4)) = w1v[i];
-      const int f2 = c / (HID / 8), q2 = c - f2 * (HID / 8), r2 = pair_row(f2);
-      *reinterpret_cast<u32x4_t*>(W2s + r2 * (HID * 2) + ((q2 ^ (r2 & 15)) << 4)) = w2v[i];
+    constexpr int NB = HID * (C / 8) / 64;   // 1 KB blocks per matrix
+    static_assert(NB * 64 == HID * (C / 8), "weight staging shape");
+    for (int b = wave; b < NB; b += kMlpWaves) {
+      const int c = 64 * b + lane;
+      const int r1 = c / (C / 8), qp1 = c - r1 * (C / 8);
+      __builtin_amdgcn_global_load_lds(W1 + pair_row_inv(r1) * C + ((qp1 ^ ((r1 >> 2) & 3)) << 3),
+                                       (lds_ptr_t)(W1s + 1024 * b), 16, 0, 0);
+      const int r2 = c / (HID / 8), qp2 = c - r2 * (HID / 8);
+      __builtin_amdgcn_global_load_lds(W2 + pair_row_inv(r2) * HID + ((qp2 ^ (r2 & 15)) << 3),
+                                       (lds_ptr_t)(W2s + 1024 * b), 16, 0, 0);
     }
   }
   for (int c = tid; c < HID; c += kMlpThreads) b1s[c] = b1 ? bf2f(b1[c]) : 0.f;
@@ -417,14 +417,12 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
   __syncthreads();
 
   const int swz1 = (fr >> 2) & 3;   // W1 rows 32c + 16p + fr: ((row >> 2) & 3) = (fr >> 2) & 3
-  for (; t < ntiles; t += nw) {
-    ZTile nxt;
-    ProjTileIn pnxt = pcur;
+  // front of a tile: (PROJ) z^ = x + o Wp^T + bp into cur, then LN2 into af
+  bf16x8_t af[3];
+  auto front = [&]() {
     if constexpr (PROJ) {
-      if (t + nw < ntiles) proj_tile_load(pnxt, a, t + nw);
-      // z^ = x + o Wp^T + bp: 6 output tiles (pair order) of 16 tokens, the
-      // accumulators starting at the bias; lane ends with columns
-      // 32j + 8g .. + 7 of token fr, as a ZTile
+      // 6 output tiles (pair order) of 16 tokens, the accumulators starting at
+      // the bias; lane ends with columns 32j + 8g .. + 7 of token fr, as a ZTile
       f32x4_t acc[6];
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
@@ -447,10 +445,8 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
           cur.z[j][4 + i] = xv[4 + i] + acc[2 * j + 1][i];
         }
       }
-    } else {
-      if (t + nw < ntiles) ztile_load(nxt, a.zh, L, t + nw);
     }
-    // ---- LN2 of the lane's token (4 lanes share a token: xor 16, 32)
+    // LN2 of the lane's token (4 lanes share a token: xor 16, 32)
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < 3; ++j)
@@ -470,15 +466,28 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
     q2 += __shfl_xor(q2, 16);
     q2 += __shfl_xor(q2, 32);
     const float rstd = 1.0f / sqrtf(q2 * (1.0f / C) + eps);
-    bf16x8_t af[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      float gg[8], bb[8], a[8];
+      float gg[8], bb[8], v[8];
       unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 32 * j + 8 * g), gg);
       unpack8(*reinterpret_cast<const u32x4_t*>(vecs + C + 32 * j + 8 * g), bb);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = (cur.z[j][e] - mean) * rstd * gg[e] + bb[e];
-      af[j] = __builtin_bit_cast(bf16x8_t, pack8(a));
+      for (int e = 0; e < 8; ++e) v[e] = (cur.z[j][e] - mean) * rstd * gg[e] + bb[e];
+      af[j] = __builtin_bit_cast(bf16x8_t, pack8(v));
+    }
+  };
+  if (t < ntiles) front();
+  // every wave's weight blocks are in LDS (every wave reaches this barrier)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (; t < ntiles; t += nw) {
+    ZTile nxt;
+    ProjTileIn pnxt = pcur;
+    if constexpr (PROJ) {
+      if (t + nw < ntiles) proj_tile_load(pnxt, a, t + nw);
+    } else {
+      if (t + nw < ntiles) ztile_load(nxt, a.zh, L, t + nw);
     }
     // ---- fc1 -> GELU -> fc2 over 12 chunks of 32 hidden units
     f32x4_t acc2[6];
@@ -540,6 +549,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
     }
     if constexpr (PROJ) pcur = pnxt;
     else cur = nxt;
+    if (t + nw < ntiles) front();
   }
 }
 
