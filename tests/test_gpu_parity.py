@@ -180,6 +180,30 @@ def _stack_check(x0, params, shape, dtype, flags=0, label=""):
     return xt
 
 
+# C = 96 bf16 blocks run qkv -> attention -> (projection + MLP in one kernel);
+# these geometries take that path through pads, batches and the clamp
+C96_CASES = [
+    ("padded shifted", 1, (16, 12, 13), (4, 3, 3), 0),
+    ("padded regular", 1, (16, 12, 13), (0, 0, 0), 0),
+    ("temporal pad B=2", 2, (12, 14, 14), (4, 3, 3), 0),
+    ("pads visible", 1, (16, 12, 13), (4, 3, 3), vs.F_PAD_VISIBLE),
+    ("clamp (16,7,7)", 2, (16, 7, 7), (4, 3, 3), 0),
+    ("B=2 non-square", 2, (16, 14, 21), (4, 3, 3), 0),
+]
+
+
+@pytest.mark.parametrize("case", C96_CASES, ids=[c[0] for c in C96_CASES])
+def test_block_c96_fused_projection(case):
+    name, B, size, shift, flags = case
+    say(f"C=96 block {name}")
+    C, heads, window = 96, 3, (8, 7, 7)
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=23)
+    x = _rng_tokens((B, *size, C), "bf16", 5)
+    y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift, flags=flags)
+    _, ref = oracle.block(x, p, heads, window, shift, pad_visible=bool(flags & vs.F_PAD_VISIBLE))
+    check(host64(y), ref, "bf16", f"C=96 block {name}")
+
+
 def test_workload1_fp32_pair():
     say("workload 1: fp32 block pair")
     x, params = synth.gen_workload(1)
