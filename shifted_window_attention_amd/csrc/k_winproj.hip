@@ -59,21 +59,21 @@ __device__ __forceinline__ int wswz(int r) {
 
 // Weight matrix (F x C, row-major) into LDS, row f at row perm(f), chunks
 // swizzled; every load of the thread is issued before its LDS stores.
-template <int C, int F, class Perm>
+template <int C, int F, int THREADS = kWpThreads, class Perm>
 __device__ __forceinline__ void stage_weights(const bf16_t* __restrict__ W, unsigned char* Ws, Perm perm) {
   constexpr int KC = C / 8;
   constexpr int TOTAL = F * KC;
-  constexpr int PER = (TOTAL + kWpThreads - 1) / kWpThreads;
+  constexpr int PER = (TOTAL + THREADS - 1) / THREADS;
   const int tid = threadIdx.x;
   u32x4_t v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int c = tid + i * kWpThreads;
+    const int c = tid + i * THREADS;
     if (c < TOTAL) v[i] = *reinterpret_cast<const u32x4_t*>(W + (int64_t)c * 8);
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int c = tid + i * kWpThreads;
+    const int c = tid + i * THREADS;
     if (c < TOTAL) {
       const int f = c / KC, q = c - f * KC;
       const int r = perm(f);
@@ -106,9 +106,11 @@ struct QkvParams {
   int heads, d;
   FastDiv fd;           // division by d
   WinGeo geo;
-  // workgroups from tile_blocks on write the attention's prepared tables
-  // (tg) of `table` to tab4 instead (none when tab4 is NULL)
+  // the attention's prepared tables (tg) of `table` go to tab4 (none when
+  // tab4 is NULL): written by the waves that get no tile when tab_idle, else
+  // by the workgroups from tile_blocks on
   int tile_blocks;
+  int tab_idle;
   const bf16_t* table;
   f32x4_t* tab4;
   Tab4Geo tg;
@@ -147,16 +149,20 @@ __device__ __forceinline__ void gather_rows(RowTile<C>& rt, const QkvParams& pr,
 
 }  // namespace
 
-// four waves per SIMD when two workgroups fit a CU's LDS (C = 96), else two
+// One workgroup of 16 waves per CU (four waves per SIMD), the weights staged
+// once per CU.
+constexpr int kQkvWaves = 16;
+constexpr int kQkvThreads = 64 * kQkvWaves;
+
 template <int C>
-__global__ void __launch_bounds__(kWpThreads, C == 96 ? 4 : 2) qkv_wave_kernel(QkvParams pr) {
+__global__ void __launch_bounds__(kQkvThreads, 1) qkv_wave_kernel(QkvParams pr) {
   using L = QkvLds<C>;
   constexpr int KS = C / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   if ((int)blockIdx.x >= pr.tile_blocks) {
     const int n = pr.tg.TS4 * pr.tg.heads;
-    for (int e = ((int)blockIdx.x - pr.tile_blocks) * kWpThreads + (int)threadIdx.x; e < n;
-         e += ((int)gridDim.x - pr.tile_blocks) * kWpThreads) {
+    for (int e = ((int)blockIdx.x - pr.tile_blocks) * kQkvThreads + (int)threadIdx.x; e < n;
+         e += ((int)gridDim.x - pr.tile_blocks) * kQkvThreads) {
       const int h = e / pr.tg.TS4;
       pr.tab4[e] = t4_entry(pr.table, pr.tg, h, e - h * pr.tg.TS4);
     }
@@ -168,15 +174,23 @@ __global__ void __launch_bounds__(kWpThreads, C == 96 ? 4 : 2) qkv_wave_kernel(Q
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, g = lane >> 4;
   const int64_t ntiles = ((int64_t)pr.M + 15) / 16;
-  const int64_t nw = (int64_t)pr.tile_blocks * kWpWaves;
-  int64_t t = (int64_t)blockIdx.x * kWpWaves + wave;
+  const int64_t nw = (int64_t)pr.tile_blocks * kQkvWaves;
+  int64_t t = (int64_t)blockIdx.x * kQkvWaves + wave;
   const int vt = pr.vt;
+  if (pr.tab4 && pr.tab_idle && t >= ntiles) {
+    const int n = pr.tg.TS4 * pr.tg.heads;
+    const int nidle = (int)(nw - ntiles);
+    for (int e = (int)(t - ntiles) * 64 + lane; e < n; e += nidle * 64) {
+      const int h = e / pr.tg.TS4;
+      pr.tab4[e] = t4_entry(pr.table, pr.tg, h, e - h * pr.tg.TS4);
+    }
+  }
 
   RowTile<C> cur;
   if (t < ntiles) gather_rows<C>(cur, pr, t);
   // q and k rows (and v rows unless transposed) in pair order
-  stage_weights<C, 3 * C>(pr.w, Ws, [vt](int f) { return (f < 2 * C || !vt) ? pair_row(f) : f; });
-  for (int c = tid; c < 5 * C / 8; c += kWpThreads) {
+  stage_weights<C, 3 * C, kQkvThreads>(pr.w, Ws, [vt](int f) { return (f < 2 * C || !vt) ? pair_row(f) : f; });
+  for (int c = tid; c < 5 * C / 8; c += kQkvThreads) {
     const bf16_t* src = c < 3 * C / 8 ? (pr.bias ? pr.bias + c * 8 : nullptr)
                                       : (!pr.ln ? nullptr
                                                 : (c < 4 * C / 8 ? pr.ln_g + (c - 3 * C / 8) * 8
@@ -424,21 +438,29 @@ hipError_t qkv_proj(const void* x, const void* ln_g, const void* ln_b, float eps
   QkvParams pr{(const bf16_t*)x, (const bf16_t*)ln_g, (const bf16_t*)ln_b, eps, ln, (const bf16_t*)W,
                (const bf16_t*)bias, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v, vt, qscale, (int)M, heads, d,
                make_fastdiv((uint32_t)d), geo};
-  // two workgroups per CU for C = 96 (LDS and the 4-waves-per-SIMD register bound allow it)
-  pr.tile_blocks = (int)wave_grid(M, C == 96 ? 2 : 1);
+  {
+    const int64_t tiles = (M + 15) / 16;
+    int64_t g = (tiles + kQkvWaves - 1) / kQkvWaves;
+    const int64_t cap = device_cu_count();
+    pr.tile_blocks = (int)(g > cap ? cap : (g < 1 ? 1 : g));
+  }
   int extra = 0;
   if (tab4 && table) {
     pr.table = (const bf16_t*)table;
     pr.tab4 = (f32x4_t*)tab4;
     pr.tg = tg;
     const int64_t n = (int64_t)tg.TS4 * tg.heads;
-    extra = (int)((n + kWpThreads - 1) / kWpThreads);
-    if (extra > 64) extra = 64;
+    const int64_t idle = (int64_t)pr.tile_blocks * kQkvWaves - (M + 15) / 16;
+    pr.tab_idle = idle > 0 ? 1 : 0;
+    if (!pr.tab_idle) {
+      extra = (int)((n + kQkvThreads - 1) / kQkvThreads);
+      if (extra > 64) extra = 64;
+    }
   }
   auto go = [&](auto kern, size_t lds) -> hipError_t {
     hipError_t e = ensure_dynamic_lds((const void*)kern, lds);
     if (e != hipSuccess) return e;
-    kern<<<dim3((unsigned)(pr.tile_blocks + extra)), dim3(kWpThreads), lds, st>>>(pr);
+    kern<<<dim3((unsigned)(pr.tile_blocks + extra)), dim3(kQkvThreads), lds, st>>>(pr);
     return hipGetLastError();
   };
   if (C == 96) return go(qkv_wave_kernel<96>, QkvLds<96>::bytes);
