@@ -84,6 +84,66 @@ def cpu_baseline(x, params, shape, min_seconds=12.0, max_reps=20):
                       f"({el:.1f} s, BLAS threads={cores})"}
 
 
+def memory_kernels(vs, torch, stream, launches: int = 20) -> dict:
+    """HBM rates of the standalone permutation / normalisation kernels (the
+    block path fuses them into its GEMMs): the pad + roll + partition gather,
+    the reverse + un-roll scatter with the residual, and LayerNorm, on the
+    Swin-T stage-1 token grid and on the larger Swin-B stage-1 grid (B=8,
+    16x60x60x128, padded to 16x63x63), whose tensors do not stay in cache.
+    Bytes are algorithmic: each tensor once at its stored width."""
+    out = {}
+    shapes = {"swin_t_s1": ((1, 16, 56, 56, 96), (4, 3, 3)), "swin_b_s1_b8": ((8, 16, 60, 60, 128), (4, 3, 3))}
+    g = torch.Generator(device="cuda").manual_seed(4)
+    for name, (shape, shift) in shapes.items():
+        B, T, H, W, C = shape
+        x = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+        gam = torch.ones(C, dtype=torch.bfloat16, device="cuda")
+        bet = torch.zeros(C, dtype=torch.bfloat16, device="cuda")
+        win = vs.vswin_partition_fwd(x, (8, 7, 7), shift, stream=stream)
+        L, Lp = x.numel() // C, win.numel() // C
+        runs = {
+            "gather": (lambda: vs.vswin_partition_fwd(x, (8, 7, 7), shift, stream=stream), (L + Lp) * C * 2),
+            "scatter_residual": (lambda: vs.vswin_reverse_fwd(win, shape, (8, 7, 7), shift, residual=x,
+                                                              stream=stream), 3 * L * C * 2),
+            "layernorm": (lambda: vs.vswin_layernorm_fwd(x, gam, bet, stream=stream), 2 * L * C * 2),
+        }
+        res = {}
+        for k, (fn, nbytes) in runs.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(launches):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / launches
+            gbs = nbytes / (us * 1e-6) / 1e9
+            res[k] = {"us": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 3)}
+        out[name] = res
+    return out
+
+
+def step_percentiles(step, torch, stream, n: int, scrub=None) -> dict:
+    """Per-step times (ms) from HIP events around each step; with `scrub` (a
+    callable run between steps, outside the events) the caches start cold."""
+    ts = []
+    for _ in range(n):
+        if scrub is not None:
+            scrub()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    q = lambda f: ts[min(len(ts) - 1, int(f * (len(ts) - 1) + 0.5))]
+    return {"p10": round(q(0.1), 4), "p50": round(q(0.5), 4), "p90": round(q(0.9), 4), "n": n}
+
+
 def counter_pass():
     """A plain copy of known size (the scale of FETCH_SIZE / WRITE_SIZE), then
     the attention kernel alone on seeded q, k, V^T of the Swin-T stage-1 shape."""
@@ -176,6 +236,12 @@ def main():
         step(stream)
     # eager calls through the binding (host submission stays ahead of the GPU)
     ms, wall = timed(lambda: step(stream), stream)
+    # per-step distribution, warm, then with a 512 MiB scrub between steps (larger
+    # than the 256 MB last-level cache) so that each step starts from HBM
+    warm = step_percentiles(step, torch, stream, 50)
+    scrub_buf = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
+    cold = step_percentiles(step, torch, stream, 20, scrub=lambda: scrub_buf.fill_(1.0))
+    del scrub_buf
     flops = [block_flops(p, s.C, hid) for p in plans]
     step_flops = sum(f["total"] for f in flops)
     tokens_per_step = s.tokens * len(shifts)
@@ -229,6 +295,8 @@ def main():
         "tflops": round(tflops, 2), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "step_gflop": round(step_flops / 1e9, 3), "wall_ms_per_step": round(wall, 4),
         "roofline": roofline,
+        "step_ms_warm": warm, "step_ms_cold": cold,
+        "memory_kernels": memory_kernels(vs, torch, stream),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_np, params, s)
