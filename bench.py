@@ -168,6 +168,16 @@ def counter_pass():
         for _ in range(3):
             vs.vswin_attention_fwd(d, q, k, v, tab, out=o)
     torch.cuda.synchronize()
+    # the standalone gather, scatter + residual and LayerNorm, once each, in this
+    # order, on the Swin-B stage-1 grid (B=8, 16x60x60x128 padded to 16x63x63)
+    shape, C = (8, 16, 60, 60, 128), 128
+    x = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    gam = torch.ones(C, dtype=torch.bfloat16, device="cuda")
+    bet = torch.zeros(C, dtype=torch.bfloat16, device="cuda")
+    win = vs.vswin_partition_fwd(x, (8, 7, 7), (4, 3, 3))
+    vs.vswin_reverse_fwd(win, shape, (8, 7, 7), (4, 3, 3), residual=x)
+    vs.vswin_layernorm_fwd(x, gam, bet)
+    torch.cuda.synchronize()
     print("counter pass done", flush=True)
 
 
@@ -180,8 +190,9 @@ def main():
                     help="attention-kernel launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
-                    help="no timing: one 256 MiB device copy (counter calibration), then 3 attention launches per "
-                         "shift of the stage-1 shape; for rocprofv3 --pmc runs")
+                    help="no timing: one 256 MiB device copy (counter calibration), 3 attention launches per "
+                         "shift of the stage-1 shape, then one gather, scatter and LayerNorm of the Swin-B stage-1 "
+                         "B=8 grid; for rocprofv3 --pmc runs")
     ap.add_argument("--traffic", default=TRAFFIC_SUMMARY,
                     help="counter summary with the attention kernel's HBM bytes per launch")
     args = ap.parse_args()

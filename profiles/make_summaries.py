@@ -34,8 +34,12 @@ def stats(stats_dir: str) -> str:
            "    cd /tmp && export TMPDIR=/tmp && cd -",
            "    rocprofv3 --kernel-trace --stats --output-format csv -d out -o bench -- \\",
            "        python bench.py --steps 10 --warmup 2 --no-cpu-baseline", "",
-           "The run covers 12 block pairs (10 timed + 2 warm-up) and 2 x (5 + 50) standalone attention launches",
-           "for the roofline leg; torch kernels are input generation.", "",
+           "The run covers 12 block pairs (10 timed + 2 warm-up), 70 individually timed pairs (50 warm, then 20 with",
+           "a 512 MiB fill, the torch FillFunctor kernel, between them), 2 x (5 + 50) standalone attention launches",
+           "for the roofline leg, and 23 launches each of the gather (`ln_rows_v8_kernel` with the slot map), the",
+           "scatter + residual (`reverse_v8_kernel`) and LayerNorm (`ln_rows_v8_kernel`) on the Swin-T stage-1 grid",
+           "(<4, 3> instances, C = 96) and the Swin-B stage-1 B=8 grid (<16, 1> instances, C = 128); other torch",
+           "kernels are input generation.", "",
            "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -64,7 +68,8 @@ Commands (one counter per run, one MI355X):
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d out/WRITE_SIZE -o WRITE_SIZE -- python bench.py --counter-pass
 
 `bench.py --counter-pass` copies 256 MiB three times with a plain device copy (`__amd_rocclr_copyBuffer`), then launches
-the attention kernel three times with shift (0,0,0) and three times with shift (4,3,3).
+the attention kernel three times with shift (0,0,0) and three times with shift (4,3,3), then the gather, scatter and
+LayerNorm kernels once each (section at the end).
 
 Per-dispatch counter values (KiB):
 
@@ -83,7 +88,35 @@ Calibration against the copy of known size (262144 KiB read and written): FETCH_
 
 The kernel fetches {fb / alg_r:.2f}x the algorithmic q/k/V^T bytes (a window shared by two workgroups' runs is read
 by both; each workgroup also copies its head's prepared bias table, built once per call, from L2) and writes the output exactly once.
-"""
+""" + memory_traffic(pmc_dir, ff, fw)
+
+
+def memory_traffic(pmc_dir: str, ff: float, fw: float) -> str:
+    """The gather, scatter + residual and LayerNorm dispatches of the counter
+    pass (in that order), Swin-B stage-1 grid B=8, C=128, bf16."""
+    def rows(c):
+        rs = list(csv.DictReader(open(os.path.join(pmc_dir, c, f"{c}_counter_collection.csv"))))
+        rs = [r for r in rs if "ln_rows" in r["Kernel_Name"] or "reverse" in r["Kernel_Name"]]
+        key = "Dispatch_Id" if rs and "Dispatch_Id" in rs[0] else None
+        if key:
+            rs.sort(key=lambda r: int(r[key]))
+        return [float(r["Counter_Value"]) for r in rs]
+    f, w = rows("FETCH_SIZE"), rows("WRITE_SIZE")
+    if len(f) < 3 or len(w) < 3:
+        return ""
+    L, Lp, C = 8 * 16 * 60 * 60, 8 * 16 * 63 * 63, 128
+    alg = [((L + Lp) * C * 2, "read x once, write the padded windows once"),
+           (3 * L * C * 2, "read the windows' real slots and the residual, write y"),
+           (2 * L * C * 2, "read x, write y")]
+    names = ["gather (pad + roll + partition)", "scatter + residual (reverse + un-roll + crop)", "LayerNorm"]
+    out = ["", "## Memory-bound kernels, Swin-B stage-1 grid (B=8, 16x60x60x128 -> 16x63x63), bf16", "",
+           "One dispatch each at the end of the same counter pass, scaled by the same copy calibration.", "",
+           "| kernel | FETCH bytes | WRITE bytes | HBM bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|---|"]
+    for i in range(3):
+        fb, wb = f[i] * 1024 * ff, w[i] * 1024 * fw
+        out.append(f"| {names[i]} | {int(round(fb))} | {int(round(wb))} | {int(round(fb + wb))} | "
+                   f"{alg[i][0]} ({alg[i][1]}) | {(fb + wb) / alg[i][0]:.2f} |")
+    return "\n".join(out) + "\n"
 
 
 if __name__ == "__main__":
