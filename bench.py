@@ -125,6 +125,22 @@ def memory_kernels(vs, torch, stream, launches: int = 20) -> dict:
     return out
 
 
+def mfma_measured_peak(vs, torch, stream, iters: int = 4000) -> float:
+    """TFLOP/s of the library's v_mfma_f32_16x16x32_bf16 throughput kernel with
+    two workgroups of 8 waves per CU (four waves per SIMD)."""
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    flops = vs.vswin_mfma_rate_probe(out, blocks, iters, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        vs.vswin_mfma_rate_probe(out, blocks, iters, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return flops / (e0.elapsed_time(e1) * 1e-3 / 5) / 1e12
+
+
 def step_percentiles(step, torch, stream, n: int, scrub=None) -> dict:
     """Per-step times (ms) from HIP events around each step; with `scrub` (a
     callable run between steps, outside the events) the caches start cold."""
@@ -288,8 +304,11 @@ def main():
     attn_us = sum(kern_us) / len(kern_us)
     achieved = attn_flops / (attn_us * 1e-6) / 1e12
     traffic = counter_traffic(args.traffic) if args.traffic else None
+    measured_peak = mfma_measured_peak(vs, torch, stream)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "measured_mfma_peak": round(measured_peak, 1),
+                "frac_of_measured_peak": round(achieved / measured_peak, 4),
                 "kernel": "attn_mfma_kernel", "avg_us": round(attn_us, 3),
                 "avg_us_regular": round(kern_us[0], 3), "avg_us_shifted": round(kern_us[1], 3),
                 "flops_per_launch": attn_flops}
@@ -304,6 +323,7 @@ def main():
                    "global_batch": s.B, "tokens_per_block": s.tokens, "blocks_per_step": len(shifts),
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 2), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_measured_peak_frac": round(tflops / measured_peak, 4),
         "step_gflop": round(step_flops / 1e9, 3), "wall_ms_per_step": round(wall, 4),
         "roofline": roofline,
         "step_ms_warm": warm, "step_ms_cold": cold,

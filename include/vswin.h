@@ -228,6 +228,15 @@ vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, i
                                    const void* b, float eps, void* y, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Measurement helper, not part of the block: launches `blocks` workgroups of
+ * 512 threads that each issue `iters` rounds of 8 independent
+ * v_mfma_f32_16x16x32_bf16 per wave (16384 FLOP each), so a caller timing it
+ * on `stream` gets the MFMA rate the device sustains (FLOP = blocks * 8 waves
+ * * 8 * iters * 16384).  out: device buffer of blocks * 512 floats (written,
+ * values meaningless).  Errors: VSWIN_ERR_INVALID_ARG for blocks < 1,
+ * iters < 1 or a NULL / unaligned out; VSWIN_ERR_HIP for a launch failure.    */
+vswin_status vswin_mfma_rate_probe(float* out, int32_t blocks, int32_t iters, void* stream);
+
 const char* vswin_status_string(vswin_status s);
 const char* vswin_last_error(void);
 int32_t vswin_abi_version(void);

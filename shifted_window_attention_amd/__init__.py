@@ -23,7 +23,7 @@ __all__ = [
     "vswin_plan_query", "vswin_block_fwd", "vswin_window_msa_fwd", "vswin_attention_fwd",
     "vswin_index_map",
     "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
-    "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd",
+    "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd", "vswin_mfma_rate_probe",
     "F_PAD_VISIBLE", "F_CLAMP_STRICT", "F_MASK_M100", "F_TABLES_READY", "LIB_PATH",
 ]
 
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
         "vswin_status_string": (ctypes.c_char_p, [i32]),
         "vswin_last_error": (ctypes.c_char_p, []),
         "vswin_abi_version": (i32, []),
+        "vswin_mfma_rate_probe": (i32, [vp, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -259,6 +260,16 @@ def vswin_reverse_fwd(windows: torch.Tensor, shape, window, shift, *, residual=N
     _check(lib().vswin_reverse_fwd(ctypes.byref(d), _ptr(windows), _ptr(residual), _ptr(y),
                                    _stream(stream)))
     return y
+
+
+def vswin_mfma_rate_probe(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """Launch the MFMA throughput kernel (measurement helper; see include/vswin.h).
+    out: float32 device tensor of >= blocks * 512 elements.  Returns the FLOPs
+    one launch performs."""
+    if out.dtype != torch.float32 or out.numel() < blocks * 512:
+        raise ValueError("out must be float32 with at least blocks * 512 elements")
+    _check(lib().vswin_mfma_rate_probe(_ptr(out), blocks, iters, _stream(stream)))
+    return blocks * 8 * 8 * iters * 16384
 
 
 def vswin_layernorm_fwd(x: torch.Tensor, g: torch.Tensor, b: torch.Tensor, eps: float = 1e-5,

@@ -426,6 +426,13 @@ vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const vo
   return VSWIN_OK;
 }
 
+vswin_status vswin_mfma_rate_probe(float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (blocks < 1 || iters < 1) return fail(VSWIN_ERR_INVALID_ARG, "blocks=%d iters=%d", blocks, iters);
+  CHECK(check_ptr(out, "out"));
+  HIPCHECK(mfma_rate(out, blocks, iters, (hipStream_t)stream), "mfma rate probe");
+  return VSWIN_OK;
+}
+
 vswin_status vswin_index_map(const vswin_desc* desc, int32_t* map, uint8_t* region, void* stream) {
   Plan p{};
   CHECK(make_plan(desc, p, false));

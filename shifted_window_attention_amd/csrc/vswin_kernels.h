@@ -112,6 +112,11 @@ bool mlp_fused_supported(vswin_dtype dt, int C, int hid);
 hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const void* W1, const void* b1,
                      const void* W2, const void* bo, void* y, int64_t L, int C, float eps, hipStream_t st);
 
+// --- measurement helper (k_probe.hip) --------------------------------------
+// blocks x 512 threads of v_mfma_f32_16x16x32_bf16 chains: 8 per wave per
+// round, `iters` rounds; out holds blocks * 512 floats
+hipError_t mfma_rate(float* out, int blocks, int iters, hipStream_t st);
+
 // --- patch embedding / merging gathers (k_patch.hip) ----------------------
 hipError_t patch_gather(vswin_dtype dt, const void* video, void* out, int B, int Cin, int T, int H, int W,
                         int pt, int ph, int pw, hipStream_t st);

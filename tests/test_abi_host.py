@@ -157,3 +157,11 @@ def test_empty_batch_is_a_no_op():
     assert p["num_windows"] == 0 and p["tokens"] == 0
     # nothing is enqueued, so this runs without a GPU
     assert _call_block(d, 0x100000, _fake_weights(), 0x200000, None, 0) == 0
+
+
+def test_mfma_rate_probe_rejects_bad_arguments():
+    """The measurement helper validates its arguments on the host (no launch)."""
+    L = vs.lib()
+    for blocks, iters in [(0, 10), (1, 0), (-3, 5)]:
+        assert L.vswin_mfma_rate_probe(None, blocks, iters, None) == -1
+    assert L.vswin_mfma_rate_probe(None, 1, 1, None) == -1   # NULL out

@@ -423,3 +423,14 @@ def test_attention_prepared_tables_reuse():
     assert torch.equal(o1, o1r)
     assert torch.equal(o2, o2f)
     assert not torch.equal(o1, o2)
+
+
+def test_mfma_rate_probe_runs():
+    """The MFMA throughput helper launches and leaves finite values; the FLOP
+    count it reports is blocks x 8 waves x 8 MFMAs x iters x 16384."""
+    say("mfma rate probe")
+    out = torch.full((4 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    flops = vs.vswin_mfma_rate_probe(out, 4, 16)
+    torch.cuda.synchronize()
+    assert flops == 4 * 8 * 8 * 16 * 16384
+    assert torch.isfinite(out).all()
