@@ -2,11 +2,12 @@
 //   per (window, head): S = q k^T / sqrt(d) + B[idx(i, j)], masked pairs
 //   excluded, P = softmax_j(S), O = P v, heads concatenated as h*32 + e.
 //
-// Work split.  The workgroups (W waves, one per CU) are divided among the
-// heads; the query tiles (16 queries) of one head's windows form a list and
-// each of that head's workgroups takes an equal contiguous run of it, so a
-// workgroup copies its head's prepared bias table (built once per call) to
-// LDS once.  A window's K and V^T are staged once in LDS for all of the run's
+// Work split.  The query tiles (16 queries) of all (head, window) items,
+// head-major, form one list; each workgroup (W waves, one per CU) takes an
+// equal contiguous run of it and copies the run's head's prepared bias table
+// (built once per call) to LDS, again only where the run crosses into the next
+// head.  At Swin-T stage 1 every run is 1.5 windows and spans exactly two
+// windows.  A window's K and V^T are staged once in LDS for all of the run's
 // tiles of that window by direct global-to-LDS loads, and the next window's
 // are in flight while the current one is computed (two LDS buffers when they
 // fit, else one).  Waves own tiles, not steps: inside a window no barrier is
@@ -71,7 +72,7 @@ struct A5 {
   int Rp, Rw, R, TD, TH, A;   // table: temporal stride R', row stride, true R, extents, query base
   int TS4;                    // 4-tuples incl. the -inf one at the end
   int nW, heads;
-  FastDiv fdRp, fdRw, fdKC, fdH;
+  FastDiv fdRp, fdRw, fdKC, fdH, fdNW;
   Tab4Geo tg;                 // the prepared table (same extents as above)
   float qscale;               // multiplier applied to q on load (1 when pre-scaled)
   int force_max;
@@ -88,15 +89,18 @@ struct QState {
 };
 
 struct Win {          // one (head, window) item
-  int w, mem;         // window, item index in q/k/v (w * heads + h)
+  int h, w, mem;      // head, window, item index in q/k/v (w * heads + h)
   int rt0, rh0, rw0;  // rolled origin of the window
 };
 
-__device__ __forceinline__ Win window_of(const AttnArgs& a, const A5& L, int h, int w) {
+// item it of the head-major work list: head it / nW, window it % nW
+__device__ __forceinline__ Win window_of(const AttnArgs& a, const A5& L, int it) {
   const WinGeo& g = a.geo;
   Win r;
+  r.h = (int)fdiv((uint32_t)it, L.fdNW);
+  const int w = it - r.h * L.nW;
   r.w = w;
-  r.mem = w * L.heads + h;
+  r.mem = w * L.heads + r.h;
   const int wr = w - (int)fdiv((uint32_t)w, g.fnws) * g.nws;
   const int wt = (int)fdiv((uint32_t)wr, g.fwpl);
   const int rem = wr - wt * g.nwh * g.nww;
@@ -459,7 +463,7 @@ __device__ __forceinline__ void tiles_dispatch(int cnt, const AttnArgs& a, const
 
 // Tile t of the workgroup's run [t0, t1) belongs to wave (t - t0) mod W, so
 // the waves' totals over the run differ by at most one tile.  Wave wv's
-// tiles of window w: jt, jt + W, ... (cnt of them) of the window's list.
+// tiles of item w: jt, jt + W, ... (cnt of them) of the item's list.
 struct TileRun {
   int jt, cnt;
 };
@@ -485,41 +489,41 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
   int b = blockIdx.x;
   const int G = gridDim.x;
   if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
-  // this workgroup's head and its run of the head's tile list
-  const int h = (int)(((int64_t)(b + 1) * L.heads - 1) / G);
-  const int gb = (int)((int64_t)h * G / L.heads);
-  const int gh = (int)((int64_t)(h + 1) * G / L.heads) - gb;
-  const int64_t th = (int64_t)L.nW * L.QTT;
-  const int64_t t0 = (int64_t)(b - gb) * th / gh, t1 = (int64_t)(b - gb + 1) * th / gh;
+  // The query tiles of all (head, window) items, head-major, form one list and
+  // each workgroup takes an equal contiguous run of it: with 1.5 windows per
+  // workgroup every run spans exactly two windows.  A run that crosses into
+  // the next head reloads the bias table at that window boundary.
+  const int64_t total = (int64_t)L.heads * L.nW * L.QTT;
+  const int64_t t0 = (int64_t)b * total / G, t1 = (int64_t)(b + 1) * total / G;
   if (t0 >= t1) return;
-  const int w0 = (int)(t0 / L.QTT), w1 = (int)((t1 - 1) / L.QTT);
+  const int i0 = (int)(t0 / L.QTT), i1 = (int)((t1 - 1) / L.QTT);
 
   int* kp = reinterpret_cast<int*>(smem + L.off_kp);
   stage_offsets<CF>(a, L, kp);
   zero_pads<CF>(L, smem);
   QPre<CF> qcur, qnext;
-  Win cur = window_of(a, L, h, w0);
-  TileRun run = tile_run<CF>(wv, w0, t0, t1, L.QTT);
+  Win cur = window_of(a, L, i0);
+  TileRun run = tile_run<CF>(wv, i0, t0, t1, L.QTT);
   q_load<CF>(qcur, a, L, cur.mem, run.jt, run.cnt);
   stage_kv<CF>(a, L, cur.mem, smem + L.off_buf, wv);
-  tab_copy<CF>(a, L, h, smem, wv);
+  tab_copy<CF>(a, L, cur.h, smem, wv);
   stage_labels<CF>(a, L, cur, smem + L.off_buf);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's direct loads are in LDS
   __syncthreads();
 
   // Window k of the run sits in buffer k & 1 (two buffers) or 0; the next
   // window is staged while this one is computed (after it, with one buffer).
-  const int nwin = w1 - w0 + 1;
+  const int nwin = i1 - i0 + 1;
   for (int k = 0; k < nwin; ++k) {
-    const int w = w0 + k;
+    const int it = i0 + k;
     const int buf = L.NB == 2 ? (k & 1) : 0;
     const unsigned char* B = smem + L.off_buf + (size_t)buf * L.buf_bytes;
     const bool more = k + 1 < nwin;
     Win nxt{};
     TileRun rnext{};
     if (more) {
-      nxt = window_of(a, L, h, w + 1);
-      rnext = tile_run<CF>(wv, w + 1, t0, t1, L.QTT);
+      nxt = window_of(a, L, it + 1);
+      rnext = tile_run<CF>(wv, it + 1, t0, t1, L.QTT);
       q_load<CF>(qnext, a, L, nxt.mem, rnext.jt, rnext.cnt);
       if (L.NB == 2) {
         unsigned char* Bn = smem + L.off_buf + (size_t)(buf ^ 1) * L.buf_bytes;
@@ -527,7 +531,7 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
         stage_labels<CF>(a, L, nxt, Bn);
       }
     }
-    tiles_dispatch<CF>(run.cnt, a, L, cur, h, run.jt, qcur, B, smem, kp);
+    tiles_dispatch<CF>(run.cnt, a, L, cur, cur.h, run.jt, qcur, B, smem, kp);
     if (more) {
       if (L.NB == 1) {
         __syncthreads();
@@ -535,11 +539,16 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
         stage_kv<CF>(a, L, nxt.mem, Bn, wv);
         stage_labels<CF>(a, L, nxt, Bn);
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (nxt.h != cur.h) {   // every wave is done with the old table
+        tab_copy<CF>(a, L, nxt.h, smem, wv);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
       cur = nxt;
       run = rnext;
       qcur = qnext;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
     }
   }
 }
@@ -572,6 +581,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.fdRw = make_fastdiv((uint32_t)L.Rw);
   L.fdKC = make_fastdiv((uint32_t)kc);
   L.fdH = make_fastdiv((uint32_t)a.heads);
+  L.fdNW = make_fastdiv((uint32_t)L.nW);
   L.tg = tab4_geo(a.rel, a.heads);
   L.qscale = a.q_scaled ? 1.0f : kLog2e / sqrtf((float)a.d);
   L.force_max = a.force_max;
