@@ -254,7 +254,8 @@ __device__ __forceinline__ void tab_copy(const AttnArgs& a, const A5& L, int h, 
 //   MODE 0: P = exp2(x); 1: row max of x only; 2: P = exp2(x - max).
 //   SEL: per key group, masked / dummy groups read the -inf 4-tuple.
 //   gk / lk: this step's key-group offsets / labels for lane group g4.
-template <int MODE, bool SEL, int QT>
+//   HALF: keys 32p + 16 .. + 31 are all padding; that half is skipped (P = 0).
+template <int MODE, bool SEL, int QT, bool HALF = false>
 __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict__ B, const A5& L,
                                           const unsigned char* __restrict__ tabb, int2 gk, int2 lk, int zone,
                                           const bf16x8_t& ones, QState<QT>& st) {
@@ -262,7 +263,8 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
   const int fr = lane & 15, g4 = lane >> 4;
   const int sw = (fr >> 2) & 3;
   const bf16x8_t kA = *reinterpret_cast<const bf16x8_t*>(B + (32 * p + fr) * 64 + ((g4 ^ sw) << 4));
-  const bf16x8_t kB = *reinterpret_cast<const bf16x8_t*>(B + (32 * p + 16 + fr) * 64 + ((g4 ^ sw) << 4));
+  bf16x8_t kB = bf16x8_t{};
+  if (!HALF) kB = *reinterpret_cast<const bf16x8_t*>(B + (32 * p + 16 + fr) * 64 + ((g4 ^ sw) << 4));
   bf16x8_t vA0 = bf16x8_t{}, vA1 = bf16x8_t{};
   if (MODE != 1) {
     const int d0 = 8 * (fr >> 2) + (fr & 3);
@@ -279,25 +281,26 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
       adB = (lk.y == st.qlab[u]) ? adB : zone;
     }
     tA[u] = *reinterpret_cast<const f32x4_t*>(tabb + adA);
-    tB[u] = *reinterpret_cast<const f32x4_t*>(tabb + adB);
+    if (!HALF) tB[u] = *reinterpret_cast<const f32x4_t*>(tabb + adB);
   }
   // every LDS read of the step is in flight before the first MFMA waits on one
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     const f32x4_t sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, st.q[u], tA[u], 0, 0, 0);
-    const f32x4_t sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, st.q[u], tB[u], 0, 0, 0);
+    f32x4_t sB = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (!HALF) sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, st.q[u], tB[u], 0, 0, 0);
     if (MODE == 1) {
       float m = st.mrow[u];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(sA[i], sB[i]));
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, HALF ? sA[i] : fmaxf(sA[i], sB[i]));
       st.mrow[u] = m;
     } else {
       float pA[4], pB[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pA[i] = __builtin_amdgcn_exp2f(MODE == 2 ? sA[i] - st.mrow[u] : sA[i]);
-        pB[i] = __builtin_amdgcn_exp2f(MODE == 2 ? sB[i] - st.mrow[u] : sB[i]);
+        pB[i] = HALF ? 0.f : __builtin_amdgcn_exp2f(MODE == 2 ? sB[i] - st.mrow[u] : sB[i]);
       }
       u32x4_t pk;
       pk[0] = pack_bf16x2(pA[0], pA[1]);
@@ -321,7 +324,10 @@ __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, c
   const int nclean = L.N >> 5;   // steps whose 32 keys are all real
   int2 gk = kp2[g4];
   int2 lk = lp2[g4];
-  for (int p = 0; p < L.NP; ++p) {
+  // the last step's second 16 keys are all padding when N mod 32 is in 1..16
+  const bool half = L.N - 32 * (L.NP - 1) <= 16;
+  const int full = half ? L.NP - 1 : L.NP;
+  for (int p = 0; p < full; ++p) {
     const int pn = p + 1 < L.NP ? p + 1 : p;
     const int2 gkn = kp2[4 * pn + g4];
     const int2 lkn = lp2[4 * pn + g4];
@@ -330,6 +336,7 @@ __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, c
     gk = gkn;
     lk = lkn;
   }
+  if (half) attn_step<MODE, true, QT, true>(L.NP - 1, B, L, tabb, gk, lk, zone, ones, st);
 }
 
 // The wave's QT query tiles jt, jt + W, ... of one window.
