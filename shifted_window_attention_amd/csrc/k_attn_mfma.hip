@@ -56,13 +56,22 @@ constexpr int kMaxTab = 4096;     // table 4-tuples held in LDS at most
 constexpr int kDummyLab = 0x7fff0000;
 constexpr size_t kLdsMax = 160 * 1024;
 
-// W waves per workgroup; a wave carries at most QTM query tiles of a window.
-template <int W, int QTM>
+// Temporal stride of the scalar bias table for the 7 x 7 spatial window
+// (R = 169): a compile-time constant, so a 4-tuple is two ds_read2_b32.
+constexpr int kBigRp = 180;
+
+// W waves per workgroup; a wave carries at most QTM query tiles of a window,
+// in groups of at most 4.  BIG: windows of more than kMfmaMaxN tokens, with
+// the scalar bias table and one K / V^T buffer.
+template <int W, int QTM, bool BIG = false>
 struct Cfg {
   static constexpr int kWaves = W;
   static constexpr int kQTM = QTM;
+  static constexpr bool kBig = BIG;
+  static constexpr int kTabEs = BIG ? 4 : 16;   // bytes per table index step
   static constexpr int kThreads = 64 * W;
-  static_assert((kMfmaMaxN / 16 + W - 1) / W <= QTM, "a wave's tiles of one window exceed QTM");
+  static_assert(((BIG ? kMfmaBigN : kMfmaMaxN) / 16 + W - 1) / W <= QTM, "a wave's tiles of one window exceed QTM");
+  static_assert(QTM <= 4 || QTM == 8, "tile groups of 4");
   static_assert(W <= kMaxWaves, "too many waves");
 };
 
@@ -70,7 +79,8 @@ struct A5 {
   int N, NPAD, NP, QTT, NB;
   int pitch_v;                // V^T row pitch (16-byte chunks)
   int Rp, Rw, R, TD, TH, A;   // table: temporal stride R', row stride, true R, extents, query base
-  int TS4;                    // 4-tuples incl. the -inf one at the end
+  int TS4;                    // 16-byte table entries per head
+  int zone;                   // LDS byte address of the -inf 4-tuple
   int nW, heads;
   FastDiv fdRp, fdRw, fdKC, fdH, fdNW;
   Tab4Geo tg;                 // the prepared table (same extents as above)
@@ -215,6 +225,7 @@ __device__ __forceinline__ void stage_labels(const AttnArgs& a, const A5& L, con
 // key-group table offsets (bytes; the same for every window)
 template <class CF>
 __device__ __forceinline__ void stage_offsets(const AttnArgs& a, const A5& L, int* kp) {
+  constexpr int ES = CF::kTabEs;
   const WinGeo& g = a.geo;
   const int mhw = g.Mh * g.Mw;
   for (int m = (int)threadIdx.x; m < L.NP * 8; m += CF::kThreads) {
@@ -222,7 +233,7 @@ __device__ __forceinline__ void stage_offsets(const AttnArgs& a, const A5& L, in
     if (m < L.N / 4) {
       const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
       const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
-      off = 16 * (4 * aa * L.Rp + kh * L.Rw + kw);
+      off = ES * (4 * aa * L.Rp + kh * L.Rw + kw);
     }
     kp[pair_slot(m)] = off;
   }
@@ -234,7 +245,7 @@ __global__ void __launch_bounds__(256) attn_table_kernel(const bf16_t* __restric
                                                          const A5 L) {
   const int x = blockIdx.x * 256 + (int)threadIdx.x;
   const int h = blockIdx.y;
-  if (x < L.TS4) out[(size_t)h * L.TS4 + x] = t4_entry(T, L.tg, h, x);
+  if (x < L.TS4) out[(size_t)h * L.TS4 + x] = tab_entry(T, L.tg, h, x);
 }
 
 // head h's prepared table into LDS by direct global-to-LDS loads (1 KB per
@@ -255,7 +266,8 @@ __device__ __forceinline__ void tab_copy(const AttnArgs& a, const A5& L, int h, 
 //   SEL: per key group, masked / dummy groups read the -inf 4-tuple.
 //   gk / lk: this step's key-group offsets / labels for lane group g4.
 //   HALF: keys 32p + 16 .. + 31 are all padding; that half is skipped (P = 0).
-template <int MODE, bool SEL, int QT, bool HALF = false>
+//   BIG: scalar bias table (a 4-tuple is 4 floats kBigRp apart).
+template <int MODE, bool SEL, int QT, bool HALF, bool BIG>
 __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict__ B, const A5& L,
                                           const unsigned char* __restrict__ tabb, int2 gk, int2 lk, int zone,
                                           const bf16x8_t& ones, QState<QT>& st) {
@@ -280,8 +292,17 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
       adA = (lk.x == st.qlab[u]) ? adA : zone;
       adB = (lk.y == st.qlab[u]) ? adB : zone;
     }
-    tA[u] = *reinterpret_cast<const f32x4_t*>(tabb + adA);
-    if (!HALF) tB[u] = *reinterpret_cast<const f32x4_t*>(tabb + adB);
+    if constexpr (BIG) {
+      const float* sa = reinterpret_cast<const float*>(tabb + adA);
+      tA[u] = f32x4_t{sa[0], sa[kBigRp], sa[2 * kBigRp], sa[3 * kBigRp]};
+      if (!HALF) {
+        const float* sb = reinterpret_cast<const float*>(tabb + adB);
+        tB[u] = f32x4_t{sb[0], sb[kBigRp], sb[2 * kBigRp], sb[3 * kBigRp]};
+      }
+    } else {
+      tA[u] = *reinterpret_cast<const f32x4_t*>(tabb + adA);
+      if (!HALF) tB[u] = *reinterpret_cast<const f32x4_t*>(tabb + adB);
+    }
   }
   // every LDS read of the step is in flight before the first MFMA waits on one
   __builtin_amdgcn_sched_barrier(0);
@@ -316,7 +337,7 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
 }
 
 // One pass over the keys; the next step's offsets and labels are read a step ahead.
-template <int MODE, bool MASKED, int QT>
+template <int MODE, bool MASKED, int QT, bool BIG>
 __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, const unsigned char* tabb,
                                           const int2* kp2, int zone, const bf16x8_t& ones, QState<QT>& st) {
   const int g4 = (threadIdx.x & 63) >> 4;
@@ -331,12 +352,12 @@ __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, c
     const int pn = p + 1 < L.NP ? p + 1 : p;
     const int2 gkn = kp2[4 * pn + g4];
     const int2 lkn = lp2[4 * pn + g4];
-    if (MASKED || p >= nclean) attn_step<MODE, true, QT>(p, B, L, tabb, gk, lk, zone, ones, st);
-    else attn_step<MODE, false, QT>(p, B, L, tabb, gk, lk, zone, ones, st);
+    if (MASKED || p >= nclean) attn_step<MODE, true, QT, false, BIG>(p, B, L, tabb, gk, lk, zone, ones, st);
+    else attn_step<MODE, false, QT, false, BIG>(p, B, L, tabb, gk, lk, zone, ones, st);
     gk = gkn;
     lk = lkn;
   }
-  if (half) attn_step<MODE, true, QT, true>(L.NP - 1, B, L, tabb, gk, lk, zone, ones, st);
+  if (half) attn_step<MODE, true, QT, true, BIG>(L.NP - 1, B, L, tabb, gk, lk, zone, ones, st);
 }
 
 // The wave's QT query tiles jt, jt + W, ... of one window.
@@ -359,7 +380,8 @@ __device__ __forceinline__ void q_load(QPre<CF>& qp, const AttnArgs& a, const A5
   }
 }
 
-template <class CF, int QT>
+// The wave's tiles U0 .. U0 + QT - 1 of its list for this window.
+template <class CF, int QT, int U0>
 __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const Win& wi, int h, int jt,
                                            const QPre<CF>& qp, const unsigned char* B, const unsigned char* smem,
                                            const int* kp) {
@@ -369,7 +391,9 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   // table addresses are taken from the LDS base: the query offsets and the
   // -inf slot carry the table's own offset
   const unsigned char* tabb = smem;
-  const int zone = (int)L.off_tab + 16 * (L.TS4 - 1);
+  constexpr int ES = CF::kTabEs;
+  constexpr bool BIG = CF::kBig;
+  const int zone = L.zone;
   const int* lp = reinterpret_cast<const int*>(B + L.off_lp);
   int masked = 0;
 #pragma unroll
@@ -378,12 +402,12 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   QState<QT> st;
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
-    const int qs = 16 * (jt + CF::kWaves * u) + fr;
+    const int qs = 16 * (jt + CF::kWaves * (U0 + u)) + fr;
     // the query's key group: same table base (plus its temporal index) and label
     const int ps = pair_slot(qs >> 2);
-    st.qaddr[u] = (int)L.off_tab + 16 * L.A - kp[ps] - 16 * (qs & 3) * L.Rp;
+    st.qaddr[u] = (int)L.off_tab + ES * L.A - kp[ps] - ES * (qs & 3) * L.Rp;
     st.qlab[u] = lp[ps];
-    u32x4_t qv = qp.q[u];
+    u32x4_t qv = qp.q[U0 + u];
     if (L.qscale != 1.0f) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) qv[e] = pack_bf16x2(bflo(qv[e]) * L.qscale, bfhi(qv[e]) * L.qscale);
@@ -409,12 +433,12 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   bool exact = L.force_max != 0;
   if (!exact) {
     clear();
-    if (masked) attn_pass<0, true, QT>(B, L, tabb, kp2, zone, ones, st);
-    else attn_pass<0, false, QT>(B, L, tabb, kp2, zone, ones, st);
+    if (masked) attn_pass<0, true, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<0, false, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
     bool bad = false;
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
-      const int qs = 16 * (jt + CF::kWaves * u) + fr;
+      const int qs = 16 * (jt + CF::kWaves * (U0 + u)) + fr;
       const float sum = st.os[u][0];
       float t = 0.f;
 #pragma unroll
@@ -425,8 +449,8 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   }
   if (exact) {
     clear();
-    if (masked) attn_pass<1, true, QT>(B, L, tabb, kp2, zone, ones, st);
-    else attn_pass<1, false, QT>(B, L, tabb, kp2, zone, ones, st);
+    if (masked) attn_pass<1, true, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<1, false, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       float m = st.mrow[u];
@@ -434,15 +458,15 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
       m = fmaxf(m, __shfl_xor(m, 32));
       st.mrow[u] = (m == -INFINITY) ? 0.f : m;
     }
-    if (masked) attn_pass<2, true, QT>(B, L, tabb, kp2, zone, ones, st);
-    else attn_pass<2, false, QT>(B, L, tabb, kp2, zone, ones, st);
+    if (masked) attn_pass<2, true, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<2, false, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
   }
 
   // lane: query fr, output features 8 g4 .. + 7 of head h
   bf16_t* Og = reinterpret_cast<bf16_t*>(a.o);
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
-    const int qs = 16 * (jt + CF::kWaves * u) + fr;
+    const int qs = 16 * (jt + CF::kWaves * (U0 + u)) + fr;
     if (qs >= N) continue;
     const float inv = __builtin_amdgcn_rcpf(st.os[u][0]);
     u32x4_t pk;
@@ -454,18 +478,19 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   }
 }
 
-template <class CF>
+// tiles U0 .. U0 + cnt - 1 (cnt <= 4) of the wave's list for this window
+template <class CF, int U0>
 __device__ __forceinline__ void tiles_dispatch(int cnt, const AttnArgs& a, const A5& L, const Win& wi, int h, int jt,
                                                const QPre<CF>& qp, const unsigned char* B, const unsigned char* smem,
                                                const int* kp) {
   if constexpr (CF::kQTM >= 4) {
-    if (cnt == 4) { attn_tiles<CF, 4>(a, L, wi, h, jt, qp, B, smem, kp); return; }
+    if (cnt == 4) { attn_tiles<CF, 4, U0>(a, L, wi, h, jt, qp, B, smem, kp); return; }
   }
   if constexpr (CF::kQTM >= 3) {
-    if (cnt == 3) { attn_tiles<CF, 3>(a, L, wi, h, jt, qp, B, smem, kp); return; }
+    if (cnt == 3) { attn_tiles<CF, 3, U0>(a, L, wi, h, jt, qp, B, smem, kp); return; }
   }
-  if (cnt == 2) { attn_tiles<CF, 2>(a, L, wi, h, jt, qp, B, smem, kp); return; }
-  if (cnt == 1) attn_tiles<CF, 1>(a, L, wi, h, jt, qp, B, smem, kp);
+  if (cnt == 2) { attn_tiles<CF, 2, U0>(a, L, wi, h, jt, qp, B, smem, kp); return; }
+  if (cnt == 1) attn_tiles<CF, 1, U0>(a, L, wi, h, jt, qp, B, smem, kp);
 }
 
 // Tile t of the workgroup's run [t0, t1) belongs to wave (t - t0) mod W, so
@@ -531,15 +556,22 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
     if (more) {
       nxt = window_of(a, L, it + 1);
       rnext = tile_run<CF>(wv, it + 1, t0, t1, L.QTT);
-      q_load<CF>(qnext, a, L, nxt.mem, rnext.jt, rnext.cnt);
+      // (BIG: after the compute, keeping its registers free)
+      if constexpr (!CF::kBig) q_load<CF>(qnext, a, L, nxt.mem, rnext.jt, rnext.cnt);
       if (L.NB == 2) {
         unsigned char* Bn = smem + L.off_buf + (size_t)(buf ^ 1) * L.buf_bytes;
         stage_kv<CF>(a, L, nxt.mem, Bn, wv);
         stage_labels<CF>(a, L, nxt, Bn);
       }
     }
-    tiles_dispatch<CF>(run.cnt, a, L, cur, cur.h, run.jt, qcur, B, smem, kp);
+    if constexpr (CF::kQTM > 4) {
+      tiles_dispatch<CF, 0>(run.cnt < 4 ? run.cnt : 4, a, L, cur, cur.h, run.jt, qcur, B, smem, kp);
+      if (run.cnt > 4) tiles_dispatch<CF, 4>(run.cnt - 4, a, L, cur, cur.h, run.jt, qcur, B, smem, kp);
+    } else {
+      tiles_dispatch<CF, 0>(run.cnt, a, L, cur, cur.h, run.jt, qcur, B, smem, kp);
+    }
     if (more) {
+      if constexpr (CF::kBig) q_load<CF>(qnext, a, L, nxt.mem, rnext.jt, rnext.cnt);
       if (L.NB == 1) {
         __syncthreads();
         unsigned char* Bn = smem + L.off_buf;
@@ -581,7 +613,6 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.TH = a.rel.R / a.rel.Rw;                 // 2 Mh0 - 1
   L.Rp = tab_rp(L.R);
   L.A = (L.TD / 2) * L.Rp + (L.TH / 2) * L.Rw + L.Rw / 2;
-  L.TS4 = L.TD * L.Rp + 1;
   L.nW = (int)a.nW;
   L.heads = a.heads;
   L.fdRp = make_fastdiv((uint32_t)L.Rp);
@@ -589,7 +620,9 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   L.fdKC = make_fastdiv((uint32_t)kc);
   L.fdH = make_fastdiv((uint32_t)a.heads);
   L.fdNW = make_fastdiv((uint32_t)L.nW);
-  L.tg = tab4_geo(a.rel, a.heads);
+  L.tg = tab4_geo(a.rel, a.heads, a.N);
+  L.TS4 = L.tg.TS4;
+  if (L.tg.scalar && L.Rp != kBigRp) return false;
   L.qscale = a.q_scaled ? 1.0f : kLog2e / sqrtf((float)a.d);
   L.force_max = a.force_max;
   if (L.TS4 > kMaxTab || a.heads > 256) return false;
@@ -598,6 +631,7 @@ bool plan_a5(const AttnArgs& a, A5& L) {
   off += (size_t)L.NP * 8 * 4;
   off = (off + 15) & ~(size_t)15;
   L.off_tab = (uint32_t)off;
+  L.zone = (int)L.off_tab + (L.tg.scalar ? 4 * L.TD * L.Rp : 16 * (L.TS4 - 1));
   off += (size_t)L.TS4 * 16;
   L.off_buf = (uint32_t)off;
   size_t bb = (size_t)L.NPAD * 64;
@@ -628,28 +662,29 @@ hipError_t launch_cfg(const AttnArgs& ak, const A5& L, hipStream_t st) {
 
 }  // namespace
 
-Tab4Geo tab4_geo(const RelTab& rel, int heads) {
+Tab4Geo tab4_geo(const RelTab& rel, int heads, int N) {
   Tab4Geo t{};
   t.R = rel.R;
   t.Rw = rel.Rw;
   t.TD = rel.rows / rel.R;
   t.TH = rel.R / rel.Rw;
   t.Rp = tab_rp(rel.R);
-  t.TS4 = t.TD * t.Rp + 1;
+  t.scalar = N > kMfmaMaxN ? 1 : 0;
+  t.TS4 = t.scalar ? ((t.TD + 3) * t.Rp + 1 + 3) / 4 : t.TD * t.Rp + 1;
   t.heads = heads;
   t.fdRp = make_fastdiv((uint32_t)t.Rp);
   t.fdRw = make_fastdiv((uint32_t)t.Rw);
   return t;
 }
 
-size_t attention_workspace_bytes(const RelTab& rel, int heads) {
-  const Tab4Geo t = tab4_geo(rel, heads);
+size_t attention_workspace_bytes(const RelTab& rel, int heads, int N) {
+  const Tab4Geo t = tab4_geo(rel, heads, N);
   return ((size_t)heads * t.TS4 * 16 + 255) & ~(size_t)255;
 }
 
 bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
   if (dt != VSWIN_BF16 || a.d != 32 || a.mask_m100) return false;
-  if (a.geo.P % 4 != 0 || a.N > kMfmaMaxN) return false;
+  if (a.geo.P % 4 != 0 || a.N > kMfmaBigN) return false;
   // every group of 4 temporal positions (kt = 4a .. 4a+3) of every window
   // must share its temporal label and temporal pad status
   const WinGeo& g = a.geo;
@@ -681,6 +716,7 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (L.tg.scalar) return launch_cfg<Cfg<8, 8, true>>(ak, L, st);
   return launch_cfg<Cfg<8, 4>>(ak, L, st);
 }
 

@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(kQkvThreads, 1) qkv_wave_kernel(QkvParams pr) 
     for (int e = ((int)blockIdx.x - pr.tile_blocks) * kQkvThreads + (int)threadIdx.x; e < n;
          e += ((int)gridDim.x - pr.tile_blocks) * kQkvThreads) {
       const int h = e / pr.tg.TS4;
-      pr.tab4[e] = t4_entry(pr.table, pr.tg, h, e - h * pr.tg.TS4);
+      pr.tab4[e] = tab_entry(pr.table, pr.tg, h, e - h * pr.tg.TS4);
     }
     return;
   }
@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(kQkvThreads, 1) qkv_wave_kernel(QkvParams pr) 
     const int nidle = (int)(nw - ntiles);
     for (int e = (int)(t - ntiles) * 64 + lane; e < n; e += nidle * 64) {
       const int h = e / pr.tg.TS4;
-      pr.tab4[e] = t4_entry(pr.table, pr.tg, h, e - h * pr.tg.TS4);
+      pr.tab4[e] = tab_entry(pr.table, pr.tg, h, e - h * pr.tg.TS4);
     }
   }
 

@@ -171,7 +171,7 @@ vswin_status make_plan(const vswin_desc* d, Plan& p, bool compute = true) {
   g.slot_perm = p.fast ? 1 : 0;     // window rows in the MFMA kernel's slot order
   const size_t es = elem_size(d->dtype);
   const size_t act = align256((size_t)p.Lp * p.C * es);
-  p.ws_attn = p.fast ? attention_workspace_bytes(p.rel, p.heads) : 0;
+  p.ws_attn = p.fast ? attention_workspace_bytes(p.rel, p.heads, p.N) : 0;
   p.off_xw = 0;
   p.off_q = act;
   p.off_k = 2 * act;
@@ -237,7 +237,7 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
     // the MFMA attention's prepared bias tables are written by the qkv launch
     HIPCHECK(qkv_proj(ga->x, ga->g, ga->b, ga->eps, ga->ln, w->qkv_w, w->qkv_b, q, k, v, vt, qscale, p.Lp, p.C,
                       p.heads, p.d, p.geo, p.fast ? w->rpb_table : nullptr, p.fast ? ws + p.off_tab : nullptr,
-                      tab4_geo(p.rel, p.heads), st),
+                      tab4_geo(p.rel, p.heads, p.N), st),
              "qkv projection");
     AttnArgs a = attn_args(p, q, k, v, w->rpb_table, xw, d->flags, ws + p.off_tab);
     a.q_scaled = p.fast ? 1 : 0;

@@ -171,8 +171,15 @@ struct RelTab {
 // x = dtr * Rp + rem for the offset from the query base (dtr + i, rem / Rw,
 // rem % Rw), i = 0..3; Rp >= R is the temporal stride (4 mod 16 for
 // conflict-free LDS reads); the last entry TS4 - 1 is a tuple of -inf.
+// Scalar form (scalar = 1, windows of more than 512 tokens, whose 4-tuple
+// table would not fit in LDS beside one window's K and V^T): the plain fp32
+// column S[y] = B(y) * log2(e) for y < TD * Rp (offset y / Rp, y % Rp as
+// above), then 3 Rp + 1 entries of -inf; the 4-tuple at y is read as
+// S[y], S[y + Rp], S[y + 2 Rp], S[y + 3 Rp], the -inf one at y = TD * Rp.
+// TS4 counts 16-byte entries per head in either form (scalar: entry x holds
+// S[4x .. 4x + 3]).
 struct Tab4Geo {
-  int TD, TH, R, Rw, Rp, TS4, heads;
+  int TD, TH, R, Rw, Rp, TS4, heads, scalar;
   FastDiv fdRp, fdRw;
 };
 
@@ -221,6 +228,31 @@ __device__ __forceinline__ f32x4_t t4_entry(const bf16_t* __restrict__ T, const 
     }
   }
   return v;
+}
+
+// entry x of head h's prepared table in the scalar form: S[4x .. 4x + 3]
+__device__ __forceinline__ f32x4_t ts_entry(const bf16_t* __restrict__ T, const Tab4Geo& tg, int h, int x) {
+  f32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int y = 4 * x + i;
+    float e = -INFINITY;
+    if (y < tg.TD * tg.Rp) {
+      const int dtr = (int)fdiv((uint32_t)y, tg.fdRp);
+      const int rem = y - dtr * tg.Rp;
+      const int dhr = (int)fdiv((uint32_t)rem, tg.fdRw);
+      const int dwr = rem - dhr * tg.Rw;
+      const bool ok = rem < tg.R;
+      const int row = ok ? (tg.TD - 1 - dtr) * tg.R + (tg.TH - 1 - dhr) * tg.Rw + (tg.Rw - 1 - dwr) : 0;
+      e = ok ? bf2f(T[(size_t)row * tg.heads + h]) * 1.4426950408889634f : 0.f;
+    }
+    v[i] = e;
+  }
+  return v;
+}
+
+__device__ __forceinline__ f32x4_t tab_entry(const bf16_t* __restrict__ T, const Tab4Geo& tg, int h, int x) {
+  return tg.scalar ? ts_entry(T, tg, h, x) : t4_entry(T, tg, h, x);
 }
 
 template <typename T> struct Elem;

@@ -91,13 +91,16 @@ struct AttnArgs {
 };
 // bytes of workspace the MFMA kernel needs for its prepared bias tables
 // (heads * TS4 fp32 4-tuples) and their extents
-size_t attention_workspace_bytes(const RelTab& rel, int heads);
-Tab4Geo tab4_geo(const RelTab& rel, int heads);
+size_t attention_workspace_bytes(const RelTab& rel, int heads, int N);
+Tab4Geo tab4_geo(const RelTab& rel, int heads, int N);
 hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st);
 hipError_t attention_mfma(const AttnArgs& a, hipStream_t st);
 // shapes the MFMA kernel serves (bf16, d = 32, temporal window % 4 == 0 with
-// group-uniform temporal labels, N <= kMfmaMaxN, no additive -100 mask)
+// group-uniform temporal labels, no additive -100 mask): N <= kMfmaMaxN with
+// the 4-tuple bias table, or up to kMfmaBigN with the scalar table and the
+// 7 x 7 spatial window
 constexpr int kMfmaMaxN = 512;
+constexpr int kMfmaBigN = 1024;
 bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a);
 
 // --- fused LN2 -> fc1 -> GELU -> fc2 -> residual (k_mlp.hip) --------------

@@ -78,6 +78,13 @@ def test_fast_path_selection():
     # fp32 and windows whose temporal extent is not a multiple of 4 use the generic kernel
     assert not vs.vswin_plan_query(vs.make_desc(1, 4, 14, 14, 32, 2, (2, 7, 7), (1, 3, 3), dtype=0))["fast_attention"]
     assert not vs.vswin_plan_query(vs.make_desc(1, 6, 14, 14, 64, 2, (6, 7, 7), (3, 3, 3), dtype=1))["fast_attention"]
+    # temporal window 16 (784 tokens) runs on the MFMA kernel's scalar-table form;
+    # longer windows, or N > 512 with another spatial window, do not
+    assert vs.vswin_plan_query(vs.make_desc(1, 16, 56, 56, 96, 3, (16, 7, 7), (8, 3, 3), dtype=1))["fast_attention"]
+    assert not vs.vswin_plan_query(vs.make_desc(1, 24, 14, 14, 64, 2, (24, 7, 7), (12, 3, 3),
+                                                dtype=1))["fast_attention"]
+    assert not vs.vswin_plan_query(vs.make_desc(1, 16, 12, 12, 64, 2, (16, 6, 6), (8, 3, 3),
+                                                dtype=1))["fast_attention"]
     # code-compat -100 mask is only in the generic kernel
     assert not vs.vswin_plan_query(vs.make_desc(1, 16, 14, 14, 64, 2, (8, 7, 7), (4, 3, 3), dtype=1,
                                                 flags=vs.F_MASK_M100))["fast_attention"]

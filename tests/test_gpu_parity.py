@@ -110,6 +110,11 @@ MSA_CASES = [
     ("bf16 clamp strict", 1, (16, 7, 7), 64, 2, (8, 7, 7), (4, 3, 3), "bf16", "stress", vs.F_CLAMP_STRICT),
     ("bf16 window 16", 1, (16, 7, 7), 64, 2, (16, 7, 7), (8, 3, 3), "bf16", "stress", vs.F_CLAMP_STRICT),
     ("bf16 window 4", 1, (16, 14, 14), 64, 2, (4, 7, 7), (2, 3, 3), "bf16", "stress", 0),
+    # temporal window 16 (784 tokens): the MFMA kernel's scalar-table form
+    ("bf16 window 16 regular", 1, (16, 14, 14), 96, 3, (16, 7, 7), (0, 0, 0), "bf16", "stress", 0),
+    ("bf16 window 16 shifted", 1, (16, 14, 14), 96, 3, (16, 7, 7), (8, 3, 3), "bf16", "stress", 0),
+    ("bf16 window 16 padded", 1, (16, 12, 13), 64, 2, (16, 7, 7), (8, 3, 3), "bf16", "stress", 0),
+    ("bf16 window 16 spec", 1, (32, 14, 14), 64, 2, (16, 7, 7), (8, 3, 3), "bf16", "spec", 0),
 ]
 
 
@@ -132,12 +137,12 @@ def test_window_msa(case):
     check(host64(y), ref, dtype, name)
 
 
-@pytest.mark.parametrize("shift", [(0, 0, 0), (4, 3, 3)])
-def test_window_msa_forced_row_max_pass(shift, monkeypatch):
+@pytest.mark.parametrize("window,shift", [((8, 7, 7), (0, 0, 0)), ((8, 7, 7), (4, 3, 3)), ((16, 7, 7), (8, 3, 3))])
+def test_window_msa_forced_row_max_pass(window, shift, monkeypatch):
     """The exact row-max pass of the MFMA kernel at stress init."""
-    say(f"window_msa forced max pass shift {shift}")
+    say(f"window_msa forced max pass window {window} shift {shift}")
     monkeypatch.setenv("VSWIN_ATTN_MAXPASS", "1")
-    C, heads, window = 96, 3, (8, 7, 7)
+    C, heads = 96, 3
     p = _msa_params(C, heads, window, "bf16", "stress")
     x = _rng_tokens((1, 16, 14, 21, C), "bf16", 4)
     y = vs.vswin_window_msa_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
@@ -202,6 +207,22 @@ def test_block_c96_fused_projection(case):
     y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift, flags=flags)
     _, ref = oracle.block(x, p, heads, window, shift, pad_visible=bool(flags & vs.F_PAD_VISIBLE))
     check(host64(y), ref, "bf16", f"C=96 block {name}")
+
+
+@pytest.mark.parametrize("shift", [(0, 0, 0), (8, 3, 3)])
+def test_block_window16_stage1_grid(shift):
+    """Temporal window 16 (784 tokens per window) on the Swin-T stage-1 token
+    grid: more than 4 query tiles per wave and window (two tile groups), and
+    the scalar bias tables written by the qkv launch."""
+    say(f"window 16 block, stage-1 grid, shift {shift}")
+    C, heads, window = 96, 3, (16, 7, 7)
+    plan = vs.vswin_plan_query(vs.make_desc(1, 16, 56, 56, C, heads, window, shift, dtype=1))
+    assert plan["fast_attention"] and plan["tokens_per_window"] == 784
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=29)
+    x = _rng_tokens((1, 16, 56, 56, C), "bf16", 6)
+    y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
+    _, ref = oracle.block(x, p, heads, window, shift)
+    check(host64(y), ref, "bf16", f"window 16 block shift {shift}")
 
 
 def test_workload1_fp32_pair():
