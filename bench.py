@@ -125,6 +125,75 @@ def memory_kernels(vs, torch, stream, launches: int = 20) -> dict:
     return out
 
 
+def window_variants(vs, torch, np, stream, steps: int = 20) -> dict:
+    """The block pair on the Swin-T stage-1 token grid (1,16,56,56,96) with
+    the other temporal windows of the window-size ablation, 4 and 16 (196 and
+    784 tokens per window; shift half the window), and with the -100 form of
+    the region mask at window 8: ms per pair (eager, HIP events) and the
+    attention kernel alone (prepared tables reused) in us and TFLOP/s."""
+    import synth
+    C, heads, hid = 96, 3, 384
+    shape = (1, 16, 56, 56, C)
+    g = np.random.default_rng(5)
+    xd = torch.from_numpy(g.standard_normal(shape).astype(np.float32)).to(torch.bfloat16).cuda()
+    cases = {"window_4": ((4, 7, 7), (2, 3, 3), 0), "window_16": ((16, 7, 7), (8, 3, 3), 0),
+             "window_8_mask_m100": ((8, 7, 7), (4, 3, 3), vs.F_MASK_M100)}
+    out = {}
+    for name, (window, shift, flags) in cases.items():
+        rows = (2 * window[0] - 1) * 13 * 13
+        ps = [synth.gen_block_params(C, heads, rows, 4, np.random.SeedSequence(40 + k), "bf16", "spec")
+              for k in range(2)]
+        w = [{k: torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.bfloat16).cuda()
+              for k, v in p.items()} for p in ps]
+        shifts = [(0, 0, 0), shift]
+        descs = [vs.make_desc(*shape, heads, window, sh, mlp_hidden=hid, dtype=torch.bfloat16, flags=flags)
+                 for sh in shifts]
+        plans = [vs.vswin_plan_query(d) for d in descs]
+        ws = torch.empty(max(p["workspace_bytes"] for p in plans), dtype=torch.uint8, device="cuda")
+        y1, y2 = torch.empty_like(xd), torch.empty_like(xd)
+
+        def pair():
+            vs.vswin_block_fwd(xd, w[0], heads, window, shifts[0], out=y1, workspace=ws, flags=flags, stream=stream)
+            vs.vswin_block_fwd(y1, w[1], heads, window, shifts[1], out=y2, workspace=ws, flags=flags, stream=stream)
+
+        for _ in range(3):
+            pair()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            pair()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pair_ms = e0.elapsed_time(e1) / steps
+        # the attention kernel alone, shifted block
+        nW, N = plans[1]["num_windows"], plans[1]["tokens_per_window"]
+        gq = torch.Generator(device="cuda").manual_seed(6)
+        qkv = [torch.randn((nW, heads, N, C // heads), generator=gq, device="cuda").to(torch.bfloat16)
+               for _ in range(3)]
+        o = torch.empty((nW, N, C), dtype=torch.bfloat16, device="cuda")
+        aws = torch.empty(max(256, plans[1]["attention_workspace_bytes"]), dtype=torch.uint8, device="cuda")
+        vs.vswin_attention_fwd(descs[1], *qkv, w[1]["rpb_table"], out=o, workspace=aws, stream=stream)
+        ready = vs.make_desc(*shape, heads, window, shift, mlp_hidden=hid, dtype=torch.bfloat16,
+                             flags=flags | vs.F_TABLES_READY)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            vs.vswin_attention_fwd(ready, *qkv, w[1]["rpb_table"], out=o, workspace=aws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        attn_us = e0.elapsed_time(e1) * 1e3 / steps
+        fl = block_flops(plans[1], C, hid)
+        pair_flops = sum(block_flops(p, C, hid)["total"] for p in plans)
+        out[name] = {"window": list(window), "shift": list(shift), "tokens_per_window": N,
+                     "fast_attention": bool(plans[1]["fast_attention"]),
+                     "pair_ms": round(pair_ms, 4), "pair_tflops": round(pair_flops / (pair_ms * 1e-3) / 1e12, 2),
+                     "tokens_per_s": round(2 * 50176 / (pair_ms * 1e-3), 1),
+                     "attn_us_shifted": round(attn_us, 3),
+                     "attn_tflops": round(fl["attn"] / (attn_us * 1e-6) / 1e12, 2)}
+    return out
+
+
 def mfma_measured_peak(vs, torch, stream, iters: int = 4000) -> float:
     """TFLOP/s of the library's v_mfma_f32_16x16x32_bf16 throughput kernel with
     two workgroups of 8 waves per CU (four waves per SIMD)."""
@@ -328,6 +397,7 @@ def main():
         "roofline": roofline,
         "step_ms_warm": warm, "step_ms_cold": cold,
         "memory_kernels": memory_kernels(vs, torch, stream),
+        "window_variants": window_variants(vs, torch, np, stream),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_np, params, s)

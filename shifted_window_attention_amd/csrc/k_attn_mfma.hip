@@ -54,6 +54,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxWaves = 16;
 constexpr int kMaxTab = 4096;     // table 4-tuples held in LDS at most
 constexpr int kDummyLab = 0x7fff0000;
+// per-key labels: one byte per key of the group (region labels are < 27, pads
+// 255), dummy keys 0xfe, which no query carries
+constexpr uint32_t kDummyLab4 = 0xfefefefeu;
 constexpr size_t kLdsMax = 160 * 1024;
 
 // Temporal stride of the scalar bias table for the 7 x 7 spatial window
@@ -62,12 +65,19 @@ constexpr int kBigRp = 180;
 
 // W waves per workgroup; a wave carries at most QTM query tiles of a window,
 // in groups of at most 4.  BIG: windows of more than kMfmaMaxN tokens, with
-// the scalar bias table and one K / V^T buffer.
-template <int W, int QTM, bool BIG = false>
+// the scalar bias table and one K / V^T buffer.  M100: pairs of different
+// regions get -100 added to their logit instead of being excluded.  PERKEY:
+// the 4 keys of a key group may lie in different regions (a temporal region
+// boundary inside a group, e.g. window 4 with temporal shift 2); their labels
+// are compared one by one and masked keys get P = 0.
+template <int W, int QTM, bool BIG = false, bool M100 = false, bool PERKEY = false>
 struct Cfg {
   static constexpr int kWaves = W;
   static constexpr int kQTM = QTM;
   static constexpr bool kBig = BIG;
+  static constexpr bool kM100 = M100;
+  static constexpr bool kPerKey = PERKEY;
+  static_assert(!(M100 && PERKEY), "the -100 mask needs group-uniform labels");
   static constexpr int kTabEs = BIG ? 4 : 16;   // bytes per table index step
   static constexpr int kThreads = 64 * W;
   static_assert(((BIG ? kMfmaBigN : kMfmaMaxN) / 16 + W - 1) / W <= QTM, "a wave's tiles of one window exceed QTM");
@@ -93,7 +103,7 @@ template <int QT>
 struct QState {
   bf16x8_t q[QT];
   int qaddr[QT];      // byte offset of the query's table base
-  int qlab[QT];
+  int qlab[QT];       // (PERKEY: the query's label byte in all 4 bytes)
   float mrow[QT];
   f32x4_t o0[QT], o1[QT], os[QT];
 };
@@ -209,12 +219,22 @@ __device__ __forceinline__ void stage_labels(const AttnArgs& a, const A5& L, con
   int* lp = reinterpret_cast<int*>(B + L.off_lp);
   bool differs = false;
   for (int m = tid; m < L.NP * 8; m += CF::kThreads) {
-    int lab = kDummyLab;
+    int lab = CF::kPerKey ? (int)kDummyLab4 : kDummyLab;
     if (m < L.N / 4) {
       const int aa = (int)fdiv((uint32_t)m, g.fmhw), r2 = m - aa * mhw;
       const int kh = (int)fdiv((uint32_t)r2, g.fMw), kw = r2 - kh * g.Mw;
-      lab = slot_label_at(g, wi.rt0 + 4 * aa, wi.rh0 + kh, wi.rw0 + kw);
-      differs |= lab != lab0;
+      if constexpr (CF::kPerKey) {
+        uint32_t w4 = 0;
+        for (int i = 0; i < 4; ++i) {
+          const int li = slot_label_at(g, wi.rt0 + 4 * aa + i, wi.rh0 + kh, wi.rw0 + kw);
+          differs |= li != lab0;
+          w4 |= (uint32_t)li << (8 * i);
+        }
+        lab = (int)w4;
+      } else {
+        lab = slot_label_at(g, wi.rt0 + 4 * aa, wi.rh0 + kh, wi.rw0 + kw);
+        differs |= lab != lab0;
+      }
     }
     lp[pair_slot(m)] = lab;
   }
@@ -261,13 +281,32 @@ __device__ __forceinline__ void tab_copy(const AttnArgs& a, const A5& L, int h, 
   }
 }
 
+// PERKEY masks of one key group against a query: x = label word ^ query
+// label in every byte; bit 7 of byte i of z is set iff key i's label equals
+// the query's; m01 / m23 hold 0xffff in the 16-bit half of each kept key of
+// the bf16 pairs (keys 0, 1) / (keys 2, 3) (v_perm_b32 selectors 8..11
+// replicate the sign bits of bytes 1, 3 of the second and first operand).
+__device__ __forceinline__ uint32_t key_match(uint32_t lw, uint32_t q4) {
+  const uint32_t x = lw ^ q4;
+  return ~(((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
+}
+__device__ __forceinline__ void key_masks(uint32_t z, uint32_t& m01, uint32_t& m23) {
+  const uint32_t zs = z << 8;
+  m01 = __builtin_amdgcn_perm(zs, z, 0x08080a0au);
+  m23 = __builtin_amdgcn_perm(zs, z, 0x09090b0bu);
+}
+
 // ---- one 32-key step for the wave's QT tiles --------------------------------
 //   MODE 0: P = exp2(x); 1: row max of x only; 2: P = exp2(x - max).
 //   SEL: per key group, masked / dummy groups read the -inf 4-tuple.
 //   gk / lk: this step's key-group offsets / labels for lane group g4.
 //   HALF: keys 32p + 16 .. + 31 are all padding; that half is skipped (P = 0).
-//   BIG: scalar bias table (a 4-tuple is 4 floats kBigRp apart).
-template <int MODE, bool SEL, int QT, bool HALF, bool BIG>
+//   CF::kBig: scalar bias table (a 4-tuple is 4 floats kBigRp apart).
+//   CF::kM100 (with SEL): a key group of another region keeps its bias and
+//   gets -100 log2(e) added; only dummy key groups read the -inf 4-tuple.
+//   CF::kPerKey (with SEL): every group reads its own bias; keys whose label
+//   differs from the query's get P = 0 (and are left out of the row max).
+template <int MODE, bool SEL, int QT, bool HALF, class CF>
 __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict__ B, const A5& L,
                                           const unsigned char* __restrict__ tabb, int2 gk, int2 lk, int zone,
                                           const bf16x8_t& ones, QState<QT>& st) {
@@ -284,11 +323,19 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
     vA0 = *reinterpret_cast<const bf16x8_t*>(vb + d0 * L.pitch_v * 16);
     vA1 = *reinterpret_cast<const bf16x8_t*>(vb + (d0 + 4) * L.pitch_v * 16);
   }
+  constexpr bool BIG = CF::kBig;
   f32x4_t tA[QT], tB[QT];
+  float mA[QT], mB[QT];
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     int adA = st.qaddr[u] + gk.x, adB = st.qaddr[u] + gk.y;
-    if (SEL) {
+    if (SEL && CF::kM100) {
+      constexpr float kM = -100.0f * kLog2e;
+      mA[u] = (lk.x == st.qlab[u] || lk.x == kDummyLab) ? 0.f : kM;
+      mB[u] = (lk.y == st.qlab[u] || lk.y == kDummyLab) ? 0.f : kM;
+      adA = lk.x == kDummyLab ? zone : adA;
+      adB = lk.y == kDummyLab ? zone : adB;
+    } else if (SEL && !CF::kPerKey) {
       adA = (lk.x == st.qlab[u]) ? adA : zone;
       adB = (lk.y == st.qlab[u]) ? adB : zone;
     }
@@ -306,15 +353,34 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
   }
   // every LDS read of the step is in flight before the first MFMA waits on one
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (SEL && CF::kM100) {
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tA[u][i] += mA[u];
+        if (!HALF) tB[u][i] += mB[u];
+      }
+  }
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     const f32x4_t sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, st.q[u], tA[u], 0, 0, 0);
     f32x4_t sB = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (!HALF) sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kB, st.q[u], tB[u], 0, 0, 0);
     if (MODE == 1) {
+      f32x4_t xA = sA, xB = sB;
+      if constexpr (SEL && CF::kPerKey) {
+        const uint32_t zA = key_match((uint32_t)lk.x, (uint32_t)st.qlab[u]);
+        const uint32_t zB = key_match((uint32_t)lk.y, (uint32_t)st.qlab[u]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (!((zA >> (8 * i + 7)) & 1u)) xA[i] = -INFINITY;
+          if (!((zB >> (8 * i + 7)) & 1u)) xB[i] = -INFINITY;
+        }
+      }
       float m = st.mrow[u];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, HALF ? sA[i] : fmaxf(sA[i], sB[i]));
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, HALF ? xA[i] : fmaxf(xA[i], xB[i]));
       st.mrow[u] = m;
     } else {
       float pA[4], pB[4];
@@ -328,6 +394,17 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
       pk[1] = pack_bf16x2(pA[2], pA[3]);
       pk[2] = pack_bf16x2(pB[0], pB[1]);
       pk[3] = pack_bf16x2(pB[2], pB[3]);
+      if constexpr (SEL && CF::kPerKey) {
+        uint32_t m01, m23;
+        key_masks(key_match((uint32_t)lk.x, (uint32_t)st.qlab[u]), m01, m23);
+        pk[0] &= m01;
+        pk[1] &= m23;
+        if (!HALF) {
+          key_masks(key_match((uint32_t)lk.y, (uint32_t)st.qlab[u]), m01, m23);
+          pk[2] &= m01;
+          pk[3] &= m23;
+        }
+      }
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
       st.o0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA0, pb, st.o0[u], 0, 0, 0);
       st.o1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA1, pb, st.o1[u], 0, 0, 0);
@@ -337,7 +414,7 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
 }
 
 // One pass over the keys; the next step's offsets and labels are read a step ahead.
-template <int MODE, bool MASKED, int QT, bool BIG>
+template <int MODE, bool MASKED, int QT, class CF>
 __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, const unsigned char* tabb,
                                           const int2* kp2, int zone, const bf16x8_t& ones, QState<QT>& st) {
   const int g4 = (threadIdx.x & 63) >> 4;
@@ -352,12 +429,12 @@ __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, c
     const int pn = p + 1 < L.NP ? p + 1 : p;
     const int2 gkn = kp2[4 * pn + g4];
     const int2 lkn = lp2[4 * pn + g4];
-    if (MASKED || p >= nclean) attn_step<MODE, true, QT, false, BIG>(p, B, L, tabb, gk, lk, zone, ones, st);
-    else attn_step<MODE, false, QT, false, BIG>(p, B, L, tabb, gk, lk, zone, ones, st);
+    if (MASKED || p >= nclean) attn_step<MODE, true, QT, false, CF>(p, B, L, tabb, gk, lk, zone, ones, st);
+    else attn_step<MODE, false, QT, false, CF>(p, B, L, tabb, gk, lk, zone, ones, st);
     gk = gkn;
     lk = lkn;
   }
-  if (half) attn_step<MODE, true, QT, true, BIG>(L.NP - 1, B, L, tabb, gk, lk, zone, ones, st);
+  if (half) attn_step<MODE, true, QT, true, CF>(L.NP - 1, B, L, tabb, gk, lk, zone, ones, st);
 }
 
 // The wave's QT query tiles jt, jt + W, ... of one window.
@@ -392,7 +469,6 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   // -inf slot carry the table's own offset
   const unsigned char* tabb = smem;
   constexpr int ES = CF::kTabEs;
-  constexpr bool BIG = CF::kBig;
   const int zone = L.zone;
   const int* lp = reinterpret_cast<const int*>(B + L.off_lp);
   int masked = 0;
@@ -406,7 +482,10 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
     // the query's key group: same table base (plus its temporal index) and label
     const int ps = pair_slot(qs >> 2);
     st.qaddr[u] = (int)L.off_tab + ES * L.A - kp[ps] - ES * (qs & 3) * L.Rp;
-    st.qlab[u] = lp[ps];
+    if constexpr (CF::kPerKey)
+      st.qlab[u] = (int)(((uint32_t)lp[ps] >> (8 * (qs & 3)) & 0xffu) * 0x01010101u);
+    else
+      st.qlab[u] = lp[ps];
     u32x4_t qv = qp.q[U0 + u];
     if (L.qscale != 1.0f) {
 #pragma unroll
@@ -433,8 +512,8 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   bool exact = L.force_max != 0;
   if (!exact) {
     clear();
-    if (masked) attn_pass<0, true, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
-    else attn_pass<0, false, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
+    if (masked) attn_pass<0, true, QT, CF>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<0, false, QT, CF>(B, L, tabb, kp2, zone, ones, st);
     bool bad = false;
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
@@ -449,8 +528,8 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   }
   if (exact) {
     clear();
-    if (masked) attn_pass<1, true, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
-    else attn_pass<1, false, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
+    if (masked) attn_pass<1, true, QT, CF>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<1, false, QT, CF>(B, L, tabb, kp2, zone, ones, st);
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
       float m = st.mrow[u];
@@ -458,8 +537,8 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
       m = fmaxf(m, __shfl_xor(m, 32));
       st.mrow[u] = (m == -INFINITY) ? 0.f : m;
     }
-    if (masked) attn_pass<2, true, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
-    else attn_pass<2, false, QT, BIG>(B, L, tabb, kp2, zone, ones, st);
+    if (masked) attn_pass<2, true, QT, CF>(B, L, tabb, kp2, zone, ones, st);
+    else attn_pass<2, false, QT, CF>(B, L, tabb, kp2, zone, ones, st);
   }
 
   // lane: query fr, output features 8 g4 .. + 7 of head h
@@ -682,11 +761,11 @@ size_t attention_workspace_bytes(const RelTab& rel, int heads, int N) {
   return ((size_t)heads * t.TS4 * 16 + 255) & ~(size_t)255;
 }
 
-bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
-  if (dt != VSWIN_BF16 || a.d != 32 || a.mask_m100) return false;
-  if (a.geo.P % 4 != 0 || a.N > kMfmaBigN) return false;
-  // every group of 4 temporal positions (kt = 4a .. 4a+3) of every window
-  // must share its temporal label and temporal pad status
+namespace {
+// whether every group of 4 temporal positions (kt = 4a .. 4a+3) of every
+// window shares its temporal label and temporal pad status (else the kernel
+// compares labels key by key)
+bool groups_uniform(const AttnArgs& a) {
   const WinGeo& g = a.geo;
   auto tkey = [&](int rt) {
     int ot = rt + g.st;
@@ -697,6 +776,14 @@ bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
   for (int rt = 0; rt < g.Tp; rt += 4)
     for (int i = 1; i < 4; ++i)
       if (tkey(rt + i) != tkey(rt)) return false;
+  return true;
+}
+}  // namespace
+
+bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a) {
+  if (dt != VSWIN_BF16 || a.d != 32) return false;
+  if (a.geo.P % 4 != 0 || a.N > kMfmaBigN) return false;
+  if (a.mask_m100 && !groups_uniform(a)) return false;
   A5 L;
   return plan_a5(a, L);
 }
@@ -715,6 +802,16 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
         reinterpret_cast<const bf16_t*>(ak.table), reinterpret_cast<f32x4_t*>(ak.tab4), L);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  const bool uniform = groups_uniform(ak);
+  if (ak.mask_m100) {
+    if (!uniform) return hipErrorInvalidValue;
+    if (L.tg.scalar) return launch_cfg<Cfg<8, 8, true, true>>(ak, L, st);
+    return launch_cfg<Cfg<8, 4, false, true>>(ak, L, st);
+  }
+  if (!uniform) {
+    if (L.tg.scalar) return launch_cfg<Cfg<8, 8, true, false, true>>(ak, L, st);
+    return launch_cfg<Cfg<8, 4, false, false, true>>(ak, L, st);
   }
   if (L.tg.scalar) return launch_cfg<Cfg<8, 8, true>>(ak, L, st);
   return launch_cfg<Cfg<8, 4>>(ak, L, st);

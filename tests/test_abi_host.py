@@ -85,9 +85,14 @@ def test_fast_path_selection():
                                                 dtype=1))["fast_attention"]
     assert not vs.vswin_plan_query(vs.make_desc(1, 16, 12, 12, 64, 2, (16, 6, 6), (8, 3, 3),
                                                 dtype=1))["fast_attention"]
-    # code-compat -100 mask is only in the generic kernel
-    assert not vs.vswin_plan_query(vs.make_desc(1, 16, 14, 14, 64, 2, (8, 7, 7), (4, 3, 3), dtype=1,
+    # window 4 with temporal shift 2 (labels compared key by key) runs on the MFMA
+    # kernel, except with the -100 mask
+    assert vs.vswin_plan_query(vs.make_desc(1, 16, 56, 56, 96, 3, (4, 7, 7), (2, 3, 3), dtype=1))["fast_attention"]
+    assert not vs.vswin_plan_query(vs.make_desc(1, 16, 56, 56, 96, 3, (4, 7, 7), (2, 3, 3), dtype=1,
                                                 flags=vs.F_MASK_M100))["fast_attention"]
+    # the code-compat -100 mask runs on the MFMA kernel too
+    assert vs.vswin_plan_query(vs.make_desc(1, 16, 14, 14, 64, 2, (8, 7, 7), (4, 3, 3), dtype=1,
+                                            flags=vs.F_MASK_M100))["fast_attention"]
 
 
 BAD = [

@@ -115,6 +115,17 @@ MSA_CASES = [
     ("bf16 window 16 shifted", 1, (16, 14, 14), 96, 3, (16, 7, 7), (8, 3, 3), "bf16", "stress", 0),
     ("bf16 window 16 padded", 1, (16, 12, 13), 64, 2, (16, 7, 7), (8, 3, 3), "bf16", "stress", 0),
     ("bf16 window 16 spec", 1, (32, 14, 14), 64, 2, (16, 7, 7), (8, 3, 3), "bf16", "spec", 0),
+    ("bf16 mask -100 padded", 1, (16, 12, 13), 64, 2, (8, 7, 7), (4, 3, 3), "bf16", "stress", vs.F_MASK_M100),
+    # a temporal region boundary inside a group of 4 keys: labels compared key by key
+    ("bf16 window 4 padded", 1, (14, 12, 13), 96, 3, (4, 7, 7), (2, 3, 3), "bf16", "stress", 0),
+    ("bf16 window 4 pads visible", 1, (14, 12, 13), 64, 2, (4, 7, 7), (2, 3, 3), "bf16", "stress",
+     vs.F_PAD_VISIBLE),
+    ("bf16 window 12 shift 6", 1, (24, 14, 14), 64, 2, (12, 7, 7), (6, 3, 3), "bf16", "stress", 0),
+    ("bf16 window 4 mask -100 (generic)", 1, (16, 14, 14), 64, 2, (4, 7, 7), (2, 3, 3), "bf16", "stress",
+     vs.F_MASK_M100),
+    ("bf16 spatial-only shift", 1, (16, 14, 14), 96, 3, (8, 7, 7), (0, 3, 3), "bf16", "stress", 0),
+    ("bf16 window 16 mask -100", 1, (16, 14, 14), 64, 2, (16, 7, 7), (8, 3, 3), "bf16", "stress",
+     vs.F_MASK_M100),
 ]
 
 
@@ -137,7 +148,8 @@ def test_window_msa(case):
     check(host64(y), ref, dtype, name)
 
 
-@pytest.mark.parametrize("window,shift", [((8, 7, 7), (0, 0, 0)), ((8, 7, 7), (4, 3, 3)), ((16, 7, 7), (8, 3, 3))])
+@pytest.mark.parametrize("window,shift", [((8, 7, 7), (0, 0, 0)), ((8, 7, 7), (4, 3, 3)), ((16, 7, 7), (8, 3, 3)),
+                                          ((4, 7, 7), (2, 3, 3))])
 def test_window_msa_forced_row_max_pass(window, shift, monkeypatch):
     """The exact row-max pass of the MFMA kernel at stress init."""
     say(f"window_msa forced max pass window {window} shift {shift}")
@@ -166,6 +178,34 @@ def test_window_msa_logits_beyond_exp_range():
     ref = oracle.window_msa(x, p, heads, window, shift)
     assert np.abs(ref).max() > 0.5
     check(host64(y), ref, "bf16", "logits beyond exp range")
+
+
+@pytest.mark.parametrize("window,shift", [((8, 7, 7), (4, 3, 3)), ((16, 7, 7), (8, 3, 3))])
+def test_window_msa_m100_visible(window, shift):
+    """The -100 mask where it changes the result: a few relative offsets carry
+    a bias of +150, so a query whose only such keys lie in another region puts
+    its weight on them (logit 50 against about 0) instead of excluding them;
+    logits this large also take the kernel through its row-max pass.  The
+    test first checks on the oracle that exclusion and -100 differ."""
+    say(f"window_msa -100 visible, window {window}")
+    C, heads = 64, 2
+    rng = np.random.default_rng(17)
+    rows = (2 * window[0] - 1) * 13 * 13
+    table = np.zeros((rows, heads), np.float32)
+    table[rng.random(rows) < 0.005] = 150.0
+    p = _msa_params(C, heads, window, "bf16", "spec", seed=31)
+    p["rpb_table"] = table
+    # v = x and an identity projection, so the output is the weighted tokens
+    eye = np.eye(C, dtype=np.float32)
+    p["qkv_w"] = p["qkv_w"].copy()
+    p["qkv_w"][2 * C:] = eye
+    p["proj_w"] = eye.copy()
+    x = synth.round_bf16(rng.standard_normal((1, 16, 14, 14, C)).astype(np.float32))
+    ref = oracle.window_msa(x, p, heads, window, shift, mask_m100=True)
+    excl = oracle.window_msa(x, p, heads, window, shift)
+    assert np.abs(ref - excl).max() > 10 * TOL_BF16_MAX
+    y = vs.vswin_window_msa_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift, flags=vs.F_MASK_M100)
+    check(host64(y), ref, "bf16", f"-100 visible {window}")
 
 
 # ----------------------------------------------------------------------------- blocks
@@ -209,20 +249,21 @@ def test_block_c96_fused_projection(case):
     check(host64(y), ref, "bf16", f"C=96 block {name}")
 
 
-@pytest.mark.parametrize("shift", [(0, 0, 0), (8, 3, 3)])
-def test_block_window16_stage1_grid(shift):
-    """Temporal window 16 (784 tokens per window) on the Swin-T stage-1 token
-    grid: more than 4 query tiles per wave and window (two tile groups), and
-    the scalar bias tables written by the qkv launch."""
-    say(f"window 16 block, stage-1 grid, shift {shift}")
-    C, heads, window = 96, 3, (16, 7, 7)
+@pytest.mark.parametrize("window,shift", [((16, 7, 7), (0, 0, 0)), ((16, 7, 7), (8, 3, 3)), ((4, 7, 7), (2, 3, 3))])
+def test_block_window_variants_stage1_grid(window, shift):
+    """The other temporal windows on the Swin-T stage-1 token grid: 16 (784
+    tokens per window; more than 4 query tiles per wave and window, the scalar
+    bias tables written by the qkv launch) and 4 with temporal shift 2 (a
+    region boundary inside a group of 4 keys)."""
+    say(f"window {window} block, stage-1 grid, shift {shift}")
+    C, heads = 96, 3
     plan = vs.vswin_plan_query(vs.make_desc(1, 16, 56, 56, C, heads, window, shift, dtype=1))
-    assert plan["fast_attention"] and plan["tokens_per_window"] == 784
+    assert plan["fast_attention"] and plan["tokens_per_window"] == window[0] * 49
     p = _msa_params(C, heads, window, "bf16", "stress", seed=29)
     x = _rng_tokens((1, 16, 56, 56, C), "bf16", 6)
     y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
     _, ref = oracle.block(x, p, heads, window, shift)
-    check(host64(y), ref, "bf16", f"window 16 block shift {shift}")
+    check(host64(y), ref, "bf16", f"window {window} block shift {shift}")
 
 
 def test_workload1_fp32_pair():
