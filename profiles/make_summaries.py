@@ -38,8 +38,12 @@ def stats(stats_dir: str) -> str:
            "a 512 MiB fill, the torch FillFunctor kernel, between them), 2 x (5 + 50) standalone attention launches",
            "for the roofline leg, and 23 launches each of the gather (`ln_rows_v8_kernel` with the slot map), the",
            "scatter + residual (`reverse_v8_kernel`) and LayerNorm (`ln_rows_v8_kernel`) on the Swin-T stage-1 grid",
-           "(<4, 3> instances, C = 96) and the Swin-B stage-1 B=8 grid (<16, 1> instances, C = 128); other torch",
-           "kernels are input generation.", "",
+           "(<4, 3> instances, C = 96) and the Swin-B stage-1 B=8 grid (<16, 1> instances, C = 128), then the",
+           "window variants on the stage-1 grid (window 4 with shift (2,3,3): the per-key-label form `Cfg<8, 4,",
+           "false, false, true>`; window 16: the scalar-table form `Cfg<8, 8, true, false, false>`; window 8 with the",
+           "-100 mask: `Cfg<8, 4, false, true, false>`), each 23 block pairs and 21 standalone attention launches;",
+           "the main workload's attention is `Cfg<8, 4, false, false, false>`. Other torch kernels are input",
+           "generation.", "",
            "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
