@@ -174,6 +174,50 @@ vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const vo
                                  const void* v, const void* rpb_table, void* o,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Gradients of one block's weights (training): fp32 device buffers of the
+ * weights' shapes (vswin_block_weights), each overwritten (not accumulated).
+ * Bias gradients may be NULL (not computed); weight, table and LayerNorm
+ * gradients are required by vswin_block_bwd, and vswin_window_msa_bwd uses
+ * only qkv_w, qkv_b, proj_w, proj_b and rpb_table.                          */
+typedef struct {
+  float *ln1_g, *ln1_b;
+  float *qkv_w, *qkv_b;
+  float *proj_w, *proj_b;
+  float *rpb_table;
+  float *ln2_g, *ln2_b;
+  float *fc1_w, *fc1_b;
+  float *fc2_w, *fc2_b;
+} vswin_block_grads;
+
+/* Workspace bytes of vswin_block_bwd and vswin_window_msa_bwd for `desc`.
+ * Host only.  VSWIN_ERR_UNSUPPORTED when the backward cannot serve the
+ * descriptor: it needs bf16, head_dim 32, C <= 768, the MFMA attention
+ * (temporal window a multiple of 4, at most 512 tokens per window, region
+ * labels uniform over each group of 4 temporal positions) and the
+ * exclusion mask (no VSWIN_F_MASK_M100).                                    */
+vswin_status vswin_bwd_workspace_query(const vswin_desc* desc, size_t* block_bytes, size_t* msa_bytes);
+
+/* Backward of vswin_block_fwd (eq. 1 differentiated; the backbone is
+ * fine-tuned on video, §4.1): given dy = dL/dy, writes dx = dL/dx (desc.dtype, same shape as
+ * x) and the weight gradients `g`.  The forward is recomputed inside the
+ * call (x and the weights are the forward's inputs; nothing is saved
+ * between calls).  Arithmetic: bf16 operands, fp32 accumulation; the
+ * attention probabilities are recomputed in fp32 from the forward's
+ * log-sum-exp; dS = P (dP - rowsum(dO * O)); the relative-position table
+ * gradient sums dS over the pairs of every offset (fp32 atomics, so its
+ * summation order is not fixed).  dx must not alias x or dy.
+ * workspace >= block_bytes of vswin_bwd_workspace_query, 256-byte aligned.  */
+vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w,
+                             const void* dy, void* dx, const vswin_block_grads* g,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of vswin_window_msa_fwd: given dy = dL/dy of the branch output,
+ * writes dx_norm = dL/dx_norm and the qkv, proj and table gradients of `g`.
+ * workspace >= msa_bytes of vswin_bwd_workspace_query.                     */
+vswin_status vswin_window_msa_bwd(const vswin_desc* desc, const void* x_norm, const vswin_block_weights* w,
+                                  const void* dy, void* dx_norm, const vswin_block_grads* g,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Index map of the pad + roll + partition permutation (§3.2):
  * map[w * N + n] = flat source token index b*T*H*W + (t*H + h)*W + w of
  * window slot n of window w (windows ordered (b, wt, wh, ww), slots

@@ -24,6 +24,7 @@ __all__ = [
     "vswin_index_map",
     "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
     "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd", "vswin_mfma_rate_probe",
+    "BlockGrads", "vswin_bwd_workspace_query", "vswin_block_bwd", "vswin_window_msa_bwd",
     "F_PAD_VISIBLE", "F_CLAMP_STRICT", "F_MASK_M100", "F_TABLES_READY", "LIB_PATH",
 ]
 
@@ -52,6 +53,12 @@ class Desc(ctypes.Structure):
 
 
 class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "ln1_g", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b", "rpb_table",
+        "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+
+
+class BlockGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "ln1_g", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b", "rpb_table",
         "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
@@ -100,6 +107,9 @@ def lib() -> ctypes.CDLL:
         "vswin_last_error": (ctypes.c_char_p, []),
         "vswin_abi_version": (i32, []),
         "vswin_mfma_rate_probe": (i32, [vp, i32, i32, vp]),
+        "vswin_bwd_workspace_query": (i32, [pdesc, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "vswin_block_bwd": (i32, [pdesc, vp, pw, vp, vp, ctypes.POINTER(BlockGrads), vp, sz, vp]),
+        "vswin_window_msa_bwd": (i32, [pdesc, vp, pw, vp, vp, ctypes.POINTER(BlockGrads), vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -260,6 +270,64 @@ def vswin_reverse_fwd(windows: torch.Tensor, shape, window, shift, *, residual=N
     _check(lib().vswin_reverse_fwd(ctypes.byref(d), _ptr(windows), _ptr(residual), _ptr(y),
                                    _stream(stream)))
     return y
+
+
+GRAD_NAMES = ("ln1_g", "ln1_b", "qkv_w", "qkv_b", "proj_w", "proj_b", "rpb_table",
+              "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
+MSA_GRAD_NAMES = ("qkv_w", "qkv_b", "proj_w", "proj_b", "rpb_table")
+
+
+def vswin_bwd_workspace_query(desc: Desc) -> Dict[str, int]:
+    """Workspace bytes of vswin_block_bwd ("block") and vswin_window_msa_bwd ("msa")."""
+    b, m = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().vswin_bwd_workspace_query(ctypes.byref(desc), ctypes.byref(b), ctypes.byref(m)))
+    return {"block": b.value, "msa": m.value}
+
+
+def _grads(w: Dict[str, torch.Tensor], names, grads: Optional[Dict[str, torch.Tensor]]):
+    """fp32 gradient buffers shaped like the weights (allocated unless given)."""
+    out = {} if grads is None else dict(grads)
+    for n in names:
+        if n not in out and w.get(n) is not None:
+            out[n] = torch.empty(w[n].shape, dtype=torch.float32, device=w[n].device)
+    bg = BlockGrads()
+    for n in GRAD_NAMES:
+        setattr(bg, n, _ptr(out[n]) if n in out else None)
+    return out, bg
+
+
+def vswin_block_bwd(x: torch.Tensor, w: Dict[str, torch.Tensor], dy: torch.Tensor, heads: int,
+                    window: Sequence[int], shift: Sequence[int], *, eps: float = 1e-5, flags: int = 0,
+                    dx: Optional[torch.Tensor] = None, grads: Optional[Dict[str, torch.Tensor]] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of vswin_block_fwd: (dx, {weight name: fp32 gradient})."""
+    hid = w["fc1_w"].shape[0]
+    d = _desc_for(x, heads, window, shift, eps, flags, hid)
+    nbytes = vswin_bwd_workspace_query(d)["block"]
+    dxo = torch.empty_like(x) if dx is None else dx
+    ws = _workspace(nbytes, x.device, workspace)
+    g, bg = _grads(w, GRAD_NAMES, grads)
+    bw = _weights(w)
+    _check(lib().vswin_block_bwd(ctypes.byref(d), _ptr(x), ctypes.byref(bw), _ptr(dy), _ptr(dxo),
+                                 ctypes.byref(bg), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return dxo, g
+
+
+def vswin_window_msa_bwd(x_norm: torch.Tensor, w: Dict[str, torch.Tensor], dy: torch.Tensor, heads: int,
+                         window: Sequence[int], shift: Sequence[int], *, eps: float = 1e-5, flags: int = 0,
+                         dx: Optional[torch.Tensor] = None, grads: Optional[Dict[str, torch.Tensor]] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of vswin_window_msa_fwd: (dx_norm, {qkv/proj/table name: fp32 gradient})."""
+    d = _desc_for(x_norm, heads, window, shift, eps, flags, 4 * x_norm.shape[-1])
+    nbytes = vswin_bwd_workspace_query(d)["msa"]
+    dxo = torch.empty_like(x_norm) if dx is None else dx
+    ws = _workspace(nbytes, x_norm.device, workspace)
+    g, bg = _grads(w, MSA_GRAD_NAMES, grads)
+    bw = _weights(w)
+    _check(lib().vswin_window_msa_bwd(ctypes.byref(d), _ptr(x_norm), ctypes.byref(bw), _ptr(dy), _ptr(dxo),
+                                      ctypes.byref(bg), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)))
+    return dxo, g
 
 
 def vswin_mfma_rate_probe(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:

@@ -548,6 +548,8 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
     const int qs = 16 * (jt + CF::kWaves * (U0 + u)) + fr;
     if (qs >= N) continue;
     const float inv = __builtin_amdgcn_rcpf(st.os[u][0]);
+    if (a.lse && g4 == 0)
+      a.lse[(int64_t)wi.mem * N + qs] = __builtin_amdgcn_logf(st.os[u][0]) + (exact ? st.mrow[u] : 0.f);
     u32x4_t pk;
     pk[0] = pack_bf16x2(st.o0[u][0] * inv, st.o0[u][1] * inv);
     pk[1] = pack_bf16x2(st.o0[u][2] * inv, st.o0[u][3] * inv);
@@ -815,6 +817,452 @@ hipError_t attention_mfma(const AttnArgs& a, hipStream_t st) {
   }
   if (L.tg.scalar) return launch_cfg<Cfg<8, 8, true>>(ak, L, st);
   return launch_cfg<Cfg<8, 4>>(ak, L, st);
+}
+
+// ===========================================================================
+// Backward of the window attention (training), bf16, head_dim 32.
+//
+// Per (window, head) item, with P = exp2(S2 - lse2) recomputed from the
+// forward's log2-domain logits S2 = q' k^T + B log2(e) (q' = q log2(e) /
+// sqrt(d)) and the forward's row normaliser lse2:
+//   dP = dO v^T,  D_i = sum_e dO_ie O_ie,  dS = P (dP - D)   (natural logits)
+//   dv = P^T dO,  dk = dS^T q' / log2(e),  dq = dS k / sqrt(d),
+//   dB[offset(i, j), h] += dS_ij          (the relative-position table)
+// Two MFMA kernels, one workgroup per item:
+//   attn_bwd_kv: each wave owns 16-key tiles and sweeps every query; S and
+//     dP come out as (4 queries x 1 key) per lane, so P and dS are already
+//     the B operand of dV^T = dO^T P and dK^T = q'^T dS over 32 queries (the
+//     transposes staged in pair order), and dS goes into an LDS copy of the
+//     head's table gradient (flushed with global atomics);
+//   attn_bwd_q: each wave owns 16-query tiles and sweeps every key, S^T and
+//     dP^T as in the forward (4 keys x 1 query per lane), dQ^T = k^T dS^T.
+// attn_bwd_prep writes the padded row copies (q', k, v, dO), the pair-order
+// transposes (q'^T, k^T, dO^T) and D.  The bias table is read in the scalar
+// form (a tuple is 4 floats Rp apart; query-side tuples run backwards).
+// ===========================================================================
+namespace {
+
+struct BwdL {
+  A5 L;                       // geometry, table extents, scalar table form
+  int pitch;                  // transposed LDS rows: 16-byte chunks, 4 mod 16
+  // kernel A LDS
+  uint32_t a_q, a_do, a_qt, a_dot, a_lse, a_D, a_dtab, a_lds;
+  // kernel B LDS
+  uint32_t b_k, b_v, b_kt, b_lds;
+};
+
+__device__ __forceinline__ void stage_rows16(const bf16_t* src, unsigned char* dst, int nrows, int wv, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int off = (lane >> 2) * 32 + (((lane & 3) ^ ((lane >> 4) & 3)) << 3);
+  for (int b = wv; b < nrows / 16; b += nw)
+    __builtin_amdgcn_global_load_lds(src + b * 512 + off, (lds_ptr_t)(dst + b * 1024), 16, 0, 0);
+}
+
+// 32 rows of NPAD bf16 (pair order already applied) into rows of `pitch`
+// 16-byte chunks, chunk c of row d at c ^ ((d >> 3) & 3)
+__device__ __forceinline__ void stage_trows(const bf16_t* src, unsigned char* dst, int NPAD, int pitch, int wv,
+                                            int nw) {
+  const int lane = threadIdx.x & 63;
+  const int kc = NPAD / 8;
+  const int nb = (kc + 63) / 64;
+  for (int x = wv; x < 32 * nb; x += nw) {
+    const int d = x / nb, base = 64 * (x - d * nb);
+    const int slot = base + lane;
+    if (slot < kc)
+      __builtin_amdgcn_global_load_lds(src + (size_t)d * NPAD + ((slot ^ ((d >> 3) & 3)) << 3),
+                                       (lds_ptr_t)(dst + ((size_t)d * pitch + base) * 16), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void stage_f32(const float* src, unsigned char* dst, int n, int wv, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int nc = n / 4;
+  for (int b = wv; b * 64 < nc; b += nw)
+    if (64 * b + lane < nc)
+      __builtin_amdgcn_global_load_lds(src + 4 * (64 * b + lane), (lds_ptr_t)(dst + 1024 * b), 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t pack8f(const float* v) {
+  u32x4_t p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  return __builtin_bit_cast(bf16x8_t, p);
+}
+
+using BwdCF = Cfg<8, 8, true>;   // 8 waves, scalar table (byte step 4)
+
+}  // namespace
+
+__global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const AttnBwdArgs b, const BwdL BL) {
+  const A5& L = BL.L;
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64 * 40];
+  const int mem = blockIdx.x;
+  const int w = (int)fdiv((uint32_t)mem, L.fdH), h = mem - w * L.heads;
+  const int N = L.N, NPAD = L.NPAD, C = b.a.C;
+  const int t = threadIdx.x;
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(b.a.q);
+  const bf16_t* k = reinterpret_cast<const bf16_t*>(b.a.k);
+  const bf16_t* vt = reinterpret_cast<const bf16_t*>(b.a.v);
+  const bf16_t* o = reinterpret_cast<const bf16_t*>(b.a.o);
+  const bf16_t* dout = reinterpret_cast<const bf16_t*>(b.dout);
+  for (int which = 0; which < 4; ++which) {   // q', k, dO (+ D), v
+    bf16_t* rows = which == 0 ? b.qr : which == 1 ? b.kr : which == 2 ? b.dor : b.vr;
+    bf16_t* tr = which == 0 ? b.qt : which == 1 ? b.kt : b.dot;
+    for (int r0 = 0; r0 < NPAD; r0 += 64) {
+      if (which < 3) {
+        // thread t: row r0 + t / 4, 8 channels 8 (t % 4) ..
+        const int r = r0 + (t >> 2), c = t & 3;
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        float dsum = 0.f;
+        if (r < N) {
+          const bf16_t* src = which == 0 ? q + ((int64_t)mem * N + r) * 32
+                            : which == 1 ? k + ((int64_t)mem * N + r) * 32
+                                         : dout + ((int64_t)w * N + r) * C + h * 32;
+          v = *reinterpret_cast<const u32x4_t*>(src + 8 * c);
+          if (which == 0 && L.qscale != 1.0f) {   // the forward's q' (same rounding as its q load)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(bflo(v[e]) * L.qscale, bfhi(v[e]) * L.qscale);
+          }
+          if (which == 2) {
+            const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(o + ((int64_t)w * N + r) * C + h * 32 + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dsum += bflo(v[e]) * bflo(ov[e]) + bfhi(v[e]) * bfhi(ov[e]);
+          }
+        }
+        if (which == 2) {
+          dsum += __shfl_xor(dsum, 1);
+          dsum += __shfl_xor(dsum, 2);
+          if (c == 0 && r < NPAD) b.D[(int64_t)mem * NPAD + r] = dsum;
+        }
+        if (r < NPAD) *reinterpret_cast<u32x4_t*>(rows + ((int64_t)mem * NPAD + r) * 32 + 8 * c) = v;
+        *reinterpret_cast<u32x4_t*>(tile + (t >> 2) * 40 + 8 * c) = v;
+        __syncthreads();
+        // thread t: dim t / 8, output chunk t % 8 of the 64 rows (pair order
+        // inside each 32-row block: chunk g holds rows 4g..4g+3, 16+4g..16+4g+3)
+        const int d = t >> 3, cc = t & 7, pl = cc >> 2, g = cc & 3;
+        if (r0 + 32 * pl < NPAD) {
+          float vals[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vals[e] = bf2f(tile[(32 * pl + 16 * (e >> 2) + 4 * g + (e & 3)) * 40 + d]);
+          *reinterpret_cast<bf16x8_t*>(tr + ((int64_t)mem * 32 + d) * NPAD + r0 + 8 * cc) = pack8f(vals);
+        }
+        __syncthreads();
+      } else {
+        // V^T -> rows: thread t: dim t / 8, keys r0 + 8 (t % 8) .. + 7
+        const int d = t >> 3, kc = t & 7;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int key = r0 + 8 * kc + 4 * hh;
+          u32x2_t v = u32x2_t{0u, 0u};
+          if (key < N) v = *reinterpret_cast<const u32x2_t*>(vt + ((int64_t)mem * 32 + d) * N + key);
+          tile[(8 * kc + 4 * hh + 0) * 40 + d] = (bf16_t)(v[0] & 0xffffu);
+          tile[(8 * kc + 4 * hh + 1) * 40 + d] = (bf16_t)(v[0] >> 16);
+          tile[(8 * kc + 4 * hh + 2) * 40 + d] = (bf16_t)(v[1] & 0xffffu);
+          tile[(8 * kc + 4 * hh + 3) * 40 + d] = (bf16_t)(v[1] >> 16);
+        }
+        __syncthreads();
+        const int r = r0 + (t >> 2), c = t & 3;
+        if (r < NPAD)
+          *reinterpret_cast<u32x4_t*>(rows + ((int64_t)mem * NPAD + r) * 32 + 8 * c) =
+              *reinterpret_cast<const u32x4_t*>(tile + (t >> 2) * 40 + 8 * c);
+        __syncthreads();
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, const BwdL BL) {
+  using CF = BwdCF;
+  constexpr int ES = CF::kTabEs;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const A5& L = BL.L;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, fr = lane & 15, g4 = lane >> 4;
+  const Win wi = window_of(b.a, L, blockIdx.x);
+  const int mem = wi.mem, h = wi.h;
+  const int N = L.N, NPAD = L.NPAD, Rp = L.Rp;
+  const int nd = L.TD * Rp;
+  int* kp = reinterpret_cast<int*>(smem + L.off_kp);
+  const int* lp = reinterpret_cast<const int*>(smem + L.off_lp);
+  float* dtab = reinterpret_cast<float*>(smem + BL.a_dtab);
+  stage_offsets<CF>(b.a, L, kp);
+  stage_labels<CF>(b.a, L, wi, smem);
+  for (int i = (int)threadIdx.x; i < nd; i += CF::kThreads) dtab[i] = 0.f;
+  stage_rows16(b.qr + (int64_t)mem * NPAD * 32, smem + BL.a_q, NPAD, wv, CF::kWaves);
+  stage_rows16(b.dor + (int64_t)mem * NPAD * 32, smem + BL.a_do, NPAD, wv, CF::kWaves);
+  stage_trows(b.qt + (int64_t)mem * 32 * NPAD, smem + BL.a_qt, NPAD, BL.pitch, wv, CF::kWaves);
+  stage_trows(b.dot + (int64_t)mem * 32 * NPAD, smem + BL.a_dot, NPAD, BL.pitch, wv, CF::kWaves);
+  stage_f32(b.lse + (int64_t)mem * N, smem + BL.a_lse, N, wv, CF::kWaves);
+  stage_f32(b.D + (int64_t)mem * NPAD, smem + BL.a_D, NPAD, wv, CF::kWaves);
+  tab_copy<CF>(b.a, L, h, smem, wv);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  const unsigned char* tabb = smem;
+  const float* lse = reinterpret_cast<const float*>(smem + BL.a_lse);
+  const float* Dl = reinterpret_cast<const float*>(smem + BL.a_D);
+  const int sw = (fr >> 2) & 3;
+  bf16_t* dqkv = b.dqkv;
+  const int C = b.a.C;
+  for (int kt = wv; kt * 16 < N; kt += CF::kWaves) {
+    const int key = kt * 16 + fr;
+    const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(b.kr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
+    const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(b.vr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
+    const int kps = pair_slot(key >> 2);
+    const int klab = lp[kps];
+    const int kadd = (int)L.off_tab + ES * L.A + kp[kps] + ES * (key & 3) * Rp;
+    const bool kval = key < N;
+    f32x4_t dv0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, dv1 = dv0, dk0 = dv0, dk1 = dv0;
+    for (int qb = 0; qb < NPAD; qb += 32) {
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int qs0 = qb + 16 * s;
+        const int qr = qs0 + fr;
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_q + qr * 64 + ((g4 ^ sw) << 4));
+        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_do + qr * 64 + ((g4 ^ sw) << 4));
+        const int qps = pair_slot((qs0 + 4 * g4) >> 2);
+        const int qlab = lp[qps];
+        const int base = kadd - kp[qps];   // query temporal i: - i Rp
+        const float* tp = reinterpret_cast<const float*>(tabb + base);
+        const f32x4_t tb = f32x4_t{tp[0], tp[-Rp], tp[-2 * Rp], tp[-3 * Rp]};
+        const f32x4_t s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf, tb, 0, 0, 0);
+        const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse + qs0 + 4 * g4);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(Dl + qs0 + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = kval && qs0 + 4 * g4 + i < N && qlab == klab;
+          const float P = valid ? __builtin_amdgcn_exp2f(s2[i] - l4[i]) : 0.f;
+          const float ds = P * (dp[i] - d4[i]);
+          if (valid) atomicAdd(dtab + (base - (int)L.off_tab) / ES - i * Rp, ds);
+          pv[4 * s + i] = P;
+          dsv[4 * s + i] = ds;
+        }
+      }
+      const bf16x8_t pb = pack8f(pv), db = pack8f(dsv);
+      const int ch = qb / 8 + g4;
+      const unsigned char* t0 = smem + (fr * BL.pitch + (ch ^ ((fr >> 3) & 3))) * 16;
+      const unsigned char* t1 = smem + ((16 + fr) * BL.pitch + (ch ^ (((16 + fr) >> 3) & 3))) * 16;
+      const bf16x8_t do0 = *reinterpret_cast<const bf16x8_t*>(t0 + BL.a_dot);
+      const bf16x8_t do1 = *reinterpret_cast<const bf16x8_t*>(t1 + BL.a_dot);
+      const bf16x8_t qt0 = *reinterpret_cast<const bf16x8_t*>(t0 + BL.a_qt);
+      const bf16x8_t qt1 = *reinterpret_cast<const bf16x8_t*>(t1 + BL.a_qt);
+      dv0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do0, pb, dv0, 0, 0, 0);
+      dv1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do1, pb, dv1, 0, 0, 0);
+      dk0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt0, db, dk0, 0, 0, 0);
+      dk1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt1, db, dk1, 0, 0, 0);
+    }
+    if (kval) {
+      // lane: dims 4 g4 .. + 3 (and + 16) of key `key`
+      bf16_t* row = dqkv + ((int64_t)wi.w * N + key) * 3 * C + h * 32 + 4 * g4;
+      const float ks = b.dk_scale;
+      *reinterpret_cast<u32x2_t*>(row + 2 * C) = u32x2_t{pack_bf16x2(dv0[0], dv0[1]), pack_bf16x2(dv0[2], dv0[3])};
+      *reinterpret_cast<u32x2_t*>(row + 2 * C + 16) =
+          u32x2_t{pack_bf16x2(dv1[0], dv1[1]), pack_bf16x2(dv1[2], dv1[3])};
+      *reinterpret_cast<u32x2_t*>(row + C) =
+          u32x2_t{pack_bf16x2(dk0[0] * ks, dk0[1] * ks), pack_bf16x2(dk0[2] * ks, dk0[3] * ks)};
+      *reinterpret_cast<u32x2_t*>(row + C + 16) =
+          u32x2_t{pack_bf16x2(dk1[0] * ks, dk1[1] * ks), pack_bf16x2(dk1[2] * ks, dk1[3] * ks)};
+    }
+  }
+  __syncthreads();
+  float* gt = b.dtab + (int64_t)h * nd;
+  for (int i = (int)threadIdx.x; i < nd; i += CF::kThreads) {
+    const float v = dtab[i];
+    if (v != 0.f) atomicAdd(gt + i, v);
+  }
+}
+
+__global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, const BwdL BL) {
+  using CF = BwdCF;
+  constexpr int ES = CF::kTabEs;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const A5& L = BL.L;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, fr = lane & 15, g4 = lane >> 4;
+  const Win wi = window_of(b.a, L, blockIdx.x);
+  const int mem = wi.mem, h = wi.h;
+  const int N = L.N, NPAD = L.NPAD, Rp = L.Rp;
+  int* kp = reinterpret_cast<int*>(smem + L.off_kp);
+  const int* lp = reinterpret_cast<const int*>(smem + L.off_lp);
+  stage_offsets<CF>(b.a, L, kp);
+  stage_labels<CF>(b.a, L, wi, smem);
+  stage_rows16(b.kr + (int64_t)mem * NPAD * 32, smem + BL.b_k, NPAD, wv, CF::kWaves);
+  stage_rows16(b.vr + (int64_t)mem * NPAD * 32, smem + BL.b_v, NPAD, wv, CF::kWaves);
+  stage_trows(b.kt + (int64_t)mem * 32 * NPAD, smem + BL.b_kt, NPAD, BL.pitch, wv, CF::kWaves);
+  tab_copy<CF>(b.a, L, h, smem, wv);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  const unsigned char* tabb = smem;
+  const int sw = (fr >> 2) & 3;
+  const int C = b.a.C;
+  for (int qt = wv; qt * 16 < N; qt += CF::kWaves) {
+    const int q = qt * 16 + fr;
+    const bool qval = q < N;
+    const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(b.qr + ((int64_t)mem * NPAD + q) * 32 + 8 * g4);
+    const bf16x8_t df = *reinterpret_cast<const bf16x8_t*>(b.dor + ((int64_t)mem * NPAD + q) * 32 + 8 * g4);
+    const float l2 = qval ? b.lse[(int64_t)mem * N + q] : 0.f;
+    const float Dq = b.D[(int64_t)mem * NPAD + q];
+    const int qps = pair_slot(q >> 2);
+    const int qlab = lp[qps];
+    const int qaddr = (int)L.off_tab + ES * L.A - kp[qps] - ES * (q & 3) * Rp;
+    f32x4_t dq0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, dq1 = dq0;
+    for (int kb = 0; kb < NPAD; kb += 32) {
+      float dsv[8];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ks0 = kb + 16 * s;
+        const int kr = ks0 + fr;
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_k + kr * 64 + ((g4 ^ sw) << 4));
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_v + kr * 64 + ((g4 ^ sw) << 4));
+        const int kps = pair_slot((ks0 + 4 * g4) >> 2);
+        const int klab = lp[kps];
+        const float* tp = reinterpret_cast<const float*>(tabb + qaddr + kp[kps]);
+        const f32x4_t tb = f32x4_t{tp[0], tp[Rp], tp[2 * Rp], tp[3 * Rp]};
+        const f32x4_t s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf, tb, 0, 0, 0);
+        const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = qval && ks0 + 4 * g4 + i < N && qlab == klab;
+          const float P = valid ? __builtin_amdgcn_exp2f(s2[i] - l2) : 0.f;
+          dsv[4 * s + i] = P * (dp[i] - Dq);
+        }
+      }
+      const bf16x8_t db = pack8f(dsv);
+      const int ch = kb / 8 + g4;
+      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(
+          smem + BL.b_kt + (fr * BL.pitch + (ch ^ ((fr >> 3) & 3))) * 16);
+      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(
+          smem + BL.b_kt + ((16 + fr) * BL.pitch + (ch ^ (((16 + fr) >> 3) & 3))) * 16);
+      dq0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, db, dq0, 0, 0, 0);
+      dq1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, db, dq1, 0, 0, 0);
+    }
+    if (qval) {
+      bf16_t* row = b.dqkv + ((int64_t)wi.w * N + q) * 3 * C + h * 32 + 4 * g4;
+      const float qs = b.dq_scale;
+      *reinterpret_cast<u32x2_t*>(row) =
+          u32x2_t{pack_bf16x2(dq0[0] * qs, dq0[1] * qs), pack_bf16x2(dq0[2] * qs, dq0[3] * qs)};
+      *reinterpret_cast<u32x2_t*>(row + 16) =
+          u32x2_t{pack_bf16x2(dq1[0] * qs, dq1[1] * qs), pack_bf16x2(dq1[2] * qs, dq1[3] * qs)};
+    }
+  }
+}
+
+// table-row layout of the accumulated scalar-form gradient (the inverse of
+// ts_entry's index map); every row has exactly one scalar index
+__global__ void __launch_bounds__(256) attn_bwd_dtab_kernel(const float* __restrict__ dtab, float* __restrict__ out,
+                                                             const Tab4Geo tg, int rows) {
+  const int x = blockIdx.x * 256 + (int)threadIdx.x;
+  if (x >= rows * tg.heads) return;
+  const int row = x / tg.heads, h = x - row * tg.heads;
+  const int dtr = tg.TD - 1 - row / tg.R;
+  const int rem = row - (row / tg.R) * tg.R;
+  const int dhr = tg.TH - 1 - rem / tg.Rw;
+  const int dwr = tg.Rw - 1 - (rem - (rem / tg.Rw) * tg.Rw);
+  out[x] = dtab[(size_t)h * tg.TD * tg.Rp + dtr * tg.Rp + dhr * tg.Rw + dwr];
+}
+
+__global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+namespace {
+
+bool plan_bwd(const AttnArgs& a, BwdL& B) {
+  B = BwdL{};
+  A5& L = B.L;
+  if (!plan_a5(a, L)) return false;
+  // scalar table form, whatever N
+  L.tg = tab4_geo(a.rel, a.heads, kMfmaMaxN + 1);
+  L.TS4 = L.tg.TS4;
+  const int kc = L.NPAD / 8;
+  B.pitch = kc + ((4 - kc) % 16 + 16) % 16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 15) & ~(size_t)15;
+    return (uint32_t)o;
+  };
+  L.off_kp = take((size_t)L.NP * 8 * 4);
+  L.off_lp = take((size_t)L.NP * 8 * 4);
+  L.off_red = take(4 * kMaxWaves);
+  L.off_tab = take((size_t)L.TS4 * 16);
+  const size_t common = off;
+  const size_t rows = (size_t)L.NPAD * 64, trows = (size_t)32 * B.pitch * 16;
+  B.a_q = take(rows);
+  B.a_do = take(rows);
+  B.a_qt = take(trows);
+  B.a_dot = take(trows);
+  B.a_lse = take((size_t)L.NPAD * 4);
+  B.a_D = take((size_t)L.NPAD * 4);
+  B.a_dtab = take((size_t)L.TD * L.Rp * 4);
+  B.a_lds = (uint32_t)off;
+  off = common;
+  B.b_k = take(rows);
+  B.b_v = take(rows);
+  B.b_kt = take(trows);
+  B.b_lds = (uint32_t)off;
+  L.zone = 0;
+  return B.a_lds <= kLdsMax && B.b_lds <= kLdsMax;
+}
+
+}  // namespace
+
+bool attention_bwd_supported(vswin_dtype dt, const AttnArgs& a) {
+  if (!attention_mfma_supported(dt, a) || a.mask_m100 || !groups_uniform(a)) return false;
+  BwdL B;
+  return plan_bwd(a, B);
+}
+
+size_t attention_bwd_workspace_bytes(const AttnArgs& a) {
+  BwdL B;
+  if (!plan_bwd(a, B)) return 0;
+  const A5& L = B.L;
+  const size_t items = (size_t)a.nW * a.heads;
+  const size_t arr = ((size_t)items * L.NPAD * 32 * 2 + 255) & ~(size_t)255;
+  const size_t D = ((size_t)items * L.NPAD * 4 + 255) & ~(size_t)255;
+  const size_t tabs = ((size_t)a.heads * L.TS4 * 16 + 255) & ~(size_t)255;
+  const size_t dtab = ((size_t)a.heads * L.TD * L.Rp * 4 + 255) & ~(size_t)255;
+  return 7 * arr + D + tabs + dtab;
+}
+
+hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
+  const int64_t items = in.a.nW * in.a.heads;
+  BwdL B;
+  if (!plan_bwd(in.a, B) || !in.work || !in.dtable || !in.lse) return hipErrorInvalidValue;
+  const A5& L = B.L;
+  AttnBwdArgs b = in;
+  char* w = reinterpret_cast<char*>(in.work);
+  const size_t arr = ((size_t)items * L.NPAD * 32 * 2 + 255) & ~(size_t)255;
+  bf16_t** slots[7] = {&b.qr, &b.kr, &b.vr, &b.dor, &b.qt, &b.kt, &b.dot};
+  for (int i = 0; i < 7; ++i) *slots[i] = reinterpret_cast<bf16_t*>(w + i * arr);
+  size_t off = 7 * arr;
+  b.D = reinterpret_cast<float*>(w + off);
+  off += ((size_t)items * L.NPAD * 4 + 255) & ~(size_t)255;
+  b.a.tab4 = w + off;
+  off += ((size_t)in.a.heads * L.TS4 * 16 + 255) & ~(size_t)255;
+  b.dtab = reinterpret_cast<float*>(w + off);
+  b.dq_scale = 1.0f / sqrtf((float)in.a.d);
+  b.dk_scale = 1.0f / kLog2e;
+  if (items <= 0) return hipSuccess;
+  const int64_t nd = (int64_t)in.a.heads * L.TD * L.Rp;
+  zero_f32_kernel<<<dim3((unsigned)((nd + 255) / 256 < 1024 ? (nd + 255) / 256 : 1024)), dim3(256), 0, st>>>(b.dtab,
+                                                                                                          nd);
+  attn_table_kernel<<<dim3((unsigned)((L.TS4 + 255) / 256), (unsigned)L.heads), dim3(256), 0, st>>>(
+      reinterpret_cast<const bf16_t*>(in.a.table), reinterpret_cast<f32x4_t*>(b.a.tab4), L);
+  attn_bwd_prep_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(b, B);
+  hipError_t e = ensure_dynamic_lds((const void*)attn_bwd_kv_kernel, B.a_lds);
+  if (e != hipSuccess) return e;
+  e = ensure_dynamic_lds((const void*)attn_bwd_q_kernel, B.b_lds);
+  if (e != hipSuccess) return e;
+  attn_bwd_kv_kernel<<<dim3((unsigned)items), dim3(512), B.a_lds, st>>>(b, B);
+  attn_bwd_q_kernel<<<dim3((unsigned)items), dim3(512), B.b_lds, st>>>(b, B);
+  const int rows = in.a.rel.rows;
+  attn_bwd_dtab_kernel<<<dim3((unsigned)((rows * in.a.heads + 255) / 256)), dim3(256), 0, st>>>(b.dtab, in.dtable,
+                                                                                               L.tg, rows);
+  return hipGetLastError();
 }
 
 }  // namespace vswin

@@ -1,0 +1,388 @@
+// Backward pass of the Video Swin block (training), bf16 activations with
+// fp32 accumulation (§3.1 / eq. 1 and §3.2 / eq. 2 of "Video Swin
+// Transformer", differentiated step by step):
+//   * weight gradients dW = dY^T X of the linear layers: `wgrad_kernel`, MFMA
+//     with the token dimension as the contraction (both operands staged
+//     token-contiguous in LDS by transposing 16-byte row loads), one fp32
+//     partial per group of 256-token chunks, summed by `reduce_parts_kernel`;
+//     the bias gradient (column sums of dY) in the same pass;
+//   * LayerNorm backward `ln_bwd_kernel`: one wave per token row, the
+//     statistics recomputed, dx = (dxh - mean(dxh) - xh mean(dxh xh)) / sigma
+//     with dxh = dy g, plus a residual gradient; dg, db as per-wave partials;
+//   * GELU x Phi(x) and its derivative Phi(x) + x phi(x) (erff);
+//   * the gather of an fp32 token-row gradient into bf16 window rows (zeros
+//     for pad slots) and the weight transposes the input-gradient GEMMs use.
+#include "vswin_kernels.h"
+
+#include <math.h>
+
+namespace vswin {
+
+namespace {
+
+constexpr int kWgChunk = 256;     // tokens per staged chunk
+constexpr int kWgPitch = 264;     // LDS row pitch (bf16) of the token-contiguous operands
+constexpr int kMaxParts = 128;    // fp32 partials of one weight gradient at most
+
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_d(float x) {
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * __expf(-0.5f * x * x);
+}
+
+__device__ __forceinline__ void unpack8f(const u32x4_t v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bflo(v[i]);
+    f[2 * i + 1] = bfhi(v[i]);
+  }
+}
+__device__ __forceinline__ u32x4_t pack8u(const float* f) {
+  u32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+
+}  // namespace
+
+// dst (C x R) = src (R x C)^T, bf16; 32 x 32 tiles through LDS
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
+                                                              int R, int C) {
+  __shared__ bf16_t t[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8)
+    if (r0 + i < R && c0 + tx < C) t[i][tx] = src[(int64_t)(r0 + i) * C + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8)
+    if (c0 + i < C && r0 + tx < R) dst[(int64_t)(c0 + i) * R + r0 + tx] = t[tx][i];
+}
+
+// h = GELU(a) (bwd = 0) or da = dh * GELU'(a) written over dh (bwd = 1); n % 8 == 0
+__global__ void __launch_bounds__(256) gelu_kernel(const bf16_t* __restrict__ a, bf16_t* __restrict__ io, int64_t n,
+                                                   int bwd) {
+  for (int64_t i = (blockIdx.x * 256 + (int64_t)threadIdx.x) * 8; i < n; i += (int64_t)gridDim.x * 256 * 8) {
+    float x[8], y[8];
+    unpack8f(*reinterpret_cast<const u32x4_t*>(a + i), x);
+    if (bwd) {
+      float g[8];
+      unpack8f(*reinterpret_cast<const u32x4_t*>(io + i), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = g[e] * gelu_d(x[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = gelu_f(x[e]);
+    }
+    *reinterpret_cast<u32x4_t*>(io + i) = pack8u(y);
+  }
+}
+
+// window row m of `out` (bf16) = token row src(m) of `in` (fp32), 0 for pads
+__global__ void __launch_bounds__(256) gather_f32_bf16_kernel(const float* __restrict__ in, bf16_t* __restrict__ out,
+                                                               int64_t slots, int C, const WinGeo geo) {
+  const int per = C / 8;
+  for (int64_t x = blockIdx.x * 256 + (int64_t)threadIdx.x; x < slots * per; x += (int64_t)gridDim.x * 256) {
+    const int64_t m = x / per;
+    const int c = (int)(x - m * per) * 8;
+    int lab;
+    const int64_t src = row_source(geo, (int)m, lab);
+    float v[8];
+    if (src >= 0) {
+      const float4 a = *reinterpret_cast<const float4*>(in + src * C + c);
+      const float4 b = *reinterpret_cast<const float4*>(in + src * C + c + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    *reinterpret_cast<u32x4_t*>(out + m * C + c) = pack8u(v);
+  }
+}
+
+// LayerNorm backward, one wave per row, C <= 64 * kLnJ.  x: TX (fp32 / bf16),
+// dy: bf16, res (nullable): TR added to dx, out: TO.  part: per wave, dg then db (2C).
+constexpr int kLnJ = 12;
+template <typename TX, typename TR, typename TO>
+__global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, const bf16_t* __restrict__ g,
+                                                     const bf16_t* __restrict__ dy, const TR* __restrict__ res,
+                                                     TO* __restrict__ out, float* __restrict__ part, int64_t rows,
+                                                     int C, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = blockIdx.x * 4 + (threadIdx.x >> 6), nw = (int64_t)gridDim.x * 4;
+  float dgs[kLnJ], dbs[kLnJ], gv[kLnJ];
+#pragma unroll
+  for (int j = 0; j < kLnJ; ++j) {
+    dgs[j] = dbs[j] = 0.f;
+    const int c = lane + 64 * j;
+    gv[j] = c < C ? bf2f(g[c]) : 0.f;
+  }
+  const float invC = 1.0f / C;
+  for (int64_t r = wave; r < rows; r += nw) {
+    float xv[kLnJ], dv[kLnJ];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kLnJ; ++j) {
+      const int c = lane + 64 * j;
+      xv[j] = c < C ? Elem<TX>::load(x, r * C + c) : 0.f;
+      dv[j] = c < C ? bf2f(dy[r * C + c]) : 0.f;
+      s += xv[j];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    const float mu = s * invC;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < kLnJ; ++j) {
+      const int c = lane + 64 * j;
+      const float d = c < C ? xv[j] - mu : 0.f;
+      q += d * d;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
+    const float rstd = 1.0f / sqrtf(q * invC + eps);
+    float a = 0.f, bsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kLnJ; ++j) {
+      const float xh = (xv[j] - mu) * rstd;
+      const float dxh = dv[j] * gv[j];
+      a += dxh;
+      bsum += dxh * xh;
+      dgs[j] += dv[j] * xh;
+      dbs[j] += dv[j];
+      xv[j] = xh;
+      dv[j] = dxh;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      a += __shfl_xor(a, o);
+      bsum += __shfl_xor(bsum, o);
+    }
+    a *= invC;
+    bsum *= invC;
+#pragma unroll
+    for (int j = 0; j < kLnJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C) {
+        float v = rstd * (dv[j] - a - xv[j] * bsum);
+        if (res) v += Elem<TR>::load(res, r * C + c);
+        Elem<TO>::store(out, r * C + c, v);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kLnJ; ++j) {
+    const int c = lane + 64 * j;
+    if (c < C) {
+      part[wave * 2 * C + c] = dgs[j];
+      part[wave * 2 * C + C + c] = dbs[j];
+    }
+  }
+}
+
+// Weight-gradient partials: part[p] (NO x KI) = sum over the tokens of
+// chunks p, p + P, ... of A[m, n] * B[m, k]; colp[p] (NO) = sum of A[m, n]
+// (written by the k-block-0 workgroups).  A: (M, NO), B: (M, KI), bf16 rows.
+// Workgroup tile 32 n x BK k, 4 waves, each wave BK / 32 of the 16 x 16
+// output tiles; MFMA A operand = A^T rows (n) and B operand = B^T rows (k),
+// both token-contiguous in LDS.
+template <int BK>
+__global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+                                                    float* __restrict__ part, float* __restrict__ colp, int64_t M,
+                                                    int NO, int KI, int nparts) {
+  __shared__ __attribute__((aligned(16))) bf16_t At[32 * kWgPitch];
+  __shared__ __attribute__((aligned(16))) bf16_t Bt[BK * kWgPitch];
+  const int nblk = NO / 32, kblk = (KI + BK - 1) / BK;
+  int bid = blockIdx.x;
+  const int p = bid / (nblk * kblk);
+  bid -= p * nblk * kblk;
+  const int nb = bid / kblk, kb = bid - nb * kblk;
+  const int n0 = nb * 32, k0 = kb * BK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g4 = lane >> 4;
+  constexpr int TPW = BK / 32;   // output tiles per wave
+  f32x4_t acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float cs = 0.f;
+  const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
+  for (int64_t ch = p; ch < nchunks; ch += nparts) {
+    const int64_t m0 = ch * kWgChunk;
+    __syncthreads();
+    // A^T: 256 tokens x 32 n: thread -> token tid, 4 chunks of 8 n
+    {
+      const int64_t m = m0 + tid;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (m < M) v = *reinterpret_cast<const u32x4_t*>(A + m * NO + n0 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          At[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
+          At[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
+        }
+      }
+      // B^T: 256 tokens x BK k
+#pragma unroll
+      for (int c = 0; c < BK / 8; ++c) {
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (m < M && k0 + 8 * c < KI) v = *reinterpret_cast<const u32x4_t*>(B + m * KI + k0 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Bt[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
+          Bt[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tile = wave * TPW + i;            // 0 .. 2 * BK / 16 - 1
+      const int nh = tile & 1, kq = tile >> 1;
+#pragma unroll 4
+      for (int s = 0; s < kWgChunk / 32; ++s) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(At + (16 * nh + fr) * kWgPitch + 32 * s + 8 * g4);
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(Bt + (16 * kq + fr) * kWgPitch + 32 * s + 8 * g4);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+      }
+    }
+    if (kb == 0) {
+      // column sums: thread -> n = tid / 8, tokens 32 (tid % 8) .. + 31
+      const int n = tid >> 3, q = tid & 7;
+      float s = 0.f;
+      for (int t = 0; t < 32; ++t) s += bf2f(At[n * kWgPitch + 32 * q + t]);
+      cs += s;
+    }
+  }
+  // lane: n = n0 + 16 nh + 4 g4 + r, k = k0 + 16 kq + fr
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tile = wave * TPW + i;
+    const int nh = tile & 1, kq = tile >> 1;
+    const int k = k0 + 16 * kq + fr;
+    if (k < KI) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        part[((int64_t)p * NO + n0 + 16 * nh + 4 * g4 + r) * KI + k] = acc[i][r];
+    }
+  }
+  if (kb == 0) {
+    cs += __shfl_xor(cs, 1);
+    cs += __shfl_xor(cs, 2);
+    cs += __shfl_xor(cs, 4);
+    if ((tid & 7) == 0) colp[(int64_t)p * NO + n0 + (tid >> 3)] = cs;
+  }
+}
+
+// out[i] = sum_p part[p * stride + i], i < n
+__global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                           int nparts, int64_t n, int64_t stride) {
+  for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * stride + i];
+    out[i] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+namespace {
+unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 4096) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (unsigned)(g > cap ? cap : g);
+}
+}  // namespace
+
+hipError_t transpose_bf16(const void* src, void* dst, int R, int C, hipStream_t st) {
+  transpose_bf16_kernel<<<dim3((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32)), dim3(256), 0, st>>>(
+      (const bf16_t*)src, (bf16_t*)dst, R, C);
+  return hipGetLastError();
+}
+
+hipError_t gelu_apply(const void* a, void* io, int64_t n, int bwd, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  gelu_kernel<<<dim3(grid_for(n / 8, 256)), dim3(256), 0, st>>>((const bf16_t*)a, (bf16_t*)io, n, bwd);
+  return hipGetLastError();
+}
+
+hipError_t gather_f32_bf16(const float* in, void* out, int64_t slots, int C, const WinGeo& geo, hipStream_t st) {
+  if (slots <= 0) return hipSuccess;
+  if (C % 8) return hipErrorInvalidValue;
+  gather_f32_bf16_kernel<<<dim3(grid_for(slots * (C / 8), 256)), dim3(256), 0, st>>>(in, (bf16_t*)out, slots, C, geo);
+  return hipGetLastError();
+}
+
+int ln_bwd_waves(int64_t rows) {
+  const int64_t g = rows < 4096 ? rows : 4096;
+  return (int)(((g + 3) / 4) * 4);
+}
+
+size_t ln_bwd_part_bytes(int64_t rows, int C) { return (size_t)ln_bwd_waves(rows) * 2 * C * 4; }
+
+hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int res_fp32, const void* res,
+                  int out_fp32, void* out, float* part, float* dg, float* db, int64_t rows, int C, float eps,
+                  hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (C > 64 * kLnJ) return hipErrorInvalidValue;
+  const int nw = ln_bwd_waves(rows);
+  const dim3 grid((unsigned)(nw / 4)), block(256);
+  const bf16_t* gb = (const bf16_t*)g;
+  const bf16_t* dyb = (const bf16_t*)dy;
+  if (x_fp32 && !res_fp32 && out_fp32)
+    ln_bwd_kernel<float, bf16_t, float><<<grid, block, 0, st>>>((const float*)x, gb, dyb, (const bf16_t*)res,
+                                                                (float*)out, part, rows, C, eps);
+  else if (!x_fp32 && res_fp32 && !out_fp32)
+    ln_bwd_kernel<bf16_t, float, bf16_t><<<grid, block, 0, st>>>((const bf16_t*)x, gb, dyb, (const float*)res,
+                                                                 (bf16_t*)out, part, rows, C, eps);
+  else if (!x_fp32 && !res_fp32 && !out_fp32)
+    ln_bwd_kernel<bf16_t, bf16_t, bf16_t><<<grid, block, 0, st>>>((const bf16_t*)x, gb, dyb, (const bf16_t*)res,
+                                                                  (bf16_t*)out, part, rows, C, eps);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dg = sum over waves of part[w][0:C], db of part[w][C:2C]
+  reduce_parts_kernel<<<dim3(grid_for(C, 256)), dim3(256), 0, st>>>(part, dg, nw, C, 2 * C);
+  reduce_parts_kernel<<<dim3(grid_for(C, 256)), dim3(256), 0, st>>>(part + C, db, nw, C, 2 * C);
+  return hipGetLastError();
+}
+
+size_t wgrad_part_bytes(int64_t M, int NO, int KI) {
+  const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
+  const int64_t np = nchunks < kMaxParts ? nchunks : kMaxParts;
+  return (size_t)np * ((size_t)NO * KI + NO) * 4;
+}
+
+hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
+                 hipStream_t st) {
+  if (NO % 32 || KI % 32) return hipErrorInvalidValue;
+  if (M <= 0) {
+    // no tokens: zero gradients
+    reduce_parts_kernel<<<dim3(grid_for((int64_t)NO * KI, 256)), dim3(256), 0, st>>>(part, dW, 0, (int64_t)NO * KI, 0);
+    if (db) reduce_parts_kernel<<<dim3(grid_for(NO, 256)), dim3(256), 0, st>>>(part, db, 0, NO, 0);
+    return hipGetLastError();
+  }
+  const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
+  const int np = (int)(nchunks < kMaxParts ? nchunks : kMaxParts);
+  float* colp = part + (size_t)np * NO * KI;
+  const int nblk = NO / 32;
+  auto go = [&](auto kern, int bk) {
+    const int kblk = (KI + bk - 1) / bk;
+    kern<<<dim3((unsigned)(np * nblk * kblk)), dim3(256), 0, st>>>((const bf16_t*)A, (const bf16_t*)B, part, colp, M,
+                                                                   NO, KI, np);
+  };
+  if (KI % 128 == 0) go(wgrad_kernel<128>, 128);
+  else if (KI % 96 == 0) go(wgrad_kernel<96>, 96);
+  else if (KI % 64 == 0) go(wgrad_kernel<64>, 64);
+  else go(wgrad_kernel<32>, 32);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  reduce_parts_kernel<<<dim3(grid_for((int64_t)NO * KI, 256)), dim3(256), 0, st>>>(part, dW, np, (int64_t)NO * KI,
+                                                                                   (int64_t)NO * KI);
+  if (db) reduce_parts_kernel<<<dim3(grid_for(NO, 256)), dim3(256), 0, st>>>(colp, db, np, NO, NO);
+  return hipGetLastError();
+}
+
+}  // namespace vswin

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <functional>
 #include <map>
 #include <mutex>
 #include <new>
@@ -270,6 +272,62 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
   return VSWIN_OK;
 }
 
+// Workspace of the backward entry points (bytes, 256-aligned regions).
+struct BwdWs {
+  size_t n1w, q, k, v, o, tab, lse;           // forward recompute (window rows)
+  size_t zh, n2, a1, h, dh, dzh;              // block only
+  size_t dyw, dout, dqkv, dn1w, dn1, wT, part, attn;
+  size_t block_bytes, msa_bytes;
+};
+
+bool bwd_supported(const Plan& p, const vswin_desc* d) {
+  if (p.dt != VSWIN_BF16 || !p.fast || p.d != 32 || p.C > 768 || p.hid % 32) return false;
+  return attention_bwd_supported(p.dt, attn_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, d->flags));
+}
+
+BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
+  BwdWs w{};
+  const size_t act = align256((size_t)p.Lp * p.C * 2);
+  const size_t tok = align256((size_t)p.L * p.C * 2), tok32 = align256((size_t)p.L * p.C * 4);
+  const size_t hid = align256((size_t)p.L * p.hid * 2);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.n1w = take(act);
+  w.q = take(act);
+  w.k = take(act);
+  w.v = take(act);
+  w.o = take(act);
+  w.tab = take(p.ws_attn);
+  w.lse = take((size_t)p.nW * p.heads * p.N * 4);
+  w.dyw = take(act);
+  w.dout = take(act);
+  w.dqkv = take(3 * act);
+  w.dn1w = take(act);
+  w.dn1 = take(tok);
+  const size_t wmax = (size_t)(3 * p.C > p.hid ? 3 * p.C : p.hid) * p.C * 2;
+  w.wT = take(wmax);
+  size_t part = wgrad_part_bytes(p.Lp, 3 * p.C, p.C);
+  part = std::max(part, wgrad_part_bytes(p.Lp, p.C, p.C));
+  part = std::max(part, wgrad_part_bytes(p.L, p.C, p.hid));
+  part = std::max(part, wgrad_part_bytes(p.L, p.hid, p.C));
+  part = std::max(part, ln_bwd_part_bytes(p.L, p.C));
+  w.part = take(part);
+  w.attn = take(attention_bwd_workspace_bytes(attn_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, d->flags)));
+  w.msa_bytes = off;
+  w.zh = take(tok32);
+  w.n2 = take(tok);
+  w.a1 = take(hid);
+  w.h = take(hid);
+  w.dh = take(hid);
+  w.dzh = take(tok32);
+  w.block_bytes = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -423,6 +481,193 @@ vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const vo
   a.tab_ready = (desc->flags & VSWIN_F_TABLES_READY) ? 1 : 0;
   if (p.fast) HIPCHECK(attention_mfma(a, (hipStream_t)stream), "attention (mfma)");
   else HIPCHECK(attention_generic(p.dt, a, (hipStream_t)stream), "attention (generic)");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_bwd_workspace_query(const vswin_desc* desc, size_t* block_bytes, size_t* msa_bytes) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (!bwd_supported(p, desc))
+    return fail(VSWIN_ERR_UNSUPPORTED, "backward needs bf16, head_dim 32, C <= 768 and the MFMA attention with "
+                                       "group-uniform labels and the exclusion mask");
+  const BwdWs w = bwd_layout(p, desc);
+  if (block_bytes) *block_bytes = w.block_bytes;
+  if (msa_bytes) *msa_bytes = w.msa_bytes;
+  return VSWIN_OK;
+}
+
+namespace {
+
+// Shared part of the two backward entry points: forward recompute of the
+// attention branch from the window rows in w.n1w, then, given the window-row
+// gradient of the branch output in w.dyw, the gradients of proj, attention
+// (table), qkv and of the window rows (w.dn1w) scattered to token rows dxo.
+vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_weights* wt,
+                          const vswin_block_grads* g, char* ws, const BwdWs& w, void* dxo, hipStream_t st,
+                          const std::function<vswin_status()>& mid) {
+  const int C = p.C;
+  // qkv (q unscaled, V transposed for the MFMA attention)
+  EpiArgs e{};
+  e.kind = Epi::kQKV;
+  e.bias = wt->qkv_b;
+  e.out = ws + w.q; e.out2 = ws + w.k; e.out3 = ws + w.v;
+  e.C = C; e.heads = p.heads; e.d = p.d; e.N = p.N; e.geo = p.geo;
+  e.vt = 1;
+  HIPCHECK(gemm(p.dt, ws + w.n1w, wt->qkv_w, p.Lp, 3 * C, C, e, st), "bwd: qkv gemm");
+  AttnArgs a = attn_args(p, ws + w.q, ws + w.k, ws + w.v, wt->rpb_table, ws + w.o, d->flags, ws + w.tab);
+  a.lse = (float*)(ws + w.lse);
+  HIPCHECK(attention_mfma(a, st), "bwd: attention forward");
+  // the caller's middle part: everything between the attention output and
+  // the window-row gradient of the branch output (w.dyw)
+  CHECK(mid());
+  // projection
+  HIPCHECK(wgrad(ws + w.dyw, ws + w.o, g->proj_w, g->proj_b, (float*)(ws + w.part), p.Lp, C, C, st),
+           "bwd: proj weight gradient");
+  HIPCHECK(transpose_bf16(wt->proj_w, ws + w.wT, C, C, st), "bwd: transpose proj");
+  EpiArgs eb{};
+  eb.kind = Epi::kBias;
+  eb.out = ws + w.dout;
+  eb.ld_out = C;
+  HIPCHECK(gemm(p.dt, ws + w.dyw, ws + w.wT, p.Lp, C, C, eb, st), "bwd: proj input gradient");
+  // attention
+  AttnBwdArgs b{};
+  b.a = a;
+  b.dout = ws + w.dout;
+  b.lse = (const float*)(ws + w.lse);
+  b.dqkv = (bf16_t*)(ws + w.dqkv);
+  b.dtable = g->rpb_table;
+  b.work = ws + w.attn;
+  HIPCHECK(attention_bwd(b, st), "bwd: attention");
+  // qkv
+  HIPCHECK(wgrad(ws + w.dqkv, ws + w.n1w, g->qkv_w, g->qkv_b, (float*)(ws + w.part), p.Lp, 3 * C, C, st),
+           "bwd: qkv weight gradient");
+  HIPCHECK(transpose_bf16(wt->qkv_w, ws + w.wT, 3 * C, C, st), "bwd: transpose qkv");
+  eb.out = ws + w.dn1w;
+  HIPCHECK(gemm(p.dt, ws + w.dqkv, ws + w.wT, p.Lp, C, 3 * C, eb, st), "bwd: qkv input gradient");
+  HIPCHECK(reverse_scatter(p.dt, ws + w.dn1w, nullptr, dxo, p.Lp, C, p.geo, st), "bwd: window rows to tokens");
+  return VSWIN_OK;
+}
+
+vswin_status check_bwd_args(const Plan& p, const vswin_desc* desc, const void* x, const vswin_block_weights* w,
+                            const void* dy, const void* dx, const vswin_block_grads* g, const void* workspace,
+                            size_t workspace_bytes, size_t need) {
+  if (!bwd_supported(p, desc))
+    return fail(VSWIN_ERR_UNSUPPORTED, "backward needs bf16, head_dim 32, C <= 768 and the MFMA attention with "
+                                       "group-uniform labels and the exclusion mask");
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(dy, "dy"));
+  CHECK(check_ptr(dx, "dx"));
+  if (dx == x || dx == dy) return fail(VSWIN_ERR_INVALID_ARG, "dx must not alias x or dy");
+  CHECK(check_msa_weights(w));
+  if (!g) return fail(VSWIN_ERR_INVALID_ARG, "grads is NULL");
+  CHECK(check_ptr(g->qkv_w, "g.qkv_w"));
+  CHECK(check_ptr(g->qkv_b, "g.qkv_b", true));
+  CHECK(check_ptr(g->proj_w, "g.proj_w"));
+  CHECK(check_ptr(g->proj_b, "g.proj_b", true));
+  CHECK(check_ptr(g->rpb_table, "g.rpb_table"));
+  if (!workspace || !aligned(workspace, 256))
+    return fail(VSWIN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(VSWIN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  return VSWIN_OK;
+}
+
+}  // namespace
+
+vswin_status vswin_window_msa_bwd(const vswin_desc* desc, const void* x_norm, const vswin_block_weights* w,
+                                  const void* dy, void* dx_norm, const vswin_block_grads* g, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.L == 0) return VSWIN_OK;
+  const BwdWs L = bwd_layout(p, desc);
+  CHECK(check_bwd_args(p, desc, x_norm, w, dy, dx_norm, g, workspace, workspace_bytes, L.msa_bytes));
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  HIPCHECK(ln_gather(p.dt, x_norm, nullptr, nullptr, ws + L.n1w, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
+           "bwd: partition");
+  return msa_bwd_core(p, desc, w, g, ws, L, dx_norm, st, [&]() -> vswin_status {
+    HIPCHECK(ln_gather(p.dt, dy, nullptr, nullptr, ws + L.dyw, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
+             "bwd: partition of dy");
+    return VSWIN_OK;
+  });
+}
+
+vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w, const void* dy,
+                             void* dx, const vswin_block_grads* g, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.L == 0) return VSWIN_OK;
+  const BwdWs L = bwd_layout(p, desc);
+  CHECK(check_bwd_args(p, desc, x, w, dy, dx, g, workspace, workspace_bytes, L.block_bytes));
+  CHECK(check_ptr(w->ln1_g, "ln1_g"));
+  CHECK(check_ptr(w->ln1_b, "ln1_b"));
+  CHECK(check_ptr(w->ln2_g, "ln2_g"));
+  CHECK(check_ptr(w->ln2_b, "ln2_b"));
+  CHECK(check_ptr(w->fc1_w, "fc1_w"));
+  CHECK(check_ptr(w->fc1_b, "fc1_b", true));
+  CHECK(check_ptr(w->fc2_w, "fc2_w"));
+  CHECK(check_ptr(w->fc2_b, "fc2_b", true));
+  const float* req[] = {g->ln1_g, g->ln1_b, g->ln2_g, g->ln2_b, g->fc1_w, g->fc2_w};
+  const char* names[] = {"g.ln1_g", "g.ln1_b", "g.ln2_g", "g.ln2_b", "g.fc1_w", "g.fc2_w"};
+  for (int i = 0; i < 6; ++i) CHECK(check_ptr(req[i], names[i]));
+  CHECK(check_ptr(g->fc1_b, "g.fc1_b", true));
+  CHECK(check_ptr(g->fc2_b, "g.fc2_b", true));
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int C = p.C, hid = p.hid;
+  float* part = (float*)(ws + L.part);
+  // LN1 + pad + roll + partition of x
+  HIPCHECK(ln_gather(p.dt, x, w->ln1_g, w->ln1_b, ws + L.n1w, p.Lp, C, desc->ln_eps, p.geo, 1, st),
+           "bwd: ln1 gather");
+  auto mid = [&]() -> vswin_status {
+    // forward: z^ = x + proj(o) (fp32 token rows), LN2, fc1, GELU
+    EpiArgs e2{};
+    e2.kind = Epi::kProjRes;
+    e2.bias = w->proj_b;
+    e2.out = ws + L.zh;
+    e2.res = x;
+    e2.C = C; e2.heads = p.heads; e2.d = p.d; e2.N = p.N; e2.geo = p.geo;
+    HIPCHECK(gemm(p.dt, ws + L.o, w->proj_w, p.Lp, C, C, e2, st), "bwd: proj forward");
+    HIPCHECK(ln_rows(VSWIN_FP32, p.dt, ws + L.zh, w->ln2_g, w->ln2_b, ws + L.n2, p.L, C, desc->ln_eps, st),
+             "bwd: ln2 forward");
+    EpiArgs e{};
+    e.kind = Epi::kBias;
+    e.bias = w->fc1_b;
+    e.out = ws + L.a1;
+    e.ld_out = hid;
+    HIPCHECK(gemm(p.dt, ws + L.n2, w->fc1_w, p.L, hid, C, e, st), "bwd: fc1 forward");
+    HIPCHECK(gelu_apply(ws + L.a1, ws + L.h, p.L * hid, 0, st), "bwd: gelu forward");
+    // fc2
+    HIPCHECK(wgrad(dy, ws + L.h, g->fc2_w, g->fc2_b, part, p.L, C, hid, st), "bwd: fc2 weight gradient");
+    HIPCHECK(transpose_bf16(w->fc2_w, ws + L.wT, C, hid, st), "bwd: transpose fc2");
+    EpiArgs eb{};
+    eb.kind = Epi::kBias;
+    eb.out = ws + L.dh;
+    eb.ld_out = hid;
+    HIPCHECK(gemm(p.dt, dy, ws + L.wT, p.L, hid, C, eb, st), "bwd: fc2 input gradient");
+    HIPCHECK(gelu_apply(ws + L.a1, ws + L.dh, p.L * hid, 1, st), "bwd: gelu backward");
+    // fc1
+    HIPCHECK(wgrad(ws + L.dh, ws + L.n2, g->fc1_w, g->fc1_b, part, p.L, hid, C, st), "bwd: fc1 weight gradient");
+    HIPCHECK(transpose_bf16(w->fc1_w, ws + L.wT, hid, C, st), "bwd: transpose fc1");
+    eb.out = ws + L.dn1;   // dLN2 output, token rows (the buffer is reused for dLN1 later)
+    eb.ld_out = C;
+    HIPCHECK(gemm(p.dt, ws + L.dh, ws + L.wT, p.L, C, hid, eb, st), "bwd: fc1 input gradient");
+    // LN2 (+ the residual path of y = z^ + ...)
+    HIPCHECK(ln_bwd(1, ws + L.zh, w->ln2_g, ws + L.dn1, 0, dy, 1, ws + L.dzh, part, g->ln2_g, g->ln2_b, p.L, C,
+                    desc->ln_eps, st),
+             "bwd: ln2 backward");
+    HIPCHECK(gather_f32_bf16((const float*)(ws + L.dzh), ws + L.dyw, p.Lp, C, p.geo, st), "bwd: gather dz");
+    return VSWIN_OK;
+  };
+  CHECK(msa_bwd_core(p, desc, w, g, ws, L, ws + L.dn1, st, mid));
+  // LN1 (+ the residual path of z^ = x + ...)
+  HIPCHECK(ln_bwd(0, x, w->ln1_g, ws + L.dn1, 1, ws + L.dzh, 0, dx, part, g->ln1_g, g->ln1_b, p.L, C, desc->ln_eps,
+                  st),
+           "bwd: ln1 backward");
   return VSWIN_OK;
 }
 

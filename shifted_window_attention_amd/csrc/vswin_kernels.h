@@ -88,6 +88,8 @@ struct AttnArgs {
   int q_scaled;            // MFMA kernel: q already multiplied by log2(e) / sqrt(d)
   void* tab4;              // MFMA kernel: workspace of attention_workspace_bytes for the prepared tables
   int tab_ready;           // MFMA kernel: tab4 already holds this call's tables
+  float* lse;              // MFMA kernel, nullable: (nW*heads, N) log2 of each query row's sum of
+                           // exp2 of its log2-domain logits (the backward's normaliser)
 };
 // bytes of workspace the MFMA kernel needs for its prepared bias tables
 // (heads * TS4 fp32 4-tuples) and their extents
@@ -103,6 +105,29 @@ constexpr int kMfmaMaxN = 512;
 constexpr int kMfmaBigN = 1024;
 bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a);
 
+// Backward of the MFMA attention (bf16, d = 32, group-uniform region labels,
+// exclusion mask).  In: a.q (q * log2(e) / sqrt(d)), a.k, a.v (V^T), a.o,
+// a.table as the forward had them, dout (window rows), lse (the forward's
+// a.lse output).  Out: dqkv rows (nW*N, 3C) = [dq | dk | dv] for the
+// unscaled q, k, v; dtable (rows, heads) fp32.  work: attention_bwd_workspace_bytes.
+struct AttnBwdArgs {
+  AttnArgs a;
+  const void* dout;
+  const float* lse;
+  bf16_t* dqkv;
+  float* dtable;
+  void* work;
+  // set by attention_bwd inside `work`
+  bf16_t *qr, *kr, *vr, *dor;   // padded rows (items, NPAD, 32)
+  bf16_t *qt, *kt, *dot;        // transposes (items, 32, NPAD), pair order per 32-row block
+  float* D;                     // (items, NPAD) row sums of dout * o
+  float* dtab;                  // (heads, TD * Rp) scalar-form table gradient
+  float dq_scale, dk_scale;
+};
+bool attention_bwd_supported(vswin_dtype dt, const AttnArgs& a);
+size_t attention_bwd_workspace_bytes(const AttnArgs& a);
+hipError_t attention_bwd(const AttnBwdArgs& b, hipStream_t st);
+
 // --- fused LN2 -> fc1 -> GELU -> fc2 -> residual (k_mlp.hip) --------------
 // proj_mlp (bf16, C = 96, hid = 4C): the output projection in front as well,
 // y = z^ + MLP(LN2(z^)), z^ = x + o Wp^T + bp with o the attention output in
@@ -114,6 +139,25 @@ hipError_t proj_mlp(const void* o, const void* x, const void* wp, const void* bp
 bool mlp_fused_supported(vswin_dtype dt, int C, int hid);
 hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const void* W1, const void* b1,
                      const void* W2, const void* bo, void* y, int64_t L, int C, float eps, hipStream_t st);
+
+// --- backward pieces (k_backward.hip) --------------------------------------
+// dst (C x R) = src (R x C)^T, bf16
+hipError_t transpose_bf16(const void* src, void* dst, int R, int C, hipStream_t st);
+// bwd = 0: io = GELU(a); bwd = 1: io = io * GELU'(a)  (bf16, n % 8 == 0)
+hipError_t gelu_apply(const void* a, void* io, int64_t n, int bwd, hipStream_t st);
+// bf16 window rows of an fp32 token-row tensor, zeros for pad slots
+hipError_t gather_f32_bf16(const float* in, void* out, int64_t slots, int C, const WinGeo& geo, hipStream_t st);
+// LayerNorm backward over rows of C (<= 768): out = dLN(x; g)/dx applied to dy, plus res (nullable);
+// dg, db (fp32, C) from per-wave partials in part (ln_bwd_part_bytes)
+size_t ln_bwd_part_bytes(int64_t rows, int C);
+hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int res_fp32, const void* res,
+                  int out_fp32, void* out, float* part, float* dg, float* db, int64_t rows, int C, float eps,
+                  hipStream_t st);
+// dW (NO x KI) = A^T B and db (NO, nullable) = column sums of A over M token rows,
+// A (M x NO), B (M x KI) bf16; fp32 outputs; part: wgrad_part_bytes
+size_t wgrad_part_bytes(int64_t M, int NO, int KI);
+hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
+                 hipStream_t st);
 
 // --- measurement helper (k_probe.hip) --------------------------------------
 // blocks x 512 threads of v_mfma_f32_16x16x32_bf16 chains: 8 per wave per
