@@ -846,7 +846,8 @@ struct BwdL {
   A5 L;                       // geometry, table extents, scalar table form
   int pitch;                  // transposed LDS rows: 16-byte chunks, 4 mod 16
   // kernel A LDS
-  uint32_t a_q, a_do, a_qt, a_dot, a_lse, a_D, a_dtab, a_lds;
+  uint32_t a_q, a_do, a_qt, a_dot, a_lse, a_D, a_lds;
+  int ap, mhw;                // temporal groups per window (P / 4), spatial cells (Mh * Mw)
   // kernel B LDS
   uint32_t b_k, b_v, b_kt, b_lds;
 };
@@ -880,6 +881,16 @@ __device__ __forceinline__ void stage_f32(const float* src, unsigned char* dst, 
   for (int b = wv; b * 64 < nc; b += nw)
     if (64 * b + lane < nc)
       __builtin_amdgcn_global_load_lds(src + 4 * (64 * b + lane), (lds_ptr_t)(dst + 1024 * b), 16, 0, 0);
+}
+
+// a lane's value from the lane its quad permutation selects (DPP quad_perm:
+// 0xB1 swaps neighbours, 0x4E swaps pairs)
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor(float v, int ctrl) {
+  return ctrl == 0xB1 ? quad_perm<0xB1>(v) : quad_perm<0x4E>(v);
 }
 
 __device__ __forceinline__ bf16x8_t pack8f(const float* v) {
@@ -981,13 +992,11 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
   const Win wi = window_of(b.a, L, blockIdx.x);
   const int mem = wi.mem, h = wi.h;
   const int N = L.N, NPAD = L.NPAD, Rp = L.Rp;
-  const int nd = L.TD * Rp;
+  const int ng = N / 4;   // key / query groups of 4 temporal positions
   int* kp = reinterpret_cast<int*>(smem + L.off_kp);
   const int* lp = reinterpret_cast<const int*>(smem + L.off_lp);
-  float* dtab = reinterpret_cast<float*>(smem + BL.a_dtab);
   stage_offsets<CF>(b.a, L, kp);
   stage_labels<CF>(b.a, L, wi, smem);
-  for (int i = (int)threadIdx.x; i < nd; i += CF::kThreads) dtab[i] = 0.f;
   stage_rows16(b.qr + (int64_t)mem * NPAD * 32, smem + BL.a_q, NPAD, wv, CF::kWaves);
   stage_rows16(b.dor + (int64_t)mem * NPAD * 32, smem + BL.a_do, NPAD, wv, CF::kWaves);
   stage_trows(b.qt + (int64_t)mem * 32 * NPAD, smem + BL.a_qt, NPAD, BL.pitch, wv, CF::kWaves);
@@ -1030,15 +1039,42 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
         const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse + qs0 + 4 * g4);
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(Dl + qs0 + 4 * g4);
+        float dsl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool valid = kval && qs0 + 4 * g4 + i < N && qlab == klab;
           const float P = valid ? __builtin_amdgcn_exp2f(s2[i] - l4[i]) : 0.f;
           const float ds = P * (dp[i] - d4[i]);
-          if (valid) atomicAdd(dtab + (base - (int)L.off_tab) / ES - i * Rp, ds);
           pv[4 * s + i] = P;
           dsv[4 * s + i] = ds;
+          dsl[i] = ds;
         }
+        // dS toward the table gradient.  The 4 lanes of a key group (kk =
+        // fr & 3, one quad) hold the 16 pairs of one (query group, key group);
+        // pair (kk, i) belongs to the table entry of temporal diagonal kk - i,
+        // so the quad forms the 7 diagonal sums (DPP within the quad) and
+        // stores them, each (query group, key group) once, for
+        // attn_bwd_grp_sum / attn_bwd_dtab_gather: no atomics.
+        const int kk = fr & 3;
+        float mine0 = 0.f, mine1 = 0.f;
+#pragma unroll
+        for (int dd = -3; dd <= 3; ++dd) {
+          const int i = kk - dd;
+          float v = i == 0 ? dsl[0] : i == 1 ? dsl[1] : i == 2 ? dsl[2] : i == 3 ? dsl[3] : 0.f;
+          v += quad_xor(v, 0xB1);
+          v += quad_xor(v, 0x4E);
+          if (dd == kk - 3) mine0 = v;
+          if (dd == kk + 1) mine1 = v;
+        }
+        const int mq = (qs0 >> 2) + g4, mk = 4 * kt + (fr >> 2);
+        if (mq < ng && mk < ng) {
+          const int aq = (int)fdiv((uint32_t)mq, b.a.geo.fmhw), ak = (int)fdiv((uint32_t)mk, b.a.geo.fmhw);
+          float* dp7 = b.dgrp + (((int64_t)mem * BL.ap * BL.ap + aq * BL.ap + ak) * BL.mhw + (mq - aq * BL.mhw)) *
+                                    BL.mhw * 7 + (mk - ak * BL.mhw) * 7;
+          dp7[kk] = mine0;
+          if (kk < 3) dp7[kk + 4] = mine1;
+        }
+        (void)base;
       }
       const bf16x8_t pb = pack8f(pv), db = pack8f(dsv);
       const int ch = qb / 8 + g4;
@@ -1065,12 +1101,6 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
       *reinterpret_cast<u32x2_t*>(row + C + 16) =
           u32x2_t{pack_bf16x2(dk1[0] * ks, dk1[1] * ks), pack_bf16x2(dk1[2] * ks, dk1[3] * ks)};
     }
-  }
-  __syncthreads();
-  float* gt = b.dtab + (int64_t)h * nd;
-  for (int i = (int)threadIdx.x; i < nd; i += CF::kThreads) {
-    const float v = dtab[i];
-    if (v != 0.f) atomicAdd(gt + i, v);
   }
 }
 
@@ -1150,6 +1180,59 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
   }
 }
 
+// Sum of the stored diagonal sums over the windows of each head: gsum[h][e]
+// = sum_w dgrp[(w heads + h) E + e], E = (P/4)^2 (Mh Mw)^2 7 (coalesced:
+// consecutive threads take consecutive e).
+__global__ void __launch_bounds__(256) attn_bwd_grp_sum_kernel(const float* __restrict__ dgrp,
+                                                                float* __restrict__ gsum, int64_t nW, int heads,
+                                                                int64_t E) {
+  const int h = blockIdx.y;
+  const int64_t e = blockIdx.x * 256 + (int64_t)threadIdx.x;
+  if (e >= E) return;
+  float s = 0.f;
+  for (int64_t w = 0; w < nW; ++w) s += dgrp[(w * heads + h) * E + e];
+  gsum[(int64_t)h * E + e] = s;
+}
+
+// Table gradient in the scalar index space: entry y = (dt + TD/2) Rp +
+// (dh + TH/2) Rw + (dw + Rw/2) of head h gathers, from the window sums, the
+// diagonal sums of every (query group, key group) pair whose spatial cells
+// differ by (dh, dw) and whose temporal groups and diagonal give
+// dt = 4 (ak - aq) + dd.  One wave per entry, lanes over the query cells;
+// deterministic (no atomics).
+__global__ void __launch_bounds__(256) attn_bwd_dtab_gather_kernel(const float* __restrict__ gsum,
+                                                                    float* __restrict__ dtab, const BwdL BL,
+                                                                    WinGeo g) {
+  const A5& L = BL.L;
+  const int h = blockIdx.y;
+  const int nd = L.TD * L.Rp;
+  const int y = blockIdx.x * 4 + ((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (y >= nd) return;
+  const int u = y / L.Rp, rem = y - u * L.Rp;
+  const int v = rem / L.Rw, x = rem - v * L.Rw;
+  const int64_t E = (int64_t)BL.ap * BL.ap * BL.mhw * BL.mhw * 7;
+  const float* gs = gsum + (int64_t)h * E;
+  float s = 0.f;
+  if (rem < L.R) {
+    const int dt = u - L.TD / 2, dh = v - L.TH / 2, dw = x - L.Rw / 2;
+    for (int cq = lane; cq < BL.mhw; cq += 64) {
+      const int qh = cq / g.Mw, qw = cq - qh * g.Mw;
+      const int kh = qh + dh, kw = qw + dw;
+      if (kh < 0 || kh >= g.Mh || kw < 0 || kw >= g.Mw) continue;
+      const int ck = kh * g.Mw + kw;
+      for (int aq = 0; aq < BL.ap; ++aq)
+        for (int ak = 0; ak < BL.ap; ++ak) {
+          const int dd = dt - 4 * (ak - aq);
+          if (dd >= -3 && dd <= 3) s += gs[(((int64_t)(aq * BL.ap + ak) * BL.mhw + cq) * BL.mhw + ck) * 7 + dd + 3];
+        }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) dtab[(int64_t)h * nd + y] = s;
+}
+
 // table-row layout of the accumulated scalar-form gradient (the inverse of
 // ts_entry's index map); every row has exactly one scalar index
 __global__ void __launch_bounds__(256) attn_bwd_dtab_kernel(const float* __restrict__ dtab, float* __restrict__ out,
@@ -1162,10 +1245,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dtab_kernel(const float* __restr
   const int dhr = tg.TH - 1 - rem / tg.Rw;
   const int dwr = tg.Rw - 1 - (rem - (rem / tg.Rw) * tg.Rw);
   out[x] = dtab[(size_t)h * tg.TD * tg.Rp + dtr * tg.Rp + dhr * tg.Rw + dwr];
-}
-
-__global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, int64_t n) {
-  for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
 namespace {
@@ -1197,8 +1276,9 @@ bool plan_bwd(const AttnArgs& a, BwdL& B) {
   B.a_dot = take(trows);
   B.a_lse = take((size_t)L.NPAD * 4);
   B.a_D = take((size_t)L.NPAD * 4);
-  B.a_dtab = take((size_t)L.TD * L.Rp * 4);
   B.a_lds = (uint32_t)off;
+  B.ap = a.geo.P / 4;
+  B.mhw = a.geo.Mh * a.geo.Mw;
   off = common;
   B.b_k = take(rows);
   B.b_v = take(rows);
@@ -1225,7 +1305,9 @@ size_t attention_bwd_workspace_bytes(const AttnArgs& a) {
   const size_t D = ((size_t)items * L.NPAD * 4 + 255) & ~(size_t)255;
   const size_t tabs = ((size_t)a.heads * L.TS4 * 16 + 255) & ~(size_t)255;
   const size_t dtab = ((size_t)a.heads * L.TD * L.Rp * 4 + 255) & ~(size_t)255;
-  return 7 * arr + D + tabs + dtab;
+  const size_t grp = ((size_t)items * B.ap * B.ap * B.mhw * B.mhw * 7 * 4 + 255) & ~(size_t)255;
+  const size_t gsum = ((size_t)a.heads * B.ap * B.ap * B.mhw * B.mhw * 7 * 4 + 255) & ~(size_t)255;
+  return 7 * arr + D + tabs + dtab + grp + gsum;
 }
 
 hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
@@ -1244,12 +1326,13 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
   b.a.tab4 = w + off;
   off += ((size_t)in.a.heads * L.TS4 * 16 + 255) & ~(size_t)255;
   b.dtab = reinterpret_cast<float*>(w + off);
+  off += ((size_t)in.a.heads * L.TD * L.Rp * 4 + 255) & ~(size_t)255;
+  b.dgrp = reinterpret_cast<float*>(w + off);
+  off += ((size_t)items * B.ap * B.ap * B.mhw * B.mhw * 7 * 4 + 255) & ~(size_t)255;
+  float* gsum = reinterpret_cast<float*>(w + off);
   b.dq_scale = 1.0f / sqrtf((float)in.a.d);
   b.dk_scale = 1.0f / kLog2e;
   if (items <= 0) return hipSuccess;
-  const int64_t nd = (int64_t)in.a.heads * L.TD * L.Rp;
-  zero_f32_kernel<<<dim3((unsigned)((nd + 255) / 256 < 1024 ? (nd + 255) / 256 : 1024)), dim3(256), 0, st>>>(b.dtab,
-                                                                                                          nd);
   attn_table_kernel<<<dim3((unsigned)((L.TS4 + 255) / 256), (unsigned)L.heads), dim3(256), 0, st>>>(
       reinterpret_cast<const bf16_t*>(in.a.table), reinterpret_cast<f32x4_t*>(b.a.tab4), L);
   attn_bwd_prep_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(b, B);
@@ -1259,6 +1342,12 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
   if (e != hipSuccess) return e;
   attn_bwd_kv_kernel<<<dim3((unsigned)items), dim3(512), B.a_lds, st>>>(b, B);
   attn_bwd_q_kernel<<<dim3((unsigned)items), dim3(512), B.b_lds, st>>>(b, B);
+  const int64_t E = (int64_t)B.ap * B.ap * B.mhw * B.mhw * 7;
+  attn_bwd_grp_sum_kernel<<<dim3((unsigned)((E + 255) / 256), (unsigned)in.a.heads), dim3(256), 0, st>>>(
+      b.dgrp, gsum, in.a.nW, in.a.heads, E);
+  const int nd = L.TD * L.Rp;
+  attn_bwd_dtab_gather_kernel<<<dim3((unsigned)((nd + 3) / 4), (unsigned)in.a.heads), dim3(256), 0, st>>>(
+      gsum, b.dtab, B, in.a.geo);
   const int rows = in.a.rel.rows;
   attn_bwd_dtab_kernel<<<dim3((unsigned)((rows * in.a.heads + 255) / 256)), dim3(256), 0, st>>>(b.dtab, in.dtable,
                                                                                                L.tg, rows);

@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kWgChunk = 256;     // tokens per staged chunk
 constexpr int kWgPitch = 264;     // LDS row pitch (bf16) of the token-contiguous operands
-constexpr int kMaxParts = 128;    // fp32 partials of one weight gradient at most
+constexpr int kMaxParts = 64;     // fp32 partials of one weight gradient at most
 
 __device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float gelu_d(float x) {
@@ -182,94 +182,91 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
 // Weight-gradient partials: part[p] (NO x KI) = sum over the tokens of
 // chunks p, p + P, ... of A[m, n] * B[m, k]; colp[p] (NO) = sum of A[m, n]
 // (written by the k-block-0 workgroups).  A: (M, NO), B: (M, KI), bf16 rows.
-// Workgroup tile 32 n x BK k, 4 waves, each wave BK / 32 of the 16 x 16
-// output tiles; MFMA A operand = A^T rows (n) and B operand = B^T rows (k),
-// both token-contiguous in LDS.
-template <int BK>
+// Workgroup tile BN n x BK k, 4 waves sharing the (BN/16) (BK/16) output
+// tiles; MFMA A operand = A^T rows (n) and B operand = B^T rows (k), both
+// token-contiguous in LDS.  Larger tiles re-read the operands fewer times.
+template <int BN, int BK>
 __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
                                                     float* __restrict__ part, float* __restrict__ colp, int64_t M,
                                                     int NO, int KI, int nparts) {
-  __shared__ __attribute__((aligned(16))) bf16_t At[32 * kWgPitch];
-  __shared__ __attribute__((aligned(16))) bf16_t Bt[BK * kWgPitch];
-  const int nblk = NO / 32, kblk = (KI + BK - 1) / BK;
+  extern __shared__ __attribute__((aligned(16))) unsigned char wg_lds[];
+  bf16_t* At = reinterpret_cast<bf16_t*>(wg_lds);
+  bf16_t* Bt = At + BN * kWgPitch;
+  const int nblk = NO / BN, kblk = KI / BK;
   int bid = blockIdx.x;
   const int p = bid / (nblk * kblk);
   bid -= p * nblk * kblk;
   const int nb = bid / kblk, kb = bid - nb * kblk;
-  const int n0 = nb * 32, k0 = kb * BK;
+  const int n0 = nb * BN, k0 = kb * BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g4 = lane >> 4;
-  constexpr int TPW = BK / 32;   // output tiles per wave
+  constexpr int NT = (BN / 16) * (BK / 16);
+  static_assert(NT % 4 == 0, "output tiles split over 4 waves");
+  constexpr int TPW = NT / 4;
+  constexpr int CSG = BN <= 32 ? 8 : (BN <= 64 ? 4 : 2);   // threads per column of the bias sums
+  static_assert(BN * CSG <= 256, "column-sum threads");
   f32x4_t acc[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float cs = 0.f;
   const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
   for (int64_t ch = p; ch < nchunks; ch += nparts) {
-    const int64_t m0 = ch * kWgChunk;
+    const int64_t m = ch * kWgChunk + tid;
     __syncthreads();
-    // A^T: 256 tokens x 32 n: thread -> token tid, 4 chunks of 8 n
-    {
-      const int64_t m = m0 + tid;
+    // thread -> token tid: BN / 8 chunks of A, BK / 8 of B, transposed into LDS
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (m < M) v = *reinterpret_cast<const u32x4_t*>(A + m * NO + n0 + 8 * c);
+    for (int c = 0; c < BN / 8; ++c) {
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (m < M) v = *reinterpret_cast<const u32x4_t*>(A + m * NO + n0 + 8 * c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          At[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
-          At[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
-        }
+      for (int e = 0; e < 4; ++e) {
+        At[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
+        At[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
       }
-      // B^T: 256 tokens x BK k
+    }
 #pragma unroll
-      for (int c = 0; c < BK / 8; ++c) {
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (m < M && k0 + 8 * c < KI) v = *reinterpret_cast<const u32x4_t*>(B + m * KI + k0 + 8 * c);
+    for (int c = 0; c < BK / 8; ++c) {
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (m < M) v = *reinterpret_cast<const u32x4_t*>(B + m * KI + k0 + 8 * c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Bt[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
-          Bt[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
-        }
+      for (int e = 0; e < 4; ++e) {
+        Bt[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
+        Bt[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
       }
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int tile = wave * TPW + i;            // 0 .. 2 * BK / 16 - 1
-      const int nh = tile & 1, kq = tile >> 1;
+      const int tile = wave * TPW + i;
+      const int nt = tile % (BN / 16), kt = tile / (BN / 16);
 #pragma unroll 4
       for (int s = 0; s < kWgChunk / 32; ++s) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(At + (16 * nh + fr) * kWgPitch + 32 * s + 8 * g4);
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(Bt + (16 * kq + fr) * kWgPitch + 32 * s + 8 * g4);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(At + (16 * nt + fr) * kWgPitch + 32 * s + 8 * g4);
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(Bt + (16 * kt + fr) * kWgPitch + 32 * s + 8 * g4);
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
       }
     }
-    if (kb == 0) {
-      // column sums: thread -> n = tid / 8, tokens 32 (tid % 8) .. + 31
-      const int n = tid >> 3, q = tid & 7;
-      float s = 0.f;
-      for (int t = 0; t < 32; ++t) s += bf2f(At[n * kWgPitch + 32 * q + t]);
-      cs += s;
+    if (kb == 0 && tid < BN * CSG) {
+      // column sums: thread -> n = tid / CSG, tokens (tid % CSG) * 256 / CSG ..
+      const int n = tid / CSG, q = tid % CSG;
+      float sm = 0.f;
+      for (int t = 0; t < kWgChunk / CSG; ++t) sm += bf2f(At[n * kWgPitch + q * (kWgChunk / CSG) + t]);
+      cs += sm;
     }
   }
-  // lane: n = n0 + 16 nh + 4 g4 + r, k = k0 + 16 kq + fr
+  // lane: n = n0 + 16 nt + 4 g4 + r, k = k0 + 16 kt + fr
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int tile = wave * TPW + i;
-    const int nh = tile & 1, kq = tile >> 1;
-    const int k = k0 + 16 * kq + fr;
-    if (k < KI) {
+    const int nt = tile % (BN / 16), kt = tile / (BN / 16);
+    const int k = k0 + 16 * kt + fr;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        part[((int64_t)p * NO + n0 + 16 * nh + 4 * g4 + r) * KI + k] = acc[i][r];
-    }
+    for (int r = 0; r < 4; ++r) part[((int64_t)p * NO + n0 + 16 * nt + 4 * g4 + r) * KI + k] = acc[i][r];
   }
   if (kb == 0) {
-    cs += __shfl_xor(cs, 1);
-    cs += __shfl_xor(cs, 2);
-    cs += __shfl_xor(cs, 4);
-    if ((tid & 7) == 0) colp[(int64_t)p * NO + n0 + (tid >> 3)] = cs;
+#pragma unroll
+    for (int o = 1; o < CSG; o <<= 1) cs += __shfl_xor(cs, o);
+    if (tid % CSG == 0 && tid < BN * CSG) colp[(int64_t)p * NO + n0 + tid / CSG] = cs;
   }
 }
 
@@ -281,6 +278,22 @@ __global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restri
     for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * stride + i];
     out[i] = s;
   }
+}
+
+// out[i] = sum_p part[p * stride + i], one workgroup per output (many partials)
+__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                          int nparts, int64_t stride) {
+  __shared__ float red[256];
+  const int64_t i = blockIdx.x;
+  float s = 0.f;
+  for (int p = (int)threadIdx.x; p < nparts; p += 256) s += part[(int64_t)p * stride + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[i] = red[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -315,7 +328,7 @@ hipError_t gather_f32_bf16(const float* in, void* out, int64_t slots, int C, con
 }
 
 int ln_bwd_waves(int64_t rows) {
-  const int64_t g = rows < 4096 ? rows : 4096;
+  const int64_t g = rows < 8192 ? rows : 8192;
   return (int)(((g + 3) / 4) * 4);
 }
 
@@ -344,8 +357,8 @@ hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dg = sum over waves of part[w][0:C], db of part[w][C:2C]
-  reduce_parts_kernel<<<dim3(grid_for(C, 256)), dim3(256), 0, st>>>(part, dg, nw, C, 2 * C);
-  reduce_parts_kernel<<<dim3(grid_for(C, 256)), dim3(256), 0, st>>>(part + C, db, nw, C, 2 * C);
+  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part, dg, nw, 2 * C);
+  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part + C, db, nw, 2 * C);
   return hipGetLastError();
 }
 
@@ -367,21 +380,28 @@ hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part
   const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
   const int np = (int)(nchunks < kMaxParts ? nchunks : kMaxParts);
   float* colp = part + (size_t)np * NO * KI;
-  const int nblk = NO / 32;
-  auto go = [&](auto kern, int bk) {
-    const int kblk = (KI + bk - 1) / bk;
-    kern<<<dim3((unsigned)(np * nblk * kblk)), dim3(256), 0, st>>>((const bf16_t*)A, (const bf16_t*)B, part, colp, M,
-                                                                   NO, KI, np);
+  // n tile 96 where it divides NO, else 32; k tile 96 or 128 where it divides
+  // KI, else 32
+  auto launch = [&](auto kern, int bn, int bk) -> hipError_t {
+    const size_t lds = (size_t)(bn + bk) * kWgPitch * 2;
+    hipError_t e = ensure_dynamic_lds((const void*)kern, lds);
+    if (e != hipSuccess) return e;
+    kern<<<dim3((unsigned)(np * (NO / bn) * (KI / bk))), dim3(256), lds, st>>>((const bf16_t*)A, (const bf16_t*)B,
+                                                                             part, colp, M, NO, KI, np);
+    return hipGetLastError();
   };
-  if (KI % 128 == 0) go(wgrad_kernel<128>, 128);
-  else if (KI % 96 == 0) go(wgrad_kernel<96>, 96);
-  else if (KI % 64 == 0) go(wgrad_kernel<64>, 64);
-  else go(wgrad_kernel<32>, 32);
+  hipError_t e0;
+  if (NO % 96 == 0 && KI % 96 == 0) e0 = launch(wgrad_kernel<96, 96>, 96, 96);
+  else if (NO % 96 == 0 && KI % 128 == 0) e0 = launch(wgrad_kernel<96, 128>, 96, 128);
+  else if (NO % 32 == 0 && KI % 128 == 0) e0 = launch(wgrad_kernel<32, 128>, 32, 128);
+  else if (NO % 32 == 0 && KI % 96 == 0) e0 = launch(wgrad_kernel<32, 96>, 32, 96);
+  else e0 = launch(wgrad_kernel<32, 32>, 32, 32);
+  if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   reduce_parts_kernel<<<dim3(grid_for((int64_t)NO * KI, 256)), dim3(256), 0, st>>>(part, dW, np, (int64_t)NO * KI,
                                                                                    (int64_t)NO * KI);
-  if (db) reduce_parts_kernel<<<dim3(grid_for(NO, 256)), dim3(256), 0, st>>>(colp, db, np, NO, NO);
+  if (db) reduce_rows_kernel<<<dim3((unsigned)NO), dim3(256), 0, st>>>(colp, db, np, NO);
   return hipGetLastError();
 }
 

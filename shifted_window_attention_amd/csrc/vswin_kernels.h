@@ -122,6 +122,7 @@ struct AttnBwdArgs {
   bf16_t *qt, *kt, *dot;        // transposes (items, 32, NPAD), pair order per 32-row block
   float* D;                     // (items, NPAD) row sums of dout * o
   float* dtab;                  // (heads, TD * Rp) scalar-form table gradient
+  float* dgrp;                  // per (item, query group, key group): 7 temporal-diagonal sums of dS
   float dq_scale, dk_scale;
 };
 bool attention_bwd_supported(vswin_dtype dt, const AttnArgs& a);
