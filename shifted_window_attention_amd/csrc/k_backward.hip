@@ -16,6 +16,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace vswin {
 
 namespace {
@@ -99,50 +101,51 @@ __global__ void __launch_bounds__(256) gather_f32_bf16_kernel(const float* __res
   }
 }
 
-// LayerNorm backward, one wave per row, C <= 64 * kLnJ.  x: TX (fp32 / bf16),
-// dy: bf16, res (nullable): TR added to dx, out: TO.  part: per wave, dg then db (2C).
-constexpr int kLnJ = 12;
-template <typename TX, typename TR, typename TO>
+// LayerNorm backward, LPR lanes per row (64 / LPR rows per wave in flight),
+// C <= LPR * J.  x: TX (fp32 / bf16), dy: bf16, res (nullable): TR added to
+// dx, out: TO.  part: per workgroup, dg then db (2C), the row groups' sums
+// combined in LDS.
+template <typename TX, typename TR, typename TO, int LPR, int J>
 __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, const bf16_t* __restrict__ g,
                                                      const bf16_t* __restrict__ dy, const TR* __restrict__ res,
                                                      TO* __restrict__ out, float* __restrict__ part, int64_t rows,
                                                      int C, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = blockIdx.x * 4 + (threadIdx.x >> 6), nw = (int64_t)gridDim.x * 4;
-  float dgs[kLnJ], dbs[kLnJ], gv[kLnJ];
+  const int l16 = threadIdx.x % LPR;
+  const int64_t grp = blockIdx.x * (256 / LPR) + threadIdx.x / LPR, ng = (int64_t)gridDim.x * (256 / LPR);
+  float dgs[J], dbs[J], gv[J];
 #pragma unroll
-  for (int j = 0; j < kLnJ; ++j) {
+  for (int j = 0; j < J; ++j) {
     dgs[j] = dbs[j] = 0.f;
-    const int c = lane + 64 * j;
+    const int c = l16 + LPR * j;
     gv[j] = c < C ? bf2f(g[c]) : 0.f;
   }
   const float invC = 1.0f / C;
-  for (int64_t r = wave; r < rows; r += nw) {
-    float xv[kLnJ], dv[kLnJ];
+  for (int64_t r = grp; r < rows; r += ng) {
+    float xv[J], dv[J];
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < kLnJ; ++j) {
-      const int c = lane + 64 * j;
+    for (int j = 0; j < J; ++j) {
+      const int c = l16 + LPR * j;
       xv[j] = c < C ? Elem<TX>::load(x, r * C + c) : 0.f;
       dv[j] = c < C ? bf2f(dy[r * C + c]) : 0.f;
       s += xv[j];
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     const float mu = s * invC;
     float q = 0.f;
 #pragma unroll
-    for (int j = 0; j < kLnJ; ++j) {
-      const int c = lane + 64 * j;
+    for (int j = 0; j < J; ++j) {
+      const int c = l16 + LPR * j;
       const float d = c < C ? xv[j] - mu : 0.f;
       q += d * d;
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
+    for (int o = LPR / 2; o >= 1; o >>= 1) q += __shfl_xor(q, o);
     const float rstd = 1.0f / sqrtf(q * invC + eps);
     float a = 0.f, bsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kLnJ; ++j) {
+    for (int j = 0; j < J; ++j) {
       const float xh = (xv[j] - mu) * rstd;
       const float dxh = dv[j] * gv[j];
       a += dxh;
@@ -153,15 +156,15 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
       dv[j] = dxh;
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
+    for (int o = LPR / 2; o >= 1; o >>= 1) {
       a += __shfl_xor(a, o);
       bsum += __shfl_xor(bsum, o);
     }
     a *= invC;
     bsum *= invC;
 #pragma unroll
-    for (int j = 0; j < kLnJ; ++j) {
-      const int c = lane + 64 * j;
+    for (int j = 0; j < J; ++j) {
+      const int c = l16 + LPR * j;
       if (c < C) {
         float v = rstd * (dv[j] - a - xv[j] * bsum);
         if (res) v += Elem<TR>::load(res, r * C + c);
@@ -169,14 +172,27 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
       }
     }
   }
+  // the workgroup's row groups into one partial (LDS, at most 2 x 768 floats
+  // per pass of 256 / LPR groups)
+  __shared__ float red[2 * 768];
+  constexpr int G = 256 / LPR;
+  const int gi = threadIdx.x / LPR;
+  for (int i = threadIdx.x; i < 2 * C; i += 256) red[i] = 0.f;
+  __syncthreads();
+  for (int k = 0; k < G; ++k) {
+    if (gi == k) {
 #pragma unroll
-  for (int j = 0; j < kLnJ; ++j) {
-    const int c = lane + 64 * j;
-    if (c < C) {
-      part[wave * 2 * C + c] = dgs[j];
-      part[wave * 2 * C + C + c] = dbs[j];
+      for (int j = 0; j < J; ++j) {
+        const int c = l16 + LPR * j;
+        if (c < C) {
+          red[c] += dgs[j];
+          red[C + c] += dbs[j];
+        }
+      }
     }
+    __syncthreads();
   }
+  for (int i = threadIdx.x; i < 2 * C; i += 256) part[(int64_t)blockIdx.x * 2 * C + i] = red[i];
 }
 
 // Weight-gradient partials: part[p] (NO x KI) = sum over the tokens of
@@ -275,6 +291,7 @@ __global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restri
                                                            int nparts, int64_t n, int64_t stride) {
   for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float s = 0.f;
+#pragma unroll 16
     for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * stride + i];
     out[i] = s;
   }
@@ -327,38 +344,50 @@ hipError_t gather_f32_bf16(const float* in, void* out, int64_t slots, int C, con
   return hipGetLastError();
 }
 
-int ln_bwd_waves(int64_t rows) {
-  const int64_t g = rows < 8192 ? rows : 8192;
-  return (int)(((g + 3) / 4) * 4);
+// workgroups of ln_bwd: up to 2048, each 256 / LPR row groups
+int ln_bwd_blocks(int64_t rows, int C) {
+  const int per = C <= 256 ? 16 : 4;
+  const int64_t b = (rows + per - 1) / per;
+  return (int)(b < 2048 ? b : 2048);
 }
 
-size_t ln_bwd_part_bytes(int64_t rows, int C) { return (size_t)ln_bwd_waves(rows) * 2 * C * 4; }
+size_t ln_bwd_part_bytes(int64_t rows, int C) { return (size_t)ln_bwd_blocks(rows, C) * 2 * C * 4; }
 
 hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int res_fp32, const void* res,
                   int out_fp32, void* out, float* part, float* dg, float* db, int64_t rows, int C, float eps,
                   hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (C > 64 * kLnJ) return hipErrorInvalidValue;
-  const int nw = ln_bwd_waves(rows);
-  const dim3 grid((unsigned)(nw / 4)), block(256);
+  if (C > 768) return hipErrorInvalidValue;
+  const int nb = ln_bwd_blocks(rows, C);
+  const dim3 grid((unsigned)nb), block(256);
   const bf16_t* gb = (const bf16_t*)g;
   const bf16_t* dyb = (const bf16_t*)dy;
-  if (x_fp32 && !res_fp32 && out_fp32)
-    ln_bwd_kernel<float, bf16_t, float><<<grid, block, 0, st>>>((const float*)x, gb, dyb, (const bf16_t*)res,
-                                                                (float*)out, part, rows, C, eps);
-  else if (!x_fp32 && res_fp32 && !out_fp32)
-    ln_bwd_kernel<bf16_t, float, bf16_t><<<grid, block, 0, st>>>((const bf16_t*)x, gb, dyb, (const float*)res,
-                                                                 (bf16_t*)out, part, rows, C, eps);
-  else if (!x_fp32 && !res_fp32 && !out_fp32)
-    ln_bwd_kernel<bf16_t, bf16_t, bf16_t><<<grid, block, 0, st>>>((const bf16_t*)x, gb, dyb, (const bf16_t*)res,
-                                                                  (bf16_t*)out, part, rows, C, eps);
-  else
-    return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
+  auto go = [&](auto LJ) -> hipError_t {
+    constexpr int LP = decltype(LJ)::value / 100, JJ = decltype(LJ)::value % 100;
+    if (x_fp32 && !res_fp32 && out_fp32)
+      ln_bwd_kernel<float, bf16_t, float, LP, JJ><<<grid, block, 0, st>>>((const float*)x, gb, dyb, (const bf16_t*)res,
+                                                                      (float*)out, part, rows, C, eps);
+    else if (!x_fp32 && res_fp32 && !out_fp32)
+      ln_bwd_kernel<bf16_t, float, bf16_t, LP, JJ><<<grid, block, 0, st>>>((const bf16_t*)x, gb, dyb, (const float*)res,
+                                                                       (bf16_t*)out, part, rows, C, eps);
+    else if (!x_fp32 && !res_fp32 && !out_fp32)
+      ln_bwd_kernel<bf16_t, bf16_t, bf16_t, LP, JJ><<<grid, block, 0, st>>>((const bf16_t*)x, gb, dyb,
+                                                                        (const bf16_t*)res, (bf16_t*)out, part, rows,
+                                                                        C, eps);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  };
+  hipError_t e;
+  // template value = 100 * lanes per row + elements per lane
+  if (C <= 96) e = go(std::integral_constant<int, 1606>{});
+  else if (C <= 128) e = go(std::integral_constant<int, 1608>{});
+  else if (C <= 256) e = go(std::integral_constant<int, 1616>{});
+  else e = go(std::integral_constant<int, 6412>{});
   if (e != hipSuccess) return e;
-  // dg = sum over waves of part[w][0:C], db of part[w][C:2C]
-  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part, dg, nw, 2 * C);
-  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part + C, db, nw, 2 * C);
+  // dg = sum over workgroups of part[b][0:C], db of part[b][C:2C]
+  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part, dg, nb, 2 * C);
+  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part + C, db, nb, 2 * C);
   return hipGetLastError();
 }
 
