@@ -194,6 +194,47 @@ def window_variants(vs, torch, np, stream, steps: int = 20) -> dict:
     return out
 
 
+def backward_pair(vs, torch, np, x, w, s, shifts, stream, steps: int = 10) -> dict:
+    """Training backward of the same block pair (vswin_block_bwd, forward
+    recomputed inside each call): ms per pair (HIP events) and the backward
+    FLOPs of the closed form: the forward again plus, per linear layer, 2x
+    its forward FLOPs (dX and dW), and 5 attention products per (query, key)
+    (S and dP in the key-owned kernel, S^T, dP^T and dQ in the query-owned one
+    recompute S and dP, so 7 products are issued; 4 of them are necessary:
+    dP, dV, dK, dQ, plus S)."""
+    hid = s.mlp_ratio * s.C
+    dy = torch.randn(x.shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(7)).to(x.dtype)
+    descs = [vs.make_desc(s.B, s.T, s.H, s.W, s.C, s.heads, s.window, sh, mlp_hidden=hid, dtype=torch.bfloat16)
+             for sh in shifts]
+    nbytes = max(vs.vswin_bwd_workspace_query(d)["block"] for d in descs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dx = torch.empty_like(x)
+    grads = [{k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in wi.items()} for wi in w]
+
+    def pair():
+        for i, sh in enumerate(shifts):
+            vs.vswin_block_bwd(x, w[i], dy, s.heads, s.window, sh, dx=dx, grads=grads[i], workspace=ws,
+                               stream=stream)
+
+    pair()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        pair()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    plans = [vs.vswin_plan_query(d) for d in descs]
+    fwd = [block_flops(p, s.C, hid) for p in plans]
+    lin = sum(f["qkv"] + f["proj"] + f["fc1"] + f["fc2"] for f in fwd)
+    attn = sum(f["attn"] for f in fwd)           # 2 products (S, PV) per (query, key)
+    flops = sum(f["total"] for f in fwd) + 2 * lin + 2.5 * attn
+    return {"ms_per_pair": round(ms, 4), "tokens_per_s": round(2 * s.tokens / (ms * 1e-3), 1),
+            "gflop_per_pair": round(flops / 1e9, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "note": "forward recomputed inside the call; FLOPs = forward + 2x linear + 5 attention products"}
+
+
 def mfma_measured_peak(vs, torch, stream, iters: int = 4000) -> float:
     """TFLOP/s of the library's v_mfma_f32_16x16x32_bf16 throughput kernel with
     two workgroups of 8 waves per CU (four waves per SIMD)."""
@@ -398,6 +439,7 @@ def main():
         "step_ms_warm": warm, "step_ms_cold": cold,
         "memory_kernels": memory_kernels(vs, torch, stream),
         "window_variants": window_variants(vs, torch, np, stream),
+        "backward": backward_pair(vs, torch, np, x, w, s, shifts, stream),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_np, params, s)

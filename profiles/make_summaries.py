@@ -42,8 +42,9 @@ def stats(stats_dir: str) -> str:
            "window variants on the stage-1 grid (window 4 with shift (2,3,3): the per-key-label form `Cfg<8, 4,",
            "false, false, true>`; window 16: the scalar-table form `Cfg<8, 8, true, false, false>`; window 8 with the",
            "-100 mask: `Cfg<8, 4, false, true, false>`), each 23 block pairs and 21 standalone attention launches;",
-           "the main workload's attention is `Cfg<8, 4, false, false, false>`. Other torch kernels are input",
-           "generation.", "",
+           "the main workload's attention is `Cfg<8, 4, false, false, false>`; then 11 backward block pairs",
+           "(`vswin_block_bwd`: the forward recomputed, then the `attn_bwd_*`, `wgrad_kernel`, `ln_bwd_kernel`, GELU",
+           "and GEMM kernels of the backward). Other torch kernels are input generation.", "",
            "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
