@@ -900,7 +900,23 @@ __device__ __forceinline__ bf16x8_t pack8f(const float* v) {
   return __builtin_bit_cast(bf16x8_t, p);
 }
 
-using BwdCF = Cfg<8, 8, true>;   // 8 waves, scalar table (byte step 4)
+// 8 waves, scalar table (byte step 4); group labels, or one label byte per key
+using BwdCF = Cfg<8, 8, true>;
+using BwdCFKey = Cfg<8, 8, true, false, true>;
+
+// label of element i (temporal position 4a + i) of a group's label word
+template <class CF>
+__device__ __forceinline__ int elem_label(int word, int i) {
+  if constexpr (CF::kPerKey) return (int)(((uint32_t)word >> (8 * i)) & 0xffu);
+  else return word;
+}
+
+// P of one (query, key) pair from its log2-domain logit: same region -> exp2(s2 - lse2);
+// another region -> 0, or with the -100 mask exp2(s2 - 100 log2(e) - lse2)
+__device__ __forceinline__ float pair_p(bool in_range, bool same, int m100, float s2, float l2) {
+  const float x = same ? s2 - l2 : s2 - 100.0f * kLog2e - l2;
+  return in_range && (same || m100) ? __builtin_amdgcn_exp2f(x) : 0.f;
+}
 
 }  // namespace
 
@@ -982,8 +998,8 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const AttnBwdArgs b,
   }
 }
 
+template <class CF>
 __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, const BwdL BL) {
-  using CF = BwdCF;
   constexpr int ES = CF::kTabEs;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const A5& L = BL.L;
@@ -1018,7 +1034,7 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
     const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(b.kr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
     const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(b.vr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
     const int kps = pair_slot(key >> 2);
-    const int klab = lp[kps];
+    const int klab = elem_label<CF>(lp[kps], key & 3);
     const int kadd = (int)L.off_tab + ES * L.A + kp[kps] + ES * (key & 3) * Rp;
     const bool kval = key < N;
     f32x4_t dv0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, dv1 = dv0, dk0 = dv0, dk1 = dv0;
@@ -1031,7 +1047,7 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
         const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_q + qr * 64 + ((g4 ^ sw) << 4));
         const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_do + qr * 64 + ((g4 ^ sw) << 4));
         const int qps = pair_slot((qs0 + 4 * g4) >> 2);
-        const int qlab = lp[qps];
+        const int qlw = lp[qps];
         const int base = kadd - kp[qps];   // query temporal i: - i Rp
         const float* tp = reinterpret_cast<const float*>(tabb + base);
         const f32x4_t tb = f32x4_t{tp[0], tp[-Rp], tp[-2 * Rp], tp[-3 * Rp]};
@@ -1042,8 +1058,8 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
         float dsl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool valid = kval && qs0 + 4 * g4 + i < N && qlab == klab;
-          const float P = valid ? __builtin_amdgcn_exp2f(s2[i] - l4[i]) : 0.f;
+          const float P = pair_p(kval && qs0 + 4 * g4 + i < N, elem_label<CF>(qlw, i) == klab, b.a.mask_m100,
+                                 s2[i], l4[i]);
           const float ds = P * (dp[i] - d4[i]);
           pv[4 * s + i] = P;
           dsv[4 * s + i] = ds;
@@ -1104,8 +1120,8 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
   }
 }
 
+template <class CF>
 __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, const BwdL BL) {
-  using CF = BwdCF;
   constexpr int ES = CF::kTabEs;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const A5& L = BL.L;
@@ -1136,7 +1152,7 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
     const float l2 = qval ? b.lse[(int64_t)mem * N + q] : 0.f;
     const float Dq = b.D[(int64_t)mem * NPAD + q];
     const int qps = pair_slot(q >> 2);
-    const int qlab = lp[qps];
+    const int qlab = elem_label<CF>(lp[qps], q & 3);
     const int qaddr = (int)L.off_tab + ES * L.A - kp[qps] - ES * (q & 3) * Rp;
     f32x4_t dq0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, dq1 = dq0;
     for (int kb = 0; kb < NPAD; kb += 32) {
@@ -1148,15 +1164,15 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
         const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_k + kr * 64 + ((g4 ^ sw) << 4));
         const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_v + kr * 64 + ((g4 ^ sw) << 4));
         const int kps = pair_slot((ks0 + 4 * g4) >> 2);
-        const int klab = lp[kps];
+        const int klw = lp[kps];
         const float* tp = reinterpret_cast<const float*>(tabb + qaddr + kp[kps]);
         const f32x4_t tb = f32x4_t{tp[0], tp[Rp], tp[2 * Rp], tp[3 * Rp]};
         const f32x4_t s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf, tb, 0, 0, 0);
         const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool valid = qval && ks0 + 4 * g4 + i < N && qlab == klab;
-          const float P = valid ? __builtin_amdgcn_exp2f(s2[i] - l2) : 0.f;
+          const float P =
+              pair_p(qval && ks0 + 4 * g4 + i < N, elem_label<CF>(klw, i) == qlab, b.a.mask_m100, s2[i], l2);
           dsv[4 * s + i] = P * (dp[i] - Dq);
         }
       }
@@ -1291,7 +1307,7 @@ bool plan_bwd(const AttnArgs& a, BwdL& B) {
 }  // namespace
 
 bool attention_bwd_supported(vswin_dtype dt, const AttnArgs& a) {
-  if (!attention_mfma_supported(dt, a) || a.mask_m100 || !groups_uniform(a)) return false;
+  if (!attention_mfma_supported(dt, a)) return false;
   BwdL B;
   return plan_bwd(a, B);
 }
@@ -1336,12 +1352,18 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
   attn_table_kernel<<<dim3((unsigned)((L.TS4 + 255) / 256), (unsigned)L.heads), dim3(256), 0, st>>>(
       reinterpret_cast<const bf16_t*>(in.a.table), reinterpret_cast<f32x4_t*>(b.a.tab4), L);
   attn_bwd_prep_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(b, B);
-  hipError_t e = ensure_dynamic_lds((const void*)attn_bwd_kv_kernel, B.a_lds);
+  auto run = [&](auto kv, auto qk) -> hipError_t {
+    hipError_t e = ensure_dynamic_lds((const void*)kv, B.a_lds);
+    if (e != hipSuccess) return e;
+    e = ensure_dynamic_lds((const void*)qk, B.b_lds);
+    if (e != hipSuccess) return e;
+    kv<<<dim3((unsigned)items), dim3(512), B.a_lds, st>>>(b, B);
+    qk<<<dim3((unsigned)items), dim3(512), B.b_lds, st>>>(b, B);
+    return hipGetLastError();
+  };
+  const hipError_t e = groups_uniform(in.a) ? run(attn_bwd_kv_kernel<BwdCF>, attn_bwd_q_kernel<BwdCF>)
+                                            : run(attn_bwd_kv_kernel<BwdCFKey>, attn_bwd_q_kernel<BwdCFKey>);
   if (e != hipSuccess) return e;
-  e = ensure_dynamic_lds((const void*)attn_bwd_q_kernel, B.b_lds);
-  if (e != hipSuccess) return e;
-  attn_bwd_kv_kernel<<<dim3((unsigned)items), dim3(512), B.a_lds, st>>>(b, B);
-  attn_bwd_q_kernel<<<dim3((unsigned)items), dim3(512), B.b_lds, st>>>(b, B);
   const int64_t E = (int64_t)B.ap * B.ap * B.mhw * B.mhw * 7;
   attn_bwd_grp_sum_kernel<<<dim3((unsigned)((E + 255) / 256), (unsigned)in.a.heads), dim3(256), 0, st>>>(
       b.dgrp, gsum, in.a.nW, in.a.heads, E);

@@ -49,40 +49,45 @@ def _tok(shape, seed, scale=1.0):
 
 
 CASES = [
-    # name, B, size, C, heads, window, shift, init
-    ("shifted", 1, (16, 14, 14), 64, 2, (8, 7, 7), (4, 3, 3), "stress"),
-    ("regular", 1, (16, 14, 14), 64, 2, (8, 7, 7), (0, 0, 0), "stress"),
-    ("padded shifted C=96", 1, (16, 12, 13), 96, 3, (8, 7, 7), (4, 3, 3), "stress"),
-    ("B=2 spec init", 2, (16, 14, 21), 96, 3, (8, 7, 7), (4, 3, 3), "spec"),
-    ("window 4 spatial-only shift", 1, (8, 14, 14), 64, 2, (4, 7, 7), (0, 3, 3), "stress"),
+    # name, B, size, C, heads, window, shift, init, flags
+    ("shifted", 1, (16, 14, 14), 64, 2, (8, 7, 7), (4, 3, 3), "stress", 0),
+    ("regular", 1, (16, 14, 14), 64, 2, (8, 7, 7), (0, 0, 0), "stress", 0),
+    ("padded shifted C=96", 1, (16, 12, 13), 96, 3, (8, 7, 7), (4, 3, 3), "stress", 0),
+    ("B=2 spec init", 2, (16, 14, 21), 96, 3, (8, 7, 7), (4, 3, 3), "spec", 0),
+    ("mask -100 padded", 1, (16, 12, 13), 64, 2, (8, 7, 7), (4, 3, 3), "stress", vs.F_MASK_M100),
+    ("window 4 temporal shift 2", 1, (16, 14, 14), 64, 2, (4, 7, 7), (2, 3, 3), "stress", 0),
+    ("Swin-B C=128 padded", 1, (16, 12, 13), 128, 4, (8, 7, 7), (4, 3, 3), "stress", 0),
+    ("window 4 spatial-only shift", 1, (8, 14, 14), 64, 2, (4, 7, 7), (0, 3, 3), "stress", 0),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_window_msa_bwd(case):
-    name, B, size, C, heads, window, shift, init = case
+    name, B, size, C, heads, window, shift, init, flags = case
     say(f"window_msa backward {name}")
     p = _params(C, heads, window, init, 41)
     xn = _tok((B, *size, C), 5)
     dy = _tok((B, *size, C), 6)
-    dx, g = vs.vswin_window_msa_bwd(dev(xn, "bf16"), dev_params(p, "bf16"), dev(dy, "bf16"), heads, window, shift)
+    dx, g = vs.vswin_window_msa_bwd(dev(xn, "bf16"), dev_params(p, "bf16"), dev(dy, "bf16"), heads, window, shift,
+                                    flags=flags)
     torch.cuda.synchronize()
-    rdx, rg = ob.window_msa_bwd(xn, p, heads, window, shift, dy)
+    rdx, rg = ob.window_msa_bwd(xn, p, heads, window, shift, dy, mask_m100=bool(flags & vs.F_MASK_M100))
     check_rel(host64(dx), rdx, f"{name} dx_norm")
     for k in vs.MSA_GRAD_NAMES:
         check_rel(host64(g[k]), rg[k], f"{name} d{k}")
 
 
-@pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
+@pytest.mark.parametrize("case", CASES[:7], ids=[c[0] for c in CASES[:7]])
 def test_block_bwd(case):
-    name, B, size, C, heads, window, shift, init = case
+    name, B, size, C, heads, window, shift, init, flags = case
     say(f"block backward {name}")
     p = _params(C, heads, window, init, 43)
     x = _tok((B, *size, C), 7)
     dy = _tok((B, *size, C), 8)
-    dx, g = vs.vswin_block_bwd(dev(x, "bf16"), dev_params(p, "bf16"), dev(dy, "bf16"), heads, window, shift)
+    dx, g = vs.vswin_block_bwd(dev(x, "bf16"), dev_params(p, "bf16"), dev(dy, "bf16"), heads, window, shift,
+                               flags=flags)
     torch.cuda.synchronize()
-    rdx, rg = ob.block_bwd(x, p, heads, window, shift, dy)
+    rdx, rg = ob.block_bwd(x, p, heads, window, shift, dy, mask_m100=bool(flags & vs.F_MASK_M100))
     check_rel(host64(dx), rdx, f"{name} dx")
     for k in vs.GRAD_NAMES:
         check_rel(host64(g[k]), rg[k], f"{name} d{k}")
