@@ -57,6 +57,7 @@ CASES = [
     ("mask -100 padded", 1, (16, 12, 13), 64, 2, (8, 7, 7), (4, 3, 3), "stress", vs.F_MASK_M100),
     ("window 4 temporal shift 2", 1, (16, 14, 14), 64, 2, (4, 7, 7), (2, 3, 3), "stress", 0),
     ("Swin-B C=128 padded", 1, (16, 12, 13), 128, 4, (8, 7, 7), (4, 3, 3), "stress", 0),
+    ("Swin-L C=192", 1, (16, 14, 14), 192, 6, (8, 7, 7), (4, 3, 3), "stress", 0),
     ("window 4 spatial-only shift", 1, (8, 14, 14), 64, 2, (4, 7, 7), (0, 3, 3), "stress", 0),
 ]
 
@@ -77,7 +78,7 @@ def test_window_msa_bwd(case):
         check_rel(host64(g[k]), rg[k], f"{name} d{k}")
 
 
-@pytest.mark.parametrize("case", CASES[:7], ids=[c[0] for c in CASES[:7]])
+@pytest.mark.parametrize("case", CASES[:8], ids=[c[0] for c in CASES[:8]])
 def test_block_bwd(case):
     name, B, size, C, heads, window, shift, init, flags = case
     say(f"block backward {name}")

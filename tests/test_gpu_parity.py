@@ -266,6 +266,19 @@ def test_block_window_variants_stage1_grid(window, shift):
     check(host64(y), ref, "bf16", f"window {window} block shift {shift}")
 
 
+def test_block_swin_l_width():
+    """Swin-L's stage-1 width (C = 192, 6 heads of 32): the generic GEMM path
+    around the MFMA attention, regular and shifted."""
+    C, heads, window = 192, 6, (8, 7, 7)
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=37)
+    x = _rng_tokens((1, 16, 14, 14, C), "bf16", 12)
+    for shift in ((0, 0, 0), (4, 3, 3)):
+        say(f"Swin-L width block, shift {shift}")
+        y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
+        _, ref = oracle.block(x, p, heads, window, shift)
+        check(host64(y), ref, "bf16", f"C=192 block shift {shift}")
+
+
 def test_workload1_fp32_pair():
     say("workload 1: fp32 block pair")
     x, params = synth.gen_workload(1)
