@@ -203,8 +203,9 @@ vswin_status vswin_bwd_workspace_query(const vswin_desc* desc, size_t* block_byt
  * between calls).  Arithmetic: bf16 operands, fp32 accumulation; the
  * attention probabilities are recomputed in fp32 from the forward's
  * log-sum-exp; dS = P (dP - rowsum(dO * O)); the relative-position table
- * gradient sums dS over the pairs of every offset (fp32 atomics, so its
- * summation order is not fixed).  dx must not alias x or dy.
+ * gradient sums dS over the pairs of every offset (deterministic: no
+ * atomics on the path).  An empty batch (B = 0) sets every gradient passed
+ * to zero.  dx must not alias x or dy.
  * workspace >= block_bytes of vswin_bwd_workspace_query, 256-byte aligned.  */
 vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w,
                              const void* dy, void* dx, const vswin_block_grads* g,

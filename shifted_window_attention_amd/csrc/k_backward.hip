@@ -297,6 +297,10 @@ __global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restri
   }
 }
 
+__global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
 // out[i] = sum_p part[p * stride + i], one workgroup per output (many partials)
 __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                           int nparts, int64_t stride) {
@@ -388,6 +392,12 @@ hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int 
   // dg = sum over workgroups of part[b][0:C], db of part[b][C:2C]
   reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part, dg, nb, 2 * C);
   reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part + C, db, nb, 2 * C);
+  return hipGetLastError();
+}
+
+hipError_t zero_f32(float* p, int64_t n, hipStream_t st) {
+  if (!p || n <= 0) return hipSuccess;
+  zero_f32_kernel<<<dim3(grid_for(n, 256)), dim3(256), 0, st>>>(p, n);
   return hipGetLastError();
 }
 

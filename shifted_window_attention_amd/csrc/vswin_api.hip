@@ -548,6 +548,18 @@ vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_
   return VSWIN_OK;
 }
 
+// an empty batch: every gradient the caller passed is zero
+vswin_status zero_grads(const Plan& p, const vswin_block_grads* g, hipStream_t st) {
+  if (!g) return VSWIN_OK;
+  const int64_t C = p.C, H = p.hid;
+  const std::pair<float*, int64_t> z[] = {
+      {g->ln1_g, C}, {g->ln1_b, C}, {g->qkv_w, 3 * C * C}, {g->qkv_b, 3 * C}, {g->proj_w, C * C},
+      {g->proj_b, C}, {g->rpb_table, (int64_t)p.rel.rows * p.heads}, {g->ln2_g, C}, {g->ln2_b, C},
+      {g->fc1_w, H * C}, {g->fc1_b, H}, {g->fc2_w, C * H}, {g->fc2_b, C}};
+  for (const auto& e : z) HIPCHECK(zero_f32(e.first, e.second, st), "bwd: zero gradients");
+  return VSWIN_OK;
+}
+
 vswin_status check_bwd_args(const Plan& p, const vswin_desc* desc, const void* x, const vswin_block_weights* w,
                             const void* dy, const void* dx, const vswin_block_grads* g, const void* workspace,
                             size_t workspace_bytes, size_t need) {
@@ -579,7 +591,14 @@ vswin_status vswin_window_msa_bwd(const vswin_desc* desc, const void* x_norm, co
                                   size_t workspace_bytes, void* stream) {
   Plan p{};
   CHECK(make_plan(desc, p));
-  if (p.L == 0) return VSWIN_OK;
+  if (p.L == 0) {   // empty batch: the gradients the caller passed are zero
+    vswin_block_grads gm{};
+    if (g) {
+      gm.qkv_w = g->qkv_w; gm.qkv_b = g->qkv_b; gm.proj_w = g->proj_w; gm.proj_b = g->proj_b;
+      gm.rpb_table = g->rpb_table;
+    }
+    return zero_grads(p, g ? &gm : nullptr, (hipStream_t)stream);
+  }
   const BwdWs L = bwd_layout(p, desc);
   CHECK(check_bwd_args(p, desc, x_norm, w, dy, dx_norm, g, workspace, workspace_bytes, L.msa_bytes));
   if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
@@ -599,7 +618,7 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
                              void* stream) {
   Plan p{};
   CHECK(make_plan(desc, p));
-  if (p.L == 0) return VSWIN_OK;
+  if (p.L == 0) return zero_grads(p, g, (hipStream_t)stream);   // empty batch: zero gradients
   const BwdWs L = bwd_layout(p, desc);
   CHECK(check_bwd_args(p, desc, x, w, dy, dx, g, workspace, workspace_bytes, L.block_bytes));
   CHECK(check_ptr(w->ln1_g, "ln1_g"));

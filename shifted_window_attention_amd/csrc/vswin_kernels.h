@@ -154,6 +154,8 @@ size_t ln_bwd_part_bytes(int64_t rows, int C);
 hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int res_fp32, const void* res,
                   int out_fp32, void* out, float* part, float* dg, float* db, int64_t rows, int C, float eps,
                   hipStream_t st);
+// p[0 .. n) = 0 (a kernel, so that it may sit inside a captured graph); p nullable
+hipError_t zero_f32(float* p, int64_t n, hipStream_t st);
 // dW (NO x KI) = A^T B and db (NO, nullable) = column sums of A over M token rows,
 // A (M x NO), B (M x KI) bf16; fp32 outputs; part: wgrad_part_bytes
 size_t wgrad_part_bytes(int64_t M, int NO, int KI);

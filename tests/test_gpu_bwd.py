@@ -108,3 +108,26 @@ def test_block_bwd_stage1_shape(shift):
     check_rel(host64(dx), rdx, "stage-1 dx")
     for k in vs.GRAD_NAMES:
         check_rel(host64(g[k]), rg[k], f"stage-1 d{k}")
+
+
+def test_bwd_deterministic_and_empty_batch():
+    """Two backward calls give bitwise-identical gradients (no atomics on the
+    path), and an empty batch sets every gradient to zero."""
+    C, heads, window, shift = 96, 3, (8, 7, 7), (4, 3, 3)
+    p = _params(C, heads, window, "stress", 47)
+    x = dev(_tok((1, 16, 14, 14, C), 10), "bf16")
+    dy = dev(_tok((1, 16, 14, 14, C), 11), "bf16")
+    w = dev_params(p, "bf16")
+    dx1, g1 = vs.vswin_block_bwd(x, w, dy, heads, window, shift)
+    dx2, g2 = vs.vswin_block_bwd(x, w, dy, heads, window, shift)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2)
+    for k in vs.GRAD_NAMES:
+        assert torch.equal(g1[k], g2[k]), k
+    e = torch.empty((0, 16, 14, 14, C), dtype=torch.bfloat16, device="cuda")
+    filled = {k: torch.full(v.shape, 7.0, device="cuda") for k, v in g1.items()}
+    dx0, g0 = vs.vswin_block_bwd(e, w, e, heads, window, shift, grads=filled)
+    torch.cuda.synchronize()
+    assert dx0.shape == e.shape
+    for k in vs.GRAD_NAMES:
+        assert torch.count_nonzero(g0[k]) == 0, k
