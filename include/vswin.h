@@ -192,8 +192,8 @@ typedef struct {
 /* Workspace bytes of vswin_block_bwd and vswin_window_msa_bwd for `desc`.
  * Host only.  VSWIN_ERR_UNSUPPORTED when the backward cannot serve the
  * descriptor: it needs bf16, head_dim 32, C <= 768 and the MFMA attention
- * with at most 512 tokens per window (temporal window a multiple of 4; the
- * -100 mask and key-by-key region labels as in the forward).               */
+ * (temporal window a multiple of 4, at most 1024 tokens per window; the -100
+ * mask and key-by-key region labels as in the forward).                    */
 vswin_status vswin_bwd_workspace_query(const vswin_desc* desc, size_t* block_bytes, size_t* msa_bytes);
 
 /* Backward of vswin_block_fwd (eq. 1 differentiated; the backbone is

@@ -848,6 +848,7 @@ struct BwdL {
   // kernel A LDS
   uint32_t a_q, a_do, a_qt, a_dot, a_lse, a_D, a_lds;
   int ap, mhw;                // temporal groups per window (P / 4), spatial cells (Mh * Mw)
+  int gf;                     // windows over 512 tokens: row fragments read from global memory (L2), not LDS
   // kernel B LDS
   uint32_t b_k, b_v, b_kt, b_lds;
 };
@@ -998,7 +999,7 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const AttnBwdArgs b,
   }
 }
 
-template <class CF>
+template <class CF, bool GF>
 __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, const BwdL BL) {
   constexpr int ES = CF::kTabEs;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1013,8 +1014,10 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
   const int* lp = reinterpret_cast<const int*>(smem + L.off_lp);
   stage_offsets<CF>(b.a, L, kp);
   stage_labels<CF>(b.a, L, wi, smem);
-  stage_rows16(b.qr + (int64_t)mem * NPAD * 32, smem + BL.a_q, NPAD, wv, CF::kWaves);
-  stage_rows16(b.dor + (int64_t)mem * NPAD * 32, smem + BL.a_do, NPAD, wv, CF::kWaves);
+  if constexpr (!GF) {
+    stage_rows16(b.qr + (int64_t)mem * NPAD * 32, smem + BL.a_q, NPAD, wv, CF::kWaves);
+    stage_rows16(b.dor + (int64_t)mem * NPAD * 32, smem + BL.a_do, NPAD, wv, CF::kWaves);
+  }
   stage_trows(b.qt + (int64_t)mem * 32 * NPAD, smem + BL.a_qt, NPAD, BL.pitch, wv, CF::kWaves);
   stage_trows(b.dot + (int64_t)mem * 32 * NPAD, smem + BL.a_dot, NPAD, BL.pitch, wv, CF::kWaves);
   stage_f32(b.lse + (int64_t)mem * N, smem + BL.a_lse, N, wv, CF::kWaves);
@@ -1044,8 +1047,14 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
       for (int s = 0; s < 2; ++s) {
         const int qs0 = qb + 16 * s;
         const int qr = qs0 + fr;
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_q + qr * 64 + ((g4 ^ sw) << 4));
-        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_do + qr * 64 + ((g4 ^ sw) << 4));
+        bf16x8_t qa, da;
+        if constexpr (GF) {
+          qa = *reinterpret_cast<const bf16x8_t*>(b.qr + ((int64_t)mem * NPAD + qr) * 32 + 8 * g4);
+          da = *reinterpret_cast<const bf16x8_t*>(b.dor + ((int64_t)mem * NPAD + qr) * 32 + 8 * g4);
+        } else {
+          qa = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_q + qr * 64 + ((g4 ^ sw) << 4));
+          da = *reinterpret_cast<const bf16x8_t*>(smem + BL.a_do + qr * 64 + ((g4 ^ sw) << 4));
+        }
         const int qps = pair_slot((qs0 + 4 * g4) >> 2);
         const int qlw = lp[qps];
         const int base = kadd - kp[qps];   // query temporal i: - i Rp
@@ -1120,7 +1129,7 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
   }
 }
 
-template <class CF>
+template <class CF, bool GF>
 __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, const BwdL BL) {
   constexpr int ES = CF::kTabEs;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1134,8 +1143,10 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
   const int* lp = reinterpret_cast<const int*>(smem + L.off_lp);
   stage_offsets<CF>(b.a, L, kp);
   stage_labels<CF>(b.a, L, wi, smem);
-  stage_rows16(b.kr + (int64_t)mem * NPAD * 32, smem + BL.b_k, NPAD, wv, CF::kWaves);
-  stage_rows16(b.vr + (int64_t)mem * NPAD * 32, smem + BL.b_v, NPAD, wv, CF::kWaves);
+  if constexpr (!GF) {
+    stage_rows16(b.kr + (int64_t)mem * NPAD * 32, smem + BL.b_k, NPAD, wv, CF::kWaves);
+    stage_rows16(b.vr + (int64_t)mem * NPAD * 32, smem + BL.b_v, NPAD, wv, CF::kWaves);
+  }
   stage_trows(b.kt + (int64_t)mem * 32 * NPAD, smem + BL.b_kt, NPAD, BL.pitch, wv, CF::kWaves);
   tab_copy<CF>(b.a, L, h, smem, wv);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1161,8 +1172,14 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
       for (int s = 0; s < 2; ++s) {
         const int ks0 = kb + 16 * s;
         const int kr = ks0 + fr;
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_k + kr * 64 + ((g4 ^ sw) << 4));
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_v + kr * 64 + ((g4 ^ sw) << 4));
+        bf16x8_t ka, va;
+        if constexpr (GF) {
+          ka = *reinterpret_cast<const bf16x8_t*>(b.kr + ((int64_t)mem * NPAD + kr) * 32 + 8 * g4);
+          va = *reinterpret_cast<const bf16x8_t*>(b.vr + ((int64_t)mem * NPAD + kr) * 32 + 8 * g4);
+        } else {
+          ka = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_k + kr * 64 + ((g4 ^ sw) << 4));
+          va = *reinterpret_cast<const bf16x8_t*>(smem + BL.b_v + kr * 64 + ((g4 ^ sw) << 4));
+        }
         const int kps = pair_slot((ks0 + 4 * g4) >> 2);
         const int klw = lp[kps];
         const float* tp = reinterpret_cast<const float*>(tabb + qaddr + kp[kps]);
@@ -1285,7 +1302,12 @@ bool plan_bwd(const AttnArgs& a, BwdL& B) {
   L.off_red = take(4 * kMaxWaves);
   L.off_tab = take((size_t)L.TS4 * 16);
   const size_t common = off;
-  const size_t rows = (size_t)L.NPAD * 64, trows = (size_t)32 * B.pitch * 16;
+  const size_t trows = (size_t)32 * B.pitch * 16;
+  // the row copies (q', dO for the key-owned kernel, k, v for the query-owned
+  // one) sit in LDS while they fit with the transposes; beyond that (windows of
+  // more than 512 tokens) the MFMA row fragments come from global memory
+  B.gf = (size_t)L.NPAD * 64 * 2 + 2 * trows + common + (size_t)L.NPAD * 8 > kLdsMax ? 1 : 0;
+  const size_t rows = B.gf ? 0 : (size_t)L.NPAD * 64;
   B.a_q = take(rows);
   B.a_do = take(rows);
   B.a_qt = take(trows);
@@ -1361,8 +1383,14 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
     qk<<<dim3((unsigned)items), dim3(512), B.b_lds, st>>>(b, B);
     return hipGetLastError();
   };
-  const hipError_t e = groups_uniform(in.a) ? run(attn_bwd_kv_kernel<BwdCF>, attn_bwd_q_kernel<BwdCF>)
-                                            : run(attn_bwd_kv_kernel<BwdCFKey>, attn_bwd_q_kernel<BwdCFKey>);
+  const bool uni = groups_uniform(in.a);
+  hipError_t e;
+  if (B.gf)
+    e = uni ? run(attn_bwd_kv_kernel<BwdCF, true>, attn_bwd_q_kernel<BwdCF, true>)
+            : run(attn_bwd_kv_kernel<BwdCFKey, true>, attn_bwd_q_kernel<BwdCFKey, true>);
+  else
+    e = uni ? run(attn_bwd_kv_kernel<BwdCF, false>, attn_bwd_q_kernel<BwdCF, false>)
+            : run(attn_bwd_kv_kernel<BwdCFKey, false>, attn_bwd_q_kernel<BwdCFKey, false>);
   if (e != hipSuccess) return e;
   const int64_t E = (int64_t)B.ap * B.ap * B.mhw * B.mhw * 7;
   attn_bwd_grp_sum_kernel<<<dim3((unsigned)((E + 255) / 256), (unsigned)in.a.heads), dim3(256), 0, st>>>(

@@ -488,8 +488,8 @@ vswin_status vswin_bwd_workspace_query(const vswin_desc* desc, size_t* block_byt
   Plan p{};
   CHECK(make_plan(desc, p));
   if (!bwd_supported(p, desc))
-    return fail(VSWIN_ERR_UNSUPPORTED, "backward needs bf16, head_dim 32, C <= 768 and the MFMA attention with at most "
-                                       "512 tokens per window");
+    return fail(VSWIN_ERR_UNSUPPORTED, "backward needs bf16, head_dim 32, C <= 768 and the MFMA attention (at most "
+                                       "1024 tokens per window)");
   const BwdWs w = bwd_layout(p, desc);
   if (block_bytes) *block_bytes = w.block_bytes;
   if (msa_bytes) *msa_bytes = w.msa_bytes;
@@ -564,8 +564,8 @@ vswin_status check_bwd_args(const Plan& p, const vswin_desc* desc, const void* x
                             const void* dy, const void* dx, const vswin_block_grads* g, const void* workspace,
                             size_t workspace_bytes, size_t need) {
   if (!bwd_supported(p, desc))
-    return fail(VSWIN_ERR_UNSUPPORTED, "backward needs bf16, head_dim 32, C <= 768 and the MFMA attention with at most "
-                                       "512 tokens per window");
+    return fail(VSWIN_ERR_UNSUPPORTED, "backward needs bf16, head_dim 32, C <= 768 and the MFMA attention (at most "
+                                       "1024 tokens per window)");
   CHECK(check_ptr(x, "x"));
   CHECK(check_ptr(dy, "dy"));
   CHECK(check_ptr(dx, "dx"));

@@ -180,17 +180,18 @@ def test_mfma_rate_probe_rejects_bad_arguments():
 
 
 def test_bwd_workspace_query_refuses_unsupported_shapes():
-    """The backward serves bf16 MFMA-attention shapes of up to 512 tokens per
-    window (the -100 mask and key-by-key labels included); windows over 512
-    tokens, -100 with a boundary inside a key group, and fp32 are refused on
-    the host."""
+    """The backward serves the bf16 MFMA-attention shapes (the -100 mask,
+    key-by-key labels and windows of up to 1024 tokens included); -100 with a
+    boundary inside a key group, windows over 1024 tokens and fp32 are refused
+    on the host."""
     ok = vs.vswin_bwd_workspace_query(vs.make_desc(1, 16, 56, 56, 96, 3, (8, 7, 7), (4, 3, 3), dtype=1))
     assert ok["block"] > ok["msa"] > 0
     for d in (vs.make_desc(1, 16, 14, 14, 64, 2, (8, 7, 7), (4, 3, 3), dtype=1, flags=vs.F_MASK_M100),
-              vs.make_desc(1, 16, 14, 14, 64, 2, (4, 7, 7), (2, 3, 3), dtype=1)):
+              vs.make_desc(1, 16, 14, 14, 64, 2, (4, 7, 7), (2, 3, 3), dtype=1),
+              vs.make_desc(1, 16, 14, 14, 64, 2, (16, 7, 7), (8, 3, 3), dtype=1)):
         assert vs.vswin_bwd_workspace_query(d)["block"] > 0
     for d in (vs.make_desc(1, 16, 14, 14, 64, 2, (4, 7, 7), (2, 3, 3), dtype=1, flags=vs.F_MASK_M100),
-              vs.make_desc(1, 16, 14, 14, 64, 2, (16, 7, 7), (8, 3, 3), dtype=1),
+              vs.make_desc(1, 24, 14, 14, 64, 2, (24, 7, 7), (12, 3, 3), dtype=1),
               vs.make_desc(1, 4, 14, 14, 32, 2, (2, 7, 7), (1, 3, 3), dtype=0)):
         with pytest.raises(vs.VswinError) as e:
             vs.vswin_bwd_workspace_query(d)

@@ -58,6 +58,7 @@ CASES = [
     ("window 4 temporal shift 2", 1, (16, 14, 14), 64, 2, (4, 7, 7), (2, 3, 3), "stress", 0),
     ("Swin-B C=128 padded", 1, (16, 12, 13), 128, 4, (8, 7, 7), (4, 3, 3), "stress", 0),
     ("Swin-L C=192", 1, (16, 14, 14), 192, 6, (8, 7, 7), (4, 3, 3), "stress", 0),
+    ("window 16 shifted", 1, (16, 14, 14), 96, 3, (16, 7, 7), (8, 3, 3), "stress", 0),
     ("window 4 spatial-only shift", 1, (8, 14, 14), 64, 2, (4, 7, 7), (0, 3, 3), "stress", 0),
 ]
 
@@ -78,7 +79,7 @@ def test_window_msa_bwd(case):
         check_rel(host64(g[k]), rg[k], f"{name} d{k}")
 
 
-@pytest.mark.parametrize("case", CASES[:8], ids=[c[0] for c in CASES[:8]])
+@pytest.mark.parametrize("case", CASES[:9], ids=[c[0] for c in CASES[:9]])
 def test_block_bwd(case):
     name, B, size, C, heads, window, shift, init, flags = case
     say(f"block backward {name}")
