@@ -42,11 +42,19 @@ Readings of points the pages leave open (each listed in the design notes):
   D15 dropout / drop-path are identity (inference);
   D16 windows ordered (b, wt, wh, ww), tokens (pt, ph, pw), row-major;
   D17 patch vector order (c, kt, kh, kw), no patch norm;
-  D18 merge concat order (h,w) offsets (0,0),(1,0),(0,1),(1,1), LN(4C), Linear.
+  D18 merge concat order (h,w) offsets (0,0),(1,0),(0,1),(1,1), LN(4C), Linear;
+  D23 classification head = mean of the final tokens over (T', H', W'), then
+      Linear(C -> classes) (the 2D Swin page's global average pooling and
+      linear classifier, applied to the 3D token grid);
+  D24 several views of one video (temporal clips x spatial crops, Table 1)
+      combine as the mean over views of each view's softmax probabilities;
+  D25 inflation (§3.4): the 2D patch kernel is repeated over the pt temporal
+      slots and divided by pt (0.5 for pt = 2); the 2D bias table is repeated
+      over the 2P - 1 temporal offsets, temporal offset outermost (D9).
 
 Parity unpinned (no page value separates the alternatives; shared written
 conventions): D9 offset sign and h/w order, D12 eps, D13 erf vs tanh, D17/D18
-flatten and concat orders, D4 equality case.
+flatten and concat orders, D4 equality case, D24 probabilities vs logits.
 """
 from __future__ import annotations
 
@@ -456,6 +464,44 @@ def backbone_macs(cfg: dict) -> Dict[str, int]:
             C *= 2
     out["total"] = out["embed"] + out["blocks"] + out["merges"]
     return out
+
+
+# --------------------------------------------------------------------------
+# around the backbone: 2D -> 3D inflation (§3.4), classification head and
+# multi-view scores (readings D23-D25)
+# --------------------------------------------------------------------------
+def inflate_patch_embed(w2d: np.ndarray, pt: int) -> np.ndarray:
+    """2D patch kernel (C, Cin, ph, pw) -> 3D (C, Cin, pt, ph, pw): the same
+    kernel in each of the pt temporal slots, divided by pt (§3.4 "Initialisation
+    from an image model": 0.5 for the two slots), so a video whose pt frames
+    are equal embeds as its single frame did in 2D."""
+    w = np.asarray(w2d, np.float64)
+    return np.repeat(w[:, :, None, :, :], pt, axis=2) / pt
+
+
+def inflate_bias_table(t2d: np.ndarray, P: int) -> np.ndarray:
+    """2D relative-bias table ((2M-1)^2, heads) -> 3D ((2P-1)(2M-1)^2, heads):
+    one copy per temporal offset (§3.4), temporal offset outermost as in the
+    3D table's row order (reading D9), so every frame pair sees the 2D bias."""
+    t = np.asarray(t2d, np.float64)
+    return np.concatenate([t] * (2 * P - 1), axis=0)
+
+
+def head(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """Final tokens (B, T', H', W', C) -> class logits (B, classes): the mean
+    over all tokens of a clip, then Linear(C -> classes) (reading D23)."""
+    v = np.asarray(x, np.float64)
+    pooled = v.reshape(v.shape[0], -1, v.shape[-1]).mean(axis=1)
+    return linear(pooled, w, b)
+
+
+def multiview_average(logits: np.ndarray) -> np.ndarray:
+    """Logits of V views of each video (B, V, classes) -> (B, classes): the
+    mean over the views of each view's softmax (reading D24)."""
+    z = np.asarray(logits, np.float64)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=-1, keepdims=True)).mean(axis=1)
 
 
 def backbone_params(cfg: dict, num_classes: int = 0, qkv_bias: bool = True) -> int:
