@@ -125,6 +125,49 @@ def memory_kernels(vs, torch, stream, launches: int = 20) -> dict:
     return out
 
 
+def inference_head(vs, torch, stream, launches: int = 20) -> dict:
+    """The pieces around the backbone at the Swin-T K400 test protocol: the
+    classification head on 2 videos x 12 views (4 clips x 3 crops) of final
+    tokens (16, 7, 7, 768) in bf16 with 400 classes, then the average of the
+    views' softmax probabilities; plus the inflation of a Swin-T 2D patch
+    kernel and (13*13, 3) bias table.  us per launch (HIP events) and the
+    head's algorithmic bytes (tokens and weights once) over its time."""
+    g = torch.Generator(device="cuda").manual_seed(6)
+    B, V, K, C = 2, 12, 400, 768
+    x = torch.randn((B * V, 16, 7, 7, C), generator=g, device="cuda").to(torch.bfloat16)
+    w = (0.02 * torch.randn((K, C), generator=g, device="cuda")).to(torch.bfloat16)
+    b = torch.zeros(K, dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((B * V, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(vs.lib().vswin_head_workspace(B * V, 16 * 49, C), 256), dtype=torch.uint8, device="cuda")
+    w2 = (0.02 * torch.randn((96, 3, 4, 4), generator=g, device="cuda")).to(torch.bfloat16)
+    t2 = (0.02 * torch.randn((169, 3), generator=g, device="cuda")).to(torch.bfloat16)
+    runs = {
+        "head": (lambda: vs.vswin_head_fwd(x, w, b, out=logits, workspace=ws, stream=stream),
+                 x.numel() * 2 + w.numel() * 2 + B * V * K * 4),
+        "multiview_average": (lambda: vs.vswin_multiview_average(logits.view(B, V, K), stream=stream), None),
+        "inflate_patch_embed": (lambda: vs.vswin_inflate_patch_embed(w2, 2, stream=stream), None),
+        "inflate_bias_table": (lambda: vs.vswin_inflate_bias_table(t2, 8, stream=stream), None),
+    }
+    out = {"workload": "2 videos x 12 views, tokens (16,7,7,768) bf16, 400 classes"}
+    for k, (fn, nbytes) in runs.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        r = {"us": round(us, 2)}
+        if nbytes:
+            gbs = nbytes / (us * 1e-6) / 1e9
+            r.update({"bytes": nbytes, "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 3)})
+        out[k] = r
+    return out
+
+
 def window_variants(vs, torch, np, stream, steps: int = 20) -> dict:
     """The block pair on the Swin-T stage-1 token grid (1,16,56,56,96) with
     the other temporal windows of the window-size ablation, 4 and 16 (196 and
@@ -440,6 +483,7 @@ def main():
         "memory_kernels": memory_kernels(vs, torch, stream),
         "window_variants": window_variants(vs, torch, np, stream),
         "backward": backward_pair(vs, torch, np, x, w, s, shifts, stream),
+        "inference_head": inference_head(vs, torch, stream),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_np, params, s)

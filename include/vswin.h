@@ -272,6 +272,43 @@ vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, i
                                    const void* b, float eps, void* y, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Classification head (the 2D Swin page's global average pooling and linear
+ * classifier, taken over the 3D grid of final tokens): logits (B, K) fp32 =
+ * (mean over the L tokens of x (B, L, C), L = T' H' W', any token order)
+ * times w^T + b, with w (K, C) and b (K, nullable) in `dtype` like x (bf16 or
+ * fp32).  fp32 accumulation in a fixed order: repeated calls give identical
+ * bits.  C a multiple of 4 (<= 16384); pointers 16-byte aligned.  Needs a
+ * workspace of vswin_head_workspace() bytes (256-byte aligned).  Errors:
+ * VSWIN_ERR_INVALID_ARG (sizes, dtype, NULL or misaligned pointers),
+ * VSWIN_ERR_WORKSPACE (too small), VSWIN_ERR_HIP (launch).  B == 0 or
+ * K == 0 does nothing.                                                       */
+size_t vswin_head_workspace(int32_t B, int64_t L, int32_t C);
+vswin_status vswin_head_fwd(int32_t B, int64_t L, int32_t C, int32_t K, vswin_dtype dtype,
+                            const void* x, const void* w, const void* b, float* logits,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scores of several views of each video (temporal clips x spatial crops,
+ * Table 1 of the Video Swin Transformer page): probs (B, K) = the mean over
+ * the V views of softmax(logits[b, v, :]); logits (B, V, K) fp32 with the
+ * views of one video adjacent (a batch of B * V clips in video-major order).
+ * 1 <= V <= 4096.  Errors: VSWIN_ERR_INVALID_ARG, VSWIN_ERR_HIP.              */
+vswin_status vswin_multiview_average(int32_t B, int32_t V, int32_t K, const float* logits,
+                                     float* probs, void* stream);
+
+/* 2D -> 3D inflation of an image model (§3.4, initialisation from an image
+ * model).  Patch kernel: w3 (C, Cin, pt, ph, pw) = the 2D kernel w2
+ * (C, Cin, ph, pw) in each of the pt temporal slots, divided by pt (0.5 for
+ * the pages' pt = 2; fp32 division, bf16 rounded to nearest even).  Bias
+ * table: t3 ((2P-1) rows2d, heads) = the 2D table t2 (rows2d, heads),
+ * rows2d = (2Mh-1)(2Mw-1), repeated once per temporal offset with the
+ * temporal offset outermost, the row order of the block's own table, so every
+ * frame pair gets the 2D bias (a plain copy).  Caller-owned device buffers,
+ * 16-byte aligned.  Errors: VSWIN_ERR_INVALID_ARG, VSWIN_ERR_HIP.              */
+vswin_status vswin_inflate_patch_embed(int32_t C, int32_t Cin, int32_t pt, int32_t ph, int32_t pw,
+                                       vswin_dtype dtype, const void* w2, void* w3, void* stream);
+vswin_status vswin_inflate_bias_table(int32_t rows2d, int32_t heads, int32_t P, vswin_dtype dtype,
+                                      const void* t2, void* t3, void* stream);
+
 /* Measurement helper, not part of the block: launches `blocks` workgroups of
  * 512 threads that each issue `iters` rounds of 8 independent
  * v_mfma_f32_16x16x32_bf16 per wave (16384 FLOP each), so a caller timing it

@@ -25,6 +25,7 @@ __all__ = [
     "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
     "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd", "vswin_mfma_rate_probe",
     "BlockGrads", "vswin_bwd_workspace_query", "vswin_block_bwd", "vswin_window_msa_bwd",
+    "vswin_head_fwd", "vswin_multiview_average", "vswin_inflate_patch_embed", "vswin_inflate_bias_table",
     "F_PAD_VISIBLE", "F_CLAMP_STRICT", "F_MASK_M100", "F_TABLES_READY", "LIB_PATH",
 ]
 
@@ -103,6 +104,11 @@ def lib() -> ctypes.CDLL:
         "vswin_patch_merge_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "vswin_patch_merge_fwd": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp,
                                         vp, sz, vp]),
+        "vswin_head_workspace": (sz, [i32, i64, i32]),
+        "vswin_head_fwd": (i32, [i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "vswin_multiview_average": (i32, [i32, i32, i32, vp, vp, vp]),
+        "vswin_inflate_patch_embed": (i32, [i32, i32, i32, i32, i32, i32, vp, vp, vp]),
+        "vswin_inflate_bias_table": (i32, [i32, i32, i32, i32, vp, vp, vp]),
         "vswin_status_string": (ctypes.c_char_p, [i32]),
         "vswin_last_error": (ctypes.c_char_p, []),
         "vswin_abi_version": (i32, []),
@@ -377,6 +383,50 @@ def vswin_patch_merge_fwd(x: torch.Tensor, ln_g, ln_b, w, b=None, eps: float = 1
     _check(lib().vswin_patch_merge_fwd(B, T, H, W, C, Cout, dt, _ptr(x), _ptr(ln_g), _ptr(ln_b), _ptr(w),
                                        _ptr(b), eps, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def vswin_head_fwd(x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None, *, out=None,
+                   workspace=None, stream=None) -> torch.Tensor:
+    """Final tokens x (B, T', H', W', C) (or (B, L, C)), w (K, C), b (K) ->
+    logits (B, K) fp32: the mean over the tokens, then the linear classifier."""
+    B, C = x.shape[0], x.shape[-1]
+    L = 1
+    for n in x.shape[1:-1]:
+        L *= n
+    K = w.shape[0]
+    nbytes = lib().vswin_head_workspace(B, L, C)
+    ws = workspace if workspace is not None else torch.empty(max(nbytes, 256), dtype=torch.uint8,
+                                                             device=x.device)
+    y = out if out is not None else torch.empty((B, K), dtype=torch.float32, device=x.device)
+    _check(lib().vswin_head_fwd(B, L, C, K, _dt(x.dtype), _ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(ws),
+                                ws.numel(), _stream(stream)))
+    return y
+
+
+def vswin_multiview_average(logits: torch.Tensor, *, out=None, stream=None) -> torch.Tensor:
+    """logits (B, V, K) fp32 of V views per video -> (B, K): the mean of the
+    views' softmax probabilities."""
+    B, V, K = logits.shape
+    y = out if out is not None else torch.empty((B, K), dtype=torch.float32, device=logits.device)
+    _check(lib().vswin_multiview_average(B, V, K, _ptr(logits), _ptr(y), _stream(stream)))
+    return y
+
+
+def vswin_inflate_patch_embed(w2: torch.Tensor, pt: int, *, stream=None) -> torch.Tensor:
+    """2D patch kernel (C, Cin, ph, pw) -> 3D (C, Cin, pt, ph, pw), divided by pt."""
+    C, Cin, ph, pw = w2.shape
+    w3 = torch.empty((C, Cin, pt, ph, pw), dtype=w2.dtype, device=w2.device)
+    _check(lib().vswin_inflate_patch_embed(C, Cin, pt, ph, pw, _dt(w2.dtype), _ptr(w2), _ptr(w3),
+                                           _stream(stream)))
+    return w3
+
+
+def vswin_inflate_bias_table(t2: torch.Tensor, P: int, *, stream=None) -> torch.Tensor:
+    """2D relative-bias table (rows2d, heads) -> ((2P-1) rows2d, heads)."""
+    rows2d, heads = t2.shape
+    t3 = torch.empty(((2 * P - 1) * rows2d, heads), dtype=t2.dtype, device=t2.device)
+    _check(lib().vswin_inflate_bias_table(rows2d, heads, P, _dt(t2.dtype), _ptr(t2), _ptr(t3), _stream(stream)))
+    return t3
 
 
 def vswin_backbone_fwd(video: torch.Tensor, params: dict, cfg: dict, *, eps: float = 1e-5,

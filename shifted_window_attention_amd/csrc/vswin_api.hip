@@ -841,4 +841,66 @@ vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, i
   return VSWIN_OK;
 }
 
+
+size_t vswin_head_workspace(int32_t B, int64_t L, int32_t C) {
+  if (B < 0 || L < 1 || C < 1) return 0;
+  return align256((size_t)B * head_splits(B, L) * C * sizeof(float));
+}
+
+vswin_status vswin_head_fwd(int32_t B, int64_t L, int32_t C, int32_t K, vswin_dtype dtype, const void* x,
+                            const void* w, const void* b, float* logits, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (B < 0 || L < 1 || K < 0 || C < 4 || C % 4 || C > 16384)
+    return fail(VSWIN_ERR_INVALID_ARG, "head: B=%d L=%lld C=%d K=%d", B, (long long)L, C, K);
+  if (dtype != VSWIN_FP32 && dtype != VSWIN_BF16) return fail(VSWIN_ERR_INVALID_ARG, "bad dtype");
+  if (B == 0 || K == 0) return VSWIN_OK;
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(w, "w"));
+  CHECK(check_ptr(b, "b", true));
+  CHECK(check_ptr(logits, "logits"));
+  const size_t need = vswin_head_workspace(B, L, C);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(VSWIN_ERR_WORKSPACE, "head needs %zu workspace bytes", need);
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  HIPCHECK(head_fwd(dtype, x, w, b, logits, (float*)workspace, B, L, C, K, (hipStream_t)stream), "head");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_multiview_average(int32_t B, int32_t V, int32_t K, const float* logits, float* probs,
+                                     void* stream) {
+  if (B < 0 || V < 1 || V > view_avg_max_views() || K < 1)
+    return fail(VSWIN_ERR_INVALID_ARG, "multiview: B=%d V=%d K=%d (V <= %d)", B, V, K, view_avg_max_views());
+  if (B == 0) return VSWIN_OK;
+  CHECK(check_ptr(logits, "logits"));
+  CHECK(check_ptr(probs, "probs"));
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  HIPCHECK(view_avg(logits, probs, B, V, K, (hipStream_t)stream), "multiview average");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_inflate_patch_embed(int32_t C, int32_t Cin, int32_t pt, int32_t ph, int32_t pw,
+                                       vswin_dtype dtype, const void* w2, void* w3, void* stream) {
+  if (C < 1 || Cin < 1 || pt < 1 || ph < 1 || pw < 1)
+    return fail(VSWIN_ERR_INVALID_ARG, "inflate patch: C=%d Cin=%d patch=(%d,%d,%d)", C, Cin, pt, ph, pw);
+  if (dtype != VSWIN_FP32 && dtype != VSWIN_BF16) return fail(VSWIN_ERR_INVALID_ARG, "bad dtype");
+  CHECK(check_ptr(w2, "w2"));
+  CHECK(check_ptr(w3, "w3"));
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  HIPCHECK(inflate_patch(dtype, w2, w3, (int64_t)C * Cin, pt, ph, pw, (hipStream_t)stream), "inflate patch");
+  return VSWIN_OK;
+}
+
+vswin_status vswin_inflate_bias_table(int32_t rows2d, int32_t heads, int32_t P, vswin_dtype dtype, const void* t2,
+                                      void* t3, void* stream) {
+  if (rows2d < 1 || heads < 1 || P < 1)
+    return fail(VSWIN_ERR_INVALID_ARG, "inflate table: rows=%d heads=%d P=%d", rows2d, heads, P);
+  if (dtype != VSWIN_FP32 && dtype != VSWIN_BF16) return fail(VSWIN_ERR_INVALID_ARG, "bad dtype");
+  CHECK(check_ptr(t2, "t2"));
+  CHECK(check_ptr(t3, "t3"));
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  const int64_t halves = (int64_t)rows2d * heads * (dtype == VSWIN_FP32 ? 2 : 1);
+  HIPCHECK(inflate_table(t2, t3, halves, 2 * P - 1, (hipStream_t)stream), "inflate table");
+  return VSWIN_OK;
+}
+
 }  // extern "C"

@@ -173,4 +173,16 @@ hipError_t patch_gather(vswin_dtype dt, const void* video, void* out, int B, int
 hipError_t merge_gather(vswin_dtype dt, const void* x, void* out, int B, int T, int H, int W, int C,
                         hipStream_t st);
 
+// --- classification head, view average, inflation (k_head.hip) -------------
+// token-row splits of the head's pooling (partials: B * splits * C floats)
+int head_splits(int B, int64_t L);
+hipError_t head_fwd(vswin_dtype dt, const void* x, const void* w, const void* b, float* logits, float* part,
+                    int B, int64_t L, int C, int K, hipStream_t st);
+int view_avg_max_views();
+hipError_t view_avg(const float* logits, float* probs, int B, int V, int K, hipStream_t st);
+hipError_t inflate_patch(vswin_dtype dt, const void* w2, void* w3, int64_t C_Cin, int pt, int ph, int pw,
+                         hipStream_t st);
+// t3 = reps copies of t2 (n2_halves 2-byte units; fp32 tables pass 2x the count)
+hipError_t inflate_table(const void* t2, void* t3, int64_t n2_halves, int reps, hipStream_t st);
+
 }  // namespace vswin

@@ -196,3 +196,24 @@ def test_bwd_workspace_query_refuses_unsupported_shapes():
         with pytest.raises(vs.VswinError) as e:
             vs.vswin_bwd_workspace_query(d)
         assert e.value.status == -2
+
+
+def test_head_views_inflation_reject_bad_arguments():
+    """Argument checks of the inference entry points return before any device
+    work (no GPU needed)."""
+    L = vs.lib()
+    # head: C not a multiple of 4; negative K; bad dtype
+    assert L.vswin_head_fwd(1, 10, 6, 4, 0, None, None, None, None, None, 0, None) == -1
+    assert L.vswin_head_fwd(1, 10, 8, -1, 0, None, None, None, None, None, 0, None) == -1
+    assert L.vswin_head_fwd(1, 10, 8, 4, 7, None, None, None, None, None, 0, None) == -1
+    # empty batch or no classes: nothing to do
+    assert L.vswin_head_fwd(0, 10, 8, 4, 0, None, None, None, None, None, 0, None) == 0
+    assert L.vswin_head_fwd(1, 10, 8, 0, 0, None, None, None, None, None, 0, None) == 0
+    # views: too many views, no views
+    assert L.vswin_multiview_average(1, 4097, 10, None, None, None) == -1
+    assert L.vswin_multiview_average(1, 0, 10, None, None, None) == -1
+    assert L.vswin_multiview_average(0, 2, 10, None, None, None) == 0
+    # inflation: bad sizes
+    assert L.vswin_inflate_patch_embed(96, 3, 0, 4, 4, 0, None, None, None) == -1
+    assert L.vswin_inflate_bias_table(169, 3, 0, 0, None, None, None) == -1
+    assert L.vswin_head_workspace(2, 392, 768) >= 2 * 768 * 4
