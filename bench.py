@@ -294,6 +294,30 @@ def mfma_measured_peak(vs, torch, stream, iters: int = 4000) -> float:
     return flops / (e0.elapsed_time(e1) * 1e-3 / 5) / 1e12
 
 
+def issue_overlap(vs, torch, stream, iters: int = 2000) -> dict:
+    """us per launch of the library's MFMA / VALU overlap probe (4 waves per
+    SIMD): MFMA part only, VALU part only, the two split over the waves, both
+    in every wave.  serial_fraction = t_both / (t_mfma + t_valu): 1 when the
+    SIMD runs the two kinds of work back to back, max / sum when it overlaps
+    them fully."""
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    t = {}
+    for mode, name in enumerate(["mfma_us", "valu_us", "split_us", "both_us"]):
+        vs.vswin_issue_probe(out, blocks, iters, mode, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            vs.vswin_issue_probe(out, blocks, iters, mode, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t[name] = round(e0.elapsed_time(e1) * 1e3 / 3, 1)
+    t["serial_fraction"] = round(t["both_us"] / (t["mfma_us"] + t["valu_us"]), 3)
+    t["full_overlap_would_be"] = round(max(t["mfma_us"], t["valu_us"]) / (t["mfma_us"] + t["valu_us"]), 3)
+    return t
+
+
 def step_percentiles(step, torch, stream, n: int, scrub=None) -> dict:
     """Per-step times (ms) from HIP events around each step; with `scrub` (a
     callable run between steps, outside the events) the caches start cold."""
@@ -464,7 +488,8 @@ def main():
                 "frac_of_measured_peak": round(achieved / measured_peak, 4),
                 "kernel": "attn_mfma_kernel", "avg_us": round(attn_us, 3),
                 "avg_us_regular": round(kern_us[0], 3), "avg_us_shifted": round(kern_us[1], 3),
-                "flops_per_launch": attn_flops}
+                "flops_per_launch": attn_flops,
+                "mfma_valu_issue": issue_overlap(vs, torch, stream)}
 
     out = {
         "metric": METRIC, "value": round(tokens_per_step / (ms * 1e-3), 1), "unit": "tokens/s",

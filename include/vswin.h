@@ -318,6 +318,17 @@ vswin_status vswin_inflate_bias_table(int32_t rows2d, int32_t heads, int32_t P, 
  * iters < 1 or a NULL / unaligned out; VSWIN_ERR_HIP for a launch failure.    */
 vswin_status vswin_mfma_rate_probe(float* out, int32_t blocks, int32_t iters, void* stream);
 
+/* Measurement helper, not part of the block: whether MFMA and VALU work
+ * overlap on a SIMD.  `blocks` workgroups of 512 threads run `iters` rounds;
+ * per round a wave issues 8 independent v_mfma_f32_16x16x32_bf16 (mode 0),
+ * 8 independent v_exp_f32 + v_fma_f32 pairs (mode 1), one of the two by wave
+ * parity (mode 2), or both (mode 3).  The caller times the launches: with
+ * concurrent units mode 3 would take max(t0, t1), run back to back t0 + t1.
+ * out: device buffer of blocks * 512 floats (values meaningless).  Errors:
+ * VSWIN_ERR_INVALID_ARG (blocks, iters < 1, mode outside 0..3, NULL or
+ * unaligned out), VSWIN_ERR_HIP.                                              */
+vswin_status vswin_issue_probe(float* out, int32_t blocks, int32_t iters, int32_t mode, void* stream);
+
 const char* vswin_status_string(vswin_status s);
 const char* vswin_last_error(void);
 int32_t vswin_abi_version(void);

@@ -24,6 +24,7 @@ __all__ = [
     "vswin_index_map",
     "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
     "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd", "vswin_mfma_rate_probe",
+    "vswin_issue_probe",
     "BlockGrads", "vswin_bwd_workspace_query", "vswin_block_bwd", "vswin_window_msa_bwd",
     "vswin_head_fwd", "vswin_multiview_average", "vswin_inflate_patch_embed", "vswin_inflate_bias_table",
     "F_PAD_VISIBLE", "F_CLAMP_STRICT", "F_MASK_M100", "F_TABLES_READY", "LIB_PATH",
@@ -113,6 +114,7 @@ def lib() -> ctypes.CDLL:
         "vswin_last_error": (ctypes.c_char_p, []),
         "vswin_abi_version": (i32, []),
         "vswin_mfma_rate_probe": (i32, [vp, i32, i32, vp]),
+        "vswin_issue_probe": (i32, [vp, i32, i32, i32, vp]),
         "vswin_bwd_workspace_query": (i32, [pdesc, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "vswin_block_bwd": (i32, [pdesc, vp, pw, vp, vp, ctypes.POINTER(BlockGrads), vp, sz, vp]),
         "vswin_window_msa_bwd": (i32, [pdesc, vp, pw, vp, vp, ctypes.POINTER(BlockGrads), vp, sz, vp]),
@@ -344,6 +346,14 @@ def vswin_mfma_rate_probe(out: torch.Tensor, blocks: int, iters: int, stream=Non
         raise ValueError("out must be float32 with at least blocks * 512 elements")
     _check(lib().vswin_mfma_rate_probe(_ptr(out), blocks, iters, _stream(stream)))
     return blocks * 8 * 8 * iters * 16384
+
+
+def vswin_issue_probe(out: torch.Tensor, blocks: int, iters: int, mode: int, stream=None) -> None:
+    """Launch the MFMA / VALU overlap probe (measurement helper; see
+    include/vswin.h).  out: float32 device tensor of >= blocks * 512 elements."""
+    if out.dtype != torch.float32 or out.numel() < blocks * 512:
+        raise ValueError("out must be float32 with at least blocks * 512 elements")
+    _check(lib().vswin_issue_probe(_ptr(out), blocks, iters, mode, _stream(stream)))
 
 
 def vswin_layernorm_fwd(x: torch.Tensor, g: torch.Tensor, b: torch.Tensor, eps: float = 1e-5,

@@ -697,6 +697,14 @@ vswin_status vswin_mfma_rate_probe(float* out, int32_t blocks, int32_t iters, vo
   return VSWIN_OK;
 }
 
+vswin_status vswin_issue_probe(float* out, int32_t blocks, int32_t iters, int32_t mode, void* stream) {
+  if (blocks < 1 || iters < 1 || mode < 0 || mode > 3)
+    return fail(VSWIN_ERR_INVALID_ARG, "blocks=%d iters=%d mode=%d", blocks, iters, mode);
+  CHECK(check_ptr(out, "out"));
+  HIPCHECK(issue_probe(out, blocks, iters, mode, (hipStream_t)stream), "issue probe");
+  return VSWIN_OK;
+}
+
 vswin_status vswin_index_map(const vswin_desc* desc, int32_t* map, uint8_t* region, void* stream) {
   Plan p{};
   CHECK(make_plan(desc, p, false));

@@ -165,6 +165,7 @@ hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part
 // --- measurement helper (k_probe.hip) --------------------------------------
 // blocks x 512 threads of v_mfma_f32_16x16x32_bf16 chains: 8 per wave per
 // round, `iters` rounds; out holds blocks * 512 floats
+hipError_t issue_probe(float* out, int blocks, int iters, int mode, hipStream_t st);
 hipError_t mfma_rate(float* out, int blocks, int iters, hipStream_t st);
 
 // --- patch embedding / merging gathers (k_patch.hip) ----------------------
