@@ -277,7 +277,7 @@ vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, i
  * (mean over the L tokens of x (B, L, C), L = T' H' W', any token order)
  * times w^T + b, with w (K, C) and b (K, nullable) in `dtype` like x (bf16 or
  * fp32).  fp32 accumulation in a fixed order: repeated calls give identical
- * bits.  C a multiple of 4 (<= 16384); pointers 16-byte aligned.  Needs a
+ * bits.  C a multiple of 4 (<= 4096); pointers 16-byte aligned.  Needs a
  * workspace of vswin_head_workspace() bytes (256-byte aligned).  Errors:
  * VSWIN_ERR_INVALID_ARG (sizes, dtype, NULL or misaligned pointers),
  * VSWIN_ERR_WORKSPACE (too small), VSWIN_ERR_HIP (launch).  B == 0 or

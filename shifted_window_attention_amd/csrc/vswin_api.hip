@@ -852,13 +852,13 @@ vswin_status vswin_patch_merge_fwd(int32_t B, int32_t T, int32_t H, int32_t W, i
 
 size_t vswin_head_workspace(int32_t B, int64_t L, int32_t C) {
   if (B < 0 || L < 1 || C < 1) return 0;
-  return align256((size_t)B * head_splits(B, L) * C * sizeof(float));
+  return align256(head_workspace_floats(B, L, C) * sizeof(float));
 }
 
 vswin_status vswin_head_fwd(int32_t B, int64_t L, int32_t C, int32_t K, vswin_dtype dtype, const void* x,
                             const void* w, const void* b, float* logits, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  if (B < 0 || L < 1 || K < 0 || C < 4 || C % 4 || C > 16384)
+  if (B < 0 || L < 1 || K < 0 || C < 4 || C % 4 || C > 4096)
     return fail(VSWIN_ERR_INVALID_ARG, "head: B=%d L=%lld C=%d K=%d", B, (long long)L, C, K);
   if (dtype != VSWIN_FP32 && dtype != VSWIN_BF16) return fail(VSWIN_ERR_INVALID_ARG, "bad dtype");
   if (B == 0 || K == 0) return VSWIN_OK;

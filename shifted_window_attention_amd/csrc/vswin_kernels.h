@@ -175,9 +175,11 @@ hipError_t merge_gather(vswin_dtype dt, const void* x, void* out, int B, int T, 
                         hipStream_t st);
 
 // --- classification head, view average, inflation (k_head.hip) -------------
-// token-row splits of the head's pooling (partials: B * splits * C floats)
+// token-row splits of the head's pooling; its fp32 workspace (partial sums,
+// then the pooled vectors)
 int head_splits(int B, int64_t L);
-hipError_t head_fwd(vswin_dtype dt, const void* x, const void* w, const void* b, float* logits, float* part,
+size_t head_workspace_floats(int B, int64_t L, int C);
+hipError_t head_fwd(vswin_dtype dt, const void* x, const void* w, const void* b, float* logits, float* work,
                     int B, int64_t L, int C, int K, hipStream_t st);
 int view_avg_max_views();
 hipError_t view_avg(const float* logits, float* probs, int B, int V, int K, hipStream_t st);

@@ -216,4 +216,4 @@ def test_head_views_inflation_reject_bad_arguments():
     # inflation: bad sizes
     assert L.vswin_inflate_patch_embed(96, 3, 0, 4, 4, 0, None, None, None) == -1
     assert L.vswin_inflate_bias_table(169, 3, 0, 0, None, None, None) == -1
-    assert L.vswin_head_workspace(2, 392, 768) >= 2 * 768 * 4
+    assert L.vswin_head_workspace(2, 392, 768) >= 2 * 768 * 4 * 2
