@@ -44,7 +44,11 @@ def stats(stats_dir: str) -> str:
            "-100 mask: `Cfg<8, 4, false, true, false>`), each 23 block pairs and 21 standalone attention launches;",
            "the main workload's attention is `Cfg<8, 4, false, false, false>`; then 11 backward block pairs",
            "(`vswin_block_bwd`: the forward recomputed, then the `attn_bwd_*`, `wgrad_kernel`, `ln_bwd_kernel`, GELU",
-           "and GEMM kernels of the backward). Other torch kernels are input generation.", "",
+           "and GEMM kernels of the backward); then the inference pieces, 23 launches each (the head's",
+           "`head_pool_kernel` / `head_reduce_kernel` / `head_fc_kernel` on 24 clips of (16,7,7,768) tokens,",
+           "`view_avg_kernel`, `inflate_patch_kernel`, `inflate_table_kernel`), and the MFMA / VALU overlap probe",
+           "(`issue_probe_kernel`, 4 modes x 4 launches) next to the MFMA rate probe (`mfma_rate_kernel`). Other",
+           "torch kernels are input generation.", "",
            "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
