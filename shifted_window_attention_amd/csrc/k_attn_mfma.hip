@@ -851,6 +851,9 @@ struct BwdL {
   int gf;                     // windows over 512 tokens: row fragments read from global memory (L2), not LDS
   // kernel B LDS
   uint32_t b_k, b_v, b_kt, b_lds;
+  // workgroups per (head, window) item of kernels A and B: part p owns tiles
+  // p, p + parts, ... (more than one when that evens out the workgroups per CU)
+  int parts;
 };
 
 __device__ __forceinline__ void stage_rows16(const bf16_t* src, unsigned char* dst, int nrows, int wv, int nw) {
@@ -924,7 +927,12 @@ __device__ __forceinline__ float pair_p(bool in_range, bool same, int m100, floa
 __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const AttnBwdArgs b, const BwdL BL) {
   const A5& L = BL.L;
   __shared__ __attribute__((aligned(16))) bf16_t tile[64 * 40];
-  const int mem = blockIdx.x;
+  // workgroup: one (item, tensor, 64-row block), so that the blocks' loads are
+  // in flight together instead of one after the other
+  const int nrb = (L.NPAD + 63) / 64;
+  const int mem = blockIdx.x / (4 * nrb);
+  const int which = (blockIdx.x / nrb) % 4;
+  const int r0 = (blockIdx.x % nrb) * 64;
   const int w = (int)fdiv((uint32_t)mem, L.fdH), h = mem - w * L.heads;
   const int N = L.N, NPAD = L.NPAD, C = b.a.C;
   const int t = threadIdx.x;
@@ -933,10 +941,10 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const AttnBwdArgs b,
   const bf16_t* vt = reinterpret_cast<const bf16_t*>(b.a.v);
   const bf16_t* o = reinterpret_cast<const bf16_t*>(b.a.o);
   const bf16_t* dout = reinterpret_cast<const bf16_t*>(b.dout);
-  for (int which = 0; which < 4; ++which) {   // q', k, dO (+ D), v
+  {   // which: q', k, dO (+ D), v
     bf16_t* rows = which == 0 ? b.qr : which == 1 ? b.kr : which == 2 ? b.dor : b.vr;
     bf16_t* tr = which == 0 ? b.qt : which == 1 ? b.kt : b.dot;
-    for (int r0 = 0; r0 < NPAD; r0 += 64) {
+    {
       if (which < 3) {
         // thread t: row r0 + t / 4, 8 channels 8 (t % 4) ..
         const int r = r0 + (t >> 2), c = t & 3;
@@ -1006,7 +1014,8 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
   const A5& L = BL.L;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, fr = lane & 15, g4 = lane >> 4;
-  const Win wi = window_of(b.a, L, blockIdx.x);
+  const int part = (int)blockIdx.x % BL.parts;
+  const Win wi = window_of(b.a, L, (int)blockIdx.x / BL.parts);
   const int mem = wi.mem, h = wi.h;
   const int N = L.N, NPAD = L.NPAD, Rp = L.Rp;
   const int ng = N / 4;   // key / query groups of 4 temporal positions
@@ -1032,7 +1041,7 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
   const int sw = (fr >> 2) & 3;
   bf16_t* dqkv = b.dqkv;
   const int C = b.a.C;
-  for (int kt = wv; kt * 16 < N; kt += CF::kWaves) {
+  for (int kt = part + BL.parts * wv; kt * 16 < N; kt += BL.parts * CF::kWaves) {
     const int key = kt * 16 + fr;
     const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(b.kr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
     const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(b.vr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
@@ -1136,7 +1145,8 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
   const A5& L = BL.L;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, fr = lane & 15, g4 = lane >> 4;
-  const Win wi = window_of(b.a, L, blockIdx.x);
+  const int part = (int)blockIdx.x % BL.parts;
+  const Win wi = window_of(b.a, L, (int)blockIdx.x / BL.parts);
   const int mem = wi.mem, h = wi.h;
   const int N = L.N, NPAD = L.NPAD, Rp = L.Rp;
   int* kp = reinterpret_cast<int*>(smem + L.off_kp);
@@ -1155,7 +1165,7 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
   const unsigned char* tabb = smem;
   const int sw = (fr >> 2) & 3;
   const int C = b.a.C;
-  for (int qt = wv; qt * 16 < N; qt += CF::kWaves) {
+  for (int qt = part + BL.parts * wv; qt * 16 < N; qt += BL.parts * CF::kWaves) {
     const int q = qt * 16 + fr;
     const bool qval = q < N;
     const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(b.qr + ((int64_t)mem * NPAD + q) * 32 + 8 * g4);
@@ -1222,9 +1232,20 @@ __global__ void __launch_bounds__(256) attn_bwd_grp_sum_kernel(const float* __re
   const int h = blockIdx.y;
   const int64_t e = blockIdx.x * 256 + (int64_t)threadIdx.x;
   if (e >= E) return;
-  float s = 0.f;
-  for (int64_t w = 0; w < nW; ++w) s += dgrp[(w * heads + h) * E + e];
-  gsum[(int64_t)h * E + e] = s;
+  // four partial sums (windows w mod 4), combined in a fixed order
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  const float* p = dgrp + (int64_t)h * E + e;
+  const int64_t stride = (int64_t)heads * E;
+  int64_t w = 0;
+#pragma unroll 2
+  for (; w + 4 <= nW; w += 4) {
+    s0 += p[w * stride];
+    s1 += p[(w + 1) * stride];
+    s2 += p[(w + 2) * stride];
+    s3 += p[(w + 3) * stride];
+  }
+  for (; w < nW; ++w) s0 += p[w * stride];
+  gsum[(int64_t)h * E + e] = (s0 + s1) + (s2 + s3);
 }
 
 // Table gradient in the scalar index space: entry y = (dt + TD/2) Rp +
@@ -1353,6 +1374,22 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
   BwdL B;
   if (!plan_bwd(in.a, B) || !in.work || !in.dtable || !in.lse) return hipErrorInvalidValue;
   const A5& L = B.L;
+  {
+    // one workgroup per CU at a time (LDS): split the items so that the last
+    // round of workgroups is as full as the others, when that shortens the
+    // launch (e.g. 384 items on 256 CUs: 2 rounds of whole items against 3
+    // rounds of halves, 1.5 items long)
+    const int64_t cus = device_cu_count();
+    B.parts = 1;
+    double best = (double)((items + cus - 1) / cus);
+    for (int p = 2; p <= 4; ++p) {
+      const double t = (double)((items * p + cus - 1) / cus) / p;
+      if (t < best - 1e-9 && (L.N + 15) / 16 >= p * 8) {
+        best = t;
+        B.parts = p;
+      }
+    }
+  }
   AttnBwdArgs b = in;
   char* w = reinterpret_cast<char*>(in.work);
   const size_t arr = ((size_t)items * L.NPAD * 32 * 2 + 255) & ~(size_t)255;
@@ -1373,14 +1410,14 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
   if (items <= 0) return hipSuccess;
   attn_table_kernel<<<dim3((unsigned)((L.TS4 + 255) / 256), (unsigned)L.heads), dim3(256), 0, st>>>(
       reinterpret_cast<const bf16_t*>(in.a.table), reinterpret_cast<f32x4_t*>(b.a.tab4), L);
-  attn_bwd_prep_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(b, B);
+  attn_bwd_prep_kernel<<<dim3((unsigned)(items * 4 * ((L.NPAD + 63) / 64))), dim3(256), 0, st>>>(b, B);
   auto run = [&](auto kv, auto qk) -> hipError_t {
     hipError_t e = ensure_dynamic_lds((const void*)kv, B.a_lds);
     if (e != hipSuccess) return e;
     e = ensure_dynamic_lds((const void*)qk, B.b_lds);
     if (e != hipSuccess) return e;
-    kv<<<dim3((unsigned)items), dim3(512), B.a_lds, st>>>(b, B);
-    qk<<<dim3((unsigned)items), dim3(512), B.b_lds, st>>>(b, B);
+    kv<<<dim3((unsigned)(items * B.parts)), dim3(512), B.a_lds, st>>>(b, B);
+    qk<<<dim3((unsigned)(items * B.parts)), dim3(512), B.b_lds, st>>>(b, B);
     return hipGetLastError();
   };
   const bool uni = groups_uniform(in.a);
