@@ -195,12 +195,37 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
   for (int i = threadIdx.x; i < 2 * C; i += 256) part[(int64_t)blockIdx.x * 2 * C + i] = red[i];
 }
 
+// An 8 x 8 block of bf16 rows (8 tokens m0 .. m0 + 7 of row pitch ld, 8
+// channels from column c0) into LDS transposed: channel rows r0 .. r0 + 7
+// (pitch kWgPitch), tokens t0 .. t0 + 7.  Each output dword pairs one
+// channel of two consecutive tokens (a byte permute of the two tokens'
+// dwords); rows past M are zero.
+__device__ __forceinline__ void stage_t8x8(const bf16_t* __restrict__ X, int64_t ld, int64_t m0, int64_t M, int c0,
+                                           bf16_t* dst, int r0, int t0) {
+  u32x4_t r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    r[i] = m0 + i < M ? *reinterpret_cast<const u32x4_t*>(X + (m0 + i) * ld + c0) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {   // input dword j: channels 2j (low half), 2j + 1 (high half)
+    u32x4_t lo, hi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {   // output dword q: tokens 2q (low half), 2q + 1 (high half)
+      lo[q] = __builtin_amdgcn_perm(r[2 * q + 1][j], r[2 * q][j], 0x05040100u);
+      hi[q] = __builtin_amdgcn_perm(r[2 * q + 1][j], r[2 * q][j], 0x07060302u);
+    }
+    *reinterpret_cast<u32x4_t*>(dst + (r0 + 2 * j) * kWgPitch + t0) = lo;
+    *reinterpret_cast<u32x4_t*>(dst + (r0 + 2 * j + 1) * kWgPitch + t0) = hi;
+  }
+}
+
 // Weight-gradient partials: part[p] (NO x KI) = sum over the tokens of
 // chunks p, p + P, ... of A[m, n] * B[m, k]; colp[p] (NO) = sum of A[m, n]
 // (written by the k-block-0 workgroups).  A: (M, NO), B: (M, KI), bf16 rows.
 // Workgroup tile BN n x BK k, 4 waves sharing the (BN/16) (BK/16) output
-// tiles; MFMA A operand = A^T rows (n) and B operand = B^T rows (k), both
-// token-contiguous in LDS.  Larger tiles re-read the operands fewer times.
+// tiles in 2 x 2 blocks; MFMA A operand = A^T rows (n) and B operand = B^T
+// rows (k), both token-contiguous in LDS.  Larger tiles re-read the operands
+// fewer times.
 template <int BN, int BK>
 __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
                                                     float* __restrict__ part, float* __restrict__ colp, int64_t M,
@@ -216,9 +241,12 @@ __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A
   const int n0 = nb * BN, k0 = kb * BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g4 = lane >> 4;
-  constexpr int NT = (BN / 16) * (BK / 16);
-  static_assert(NT % 4 == 0, "output tiles split over 4 waves");
-  constexpr int TPW = NT / 4;
+  // the (BN/16) x (BK/16) output tiles as 2 x 2 blocks of TN x TK tiles, one
+  // block per wave: per 32-token step a wave reads TN A and TK B fragments
+  // for its TN TK MFMAs
+  static_assert(BN % 32 == 0 && BK % 32 == 0, "2 x 2 wave blocks of 16 x 16 tiles");
+  constexpr int TN = BN / 32, TK = BK / 32, TPW = TN * TK;
+  const int nt0 = (wave & 1) * TN, kt0 = (wave >> 1) * TK;
   constexpr int CSG = BN <= 32 ? 8 : (BN <= 64 ? 4 : 2);   // threads per column of the bias sums
   static_assert(BN * CSG <= 256, "column-sum threads");
   f32x4_t acc[TPW];
@@ -227,40 +255,37 @@ __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A
   float cs = 0.f;
   const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
   for (int64_t ch = p; ch < nchunks; ch += nparts) {
-    const int64_t m = ch * kWgChunk + tid;
+    const int64_t mc = ch * kWgChunk;
     __syncthreads();
-    // thread -> token tid: BN / 8 chunks of A, BK / 8 of B, transposed into LDS
-#pragma unroll
-    for (int c = 0; c < BN / 8; ++c) {
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (m < M) v = *reinterpret_cast<const u32x4_t*>(A + m * NO + n0 + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        At[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
-        At[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < BK / 8; ++c) {
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (m < M) v = *reinterpret_cast<const u32x4_t*>(B + m * KI + k0 + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Bt[(8 * c + 2 * e) * kWgPitch + tid] = (bf16_t)(v[e] & 0xffffu);
-        Bt[(8 * c + 2 * e + 1) * kWgPitch + tid] = (bf16_t)(v[e] >> 16);
+    // the chunk's 256 tokens of A (BN channels) and B (BK channels) into LDS,
+    // transposed in 8 x 8 blocks; consecutive threads take consecutive
+    // channel blocks of the same 8 tokens (coalesced 16-byte loads)
+    constexpr int NBA = (BN / 8) * (kWgChunk / 8), NBB = (BK / 8) * (kWgChunk / 8);
+    for (int bI = tid; bI < NBA + NBB; bI += 256) {
+      if (bI < NBA) {
+        const int cb = bI % (BN / 8), tb = bI / (BN / 8);
+        stage_t8x8(A, NO, mc + 8 * tb, M, n0 + 8 * cb, At, 8 * cb, 8 * tb);
+      } else {
+        const int b2 = bI - NBA;
+        const int cb = b2 % (BK / 8), tb = b2 / (BK / 8);
+        stage_t8x8(B, KI, mc + 8 * tb, M, k0 + 8 * cb, Bt, 8 * cb, 8 * tb);
       }
     }
     __syncthreads();
+#pragma unroll 2
+    for (int s = 0; s < kWgChunk / 32; ++s) {
+      bf16x8_t a[TN], b[TK];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tile = wave * TPW + i;
-      const int nt = tile % (BN / 16), kt = tile / (BN / 16);
-#pragma unroll 4
-      for (int s = 0; s < kWgChunk / 32; ++s) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(At + (16 * nt + fr) * kWgPitch + 32 * s + 8 * g4);
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(Bt + (16 * kt + fr) * kWgPitch + 32 * s + 8 * g4);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
-      }
+      for (int i = 0; i < TN; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(At + (16 * (nt0 + i) + fr) * kWgPitch + 32 * s + 8 * g4);
+#pragma unroll
+      for (int j = 0; j < TK; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(Bt + (16 * (kt0 + j) + fr) * kWgPitch + 32 * s + 8 * g4);
+#pragma unroll
+      for (int j = 0; j < TK; ++j)
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+          acc[j * TN + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[j * TN + i], 0, 0, 0);
     }
     if (kb == 0 && tid < BN * CSG) {
       // column sums: thread -> n = tid / CSG, tokens (tid % CSG) * 256 / CSG ..
@@ -273,8 +298,7 @@ __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A
   // lane: n = n0 + 16 nt + 4 g4 + r, k = k0 + 16 kt + fr
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    const int tile = wave * TPW + i;
-    const int nt = tile % (BN / 16), kt = tile / (BN / 16);
+    const int nt = nt0 + i % TN, kt = kt0 + i / TN;
     const int k = k0 + 16 * kt + fr;
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[((int64_t)p * NO + n0 + 16 * nt + 4 * g4 + r) * KI + k] = acc[i][r];
