@@ -856,6 +856,18 @@ struct BwdL {
   int parts;
 };
 
+// Stored diagonal sums of dS per item: record (query group mq, key group mk)
+// of 7 floats (temporal diagonals -3 .. 3) at ((mk / 4) ng + mq) 4 + mk % 4,
+// ng = N / 4 groups: a key tile's 4 key groups and 4 consecutive query groups
+// are 16 adjacent records, one contiguous store per wave and step.
+__host__ __device__ __forceinline__ int64_t dgrp_floats(int N) {
+  const int ng = N / 4;
+  return (int64_t)((ng + 3) / 4) * ng * 4 * 7;
+}
+__host__ __device__ __forceinline__ int64_t dgrp_rec(int ng, int mq, int mk) {
+  return ((int64_t)(mk >> 2) * ng + mq) * 4 + (mk & 3);
+}
+
 __device__ __forceinline__ void stage_rows16(const bf16_t* src, unsigned char* dst, int nrows, int wv, int nw) {
   const int lane = threadIdx.x & 63;
   const int off = (lane >> 2) * 32 + (((lane & 3) ^ ((lane >> 4) & 3)) << 3);
@@ -1102,9 +1114,7 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
         }
         const int mq = (qs0 >> 2) + g4, mk = 4 * kt + (fr >> 2);
         if (mq < ng && mk < ng) {
-          const int aq = (int)fdiv((uint32_t)mq, b.a.geo.fmhw), ak = (int)fdiv((uint32_t)mk, b.a.geo.fmhw);
-          float* dp7 = b.dgrp + (((int64_t)mem * BL.ap * BL.ap + aq * BL.ap + ak) * BL.mhw + (mq - aq * BL.mhw)) *
-                                    BL.mhw * 7 + (mk - ak * BL.mhw) * 7;
+          float* dp7 = b.dgrp + (int64_t)mem * dgrp_floats(N) + dgrp_rec(ng, mq, mk) * 7;
           dp7[kk] = mine0;
           if (kk < 3) dp7[kk + 4] = mine1;
         }
@@ -1224,7 +1234,7 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
 }
 
 // Sum of the stored diagonal sums over the windows of each head: gsum[h][e]
-// = sum_w dgrp[(w heads + h) E + e], E = (P/4)^2 (Mh Mw)^2 7 (coalesced:
+// = sum_w dgrp[(w heads + h) E + e], E = dgrp_floats(N) (coalesced:
 // consecutive threads take consecutive e).
 __global__ void __launch_bounds__(256) attn_bwd_grp_sum_kernel(const float* __restrict__ dgrp,
                                                                 float* __restrict__ gsum, int64_t nW, int heads,
@@ -1265,8 +1275,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dtab_gather_kernel(const float* 
   if (y >= nd) return;
   const int u = y / L.Rp, rem = y - u * L.Rp;
   const int v = rem / L.Rw, x = rem - v * L.Rw;
-  const int64_t E = (int64_t)BL.ap * BL.ap * BL.mhw * BL.mhw * 7;
-  const float* gs = gsum + (int64_t)h * E;
+  const int ng = L.N / 4;
+  const float* gs = gsum + (int64_t)h * dgrp_floats(L.N);
   float s = 0.f;
   if (rem < L.R) {
     const int dt = u - L.TD / 2, dh = v - L.TH / 2, dw = x - L.Rw / 2;
@@ -1278,7 +1288,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dtab_gather_kernel(const float* 
       for (int aq = 0; aq < BL.ap; ++aq)
         for (int ak = 0; ak < BL.ap; ++ak) {
           const int dd = dt - 4 * (ak - aq);
-          if (dd >= -3 && dd <= 3) s += gs[(((int64_t)(aq * BL.ap + ak) * BL.mhw + cq) * BL.mhw + ck) * 7 + dd + 3];
+          if (dd >= -3 && dd <= 3) s += gs[dgrp_rec(ng, aq * BL.mhw + cq, ak * BL.mhw + ck) * 7 + dd + 3];
         }
     }
   }
@@ -1364,8 +1374,8 @@ size_t attention_bwd_workspace_bytes(const AttnArgs& a) {
   const size_t D = ((size_t)items * L.NPAD * 4 + 255) & ~(size_t)255;
   const size_t tabs = ((size_t)a.heads * L.TS4 * 16 + 255) & ~(size_t)255;
   const size_t dtab = ((size_t)a.heads * L.TD * L.Rp * 4 + 255) & ~(size_t)255;
-  const size_t grp = ((size_t)items * B.ap * B.ap * B.mhw * B.mhw * 7 * 4 + 255) & ~(size_t)255;
-  const size_t gsum = ((size_t)a.heads * B.ap * B.ap * B.mhw * B.mhw * 7 * 4 + 255) & ~(size_t)255;
+  const size_t grp = ((size_t)items * dgrp_floats(a.N) * 4 + 255) & ~(size_t)255;
+  const size_t gsum = ((size_t)a.heads * dgrp_floats(a.N) * 4 + 255) & ~(size_t)255;
   return 7 * arr + D + tabs + dtab + grp + gsum;
 }
 
@@ -1403,7 +1413,7 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
   b.dtab = reinterpret_cast<float*>(w + off);
   off += ((size_t)in.a.heads * L.TD * L.Rp * 4 + 255) & ~(size_t)255;
   b.dgrp = reinterpret_cast<float*>(w + off);
-  off += ((size_t)items * B.ap * B.ap * B.mhw * B.mhw * 7 * 4 + 255) & ~(size_t)255;
+  off += ((size_t)items * dgrp_floats(in.a.N) * 4 + 255) & ~(size_t)255;
   float* gsum = reinterpret_cast<float*>(w + off);
   b.dq_scale = 1.0f / sqrtf((float)in.a.d);
   b.dk_scale = 1.0f / kLog2e;
@@ -1429,7 +1439,7 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
     e = uni ? run(attn_bwd_kv_kernel<BwdCF, false>, attn_bwd_q_kernel<BwdCF, false>)
             : run(attn_bwd_kv_kernel<BwdCFKey, false>, attn_bwd_q_kernel<BwdCFKey, false>);
   if (e != hipSuccess) return e;
-  const int64_t E = (int64_t)B.ap * B.ap * B.mhw * B.mhw * 7;
+  const int64_t E = dgrp_floats(in.a.N);
   attn_bwd_grp_sum_kernel<<<dim3((unsigned)((E + 255) / 256), (unsigned)in.a.heads), dim3(256), 0, st>>>(
       b.dgrp, gsum, in.a.nW, in.a.heads, E);
   const int nd = L.TD * L.Rp;
