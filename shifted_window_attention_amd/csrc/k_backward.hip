@@ -219,17 +219,18 @@ __device__ __forceinline__ void stage_t8x8(const bf16_t* __restrict__ X, int64_t
   }
 }
 
-// Weight-gradient partials: part[p] (NO x KI) = sum over the tokens of
-// chunks p, p + P, ... of A[m, n] * B[m, k]; colp[p] (NO) = sum of A[m, n]
-// (written by the k-block-0 workgroups).  A: (M, NO), B: (M, KI), bf16 rows.
+// Weight-gradient partials, one row of NO KI + NO floats per part p: the
+// NO x KI sums over the tokens of chunks p, p + P, ... of A[m, n] * B[m, k],
+// then the NO column sums of A (written by the k-block-0 workgroups).
+// A: (M, NO), B: (M, KI), bf16 rows.
 // Workgroup tile BN n x BK k, 4 waves sharing the (BN/16) (BK/16) output
 // tiles in 2 x 2 blocks; MFMA A operand = A^T rows (n) and B operand = B^T
 // rows (k), both token-contiguous in LDS.  Larger tiles re-read the operands
 // fewer times.
 template <int BN, int BK>
 __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-                                                    float* __restrict__ part, float* __restrict__ colp, int64_t M,
-                                                    int NO, int KI, int nparts) {
+                                                    float* __restrict__ part, int64_t M, int NO, int KI,
+                                                    int nparts) {
   extern __shared__ __attribute__((aligned(16))) unsigned char wg_lds[];
   bf16_t* At = reinterpret_cast<bf16_t*>(wg_lds);
   bf16_t* Bt = At + BN * kWgPitch;
@@ -296,28 +297,32 @@ __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A
     }
   }
   // lane: n = n0 + 16 nt + 4 g4 + r, k = k0 + 16 kt + fr
+  float* prow = part + (int64_t)p * ((int64_t)NO * KI + NO);
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int nt = nt0 + i % TN, kt = kt0 + i / TN;
     const int k = k0 + 16 * kt + fr;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[((int64_t)p * NO + n0 + 16 * nt + 4 * g4 + r) * KI + k] = acc[i][r];
+    for (int r = 0; r < 4; ++r) prow[(int64_t)(n0 + 16 * nt + 4 * g4 + r) * KI + k] = acc[i][r];
   }
   if (kb == 0) {
 #pragma unroll
     for (int o = 1; o < CSG; o <<= 1) cs += __shfl_xor(cs, o);
-    if (tid % CSG == 0 && tid < BN * CSG) colp[(int64_t)p * NO + n0 + tid / CSG] = cs;
+    if (tid % CSG == 0 && tid < BN * CSG) prow[(int64_t)NO * KI + n0 + tid / CSG] = cs;
   }
 }
 
-// out[i] = sum_p part[p * stride + i], i < n
+// s_i = sum_p part[p * stride + i], i < n; out[i] = s_i for i < n1, else
+// out2[i - n1]
 __global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restrict__ part, float* __restrict__ out,
-                                                           int nparts, int64_t n, int64_t stride) {
+                                                           float* __restrict__ out2, int nparts, int64_t n,
+                                                           int64_t n1, int64_t stride) {
   for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float s = 0.f;
 #pragma unroll 16
     for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * stride + i];
-    out[i] = s;
+    if (i < n1) out[i] = s;
+    else out2[i - n1] = s;
   }
 }
 
@@ -325,9 +330,11 @@ __global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, in
   for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-// out[i] = sum_p part[p * stride + i], one workgroup per output (many partials)
+// s_i = sum_p part[p * stride + i], one workgroup per output i (many
+// partials); out[i] = s_i for i < n1, else out2[i - n1]
 __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ part, float* __restrict__ out,
-                                                          int nparts, int64_t stride) {
+                                                          float* __restrict__ out2, int nparts, int64_t n1,
+                                                          int64_t stride) {
   __shared__ float red[256];
   const int64_t i = blockIdx.x;
   float s = 0.f;
@@ -338,7 +345,10 @@ __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restric
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[i] = red[0];
+  if (threadIdx.x == 0) {
+    if (i < n1) out[i] = red[0];
+    else out2[i - n1] = red[0];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -414,8 +424,7 @@ hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int 
   else e = go(std::integral_constant<int, 6412>{});
   if (e != hipSuccess) return e;
   // dg = sum over workgroups of part[b][0:C], db of part[b][C:2C]
-  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part, dg, nb, 2 * C);
-  reduce_rows_kernel<<<dim3((unsigned)C), dim3(256), 0, st>>>(part + C, db, nb, 2 * C);
+  reduce_rows_kernel<<<dim3((unsigned)(2 * C)), dim3(256), 0, st>>>(part, dg, db, nb, C, 2 * C);
   return hipGetLastError();
 }
 
@@ -434,15 +443,14 @@ size_t wgrad_part_bytes(int64_t M, int NO, int KI) {
 hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
                  hipStream_t st) {
   if (NO % 32 || KI % 32) return hipErrorInvalidValue;
+  const int64_t nw = (int64_t)NO * KI, ntot = nw + (db ? NO : 0);
   if (M <= 0) {
     // no tokens: zero gradients
-    reduce_parts_kernel<<<dim3(grid_for((int64_t)NO * KI, 256)), dim3(256), 0, st>>>(part, dW, 0, (int64_t)NO * KI, 0);
-    if (db) reduce_parts_kernel<<<dim3(grid_for(NO, 256)), dim3(256), 0, st>>>(part, db, 0, NO, 0);
+    reduce_parts_kernel<<<dim3(grid_for(ntot, 256)), dim3(256), 0, st>>>(part, dW, db, 0, ntot, nw, 0);
     return hipGetLastError();
   }
   const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
   const int np = (int)(nchunks < kMaxParts ? nchunks : kMaxParts);
-  float* colp = part + (size_t)np * NO * KI;
   // n tile 96 where it divides NO, else 32; k tile 96 or 128 where it divides
   // KI, else 32
   auto launch = [&](auto kern, int bn, int bk) -> hipError_t {
@@ -450,7 +458,7 @@ hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part
     hipError_t e = ensure_dynamic_lds((const void*)kern, lds);
     if (e != hipSuccess) return e;
     kern<<<dim3((unsigned)(np * (NO / bn) * (KI / bk))), dim3(256), lds, st>>>((const bf16_t*)A, (const bf16_t*)B,
-                                                                             part, colp, M, NO, KI, np);
+                                                                             part, M, NO, KI, np);
     return hipGetLastError();
   };
   hipError_t e0;
@@ -460,11 +468,8 @@ hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part
   else if (NO % 32 == 0 && KI % 96 == 0) e0 = launch(wgrad_kernel<32, 96>, 32, 96);
   else e0 = launch(wgrad_kernel<32, 32>, 32, 32);
   if (e0 != hipSuccess) return e0;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  reduce_parts_kernel<<<dim3(grid_for((int64_t)NO * KI, 256)), dim3(256), 0, st>>>(part, dW, np, (int64_t)NO * KI,
-                                                                                   (int64_t)NO * KI);
-  if (db) reduce_rows_kernel<<<dim3((unsigned)NO), dim3(256), 0, st>>>(colp, db, np, NO);
+  // dW and db from the same partial rows in one pass
+  reduce_parts_kernel<<<dim3(grid_for(ntot, 256)), dim3(256), 0, st>>>(part, dW, db, np, ntot, nw, nw + NO);
   return hipGetLastError();
 }
 
