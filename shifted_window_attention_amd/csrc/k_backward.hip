@@ -172,27 +172,31 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
       }
     }
   }
-  // the workgroup's row groups into one partial (LDS, at most 2 x 768 floats
-  // per pass of 256 / LPR groups)
-  __shared__ float red[2 * 768];
-  constexpr int G = 256 / LPR;
-  const int gi = threadIdx.x / LPR;
-  for (int i = threadIdx.x; i < 2 * C; i += 256) red[i] = 0.f;
-  __syncthreads();
-  for (int k = 0; k < G; ++k) {
-    if (gi == k) {
+  // the workgroup's row groups into one partial: the wave's groups by
+  // shuffles (lanes LPR apart), then the 4 waves' sums through LDS, in a
+  // fixed order
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int c = l16 + LPR * j;
-        if (c < C) {
-          red[c] += dgs[j];
-          red[C + c] += dbs[j];
-        }
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      dgs[j] += __shfl_xor(dgs[j], o);
+      dbs[j] += __shfl_xor(dbs[j], o);
+    }
+  __shared__ float red[4][2 * 768];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) < LPR) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = l16 + LPR * j;
+      if (c < C) {
+        red[wave][c] = dgs[j];
+        red[wave][C + c] = dbs[j];
       }
     }
-    __syncthreads();
   }
-  for (int i = threadIdx.x; i < 2 * C; i += 256) part[(int64_t)blockIdx.x * 2 * C + i] = red[i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * C; i += 256)
+    part[(int64_t)blockIdx.x * 2 * C + i] = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
 }
 
 // An 8 x 8 block of bf16 rows (8 tokens m0 .. m0 + 7 of row pitch ld, 8
