@@ -217,3 +217,10 @@ def test_head_views_inflation_reject_bad_arguments():
     assert L.vswin_inflate_patch_embed(96, 3, 0, 4, 4, 0, None, None, None) == -1
     assert L.vswin_inflate_bias_table(169, 3, 0, 0, None, None, None) == -1
     assert L.vswin_head_workspace(2, 392, 768) >= 2 * 768 * 4 * 2
+
+
+def test_issue_probe_rejects_bad_arguments():
+    L = vs.lib()
+    assert L.vswin_issue_probe(None, 1, 1, 4, None) == -1
+    assert L.vswin_issue_probe(None, 0, 1, 0, None) == -1
+    assert L.vswin_issue_probe(None, 1, 1, 0, None) == -1   # NULL out
