@@ -1053,17 +1053,28 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
   const int sw = (fr >> 2) & 3;
   bf16_t* dqkv = b.dqkv;
   const int C = b.a.C;
-  for (int kt = part + BL.parts * wv; kt * 16 < N; kt += BL.parts * CF::kWaves) {
-    const int key = kt * 16 + fr;
-    const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(b.kr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
-    const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(b.vr + ((int64_t)mem * NPAD + key) * 32 + 8 * g4);
-    const int kps = pair_slot(key >> 2);
-    const int klab = elem_label<CF>(lp[kps], key & 3);
-    const int kadd = (int)L.off_tab + ES * L.A + kp[kps] + ES * (key & 3) * Rp;
-    const bool kval = key < N;
-    f32x4_t dv0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, dv1 = dv0, dk0 = dv0, dk1 = dv0;
+  // The wave's key tiles kt = part + parts (wv + 8 j), two per pass (their
+  // query-side operands read once for both), then a last single one.
+  auto tiles = [&](auto kt_count, int ktA, int ktB) {
+    constexpr int KT = decltype(kt_count)::value;
+    const int kts[2] = {ktA, ktB};
+    int key[KT], klab[KT], kadd[KT];
+    bool kval[KT];
+    bf16x8_t kf[KT], vf[KT];
+    f32x4_t dv0[KT], dv1[KT], dk0[KT], dk1[KT];
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      key[u] = kts[u] * 16 + fr;
+      kf[u] = *reinterpret_cast<const bf16x8_t*>(b.kr + ((int64_t)mem * NPAD + key[u]) * 32 + 8 * g4);
+      vf[u] = *reinterpret_cast<const bf16x8_t*>(b.vr + ((int64_t)mem * NPAD + key[u]) * 32 + 8 * g4);
+      const int kps = pair_slot(key[u] >> 2);
+      klab[u] = elem_label<CF>(lp[kps], key[u] & 3);
+      kadd[u] = (int)L.off_tab + ES * L.A + kp[kps] + ES * (key[u] & 3) * Rp;
+      kval[u] = key[u] < N;
+      dv0[u] = dv1[u] = dk0[u] = dk1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     for (int qb = 0; qb < NPAD; qb += 32) {
-      float pv[8], dsv[8];
+      float pv[KT][8], dsv[KT][8];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int qs0 = qb + 16 * s;
@@ -1078,49 +1089,51 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
         }
         const int qps = pair_slot((qs0 + 4 * g4) >> 2);
         const int qlw = lp[qps];
-        const int base = kadd - kp[qps];   // query temporal i: - i Rp
-        const float* tp = reinterpret_cast<const float*>(tabb + base);
-        const f32x4_t tb = f32x4_t{tp[0], tp[-Rp], tp[-2 * Rp], tp[-3 * Rp]};
-        const f32x4_t s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf, tb, 0, 0, 0);
-        const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse + qs0 + 4 * g4);
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(Dl + qs0 + 4 * g4);
-        float dsl[4];
+        const int mq = (qs0 >> 2) + g4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float P = pair_p(kval && qs0 + 4 * g4 + i < N, elem_label<CF>(qlw, i) == klab, b.a.mask_m100,
-                                 s2[i], l4[i]);
-          const float ds = P * (dp[i] - d4[i]);
-          pv[4 * s + i] = P;
-          dsv[4 * s + i] = ds;
-          dsl[i] = ds;
-        }
-        // dS toward the table gradient.  The 4 lanes of a key group (kk =
-        // fr & 3, one quad) hold the 16 pairs of one (query group, key group);
-        // pair (kk, i) belongs to the table entry of temporal diagonal kk - i,
-        // so the quad forms the 7 diagonal sums (DPP within the quad) and
-        // stores them, each (query group, key group) once, for
-        // attn_bwd_grp_sum / attn_bwd_dtab_gather: no atomics.
-        const int kk = fr & 3;
-        float mine0 = 0.f, mine1 = 0.f;
+        for (int u = 0; u < KT; ++u) {
+          const int base = kadd[u] - kp[qps];   // query temporal i: - i Rp
+          const float* tp = reinterpret_cast<const float*>(tabb + base);
+          const f32x4_t tb = f32x4_t{tp[0], tp[-Rp], tp[-2 * Rp], tp[-3 * Rp]};
+          const f32x4_t s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[u], tb, 0, 0, 0);
+          const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[u], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          float dsl[4];
 #pragma unroll
-        for (int dd = -3; dd <= 3; ++dd) {
-          const int i = kk - dd;
-          float v = i == 0 ? dsl[0] : i == 1 ? dsl[1] : i == 2 ? dsl[2] : i == 3 ? dsl[3] : 0.f;
-          v += quad_xor(v, 0xB1);
-          v += quad_xor(v, 0x4E);
-          if (dd == kk - 3) mine0 = v;
-          if (dd == kk + 1) mine1 = v;
+          for (int i = 0; i < 4; ++i) {
+            const float P = pair_p(kval[u] && qs0 + 4 * g4 + i < N, elem_label<CF>(qlw, i) == klab[u],
+                                   b.a.mask_m100, s2[i], l4[i]);
+            const float ds = P * (dp[i] - d4[i]);
+            pv[u][4 * s + i] = P;
+            dsv[u][4 * s + i] = ds;
+            dsl[i] = ds;
+          }
+          // dS toward the table gradient.  The 4 lanes of a key group (kk =
+          // fr & 3, one quad) hold the 16 pairs of one (query group, key
+          // group); pair (kk, i) belongs to the table entry of temporal
+          // diagonal kk - i, so the quad forms the 7 diagonal sums (DPP
+          // within the quad) and stores them, each (query group, key group)
+          // once, for attn_bwd_grp_sum / attn_bwd_dtab_gather: no atomics.
+          const int kk = fr & 3;
+          float mine0 = 0.f, mine1 = 0.f;
+#pragma unroll
+          for (int dd = -3; dd <= 3; ++dd) {
+            const int i = kk - dd;
+            float v = i == 0 ? dsl[0] : i == 1 ? dsl[1] : i == 2 ? dsl[2] : i == 3 ? dsl[3] : 0.f;
+            v += quad_xor(v, 0xB1);
+            v += quad_xor(v, 0x4E);
+            if (dd == kk - 3) mine0 = v;
+            if (dd == kk + 1) mine1 = v;
+          }
+          const int mk = 4 * kts[u] + (fr >> 2);
+          if (mq < ng && mk < ng) {
+            float* dp7 = b.dgrp + (int64_t)mem * dgrp_floats(N) + dgrp_rec(ng, mq, mk) * 7;
+            dp7[kk] = mine0;
+            if (kk < 3) dp7[kk + 4] = mine1;
+          }
         }
-        const int mq = (qs0 >> 2) + g4, mk = 4 * kt + (fr >> 2);
-        if (mq < ng && mk < ng) {
-          float* dp7 = b.dgrp + (int64_t)mem * dgrp_floats(N) + dgrp_rec(ng, mq, mk) * 7;
-          dp7[kk] = mine0;
-          if (kk < 3) dp7[kk + 4] = mine1;
-        }
-        (void)base;
       }
-      const bf16x8_t pb = pack8f(pv), db = pack8f(dsv);
       const int ch = qb / 8 + g4;
       const unsigned char* t0 = smem + (fr * BL.pitch + (ch ^ ((fr >> 3) & 3))) * 16;
       const unsigned char* t1 = smem + ((16 + fr) * BL.pitch + (ch ^ (((16 + fr) >> 3) & 3))) * 16;
@@ -1128,24 +1141,35 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
       const bf16x8_t do1 = *reinterpret_cast<const bf16x8_t*>(t1 + BL.a_dot);
       const bf16x8_t qt0 = *reinterpret_cast<const bf16x8_t*>(t0 + BL.a_qt);
       const bf16x8_t qt1 = *reinterpret_cast<const bf16x8_t*>(t1 + BL.a_qt);
-      dv0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do0, pb, dv0, 0, 0, 0);
-      dv1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do1, pb, dv1, 0, 0, 0);
-      dk0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt0, db, dk0, 0, 0, 0);
-      dk1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt1, db, dk1, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < KT; ++u) {
+        const bf16x8_t pb = pack8f(pv[u]), db = pack8f(dsv[u]);
+        dv0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do0, pb, dv0[u], 0, 0, 0);
+        dv1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(do1, pb, dv1[u], 0, 0, 0);
+        dk0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt0, db, dk0[u], 0, 0, 0);
+        dk1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt1, db, dk1[u], 0, 0, 0);
+      }
     }
-    if (kval) {
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      if (!kval[u]) continue;
       // lane: dims 4 g4 .. + 3 (and + 16) of key `key`
-      bf16_t* row = dqkv + ((int64_t)wi.w * N + key) * 3 * C + h * 32 + 4 * g4;
+      bf16_t* row = dqkv + ((int64_t)wi.w * N + key[u]) * 3 * C + h * 32 + 4 * g4;
       const float ks = b.dk_scale;
-      *reinterpret_cast<u32x2_t*>(row + 2 * C) = u32x2_t{pack_bf16x2(dv0[0], dv0[1]), pack_bf16x2(dv0[2], dv0[3])};
+      *reinterpret_cast<u32x2_t*>(row + 2 * C) =
+          u32x2_t{pack_bf16x2(dv0[u][0], dv0[u][1]), pack_bf16x2(dv0[u][2], dv0[u][3])};
       *reinterpret_cast<u32x2_t*>(row + 2 * C + 16) =
-          u32x2_t{pack_bf16x2(dv1[0], dv1[1]), pack_bf16x2(dv1[2], dv1[3])};
+          u32x2_t{pack_bf16x2(dv1[u][0], dv1[u][1]), pack_bf16x2(dv1[u][2], dv1[u][3])};
       *reinterpret_cast<u32x2_t*>(row + C) =
-          u32x2_t{pack_bf16x2(dk0[0] * ks, dk0[1] * ks), pack_bf16x2(dk0[2] * ks, dk0[3] * ks)};
+          u32x2_t{pack_bf16x2(dk0[u][0] * ks, dk0[u][1] * ks), pack_bf16x2(dk0[u][2] * ks, dk0[u][3] * ks)};
       *reinterpret_cast<u32x2_t*>(row + C + 16) =
-          u32x2_t{pack_bf16x2(dk1[0] * ks, dk1[1] * ks), pack_bf16x2(dk1[2] * ks, dk1[3] * ks)};
+          u32x2_t{pack_bf16x2(dk1[u][0] * ks, dk1[u][1] * ks), pack_bf16x2(dk1[u][2] * ks, dk1[u][3] * ks)};
     }
-  }
+  };
+  const int kstep = BL.parts * CF::kWaves;
+  int kt = part + BL.parts * wv;
+  for (; (kt + kstep) * 16 < N; kt += 2 * kstep) tiles(std::integral_constant<int, 2>{}, kt, kt + kstep);
+  if (kt * 16 < N) tiles(std::integral_constant<int, 1>{}, kt, kt);
 }
 
 template <class CF, bool GF>
