@@ -1199,19 +1199,31 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
   const unsigned char* tabb = smem;
   const int sw = (fr >> 2) & 3;
   const int C = b.a.C;
-  for (int qt = part + BL.parts * wv; qt * 16 < N; qt += BL.parts * CF::kWaves) {
-    const int q = qt * 16 + fr;
-    const bool qval = q < N;
-    const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(b.qr + ((int64_t)mem * NPAD + q) * 32 + 8 * g4);
-    const bf16x8_t df = *reinterpret_cast<const bf16x8_t*>(b.dor + ((int64_t)mem * NPAD + q) * 32 + 8 * g4);
-    const float l2 = qval ? b.lse[(int64_t)mem * N + q] : 0.f;
-    const float Dq = b.D[(int64_t)mem * NPAD + q];
-    const int qps = pair_slot(q >> 2);
-    const int qlab = elem_label<CF>(lp[qps], q & 3);
-    const int qaddr = (int)L.off_tab + ES * L.A - kp[qps] - ES * (q & 3) * Rp;
-    f32x4_t dq0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, dq1 = dq0;
+  // The wave's query tiles qt = part + parts (wv + 8 j), two per pass (their
+  // key-side operands read once for both), then a last single one.
+  auto tiles = [&](auto qt_count, int qtA, int qtB) {
+    constexpr int QT = decltype(qt_count)::value;
+    const int qts[2] = {qtA, qtB};
+    int q[QT], qlab[QT], qaddr[QT];
+    bool qval[QT];
+    float l2[QT], Dq[QT];
+    bf16x8_t qf[QT], df[QT];
+    f32x4_t dq0[QT], dq1[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      q[u] = qts[u] * 16 + fr;
+      qval[u] = q[u] < N;
+      qf[u] = *reinterpret_cast<const bf16x8_t*>(b.qr + ((int64_t)mem * NPAD + q[u]) * 32 + 8 * g4);
+      df[u] = *reinterpret_cast<const bf16x8_t*>(b.dor + ((int64_t)mem * NPAD + q[u]) * 32 + 8 * g4);
+      l2[u] = qval[u] ? b.lse[(int64_t)mem * N + q[u]] : 0.f;
+      Dq[u] = b.D[(int64_t)mem * NPAD + q[u]];
+      const int qps = pair_slot(q[u] >> 2);
+      qlab[u] = elem_label<CF>(lp[qps], q[u] & 3);
+      qaddr[u] = (int)L.off_tab + ES * L.A - kp[qps] - ES * (q[u] & 3) * Rp;
+      dq0[u] = dq1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     for (int kb = 0; kb < NPAD; kb += 32) {
-      float dsv[8];
+      float dsv[QT][8];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int ks0 = kb + 16 * s;
@@ -1226,35 +1238,47 @@ __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, co
         }
         const int kps = pair_slot((ks0 + 4 * g4) >> 2);
         const int klw = lp[kps];
-        const float* tp = reinterpret_cast<const float*>(tabb + qaddr + kp[kps]);
-        const f32x4_t tb = f32x4_t{tp[0], tp[Rp], tp[2 * Rp], tp[3 * Rp]};
-        const f32x4_t s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf, tb, 0, 0, 0);
-        const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float P =
-              pair_p(qval && ks0 + 4 * g4 + i < N, elem_label<CF>(klw, i) == qlab, b.a.mask_m100, s2[i], l2);
-          dsv[4 * s + i] = P * (dp[i] - Dq);
+        for (int u = 0; u < QT; ++u) {
+          const float* tp = reinterpret_cast<const float*>(tabb + qaddr[u] + kp[kps]);
+          const f32x4_t tb = f32x4_t{tp[0], tp[Rp], tp[2 * Rp], tp[3 * Rp]};
+          const f32x4_t s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[u], tb, 0, 0, 0);
+          const f32x4_t dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df[u], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float P = pair_p(qval[u] && ks0 + 4 * g4 + i < N, elem_label<CF>(klw, i) == qlab[u],
+                                   b.a.mask_m100, s2[i], l2[u]);
+            dsv[u][4 * s + i] = P * (dp[i] - Dq[u]);
+          }
         }
       }
-      const bf16x8_t db = pack8f(dsv);
       const int ch = kb / 8 + g4;
       const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(
           smem + BL.b_kt + (fr * BL.pitch + (ch ^ ((fr >> 3) & 3))) * 16);
       const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(
           smem + BL.b_kt + ((16 + fr) * BL.pitch + (ch ^ (((16 + fr) >> 3) & 3))) * 16);
-      dq0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, db, dq0, 0, 0, 0);
-      dq1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, db, dq1, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        const bf16x8_t db = pack8f(dsv[u]);
+        dq0[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, db, dq0[u], 0, 0, 0);
+        dq1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, db, dq1[u], 0, 0, 0);
+      }
     }
-    if (qval) {
-      bf16_t* row = b.dqkv + ((int64_t)wi.w * N + q) * 3 * C + h * 32 + 4 * g4;
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      if (!qval[u]) continue;
+      bf16_t* row = b.dqkv + ((int64_t)wi.w * N + q[u]) * 3 * C + h * 32 + 4 * g4;
       const float qs = b.dq_scale;
       *reinterpret_cast<u32x2_t*>(row) =
-          u32x2_t{pack_bf16x2(dq0[0] * qs, dq0[1] * qs), pack_bf16x2(dq0[2] * qs, dq0[3] * qs)};
+          u32x2_t{pack_bf16x2(dq0[u][0] * qs, dq0[u][1] * qs), pack_bf16x2(dq0[u][2] * qs, dq0[u][3] * qs)};
       *reinterpret_cast<u32x2_t*>(row + 16) =
-          u32x2_t{pack_bf16x2(dq1[0] * qs, dq1[1] * qs), pack_bf16x2(dq1[2] * qs, dq1[3] * qs)};
+          u32x2_t{pack_bf16x2(dq1[u][0] * qs, dq1[u][1] * qs), pack_bf16x2(dq1[u][2] * qs, dq1[u][3] * qs)};
     }
-  }
+  };
+  const int qstep = BL.parts * CF::kWaves;
+  int qt = part + BL.parts * wv;
+  for (; (qt + qstep) * 16 < N; qt += 2 * qstep) tiles(std::integral_constant<int, 2>{}, qt, qt + qstep);
+  if (qt * 16 < N) tiles(std::integral_constant<int, 1>{}, qt, qt);
 }
 
 // Sum of the stored diagonal sums over the windows of each head: gsum[h][e]
