@@ -47,18 +47,6 @@ __device__ __forceinline__ u32x4_t pack8u(const float* f) {
 
 }  // namespace
 
-// dst (C x R) = src (R x C)^T, bf16; 32 x 32 tiles through LDS
-__global__ void __launch_bounds__(256) transpose_bf16_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
-                                                              int R, int C) {
-  __shared__ bf16_t t[32][33];
-  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8)
-    if (r0 + i < R && c0 + tx < C) t[i][tx] = src[(int64_t)(r0 + i) * C + c0 + tx];
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8)
-    if (c0 + i < C && r0 + tx < R) dst[(int64_t)(c0 + i) * R + r0 + tx] = t[tx][i];
-}
 
 // h = GELU(a) (bwd = 0) or da = dh * GELU'(a) written over dh (bwd = 1); n % 8 == 0
 __global__ void __launch_bounds__(256) gelu_kernel(const bf16_t* __restrict__ a, bf16_t* __restrict__ io, int64_t n,
@@ -366,11 +354,35 @@ unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 4096) {
 }
 }  // namespace
 
-hipError_t transpose_bf16(const void* src, void* dst, int R, int C, hipStream_t st) {
-  transpose_bf16_kernel<<<dim3((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32)), dim3(256), 0, st>>>(
-      (const bf16_t*)src, (bf16_t*)dst, R, C);
+// dst (C x R) = src (R x C)^T, bf16, 32 x 32 tiles through LDS; up to 4
+// matrices in one launch, blockIdx.z picking the job
+__global__ void __launch_bounds__(256) transpose_jobs_kernel(const TransposeJobs jobs) {
+  const TransposeJob& j = jobs.job[blockIdx.z];
+  __shared__ bf16_t t[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  if (c0 >= j.C || r0 >= j.R) return;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const bf16_t* src = (const bf16_t*)j.src;
+  bf16_t* dst = (bf16_t*)j.dst;
+  for (int i = ty; i < 32; i += 8)
+    if (r0 + i < j.R && c0 + tx < j.C) t[i][tx] = src[(int64_t)(r0 + i) * j.C + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8)
+    if (c0 + i < j.C && r0 + tx < j.R) dst[(int64_t)(c0 + i) * j.R + r0 + tx] = t[tx][i];
+}
+
+hipError_t transpose_jobs(const TransposeJobs& jobs, hipStream_t st) {
+  if (jobs.n <= 0) return hipSuccess;
+  int mr = 1, mc = 1;
+  for (int i = 0; i < jobs.n; ++i) {
+    mr = jobs.job[i].R > mr ? jobs.job[i].R : mr;
+    mc = jobs.job[i].C > mc ? jobs.job[i].C : mc;
+  }
+  transpose_jobs_kernel<<<dim3((unsigned)((mc + 31) / 32), (unsigned)((mr + 31) / 32), (unsigned)jobs.n), dim3(256),
+                          0, st>>>(jobs);
   return hipGetLastError();
 }
+
 
 hipError_t gelu_apply(const void* a, void* io, int64_t n, int bwd, hipStream_t st) {
   if (n <= 0) return hipSuccess;

@@ -276,7 +276,8 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
 struct BwdWs {
   size_t n1w, q, k, v, o, tab, lse;           // forward recompute (window rows)
   size_t zh, n2, a1, h, dh, dzh;              // block only
-  size_t dyw, dout, dqkv, dn1w, dn1, wT, part, attn;
+  size_t dyw, dout, dqkv, dn1w, dn1, part, attn;
+  size_t wTqkv, wTproj, wTfc2, wTfc1;          // transposed weights (fc: block only)
   size_t block_bytes, msa_bytes;
 };
 
@@ -308,8 +309,8 @@ BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
   w.dqkv = take(3 * act);
   w.dn1w = take(act);
   w.dn1 = take(tok);
-  const size_t wmax = (size_t)(3 * p.C > p.hid ? 3 * p.C : p.hid) * p.C * 2;
-  w.wT = take(wmax);
+  w.wTqkv = take((size_t)3 * p.C * p.C * 2);
+  w.wTproj = take((size_t)p.C * p.C * 2);
   size_t part = wgrad_part_bytes(p.Lp, 3 * p.C, p.C);
   part = std::max(part, wgrad_part_bytes(p.Lp, p.C, p.C));
   part = std::max(part, wgrad_part_bytes(p.L, p.C, p.hid));
@@ -324,6 +325,8 @@ BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
   w.h = take(hid);
   w.dh = take(hid);
   w.dzh = take(tok32);
+  w.wTfc2 = take((size_t)p.hid * p.C * 2);
+  w.wTfc1 = take((size_t)p.hid * p.C * 2);
   w.block_bytes = off;
   return w;
 }
@@ -504,8 +507,20 @@ namespace {
 // (table), qkv and of the window rows (w.dn1w) scattered to token rows dxo.
 vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_weights* wt,
                           const vswin_block_grads* g, char* ws, const BwdWs& w, void* dxo, hipStream_t st,
-                          const std::function<vswin_status()>& mid) {
+                          bool with_mlp, const std::function<vswin_status()>& mid) {
   const int C = p.C;
+  // every weight the input-gradient GEMMs need transposed, in one launch
+  // (the block's MLP weights too)
+  {
+    TransposeJobs tj{};
+    tj.job[tj.n++] = TransposeJob{wt->proj_w, ws + w.wTproj, C, C};
+    tj.job[tj.n++] = TransposeJob{wt->qkv_w, ws + w.wTqkv, 3 * C, C};
+    if (with_mlp) {
+      tj.job[tj.n++] = TransposeJob{wt->fc2_w, ws + w.wTfc2, C, p.hid};
+      tj.job[tj.n++] = TransposeJob{wt->fc1_w, ws + w.wTfc1, p.hid, C};
+    }
+    HIPCHECK(transpose_jobs(tj, st), "bwd: weight transposes");
+  }
   // qkv (q unscaled, V transposed for the MFMA attention)
   EpiArgs e{};
   e.kind = Epi::kQKV;
@@ -523,12 +538,11 @@ vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_
   // projection
   HIPCHECK(wgrad(ws + w.dyw, ws + w.o, g->proj_w, g->proj_b, (float*)(ws + w.part), p.Lp, C, C, st),
            "bwd: proj weight gradient");
-  HIPCHECK(transpose_bf16(wt->proj_w, ws + w.wT, C, C, st), "bwd: transpose proj");
   EpiArgs eb{};
   eb.kind = Epi::kBias;
   eb.out = ws + w.dout;
   eb.ld_out = C;
-  HIPCHECK(gemm(p.dt, ws + w.dyw, ws + w.wT, p.Lp, C, C, eb, st), "bwd: proj input gradient");
+  HIPCHECK(gemm(p.dt, ws + w.dyw, ws + w.wTproj, p.Lp, C, C, eb, st), "bwd: proj input gradient");
   // attention
   AttnBwdArgs b{};
   b.a = a;
@@ -541,9 +555,8 @@ vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_
   // qkv
   HIPCHECK(wgrad(ws + w.dqkv, ws + w.n1w, g->qkv_w, g->qkv_b, (float*)(ws + w.part), p.Lp, 3 * C, C, st),
            "bwd: qkv weight gradient");
-  HIPCHECK(transpose_bf16(wt->qkv_w, ws + w.wT, 3 * C, C, st), "bwd: transpose qkv");
   eb.out = ws + w.dn1w;
-  HIPCHECK(gemm(p.dt, ws + w.dqkv, ws + w.wT, p.Lp, C, 3 * C, eb, st), "bwd: qkv input gradient");
+  HIPCHECK(gemm(p.dt, ws + w.dqkv, ws + w.wTqkv, p.Lp, C, 3 * C, eb, st), "bwd: qkv input gradient");
   HIPCHECK(reverse_scatter(p.dt, ws + w.dn1w, nullptr, dxo, p.Lp, C, p.geo, st), "bwd: window rows to tokens");
   return VSWIN_OK;
 }
@@ -606,7 +619,7 @@ vswin_status vswin_window_msa_bwd(const vswin_desc* desc, const void* x_norm, co
   char* ws = (char*)workspace;
   HIPCHECK(ln_gather(p.dt, x_norm, nullptr, nullptr, ws + L.n1w, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
            "bwd: partition");
-  return msa_bwd_core(p, desc, w, g, ws, L, dx_norm, st, [&]() -> vswin_status {
+  return msa_bwd_core(p, desc, w, g, ws, L, dx_norm, st, false, [&]() -> vswin_status {
     HIPCHECK(ln_gather(p.dt, dy, nullptr, nullptr, ws + L.dyw, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
              "bwd: partition of dy");
     return VSWIN_OK;
@@ -662,19 +675,17 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
     HIPCHECK(gelu_apply(ws + L.a1, ws + L.h, p.L * hid, 0, st), "bwd: gelu forward");
     // fc2
     HIPCHECK(wgrad(dy, ws + L.h, g->fc2_w, g->fc2_b, part, p.L, C, hid, st), "bwd: fc2 weight gradient");
-    HIPCHECK(transpose_bf16(w->fc2_w, ws + L.wT, C, hid, st), "bwd: transpose fc2");
     EpiArgs eb{};
     eb.kind = Epi::kBias;
     eb.out = ws + L.dh;
     eb.ld_out = hid;
-    HIPCHECK(gemm(p.dt, dy, ws + L.wT, p.L, hid, C, eb, st), "bwd: fc2 input gradient");
+    HIPCHECK(gemm(p.dt, dy, ws + L.wTfc2, p.L, hid, C, eb, st), "bwd: fc2 input gradient");
     HIPCHECK(gelu_apply(ws + L.a1, ws + L.dh, p.L * hid, 1, st), "bwd: gelu backward");
     // fc1
     HIPCHECK(wgrad(ws + L.dh, ws + L.n2, g->fc1_w, g->fc1_b, part, p.L, hid, C, st), "bwd: fc1 weight gradient");
-    HIPCHECK(transpose_bf16(w->fc1_w, ws + L.wT, hid, C, st), "bwd: transpose fc1");
     eb.out = ws + L.dn1;   // dLN2 output, token rows (the buffer is reused for dLN1 later)
     eb.ld_out = C;
-    HIPCHECK(gemm(p.dt, ws + L.dh, ws + L.wT, p.L, C, hid, eb, st), "bwd: fc1 input gradient");
+    HIPCHECK(gemm(p.dt, ws + L.dh, ws + L.wTfc1, p.L, C, hid, eb, st), "bwd: fc1 input gradient");
     // LN2 (+ the residual path of y = z^ + ...)
     HIPCHECK(ln_bwd(1, ws + L.zh, w->ln2_g, ws + L.dn1, 0, dy, 1, ws + L.dzh, part, g->ln2_g, g->ln2_b, p.L, C,
                     desc->ln_eps, st),
@@ -682,7 +693,7 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
     HIPCHECK(gather_f32_bf16((const float*)(ws + L.dzh), ws + L.dyw, p.Lp, C, p.geo, st), "bwd: gather dz");
     return VSWIN_OK;
   };
-  CHECK(msa_bwd_core(p, desc, w, g, ws, L, ws + L.dn1, st, mid));
+  CHECK(msa_bwd_core(p, desc, w, g, ws, L, ws + L.dn1, st, true, mid));
   // LN1 (+ the residual path of z^ = x + ...)
   HIPCHECK(ln_bwd(0, x, w->ln1_g, ws + L.dn1, 1, ws + L.dzh, 0, dx, part, g->ln1_g, g->ln1_b, p.L, C, desc->ln_eps,
                   st),

@@ -143,9 +143,19 @@ hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const vo
 
 // --- backward pieces (k_backward.hip) --------------------------------------
 // dst (C x R) = src (R x C)^T, bf16
-hipError_t transpose_bf16(const void* src, void* dst, int R, int C, hipStream_t st);
 // bwd = 0: io = GELU(a); bwd = 1: io = io * GELU'(a)  (bf16, n % 8 == 0)
 hipError_t gelu_apply(const void* a, void* io, int64_t n, int bwd, hipStream_t st);
+// dst (C, R) = src (R, C)^T for up to 4 bf16 matrices in one launch
+struct TransposeJob {
+  const void* src;
+  void* dst;
+  int R, C;
+};
+struct TransposeJobs {
+  TransposeJob job[4];
+  int n;
+};
+hipError_t transpose_jobs(const TransposeJobs& jobs, hipStream_t st);
 // bf16 window rows of an fp32 token-row tensor, zeros for pad slots
 hipError_t gather_f32_bf16(const float* in, void* out, int64_t slots, int C, const WinGeo& geo, hipStream_t st);
 // LayerNorm backward over rows of C (<= 768): out = dLN(x; g)/dx applied to dy, plus res (nullable);
