@@ -1313,7 +1313,7 @@ __global__ void __launch_bounds__(256) attn_bwd_grp_sum_kernel(const float* __re
 // dt = 4 (ak - aq) + dd.  One wave per entry, lanes over the query cells;
 // deterministic (no atomics).
 __global__ void __launch_bounds__(256) attn_bwd_dtab_gather_kernel(const float* __restrict__ gsum,
-                                                                    float* __restrict__ dtab, const BwdL BL,
+                                                                    float* __restrict__ out, const BwdL BL,
                                                                     WinGeo g) {
   const A5& L = BL.L;
   const int h = blockIdx.y;
@@ -1342,22 +1342,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dtab_gather_kernel(const float* 
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) dtab[(int64_t)h * nd + y] = s;
+  // straight into the (rows, heads) table layout: entry (u, v, x) is row
+  // (TD-1-u) R + (TH-1-v) Rw + (Rw-1-x), the inverse of ts_entry's index map
+  // (every row has exactly one scalar index; indices with rem >= R are padding)
+  if (lane == 0 && rem < L.R)
+    out[((int64_t)(L.TD - 1 - u) * L.R + (L.TH - 1 - v) * L.Rw + (L.Rw - 1 - x)) * L.heads + h] = s;
 }
 
-// table-row layout of the accumulated scalar-form gradient (the inverse of
-// ts_entry's index map); every row has exactly one scalar index
-__global__ void __launch_bounds__(256) attn_bwd_dtab_kernel(const float* __restrict__ dtab, float* __restrict__ out,
-                                                             const Tab4Geo tg, int rows) {
-  const int x = blockIdx.x * 256 + (int)threadIdx.x;
-  if (x >= rows * tg.heads) return;
-  const int row = x / tg.heads, h = x - row * tg.heads;
-  const int dtr = tg.TD - 1 - row / tg.R;
-  const int rem = row - (row / tg.R) * tg.R;
-  const int dhr = tg.TH - 1 - rem / tg.Rw;
-  const int dwr = tg.Rw - 1 - (rem - (rem / tg.Rw) * tg.Rw);
-  out[x] = dtab[(size_t)h * tg.TD * tg.Rp + dtr * tg.Rp + dhr * tg.Rw + dwr];
-}
 
 namespace {
 
@@ -1421,10 +1412,9 @@ size_t attention_bwd_workspace_bytes(const AttnArgs& a) {
   const size_t arr = ((size_t)items * L.NPAD * 32 * 2 + 255) & ~(size_t)255;
   const size_t D = ((size_t)items * L.NPAD * 4 + 255) & ~(size_t)255;
   const size_t tabs = ((size_t)a.heads * L.TS4 * 16 + 255) & ~(size_t)255;
-  const size_t dtab = ((size_t)a.heads * L.TD * L.Rp * 4 + 255) & ~(size_t)255;
   const size_t grp = ((size_t)items * dgrp_floats(a.N) * 4 + 255) & ~(size_t)255;
   const size_t gsum = ((size_t)a.heads * dgrp_floats(a.N) * 4 + 255) & ~(size_t)255;
-  return 7 * arr + D + tabs + dtab + grp + gsum;
+  return 7 * arr + D + tabs + grp + gsum;
 }
 
 hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
@@ -1458,8 +1448,6 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
   off += ((size_t)items * L.NPAD * 4 + 255) & ~(size_t)255;
   b.a.tab4 = w + off;
   off += ((size_t)in.a.heads * L.TS4 * 16 + 255) & ~(size_t)255;
-  b.dtab = reinterpret_cast<float*>(w + off);
-  off += ((size_t)in.a.heads * L.TD * L.Rp * 4 + 255) & ~(size_t)255;
   b.dgrp = reinterpret_cast<float*>(w + off);
   off += ((size_t)items * dgrp_floats(in.a.N) * 4 + 255) & ~(size_t)255;
   float* gsum = reinterpret_cast<float*>(w + off);
@@ -1492,10 +1480,7 @@ hipError_t attention_bwd(const AttnBwdArgs& in, hipStream_t st) {
       b.dgrp, gsum, in.a.nW, in.a.heads, E);
   const int nd = L.TD * L.Rp;
   attn_bwd_dtab_gather_kernel<<<dim3((unsigned)((nd + 3) / 4), (unsigned)in.a.heads), dim3(256), 0, st>>>(
-      gsum, b.dtab, B, in.a.geo);
-  const int rows = in.a.rel.rows;
-  attn_bwd_dtab_kernel<<<dim3((unsigned)((rows * in.a.heads + 255) / 256)), dim3(256), 0, st>>>(b.dtab, in.dtable,
-                                                                                               L.tg, rows);
+      gsum, in.dtable, B, in.a.geo);
   return hipGetLastError();
 }
 

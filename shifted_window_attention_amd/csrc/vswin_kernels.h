@@ -121,7 +121,6 @@ struct AttnBwdArgs {
   bf16_t *qr, *kr, *vr, *dor;   // padded rows (items, NPAD, 32)
   bf16_t *qt, *kt, *dot;        // transposes (items, 32, NPAD), pair order per 32-row block
   float* D;                     // (items, NPAD) row sums of dout * o
-  float* dtab;                  // (heads, TD * Rp) scalar-form table gradient
   float* dgrp;                  // per (item, query group, key group): 7 temporal-diagonal sums of dS
   float dq_scale, dk_scale;
 };
