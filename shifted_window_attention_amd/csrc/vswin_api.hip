@@ -507,7 +507,7 @@ namespace {
 // (table), qkv and of the window rows (w.dn1w) scattered to token rows dxo.
 vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_weights* wt,
                           const vswin_block_grads* g, char* ws, const BwdWs& w, void* dxo, hipStream_t st,
-                          bool with_mlp, const std::function<vswin_status()>& mid) {
+                          bool with_mlp, const GatherA& ga, const std::function<vswin_status()>& mid) {
   const int C = p.C;
   // every weight the input-gradient GEMMs need transposed, in one launch
   // (the block's MLP weights too)
@@ -521,15 +521,24 @@ vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_
     }
     HIPCHECK(transpose_jobs(tj, st), "bwd: weight transposes");
   }
-  // qkv (q unscaled, V transposed for the MFMA attention)
-  EpiArgs e{};
-  e.kind = Epi::kQKV;
-  e.bias = wt->qkv_b;
-  e.out = ws + w.q; e.out2 = ws + w.k; e.out3 = ws + w.v;
-  e.C = C; e.heads = p.heads; e.d = p.d; e.N = p.N; e.geo = p.geo;
-  e.vt = 1;
-  HIPCHECK(gemm(p.dt, ws + w.n1w, wt->qkv_w, p.Lp, 3 * C, C, e, st), "bwd: qkv gemm");
+  // qkv (q unscaled, V transposed for the MFMA attention): the fused wave
+  // kernel gathers (and normalises) the token rows itself and also writes the
+  // attention's prepared bias tables; else a GEMM on the window rows w.n1w
   AttnArgs a = attn_args(p, ws + w.q, ws + w.k, ws + w.v, wt->rpb_table, ws + w.o, d->flags, ws + w.tab);
+  if (winproj_supported(p.dt, C, p.d, p.N, 1)) {
+    HIPCHECK(qkv_proj(ga.x, ga.g, ga.b, ga.eps, ga.ln, wt->qkv_w, wt->qkv_b, ws + w.q, ws + w.k, ws + w.v, 1, 1.0f,
+                      p.Lp, C, p.heads, p.d, p.geo, wt->rpb_table, ws + w.tab, tab4_geo(p.rel, p.heads, p.N), st),
+             "bwd: qkv projection");
+    a.tab_ready = 1;
+  } else {
+    EpiArgs e{};
+    e.kind = Epi::kQKV;
+    e.bias = wt->qkv_b;
+    e.out = ws + w.q; e.out2 = ws + w.k; e.out3 = ws + w.v;
+    e.C = C; e.heads = p.heads; e.d = p.d; e.N = p.N; e.geo = p.geo;
+    e.vt = 1;
+    HIPCHECK(gemm(p.dt, ws + w.n1w, wt->qkv_w, p.Lp, 3 * C, C, e, st), "bwd: qkv gemm");
+  }
   a.lse = (float*)(ws + w.lse);
   HIPCHECK(attention_mfma(a, st), "bwd: attention forward");
   // the caller's middle part: everything between the attention output and
@@ -619,7 +628,8 @@ vswin_status vswin_window_msa_bwd(const vswin_desc* desc, const void* x_norm, co
   char* ws = (char*)workspace;
   HIPCHECK(ln_gather(p.dt, x_norm, nullptr, nullptr, ws + L.n1w, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
            "bwd: partition");
-  return msa_bwd_core(p, desc, w, g, ws, L, dx_norm, st, false, [&]() -> vswin_status {
+  const GatherA ga{x_norm, nullptr, nullptr, desc->ln_eps, 0, p.geo};
+  return msa_bwd_core(p, desc, w, g, ws, L, dx_norm, st, false, ga, [&]() -> vswin_status {
     HIPCHECK(ln_gather(p.dt, dy, nullptr, nullptr, ws + L.dyw, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
              "bwd: partition of dy");
     return VSWIN_OK;
@@ -693,7 +703,8 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
     HIPCHECK(gather_f32_bf16((const float*)(ws + L.dzh), ws + L.dyw, p.Lp, C, p.geo, st), "bwd: gather dz");
     return VSWIN_OK;
   };
-  CHECK(msa_bwd_core(p, desc, w, g, ws, L, ws + L.dn1, st, true, mid));
+  const GatherA ga{x, w->ln1_g, w->ln1_b, desc->ln_eps, 1, p.geo};
+  CHECK(msa_bwd_core(p, desc, w, g, ws, L, ws + L.dn1, st, true, ga, mid));
   // LN1 (+ the residual path of z^ = x + ...)
   HIPCHECK(ln_bwd(0, x, w->ln1_g, ws + L.dn1, 1, ws + L.dzh, 0, dx, part, g->ln1_g, g->ln1_b, p.L, C, desc->ln_eps,
                   st),
