@@ -4,8 +4,9 @@
 //   * weight gradients dW = dY^T X of the linear layers: `wgrad_kernel`, MFMA
 //     with the token dimension as the contraction (both operands staged
 //     token-contiguous in LDS by transposing 16-byte row loads), one fp32
-//     partial per group of 256-token chunks, summed by `reduce_parts_kernel`;
-//     the bias gradient (column sums of dY) in the same pass;
+//     partial per group of 256-token chunks; the bias gradient (column sums of
+//     dY) in the same pass; the partials of every weight gradient of a
+//     backward call summed by one `wgrad_reduce_kernel` launch;
 //   * LayerNorm backward `ln_bwd_kernel`: one wave per token row, the
 //     statistics recomputed, dx = (dxh - mean(dxh) - xh mean(dxh xh)) / sigma
 //     with dxh = dy g, plus a residual gradient; dg, db as per-wave partials;
@@ -304,20 +305,6 @@ __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A
   }
 }
 
-// s_i = sum_p part[p * stride + i], i < n; out[i] = s_i for i < n1, else
-// out2[i - n1]
-__global__ void __launch_bounds__(256) reduce_parts_kernel(const float* __restrict__ part, float* __restrict__ out,
-                                                           float* __restrict__ out2, int nparts, int64_t n,
-                                                           int64_t n1, int64_t stride) {
-  for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    float s = 0.f;
-#pragma unroll 16
-    for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * stride + i];
-    if (i < n1) out[i] = s;
-    else out2[i - n1] = s;
-  }
-}
-
 __global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
@@ -456,17 +443,15 @@ size_t wgrad_part_bytes(int64_t M, int NO, int KI) {
   return (size_t)np * ((size_t)NO * KI + NO) * 4;
 }
 
-hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
-                 hipStream_t st) {
+hipError_t wgrad_partials(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
+                          WgradJob& job, hipStream_t st) {
   if (NO % 32 || KI % 32) return hipErrorInvalidValue;
-  const int64_t nw = (int64_t)NO * KI, ntot = nw + (db ? NO : 0);
-  if (M <= 0) {
-    // no tokens: zero gradients
-    reduce_parts_kernel<<<dim3(grid_for(ntot, 256)), dim3(256), 0, st>>>(part, dW, db, 0, ntot, nw, 0);
-    return hipGetLastError();
-  }
+  const int64_t nw = (int64_t)NO * KI;
+  job = WgradJob{part, dW, db, 0, nw + (db ? NO : 0), nw, nw + NO};
+  if (M <= 0) return hipSuccess;   // no tokens: the reduction writes zeros
   const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
   const int np = (int)(nchunks < kMaxParts ? nchunks : kMaxParts);
+  job.np = np;
   // n tile 96 where it divides NO, else 32; k tile 96 or 128 where it divides
   // KI, else 32
   auto launch = [&](auto kern, int bn, int bk) -> hipError_t {
@@ -477,15 +462,30 @@ hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part
                                                                              part, M, NO, KI, np);
     return hipGetLastError();
   };
-  hipError_t e0;
-  if (NO % 96 == 0 && KI % 96 == 0) e0 = launch(wgrad_kernel<96, 96>, 96, 96);
-  else if (NO % 96 == 0 && KI % 128 == 0) e0 = launch(wgrad_kernel<96, 128>, 96, 128);
-  else if (NO % 32 == 0 && KI % 128 == 0) e0 = launch(wgrad_kernel<32, 128>, 32, 128);
-  else if (NO % 32 == 0 && KI % 96 == 0) e0 = launch(wgrad_kernel<32, 96>, 32, 96);
-  else e0 = launch(wgrad_kernel<32, 32>, 32, 32);
-  if (e0 != hipSuccess) return e0;
-  // dW and db from the same partial rows in one pass
-  reduce_parts_kernel<<<dim3(grid_for(ntot, 256)), dim3(256), 0, st>>>(part, dW, db, np, ntot, nw, nw + NO);
+  if (NO % 96 == 0 && KI % 96 == 0) return launch(wgrad_kernel<96, 96>, 96, 96);
+  if (NO % 96 == 0 && KI % 128 == 0) return launch(wgrad_kernel<96, 128>, 96, 128);
+  if (NO % 32 == 0 && KI % 128 == 0) return launch(wgrad_kernel<32, 128>, 32, 128);
+  if (NO % 32 == 0 && KI % 96 == 0) return launch(wgrad_kernel<32, 96>, 32, 96);
+  return launch(wgrad_kernel<32, 32>, 32, 32);
+}
+
+// every job's dW and db from its partial rows, one launch (blockIdx.y = job)
+__global__ void __launch_bounds__(256) wgrad_reduce_kernel(const WgradJobs jobs) {
+  const WgradJob& j = jobs.job[blockIdx.y];
+  for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < j.n; i += (int64_t)gridDim.x * 256) {
+    float s = 0.f;
+#pragma unroll 16
+    for (int p = 0; p < j.np; ++p) s += j.part[(int64_t)p * j.stride + i];
+    if (i < j.n1) j.dW[i] = s;
+    else j.db[i - j.n1] = s;
+  }
+}
+
+hipError_t wgrad_reduce(const WgradJobs& jobs, hipStream_t st) {
+  if (jobs.n <= 0) return hipSuccess;
+  int64_t nmax = 1;
+  for (int i = 0; i < jobs.n; ++i) nmax = jobs.job[i].n > nmax ? jobs.job[i].n : nmax;
+  wgrad_reduce_kernel<<<dim3(grid_for(nmax, 256), (unsigned)jobs.n), dim3(256), 0, st>>>(jobs);
   return hipGetLastError();
 }
 

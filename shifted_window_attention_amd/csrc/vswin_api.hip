@@ -277,6 +277,7 @@ struct BwdWs {
   size_t n1w, q, k, v, o, tab, lse;           // forward recompute (window rows)
   size_t zh, n2, a1, h, dh, dzh;              // block only
   size_t dyw, dout, dqkv, dn1w, dn1, part, attn;
+  size_t pproj, pqkv, pfc2, pfc1;              // weight-gradient partials (fc: block only)
   size_t wTqkv, wTproj, wTfc2, wTfc1;          // transposed weights (fc: block only)
   size_t block_bytes, msa_bytes;
 };
@@ -311,12 +312,9 @@ BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
   w.dn1 = take(tok);
   w.wTqkv = take((size_t)3 * p.C * p.C * 2);
   w.wTproj = take((size_t)p.C * p.C * 2);
-  size_t part = wgrad_part_bytes(p.Lp, 3 * p.C, p.C);
-  part = std::max(part, wgrad_part_bytes(p.Lp, p.C, p.C));
-  part = std::max(part, wgrad_part_bytes(p.L, p.C, p.hid));
-  part = std::max(part, wgrad_part_bytes(p.L, p.hid, p.C));
-  part = std::max(part, ln_bwd_part_bytes(p.L, p.C));
-  w.part = take(part);
+  w.part = take(ln_bwd_part_bytes(p.L, p.C));
+  w.pproj = take(wgrad_part_bytes(p.Lp, p.C, p.C));
+  w.pqkv = take(wgrad_part_bytes(p.Lp, 3 * p.C, p.C));
   w.attn = take(attention_bwd_workspace_bytes(attn_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, d->flags)));
   w.msa_bytes = off;
   w.zh = take(tok32);
@@ -327,6 +325,8 @@ BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
   w.dzh = take(tok32);
   w.wTfc2 = take((size_t)p.hid * p.C * 2);
   w.wTfc1 = take((size_t)p.hid * p.C * 2);
+  w.pfc2 = take(wgrad_part_bytes(p.L, p.C, p.hid));
+  w.pfc1 = take(wgrad_part_bytes(p.L, p.hid, p.C));
   w.block_bytes = off;
   return w;
 }
@@ -505,9 +505,12 @@ namespace {
 // attention branch from the window rows in w.n1w, then, given the window-row
 // gradient of the branch output in w.dyw, the gradients of proj, attention
 // (table), qkv and of the window rows (w.dn1w) scattered to token rows dxo.
+// The proj and qkv weight gradients are left as partials, their reductions
+// appended to `wj` (the caller launches all of them at once).
 vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_weights* wt,
                           const vswin_block_grads* g, char* ws, const BwdWs& w, void* dxo, hipStream_t st,
-                          bool with_mlp, const GatherA& ga, const std::function<vswin_status()>& mid) {
+                          bool with_mlp, const GatherA& ga, WgradJobs& wj,
+                          const std::function<vswin_status()>& mid) {
   const int C = p.C;
   // every weight the input-gradient GEMMs need transposed, in one launch
   // (the block's MLP weights too)
@@ -545,7 +548,8 @@ vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_
   // the window-row gradient of the branch output (w.dyw)
   CHECK(mid());
   // projection
-  HIPCHECK(wgrad(ws + w.dyw, ws + w.o, g->proj_w, g->proj_b, (float*)(ws + w.part), p.Lp, C, C, st),
+  HIPCHECK(wgrad_partials(ws + w.dyw, ws + w.o, g->proj_w, g->proj_b, (float*)(ws + w.pproj), p.Lp, C, C,
+                          wj.job[wj.n++], st),
            "bwd: proj weight gradient");
   EpiArgs eb{};
   eb.kind = Epi::kBias;
@@ -562,7 +566,8 @@ vswin_status msa_bwd_core(const Plan& p, const vswin_desc* d, const vswin_block_
   b.work = ws + w.attn;
   HIPCHECK(attention_bwd(b, st), "bwd: attention");
   // qkv
-  HIPCHECK(wgrad(ws + w.dqkv, ws + w.n1w, g->qkv_w, g->qkv_b, (float*)(ws + w.part), p.Lp, 3 * C, C, st),
+  HIPCHECK(wgrad_partials(ws + w.dqkv, ws + w.n1w, g->qkv_w, g->qkv_b, (float*)(ws + w.pqkv), p.Lp, 3 * C, C,
+                          wj.job[wj.n++], st),
            "bwd: qkv weight gradient");
   eb.out = ws + w.dn1w;
   HIPCHECK(gemm(p.dt, ws + w.dqkv, ws + w.wTqkv, p.Lp, C, 3 * C, eb, st), "bwd: qkv input gradient");
@@ -629,11 +634,14 @@ vswin_status vswin_window_msa_bwd(const vswin_desc* desc, const void* x_norm, co
   HIPCHECK(ln_gather(p.dt, x_norm, nullptr, nullptr, ws + L.n1w, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
            "bwd: partition");
   const GatherA ga{x_norm, nullptr, nullptr, desc->ln_eps, 0, p.geo};
-  return msa_bwd_core(p, desc, w, g, ws, L, dx_norm, st, false, ga, [&]() -> vswin_status {
+  WgradJobs wj{};
+  CHECK(msa_bwd_core(p, desc, w, g, ws, L, dx_norm, st, false, ga, wj, [&]() -> vswin_status {
     HIPCHECK(ln_gather(p.dt, dy, nullptr, nullptr, ws + L.dyw, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
              "bwd: partition of dy");
     return VSWIN_OK;
-  });
+  }));
+  HIPCHECK(wgrad_reduce(wj, st), "bwd: weight gradient reduction");
+  return VSWIN_OK;
 }
 
 vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w, const void* dy,
@@ -662,6 +670,7 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
   char* ws = (char*)workspace;
   const int C = p.C, hid = p.hid;
   float* part = (float*)(ws + L.part);
+  WgradJobs wj{};
   // LN1 + pad + roll + partition of x
   HIPCHECK(ln_gather(p.dt, x, w->ln1_g, w->ln1_b, ws + L.n1w, p.Lp, C, desc->ln_eps, p.geo, 1, st),
            "bwd: ln1 gather");
@@ -684,7 +693,9 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
     HIPCHECK(gemm(p.dt, ws + L.n2, w->fc1_w, p.L, hid, C, e, st), "bwd: fc1 forward");
     HIPCHECK(gelu_apply(ws + L.a1, ws + L.h, p.L * hid, 0, st), "bwd: gelu forward");
     // fc2
-    HIPCHECK(wgrad(dy, ws + L.h, g->fc2_w, g->fc2_b, part, p.L, C, hid, st), "bwd: fc2 weight gradient");
+    HIPCHECK(wgrad_partials(dy, ws + L.h, g->fc2_w, g->fc2_b, (float*)(ws + L.pfc2), p.L, C, hid, wj.job[wj.n++],
+                            st),
+             "bwd: fc2 weight gradient");
     EpiArgs eb{};
     eb.kind = Epi::kBias;
     eb.out = ws + L.dh;
@@ -692,7 +703,9 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
     HIPCHECK(gemm(p.dt, dy, ws + L.wTfc2, p.L, hid, C, eb, st), "bwd: fc2 input gradient");
     HIPCHECK(gelu_apply(ws + L.a1, ws + L.dh, p.L * hid, 1, st), "bwd: gelu backward");
     // fc1
-    HIPCHECK(wgrad(ws + L.dh, ws + L.n2, g->fc1_w, g->fc1_b, part, p.L, hid, C, st), "bwd: fc1 weight gradient");
+    HIPCHECK(wgrad_partials(ws + L.dh, ws + L.n2, g->fc1_w, g->fc1_b, (float*)(ws + L.pfc1), p.L, hid, C,
+                            wj.job[wj.n++], st),
+             "bwd: fc1 weight gradient");
     eb.out = ws + L.dn1;   // dLN2 output, token rows (the buffer is reused for dLN1 later)
     eb.ld_out = C;
     HIPCHECK(gemm(p.dt, ws + L.dh, ws + L.wTfc1, p.L, C, hid, eb, st), "bwd: fc1 input gradient");
@@ -704,7 +717,9 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
     return VSWIN_OK;
   };
   const GatherA ga{x, w->ln1_g, w->ln1_b, desc->ln_eps, 1, p.geo};
-  CHECK(msa_bwd_core(p, desc, w, g, ws, L, ws + L.dn1, st, true, ga, mid));
+  CHECK(msa_bwd_core(p, desc, w, g, ws, L, ws + L.dn1, st, true, ga, wj, mid));
+  // the four weight gradients from their partials, one launch
+  HIPCHECK(wgrad_reduce(wj, st), "bwd: weight gradient reduction");
   // LN1 (+ the residual path of z^ = x + ...)
   HIPCHECK(ln_bwd(0, x, w->ln1_g, ws + L.dn1, 1, ws + L.dzh, 0, dx, part, g->ln1_g, g->ln1_b, p.L, C, desc->ln_eps,
                   st),

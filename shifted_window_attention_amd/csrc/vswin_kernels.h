@@ -168,8 +168,24 @@ hipError_t zero_f32(float* p, int64_t n, hipStream_t st);
 // dW (NO x KI) = A^T B and db (NO, nullable) = column sums of A over M token rows,
 // A (M x NO), B (M x KI) bf16; fp32 outputs; part: wgrad_part_bytes
 size_t wgrad_part_bytes(int64_t M, int NO, int KI);
-hipError_t wgrad(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
-                 hipStream_t st);
+// One weight gradient's reduction: dW (n1 floats) and db (n - n1, or none)
+// from np partial rows of `stride` floats.
+struct WgradJob {
+  const float* part;
+  float* dW;
+  float* db;
+  int np;
+  int64_t n, n1, stride;
+};
+struct WgradJobs {
+  WgradJob job[4];
+  int n;
+};
+// the partial rows of dW = A^T B (and db = column sums of A) into `part`,
+// and the job that reduces them (wgrad_reduce, several jobs in one launch)
+hipError_t wgrad_partials(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
+                          WgradJob& job, hipStream_t st);
+hipError_t wgrad_reduce(const WgradJobs& jobs, hipStream_t st);
 
 // --- measurement helper (k_probe.hip) --------------------------------------
 // blocks x 512 threads of v_mfma_f32_16x16x32_bf16 chains: 8 per wave per
