@@ -309,27 +309,6 @@ __global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ p, in
   for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-// s_i = sum_p part[p * stride + i], one workgroup per output i (many
-// partials); out[i] = s_i for i < n1, else out2[i - n1]
-__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ part, float* __restrict__ out,
-                                                          float* __restrict__ out2, int nparts, int64_t n1,
-                                                          int64_t stride) {
-  __shared__ float red[256];
-  const int64_t i = blockIdx.x;
-  float s = 0.f;
-  for (int p = (int)threadIdx.x; p < nparts; p += 256) s += part[(int64_t)p * stride + i];
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    if (i < n1) out[i] = red[0];
-    else out2[i - n1] = red[0];
-  }
-}
-
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -396,7 +375,8 @@ size_t ln_bwd_part_bytes(int64_t rows, int C) { return (size_t)ln_bwd_blocks(row
 
 hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int res_fp32, const void* res,
                   int out_fp32, void* out, float* part, float* dg, float* db, int64_t rows, int C, float eps,
-                  hipStream_t st) {
+                  LnRed& red, hipStream_t st) {
+  red = LnRed{part, dg, db, 0, C};
   if (rows <= 0) return hipSuccess;
   if (C > 768) return hipErrorInvalidValue;
   const int nb = ln_bwd_blocks(rows, C);
@@ -425,9 +405,36 @@ hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int 
   else if (C <= 128) e = go(std::integral_constant<int, 1608>{});
   else if (C <= 256) e = go(std::integral_constant<int, 1616>{});
   else e = go(std::integral_constant<int, 6412>{});
-  if (e != hipSuccess) return e;
-  // dg = sum over workgroups of part[b][0:C], db of part[b][C:2C]
-  reduce_rows_kernel<<<dim3((unsigned)(2 * C)), dim3(256), 0, st>>>(part, dg, db, nb, C, 2 * C);
+  red.np = nb;
+  return e;
+}
+
+// dg = sum over workgroups of part[b][0:C], db of part[b][C:2C]; one
+// workgroup per output, blockIdx.y = job
+__global__ void __launch_bounds__(256) ln_reduce_kernel(const LnReds jobs) {
+  const LnRed& j = jobs.job[blockIdx.y];
+  const int i = blockIdx.x;
+  if (i >= 2 * j.C) return;   // the whole workgroup
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int p = (int)threadIdx.x; p < j.np; p += 256) s += j.part[(int64_t)p * 2 * j.C + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (i < j.C) j.dg[i] = red[0];
+    else j.db[i - j.C] = red[0];
+  }
+}
+
+hipError_t ln_reduce(const LnReds& jobs, hipStream_t st) {
+  if (jobs.n <= 0) return hipSuccess;
+  int cmax = 1;
+  for (int i = 0; i < jobs.n; ++i) cmax = jobs.job[i].C > cmax ? jobs.job[i].C : cmax;
+  ln_reduce_kernel<<<dim3((unsigned)(2 * cmax), (unsigned)jobs.n), dim3(256), 0, st>>>(jobs);
   return hipGetLastError();
 }
 

@@ -276,8 +276,9 @@ vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weigh
 struct BwdWs {
   size_t n1w, q, k, v, o, tab, lse;           // forward recompute (window rows)
   size_t zh, n2, a1, h, dh, dzh;              // block only
-  size_t dyw, dout, dqkv, dn1w, dn1, part, attn;
-  size_t pproj, pqkv, pfc2, pfc1;              // weight-gradient partials (fc: block only)
+  size_t dyw, dout, dqkv, dn1w, dn1, attn;
+  size_t part;                                 // block only
+  size_t pproj, pqkv, pfc2, pfc1, pln2;        // weight-gradient partials (fc, ln2: block only)
   size_t wTqkv, wTproj, wTfc2, wTfc1;          // transposed weights (fc: block only)
   size_t block_bytes, msa_bytes;
 };
@@ -312,7 +313,6 @@ BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
   w.dn1 = take(tok);
   w.wTqkv = take((size_t)3 * p.C * p.C * 2);
   w.wTproj = take((size_t)p.C * p.C * 2);
-  w.part = take(ln_bwd_part_bytes(p.L, p.C));
   w.pproj = take(wgrad_part_bytes(p.Lp, p.C, p.C));
   w.pqkv = take(wgrad_part_bytes(p.Lp, 3 * p.C, p.C));
   w.attn = take(attention_bwd_workspace_bytes(attn_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, d->flags)));
@@ -327,6 +327,8 @@ BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
   w.wTfc1 = take((size_t)p.hid * p.C * 2);
   w.pfc2 = take(wgrad_part_bytes(p.L, p.C, p.hid));
   w.pfc1 = take(wgrad_part_bytes(p.L, p.hid, p.C));
+  w.part = take(ln_bwd_part_bytes(p.L, p.C));   // LN1's dγ/dβ partials
+  w.pln2 = take(ln_bwd_part_bytes(p.L, p.C));
   w.block_bytes = off;
   return w;
 }
@@ -671,6 +673,8 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
   const int C = p.C, hid = p.hid;
   float* part = (float*)(ws + L.part);
   WgradJobs wj{};
+  LnReds lr{};
+  lr.n = 2;
   // LN1 + pad + roll + partition of x
   HIPCHECK(ln_gather(p.dt, x, w->ln1_g, w->ln1_b, ws + L.n1w, p.Lp, C, desc->ln_eps, p.geo, 1, st),
            "bwd: ln1 gather");
@@ -710,8 +714,8 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
     eb.ld_out = C;
     HIPCHECK(gemm(p.dt, ws + L.dh, ws + L.wTfc1, p.L, C, hid, eb, st), "bwd: fc1 input gradient");
     // LN2 (+ the residual path of y = z^ + ...)
-    HIPCHECK(ln_bwd(1, ws + L.zh, w->ln2_g, ws + L.dn1, 0, dy, 1, ws + L.dzh, part, g->ln2_g, g->ln2_b, p.L, C,
-                    desc->ln_eps, st),
+    HIPCHECK(ln_bwd(1, ws + L.zh, w->ln2_g, ws + L.dn1, 0, dy, 1, ws + L.dzh, (float*)(ws + L.pln2), g->ln2_g,
+                    g->ln2_b, p.L, C, desc->ln_eps, lr.job[1], st),
              "bwd: ln2 backward");
     HIPCHECK(gather_f32_bf16((const float*)(ws + L.dzh), ws + L.dyw, p.Lp, C, p.geo, st), "bwd: gather dz");
     return VSWIN_OK;
@@ -722,8 +726,10 @@ vswin_status vswin_block_bwd(const vswin_desc* desc, const void* x, const vswin_
   HIPCHECK(wgrad_reduce(wj, st), "bwd: weight gradient reduction");
   // LN1 (+ the residual path of z^ = x + ...)
   HIPCHECK(ln_bwd(0, x, w->ln1_g, ws + L.dn1, 1, ws + L.dzh, 0, dx, part, g->ln1_g, g->ln1_b, p.L, C, desc->ln_eps,
-                  st),
+                  lr.job[0], st),
            "bwd: ln1 backward");
+  // dγ, dβ of both LayerNorms from their partials, one launch
+  HIPCHECK(ln_reduce(lr, st), "bwd: layernorm gradient reduction");
   return VSWIN_OK;
 }
 

@@ -160,9 +160,22 @@ hipError_t gather_f32_bf16(const float* in, void* out, int64_t slots, int C, con
 // LayerNorm backward over rows of C (<= 768): out = dLN(x; g)/dx applied to dy, plus res (nullable);
 // dg, db (fp32, C) from per-wave partials in part (ln_bwd_part_bytes)
 size_t ln_bwd_part_bytes(int64_t rows, int C);
+// the reduction of one LayerNorm backward's dg / db partials (np of them,
+// 2C floats each); several run as one ln_reduce launch
+struct LnRed {
+  const float* part;
+  float* dg;
+  float* db;
+  int np, C;
+};
+struct LnReds {
+  LnRed job[2];
+  int n;
+};
+hipError_t ln_reduce(const LnReds& jobs, hipStream_t st);
 hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int res_fp32, const void* res,
                   int out_fp32, void* out, float* part, float* dg, float* db, int64_t rows, int C, float eps,
-                  hipStream_t st);
+                  LnRed& red, hipStream_t st);
 // p[0 .. n) = 0 (a kernel, so that it may sit inside a captured graph); p nullable
 hipError_t zero_f32(float* p, int64_t n, hipStream_t st);
 // dW (NO x KI) = A^T B and db (NO, nullable) = column sums of A over M token rows,
