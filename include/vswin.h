@@ -228,19 +228,39 @@ vswin_status vswin_index_map(const vswin_desc* desc, int32_t* map, uint8_t* regi
                              void* stream);
 
 /* Pad + roll(-shift) + partition of x (B,T,H,W,C) into windows
- * (num_windows, N, C), pad slots zero.  Bit-exact permutation.              */
+ * (num_windows, N, C), pad slots zero (Video Swin Transformer, §3.2 and its
+ * pseudo-code for window_msa: roll by the negated shift, pad to window
+ * multiples, partition; the pad-before-roll order and end-of-axis zeros follow
+ * the paper-vs-code notes, "Mask value and padding").  Windows are ordered
+ * (b, wt, wh, ww) and slots (pt, ph, pw), both row-major.  x and windows are
+ * device buffers of desc->dtype; windows holds num_windows * N * C elements
+ * (vswin_plan_query).  Bit-exact permutation: no arithmetic on the values.
+ * Argument errors (bad descriptor, null pointers) return
+ * VSWIN_ERR_INVALID_ARG before anything is enqueued.                       */
 vswin_status vswin_partition_fwd(const vswin_desc* desc, const void* x, void* windows,
                                  void* stream);
 
 /* Inverse: reverse partition + roll(+shift) + crop of windows
- * (num_windows, N, C) into y (B,T,H,W,C); with residual != NULL,
- * y = residual + unpartitioned windows.  Pad slots are dropped.             */
+ * (num_windows, N, C) into y (B,T,H,W,C) (Video Swin Transformer, §3.2
+ * pseudo-code for window_msa: merge the windows back, roll by +shift, crop the
+ * padding); with residual != NULL, y = residual + unpartitioned windows in
+ * desc->dtype arithmetic rounded once (the first residual of eq. 1).  Pad
+ * slots are dropped.  All pointers are device buffers of desc->dtype;
+ * residual and y hold B*T*H*W*C elements.  Without a residual the result is
+ * a bit-exact permutation.  Argument errors return VSWIN_ERR_INVALID_ARG
+ * before anything is enqueued.                                               */
 vswin_status vswin_reverse_fwd(const vswin_desc* desc, const void* windows,
                                const void* residual, void* y, void* stream);
 
 /* LayerNorm over the last axis of `rows` rows of width C (biased variance):
- * y = (x - mean) / sqrt(var + eps) * g + b.  x of in_dtype, y of out_dtype,
- * g and b of out_dtype.                                                      */
+ * y = (x - mean) / sqrt(var + eps) * g + b.  It is the LN of eq. 1 (Video
+ * Swin Transformer, §3.1, Method step 3: pre-norm before the MSA and the
+ * MLP), of patch merging (CSDN walk-through, PatchMerging: LN over the 4C
+ * concatenation) and the backbone's final norm.  Statistics in fp32.  x
+ * (rows * C of in_dtype), g and b (C of out_dtype), y (rows * C of out_dtype)
+ * are device buffers.  rows = 0 is a no-op; C odd or outside 2..4096, eps <= 0,
+ * a bad dtype or null pointers return VSWIN_ERR_INVALID_ARG before anything
+ * is enqueued.                                                               */
 vswin_status vswin_layernorm_fwd(int64_t rows, int32_t C, vswin_dtype in_dtype,
                                  vswin_dtype out_dtype, const void* x, const void* g,
                                  const void* b, float eps, void* y, void* stream);

@@ -190,6 +190,54 @@ def _desc_for(x: torch.Tensor, heads, window, shift, eps, flags, mlp_hidden) -> 
                      eps=eps, flags=flags)
 
 
+# weights the C ABI accepts as NULL (their term is then zero)
+_OPTIONAL = ("qkv_b", "proj_b", "fc1_b", "fc2_b")
+
+
+def _weight_shapes(C: int, heads: int, window: Sequence[int], hid: int) -> Dict[str, tuple]:
+    """PyTorch layouts of one block's tensors; the table is sized by the
+    requested (unclamped) window."""
+    P, Mh, Mw = (int(v) for v in window)
+    return {"ln1_g": (C,), "ln1_b": (C,), "qkv_w": (3 * C, C), "qkv_b": (3 * C,),
+            "proj_w": (C, C), "proj_b": (C,), "rpb_table": ((2 * P - 1) * (2 * Mh - 1) * (2 * Mw - 1), heads),
+            "ln2_g": (C,), "ln2_b": (C,), "fc1_w": (hid, C), "fc1_b": (hid,),
+            "fc2_w": (C, hid), "fc2_b": (C,)}
+
+
+def _like(t: torch.Tensor, ref: torch.Tensor, what: str) -> None:
+    if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or t.device != ref.device:
+        raise ValueError(f"{what} must match x: shape {tuple(ref.shape)}, {ref.dtype}, {ref.device} "
+                         f"(got {tuple(t.shape)}, {t.dtype}, {t.device})")
+
+
+def _check_weights(x: torch.Tensor, w: Dict[str, torch.Tensor], heads: int, window: Sequence[int],
+                   names: Sequence[str]) -> int:
+    """Every weight the call reads must have x's dtype and device and its
+    block layout, so that no kernel reads past an allocation.  Returns the
+    MLP width (fc1_w rows, or 4C when the call does not read fc1_w)."""
+    C = x.shape[-1]
+    if x.dim() != 5:
+        raise ValueError(f"x must be (B, T, H, W, C), got shape {tuple(x.shape)}")
+    if heads <= 0 or C % heads:
+        raise ValueError(f"C={C} is not a multiple of heads={heads}")
+    fc1 = w.get("fc1_w")
+    hid = int(fc1.shape[0]) if ("fc1_w" in names and fc1 is not None and fc1.dim() == 2) else 4 * C
+    shapes = _weight_shapes(C, heads, window, hid)
+    for n in names:
+        t = w.get(n)
+        if t is None:
+            if n in _OPTIONAL:
+                continue
+            raise ValueError(f"weight {n} is missing")
+        if tuple(t.shape) != shapes[n]:
+            raise ValueError(f"weight {n} must have shape {shapes[n]}, got {tuple(t.shape)}")
+        if t.dtype != x.dtype:
+            raise ValueError(f"weight {n} must be {x.dtype} like x, got {t.dtype}")
+        if t.device != x.device:
+            raise ValueError(f"weight {n} is on {t.device}, x on {x.device}")
+    return hid
+
+
 def _weights(w: Dict[str, torch.Tensor]) -> BlockWeights:
     bw = BlockWeights()
     for name, _ in BlockWeights._fields_:
@@ -211,10 +259,11 @@ def vswin_block_fwd(x: torch.Tensor, w: Dict[str, torch.Tensor], heads: int, win
                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
     """One Video Swin block (eq. 1) on x (B, T, H, W, C); returns y of x's shape."""
-    hid = w["fc1_w"].shape[0]
+    hid = _check_weights(x, w, heads, window, GRAD_NAMES)
     d = _desc_for(x, heads, window, shift, eps, flags, hid)
     plan = vswin_plan_query(d)
     y = torch.empty_like(x) if out is None else out
+    _like(y, x, "out")
     ws = _workspace(plan["workspace_bytes"], x.device, workspace)
     bw = _weights(w)
     _check(lib().vswin_block_fwd(ctypes.byref(d), _ptr(x), ctypes.byref(bw), _ptr(y), _ptr(ws),
@@ -227,9 +276,11 @@ def vswin_window_msa_fwd(x_norm: torch.Tensor, w: Dict[str, torch.Tensor], heads
                          flags: int = 0, out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """The (S)W-MSA branch (§3.2) on the LayerNorm output; no residual."""
+    _check_weights(x_norm, w, heads, window, MSA_GRAD_NAMES)
     d = _desc_for(x_norm, heads, window, shift, eps, flags, 4 * x_norm.shape[-1])
     plan = vswin_plan_query(d)
     y = torch.empty_like(x_norm) if out is None else out
+    _like(y, x_norm, "out")
     ws = _workspace(plan["msa_workspace_bytes"], x_norm.device, workspace)
     bw = _weights(w)
     _check(lib().vswin_window_msa_fwd(ctypes.byref(d), _ptr(x_norm), ctypes.byref(bw), _ptr(y),
@@ -243,8 +294,19 @@ def vswin_attention_fwd(desc: Desc, q: torch.Tensor, k: torch.Tensor, v: torch.T
     """Attention core on projected windows in the block's internal layout (see
     vswin_attention_fwd in include/vswin.h): o (nW, N, C), heads concatenated."""
     plan = vswin_plan_query(desc)
-    o = out if out is not None else torch.empty((plan["num_windows"], plan["tokens_per_window"], desc.C),
-                                                 dtype=q.dtype, device=q.device)
+    nW, N, C, h = plan["num_windows"], plan["tokens_per_window"], desc.C, desc.heads
+    n_qkv = nW * h * N * (C // h)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.numel() != n_qkv or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must hold num_windows*heads*N*d = {n_qkv} elements of {q.dtype} "
+                             f"(got {t.numel()} of {t.dtype} on {t.device})")
+    P, Mh, Mw = (int(v_) for v_ in desc.window)
+    rows = (2 * P - 1) * (2 * Mh - 1) * (2 * Mw - 1)
+    if tuple(table.shape) != (rows, h) or table.dtype != q.dtype or table.device != q.device:
+        raise ValueError(f"table must be ({rows}, {h}) {q.dtype}, got {tuple(table.shape)} {table.dtype}")
+    o = out if out is not None else torch.empty((nW, N, C), dtype=q.dtype, device=q.device)
+    if o.numel() != nW * N * C or o.dtype != q.dtype or o.device != q.device:
+        raise ValueError(f"out must hold num_windows*N*C = {nW * N * C} elements of {q.dtype}")
     ws = _workspace(plan["attention_workspace_bytes"], q.device, workspace)
     _check(lib().vswin_attention_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(table), _ptr(o),
                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
@@ -295,6 +357,15 @@ def vswin_bwd_workspace_query(desc: Desc) -> Dict[str, int]:
 def _grads(w: Dict[str, torch.Tensor], names, grads: Optional[Dict[str, torch.Tensor]]):
     """fp32 gradient buffers shaped like the weights (allocated unless given)."""
     out = {} if grads is None else dict(grads)
+    for n, t in out.items():
+        if n not in names:
+            raise ValueError(f"no gradient {n} is written by this call (it writes {', '.join(names)})")
+        ref = w.get(n)
+        if ref is None:
+            raise ValueError(f"gradient {n} given for an absent weight")
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(ref.shape) or t.device != ref.device:
+            raise ValueError(f"gradient {n} must be float32 with shape {tuple(ref.shape)} on {ref.device} "
+                             f"(got {t.dtype}, {tuple(t.shape)}, {t.device})")
     for n in names:
         if n not in out and w.get(n) is not None:
             out[n] = torch.empty(w[n].shape, dtype=torch.float32, device=w[n].device)
@@ -309,12 +380,14 @@ def vswin_block_bwd(x: torch.Tensor, w: Dict[str, torch.Tensor], dy: torch.Tenso
                     dx: Optional[torch.Tensor] = None, grads: Optional[Dict[str, torch.Tensor]] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None):
     """Backward of vswin_block_fwd: (dx, {weight name: fp32 gradient})."""
-    hid = w["fc1_w"].shape[0]
+    hid = _check_weights(x, w, heads, window, GRAD_NAMES)
+    _like(dy, x, "dy")
+    dxo = torch.empty_like(x) if dx is None else dx
+    _like(dxo, x, "dx")
+    g, bg = _grads(w, GRAD_NAMES, grads)
     d = _desc_for(x, heads, window, shift, eps, flags, hid)
     nbytes = vswin_bwd_workspace_query(d)["block"]
-    dxo = torch.empty_like(x) if dx is None else dx
     ws = _workspace(nbytes, x.device, workspace)
-    g, bg = _grads(w, GRAD_NAMES, grads)
     bw = _weights(w)
     _check(lib().vswin_block_bwd(ctypes.byref(d), _ptr(x), ctypes.byref(bw), _ptr(dy), _ptr(dxo),
                                  ctypes.byref(bg), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
@@ -326,11 +399,14 @@ def vswin_window_msa_bwd(x_norm: torch.Tensor, w: Dict[str, torch.Tensor], dy: t
                          dx: Optional[torch.Tensor] = None, grads: Optional[Dict[str, torch.Tensor]] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None):
     """Backward of vswin_window_msa_fwd: (dx_norm, {qkv/proj/table name: fp32 gradient})."""
+    _check_weights(x_norm, w, heads, window, MSA_GRAD_NAMES)
+    _like(dy, x_norm, "dy")
+    dxo = torch.empty_like(x_norm) if dx is None else dx
+    _like(dxo, x_norm, "dx")
+    g, bg = _grads(w, MSA_GRAD_NAMES, grads)
     d = _desc_for(x_norm, heads, window, shift, eps, flags, 4 * x_norm.shape[-1])
     nbytes = vswin_bwd_workspace_query(d)["msa"]
-    dxo = torch.empty_like(x_norm) if dx is None else dx
     ws = _workspace(nbytes, x_norm.device, workspace)
-    g, bg = _grads(w, MSA_GRAD_NAMES, grads)
     bw = _weights(w)
     _check(lib().vswin_window_msa_bwd(ctypes.byref(d), _ptr(x_norm), ctypes.byref(bw), _ptr(dy), _ptr(dxo),
                                       ctypes.byref(bg), _ptr(ws), ws.numel() * ws.element_size(),

@@ -224,3 +224,83 @@ def test_issue_probe_rejects_bad_arguments():
     assert L.vswin_issue_probe(None, 1, 1, 4, None) == -1
     assert L.vswin_issue_probe(None, 0, 1, 0, None) == -1
     assert L.vswin_issue_probe(None, 1, 1, 0, None) == -1   # NULL out
+
+
+def _host_block(C=32, heads=2, window=(2, 7, 7), dtype="fp32"):
+    import torch
+    p = synth.gen_block_params(C, heads, (2 * window[0] - 1) * (2 * window[1] - 1) * (2 * window[2] - 1), 4,
+                               np.random.SeedSequence(3), dtype)
+    td = torch.float32 if dtype == "fp32" else torch.bfloat16
+    w = {k: torch.from_numpy(v).to(td) for k, v in p.items()}
+    x = torch.zeros((1, 4, 14, 14, C), dtype=td)
+    return x, w
+
+
+@pytest.mark.parametrize("mutate", [
+    "table for another window", "qkv_w transposed", "weight dtype", "proj_w missing", "fc2_w width",
+    "heads not dividing C",
+])
+def test_binding_rejects_mismatched_weights(mutate):
+    """The binding checks every weight's shape, dtype and device against x
+    before any library call, so a mismatch is a ValueError, not a kernel
+    reading past an allocation."""
+    import torch
+    x, w = _host_block()
+    heads = 2
+    if mutate == "table for another window":
+        w["rpb_table"] = torch.zeros((15 * 13 * 13, 2))
+    elif mutate == "qkv_w transposed":
+        w["qkv_w"] = w["qkv_w"].t().contiguous()
+    elif mutate == "weight dtype":
+        w["fc1_w"] = w["fc1_w"].to(torch.bfloat16)
+    elif mutate == "proj_w missing":
+        del w["proj_w"]
+    elif mutate == "fc2_w width":
+        w["fc2_w"] = torch.zeros((32, 100))
+    elif mutate == "heads not dividing C":
+        heads = 3
+    for fn in (vs.vswin_block_fwd, vs.vswin_window_msa_fwd):
+        if fn is vs.vswin_window_msa_fwd and mutate in ("weight dtype", "fc2_w width"):
+            continue          # the MSA branch does not read the MLP weights
+        with pytest.raises(ValueError):
+            fn(x, w, heads, (2, 7, 7), (1, 3, 3))
+    with pytest.raises(ValueError):
+        vs.vswin_block_bwd(x, w, torch.zeros_like(x), heads, (2, 7, 7), (1, 3, 3))
+
+
+def test_binding_rejects_mismatched_outputs_and_grads():
+    import torch
+    x, w = _host_block()
+    args = (w, 2, (2, 7, 7), (1, 3, 3))
+    with pytest.raises(ValueError):
+        vs.vswin_block_fwd(x, *args, out=torch.zeros((1, 4, 14, 14, 32), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        vs.vswin_window_msa_fwd(x, *args, out=torch.zeros((1, 4, 14, 13, 32)))
+    with pytest.raises(ValueError):
+        vs.vswin_block_bwd(x, w, torch.zeros((1, 4, 14, 14, 16)), 2, (2, 7, 7), (1, 3, 3))
+    with pytest.raises(ValueError):
+        vs.vswin_block_bwd(x, w, torch.zeros_like(x), 2, (2, 7, 7), (1, 3, 3), dx=torch.zeros((5,)))
+    with pytest.raises(ValueError):        # gradients are fp32 and shaped like their weight
+        vs.vswin_block_bwd(x, w, torch.zeros_like(x), 2, (2, 7, 7), (1, 3, 3),
+                           grads={"qkv_w": torch.zeros((96, 32), dtype=torch.bfloat16)})
+    with pytest.raises(ValueError):
+        vs.vswin_block_bwd(x, w, torch.zeros_like(x), 2, (2, 7, 7), (1, 3, 3),
+                           grads={"proj_w": torch.zeros((32, 33))})
+    with pytest.raises(ValueError):        # the MSA backward writes no MLP gradient
+        vs.vswin_window_msa_bwd(x, w, torch.zeros_like(x), 2, (2, 7, 7), (1, 3, 3),
+                                grads={"fc1_w": torch.zeros((128, 32))})
+
+
+def test_binding_attention_core_checks_buffer_sizes():
+    import torch
+    d = vs.make_desc(1, 16, 14, 14, 96, 3, (8, 7, 7), (4, 3, 3))
+    plan = vs.vswin_plan_query(d)
+    nW, N = plan["num_windows"], plan["tokens_per_window"]
+    q = torch.zeros((nW, 3, N, 32), dtype=torch.bfloat16)
+    tab = torch.zeros((15 * 13 * 13, 3), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        vs.vswin_attention_fwd(d, q, q, q[:, :, :-1], tab)
+    with pytest.raises(ValueError):
+        vs.vswin_attention_fwd(d, q, q, q, tab[:-1])
+    with pytest.raises(ValueError):
+        vs.vswin_attention_fwd(d, q, q, q, tab, out=torch.zeros((nW, N, 95), dtype=torch.bfloat16))

@@ -309,39 +309,59 @@ def test_workload3_bf16_six_blocks():
     _stack_check(x, params, synth.WORKLOADS[3].shape, "bf16", label="wl3")
 
 
-def test_workload4_bf16_pair_sampled():
-    say("workload 4: Swin-B stage-1 padded pair, B=8 (sampled tokens)")
-    wl = synth.WORKLOADS[4]
-    s = wl.shape
-    x, params = synth.gen_workload(4)
-    L = s.tokens
-    rng = np.random.default_rng(44)
-    # random tokens plus the last rows/columns next to the pads and the clip corners
-    edge = [((b * s.T + t) * s.H + h) * s.W + w for b in (0, s.B - 1) for t in (0, s.T - 1)
-            for h in (0, s.H - 4, s.H - 1) for w in (0, s.W - 4, s.W - 1)]
-    toks = sorted(set(rng.choice(L, 160, replace=False).tolist() + edge))
-    xt = dev(x, "bf16")
-    for k, p in enumerate(params):
-        shift = (0, 0, 0) if k % 2 == 0 else s.shift
-        yt = vs.vswin_block_fwd(xt, dev_params(p, "bf16"), s.heads, s.window, shift)
-        xin = host64(xt)
-        _, ref = ov.block_sampled(xin, p, s.heads, s.window, shift, toks)
-        got = host64(yt).reshape(-1, s.C)[toks]
-        check(got, ref, "bf16", f"wl4 block {k} ({len(toks)} sampled tokens)")
-        xt = yt
+def test_workload3_bf16_six_blocks_stress():
+    """Workload 3's shapes (C = 384: the generic GEMM + unfused MLP path) at
+    stress init, where a missing bias, a flipped offset sign or a wrong mask
+    moves the outputs far beyond the bar."""
+    say("workload 3 shapes, stress init")
+    x, params = synth.gen_workload(3, init="stress")
+    _stack_check(x, params, synth.WORKLOADS[3].shape, "bf16", label="wl3 stress")
 
 
-def test_workload5_backbone():
-    say("workload 5: Swin-T backbone B=2 (per-block teacher-forced)")
-    cfg = synth.WORKLOADS[5].backbone
-    video = synth.gen_video(cfg["B"], cfg["in_chans"], cfg["frames"], cfg["height"], cfg["width"], 5, "bf16")
-    params = synth.gen_backbone_params(cfg, 5, "bf16")
-    dparams = {
+@pytest.mark.parametrize("init", ["spec", "stress"])
+def test_workload4_bf16_pair_full(init):
+    """Workload 4 (Swin-B stage 1, B=8, (16,60,60,128) padded to (16,63,63);
+    the C = 128 fused MLP with its erf) on every output token of both blocks
+    of the pair, at spec and at stress init."""
+    say(f"workload 4: Swin-B stage-1 padded pair, B=8, every token, {init} init")
+    x, params = synth.gen_workload(4, init=init)
+    _stack_check(x, params, synth.WORKLOADS[4].shape, "bf16", label=f"wl4 {init}")
+
+
+def test_block_c128_padded_stress_full():
+    """C = 128 (the fused MLP with the Abramowitz-Stegun erf) on a small padded
+    grid with B = 2, every output token, regular and shifted, stress init."""
+    C, heads, window = 128, 4, (8, 7, 7)
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=41)
+    x = _rng_tokens((2, 16, 12, 13, C), "bf16", 14)
+    for shift in ((0, 0, 0), (4, 3, 3)):
+        say(f"C=128 padded block B=2, stress, shift {shift}")
+        y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
+        _, ref = oracle.block(x, p, heads, window, shift)
+        check(host64(y), ref, "bf16", f"C=128 padded block shift {shift}")
+
+
+def _backbone_dev(params):
+    return {
         "embed_w": dev(params["embed_w"], "bf16"), "embed_b": dev(params["embed_b"], "bf16"),
         "stages": [[dev_params(p, "bf16") for p in st] for st in params["stages"]],
         "merges": [dev_params(m, "bf16") for m in params["merges"]],
         "norm_g": dev(params["norm_g"], "bf16"), "norm_b": dev(params["norm_b"], "bf16"),
     }
+
+
+def test_workload5_backbone():
+    """Workload 5 (Swin-T backbone, B=2 clips of 3x32x224x224).  Gate: every
+    block, merge, the embedding and the final LN teacher-forced (each compared
+    with the oracle fed the GPU's own input).  Report: the composed
+    vswin_backbone_fwd against oracle.backbone() on the same clip, end to end
+    in fp64, per stage (the drift of bf16 storage between kernels, which no
+    per-block bar covers)."""
+    say("workload 5: Swin-T backbone B=2 (per-block teacher-forced, then end to end)")
+    cfg = synth.WORKLOADS[5].backbone
+    video = synth.gen_video(cfg["B"], cfg["in_chans"], cfg["frames"], cfg["height"], cfg["width"], 5, "bf16")
+    params = synth.gen_backbone_params(cfg, 5, "bf16")
+    dparams = _backbone_dev(params)
     vt = dev(video, "bf16")
     x = vs.vswin_patch_embed_fwd(vt, dparams["embed_w"], dparams["embed_b"])
     check(host64(x), oracle.patch_embed(video, params["embed_w"], params["embed_b"]), "bf16", "patch embed")
@@ -360,8 +380,42 @@ def test_workload5_backbone():
             x = y
     out = vs.vswin_layernorm_fwd(x, dparams["norm_g"], dparams["norm_b"])
     check(host64(out), oracle.layer_norm(host64(x), params["norm_g"], params["norm_b"]), "bf16", "final LN")
-    full = vs.vswin_backbone_fwd(vt, dparams, cfg)
-    assert torch.equal(full, out)         # the orchestrated forward is the same call sequence
+    # the composed forward: the same call sequence, so the same bits ...
+    full, trace = vs.vswin_backbone_fwd(vt, dparams, cfg, collect=True)
+    assert torch.equal(full, out)
+    # ... and end to end against the oracle's own backbone (no teacher forcing)
+    ref_out, ref_trace = oracle.backbone(video.astype(np.float64), params, cfg, collect=True)
+    k = 0
+    for i, depth in enumerate(cfg["depths"]):
+        k += depth
+        e = np.abs(host64(trace[k - 1][1]) - ref_trace[k - 1][1])
+        say(f"  end-to-end drift after stage {i + 1}: max-abs {e.max():.3e} mean-abs {e.mean():.3e} "
+            f"(output scale {np.abs(ref_trace[k - 1][1]).max():.2f})")
+    e = np.abs(host64(full) - ref_out)
+    say(f"  end-to-end drift of the final LN output: max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    # drift over 12 blocks and 3 merges of bf16 storage is reported, not gated
+    # by the per-block bar; a composition mistake (stage order, shift
+    # alternation, merge placement, the stage-4 clamp) moves the LN output by O(1)
+    assert e.mean() <= 3e-2, f"end-to-end mean-abs drift {e.mean():.3e}"
+
+
+def test_workload5_stage_blocks_stress():
+    """One regular + shifted pair at each deeper Swin-T stage's shape (B=2;
+    stage 2 (16,28,28,192), stage 3 (16,14,14,384), stage 4 (16,7,7,768) with
+    its clamped shift (4,0,0)) at stress init, every output token."""
+    cfg = synth.WORKLOADS[5].backbone
+    params = synth.gen_backbone_params(cfg, 15, "bf16", init="stress")
+    for i, (H, C) in enumerate([(28, 192), (14, 384), (7, 768)], start=1):
+        x = _rng_tokens((2, 16, H, H, C), "bf16", 60 + i)
+        xt = dev(x, "bf16")
+        for j in range(2):
+            shift = (0, 0, 0) if j == 0 else (4, 3, 3)
+            say(f"stage {i + 1} shapes, stress init, block {j}")
+            p = params["stages"][i][j]
+            y = vs.vswin_block_fwd(xt, dev_params(p, "bf16"), cfg["heads"][i], cfg["window"], shift)
+            _, ref = oracle.block(host64(xt), p, cfg["heads"][i], cfg["window"], shift)
+            check(host64(y), ref, "bf16", f"stage {i + 1} stress block {j}")
+            xt = y
 
 
 def test_block_is_deterministic():
