@@ -142,6 +142,23 @@ vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* vswin_block_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and result, with the scratch taken from a
+ * static device array of VSWIN_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per GPU the library runs on, held until the process ends) instead of
+ * a caller workspace.  The call allocates and frees nothing.  A block whose
+ * scratch need exceeds the array (at most plan.workspace_bytes; the Swin-T
+ * stage-1 to stage-4 blocks at B = 1 and the stage-1 block at B = 2 fit)
+ * returns VSWIN_ERR_WORKSPACE before anything is enqueued.  Every call on a
+ * GPU shares that GPU's array and leaves its own contents there: calls that
+ * overlap on one GPU (other streams, other host threads) race, so serialise
+ * them.  Other arguments and errors as vswin_block_fwd.                    */
+#define VSWIN_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+vswin_status vswin_block_fwd_noalloc(const vswin_desc* desc, const void* x,
+                                     const vswin_block_weights* w, void* y,
+                                     void* stream);
+
 /* The window attention branch alone (the pages' window_msa, §3.2 / eq. 2):
  * x_norm (B,T,H,W,C) is the LayerNorm output; y (same shape) receives the
  * projected attention output with no residual.  Zero padding is appended at

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "VswinError", "lib", "Desc", "BlockWeights", "PlanInfo", "make_desc",
-    "vswin_plan_query", "vswin_block_fwd", "vswin_window_msa_fwd", "vswin_attention_fwd",
+    "vswin_plan_query", "vswin_block_fwd", "vswin_block_fwd_noalloc", "vswin_window_msa_fwd", "vswin_attention_fwd",
     "vswin_index_map",
     "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
     "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd", "vswin_mfma_rate_probe",
@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "vswin_plan_query": (i32, [pdesc, ctypes.POINTER(PlanInfo)]),
         "vswin_block_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
+        "vswin_block_fwd_noalloc": (i32, [pdesc, vp, pw, vp, vp]),
         "vswin_window_msa_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
         "vswin_attention_fwd": (i32, [pdesc, vp, vp, vp, vp, vp, vp, sz, vp]),
         "vswin_index_map": (i32, [pdesc, vp, vp, vp]),
@@ -268,6 +269,20 @@ def vswin_block_fwd(x: torch.Tensor, w: Dict[str, torch.Tensor], heads: int, win
     bw = _weights(w)
     _check(lib().vswin_block_fwd(ctypes.byref(d), _ptr(x), ctypes.byref(bw), _ptr(y), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+def vswin_block_fwd_noalloc(x: torch.Tensor, w: Dict[str, torch.Tensor], heads: int, window: Sequence[int],
+                            shift: Sequence[int], *, eps: float = 1e-5, flags: int = 0,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """vswin_block_fwd on the library's static scratch array (the C entry
+    point allocates nothing; calls overlapping on one GPU race)."""
+    hid = _check_weights(x, w, heads, window, GRAD_NAMES)
+    d = _desc_for(x, heads, window, shift, eps, flags, hid)
+    y = torch.empty_like(x) if out is None else out
+    _like(y, x, "out")
+    bw = _weights(w)
+    _check(lib().vswin_block_fwd_noalloc(ctypes.byref(d), _ptr(x), ctypes.byref(bw), _ptr(y), _stream(stream)))
     return y
 
 

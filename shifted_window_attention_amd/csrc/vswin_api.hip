@@ -333,49 +333,9 @@ BwdWs bwd_layout(const Plan& p, const vswin_desc* d) {
   return w;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* vswin_last_error(void) { return g_err; }
-int32_t vswin_abi_version(void) { return VSWIN_ABI_VERSION; }
-
-const char* vswin_status_string(vswin_status s) {
-  switch (s) {
-    case VSWIN_OK: return "ok";
-    case VSWIN_ERR_INVALID_ARG: return "invalid argument";
-    case VSWIN_ERR_UNSUPPORTED: return "unsupported";
-    case VSWIN_ERR_WORKSPACE: return "workspace too small";
-    case VSWIN_ERR_HIP: return "HIP error";
-  }
-  return "unknown status";
-}
-
-vswin_status vswin_plan_query(const vswin_desc* desc, vswin_plan* plan) {
-  if (!plan) return fail(VSWIN_ERR_INVALID_ARG, "plan is NULL");
-  Plan p{};
-  CHECK(make_plan(desc, p, false));
-  plan->eff_window[0] = p.geo.P; plan->eff_window[1] = p.geo.Mh; plan->eff_window[2] = p.geo.Mw;
-  plan->eff_shift[0] = p.geo.st; plan->eff_shift[1] = p.geo.sh; plan->eff_shift[2] = p.geo.sw;
-  plan->padded[0] = p.geo.Tp; plan->padded[1] = p.geo.Hp; plan->padded[2] = p.geo.Wp;
-  plan->tokens_per_window = p.N;
-  plan->num_windows = p.nW;
-  plan->tokens = p.L;
-  plan->masked = p.use_mask ? 1 : 0;
-  plan->fast_attention = p.fast ? 1 : 0;
-  plan->workspace_bytes = p.ws_block;
-  plan->msa_workspace_bytes = p.ws_msa;
-  plan->attention_workspace_bytes = p.ws_attn;
-  // geometry is filled in; now the constraints of the compute entry points
-  Plan q{};
-  return make_plan(desc, q, true);
-}
-
-vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w, void* y,
-                             void* workspace, size_t workspace_bytes, void* stream) {
-  Plan p{};
-  CHECK(make_plan(desc, p));
-  if (p.L == 0) return VSWIN_OK;   // empty batch: nothing to read or write
+// Argument checks of the block forward on a planned descriptor (before
+// anything is enqueued).
+vswin_status block_fwd_check(const void* x, const vswin_block_weights* w, void* y) {
   CHECK(check_ptr(x, "x"));
   CHECK(check_ptr(y, "y"));
   if (x == y) return fail(VSWIN_ERR_INVALID_ARG, "x and y must not alias");
@@ -388,14 +348,20 @@ vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x, const vswin_
   CHECK(check_ptr(w->fc1_b, "fc1_b", true));
   CHECK(check_ptr(w->fc2_w, "fc2_w"));
   CHECK(check_ptr(w->fc2_b, "fc2_b", true));
-  if (p.L == 0) return VSWIN_OK;
-  if (!workspace || !aligned(workspace, 256))
-    return fail(VSWIN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
-  if (workspace_bytes < p.ws_block)
-    return fail(VSWIN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, p.ws_block);
-  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  return VSWIN_OK;
+}
+
+// Workspace bytes the block's launch sequence touches: the window-MSA regions
+// when the projection is fused into the MLP kernel, else the whole block
+// layout.
+size_t block_ws_needed(const Plan& p) { return block_proj_fused(p) ? p.ws_msa : p.ws_block; }
+
+// One block on a workspace the caller checked (`ws`, at least
+// block_ws_needed(p) bytes): the launch sequence shared by vswin_block_fwd
+// and vswin_block_fwd_noalloc.
+vswin_status block_fwd_run(const Plan& p, const vswin_desc* desc, const void* x, const vswin_block_weights* w,
+                           void* y, char* ws, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
   // LN1 + pad + roll + partition: fused into the qkv projection when it can
   // stage whole rows, else a separate gather kernel
   if (block_proj_fused(p)) {
@@ -439,6 +405,100 @@ vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x, const vswin_
   e2.ld_out = p.C;
   HIPCHECK(gemm(p.dt, ws + p.off_h, w->fc2_w, p.L, p.C, p.hid, e2, st), "fc2 gemm");
   return VSWIN_OK;
+}
+
+// Scratch memory of vswin_block_fwd_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never uses its name
+// as an address (on the host it is a stand-in); the device address comes from
+// hipGetSymbolAddress once per device, with that device current, and is kept
+// per device.
+static __device__ __align__(256) unsigned char scratch[VSWIN_NOALLOC_SCRATCH_BYTES];
+
+vswin_status noalloc_scratch(char** out) {
+  static std::mutex mu;
+  static std::unordered_map<int, char*> ptrs;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "noalloc: hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "noalloc: hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(VSWIN_ERR_HIP, "noalloc: scratch address %p is unusable", ptr);
+    it = ptrs.emplace(dev, static_cast<char*>(ptr)).first;
+  }
+  *out = it->second;
+  return VSWIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vswin_last_error(void) { return g_err; }
+int32_t vswin_abi_version(void) { return VSWIN_ABI_VERSION; }
+
+const char* vswin_status_string(vswin_status s) {
+  switch (s) {
+    case VSWIN_OK: return "ok";
+    case VSWIN_ERR_INVALID_ARG: return "invalid argument";
+    case VSWIN_ERR_UNSUPPORTED: return "unsupported";
+    case VSWIN_ERR_WORKSPACE: return "workspace too small";
+    case VSWIN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+vswin_status vswin_plan_query(const vswin_desc* desc, vswin_plan* plan) {
+  if (!plan) return fail(VSWIN_ERR_INVALID_ARG, "plan is NULL");
+  Plan p{};
+  CHECK(make_plan(desc, p, false));
+  plan->eff_window[0] = p.geo.P; plan->eff_window[1] = p.geo.Mh; plan->eff_window[2] = p.geo.Mw;
+  plan->eff_shift[0] = p.geo.st; plan->eff_shift[1] = p.geo.sh; plan->eff_shift[2] = p.geo.sw;
+  plan->padded[0] = p.geo.Tp; plan->padded[1] = p.geo.Hp; plan->padded[2] = p.geo.Wp;
+  plan->tokens_per_window = p.N;
+  plan->num_windows = p.nW;
+  plan->tokens = p.L;
+  plan->masked = p.use_mask ? 1 : 0;
+  plan->fast_attention = p.fast ? 1 : 0;
+  plan->workspace_bytes = p.ws_block;
+  plan->msa_workspace_bytes = p.ws_msa;
+  plan->attention_workspace_bytes = p.ws_attn;
+  // geometry is filled in; now the constraints of the compute entry points
+  Plan q{};
+  return make_plan(desc, q, true);
+}
+
+vswin_status vswin_block_fwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.L == 0) return VSWIN_OK;   // empty batch: nothing to read or write
+  CHECK(block_fwd_check(x, w, y));
+  if (!workspace || !aligned(workspace, 256))
+    return fail(VSWIN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.ws_block)
+    return fail(VSWIN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, p.ws_block);
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  return block_fwd_run(p, desc, x, w, y, (char*)workspace, stream);
+}
+
+vswin_status vswin_block_fwd_noalloc(const vswin_desc* desc, const void* x, const vswin_block_weights* w, void* y,
+                                     void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.L == 0) return VSWIN_OK;
+  CHECK(block_fwd_check(x, w, y));
+  const size_t need = block_ws_needed(p);
+  if (need > (size_t)VSWIN_NOALLOC_SCRATCH_BYTES)
+    return fail(VSWIN_ERR_WORKSPACE, "this block needs %zu bytes of scratch; the static buffer holds %zu", need,
+                (size_t)VSWIN_NOALLOC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  CHECK(noalloc_scratch(&ws));
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  return block_fwd_run(p, desc, x, w, y, ws, stream);
 }
 
 vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm, const vswin_block_weights* w,
