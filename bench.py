@@ -7,11 +7,14 @@ clip with 2x4x4 patches, 3 heads of 32, window (8,7,7), shift (4,3,3), MLP
 ratio 4, seeded synthetic inputs and weights (no dataset).  Inputs, weights,
 outputs and workspace are resident in HBM before the timed region.
 
-Prints one JSON line: tokens/s through a block (tokens x blocks per second),
-TFLOP/s and the fraction of the bf16 MFMA peak, the roofline of the dominant
-kernel (the fused window attention, timed alone with HIP events on the
-stream it is launched on) and the fp64 CPU oracle's rate on the same
-workload.
+The K timed steps are captured into one HIP graph, replayed once between
+synchronisations (every kernel of every pair runs; the graph only removes
+the Python binding's per-call host work, reported separately as the eager
+rate).  Prints one JSON line: tokens/s through a block (tokens x blocks per
+second), TFLOP/s and the fraction of the bf16 MFMA peak, the roofline of the
+dominant kernel (the window attention, launched alone and timed with HIP
+events on its stream), the one-kernel LN1 + gather + qkv + attention
+variant, and the fp64 CPU oracle's rate on the same workload.
 """
 import argparse
 import json
@@ -25,24 +28,35 @@ sys.path.insert(0, ROOT)
 METRIC = "window-attention block tokens/s + TFLOP/s (% of MFMA peak) at Swin-T stage 1"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-ATTN_SOURCE = os.path.join(ROOT, "shifted_window_attention_amd", "csrc", "k_attn_mfma.hip")
+CSRC = os.path.join(ROOT, "shifted_window_attention_amd", "csrc")
+# the sources whose sha256 a counter summary records (the kernel's own file
+# and the attention core it includes)
+ATTN_SOURCES = [os.path.join(CSRC, "k_attn_mfma.hip"), os.path.join(CSRC, "attn_core.h")]
+FUSED_SOURCES = [os.path.join(CSRC, "k_attn_fused.hip"), os.path.join(CSRC, "attn_core.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_mfma_swin_t_stage1_traffic.md")
+FUSED_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "wattn_fused_swin_t_stage1_traffic.md")
 
 
-def counter_traffic(path: str = TRAFFIC_SUMMARY):
-    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE
-    summary, or None when the summary is missing or was taken on another
-    version of the kernel source (its sha256 is recorded in the summary)."""
+def sources_sha256(paths) -> str:
     import hashlib
-    if not os.path.exists(path):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def counter_traffic(path: str, sources) -> int:
+    """HBM bytes per launch from a committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when the summary is missing or was taken on another version of
+    the kernel's sources (their sha256 is recorded in the summary)."""
+    if not path or not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
         if ":" in line and line.lstrip().startswith("- "):
             k, v = line.lstrip()[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    if fields.get("kernel source sha256") != src or "hbm bytes per launch" not in fields:
+    if fields.get("kernel source sha256") != sources_sha256(sources) or "hbm bytes per launch" not in fields:
         return None
     return int(fields["hbm bytes per launch"])
 
@@ -79,21 +93,175 @@ def cpu_baseline(x, params, shape, min_seconds=12.0, max_reps=20):
         el = time.perf_counter() - t0
         if el >= min_seconds or reps >= max_reps:
             break
+    info = host_info()
     return {"value": 2 * shape.tokens * reps / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{reps} full block pair(s) of the same workload in fp64 numpy "
-                      f"({el:.1f} s, BLAS threads={cores})"}
+                      f"({el:.1f} s, BLAS threads={cores})",
+            "cpu_model": info["cpu_model"], "nproc": info["nproc"], "usable_cpus": info["usable_cpus"]}
 
 
-def memory_kernels(vs, torch, stream, launches: int = 20) -> dict:
+def host_info() -> dict:
+    """The host the CPU baseline runs on: CPU model, logical CPUs, the CPUs
+    this process may use, and the BLAS pool size."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        blas = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable, "blas_threads": blas}
+
+
+def oracle_per_config(max_seconds: float = 8.0) -> dict:
+    """The fp64 oracle, untouched, on a bounded sample of each other workload:
+    whole windows of one shifted block (every real token of the sampled
+    windows through attention and MLP, oracle.block_sampled), the fp32 smoke
+    pair whole, and the backbone on one clip; real tokens per second through
+    a block (backbone: clips per second)."""
+    import numpy as np
+    import oracle
+    from oracle import vswin as ov
+    import synth
+    out = {}
+    x1, p1 = synth.gen_workload(1)
+    s1 = synth.WORKLOADS[1].shape
+    t0 = time.perf_counter()
+    _, y = oracle.block(x1.astype(np.float64), p1[0], s1.heads, s1.window, (0, 0, 0))
+    oracle.block(y, p1[1], s1.heads, s1.window, s1.shift)
+    el = time.perf_counter() - t0
+    out["workload1"] = {"value": round(2 * s1.tokens / el, 1), "unit": "tokens/s", "sample": "the whole fp32 pair"}
+    for wid, nwin in ((3, 4), (4, 6)):
+        x, params = synth.gen_workload(wid)
+        s = synth.WORKLOADS[wid].shape
+        g = ov.Geometry(s.B, (s.T, s.H, s.W), s.window, s.shift)
+        imap = g.index_map()
+        toks, done, t0 = [], 0, time.perf_counter()
+        for w in np.linspace(0, g.nW - 1, nwin).astype(int):
+            tk = imap[w][imap[w] >= 0].tolist()
+            oracle.vswin.block_sampled(x.astype(np.float64), params[1], s.heads, s.window, s.shift, tk)
+            done += len(tk)
+            if time.perf_counter() - t0 > max_seconds:
+                break
+        el = time.perf_counter() - t0
+        out[f"workload{wid}"] = {"value": round(done / el, 1), "unit": "tokens/s",
+                                 "sample": f"{done} real tokens (whole windows) of one shifted block"}
+    cfg = dict(synth.WORKLOADS[5].backbone)
+    video = synth.gen_video(1, cfg["in_chans"], cfg["frames"], cfg["height"], cfg["width"], 5, "bf16")
+    params = synth.gen_backbone_params(cfg, 5, "bf16")
+    t0 = time.perf_counter()
+    oracle.vswin.backbone(video.astype(np.float64), params, cfg)
+    el = time.perf_counter() - t0
+    out["workload5"] = {"value": round(1 / el, 4), "unit": "clips/s", "sample": "the whole backbone on one clip"}
+    return out
+
+
+def other_workloads(vs, torch, np, stream, reps: int = 5) -> dict:
+    """GPU throughput of the other workloads (eager library calls, HIP events
+    on the calls' stream, inputs and weights resident): Swin-T stage-3 six
+    blocks at B=4 (C=384), the Swin-B stage-1 padded pair at B=8 (C=128), the
+    Swin-T backbone on two clips, and the fp32 smoke pair.  TFLOP/s from the
+    closed form (2 per multiply-accumulate; padded windows for qkv, attention
+    and proj, real tokens for the MLP; backbone: embed and merges added)."""
+    import synth
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).cuda()
+    out = {}
+
+    def timeit(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for wid, n in ((1, 20), (3, reps), (4, reps)):
+        wl = synth.WORKLOADS[wid]
+        s = wl.shape
+        td = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
+        x_np, params = synth.gen_workload(wid)
+        x = dev(x_np, td)
+        w = [{k: dev(v, td) for k, v in p.items()} for p in params]
+        hid = s.mlp_ratio * s.C
+        shifts = [(0, 0, 0) if k % 2 == 0 else s.shift for k in range(len(params))]
+        plans = [vs.vswin_plan_query(vs.make_desc(s.B, s.T, s.H, s.W, s.C, s.heads, s.window, sh, mlp_hidden=hid,
+                                                  dtype=td)) for sh in shifts]
+        ws = torch.empty(max(p["workspace_bytes"] for p in plans), dtype=torch.uint8, device="cuda")
+        ys = [torch.empty_like(x), torch.empty_like(x)]
+
+        def stack():
+            cur = x
+            for k, p in enumerate(w):
+                vs.vswin_block_fwd(cur, p, s.heads, s.window, shifts[k], out=ys[k % 2], workspace=ws, stream=stream)
+                cur = ys[k % 2]
+
+        ms = timeit(stack, n)
+        flops = sum(block_flops(p, s.C, hid)["total"] for p in plans)
+        out[f"workload{wid}"] = {"workload": wl.name, "dtype": wl.dtype, "blocks": len(params),
+                                 "ms_per_stack": round(ms, 4),
+                                 "tokens_per_s": round(s.tokens * len(params) / (ms * 1e-3), 1),
+                                 "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "gflop": round(flops / 1e9, 3)}
+    cfg = synth.WORKLOADS[5].backbone
+    video = dev(synth.gen_video(cfg["B"], cfg["in_chans"], cfg["frames"], cfg["height"], cfg["width"], 5, "bf16"),
+                torch.bfloat16)
+    bp = synth.gen_backbone_params(cfg, 5, "bf16")
+    dp = {"embed_w": dev(bp["embed_w"], torch.bfloat16), "embed_b": dev(bp["embed_b"], torch.bfloat16),
+          "stages": [[{k: dev(v, torch.bfloat16) for k, v in p.items()} for p in st] for st in bp["stages"]],
+          "merges": [{k: dev(v, torch.bfloat16) for k, v in m.items()} for m in bp["merges"]],
+          "norm_g": dev(bp["norm_g"], torch.bfloat16), "norm_b": dev(bp["norm_b"], torch.bfloat16)}
+    ms = timeit(lambda: vs.vswin_backbone_fwd(video, dp, cfg, stream=stream), reps)
+    # closed form of the backbone: embed, blocks, merges
+    B, C = cfg["B"], cfg["embed_dim"]
+    T, H, W = cfg["frames"] // 2, cfg["height"] // 4, cfg["width"] // 4
+    flops = 2 * B * T * H * W * (cfg["in_chans"] * 2 * 4 * 4) * C
+    for i, depth in enumerate(cfg["depths"]):
+        for j in range(depth):
+            sh = (0, 0, 0) if j % 2 == 0 else tuple(v // 2 for v in cfg["window"])
+            p = vs.vswin_plan_query(vs.make_desc(B, T, H, W, C, cfg["heads"][i], cfg["window"], sh))
+            flops += block_flops(p, C, 4 * C)["total"]
+        if i < len(cfg["depths"]) - 1:
+            H, W = (H + 1) // 2, (W + 1) // 2
+            flops += 2 * B * T * H * W * 4 * C * 2 * C
+            C *= 2
+    out["workload5"] = {"workload": synth.WORKLOADS[5].name, "dtype": "bf16", "ms_per_forward": round(ms, 4),
+                        "clips_per_s": round(B / (ms * 1e-3), 2), "stage1_tokens_per_s":
+                        round(B * (cfg["frames"] // 2) * (cfg["height"] // 4) * (cfg["width"] // 4) / (ms * 1e-3), 1),
+                        "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "gflop": round(flops / 1e9, 3)}
+    return out
+
+
+def memory_kernels(vs, torch, stream, launches: int = 20, cold_launches: int = 10) -> dict:
     """HBM rates of the standalone permutation / normalisation kernels (the
     block path fuses them into its GEMMs): the pad + roll + partition gather,
     the reverse + un-roll scatter with the residual, and LayerNorm, on the
-    Swin-T stage-1 token grid and on the larger Swin-B stage-1 grid (B=8,
-    16x60x60x128, padded to 16x63x63), whose tensors do not stay in cache.
-    Bytes are algorithmic: each tensor once at its stored width."""
+    Swin-T stage-1 token grid and on the Swin-B stage-1 grid (B=8,
+    16x60x60x128, padded to 16x63x63).  Bytes are algorithmic: each tensor once
+    at its stored width.  Two timings per kernel:
+      warm  `launches` launches back to back on the same buffers (a kernel's
+            working set of up to ~250 MB can stay in the 256 MB last-level
+            cache between launches);
+      cold  each launch alone between HIP events after a 512 MiB fill of a
+            scrub buffer (larger than that cache), median of `cold_launches`:
+            the inputs come from HBM; this is the figure the HBM fractions
+            rest on."""
+    import statistics
     out = {}
     shapes = {"swin_t_s1": ((1, 16, 56, 56, 96), (4, 3, 3)), "swin_b_s1_b8": ((8, 16, 60, 60, 128), (4, 3, 3))}
     g = torch.Generator(device="cuda").manual_seed(4)
+    scrub = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
     for name, (shape, shift) in shapes.items():
         B, T, H, W, C = shape
         x = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
@@ -118,10 +286,25 @@ def memory_kernels(vs, torch, stream, launches: int = 20) -> dict:
                 fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / launches
-            gbs = nbytes / (us * 1e-6) / 1e9
-            res[k] = {"us": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 3)}
+            warm_us = e0.elapsed_time(e1) * 1e3 / launches
+            cold = []
+            for _ in range(cold_launches):
+                scrub.fill_(1.0)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1) * 1e3)
+            cold_us = statistics.median(cold)
+            rate = lambda us: nbytes / (us * 1e-6) / 1e9
+            res[k] = {"bytes": nbytes,
+                      "cold_us": round(cold_us, 2), "cold_GB/s": round(rate(cold_us), 1),
+                      "cold_frac": round(rate(cold_us) / PEAK_HBM_GBS, 3),
+                      "warm_us": round(warm_us, 2), "warm_GB/s": round(rate(warm_us), 1),
+                      "warm_frac": round(rate(warm_us) / PEAK_HBM_GBS, 3)}
         out[name] = res
+    del scrub
     return out
 
 
@@ -339,7 +522,9 @@ def step_percentiles(step, torch, stream, n: int, scrub=None) -> dict:
 
 def counter_pass():
     """A plain copy of known size (the scale of FETCH_SIZE / WRITE_SIZE), then
-    the attention kernel alone on seeded q, k, V^T of the Swin-T stage-1 shape."""
+    the attention kernel alone on seeded q, k, V^T of the Swin-T stage-1 shape,
+    the one-kernel qkv + attention and one block pair on the stage-1 tokens,
+    and the standalone memory-bound kernels."""
     import torch
     import synth
     import shifted_window_attention_amd as vs
@@ -360,6 +545,20 @@ def counter_pass():
         o = torch.empty((nW, N, s.C), dtype=torch.bfloat16, device="cuda")
         for _ in range(3):
             vs.vswin_attention_fwd(d, q, k, v, tab, out=o)
+    torch.cuda.synchronize()
+    # LN1 + gather + qkv + attention in one kernel on the stage-1 tokens, 3
+    # launches per shift
+    x_np, params = synth.gen_workload(2)
+    x = torch.from_numpy(x_np).to(torch.bfloat16).cuda()
+    ws = [{k_: torch.from_numpy(v_).to(torch.bfloat16).cuda() for k_, v_ in p_.items()} for p_ in params]
+    os.environ["VSWIN_FUSED"] = "1"
+    for i, sh in enumerate([(0, 0, 0), s.shift]):
+        for _ in range(3):
+            vs.vswin_qkv_attention_fwd(x, ws[i], s.heads, s.window, sh)
+    os.environ.pop("VSWIN_FUSED")
+    # one block pair (qkv, attention, projection + MLP kernels, twice)
+    y1 = vs.vswin_block_fwd(x, ws[0], s.heads, s.window, (0, 0, 0))
+    vs.vswin_block_fwd(y1, ws[1], s.heads, s.window, s.shift)
     torch.cuda.synchronize()
     # the standalone gather, scatter + residual and LayerNorm, once each, in this
     # order, on the Swin-B stage-1 grid (B=8, 16x60x60x128 padded to 16x63x63)
@@ -384,10 +583,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="no timing: one 256 MiB device copy (counter calibration), 3 attention launches per "
-                         "shift of the stage-1 shape, then one gather, scatter and LayerNorm of the Swin-B stage-1 "
-                         "B=8 grid; for rocprofv3 --pmc runs")
-    ap.add_argument("--traffic", default=TRAFFIC_SUMMARY,
-                    help="counter summary with the attention kernel's HBM bytes per launch")
+                         "shift of the stage-1 shape, 3 one-kernel qkv + attention launches per shift and one "
+                         "block pair on the stage-1 tokens, then one gather, scatter and LayerNorm of the Swin-B "
+                         "stage-1 B=8 grid; for rocprofv3 --pmc runs")
+    ap.add_argument("--no-traffic", action="store_true",
+                    help="leave roofline.traffic null (ignore the committed counter summaries)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -438,21 +638,94 @@ def main():
 
     for _ in range(args.warmup):
         step(stream)
-    # eager calls through the binding (host submission stays ahead of the GPU)
-    ms, wall = timed(lambda: step(stream), stream)
-    # per-step distribution, warm, then with a 512 MiB scrub between steps (larger
-    # than the 256 MB last-level cache) so that each step starts from HBM
-    warm = step_percentiles(step, torch, stream, 50)
+    torch.cuda.synchronize()
+    ref_y = y2.clone()
+    # The K timed steps are captured into one HIP graph and replayed once: the
+    # same kernels on the same buffers, K times over, without the Python
+    # binding's per-call argument checks on the host (which take about as long
+    # as the GPU work).  The eager rate through the binding is reported too.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step(torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(y2, ref_y):
+        raise RuntimeError("the graph replay differs from the eager pair")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graph
+    eager_ms, eager_wall = timed(lambda: step(stream), stream)
+    # per-step distribution (one pair per graph replay, events around each),
+    # warm, then with a 512 MiB scrub between steps (larger than the 256 MB
+    # last-level cache) so that each step starts from HBM
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        step(torch.cuda.current_stream())
+    replay = lambda st: g1.replay()
+    warm = step_percentiles(replay, torch, stream, 50)
     scrub_buf = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
-    cold = step_percentiles(step, torch, stream, 20, scrub=lambda: scrub_buf.fill_(1.0))
-    del scrub_buf
+    cold = step_percentiles(replay, torch, stream, 20, scrub=lambda: scrub_buf.fill_(1.0))
+    del scrub_buf, g1
     flops = [block_flops(p, s.C, hid) for p in plans]
     step_flops = sum(f["total"] for f in flops)
     tokens_per_step = s.tokens * len(shifts)
     tflops = step_flops / (ms * 1e-3) / 1e12
 
-    # ---- dominant kernel: the fused window attention, alone, on the same stream
+    def time_launches(fn, n):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(n):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / n
+
+    # the same pair with LN1 + gather + qkv + attention as one kernel
+    # (VSWIN_FUSED=1), and that kernel alone, for comparison
+    os.environ["VSWIN_FUSED"] = "1"
+    g10 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g10):
+        for _ in range(10):
+            step(torch.cuda.current_stream())
+    g10.replay()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    g10.replay()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    one_kernel_pair_ms = f0.elapsed_time(f1) / 10
+    del g10
     Lp = plans[0]["num_windows"] * plans[0]["tokens_per_window"]
+    o_rows = torch.empty((Lp, s.C), dtype=torch.bfloat16, device="cuda")
+    msa_ws = torch.empty(max(p["msa_workspace_bytes"] for p in plans), dtype=torch.uint8, device="cuda")
+    fused_us = [time_launches(lambda: vs.vswin_qkv_attention_fwd(x, w[i], s.heads, s.window, shifts[i],
+                                                                  out=o_rows, workspace=msa_ws, stream=stream),
+                              args.kernel_launches) for i in range(len(shifts))]
+    os.environ.pop("VSWIN_FUSED")
+    fused_flops = flops[0]["qkv"] + flops[0]["attn"]
+    f_us = sum(fused_us) / len(fused_us)
+    one_kernel = {"kernel": "wattn_fused_kernel<96> (LN1 + gather + qkv + window attention, VSWIN_FUSED=1)",
+                  "pair_ms": round(one_kernel_pair_ms, 4), "avg_us": round(f_us, 3),
+                  "tflops": round(fused_flops / (f_us * 1e-6) / 1e12, 2),
+                  "frac": round(fused_flops / (f_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "flops_per_launch": fused_flops,
+                  "traffic": None if args.no_traffic else counter_traffic(FUSED_TRAFFIC_SUMMARY, FUSED_SOURCES)}
+
+    # ---- the attention core alone (the kernel of the separate-launch path) on
+    # prepared q, k, V^T; the first calls prepare the bias tables in attn_ws,
+    # the timed ones reuse them (F_TABLES_READY)
     d = s.C // s.heads
     g = torch.Generator(device="cuda").manual_seed(2)
     qkv = [torch.randn((plans[0]["num_windows"], s.heads, plans[0]["tokens_per_window"], d),
@@ -461,34 +734,25 @@ def main():
                     device="cuda")
     attn_ws = torch.empty(max(256, max(p["attention_workspace_bytes"] for p in plans)), dtype=torch.uint8,
                           device="cuda")
-    # the first calls prepare the bias tables in attn_ws; the timed ones reuse
-    # them (F_TABLES_READY), so the events bracket the attention kernel alone
     ready = [vs.make_desc(s.B, s.T, s.H, s.W, s.C, s.heads, s.window, sh, mlp_hidden=hid,
                           dtype=torch.bfloat16, flags=vs.F_TABLES_READY) for sh in shifts]
     kern_us = []
     for i, dsc in enumerate(descs):
-        for _ in range(5):
-            vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, workspace=attn_ws, stream=stream)
-        torch.cuda.synchronize()
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        for _ in range(args.kernel_launches):
-            vs.vswin_attention_fwd(ready[i], *qkv, w[i]["rpb_table"], out=o, workspace=attn_ws, stream=stream)
-        a1.record(stream)
-        torch.cuda.synchronize()
-        kern_us.append(a0.elapsed_time(a1) * 1e3 / args.kernel_launches)
+        vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, workspace=attn_ws, stream=stream)
+        kern_us.append(time_launches(lambda: vs.vswin_attention_fwd(ready[i], *qkv, w[i]["rpb_table"], out=o,
+                                                                    workspace=attn_ws, stream=stream),
+                                     args.kernel_launches))
     attn_flops = flops[0]["attn"]
     attn_us = sum(kern_us) / len(kern_us)
     achieved = attn_flops / (attn_us * 1e-6) / 1e12
-    traffic = counter_traffic(args.traffic) if args.traffic else None
     measured_peak = mfma_measured_peak(vs, torch, stream)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "measured_mfma_peak": round(measured_peak, 1),
-                "frac_of_measured_peak": round(achieved / measured_peak, 4),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if args.no_traffic else counter_traffic(TRAFFIC_SUMMARY, ATTN_SOURCES),
                 "kernel": "attn_mfma_kernel", "avg_us": round(attn_us, 3),
                 "avg_us_regular": round(kern_us[0], 3), "avg_us_shifted": round(kern_us[1], 3),
-                "flops_per_launch": attn_flops,
+                "flops_per_launch": attn_flops, "measured_mfma_peak": round(measured_peak, 1),
+                "frac_of_measured_peak": round(achieved / measured_peak, 4),
                 "mfma_valu_issue": issue_overlap(vs, torch, stream)}
 
     out = {
@@ -503,15 +767,19 @@ def main():
         "tflops": round(tflops, 2), "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "mfma_measured_peak_frac": round(tflops / measured_peak, 4),
         "step_gflop": round(step_flops / 1e9, 3), "wall_ms_per_step": round(wall, 4),
-        "roofline": roofline,
+        "timing": "the K steps captured in one HIP graph, replayed once (eager binding calls: eager_ms_per_step)",
+        "eager_ms_per_step": round(eager_ms, 4), "eager_wall_ms_per_step": round(eager_wall, 4),
+        "roofline": roofline, "one_kernel_qkv_attention": one_kernel,
         "step_ms_warm": warm, "step_ms_cold": cold,
         "memory_kernels": memory_kernels(vs, torch, stream),
         "window_variants": window_variants(vs, torch, np, stream),
         "backward": backward_pair(vs, torch, np, x, w, s, shifts, stream),
         "inference_head": inference_head(vs, torch, stream),
+        "other_workloads": other_workloads(vs, torch, np, stream),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_np, params, s)
+        out["cpu_baseline_per_workload"] = oracle_per_config()
     print(json.dumps(out), flush=True)
 
 

@@ -191,6 +191,26 @@ vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const vo
                                  const void* v, const void* rpb_table, void* o,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* LN1, pad + roll + partition, the qkv projection and the attention core of
+ * one block (§3.2 / eq. 2: the (S)W-MSA branch of eq. 1 up to, not
+ * including, its output projection), from the block input x (B,T,H,W,C):
+ * o receives the heads' concatenated attention outputs in the window-row
+ * layout of vswin_attention_fwd's o, [(w * N + s) * C + h * head_dim + e]
+ * with s in the MFMA slot order (rows of pad slots unspecified).  Reads
+ * w->ln1_g, ln1_b, qkv_w, qkv_b (may be NULL) and rpb_table; the other
+ * fields are ignored.  Two launches (the qkv projection, which normalises
+ * and gathers its rows, then the attention kernel; q, k and V^T pass
+ * through the workspace); with the environment variable VSWIN_FUSED=1, and
+ * where the geometry allows (at most 512 tokens per window, key groups of
+ * uniform region), one kernel in which q, k and v never leave the chip,
+ * with the same bits (vswin_block_fwd and vswin_window_msa_fwd follow the
+ * same switch).  Needs bf16, head_dim 32, C in {96, 128} and
+ * plan.fast_attention == 1, else VSWIN_ERR_UNSUPPORTED.
+ * x and o must not alias; workspace >= plan.msa_workspace_bytes, 256-byte
+ * aligned.                                                                   */
+vswin_status vswin_qkv_attention_fwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w,
+                                     void* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Gradients of one block's weights (training): fp32 device buffers of the
  * weights' shapes (vswin_block_weights), each overwritten (not accumulated).
  * Bias gradients may be NULL (not computed); weight, table and LayerNorm

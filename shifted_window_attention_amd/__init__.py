@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "VswinError", "lib", "Desc", "BlockWeights", "PlanInfo", "make_desc",
     "vswin_plan_query", "vswin_block_fwd", "vswin_block_fwd_noalloc", "vswin_window_msa_fwd", "vswin_attention_fwd",
-    "vswin_index_map",
+    "vswin_qkv_attention_fwd", "vswin_index_map",
     "vswin_partition_fwd", "vswin_reverse_fwd", "vswin_layernorm_fwd",
     "vswin_patch_embed_fwd", "vswin_patch_merge_fwd", "vswin_backbone_fwd", "vswin_mfma_rate_probe",
     "vswin_issue_probe",
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "vswin_block_fwd_noalloc": (i32, [pdesc, vp, pw, vp, vp]),
         "vswin_window_msa_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
         "vswin_attention_fwd": (i32, [pdesc, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "vswin_qkv_attention_fwd": (i32, [pdesc, vp, pw, vp, vp, sz, vp]),
         "vswin_index_map": (i32, [pdesc, vp, vp, vp]),
         "vswin_partition_fwd": (i32, [pdesc, vp, vp, vp]),
         "vswin_reverse_fwd": (i32, [pdesc, vp, vp, vp, vp]),
@@ -325,6 +326,30 @@ def vswin_attention_fwd(desc: Desc, q: torch.Tensor, k: torch.Tensor, v: torch.T
     ws = _workspace(plan["attention_workspace_bytes"], q.device, workspace)
     _check(lib().vswin_attention_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(table), _ptr(o),
                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return o
+
+
+QKV_ATTN_NAMES = ("ln1_g", "ln1_b", "qkv_w", "qkv_b", "rpb_table")
+
+
+def vswin_qkv_attention_fwd(x: torch.Tensor, w: Dict[str, torch.Tensor], heads: int, window: Sequence[int],
+                            shift: Sequence[int], *, eps: float = 1e-5, flags: int = 0,
+                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """LN1 + window partition + qkv + attention of one block on its input x
+    (B, T, H, W, C): the heads' outputs in window rows (num_windows * N, C),
+    slot order as vswin_attention_fwd's o (see include/vswin.h)."""
+    _check_weights(x, w, heads, window, QKV_ATTN_NAMES)
+    d = _desc_for(x, heads, window, shift, eps, flags, 4 * x.shape[-1])
+    plan = vswin_plan_query(d)
+    rows = plan["num_windows"] * plan["tokens_per_window"]
+    o = torch.empty((rows, x.shape[-1]), dtype=x.dtype, device=x.device) if out is None else out
+    if o.numel() != rows * x.shape[-1] or o.dtype != x.dtype or o.device != x.device:
+        raise ValueError(f"out must hold num_windows*N*C = {rows * x.shape[-1]} elements of {x.dtype} on {x.device}")
+    ws = _workspace(plan["msa_workspace_bytes"], x.device, workspace)
+    bw = _weights(w)
+    _check(lib().vswin_qkv_attention_fwd(ctypes.byref(d), _ptr(x), ctypes.byref(bw), _ptr(o), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
     return o
 
 

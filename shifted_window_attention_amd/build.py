@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvswin.so")
 SOURCES = ["vswin_api.hip", "k_layout.hip", "k_gemm.hip", "k_winproj.hip", "k_attention.hip", "k_attn_mfma.hip",
-           "k_mlp.hip", "k_patch.hip", "k_probe.hip", "k_backward.hip", "k_head.hip"]
+           "k_mlp.hip", "k_patch.hip", "k_probe.hip", "k_backward.hip", "k_head.hip", "k_attn_fused.hip"]
 ARCH = os.environ.get("VSWIN_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
@@ -34,7 +34,7 @@ def _hipcc() -> str:
 # (no accumulation-register round trips between score tiles and VALU work)
 # MFMA accumulators in ordinary VGPRs (no AGPR copies) for the MFMA kernels
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"k_attn_mfma.hip": _VGPR_FORM, "k_mlp.hip": _VGPR_FORM, "k_winproj.hip": _VGPR_FORM,
+EXTRA = {"k_attn_mfma.hip": _VGPR_FORM, "k_attn_fused.hip": _VGPR_FORM, "k_mlp.hip": _VGPR_FORM, "k_winproj.hip": _VGPR_FORM,
          "k_probe.hip": _VGPR_FORM}
 
 

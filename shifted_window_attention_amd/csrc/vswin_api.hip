@@ -74,6 +74,16 @@ bool fault_injected() {
   return f && strcmp(f, "launch") == 0;
 }
 
+// VSWIN_FUSED=1 runs LN1 + gather + qkv + attention as one kernel where it
+// applies (q, k and v stay on chip); by default they are two launches (q, k,
+// V^T through the workspace), which measured faster at the Swin-T stage-1
+// shape: the one kernel recomputes the keys of windows that two workgroups
+// share and builds the bias table in every workgroup.  Both give the same bits.
+bool fused_enabled() {
+  const char* f = getenv("VSWIN_FUSED");
+  return f && strcmp(f, "1") == 0;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t elem_size(vswin_dtype d) { return d == VSWIN_BF16 ? 2 : 4; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -227,12 +237,32 @@ bool block_proj_fused(const Plan& p) {
 // after the attention, whose output rows are left in `xw`.
 vswin_status run_msa(const Plan& p, const vswin_desc* d, const vswin_block_weights* w, char* ws,
                      const void* residual, void* out, bool to_zh, hipStream_t st, const GatherA* ga = nullptr,
-                     bool no_proj = false) {
-  void* xw = ws + p.off_xw;
+                     bool no_proj = false, void* attn_out = nullptr) {
+  // the attention output rows (with `no_proj` and `ga`, `attn_out` may take them instead)
+  void* xw = attn_out ? attn_out : ws + p.off_xw;
   void* q = ws + p.off_q;
   void* k = ws + p.off_k;
   void* v = ws + p.off_v;
   const int vt = p.fast ? 1 : 0;
+  if (ga && fused_enabled()) {
+    // LN1 + gather + qkv + attention in one kernel: q, k, v stay on chip
+    FusedArgs fa{};
+    fa.a = attn_args(p, nullptr, nullptr, nullptr, w->rpb_table, xw, d->flags);
+    if (attention_fused_supported(p.dt, fa.a)) {
+      fa.x = ga->x;
+      fa.ln_g = ga->g;
+      fa.ln_b = ga->b;
+      fa.eps = ga->eps;
+      fa.ln = ga->ln;
+      fa.w = w->qkv_w;
+      fa.bias = w->qkv_b;
+      HIPCHECK(attention_fused(fa, st), "fused qkv + attention");
+      if (no_proj) return VSWIN_OK;
+      HIPCHECK(out_proj(xw, w->proj_w, w->proj_b, to_zh ? residual : nullptr, out, p.Lp, p.C, p.geo, st),
+               "output projection");
+      return VSWIN_OK;
+    }
+  }
   if (ga && winproj_supported(p.dt, p.C, p.d, p.N, vt)) {
     // the MFMA attention takes q pre-multiplied by log2(e) / sqrt(d)
     const float qscale = p.fast ? 1.4426950408889634f / sqrtf((float)p.d) : 1.0f;
@@ -349,6 +379,12 @@ vswin_status block_fwd_check(const void* x, const vswin_block_weights* w, void* 
   CHECK(check_ptr(w->fc2_w, "fc2_w"));
   CHECK(check_ptr(w->fc2_b, "fc2_b", true));
   return VSWIN_OK;
+}
+
+// Can LN1 + gather + qkv + attention run without a separate gather kernel
+// (the rows the qkv projection stages are normalised and gathered there)?
+bool qkv_attention_supported(const Plan& p) {
+  return p.fast && gemm_can_gather(p.dt, p.C) && winproj_supported(p.dt, p.C, p.d, p.N, 1);
 }
 
 // Workspace bytes the block's launch sequence touches: the window-MSA regions
@@ -525,6 +561,29 @@ vswin_status vswin_window_msa_fwd(const vswin_desc* desc, const void* x_norm, co
   HIPCHECK(ln_gather(p.dt, x_norm, nullptr, nullptr, ws + p.off_xw, p.Lp, p.C, desc->ln_eps, p.geo, 0, st),
            "partition");
   return run_msa(p, desc, w, ws, nullptr, y, false, st);
+}
+
+vswin_status vswin_qkv_attention_fwd(const vswin_desc* desc, const void* x, const vswin_block_weights* w, void* o,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p{};
+  CHECK(make_plan(desc, p));
+  if (p.L == 0) return VSWIN_OK;
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(o, "o"));
+  if (x == o) return fail(VSWIN_ERR_INVALID_ARG, "x and o must not alias");
+  CHECK(check_msa_weights(w));
+  CHECK(check_ptr(w->ln1_g, "ln1_g"));
+  CHECK(check_ptr(w->ln1_b, "ln1_b"));
+  if (!qkv_attention_supported(p))
+    return fail(VSWIN_ERR_UNSUPPORTED, "qkv + attention needs bf16, head_dim 32, C in {96, 128} and the MFMA "
+                                       "attention");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(VSWIN_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.ws_msa)
+    return fail(VSWIN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, p.ws_msa);
+  if (fault_injected()) return fail(VSWIN_ERR_HIP, "injected launch failure (VSWIN_FAULT=launch)");
+  const GatherA ga{x, w->ln1_g, w->ln1_b, desc->ln_eps, 1, p.geo};
+  return run_msa(p, desc, w, (char*)workspace, x, nullptr, false, (hipStream_t)stream, &ga, true, o);
 }
 
 vswin_status vswin_attention_fwd(const vswin_desc* desc, const void* q, const void* k, const void* v,

@@ -105,6 +105,24 @@ constexpr int kMfmaMaxN = 512;
 constexpr int kMfmaBigN = 1024;
 bool attention_mfma_supported(vswin_dtype dt, const AttnArgs& a);
 
+// LN1 + gather + qkv projection + MFMA attention in one kernel (bf16, C in
+// {96, 128}, head_dim 32, the MFMA kernel's 4-tuple-table forms with group
+// labels and the exclusion mask): o (a.o, window rows in slot order) from the
+// token rows x; a.table is the (rows, heads) bf16 table; a.q, a.k, a.v and
+// a.tab4 are not used.  With ln == 0 the rows are taken as they are.
+struct FusedArgs {
+  AttnArgs a;
+  const void* x;        // token rows (B*T*H*W, C)
+  const void* ln_g;     // LN1 gamma, beta (C)
+  const void* ln_b;
+  float eps;
+  int ln;
+  const void* w;        // (3C, C)
+  const void* bias;     // (3C) or NULL
+};
+bool attention_fused_supported(vswin_dtype dt, const AttnArgs& a);
+hipError_t attention_fused(const FusedArgs& f, hipStream_t st);
+
 // Backward of the MFMA attention (bf16, d = 32, group-uniform region labels,
 // exclusion mask).  In: a.q (q * log2(e) / sqrt(d)), a.k, a.v (V^T), a.o,
 // a.table as the forward had them, dout (window rows), lse (the forward's

@@ -155,6 +155,32 @@ def test_block_argument_errors_before_launch():
     assert _call_block(d, X, w, Y, WS, need_msa - 1, "vswin_window_msa_fwd") == -3
 
 
+def test_qkv_attention_argument_errors_before_launch():
+    """vswin_qkv_attention_fwd: argument, support and workspace errors come
+    back before anything is enqueued."""
+    d = vs.make_desc(1, 16, 14, 14, 96, 3, (8, 7, 7), (4, 3, 3), dtype=1)
+    need = vs.vswin_plan_query(d)["msa_workspace_bytes"]
+    w = _fake_weights()
+    X, O, WS = 0x100000, 0x200000, 0x300000
+    fn = "vswin_qkv_attention_fwd"
+    L = vs.lib()
+    assert _call_block(d, None, w, O, WS, need, fn) == -1             # null x
+    assert _call_block(d, X, w, X, WS, need, fn) == -1                # aliasing
+    w2 = _fake_weights(); w2.ln1_g = None
+    assert _call_block(d, X, w2, O, WS, need, fn) == -1
+    assert b"ln1_g" in L.vswin_last_error()
+    assert _call_block(d, X, w, O, WS, need - 1, fn) == -3            # workspace too small
+    assert _call_block(d, X, w, O, WS + 16, need, fn) == -3           # workspace misaligned
+    # fp32, and a width whose qkv projection cannot gather its own rows
+    for dd in (vs.make_desc(1, 4, 14, 14, 32, 2, (2, 7, 7), (1, 3, 3), dtype=0),
+               vs.make_desc(1, 16, 14, 14, 192, 6, (8, 7, 7), (4, 3, 3), dtype=1)):
+        n = vs.vswin_plan_query(dd)["msa_workspace_bytes"]
+        assert _call_block(dd, X, w, O, WS, n, fn) == -2
+    # nothing to do for an empty batch
+    d0 = vs.make_desc(0, 16, 14, 14, 96, 3, (8, 7, 7), (4, 3, 3), dtype=1)
+    assert _call_block(d0, X, w, O, None, 0, fn) == 0
+
+
 def test_fault_hook_reports_hip_error(monkeypatch):
     monkeypatch.setenv("VSWIN_FAULT", "launch")
     d = vs.make_desc(1, 16, 14, 14, 96, 3, (8, 7, 7), (4, 3, 3), dtype=1)

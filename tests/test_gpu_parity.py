@@ -249,6 +249,45 @@ def test_block_c96_fused_projection(case):
     check(host64(y), ref, "bf16", f"C=96 block {name}")
 
 
+@pytest.mark.parametrize("case", C96_CASES[:3] + [("C=128 padded B=2", 2, (16, 12, 13), (4, 3, 3), 0)],
+                         ids=[c[0] for c in C96_CASES[:3]] + ["C=128 padded B=2"])
+def test_block_one_kernel_qkv_attention_path(case, monkeypatch):
+    """VSWIN_FUSED=1 routes the block through the one-kernel LN1 + gather +
+    qkv + attention (q, k, v on chip) instead of the separate launches; it
+    must meet the same bar."""
+    name, B, size, shift, flags = case
+    C = 128 if "128" in name else 96
+    heads, window = C // 32, (8, 7, 7)
+    say(f"one-kernel qkv + attention path: {name}")
+    monkeypatch.setenv("VSWIN_FUSED", "1")
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=23)
+    x = _rng_tokens((B, *size, C), "bf16", 5)
+    y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift, flags=flags)
+    _, ref = oracle.block(x, p, heads, window, shift, pad_visible=bool(flags & vs.F_PAD_VISIBLE))
+    check(host64(y), ref, "bf16", f"one-kernel qkv + attention {name}")
+
+
+@pytest.mark.parametrize("C,B,size", [(96, 1, (16, 56, 56)), (96, 2, (16, 56, 56)), (128, 2, (16, 12, 13)),
+                                      (128, 1, (16, 60, 60))])
+def test_block_fused_qkv_attention_equals_separate(C, B, size, monkeypatch):
+    """The one-kernel LN1 + gather + qkv + attention rounds q, k and v to bf16
+    exactly where the separate launches store them, and runs the same
+    attention arithmetic: the block outputs agree bit for bit, on grids whose
+    workgroup runs cross windows and heads."""
+    heads, window = C // 32, (8, 7, 7)
+    p = dev_params(_msa_params(C, heads, window, "bf16", "stress", seed=41), "bf16")
+    x = dev(_rng_tokens((B, *size, C), "bf16", 9), "bf16")
+    for shift in ((0, 0, 0), (4, 3, 3)):
+        say(f"fused vs separate qkv + attention: C={C} B={B} {size} shift {shift}")
+        monkeypatch.setenv("VSWIN_FUSED", "1")
+        yf = vs.vswin_block_fwd(x, p, heads, window, shift)
+        monkeypatch.setenv("VSWIN_FUSED", "0")
+        ys = vs.vswin_block_fwd(x, p, heads, window, shift)
+        torch.cuda.synchronize()
+        assert torch.isfinite(yf.float()).all()
+        assert torch.equal(yf, ys), f"max diff {(yf.float() - ys.float()).abs().max().item()}"
+
+
 @pytest.mark.parametrize("window,shift", [((16, 7, 7), (0, 0, 0)), ((16, 7, 7), (8, 3, 3)), ((4, 7, 7), (2, 3, 3))])
 def test_block_window_variants_stage1_grid(window, shift):
     """The other temporal windows on the Swin-T stage-1 token grid: 16 (784
@@ -539,6 +578,44 @@ def test_attention_core_alone(shift, size):
     # pad query rows are not outputs of the block; compare the real ones
     real = g.index_map() >= 0
     check(o_nat[real], ref[real], "bf16", "attention core")
+
+
+@pytest.mark.parametrize("case", [(96, 1, (16, 56, 56), (4, 3, 3)), (96, 1, (16, 12, 13), (0, 0, 0)),
+                                  (128, 2, (16, 12, 13), (4, 3, 3))],
+                         ids=["stage-1 shifted", "C=96 padded regular", "C=128 padded shifted B=2"])
+def test_qkv_attention_entry(case, monkeypatch):
+    """vswin_qkv_attention_fwd against the oracle's branch with an identity
+    output projection (so the branch output is the heads' concatenated
+    attention output), token by token through the slot map; the one-kernel
+    path and the separate launches agree bit for bit."""
+    C, B, size, shift = case
+    heads, window = C // 32, (8, 7, 7)
+    say(f"qkv + attention entry C={C} B={B} {size} shift {shift}")
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=43)
+    p["ln1_g"] = synth.round_bf16((1 + 0.2 * np.random.default_rng(1).standard_normal(C)).astype(np.float32))
+    p["ln1_b"] = synth.round_bf16((0.2 * np.random.default_rng(2).standard_normal(C)).astype(np.float32))
+    x = _rng_tokens((B, *size, C), "bf16", 13)
+    dp, xt = dev_params(p, "bf16"), dev(x, "bf16")
+    monkeypatch.setenv("VSWIN_FUSED", "1")
+    o = vs.vswin_qkv_attention_fwd(xt, dp, heads, window, shift)
+    monkeypatch.setenv("VSWIN_FUSED", "0")
+    o2 = vs.vswin_qkv_attention_fwd(xt, dp, heads, window, shift)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    desc = vs.make_desc(B, *size, C, heads, window, shift, dtype=torch.bfloat16)
+    plan = vs.vswin_plan_query(desc)
+    nW, N = plan["num_windows"], plan["tokens_per_window"]
+    perm = _slot_to_natural(N, *plan["eff_window"], plan["fast_attention"])
+    o_nat = np.empty((nW, N, C))
+    o_nat[:, perm] = host64(o).reshape(nW, N, C)
+    tok = vs.vswin_index_map(desc)[0].cpu().numpy().astype(np.int64).reshape(nW, N)
+    real = tok >= 0
+    q = dict(p)
+    q["proj_w"] = np.eye(C, dtype=np.float32)
+    q["proj_b"] = np.zeros(C, dtype=np.float32)
+    xn = ov.layer_norm(x.astype(np.float64), p["ln1_g"].astype(np.float64), p["ln1_b"].astype(np.float64))
+    ref = ov.window_msa(xn, q, heads, window, shift).reshape(-1, C)
+    check(o_nat[real], ref[tok[real]], "bf16", f"qkv + attention C={C} {size} {shift}")
 
 
 def test_attention_prepared_tables_reuse():
