@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvswin.so")
 SOURCES = ["vswin_api.hip", "k_layout.hip", "k_gemm.hip", "k_winproj.hip", "k_attention.hip", "k_attn_mfma.hip",
-           "k_mlp.hip", "k_patch.hip", "k_probe.hip", "k_backward.hip", "k_head.hip", "k_attn_fused.hip"]
+           "k_mlp.hip", "k_patch.hip", "k_probe.hip", "k_backward.hip", "k_head.hip", "k_attn_fused.hip",
+           "k_attn_f32.hip"]
 ARCH = os.environ.get("VSWIN_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

@@ -4,8 +4,8 @@
 //   O = P v, heads concatenated as h*d + e.
 //
 // SIMT fp32 arithmetic for any dtype / head_dim <= 64 / window of up to 2048
-// tokens, two passes (row max, then exp-sum and P v); it serves the fp32
-// workload and the shapes the MFMA kernel (k_attn_mfma.hip) does not.
+// tokens, two passes (row max, then exp-sum and P v); it serves the shapes
+// neither MFMA kernel does (bf16: k_attn_mfma.hip; fp32: k_attn_f32.hip).
 #include "vswin_kernels.h"
 
 #include <math.h>
@@ -87,6 +87,7 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(const AttnArgs a) {
 hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st) {
   const int64_t items = a.nW * a.heads;
   if (items <= 0) return hipSuccess;
+  if (attention_f32_mfma_supported(dt, a)) return attention_f32_mfma(a, st);
   if (a.N > kGenMaxN || a.d > 64) return hipErrorInvalidValue;
   const dim3 grid((unsigned)items), block(256);
   if (dt == VSWIN_BF16) {

@@ -8,8 +8,8 @@
 // and the epilogue writes 8- or 16-byte vectors.  Block tile 128 tokens x BN
 // features, 4 waves as 2 x 2, K staged 32 at a time through double-buffered
 // LDS with an 80-byte row pitch (conflict-free 16-byte fragment reads).
-// fp32 path: a plain LDS-tiled FMA kernel (it serves the small fp32
-// workload; throughput is not its purpose).
+// fp32 path: v_mfma_f32_16x16x4_f32 with the same C^T tiling (a plain
+// LDS-tiled FMA kernel for feature counts that are not a multiple of 4).
 #include "vswin_kernels.h"
 
 #include <type_traits>
@@ -386,7 +386,74 @@ __global__ void __launch_bounds__(256) gemm_bf16_fullk_kernel(const bf16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// fp32 FMA GEMM (64 x 64 tile, 4 x 4 outputs per thread)
+// fp32 MFMA GEMM: v_mfma_f32_16x16x4_f32 (fp32 operands, fp32 accumulate).
+// Block tile 64 tokens x 64 features, 4 waves as 2 x 2 of 32 x 32; K staged
+// 16 at a time through LDS (row pitch 17 floats: conflict-free column
+// reads).  As in the bf16 kernel the product is C^T (operand A = weight rows,
+// operand B = token rows), so a lane ends with 4 consecutive features of one
+// token for the epilogue.
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ void __launch_bounds__(256) gemm_f32_mfma_kernel(const float* __restrict__ A, const float* __restrict__ W,
+                                                            int64_t M, int N, int K, E epi) {
+  __shared__ float As[64 * 17];
+  __shared__ float Ws[64 * 17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g4 = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nb = (N + 63) / 64;
+  const int64_t bm = blockIdx.x / nb;
+  const int bn = (int)(blockIdx.x - bm * nb);
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 4, kk = idx & 15;
+      const int64_t m = bm * 64 + r;
+      const int n = bn * 64 + r;
+      As[r * 17 + kk] = (m < M && k0 + kk < K) ? A[m * K + k0 + kk] : 0.f;
+      Ws[r * 17 + kk] = (n < N && k0 + kk < K) ? W[(int64_t)n * K + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      float af[2], wf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = As[(wm * 32 + i * 16 + fr) * 17 + 4 * k4 + g4];
+        wf[i] = Ws[(wn * 32 + i * 16 + fr) * 17 + 4 * k4 + g4];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // lane: token wm*32 + i*16 + fr, features wn*32 + j*16 + 4 g4 .. + 3
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t m = bm * 64 + wm * 32 + i * 16 + fr;
+    if (m >= M) continue;
+    const int64_t rc = epi.row_ctx(m);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = bn * 64 + wn * 32 + j * 16 + 4 * g4;
+      if (n >= N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      epi.store(m, rc, n, v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 FMA GEMM (64 x 64 tile, 4 x 4 outputs per thread): feature counts that
+// are not a multiple of 4
 // ---------------------------------------------------------------------------
 template <class E>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
@@ -471,8 +538,12 @@ static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int6
     if (pro.mode != 0) return hipErrorInvalidValue;
     EpiDev<float, KIND> epi{e};
     const int64_t blocks = ((M + 63) / 64) * ((N + 63) / 64);
-    gemm_f32_kernel<EpiDev<float, KIND>><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
-        (const float*)A, (const float*)W, M, N, K, epi);
+    if (N % 4 == 0)
+      gemm_f32_mfma_kernel<EpiDev<float, KIND>><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+          (const float*)A, (const float*)W, M, N, K, epi);
+    else
+      gemm_f32_kernel<EpiDev<float, KIND>><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+          (const float*)A, (const float*)W, M, N, K, epi);
   }
   return hipGetLastError();
 }

@@ -95,7 +95,12 @@ struct AttnArgs {
 // (heads * TS4 fp32 4-tuples) and their extents
 size_t attention_workspace_bytes(const RelTab& rel, int heads, int N);
 Tab4Geo tab4_geo(const RelTab& rel, int heads, int N);
+// the attention for shapes the bf16 MFMA kernel does not serve: fp32 on the
+// matrix cores where attention_f32_mfma_supported, else the SIMT kernel
 hipError_t attention_generic(vswin_dtype dt, const AttnArgs& a, hipStream_t st);
+// fp32, head_dim 16, 32 or 64, K, V and the bias column within 160 KB of LDS
+bool attention_f32_mfma_supported(vswin_dtype dt, const AttnArgs& a);
+hipError_t attention_f32_mfma(const AttnArgs& a, hipStream_t st);
 hipError_t attention_mfma(const AttnArgs& a, hipStream_t st);
 // shapes the MFMA kernel serves (bf16, d = 32, temporal window % 4 == 0 with
 // group-uniform temporal labels, no additive -100 mask): N <= kMfmaMaxN with

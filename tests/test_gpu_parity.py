@@ -96,6 +96,11 @@ MSA_CASES = [
     # name, B, size, C, heads, window, shift, dtype, init, flags
     ("fp32 smoke regular", 1, (4, 14, 14), 32, 2, (2, 7, 7), (0, 0, 0), "fp32", "spec", 0),
     ("fp32 smoke shifted", 1, (4, 14, 14), 32, 2, (2, 7, 7), (1, 3, 3), "fp32", "stress", 0),
+    # fp32 on the matrix cores: head_dim 32 and 64, padded grids, the -100 mask
+    ("fp32 window 8 d=32 shifted", 1, (16, 14, 14), 64, 2, (8, 7, 7), (4, 3, 3), "fp32", "stress", 0),
+    ("fp32 d=64 padded shifted", 2, (4, 12, 13), 128, 2, (2, 7, 7), (1, 3, 3), "fp32", "stress", 0),
+    ("fp32 d=32 mask -100", 1, (4, 14, 14), 64, 2, (2, 7, 7), (1, 3, 3), "fp32", "stress", vs.F_MASK_M100),
+    ("fp32 d=16 pads visible", 1, (5, 12, 13), 32, 2, (2, 7, 7), (1, 3, 3), "fp32", "stress", vs.F_PAD_VISIBLE),
     ("bf16 regular", 1, (16, 14, 14), 96, 3, (8, 7, 7), (0, 0, 0), "bf16", "stress", 0),
     ("bf16 shifted", 1, (16, 14, 14), 96, 3, (8, 7, 7), (4, 3, 3), "bf16", "stress", 0),
     ("bf16 shifted spec", 2, (16, 21, 14), 64, 2, (8, 7, 7), (4, 3, 3), "bf16", "spec", 0),
