@@ -342,7 +342,7 @@ __device__ __forceinline__ int pair_row_inv(int r) {
 }  // namespace
 
 template <bool PROJ>
-__global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) {
+__global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) {
   constexpr int C = kMlpC, HID = kMlpHid;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* W1s = lds;                 // HID rows x 192 B
@@ -359,30 +359,26 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, g = lane >> 4;
-  const int64_t ntiles = (L + 15) / 16;
+  // a wave owns a pair of 16-token tiles (2 t2, 2 t2 + 1): the weight
+  // fragments of every chunk serve both, and the two tiles' chains are
+  // independent work for the same wave
+  const int64_t npairs = ((L + 15) / 16 + 1) / 2;
   const int64_t nw = (int64_t)gridDim.x * kMlpWaves;
-  int64_t t = (int64_t)blockIdx.x * kMlpWaves + wave;
+  int64_t t2 = (int64_t)blockIdx.x * kMlpWaves + wave;
 
-  // first tile's inputs, then the weights (one pass, all threads)
-  ZTile cur;
-  ProjTileIn pcur;
-  // PROJ: the projection weight as 18 MFMA A fragments, held in registers for
-  // the whole launch; output tile nt covers pair-order rows 16 nt .. + 15
-  bf16x8_t wpf[PROJ ? 6 : 1][3];
-  if constexpr (PROJ) {
-    proj_tile_load(pcur, a, t);
+  ZTile z[2];
+  ProjTileIn pin[2];
+  auto load_inputs = [&](int64_t tp) {
 #pragma unroll
-    for (int nt = 0; nt < 6; ++nt)
-#pragma unroll
-      for (int kk = 0; kk < 3; ++kk)
-        wpf[nt][kk] =
-            *reinterpret_cast<const bf16x8_t*>(a.wp + pair_row_inv(16 * nt + fr) * C + 32 * kk + 8 * g);
-  } else {
-    ztile_load(cur, a.zh, L, t);
-  }
+    for (int u = 0; u < 2; ++u) {
+      if constexpr (PROJ) proj_tile_load(pin[u], a, 2 * tp + u);
+      else ztile_load(z[u], a.zh, L, 2 * tp + u);
+    }
+  };
+  if (t2 < npairs) load_inputs(t2);
   // W1 and W2 go straight from global memory into their swizzled LDS layouts
   // (global_load_lds: a wave instruction fills 1 KB of consecutive LDS chunks
-  // from per-lane addresses), still in flight while the first tile's
+  // from per-lane addresses), still in flight while the first pair's
   // projection and LN2 run; LDS chunk (r, qp) holds global row
   // pair_row_inv(r), chunk qp ^ swizzle(r)
   {
@@ -417,86 +413,95 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
   __syncthreads();
 
   const int swz1 = (fr >> 2) & 3;   // W1 rows 32c + 16p + fr: ((row >> 2) & 3) = (fr >> 2) & 3
-  // front of a tile: (PROJ) z^ = x + o Wp^T + bp into cur, then LN2 into af
-  bf16x8_t af[3];
+  // front of a pair: (PROJ) z^ = x + o Wp^T + bp into z, then LN2 into af
+  bf16x8_t af[2][3];
   auto front = [&]() {
     if constexpr (PROJ) {
-      // 6 output tiles (pair order) of 16 tokens, the accumulators starting at
-      // the bias; lane ends with columns 32j + 8g .. + 7 of token fr, as a ZTile
-      f32x4_t acc[6];
+      // 6 output tiles (pair order) of 16 tokens for each tile of the pair, the
+      // accumulators starting at the bias; the projection weight's 18 MFMA A
+      // fragments come from global memory (L2) once per pair
+      bf16x8_t wpf[6][3];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        acc[2 * j] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g);
-        acc[2 * j + 1] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g + 4);
-      }
+      for (int nt = 0; nt < 6; ++nt)
 #pragma unroll
-      for (int kk = 0; kk < 3; ++kk)
+        for (int kk = 0; kk < 3; ++kk)
+          wpf[nt][kk] =
+              *reinterpret_cast<const bf16x8_t*>(a.wp + pair_row_inv(16 * nt + fr) * C + 32 * kk + 8 * g);
 #pragma unroll
-        for (int nt = 0; nt < 6; ++nt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wpf[nt][kk], __builtin_bit_cast(bf16x8_t, pcur.o[kk]),
-                                                            acc[nt], 0, 0, 0);
+      for (int u = 0; u < 2; ++u) {
+        f32x4_t acc[6];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        float xv[8];
-        unpack8(pcur.x[j], xv);
+        for (int j = 0; j < 3; ++j) {
+          acc[2 * j] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g);
+          acc[2 * j + 1] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g + 4);
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cur.z[j][i] = xv[i] + acc[2 * j][i];
-          cur.z[j][4 + i] = xv[4 + i] + acc[2 * j + 1][i];
+        for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+          for (int nt = 0; nt < 6; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wpf[nt][kk], __builtin_bit_cast(bf16x8_t, pin[u].o[kk]),
+                                                              acc[nt], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          float xv[8];
+          unpack8(pin[u].x[j], xv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            z[u].z[j][i] = xv[i] + acc[2 * j][i];
+            z[u].z[j][4 + i] = xv[4 + i] + acc[2 * j + 1][i];
+          }
         }
       }
     }
-    // LN2 of the lane's token (4 lanes share a token: xor 16, 32)
-    float s = 0.f;
+    // LN2 of the lane's token in each tile (4 lanes share a token: xor 16, 32)
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int u = 0; u < 2; ++u) {
+      float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += cur.z[j][e];
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    const float mean = s * (1.0f / C);
-    float q2 = 0.f;
+      for (int j = 0; j < 3; ++j)
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+        for (int e = 0; e < 8; ++e) s += z[u].z[j][e];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      const float mean = s * (1.0f / C);
+      float q2 = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float dd = cur.z[j][e] - mean;
-        q2 += dd * dd;
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dd = z[u].z[j][e] - mean;
+          q2 += dd * dd;
+        }
+      q2 += __shfl_xor(q2, 16);
+      q2 += __shfl_xor(q2, 32);
+      const float rstd = 1.0f / sqrtf(q2 * (1.0f / C) + eps);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        float gg[8], bb[8], v[8];
+        unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 32 * j + 8 * g), gg);
+        unpack8(*reinterpret_cast<const u32x4_t*>(vecs + C + 32 * j + 8 * g), bb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (z[u].z[j][e] - mean) * rstd * gg[e] + bb[e];
+        af[u][j] = __builtin_bit_cast(bf16x8_t, pack8(v));
       }
-    q2 += __shfl_xor(q2, 16);
-    q2 += __shfl_xor(q2, 32);
-    const float rstd = 1.0f / sqrtf(q2 * (1.0f / C) + eps);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      float gg[8], bb[8], v[8];
-      unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 32 * j + 8 * g), gg);
-      unpack8(*reinterpret_cast<const u32x4_t*>(vecs + C + 32 * j + 8 * g), bb);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (cur.z[j][e] - mean) * rstd * gg[e] + bb[e];
-      af[j] = __builtin_bit_cast(bf16x8_t, pack8(v));
     }
   };
-  if (t < ntiles) front();
+  if (t2 < npairs) front();
   // every wave's weight blocks are in LDS (every wave reaches this barrier)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (; t < ntiles; t += nw) {
-    ZTile nxt;
-    ProjTileIn pnxt = pcur;
-    if constexpr (PROJ) {
-      if (t + nw < ntiles) proj_tile_load(pnxt, a, t + nw);
-    } else {
-      if (t + nw < ntiles) ztile_load(nxt, a.zh, L, t + nw);
-    }
-    // ---- fc1 -> GELU -> fc2 over 12 chunks of 32 hidden units
-    f32x4_t acc2[6];
+  for (; t2 < npairs; t2 += nw) {
+    // ---- fc1 -> GELU -> fc2 over 12 chunks of 32 hidden units, both tiles
+    f32x4_t acc2[2][6];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) acc2[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 6; ++i) acc2[u][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int ch = 0; ch < HID / 32; ++ch) {
       // every LDS read of the chunk (weights of both layers, fc1 bias as the
-      // fc1 accumulator's start) is in flight before the first MFMA
+      // fc1 accumulators' start) is in flight before the first MFMA
       bf16x8_t w1f[2][3], w2f[6];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -509,47 +514,63 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_wave_kernel(const MlpArgs a) 
         const int r = 16 * nt + fr;
         w2f[nt] = *reinterpret_cast<const bf16x8_t*>(W2s + r * (HID * 2) + (((4 * ch + g) ^ (r & 15)) << 4));
       }
-      f32x4_t a1[2];
-      a1[0] = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g);
-      a1[1] = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g + 4);
+      const f32x4_t bA = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g);
+      const f32x4_t bB = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g + 4);
       __builtin_amdgcn_sched_barrier(0);
+      f32x4_t a1[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        a1[u][0] = bA;
+        a1[u][1] = bB;
+      }
 #pragma unroll
       for (int kk = 0; kk < 3; ++kk)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) a1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1f[p][kk], af[kk], a1[p], 0, 0, 0);
-      float h[8];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // GELU(x) = x Phi(x), Phi from the table
-        const float x = i < 4 ? a1[0][i] : a1[1][i - 4];
-        const float u = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f), 0.0f,
-                                                (float)kPhiN - 0.5f);
-        const int k = (int)u;
-        const float2 e = phi[k];
-        h[i] = x * __builtin_fmaf(__builtin_amdgcn_fractf(u), e.y, e.x);
-      }
-      const bf16x8_t hf = __builtin_bit_cast(bf16x8_t, pack8(h));
+          for (int p = 0; p < 2; ++p)
+            a1[u][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1f[p][kk], af[u][kk], a1[u][p], 0, 0, 0);
 #pragma unroll
-      for (int nt = 0; nt < 6; ++nt) acc2[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[nt], hf, acc2[nt], 0, 0, 0);
-    }
-    // ---- y = z^ + fc2 + b2: lane holds columns 32j + 8g .. + 7 of token fr
-    const int64_t tok = t * 16 + fr;
-    if (tok < L) {
+      for (int u = 0; u < 2; ++u) {
+        float h[8];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        float ob[8], o[8];
-        unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 2 * C + 32 * j + 8 * g), ob);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[i] = cur.z[j][i] + acc2[2 * j][i] + ob[i];
-          o[4 + i] = cur.z[j][4 + i] + acc2[2 * j + 1][i] + ob[4 + i];
+        for (int i = 0; i < 8; ++i) {
+          // GELU(x) = x Phi(x), Phi from the table
+          const float x = i < 4 ? a1[u][0][i] : a1[u][1][i - 4];
+          const float uu = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f), 0.0f,
+                                                   (float)kPhiN - 0.5f);
+          const int k = (int)uu;
+          const float2 e = phi[k];
+          h[i] = x * __builtin_fmaf(__builtin_amdgcn_fractf(uu), e.y, e.x);
         }
-        *reinterpret_cast<u32x4_t*>(a.y + tok * C + 32 * j + 8 * g) = pack8(o);
+        const bf16x8_t hf = __builtin_bit_cast(bf16x8_t, pack8(h));
+#pragma unroll
+        for (int nt = 0; nt < 6; ++nt)
+          acc2[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[nt], hf, acc2[u][nt], 0, 0, 0);
       }
     }
-    if constexpr (PROJ) pcur = pnxt;
-    else cur = nxt;
-    if (t + nw < ntiles) front();
+    // ---- y = z^ + fc2 + b2: lane holds columns 32j + 8g .. + 7 of token fr of each tile
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t tok = (2 * t2 + u) * 16 + fr;
+      if (tok < L) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          float ob[8], o[8];
+          unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 2 * C + 32 * j + 8 * g), ob);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[i] = z[u].z[j][i] + acc2[u][2 * j][i] + ob[i];
+            o[4 + i] = z[u].z[j][4 + i] + acc2[u][2 * j + 1][i] + ob[4 + i];
+          }
+          *reinterpret_cast<u32x4_t*>(a.y + tok * C + 32 * j + 8 * g) = pack8(o);
+        }
+      }
+    }
+    if (t2 + nw < npairs) {
+      load_inputs(t2 + nw);
+      front();
+    }
   }
 }
 
@@ -557,12 +578,12 @@ namespace {
 template <bool PROJ>
 hipError_t launch_mlp_wave(const MlpArgs& a, hipStream_t st) {
   const int ncu = device_cu_count();
-  const int64_t tiles = (a.L + 15) / 16;
-  int64_t grid = (tiles + kMlpWaves - 1) / kMlpWaves;
+  const int64_t pairs = ((a.L + 15) / 16 + 1) / 2;
+  int64_t grid = (pairs + kMlpWaves - 1) / kMlpWaves;
   if (grid > ncu) grid = ncu;
-  hipError_t e = ensure_dynamic_lds((const void*)mlp_wave_kernel<PROJ>, kMlpLds);
+  hipError_t e = ensure_dynamic_lds((const void*)mlp_pair_kernel<PROJ>, kMlpLds);
   if (e != hipSuccess) return e;
-  mlp_wave_kernel<PROJ><<<dim3((unsigned)grid), dim3(kMlpThreads), kMlpLds, st>>>(a);
+  mlp_pair_kernel<PROJ><<<dim3((unsigned)grid), dim3(kMlpThreads), kMlpLds, st>>>(a);
   return hipGetLastError();
 }
 }  // namespace
