@@ -264,7 +264,7 @@ __device__ __forceinline__ u32x4_t pack8(const float f[8]) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kMlpWaves = 8;
+constexpr int kMlpWaves = 8;                 // at most, per workgroup (the launch picks 4..8)
 constexpr int kMlpThreads = 64 * kMlpWaves;
 constexpr int kMlpC = 96, kMlpHid = 4 * kMlpC;
 constexpr size_t kMlpW1 = (size_t)kMlpHid * kMlpC * 2;
@@ -358,13 +358,14 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   const float eps = a.eps;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwv = (int)(blockDim.x >> 6), nthr = (int)blockDim.x;
   const int fr = lane & 15, g = lane >> 4;
   // a wave owns a pair of 16-token tiles (2 t2, 2 t2 + 1): the weight
   // fragments of every chunk serve both, and the two tiles' chains are
   // independent work for the same wave
   const int64_t npairs = ((L + 15) / 16 + 1) / 2;
-  const int64_t nw = (int64_t)gridDim.x * kMlpWaves;
-  int64_t t2 = (int64_t)blockIdx.x * kMlpWaves + wave;
+  const int64_t nw = (int64_t)gridDim.x * nwv;
+  int64_t t2 = (int64_t)blockIdx.x * nwv + wave;
 
   ZTile z[2];
   ProjTileIn pin[2];
@@ -375,7 +376,24 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
       else ztile_load(z[u], a.zh, L, 2 * tp + u);
     }
   };
-  if (t2 < npairs) load_inputs(t2);
+  // the projection weight's 18 MFMA A fragments (output tile nt covers
+  // pair-order rows 16 nt .. + 15), read from L2 with the first pair's inputs
+  // and held until that pair's projection is done
+  bf16x8_t wpf[PROJ ? 6 : 1][3];
+  auto load_wp = [&]() {
+    if constexpr (PROJ) {
+#pragma unroll
+      for (int nt = 0; nt < 6; ++nt)
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk)
+          wpf[nt][kk] =
+              *reinterpret_cast<const bf16x8_t*>(a.wp + pair_row_inv(16 * nt + fr) * C + 32 * kk + 8 * g);
+    }
+  };
+  if (t2 < npairs) {
+    load_inputs(t2);
+    load_wp();
+  }
   // W1 and W2 go straight from global memory into their swizzled LDS layouts
   // (global_load_lds: a wave instruction fills 1 KB of consecutive LDS chunks
   // from per-lane addresses), still in flight while the first pair's
@@ -384,7 +402,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   {
     constexpr int NB = HID * (C / 8) / 64;   // 1 KB blocks per matrix
     static_assert(NB * 64 == HID * (C / 8), "weight staging shape");
-    for (int b = wave; b < NB; b += kMlpWaves) {
+    for (int b = wave; b < NB; b += nwv) {
       const int c = 64 * b + lane;
       const int r1 = c / (C / 8), qp1 = c - r1 * (C / 8);
       __builtin_amdgcn_global_load_lds(W1 + pair_row_inv(r1) * C + ((qp1 ^ ((r1 >> 2) & 3)) << 3),
@@ -394,17 +412,17 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
                                        (lds_ptr_t)(W2s + 1024 * b), 16, 0, 0);
     }
   }
-  for (int c = tid; c < HID; c += kMlpThreads) b1s[c] = b1 ? bf2f(b1[c]) : 0.f;
+  for (int c = tid; c < HID; c += nthr) b1s[c] = b1 ? bf2f(b1[c]) : 0.f;
   if constexpr (PROJ)
-    for (int c = tid; c < C; c += kMlpThreads) bps[c] = a.bp ? bf2f(a.bp[c]) : 0.f;
-  for (int i = tid; i < kPhiN; i += kMlpThreads) {
+    for (int c = tid; c < C; c += nthr) bps[c] = a.bp ? bf2f(a.bp[c]) : 0.f;
+  for (int i = tid; i < kPhiN; i += nthr) {
     const float h = 2.0f * kPhiX / kPhiN;
     const float x0 = -kPhiX + h * i, x1 = x0 + h;
     const float p0 = 0.5f * (1.0f + erff(x0 * 0.70710678118654752f));
     const float p1 = 0.5f * (1.0f + erff(x1 * 0.70710678118654752f));
     phi[i] = make_float2(p0, p1 - p0);
   }
-  for (int c = tid; c < 3 * (C / 8); c += kMlpThreads) {
+  for (int c = tid; c < 3 * (C / 8); c += nthr) {
     const int which = c / (C / 8), q = c - which * (C / 8);
     const bf16_t* src = which == 0 ? a.g2 : (which == 1 ? a.b2ln : a.bo);
     *reinterpret_cast<u32x4_t*>(vecs + which * C + q * 8) =
@@ -418,15 +436,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   auto front = [&]() {
     if constexpr (PROJ) {
       // 6 output tiles (pair order) of 16 tokens for each tile of the pair, the
-      // accumulators starting at the bias; the projection weight's 18 MFMA A
-      // fragments come from global memory (L2) once per pair
-      bf16x8_t wpf[6][3];
-#pragma unroll
-      for (int nt = 0; nt < 6; ++nt)
-#pragma unroll
-        for (int kk = 0; kk < 3; ++kk)
-          wpf[nt][kk] =
-              *reinterpret_cast<const bf16x8_t*>(a.wp + pair_row_inv(16 * nt + fr) * C + 32 * kk + 8 * g);
+      // accumulators starting at the bias
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         f32x4_t acc[6];
@@ -569,6 +579,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
     }
     if (t2 + nw < npairs) {
       load_inputs(t2 + nw);
+      load_wp();
       front();
     }
   }
@@ -579,11 +590,16 @@ template <bool PROJ>
 hipError_t launch_mlp_wave(const MlpArgs& a, hipStream_t st) {
   const int ncu = device_cu_count();
   const int64_t pairs = ((a.L + 15) / 16 + 1) / 2;
-  int64_t grid = (pairs + kMlpWaves - 1) / kMlpWaves;
+  // one workgroup per CU (the weights fill its LDS) with just enough waves for
+  // one pair each (Swin-T stage 1: 1568 pairs on 224 CUs x 7 waves rather than
+  // 196 x 8), at least 4 and at most 8; larger inputs loop
+  int64_t wpg = (pairs + ncu - 1) / ncu;
+  wpg = wpg < 4 ? 4 : (wpg > kMlpWaves ? kMlpWaves : wpg);
+  int64_t grid = (pairs + wpg - 1) / wpg;
   if (grid > ncu) grid = ncu;
   hipError_t e = ensure_dynamic_lds((const void*)mlp_pair_kernel<PROJ>, kMlpLds);
   if (e != hipSuccess) return e;
-  mlp_pair_kernel<PROJ><<<dim3((unsigned)grid), dim3(kMlpThreads), kMlpLds, st>>>(a);
+  mlp_pair_kernel<PROJ><<<dim3((unsigned)grid), dim3((unsigned)(64 * wpg)), kMlpLds, st>>>(a);
   return hipGetLastError();
 }
 }  // namespace
