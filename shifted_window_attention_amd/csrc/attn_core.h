@@ -62,6 +62,8 @@ struct A5 {
   Tab4Geo tg;                 // the prepared table (same extents as above)
   float qscale;               // multiplier applied to q on load (1 when pre-scaled)
   int force_max;
+  int run_q, run_r;           // the tile list split over the grid G: total = run_q G + run_r
+  FastDiv fdG;
   uint32_t off_kp, off_tab, off_buf, buf_bytes, off_v, off_lp, off_red;
 };
 
@@ -410,6 +412,25 @@ __device__ __forceinline__ void attn_pass(const unsigned char* B, const A5& L, c
 }
 
 inline size_t a5_lds(const A5& L) { return (size_t)L.off_buf + (size_t)L.NB * L.buf_bytes; }
+
+// the split of `total` tiles into G contiguous runs that run_bounds reads;
+// false when the tile count does not fit the device's 32-bit tile indices
+inline bool set_runs(A5& L, int64_t total, int64_t G) {
+  if (total <= 0 || total > 0x7fffffff || G <= 0 || G > 4096) return false;
+  L.run_q = (int)(total / G);
+  L.run_r = (int)(total % G);
+  L.fdG = make_fastdiv((uint32_t)G);
+  return true;
+}
+
+// run b of the grid: tiles [floor(b total / G), floor((b + 1) total / G)) of
+// the head-major list, in 32-bit arithmetic (b total / G = b q + b r / G).
+// The remainder is spread over the runs, so that at Swin-T stage 1 (37.5
+// tiles per run) every run spans exactly two windows.
+__device__ __forceinline__ void run_bounds(const A5& L, int b, int& t0, int& t1) {
+  t0 = b * L.run_q + (int)fdiv((uint32_t)(b * L.run_r), L.fdG);
+  t1 = (b + 1) * L.run_q + (int)fdiv((uint32_t)((b + 1) * L.run_r), L.fdG);
+}
 
 // temporal stride R' of the 4-tuple table: >= R and 4 mod 16 (conflict-free reads)
 inline int tab_rp(int R) { return R + ((4 - R) % 16 + 16) % 16; }

@@ -474,8 +474,8 @@ __global__ void __launch_bounds__(kFThreads) wattn_fused_kernel(const FusedArgs 
   int b = blockIdx.x;
   const int G = gridDim.x;
   if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
-  const int64_t total = (int64_t)L.heads * L.nW * L.QTT;   // < 2^31 (checked on the host)
-  const int t0 = (int)((int64_t)b * total / G), t1 = (int)((int64_t)(b + 1) * total / G);
+  int t0, t1;
+  run_bounds(L, b, t0, t1);
   if (t0 >= t1) return;
   const int QTT = L.QTT;
   auto item_of = [&](int tile) { return (int)fdiv((uint32_t)tile, L.fdQTT); };
@@ -704,6 +704,7 @@ hipError_t attention_fused(const FusedArgs& f, hipStream_t st) {
   // one workgroup per CU (the LDS of one), each a contiguous run
   int64_t G = device_cu_count();
   if (G > tiles) G = tiles;
+  if (!set_runs(L, tiles, G)) return hipErrorInvalidValue;
   const size_t lds = F.bytes;
   FusedArgs fk = f;
   fk.a = ak;

@@ -274,13 +274,13 @@ struct TileRun {
   int jt, cnt;
 };
 template <class CF>
-__device__ __forceinline__ TileRun tile_run(int wv, int w, int64_t t0, int64_t t1, int QTT) {
-  const int64_t base = (int64_t)w * QTT;
-  const int64_t lo = t0 > base ? t0 : base, hi = t1 < base + QTT ? t1 : base + QTT;
-  const int64_t first = lo + ((wv - (int)((lo - t0) % CF::kWaves)) + CF::kWaves) % CF::kWaves;
+__device__ __forceinline__ TileRun tile_run(int wv, int w, int t0, int t1, int QTT) {
+  const int base = w * QTT;
+  const int lo = t0 > base ? t0 : base, hi = t1 < base + QTT ? t1 : base + QTT;
+  const int first = lo + ((wv - (lo - t0) % CF::kWaves) + CF::kWaves) % CF::kWaves;
   TileRun r;
-  r.jt = (int)(first - base);
-  r.cnt = first < hi ? (int)((hi - first + CF::kWaves - 1) / CF::kWaves) : 0;
+  r.jt = first - base;
+  r.cnt = first < hi ? (hi - first + CF::kWaves - 1) / CF::kWaves : 0;
   return r;
 }
 
@@ -299,10 +299,10 @@ __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs 
   // each workgroup takes an equal contiguous run of it: with 1.5 windows per
   // workgroup every run spans exactly two windows.  A run that crosses into
   // the next head reloads the bias table at that window boundary.
-  const int64_t total = (int64_t)L.heads * L.nW * L.QTT;
-  const int64_t t0 = (int64_t)b * total / G, t1 = (int64_t)(b + 1) * total / G;
+  int t0, t1;
+  run_bounds(L, b, t0, t1);
   if (t0 >= t1) return;
-  const int i0 = (int)(t0 / L.QTT), i1 = (int)((t1 - 1) / L.QTT);
+  const int i0 = (int)fdiv((uint32_t)t0, L.fdQTT), i1 = (int)fdiv((uint32_t)(t1 - 1), L.fdQTT);
 
   int* kp = reinterpret_cast<int*>(smem + L.off_kp);
   stage_offsets<CF>(a, L, kp);
@@ -376,9 +376,11 @@ hipError_t launch_cfg(const AttnArgs& ak, const A5& L, hipStream_t st) {
   const int64_t cap = (int64_t)device_cu_count() * per_cu;
   int64_t G = cap < tiles ? cap : tiles;
   if (G < ak.heads) G = ak.heads;   // every head gets a workgroup
+  A5 LR = L;
+  if (!set_runs(LR, tiles, G)) return hipErrorInvalidValue;
   hipError_t e = ensure_dynamic_lds((const void*)attn_mfma_kernel<CF>, lds);
   if (e != hipSuccess) return e;
-  attn_mfma_kernel<CF><<<dim3((unsigned)G), dim3(CF::kThreads), lds, st>>>(ak, L);
+  attn_mfma_kernel<CF><<<dim3((unsigned)G), dim3(CF::kThreads), lds, st>>>(ak, LR);
   return hipGetLastError();
 }
 
