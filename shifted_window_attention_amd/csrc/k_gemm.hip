@@ -219,6 +219,203 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA GEMM for K a multiple of 64: block tile 128 tokens x BN features,
+// 4 waves as 2 x 2, K staged 64 at a time through a ring of S LDS stages
+// filled by global_load_lds_dwordx4 (one wave instruction moves 8 rows of 128
+// bytes straight into LDS: no register staging, no LDS store instructions).
+// Up to S - 1 stages are in flight while one is multiplied.  A stage holds
+// the 128 A rows and then the BN W rows, 128 bytes each; the 16-byte chunk c
+// of row r sits at chunk c ^ ((r >> 1) & 7), so the 16 rows of a fragment
+// read fall on 16 distinct 4-bank groups.  Workgroup b takes tile number
+// (b mod 8) * share + b / 8: the tiles of one XCD are consecutive (all
+// feature tiles of a token block share that XCD's L2).
+// The loads are issued from inline assembly and waited for with explicit
+// vmcnt counts: the compiler's own tracking of LDS DMA would wait for every
+// outstanding stage before reading any of them.  M0 carries the LDS address
+// of each load and is used for nothing else in this kernel.
+// ---------------------------------------------------------------------------
+constexpr int kDBK = 64;
+
+template <int BN, int S>
+struct DmaTile {
+  static constexpr int kRows = kBM + BN;           // LDS rows per stage
+  static constexpr int kStage = kRows * 128;        // bytes per stage
+  static constexpr int kPerWave = kRows / 8 / 4;    // DMA instructions per wave per stage
+  static constexpr int kLds = S * kStage;
+  static_assert(kRows % 32 == 0, "rows per stage must split over 4 waves x 8 rows");
+  static_assert(S >= 2 && S <= 4, "2 to 4 stages");
+};
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt left alone)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// wait until at most `stages` stages of D loads each are outstanding
+template <int S, int D>
+__device__ __forceinline__ void wait_stages(int stages) {
+  if constexpr (S == 2) {
+    wait_vm_lgkm0<0>();
+  } else if constexpr (S == 3) {
+    if (stages > 0) wait_vm_lgkm0<D>();
+    else wait_vm_lgkm0<0>();
+  } else {
+    if (stages > 1) wait_vm_lgkm0<2 * D>();
+    else if (stages > 0) wait_vm_lgkm0<D>();
+    else wait_vm_lgkm0<0>();
+  }
+}
+
+template <int BN, int S, class E>
+__global__ void __launch_bounds__(256) gemm_bf16_dma_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
+                                                            int64_t M, int N, int K, E epi, int tq, int tr) {
+  using T = DmaTile<BN, S>;
+  constexpr int WN = BN / 2;
+  constexpr int NT = WN / 16;
+  constexpr int MT = 4;
+  constexpr int D = T::kPerWave;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  // XCD-contiguous tile numbering
+  const int b = blockIdx.x, xcd = b & 7;
+  const int tile = xcd * tq + min(xcd, tr) + (b >> 3);
+  const int nb = N / BN;
+  const int bm = tile / nb;
+  const int bn = tile - bm * nb;
+  const int64_t m0 = (int64_t)bm * kBM;
+  const int n0 = bn * BN;
+
+  // per-lane source pointers of this wave's DMA instructions (stage 0)
+  const bf16_t* gp[D];
+  uint32_t lo[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const int j = wave + 4 * i;                 // instruction index: rows 8j .. 8j + 7 of the stage
+    const int row = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    if (row < kBM) {
+      int64_t m = m0 + row;
+      m = m < M ? m : M - 1;                    // rows past M load row M - 1 (never stored)
+      gp[i] = A + m * K + 8 * c;
+    } else {
+      gp[i] = W + (int64_t)(n0 + row - kBM) * K + 8 * c;
+    }
+    lo[i] = __builtin_amdgcn_readfirstlane(8 * j * 128);
+  }
+  auto issue = [&](int kt, int slot) {   // stage kt (K columns 64 kt ..) into LDS slot
+    const uint32_t sb = lds0 + (uint32_t)(slot * T::kStage);
+#pragma unroll
+    for (int i = 0; i < D; ++i) lds_dma16(gp[i] + (int64_t)kt * kDBK, sb + lo[i]);
+  };
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, g4 = lane >> 4;
+  const int sx = (fr >> 1) & 7;
+  const int xo0 = ((g4 ^ sx) << 4), xo1 = (((4 + g4) ^ sx) << 4);
+  const int nk = K / kDBK;
+  auto mainloop = [&](auto swap_tag) {
+    constexpr bool SWAP = decltype(swap_tag)::value;
+    auto frags = [&](int slot, int s, bf16x8_t (&af)[MT], bf16x8_t (&wf)[NT]) {
+      const unsigned char* st = smem + slot * T::kStage;
+      const int xo = s ? xo1 : xo0;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        af[mt] = *reinterpret_cast<const bf16x8_t*>(st + (wm * 64 + mt * 16 + fr) * 128 + xo);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        wf[nt] = *reinterpret_cast<const bf16x8_t*>(st + (kBM + wn * WN + nt * 16 + fr) * 128 + xo);
+    };
+    auto mma = [&](const bf16x8_t (&af)[MT], const bf16x8_t (&wf)[NT]) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (SWAP)   // rows = tokens, cols = features
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], wf[nt], acc[mt][nt], 0, 0, 0);
+          else                  // rows = features, cols = tokens
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], af[mt], acc[mt][nt], 0, 0, 0);
+        }
+    };
+    // Stage kt lands in slot kt % S.  A step waits for the next stage, reads
+    // its first half (32 k) of fragments while the current stage's second
+    // half multiplies, then its second half while the first half multiplies;
+    // a slot is refilled (stage kt + S) as soon as every wave holds all of
+    // stage kt's fragments.  The wait and barrier open the loop body: placed
+    // after the products, they make the compiler move the accumulators
+    // between registers at every step.
+    const int pre = nk < S ? nk : S;
+    for (int q = 0; q < pre; ++q) issue(q, q);
+    wait_stages<S, D>(pre - 1);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    bf16x8_t a0[MT], w0[NT], a1[MT], w1[NT];
+    frags(0, 0, a0, w0);
+    frags(0, 1, a1, w1);
+    mma(a0, w0);
+    int slot = 0;
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      asm volatile("" ::: "memory");
+      // stage kt + 1 landed; stages kt + 2 .. kt + S - 1 may be in flight
+      wait_stages<S, D>((kt + S - 1 < nk - 1 ? kt + S - 1 : nk - 1) - (kt + 1));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + S < nk) issue(kt + S, slot);
+      slot = slot == S - 1 ? 0 : slot + 1;
+      frags(slot, 0, a0, w0);
+      mma(a1, w1);
+      frags(slot, 1, a1, w1);
+      mma(a0, w0);
+    }
+    mma(a1, w1);
+    if constexpr (SWAP) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m4 = m0 + wm * 64 + mt * 16 + g4 * 4;
+        if (m4 >= M) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+          epi.store_t(m4, n0 + wn * WN + nt * 16 + fr, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = m0 + wm * 64 + mt * 16 + fr;
+        if (m >= M) continue;
+        const int64_t rc = epi.row_ctx(m);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = n0 + wn * WN + nt * 16 + g4 * 4;
+          float v[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+          epi.store(m, rc, n, v);
+        }
+      }
+    }
+  };
+  if (epi.swapped(n0)) mainloop(std::true_type{});
+  else mainloop(std::false_type{});
+}
+
+// ---------------------------------------------------------------------------
 // bf16 MFMA GEMM with the whole K extent (K <= 128) staged in one batch:
 // one global round trip and one barrier per workgroup.  The A rows can be
 // gathered through the window map and layer-normalised on the way into LDS
@@ -500,6 +697,27 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
   }
 }
 
+// tile of the staged-K kernel for this shape: feature width (0: not served)
+// and LDS stages.  F is the width every feature tile must stay inside (q, k,
+// v for the qkv projection).  64-wide feature tiles (24 KB per stage) let
+// several workgroups share a CU; the stage count trades depth for
+// residency: with at most one tile per CU, four stages (one workgroup per
+// CU); up to two, three stages (two per CU); more, two stages (three per
+// CU).  Measured on the Swin-T backbone's projections (K = 192 .. 3072).
+struct DmaChoice {
+  int bn, stages;
+};
+static DmaChoice dma_choice(int64_t M, int N, int K, int F) {
+  DmaChoice c{0, 2};
+  if (K % kDBK != 0 || K < kDBK || M <= 0) return c;
+  if (N % 64 == 0 && F % 64 == 0) c.bn = 64;
+  else if (N % 96 == 0 && F % 96 == 0) c.bn = 96;
+  else return c;
+  const int64_t tiles = (M + kBM - 1) / kBM * (N / c.bn);
+  c.stages = tiles <= 256 ? 4 : (tiles <= 512 ? 3 : 2);
+  return c;
+}
+
 template <Epi KIND>
 static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int64_t M, int N, int K,
                               const EpiArgs& e, const APrologue& pro, hipStream_t st) {
@@ -520,6 +738,25 @@ static hipError_t launch_kind(vswin_dtype dt, const void* A, const void* W, int6
       else if (N % 64 == 0 && F % 64 == 0) go(gemm_bf16_fullk_kernel<64, 128, EpiDev<bf16_t, KIND>>, 64);
       else go(gemm_bf16_fullk_kernel<32, 128, EpiDev<bf16_t, KIND>>, 32);
     }
+  } else if (dt == VSWIN_BF16 && pro.mode == 0 && dma_choice(M, N, K, KIND == Epi::kQKV ? e.C : N).bn != 0) {
+    EpiDev<bf16_t, KIND> epi{e};
+    const DmaChoice ch = dma_choice(M, N, K, KIND == Epi::kQKV ? e.C : N);
+    const int64_t tiles = (M + kBM - 1) / kBM * (N / ch.bn);
+    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+    auto go = [&](auto kern, int lds) -> hipError_t {
+      const hipError_t le = ensure_dynamic_lds((const void*)kern, lds);
+      if (le != hipSuccess) return le;
+      kern<<<dim3((unsigned)tiles), dim3(256), lds, st>>>((const bf16_t*)A, (const bf16_t*)W, M, N, K, epi,
+                                                         (int)(tiles / 8), (int)(tiles % 8));
+      return hipGetLastError();
+    };
+#define VSWIN_DMA_GO(BN_, S_)                                                       \
+  if (ch.bn == BN_ && ch.stages == S_)                                              \
+    return go(gemm_bf16_dma_kernel<BN_, S_, EpiDev<bf16_t, KIND>>, DmaTile<BN_, S_>::kLds);
+    VSWIN_DMA_GO(64, 2) VSWIN_DMA_GO(64, 3) VSWIN_DMA_GO(64, 4)
+    VSWIN_DMA_GO(96, 2) VSWIN_DMA_GO(96, 3) VSWIN_DMA_GO(96, 4)
+#undef VSWIN_DMA_GO
+    return hipErrorInvalidValue;
   } else if (dt == VSWIN_BF16) {
     if (pro.mode != 0) return hipErrorInvalidValue;   // gathered A rows need the full-K kernel
     EpiDev<bf16_t, KIND> epi{e};
