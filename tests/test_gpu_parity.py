@@ -323,6 +323,25 @@ def test_block_swin_l_width():
         check(host64(y), ref, "bf16", f"C=192 block shift {shift}")
 
 
+@pytest.mark.parametrize("C,heads,shape", [
+    (64, 2, (1, 16, 28, 28)),    # K = 64: a single K stage; fc2 K = 256; 3- and 4-stage rings
+    (320, 10, (1, 8, 28, 21)),   # K = 320: five stages; 4704 tokens (ragged last 128-row tile); 2-stage ring
+])
+def test_block_staged_k_gemm_shapes(C, heads, shape):
+    """Widths outside the published models that route every linear layer
+    through the staged-K GEMM: one and five K stages, a token count that is
+    not a multiple of the 128-row tile, and tile counts that pick each ring
+    depth; regular and shifted, stress init."""
+    window = (8, 7, 7)
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=41)
+    x = _rng_tokens(shape + (C,), "bf16", 14)
+    for shift in ((0, 0, 0), (4, 3, 3)):
+        say(f"staged-K widths: C={C} tokens {shape} shift {shift}")
+        y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
+        _, ref = oracle.block(x, p, heads, window, shift)
+        check(host64(y), ref, "bf16", f"C={C} block shift {shift}")
+
+
 def test_workload1_fp32_pair():
     say("workload 1: fp32 block pair")
     x, params = synth.gen_workload(1)
