@@ -268,14 +268,19 @@ constexpr int kMlpWaves = 8;                 // at most, per workgroup (the laun
 constexpr int kMlpThreads = 64 * kMlpWaves;
 constexpr int kMlpC = 96, kMlpHid = 4 * kMlpC;
 constexpr size_t kMlpW1 = (size_t)kMlpHid * kMlpC * 2;
-// Phi(x) = (1 + erf(x / sqrt 2)) / 2 by linear interpolation in a table of
-// kPhiN points over [-kPhiX, kPhiX): h = 2 kPhiX / kPhiN = 0.0176, error
-// <= max|Phi''| h^2 / 8 = 0.242 * 3.1e-4 / 8 < 1e-5 inside the range and
-// < 3.4e-6 (the tail mass) outside it, where the index is clamped.
+// GELU(x) = x Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2, as a piecewise linear
+// function in intercept-slope form: kPhiN bins of width h = 2 kPhiX / kPhiN
+// = 0.0176 over [-kPhiX, kPhiX), entry k + 1 of bin k holding (c, d) with
+// GELU(x) ~ c + d x through the bin's end points, plus entry 0 = (0, 0) for
+// x < -kPhiX and entry kPhiN + 1 = (0, 1) for x >= kPhiX, reached by
+// clamping the bin index.  Error <= max|GELU''| h^2 / 8 = 0.80 * 3.1e-4 / 8
+// < 3.1e-5 inside (GELU'' = phi(x) (2 - x^2)), and |x| (1 - Phi(|x|)) <
+// 1.6e-5 outside.  A lookup is one FMA for the index, a clamp, a convert,
+// one 8-byte LDS read and one FMA.
 constexpr int kPhiN = 512;
 constexpr float kPhiX = 4.5f;
 constexpr size_t kMlpVec = kMlpHid * 4 + kMlpC * 4 + 3 * kMlpC * 2;     // b1, proj bias (fp32), LN2 gamma / beta, fc2 bias
-constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + kPhiN * 8;
+constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + (kPhiN + 2) * 8;
 
 struct ZTile {
   float z[3][8];     // columns 32j + 8g .. + 7 of token fr
@@ -350,7 +355,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   float* b1s = reinterpret_cast<float*>(lds + 2 * kMlpW1);   // fc1 bias, fp32
   float* bps = b1s + HID;                                    // projection bias, fp32
   bf16_t* vecs = reinterpret_cast<bf16_t*>(bps + C);         // LN2 gamma, beta, fc2 bias (C each)
-  float2* phi = reinterpret_cast<float2*>(lds + 2 * kMlpW1 + kMlpVec);   // (Phi(x_i), Phi(x_i+1) - Phi(x_i))
+  float2* phi = reinterpret_cast<float2*>(lds + 2 * kMlpW1 + kMlpVec);   // GELU bins: (intercept, slope)
   const bf16_t* __restrict__ W1 = a.W1;
   const bf16_t* __restrict__ W2 = a.W2;
   const bf16_t* __restrict__ b1 = a.b1;
@@ -415,12 +420,17 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   for (int c = tid; c < HID; c += nthr) b1s[c] = b1 ? bf2f(b1[c]) : 0.f;
   if constexpr (PROJ)
     for (int c = tid; c < C; c += nthr) bps[c] = a.bp ? bf2f(a.bp[c]) : 0.f;
-  for (int i = tid; i < kPhiN; i += nthr) {
-    const float h = 2.0f * kPhiX / kPhiN;
-    const float x0 = -kPhiX + h * i, x1 = x0 + h;
-    const float p0 = 0.5f * (1.0f + erff(x0 * 0.70710678118654752f));
-    const float p1 = 0.5f * (1.0f + erff(x1 * 0.70710678118654752f));
-    phi[i] = make_float2(p0, p1 - p0);
+  for (int i = tid; i < kPhiN + 2; i += nthr) {
+    float2 e = make_float2(0.f, i == 0 ? 0.f : 1.f);   // the two tails
+    if (i >= 1 && i <= kPhiN) {
+      const float h = 2.0f * kPhiX / kPhiN;
+      const float x0 = -kPhiX + h * (i - 1), x1 = x0 + h;
+      const float g0 = x0 * 0.5f * (1.0f + erff(x0 * 0.70710678118654752f));
+      const float g1 = x1 * 0.5f * (1.0f + erff(x1 * 0.70710678118654752f));
+      const float d = (g1 - g0) / h;
+      e = make_float2(g0 - d * x0, d);
+    }
+    phi[i] = e;
   }
   for (int c = tid; c < 3 * (C / 8); c += nthr) {
     const int which = c / (C / 8), q = c - which * (C / 8);
@@ -545,13 +555,12 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
         float h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          // GELU(x) = x Phi(x), Phi from the table
+          // GELU(x) = c + d x from the bin's table entry
           const float x = i < 4 ? a1[u][0][i] : a1[u][1][i - 4];
-          const float uu = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f), 0.0f,
-                                                   (float)kPhiN - 0.5f);
-          const int k = (int)uu;
-          const float2 e = phi[k];
-          h[i] = x * __builtin_fmaf(__builtin_amdgcn_fractf(uu), e.y, e.x);
+          const float uu = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f + 1.0f),
+                                                   0.0f, (float)kPhiN + 1.5f);
+          const float2 e = phi[(int)uu];
+          h[i] = __builtin_fmaf(x, e.y, e.x);
         }
         const bf16x8_t hf = __builtin_bit_cast(bf16x8_t, pack8(h));
 #pragma unroll
