@@ -8,30 +8,45 @@
 // finally y = z^ + acc + b2 rounded to bf16.  The next chunk's weights are
 // fetched into registers while the current chunk computes.
 //
-// GELU uses erf from the Abramowitz & Stegun formula 7.1.26 (Hastings'
-// approximation, |error| <= 1.5e-7): erf(x) = 1 - (a1 t + ... + a5 t^5)
-// exp(-x^2), t = 1 / (1 + p x) for x >= 0, odd extension for x < 0.
+// GELU comes from a piecewise linear table of its values (below).
 #include "vswin_kernels.h"
 
 namespace vswin {
 
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, ax, 1.0f));
-  float p = 1.061405429f;
-  p = __builtin_fmaf(p, t, -1.453152027f);
-  p = __builtin_fmaf(p, t, 1.421413741f);
-  p = __builtin_fmaf(p, t, -0.284496736f);
-  p = __builtin_fmaf(p, t, 0.254829592f);
-  p *= t;
-  // exp(-x^2) = exp2(-x^2 log2 e)
-  const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);
-  const float r = __builtin_fmaf(-p, e, 1.0f);
-  return copysignf(r, x);
+// GELU(x) = x Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2, as a piecewise linear
+// function in intercept-slope form: kPhiN bins of width h = 2 kPhiX / kPhiN
+// = 0.0176 over [-kPhiX, kPhiX), entry k + 1 of bin k holding (c, d) with
+// GELU(x) ~ c + d x through the bin's end points, plus entry 0 = (0, 0) for
+// x < -kPhiX and entry kPhiN + 1 = (0, 1) for x >= kPhiX, reached by
+// clamping the bin index.  Error <= max|GELU''| h^2 / 8 = 0.80 * 3.1e-4 / 8
+// < 3.1e-5 inside (GELU'' = phi(x) (2 - x^2)), and |x| (1 - Phi(|x|)) <
+// 1.6e-5 outside.  A lookup is one FMA for the index, a clamp, a convert,
+// one 8-byte LDS read and one FMA.
+constexpr int kPhiN = 512;
+constexpr float kPhiX = 4.5f;
+constexpr int kGeluEntries = kPhiN + 2;
+
+// the table, built by the nthr threads of a workgroup (a barrier must follow)
+__device__ __forceinline__ void gelu_table_build(float2* t, int tid, int nthr) {
+  for (int i = tid; i < kGeluEntries; i += nthr) {
+    float2 e = make_float2(0.f, i == 0 ? 0.f : 1.f);   // the two tails
+    if (i >= 1 && i <= kPhiN) {
+      const float h = 2.0f * kPhiX / kPhiN;
+      const float x0 = -kPhiX + h * (i - 1), x1 = x0 + h;
+      const float g0 = x0 * 0.5f * (1.0f + erff(x0 * 0.70710678118654752f));
+      const float g1 = x1 * 0.5f * (1.0f + erff(x1 * 0.70710678118654752f));
+      const float d = (g1 - g0) / h;
+      e = make_float2(g0 - d * x0, d);
+    }
+    t[i] = e;
+  }
 }
 
-__device__ __forceinline__ float gelu_fast(float x) {
-  return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f));
+__device__ __forceinline__ float gelu_tab(const float2* t, float x) {
+  const float uu = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f + 1.0f), 0.0f,
+                                           (float)kPhiN + 1.5f);
+  const float2 e = t[(int)uu];
+  return __builtin_fmaf(x, e.y, e.x);
 }
 
 template <int C>
@@ -50,6 +65,7 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const float* __restrict_
   __shared__ __attribute__((aligned(16))) bf16_t Hs[BM * LDH];
   __shared__ __attribute__((aligned(16))) bf16_t W1s[HC * LDA];
   __shared__ __attribute__((aligned(16))) bf16_t W2s[C * LDH];
+  __shared__ float2 gtab[kGeluEntries];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -139,6 +155,7 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const float* __restrict_
     }
   }
   stash();
+  gelu_table_build(gtab, tid, 256);
   __syncthreads();
 
   f32x4_t acc2[2][NT2];
@@ -178,7 +195,7 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const float* __restrict_
         float bb[4] = {0.f, 0.f, 0.f, 0.f}, o[4];
         if (b1) load4(b1, hc * HC + hcol, bb);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = gelu_fast(acc1[i][j][k] + bb[k]);
+        for (int k = 0; k < 4; ++k) o[k] = gelu_tab(gtab, acc1[i][j][k] + bb[k]);
         u32x2_t pk;
         pk[0] = pack_bf16x2(o[0], o[1]);
         pk[1] = pack_bf16x2(o[2], o[3]);
@@ -268,17 +285,6 @@ constexpr int kMlpWaves = 8;                 // at most, per workgroup (the laun
 constexpr int kMlpThreads = 64 * kMlpWaves;
 constexpr int kMlpC = 96, kMlpHid = 4 * kMlpC;
 constexpr size_t kMlpW1 = (size_t)kMlpHid * kMlpC * 2;
-// GELU(x) = x Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2, as a piecewise linear
-// function in intercept-slope form: kPhiN bins of width h = 2 kPhiX / kPhiN
-// = 0.0176 over [-kPhiX, kPhiX), entry k + 1 of bin k holding (c, d) with
-// GELU(x) ~ c + d x through the bin's end points, plus entry 0 = (0, 0) for
-// x < -kPhiX and entry kPhiN + 1 = (0, 1) for x >= kPhiX, reached by
-// clamping the bin index.  Error <= max|GELU''| h^2 / 8 = 0.80 * 3.1e-4 / 8
-// < 3.1e-5 inside (GELU'' = phi(x) (2 - x^2)), and |x| (1 - Phi(|x|)) <
-// 1.6e-5 outside.  A lookup is one FMA for the index, a clamp, a convert,
-// one 8-byte LDS read and one FMA.
-constexpr int kPhiN = 512;
-constexpr float kPhiX = 4.5f;
 constexpr size_t kMlpVec = kMlpHid * 4 + kMlpC * 4 + 3 * kMlpC * 2;     // b1, proj bias (fp32), LN2 gamma / beta, fc2 bias
 constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + (kPhiN + 2) * 8;
 
@@ -420,18 +426,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   for (int c = tid; c < HID; c += nthr) b1s[c] = b1 ? bf2f(b1[c]) : 0.f;
   if constexpr (PROJ)
     for (int c = tid; c < C; c += nthr) bps[c] = a.bp ? bf2f(a.bp[c]) : 0.f;
-  for (int i = tid; i < kPhiN + 2; i += nthr) {
-    float2 e = make_float2(0.f, i == 0 ? 0.f : 1.f);   // the two tails
-    if (i >= 1 && i <= kPhiN) {
-      const float h = 2.0f * kPhiX / kPhiN;
-      const float x0 = -kPhiX + h * (i - 1), x1 = x0 + h;
-      const float g0 = x0 * 0.5f * (1.0f + erff(x0 * 0.70710678118654752f));
-      const float g1 = x1 * 0.5f * (1.0f + erff(x1 * 0.70710678118654752f));
-      const float d = (g1 - g0) / h;
-      e = make_float2(g0 - d * x0, d);
-    }
-    phi[i] = e;
-  }
+  gelu_table_build(phi, tid, nthr);
   for (int c = tid; c < 3 * (C / 8); c += nthr) {
     const int which = c / (C / 8), q = c - which * (C / 8);
     const bf16_t* src = which == 0 ? a.g2 : (which == 1 ? a.b2ln : a.bo);
@@ -555,12 +550,8 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
         float h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          // GELU(x) = c + d x from the bin's table entry
           const float x = i < 4 ? a1[u][0][i] : a1[u][1][i - 4];
-          const float uu = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, kPhiN / (2.0f * kPhiX), kPhiN / 2.0f + 1.0f),
-                                                   0.0f, (float)kPhiN + 1.5f);
-          const float2 e = phi[(int)uu];
-          h[i] = __builtin_fmaf(x, e.y, e.x);
+          h[i] = gelu_tab(phi, x);
         }
         const bf16x8_t hf = __builtin_bit_cast(bf16x8_t, pack8(h));
 #pragma unroll
