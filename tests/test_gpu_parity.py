@@ -430,6 +430,35 @@ def _backbone_dev(params):
     }
 
 
+@pytest.mark.parametrize("dtype,shape,offset", [
+    ("bf16", (1, 3, 5, 10, 12), False),   # T and H padded to the patch, 4-wide w groups
+    ("fp32", (2, 3, 4, 8, 8), False),
+    ("bf16", (1, 2, 6, 12, 16), False),   # 2 channels
+    ("bf16", (1, 3, 4, 8, 10), False),    # W not a multiple of 4: element-wise gather
+    ("bf16", (1, 3, 4, 8, 8), True),      # video not 16-byte aligned: refused before any launch
+])
+def test_patch_embed_grids(dtype, shape, offset):
+    """Patch embedding (2x4x4 patches, C = 96) on grids that exercise the
+    vector gather (4 consecutive w per thread), its zero fill past the video's
+    end and the element-wise fallback; a misaligned video is an error."""
+    say(f"patch embed {dtype} {shape} offset {offset}")
+    rng = np.random.default_rng(53)
+    video = rng.standard_normal(shape).astype(np.float32)
+    w = (0.02 * rng.standard_normal((96, shape[1], 2, 4, 4))).astype(np.float32)
+    b = (0.02 * rng.standard_normal(96)).astype(np.float32)
+    if dtype == "bf16":   # values representable in bf16, so both sides see the same inputs
+        video, w, b = (torch.from_numpy(a).to(torch.bfloat16).float().numpy() for a in (video, w, b))
+    vt = dev(video, dtype)
+    if offset:
+        big = torch.empty(vt.numel() + 1, dtype=vt.dtype, device=vt.device)
+        big[1:] = vt.reshape(-1)
+        with pytest.raises(vs.VswinError, match="aligned"):
+            vs.vswin_patch_embed_fwd(big[1:].view(vt.shape), dev(w, dtype), dev(b, dtype))
+        return
+    y = vs.vswin_patch_embed_fwd(vt, dev(w, dtype), dev(b, dtype))
+    check(host64(y), oracle.patch_embed(video, w, b), dtype, f"patch embed {shape}")
+
+
 def test_workload5_backbone():
     """Workload 5 (Swin-T backbone, B=2 clips of 3x32x224x224).  Gate: every
     block, merge, the embedding and the final LN teacher-forced (each compared
