@@ -15,12 +15,24 @@
 namespace vswin {
 
 
-template <int C>
-__global__ void __launch_bounds__(256) mlp_fused_kernel(const float* __restrict__ zh, const bf16_t* __restrict__ g2,
+// With PROJ the output projection runs in front: z^ = x + o Wp^T + bp for the
+// workgroup's 64 tokens (o gathered from window-row order, Wp fragments read
+// from L2) stays in registers in the layout of the fc2 accumulators, and LN2's
+// row statistics combine the two feature halves of a token through LDS.
+struct MlpProj {
+  const bf16_t* o;    // attention output, window rows (Lp, C)
+  const bf16_t* x;    // block input token rows (L, C): the residual
+  const bf16_t* wp;   // (C, C)
+  const bf16_t* bp;   // (C) or NULL
+  WinGeo geo;
+};
+
+template <int C, bool PROJ>
+__global__ void __launch_bounds__(256, 2) mlp_fused_kernel(const float* __restrict__ zh, const bf16_t* __restrict__ g2,
                                                         const bf16_t* __restrict__ b2ln, const bf16_t* __restrict__ W1,
                                                         const bf16_t* __restrict__ b1, const bf16_t* __restrict__ W2,
                                                         const bf16_t* __restrict__ bo, bf16_t* __restrict__ y,
-                                                        int64_t L, float eps) {
+                                                        int64_t L, float eps, const MlpProj pj) {
   constexpr int BM = 64, HC = 64, HID = 4 * C, NCH = HID / HC;
   constexpr int LDA = C + 8, LDH = HC + 8;
   constexpr int NT2 = C / 32;            // GEMM2 feature tiles of 16 per wave (C/2 features)
@@ -78,6 +90,94 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const float* __restrict_
   };
 
   fetch(0);
+  // z^ of the lane's tokens wm*32 + 16i + fr, features wn*(C/2) + 16j + 4*g4 .. +3 (PROJ)
+  float zr[PROJ ? 2 : 1][PROJ ? NT2 : 1][4];
+  if constexpr (PROJ) {
+    __shared__ float red[2][2][BM];   // [pass][feature half][token]
+    f32x4_t pacc[2][NT2];
+#pragma unroll
+    for (int j = 0; j < NT2; ++j) {
+      float bb[4] = {0.f, 0.f, 0.f, 0.f};
+      if (pj.bp) load4(pj.bp, wn * (C / 2) + j * 16 + 4 * g4, bb);
+      pacc[0][j] = pacc[1][j] = f32x4_t{bb[0], bb[1], bb[2], bb[3]};
+    }
+    int64_t orow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t tok = m0 + wm * 32 + i * 16 + fr;
+      orow[i] = tok < L ? token_row(pj.geo, (int)tok) : 0;
+    }
+#pragma unroll
+    for (int kk = 0; kk < C / 32; ++kk) {
+      bf16x8_t of[2], wf[NT2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) of[i] = *reinterpret_cast<const bf16x8_t*>(pj.o + orow[i] * C + 32 * kk + 8 * g4);
+#pragma unroll
+      for (int j = 0; j < NT2; ++j)
+        wf[j] = *reinterpret_cast<const bf16x8_t*>(pj.wp + (int64_t)(wn * (C / 2) + j * 16 + fr) * C + 32 * kk + 8 * g4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NT2; ++j)
+          pacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], of[i], pacc[i][j], 0, 0, 0);
+    }
+    // + residual; partial sums over the wave's feature half
+    float part[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t tok = m0 + wm * 32 + i * 16 + fr;
+#pragma unroll
+      for (int j = 0; j < NT2; ++j) {
+        float xr[4] = {0.f, 0.f, 0.f, 0.f};
+        if (tok < L) load4(pj.x, tok * C + wn * (C / 2) + j * 16 + 4 * g4, xr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          zr[i][j][e] = tok < L ? xr[e] + pacc[i][j][e] : 0.f;
+          part[i] += zr[i][j][e];
+        }
+      }
+      part[i] += __shfl_xor(part[i], 16);
+      part[i] += __shfl_xor(part[i], 32);
+      if (g4 == 0) red[0][wn][wm * 32 + i * 16 + fr] = part[i];
+    }
+    __syncthreads();
+    float mean[2], q[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = wm * 32 + i * 16 + fr;
+      mean[i] = (red[0][0][t] + red[0][1][t]) * (1.0f / C);
+#pragma unroll
+      for (int j = 0; j < NT2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dd = zr[i][j][e] - mean[i];
+          q[i] += dd * dd;
+        }
+      q[i] += __shfl_xor(q[i], 16);
+      q[i] += __shfl_xor(q[i], 32);
+      if (g4 == 0) red[1][wn][t] = q[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = wm * 32 + i * 16 + fr;
+      const float rstd = 1.0f / sqrtf((red[1][0][t] + red[1][1][t]) * (1.0f / C) + eps);
+      const bool live = m0 + t < L;
+#pragma unroll
+      for (int j = 0; j < NT2; ++j) {
+        const int n = wn * (C / 2) + j * 16 + 4 * g4;
+        float gg[4], bb[4], o[4];
+        load4(g2, n, gg);
+        load4(b2ln, n, bb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = live ? (zr[i][j][e] - mean[i]) * rstd * gg[e] + bb[e] : 0.f;
+        u32x2_t pk;
+        pk[0] = pack_bf16x2(o[0], o[1]);
+        pk[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2_t*>(&As[t * LDA + n]) = pk;
+      }
+    }
+  } else
   // ---- LN2: 4 lanes per token row, C/4 values each
   {
     constexpr int PER = C / 4;
@@ -199,7 +299,12 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const float* __restrict_
     for (int j = 0; j < NT2; ++j) {
       const int n = wn * (C / 2) + j * 16 + 4 * g4;
       float r[4], bb[4], o[4];
-      load4(zh, m * C + n, r);
+      if constexpr (PROJ) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = zr[i][j][e];
+      } else {
+        load4(zh, m * C + n, r);
+      }
       if (bo) load4(bo, n, bb);
       else bb[0] = bb[1] = bb[2] = bb[3] = 0.f;
 #pragma unroll
@@ -570,12 +675,22 @@ hipError_t launch_mlp_wave(const MlpArgs& a, hipStream_t st) {
 }
 }  // namespace
 
-bool proj_mlp_supported(vswin_dtype dt, int C, int hid) { return dt == VSWIN_BF16 && C == 96 && hid == 4 * C; }
+bool proj_mlp_supported(vswin_dtype dt, int C, int hid) {
+  return dt == VSWIN_BF16 && (C == 96 || C == 128) && hid == 4 * C;
+}
 
 hipError_t proj_mlp(const void* o, const void* x, const void* wp, const void* bp, const void* g2, const void* b2ln,
                     const void* W1, const void* b1, const void* W2, const void* bo, void* y, int64_t L, int C,
                     float eps, const WinGeo& geo, hipStream_t st) {
   if (L <= 0) return hipSuccess;
+  if (C == 128) {
+    if (L > 0x7fffffff) return hipErrorInvalidValue;
+    const MlpProj pj{(const bf16_t*)o, (const bf16_t*)x, (const bf16_t*)wp, (const bf16_t*)bp, geo};
+    hipLaunchKernelGGL((mlp_fused_kernel<128, true>), dim3((unsigned)((L + 63) / 64)), dim3(256), 0, st, nullptr,
+                       (const bf16_t*)g2, (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1,
+                       (const bf16_t*)W2, (const bf16_t*)bo, (bf16_t*)y, L, eps, pj);
+    return hipGetLastError();
+  }
   if (C != 96) return hipErrorInvalidValue;
   MlpArgs a{};
   a.o = (const bf16_t*)o; a.x = (const bf16_t*)x; a.wp = (const bf16_t*)wp; a.bp = (const bf16_t*)bp;
@@ -602,9 +717,9 @@ hipError_t mlp_fused(const float* zh, const void* g2, const void* b2ln, const vo
     a.y = (bf16_t*)y; a.L = L; a.eps = eps;
     return launch_mlp_wave<false>(a, st);
   } else if (C == 128)
-    hipLaunchKernelGGL(mlp_fused_kernel<128>, dim3(blocks), dim3(256), 0, st, zh, (const bf16_t*)g2,
+    hipLaunchKernelGGL((mlp_fused_kernel<128, false>), dim3(blocks), dim3(256), 0, st, zh, (const bf16_t*)g2,
                        (const bf16_t*)b2ln, (const bf16_t*)W1, (const bf16_t*)b1, (const bf16_t*)W2,
-                       (const bf16_t*)bo, (bf16_t*)y, L, eps);
+                       (const bf16_t*)bo, (bf16_t*)y, L, eps, MlpProj{});
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -152,7 +152,7 @@ size_t attention_bwd_workspace_bytes(const AttnArgs& a);
 hipError_t attention_bwd(const AttnBwdArgs& b, hipStream_t st);
 
 // --- fused LN2 -> fc1 -> GELU -> fc2 -> residual (k_mlp.hip) --------------
-// proj_mlp (bf16, C = 96, hid = 4C): the output projection in front as well,
+// proj_mlp (bf16, C = 96 or 128, hid = 4C): the output projection in front as well,
 // y = z^ + MLP(LN2(z^)), z^ = x + o Wp^T + bp with o the attention output in
 // window-row space (gathered per token) and z^ kept in fp32 registers.
 bool proj_mlp_supported(vswin_dtype dt, int C, int hid);
