@@ -270,7 +270,8 @@ __device__ __forceinline__ void wait_stages(int stages) {
     if (stages > 0) wait_vm_lgkm0<D>();
     else wait_vm_lgkm0<0>();
   } else {
-    if (stages > 1) wait_vm_lgkm0<2 * D>();
+    if (stages > 2) wait_vm_lgkm0<3 * D>();
+    else if (stages > 1) wait_vm_lgkm0<2 * D>();
     else if (stages > 0) wait_vm_lgkm0<D>();
     else wait_vm_lgkm0<0>();
   }
