@@ -459,6 +459,23 @@ def test_patch_embed_grids(dtype, shape, offset):
     check(host64(y), oracle.patch_embed(video, w, b), dtype, f"patch embed {shape}")
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 2, 2, 192), (1, 3, 5, 7, 192), (2, 4, 16, 16, 384)])
+def test_patch_merge_small_and_ragged(shape):
+    """Patch merging through the staged-K GEMM (K = 4C = 768 or 1536) at token
+    counts far below, just above and at a multiple of the 128-row tile,
+    with odd H and W (zero-padded 2x2 groups); LN scale and shift spread
+    around 1 and 0, weights sized for outputs of order 1."""
+    say(f"patch merge {shape}")
+    rng = np.random.default_rng(61)
+    B, T, H, W, C = shape
+    bf = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+    x = bf(rng.standard_normal(shape))
+    m = {"ln_g": bf(1.0 + 0.2 * rng.standard_normal(4 * C)), "ln_b": bf(0.2 * rng.standard_normal(4 * C)),
+         "w": bf(0.025 * rng.standard_normal((2 * C, 4 * C)))}   # outputs of order 1 (the bar is absolute)
+    y = vs.vswin_patch_merge_fwd(dev(x, "bf16"), dev(m["ln_g"], "bf16"), dev(m["ln_b"], "bf16"), dev(m["w"], "bf16"))
+    check(host64(y), oracle.patch_merge(x, m), "bf16", f"merge {shape}")
+
+
 def test_workload5_backbone():
     """Workload 5 (Swin-T backbone, B=2 clips of 3x32x224x224).  Gate: every
     block, merge, the embedding and the final LN teacher-forced (each compared
