@@ -25,7 +25,8 @@ namespace {
 
 constexpr int kWgChunk = 256;     // tokens per staged chunk
 constexpr int kWgPitch = 264;     // LDS row pitch (bf16) of the token-contiguous operands
-constexpr int kMaxParts = 64;     // fp32 partials of one weight gradient at most
+constexpr int kMaxParts = 256;    // fp32 partials of one weight gradient at most
+constexpr int kWgBlocks = 256;    // workgroups a weight gradient aims for (one per CU: a chunk fills most of LDS)
 
 __device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float gelu_d(float x) {
@@ -444,10 +445,30 @@ hipError_t zero_f32(float* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-size_t wgrad_part_bytes(int64_t M, int NO, int KI) {
+namespace {
+// output tiles of the wgrad kernel the launcher picks for (NO, KI)
+int64_t wgrad_tiles(int NO, int KI) {
+  if (NO % 96 == 0 && KI % 96 == 0) return (int64_t)(NO / 96) * (KI / 96);
+  if (NO % 96 == 0 && KI % 128 == 0) return (int64_t)(NO / 96) * (KI / 128);
+  if (NO % 32 == 0 && KI % 128 == 0) return (int64_t)(NO / 32) * (KI / 128);
+  if (NO % 32 == 0 && KI % 96 == 0) return (int64_t)(NO / 32) * (KI / 96);
+  return (int64_t)(NO / 32) * (KI / 32);
+}
+// token partitions of one weight gradient: 64, or more where the output
+// has so few tiles that 64 partitions leave CUs idle (enough for kWgBlocks
+// workgroups, at most kMaxParts), and at most one per 256-token chunk
+int64_t wgrad_parts(int64_t M, int NO, int KI) {
   const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
-  const int64_t np = nchunks < kMaxParts ? nchunks : kMaxParts;
-  return (size_t)np * ((size_t)NO * KI + NO) * 4;
+  const int64_t tiles = wgrad_tiles(NO, KI);
+  int64_t np = (kWgBlocks + tiles - 1) / tiles;
+  if (np < 64) np = 64;
+  if (np > kMaxParts) np = kMaxParts;
+  return np < nchunks ? np : nchunks;
+}
+}  // namespace
+
+size_t wgrad_part_bytes(int64_t M, int NO, int KI) {
+  return (size_t)wgrad_parts(M, NO, KI) * ((size_t)NO * KI + NO) * 4;
 }
 
 hipError_t wgrad_partials(const void* A, const void* B, float* dW, float* db, float* part, int64_t M, int NO, int KI,
@@ -456,8 +477,7 @@ hipError_t wgrad_partials(const void* A, const void* B, float* dW, float* db, fl
   const int64_t nw = (int64_t)NO * KI;
   job = WgradJob{part, dW, db, 0, nw + (db ? NO : 0), nw, nw + NO};
   if (M <= 0) return hipSuccess;   // no tokens: the reduction writes zeros
-  const int64_t nchunks = (M + kWgChunk - 1) / kWgChunk;
-  const int np = (int)(nchunks < kMaxParts ? nchunks : kMaxParts);
+  const int np = (int)wgrad_parts(M, NO, KI);
   job.np = np;
   // n tile 96 where it divides NO, else 32; k tile 96 or 128 where it divides
   // KI, else 32
@@ -476,15 +496,29 @@ hipError_t wgrad_partials(const void* A, const void* B, float* dW, float* db, fl
   return launch(wgrad_kernel<32, 32>, 32, 32);
 }
 
-// every job's dW and db from its partial rows, one launch (blockIdx.y = job)
+// every job's dW and db from its partial rows, one launch (blockIdx.y = job):
+// a workgroup takes 64 consecutive outputs, its 4 waves sum every fourth
+// partial row (so a long partial list is read 4 rows at a time) and one
+// wave adds the 4 sums (fixed order: the result does not depend on timing)
 __global__ void __launch_bounds__(256) wgrad_reduce_kernel(const WgradJobs jobs) {
   const WgradJob& j = jobs.job[blockIdx.y];
-  for (int64_t i = blockIdx.x * 256 + (int64_t)threadIdx.x; i < j.n; i += (int64_t)gridDim.x * 256) {
+  __shared__ float red[4][64];
+  const int o = (int)threadIdx.x & 63, g = (int)threadIdx.x >> 6;
+  for (int64_t i0 = (int64_t)blockIdx.x * 64; i0 < j.n; i0 += (int64_t)gridDim.x * 64) {
+    const int64_t i = i0 + o;
     float s = 0.f;
-#pragma unroll 16
-    for (int p = 0; p < j.np; ++p) s += j.part[(int64_t)p * j.stride + i];
-    if (i < j.n1) j.dW[i] = s;
-    else j.db[i - j.n1] = s;
+    if (i < j.n) {
+#pragma unroll 8
+      for (int p = g; p < j.np; p += 4) s += j.part[(int64_t)p * j.stride + i];
+    }
+    __syncthreads();
+    red[g][o] = s;
+    __syncthreads();
+    if (g == 0 && i < j.n) {
+      const float t = (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]);
+      if (i < j.n1) j.dW[i] = t;
+      else j.db[i - j.n1] = t;
+    }
   }
 }
 
@@ -492,7 +526,7 @@ hipError_t wgrad_reduce(const WgradJobs& jobs, hipStream_t st) {
   if (jobs.n <= 0) return hipSuccess;
   int64_t nmax = 1;
   for (int i = 0; i < jobs.n; ++i) nmax = jobs.job[i].n > nmax ? jobs.job[i].n : nmax;
-  wgrad_reduce_kernel<<<dim3(grid_for(nmax, 256), (unsigned)jobs.n), dim3(256), 0, st>>>(jobs);
+  wgrad_reduce_kernel<<<dim3(grid_for(nmax, 64), (unsigned)jobs.n), dim3(256), 0, st>>>(jobs);
   return hipGetLastError();
 }
 
