@@ -20,6 +20,7 @@ constexpr int kGenMaxN = 2048;
 // ---------------------------------------------------------------------------
 template <typename T, int DMAX>
 __global__ void __launch_bounds__(256) attn_generic_kernel(const AttnArgs a) {
+  warm_args(a);
   __shared__ int kf[kGenMaxN];
   __shared__ int klab[kGenMaxN];
   const int item = blockIdx.x;

@@ -57,6 +57,7 @@ inline bool f32_layout(const AttnArgs& a, F32Lay& F) {
 
 template <int D>
 __global__ void __launch_bounds__(64 * kF32Waves) attn_f32_mfma_kernel(const AttnArgs a, const F32Lay F) {
+  warm_args(a, F);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* Ks = reinterpret_cast<float*>(smem + F.off_k);
   float* Vs = reinterpret_cast<float*>(smem + F.off_v);

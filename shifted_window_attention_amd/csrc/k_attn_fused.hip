@@ -467,6 +467,7 @@ __device__ __forceinline__ void fused_group(int cnt, const FusedArgs& f, const A
 
 template <int C>
 __global__ void __launch_bounds__(kFThreads) wattn_fused_kernel(const FusedArgs f, const A5 L, const FLay F) {
+  warm_args_grid(f, L, F);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const AttnArgs& a = f.a;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);

@@ -112,6 +112,7 @@ __device__ __forceinline__ void zero_pads(const A5& L, unsigned char* smem) {
 // call and copied to LDS by each workgroup.
 __global__ void __launch_bounds__(256) attn_table_kernel(const bf16_t* __restrict__ T, f32x4_t* __restrict__ out,
                                                          const A5 L) {
+  warm_args(T, out, L);
   const int x = blockIdx.x * 256 + (int)threadIdx.x;
   const int h = blockIdx.y;
   if (x < L.TS4) out[(size_t)h * L.TS4 + x] = tab_entry(T, L.tg, h, x);
@@ -288,6 +289,7 @@ __device__ __forceinline__ TileRun tile_run(int wv, int w, int t0, int t1, int Q
 
 template <class CF>
 __global__ void __launch_bounds__(CF::kThreads) attn_mfma_kernel(const AttnArgs a, const A5 L) {
+  warm_args_grid(a, L);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   // XCD-aware order: consecutive runs (same head, neighbouring windows) go
@@ -562,6 +564,7 @@ __device__ __forceinline__ float pair_p(bool in_range, bool same, int m100, floa
 }  // namespace
 
 __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const AttnBwdArgs b, const BwdL BL) {
+  warm_args(b, BL);
   const A5& L = BL.L;
   __shared__ __attribute__((aligned(16))) bf16_t tile[64 * 40];
   // workgroup: one (item, tensor, 64-row block), so that the blocks' loads are
@@ -646,6 +649,7 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(const AttnBwdArgs b,
 
 template <class CF, bool GF>
 __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, const BwdL BL) {
+  warm_args(b, BL);
   constexpr int ES = CF::kTabEs;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const A5& L = BL.L;
@@ -799,6 +803,7 @@ __global__ void __launch_bounds__(512) attn_bwd_kv_kernel(const AttnBwdArgs b, c
 
 template <class CF, bool GF>
 __global__ void __launch_bounds__(512) attn_bwd_q_kernel(const AttnBwdArgs b, const BwdL BL) {
+  warm_args(b, BL);
   constexpr int ES = CF::kTabEs;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const A5& L = BL.L;
@@ -940,6 +945,7 @@ __global__ void __launch_bounds__(256) attn_bwd_grp_sum_kernel(const float* __re
 __global__ void __launch_bounds__(256) attn_bwd_dtab_gather_kernel(const float* __restrict__ gsum,
                                                                     float* __restrict__ out, const BwdL BL,
                                                                     WinGeo g) {
+  warm_args(gsum, out, BL, g);
   const A5& L = BL.L;
   const int h = blockIdx.y;
   const int nd = L.TD * L.Rp;

@@ -72,6 +72,7 @@ __global__ void __launch_bounds__(256) gelu_kernel(const bf16_t* __restrict__ a,
 // window row m of `out` (bf16) = token row src(m) of `in` (fp32), 0 for pads
 __global__ void __launch_bounds__(256) gather_f32_bf16_kernel(const float* __restrict__ in, bf16_t* __restrict__ out,
                                                                int64_t slots, int C, const WinGeo geo) {
+  warm_args_grid(in, out, slots, C, geo);
   const int per = C / 8;
   for (int64_t x = blockIdx.x * 256 + (int64_t)threadIdx.x; x < slots * per; x += (int64_t)gridDim.x * 256) {
     const int64_t m = x / per;
@@ -100,6 +101,7 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
                                                      const bf16_t* __restrict__ dy, const TR* __restrict__ res,
                                                      TO* __restrict__ out, float* __restrict__ part, int64_t rows,
                                                      int C, float eps) {
+  warm_args_grid(x, g, dy, res, out, part, rows, C, eps);
   const int l16 = threadIdx.x % LPR;
   const int64_t grp = blockIdx.x * (256 / LPR) + threadIdx.x / LPR, ng = (int64_t)gridDim.x * (256 / LPR);
   float dgs[J], dbs[J], gv[J];
@@ -225,6 +227,7 @@ template <int BN, int BK>
 __global__ void __launch_bounds__(256) wgrad_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
                                                     float* __restrict__ part, int64_t M, int NO, int KI,
                                                     int nparts) {
+  warm_args(A, B, part, M, NO, KI, nparts);
   extern __shared__ __attribute__((aligned(16))) unsigned char wg_lds[];
   bf16_t* At = reinterpret_cast<bf16_t*>(wg_lds);
   bf16_t* Bt = At + BN * kWgPitch;

@@ -102,6 +102,7 @@ constexpr int kBM = 128, kBK = 32, kLDK = 40;
 template <int BN, class E>
 __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
                                                         int64_t M, int N, int K, E epi) {
+  warm_args(A, W, M, N, K, epi);
   constexpr int WN = BN / 2;
   constexpr int NT = WN / 16;
   constexpr int MT = 4;
@@ -280,6 +281,7 @@ __device__ __forceinline__ void wait_stages(int stages) {
 template <int BN, int S, class E>
 __global__ void __launch_bounds__(256) gemm_bf16_dma_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
                                                             int64_t M, int N, int K, E epi, int tq, int tr) {
+  warm_args(A, W, M, N, K, epi, tq, tr);
   using T = DmaTile<BN, S>;
   constexpr int WN = BN / 2;
   constexpr int NT = WN / 16;
@@ -434,6 +436,7 @@ struct APrologue {
 template <int BN, int KK, class E>
 __global__ void __launch_bounds__(256) gemm_bf16_fullk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W,
                                                               int64_t M, int N, E epi, APrologue pro) {
+  warm_args(A, W, M, N, epi, pro);
   constexpr int WN = BN / 2;
   constexpr int NT = WN / 16;
   constexpr int MT = 4;
@@ -594,6 +597,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_fullk_kernel(const bf16_t* __re
 template <class E>
 __global__ void __launch_bounds__(256) gemm_f32_mfma_kernel(const float* __restrict__ A, const float* __restrict__ W,
                                                             int64_t M, int N, int K, E epi) {
+  warm_args(A, W, M, N, K, epi);
   __shared__ float As[64 * 17];
   __shared__ float Ws[64 * 17];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -137,6 +137,7 @@ __global__ void __launch_bounds__(256) ln_rows_v8_kernel(const TIN* __restrict__
                                                          const TOUT* __restrict__ b, TOUT* __restrict__ y,
                                                          int64_t rows, int C, float eps, int gather,
                                                          WinGeo geo, int apply_ln) {
+  warm_args(x, g, b, y, rows, C, eps, gather, geo, apply_ln);
   const int li = threadIdx.x % LPR;
   const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   if (row >= rows) return;
@@ -329,6 +330,7 @@ __global__ void __launch_bounds__(256) reverse_kernel(const T* __restrict__ win,
 template <typename T, int LPR, int KC>
 __global__ void __launch_bounds__(256) reverse_v8_kernel(const T* __restrict__ win, const T* __restrict__ res,
                                                          T* __restrict__ y, int64_t slots, int C, WinGeo geo) {
+  warm_args(win, res, y, slots, C, geo);
   const int li = threadIdx.x % LPR;
   const int64_t s = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   if (s >= slots) return;

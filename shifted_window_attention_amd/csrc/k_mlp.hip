@@ -33,6 +33,7 @@ __global__ void __launch_bounds__(256, 2) mlp_fused_kernel(const float* __restri
                                                         const bf16_t* __restrict__ b1, const bf16_t* __restrict__ W2,
                                                         const bf16_t* __restrict__ bo, bf16_t* __restrict__ y,
                                                         int64_t L, float eps, const MlpProj pj) {
+  warm_args(zh, g2, b2ln, W1, b1, W2, bo, y, L, eps, pj);
   constexpr int BM = 64, HC = 64, HID = 4 * C, NCH = HID / HC;
   constexpr int LDA = C + 8, LDH = HC + 8;
   constexpr int NT2 = C / 32;            // GEMM2 feature tiles of 16 per wave (C/2 features)
@@ -425,6 +426,7 @@ __device__ __forceinline__ int pair_row_inv(int r) {
 
 template <bool PROJ>
 __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) {
+  warm_args_grid(a);
   constexpr int C = kMlpC, HID = kMlpHid;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* W1s = lds;                 // HID rows x 192 B

@@ -156,6 +156,7 @@ constexpr int kQkvThreads = 64 * kQkvWaves;
 
 template <int C>
 __global__ void __launch_bounds__(kQkvThreads, 1) qkv_wave_kernel(QkvParams pr) {
+  warm_args_grid(pr);
   using L = QkvLds<C>;
   constexpr int KS = C / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -353,6 +354,7 @@ __device__ __forceinline__ void proj_load(ProjTile<C, RES>& pt, const ProjParams
 // flight at once rather than prefetched a tile ahead
 template <int C, bool RES>
 __global__ void __launch_bounds__(kWpThreads, 4) out_proj_kernel(ProjParams pr) {
+  warm_args_grid(pr);
   using L = ProjLds<C>;
   constexpr int KS = C / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];

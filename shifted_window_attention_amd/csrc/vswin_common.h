@@ -210,6 +210,95 @@ __device__ __forceinline__ uint16_t f2bf(float a) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// ---------------------------------------------------------------------------
+// kernel arguments
+// ---------------------------------------------------------------------------
+// Byte size of a kernel's explicit arguments T... in its argument segment
+// (each at its own alignment, the end rounded to 8); the hidden arguments
+// (the grid's block counts first) follow.
+template <class... T>
+constexpr int kArgBytes() {
+  int off = 0;
+  ((off = (off + (int)alignof(T) - 1) / (int)alignof(T) * (int)alignof(T) + (int)sizeof(T)), ...);
+  return (off + 7) / 8 * 8;
+}
+
+// Every 64-byte line of the first BYTES bytes of the argument segment
+// requested from the scalar cache at once, before any is used: at kernel start
+// each line is a miss to memory, and the compiler otherwise issues the loads
+// of a large argument block a few at a time as the code needs them, one
+// round trip after another.  The loads and their wait are one asm statement,
+// so the destination register is never reused while a load is in flight.
+template <int BYTES>
+__device__ __forceinline__ void kernarg_warm() {
+  constexpr int L = (BYTES + 63) / 64;
+  static_assert(L >= 1 && L <= 16, "argument block of 1 to 16 lines");
+  const auto p = __builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t d;
+  if constexpr (L == 1)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 2)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 3)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 4)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 5)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 6)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 7)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 8)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 9)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 10)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t""s_load_dword %0, %1, 0x240\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 11)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t""s_load_dword %0, %1, 0x240\n\t""s_load_dword %0, %1, 0x280\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 12)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t""s_load_dword %0, %1, 0x240\n\t""s_load_dword %0, %1, 0x280\n\t""s_load_dword %0, %1, 0x2c0\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 13)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t""s_load_dword %0, %1, 0x240\n\t""s_load_dword %0, %1, 0x280\n\t""s_load_dword %0, %1, 0x2c0\n\t""s_load_dword %0, %1, 0x300\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 14)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t""s_load_dword %0, %1, 0x240\n\t""s_load_dword %0, %1, 0x280\n\t""s_load_dword %0, %1, 0x2c0\n\t""s_load_dword %0, %1, 0x300\n\t""s_load_dword %0, %1, 0x340\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 15)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t""s_load_dword %0, %1, 0x240\n\t""s_load_dword %0, %1, 0x280\n\t""s_load_dword %0, %1, 0x2c0\n\t""s_load_dword %0, %1, 0x300\n\t""s_load_dword %0, %1, 0x340\n\t""s_load_dword %0, %1, 0x380\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  if constexpr (L == 16)
+    asm volatile("s_load_dword %0, %1, 0x0\n\t""s_load_dword %0, %1, 0x40\n\t""s_load_dword %0, %1, 0x80\n\t""s_load_dword %0, %1, 0xc0\n\t""s_load_dword %0, %1, 0x100\n\t""s_load_dword %0, %1, 0x140\n\t""s_load_dword %0, %1, 0x180\n\t""s_load_dword %0, %1, 0x1c0\n\t""s_load_dword %0, %1, 0x200\n\t""s_load_dword %0, %1, 0x240\n\t""s_load_dword %0, %1, 0x280\n\t""s_load_dword %0, %1, 0x2c0\n\t""s_load_dword %0, %1, 0x300\n\t""s_load_dword %0, %1, 0x340\n\t""s_load_dword %0, %1, 0x380\n\t""s_load_dword %0, %1, 0x3c0\n\t"
+                 "s_waitcnt lgkmcnt(0)" : "=&s"(d) : "s"(p) : "memory");
+  (void)d;
+}
+
+// kernarg_warm over a kernel's explicit arguments (pass them all, in order).
+// The segment ends with them unless the kernel reads a hidden argument (its
+// grid or workgroup size): warm_args_grid also takes the line of the first
+// hidden ones, which then follow.
+template <class... T>
+__device__ __forceinline__ void warm_args(const T&...) {
+  kernarg_warm<kArgBytes<T...>()>();
+}
+template <class... T>
+__device__ __forceinline__ void warm_args_grid(const T&...) {
+  kernarg_warm<kArgBytes<T...>() + 8>();
+}
+
 // entry x of head h's prepared table, from the (rows, heads) bf16 table T:
 // offsets outside the table give 0
 __device__ __forceinline__ f32x4_t t4_entry(const bf16_t* __restrict__ T, const Tab4Geo& tg, int h, int x) {
