@@ -57,28 +57,29 @@ __device__ __forceinline__ int wswz(int r) {
   return C == 128 ? (r & 15) : ((r >> 2) & 3);
 }
 
-// Weight matrix (F x C, row-major) into LDS, row f at row perm(f), chunks
-// swizzled; every load of the thread is issued before its LDS stores.
-template <int C, int F, int THREADS = kWpThreads, class Perm>
-__device__ __forceinline__ void stage_weights(const bf16_t* __restrict__ W, unsigned char* Ws, Perm perm) {
+__device__ __forceinline__ int pair_row_inv(int r) {
+  return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Weight matrix (F x C, row-major) into LDS by direct global-to-LDS loads
+// (no registers): LDS row r holds weight row inv(r), its 16-byte chunks
+// swizzled; a wave instruction fills 1 KB of consecutive LDS chunks (lane i:
+// chunk 64 b + i), each lane loading the global chunk that belongs there.
+// The caller waits for vmcnt and a barrier.
+template <int C, int F, int THREADS = kWpThreads, class Inv>
+__device__ __forceinline__ void stage_weights(const bf16_t* __restrict__ W, unsigned char* Ws, Inv inv) {
   constexpr int KC = C / 8;
-  constexpr int TOTAL = F * KC;
-  constexpr int PER = (TOTAL + THREADS - 1) / THREADS;
-  const int tid = threadIdx.x;
-  u32x4_t v[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = tid + i * THREADS;
-    if (c < TOTAL) v[i] = *reinterpret_cast<const u32x4_t*>(W + (int64_t)c * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = tid + i * THREADS;
-    if (c < TOTAL) {
-      const int f = c / KC, q = c - f * KC;
-      const int r = perm(f);
-      *reinterpret_cast<u32x4_t*>(Ws + r * (C * 2) + ((q ^ wswz<C>(r)) << 4)) = v[i];
-    }
+  constexpr int NB = F * KC / 64;
+  static_assert(NB * 64 == F * KC, "weight staging shape");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  for (int b = wave; b < NB; b += THREADS / 64) {
+    const int c = 64 * b + lane;
+    const int r = c / KC, qp = c - r * KC;
+    __builtin_amdgcn_global_load_lds(W + (int64_t)inv(r) * C + ((qp ^ wswz<C>(r)) << 3),
+                                     (lds_ptr_t)(Ws + 1024 * b), 16, 0, 0);
   }
 }
 
@@ -190,7 +191,7 @@ __global__ void __launch_bounds__(kQkvThreads, 1) qkv_wave_kernel(QkvParams pr) 
   RowTile<C> cur;
   if (t < ntiles) gather_rows<C>(cur, pr, t);
   // q and k rows (and v rows unless transposed) in pair order
-  stage_weights<C, 3 * C, kQkvThreads>(pr.w, Ws, [vt](int f) { return (f < 2 * C || !vt) ? pair_row(f) : f; });
+  stage_weights<C, 3 * C, kQkvThreads>(pr.w, Ws, [vt](int r) { return (r < 2 * C || !vt) ? pair_row_inv(r) : r; });
   for (int c = tid; c < 5 * C / 8; c += kQkvThreads) {
     const bf16_t* src = c < 3 * C / 8 ? (pr.bias ? pr.bias + c * 8 : nullptr)
                                       : (!pr.ln ? nullptr
@@ -198,6 +199,7 @@ __global__ void __launch_bounds__(kQkvThreads, 1) qkv_wave_kernel(QkvParams pr) 
                                                                  : pr.ln_b + (c - 4 * C / 8) * 8));
     *reinterpret_cast<u32x4_t*>(bias_s + c * 8) = src ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's weight blocks are in LDS
   __syncthreads();
 
   const int N = pr.geo.N, d = pr.d;
@@ -369,10 +371,11 @@ __global__ void __launch_bounds__(kWpThreads, 4) out_proj_kernel(ProjParams pr) 
 
   ProjTile<C, RES> cur;
   if (t < ntiles) proj_load<C, RES>(cur, pr, t);
-  stage_weights<C, C>(pr.w, Ws, [](int f) { return pair_row(f); });
+  stage_weights<C, C>(pr.w, Ws, [](int r) { return pair_row_inv(r); });
   for (int c = tid; c < C / 8; c += kWpThreads)
     *reinterpret_cast<u32x4_t*>(bias_s + c * 8) =
         pr.bias ? *reinterpret_cast<const u32x4_t*>(pr.bias + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's weight blocks are in LDS
   __syncthreads();
   if (t >= ntiles) return;
 
