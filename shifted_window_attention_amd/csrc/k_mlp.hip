@@ -358,7 +358,7 @@ constexpr int kMlpThreads = 64 * kMlpWaves;
 constexpr int kMlpC = 96, kMlpHid = 4 * kMlpC;
 constexpr size_t kMlpW1 = (size_t)kMlpHid * kMlpC * 2;
 constexpr size_t kMlpVec = kMlpHid * 4 + kMlpC * 4 + 3 * kMlpC * 2;     // b1, proj bias (fp32), LN2 gamma / beta, fc2 bias
-constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + (kPhiN + 2) * 8;
+constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + kGeluEntriesU * 8;
 
 struct ZTile {
   float z[3][8];     // columns 32j + 8g .. + 7 of token fr
@@ -431,10 +431,10 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* W1s = lds;                 // HID rows x 192 B
   unsigned char* W2s = lds + kMlpW1;        // C rows x 768 B
-  float* b1s = reinterpret_cast<float*>(lds + 2 * kMlpW1);   // fc1 bias, fp32
+  float* b1s = reinterpret_cast<float*>(lds + 2 * kMlpW1);   // 64 x fc1 bias + kGeluU0, fp32
   float* bps = b1s + HID;                                    // projection bias, fp32
   bf16_t* vecs = reinterpret_cast<bf16_t*>(bps + C);         // LN2 gamma, beta, fc2 bias (C each)
-  float2* phi = reinterpret_cast<float2*>(lds + 2 * kMlpW1 + kMlpVec);   // GELU bins: (intercept, slope)
+  float2* phi = reinterpret_cast<float2*>(lds + 2 * kMlpW1 + kMlpVec);   // GELU bins in u (gelu_table_build_u)
   const bf16_t* __restrict__ W1 = a.W1;
   const bf16_t* __restrict__ W2 = a.W2;
   const bf16_t* __restrict__ b1 = a.b1;
@@ -496,10 +496,12 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
                                        (lds_ptr_t)(W2s + 1024 * b), 16, 0, 0);
     }
   }
-  for (int c = tid; c < HID; c += nthr) b1s[c] = b1 ? bf2f(b1[c]) : 0.f;
+  // fc1 yields u = 64 x + kGeluU0 for GELU's table: its operand (LN2's output)
+  // is scaled by 64 and its accumulator starts here
+  for (int c = tid; c < HID; c += nthr) b1s[c] = 64.0f * (b1 ? bf2f(b1[c]) : 0.f) + kGeluU0;
   if constexpr (PROJ)
     for (int c = tid; c < C; c += nthr) bps[c] = a.bp ? bf2f(a.bp[c]) : 0.f;
-  gelu_table_build(phi, tid, nthr);
+  gelu_table_build_u(phi, tid, nthr);
   for (int c = tid; c < 3 * (C / 8); c += nthr) {
     const int which = c / (C / 8), q = c - which * (C / 8);
     const bf16_t* src = which == 0 ? a.g2 : (which == 1 ? a.b2ln : a.bo);
@@ -562,14 +564,15 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
         }
       q2 += __shfl_xor(q2, 16);
       q2 += __shfl_xor(q2, 32);
-      const float rstd = 1.0f / sqrtf(q2 * (1.0f / C) + eps);
+      // 64 LN2(z^): the power-of-two scale leaves every rounding unchanged
+      const float rstd = 64.0f / sqrtf(q2 * (1.0f / C) + eps);
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         float gg[8], bb[8], v[8];
         unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 32 * j + 8 * g), gg);
         unpack8(*reinterpret_cast<const u32x4_t*>(vecs + C + 32 * j + 8 * g), bb);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (z[u].z[j][e] - mean) * rstd * gg[e] + bb[e];
+        for (int e = 0; e < 8; ++e) v[e] = (z[u].z[j][e] - mean) * rstd * gg[e] + 64.0f * bb[e];
         af[u][j] = __builtin_bit_cast(bf16x8_t, pack8(v));
       }
     }
@@ -623,8 +626,8 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
         float h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float x = i < 4 ? a1[u][0][i] : a1[u][1][i - 4];
-          h[i] = gelu_tab(phi, x);
+          const float uu = i < 4 ? a1[u][0][i] : a1[u][1][i - 4];
+          h[i] = gelu_tab_u(phi, uu);
         }
         const bf16x8_t hf = __builtin_bit_cast(bf16x8_t, pack8(h));
 #pragma unroll
