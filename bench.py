@@ -7,10 +7,10 @@ clip with 2x4x4 patches, 3 heads of 32, window (8,7,7), shift (4,3,3), MLP
 ratio 4, seeded synthetic inputs and weights (no dataset).  Inputs, weights,
 outputs and workspace are resident in HBM before the timed region.
 
-The K timed steps are captured into one HIP graph, replayed once between
-synchronisations (every kernel of every pair runs; the graph only removes
-the Python binding's per-call host work, reported separately as the eager
-rate).  Prints one JSON line: tokens/s through a block (tokens x blocks per
+The K timed steps are captured into one HIP graph and replayed once between
+two events, right behind at least W untimed steps replayed from the same
+graph (every kernel of every pair runs; the graph only removes the Python
+binding's per-call host work, reported separately as the eager rate).  Prints one JSON line: tokens/s through a block (tokens x blocks per
 second), TFLOP/s and the fraction of the bf16 MFMA peak, the roofline of the
 dominant kernel (the window attention, launched alone and timed with HIP
 events on its stream), the one-kernel LN1 + gather + qkv + attention
@@ -577,7 +577,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before the timed ones (the first 10 eager, all of them as graph replays)")
     ap.add_argument("--kernel-launches", type=int, default=50,
                     help="attention-kernel launches timed for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -636,7 +637,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
 
-    for _ in range(args.warmup):
+    for _ in range(min(args.warmup, 10)):
         step(stream)
     torch.cuda.synchronize()
     ref_y = y2.clone()
@@ -652,15 +653,23 @@ def main():
     torch.cuda.synchronize()
     if not torch.equal(y2, ref_y):
         raise RuntimeError("the graph replay differs from the eager pair")
+    # warm-up: at least W steps as untimed replays of the same graph, queued
+    # right before the timed one (no host synchronisation in between), so that
+    # the timed replay starts on a GPU already in its steady state under load
+    # (the first replays after a pause run up to 10 % slower)
+    warm_replays = max(1, -(-args.warmup // args.steps))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(warm_replays):
+        graph.replay()
     e0.record(stream)
     graph.replay()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    # host clock over the warm-up and timed replays together
+    wall = (time.perf_counter() - t0) * 1e3 / ((warm_replays + 1) * args.steps)
     del graph
     eager_ms, eager_wall = timed(lambda: step(stream), stream)
     # per-step distribution (one pair per graph replay, events around each),
@@ -701,6 +710,8 @@ def main():
     g10.replay()
     torch.cuda.synchronize()
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(max(1, -(-args.warmup // 10))):   # the same warm-up as the timed pairs
+        g10.replay()
     f0.record(stream)
     g10.replay()
     f1.record(stream)
