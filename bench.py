@@ -689,13 +689,22 @@ def main():
     tflops = step_flops / (ms * 1e-3) / 1e12
 
     def time_launches(fn, n):
-        for _ in range(5):
-            fn()
+        """Average time of one launch of fn(stream): n launches captured into
+        one graph, replayed once between two events right behind at least W
+        untimed launches (replays of the same graph), like the timed pairs."""
+        fn(stream)
+        torch.cuda.synchronize()
+        gl = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gl):
+            for _ in range(n):
+                fn(torch.cuda.current_stream())
+        gl.replay()
         torch.cuda.synchronize()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(max(1, -(-args.warmup // n))):
+            gl.replay()
         a0.record(stream)
-        for _ in range(n):
-            fn()
+        gl.replay()
         a1.record(stream)
         torch.cuda.synchronize()
         return a0.elapsed_time(a1) * 1e3 / n
@@ -721,8 +730,8 @@ def main():
     Lp = plans[0]["num_windows"] * plans[0]["tokens_per_window"]
     o_rows = torch.empty((Lp, s.C), dtype=torch.bfloat16, device="cuda")
     msa_ws = torch.empty(max(p["msa_workspace_bytes"] for p in plans), dtype=torch.uint8, device="cuda")
-    fused_us = [time_launches(lambda: vs.vswin_qkv_attention_fwd(x, w[i], s.heads, s.window, shifts[i],
-                                                                  out=o_rows, workspace=msa_ws, stream=stream),
+    fused_us = [time_launches(lambda st: vs.vswin_qkv_attention_fwd(x, w[i], s.heads, s.window, shifts[i],
+                                                                     out=o_rows, workspace=msa_ws, stream=st),
                               args.kernel_launches) for i in range(len(shifts))]
     os.environ.pop("VSWIN_FUSED")
     fused_flops = flops[0]["qkv"] + flops[0]["attn"]
@@ -750,8 +759,8 @@ def main():
     kern_us = []
     for i, dsc in enumerate(descs):
         vs.vswin_attention_fwd(dsc, *qkv, w[i]["rpb_table"], out=o, workspace=attn_ws, stream=stream)
-        kern_us.append(time_launches(lambda: vs.vswin_attention_fwd(ready[i], *qkv, w[i]["rpb_table"], out=o,
-                                                                    workspace=attn_ws, stream=stream),
+        kern_us.append(time_launches(lambda st: vs.vswin_attention_fwd(ready[i], *qkv, w[i]["rpb_table"], out=o,
+                                                                       workspace=attn_ws, stream=st),
                                      args.kernel_launches))
     attn_flops = flops[0]["attn"]
     attn_us = sum(kern_us) / len(kern_us)
