@@ -221,27 +221,31 @@ __device__ __forceinline__ void attn_step(int p, const unsigned char* __restrict
 #pragma unroll
     for (int v = 0; v < NU; ++v) {
       const int u = U0 + v;
-      int adA = st.qaddr[u] + gk.x, adB = st.qaddr[u] + gk.y;
+      // pointers selected rather than offsets, so that the LDS base is not
+      // added again after each select
+      const unsigned char* pA = tabb + (st.qaddr[u] + gk.x);
+      const unsigned char* pB = tabb + (st.qaddr[u] + gk.y);
+      const unsigned char* pz = tabb + zone;
       if (SEL && CF::kM100) {
         constexpr float kM = -100.0f * kLog2e;
         mA[v] = (lk.x == st.qlab[u] || lk.x == kDummyLab) ? 0.f : kM;
         mB[v] = (lk.y == st.qlab[u] || lk.y == kDummyLab) ? 0.f : kM;
-        adA = lk.x == kDummyLab ? zone : adA;
-        adB = lk.y == kDummyLab ? zone : adB;
+        pA = lk.x == kDummyLab ? pz : pA;
+        pB = lk.y == kDummyLab ? pz : pB;
       } else if (SEL && !CF::kPerKey) {
-        adA = (lk.x == st.qlab[u]) ? adA : zone;
-        adB = (lk.y == st.qlab[u]) ? adB : zone;
+        pA = (lk.x == st.qlab[u]) ? pA : pz;
+        pB = (lk.y == st.qlab[u]) ? pB : pz;
       }
       if constexpr (BIG) {
-        const float* sa = reinterpret_cast<const float*>(tabb + adA);
+        const float* sa = reinterpret_cast<const float*>(pA);
         tA[v] = f32x4_t{sa[0], sa[kBigRp], sa[2 * kBigRp], sa[3 * kBigRp]};
         if (!HALF) {
-          const float* sb = reinterpret_cast<const float*>(tabb + adB);
+          const float* sb = reinterpret_cast<const float*>(pB);
           tB[v] = f32x4_t{sb[0], sb[kBigRp], sb[2 * kBigRp], sb[3 * kBigRp]};
         }
       } else {
-        tA[v] = *reinterpret_cast<const f32x4_t*>(tabb + adA);
-        if (!HALF) tB[v] = *reinterpret_cast<const f32x4_t*>(tabb + adB);
+        tA[v] = *reinterpret_cast<const f32x4_t*>(pA);
+        if (!HALF) tB[v] = *reinterpret_cast<const f32x4_t*>(pB);
       }
     }
     // every LDS read of the part is in flight before the first MFMA waits on one

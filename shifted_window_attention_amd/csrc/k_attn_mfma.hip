@@ -190,6 +190,8 @@ __device__ __forceinline__ void attn_tiles(const AttnArgs& a, const A5& L, const
   bf16x8_t ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  // held in VGPRs across the steps (not rebuilt from scalars in every step)
+  asm volatile("" : "+v"(ones));
   const int2* kp2 = reinterpret_cast<const int2*>(kp);
   auto clear = [&]() {
 #pragma unroll
