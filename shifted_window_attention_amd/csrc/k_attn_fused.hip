@@ -136,17 +136,6 @@ __device__ __forceinline__ void load_head_w(HeadW<C / 32>& w, const FusedArgs& f
   }
 }
 
-// Sum over the 4 lanes of a token row (lanes l, l^16, l^32, l^48) by lane
-// swaps in the VALU (v_permlane16_swap / v_permlane32_swap: with both
-// operands equal to v, the two results add up to v[l] + v[l ^ 16], resp.
-// v[l ^ 32]); the same sums as two xor-shuffle additions.
-__device__ __forceinline__ float row4_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // LayerNorm of 16 window rows held as raw bf16 chunks (lane: channels
 // 32j + 8g .. + 7 of row fr), in registers (4 lanes per row); rows that are
 // not live (pad slots, slots past N) become zero rows (the grid is padded

@@ -357,7 +357,7 @@ constexpr int kMlpWaves = 8;                 // at most, per workgroup (the laun
 constexpr int kMlpThreads = 64 * kMlpWaves;
 constexpr int kMlpC = 96, kMlpHid = 4 * kMlpC;
 constexpr size_t kMlpW1 = (size_t)kMlpHid * kMlpC * 2;
-constexpr size_t kMlpVec = kMlpHid * 4 + kMlpC * 4 + 3 * kMlpC * 2;     // b1, proj bias (fp32), LN2 gamma / beta, fc2 bias
+constexpr size_t kMlpVec = kMlpHid * 4 + 3 * kMlpC * 2;     // b1 (fp32), LN2 gamma / beta, fc2 bias
 constexpr size_t kMlpLds = 2 * kMlpW1 + kMlpVec + kGeluEntriesU * 8;
 
 struct ZTile {
@@ -432,8 +432,7 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   unsigned char* W1s = lds;                 // HID rows x 192 B
   unsigned char* W2s = lds + kMlpW1;        // C rows x 768 B
   float* b1s = reinterpret_cast<float*>(lds + 2 * kMlpW1);   // 64 x fc1 bias + kGeluU0, fp32
-  float* bps = b1s + HID;                                    // projection bias, fp32
-  bf16_t* vecs = reinterpret_cast<bf16_t*>(bps + C);         // LN2 gamma, beta, fc2 bias (C each)
+  bf16_t* vecs = reinterpret_cast<bf16_t*>(b1s + HID);       // LN2 gamma, beta, fc2 bias (C each)
   float2* phi = reinterpret_cast<float2*>(lds + 2 * kMlpW1 + kMlpVec);   // GELU bins in u (gelu_table_build_u)
   const bf16_t* __restrict__ W1 = a.W1;
   const bf16_t* __restrict__ W2 = a.W2;
@@ -464,8 +463,12 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   // pair-order rows 16 nt .. + 15), read from L2 with the first pair's inputs
   // and held until that pair's projection is done
   bf16x8_t wpf[PROJ ? 6 : 1][3];
+  u32x4_t bpr[3];   // the projection bias, columns 32j + 8g .. + 7 (bf16)
   auto load_wp = [&]() {
     if constexpr (PROJ) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        bpr[j] = a.bp ? *reinterpret_cast<const u32x4_t*>(a.bp + 32 * j + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int nt = 0; nt < 6; ++nt)
 #pragma unroll
@@ -478,10 +481,27 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
     load_inputs(t2);
     load_wp();
   }
+  // the small vectors and the GELU table into LDS first: their loads (and the
+  // first pair's inputs, issued before them) have landed once these stores
+  // are done, so nothing that the first pair's projection and LN2 statistics
+  // read below is waited for behind the weight transfer
+  for (int c = tid; c < HID; c += nthr) b1s[c] = 64.0f * (b1 ? bf2f(b1[c]) : 0.f) + kGeluU0;
+  gelu_table_build_u(phi, tid, nthr);
+  for (int c = tid; c < 3 * (C / 8); c += nthr) {
+    const int which = c / (C / 8), q = c - which * (C / 8);
+    const bf16_t* src = which == 0 ? a.g2 : (which == 1 ? a.b2ln : a.bo);
+    *reinterpret_cast<u32x4_t*>(vecs + which * C + q * 8) =
+        src ? *reinterpret_cast<const u32x4_t*>(src + q * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // every earlier load has landed (the builtin tells the compiler so; an asm
+  // wait would not, and it would wait for the weight transfer before the
+  // projection below)
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0); expcnt, lgkmcnt left alone
   // W1 and W2 go straight from global memory into their swizzled LDS layouts
   // (global_load_lds: a wave instruction fills 1 KB of consecutive LDS chunks
-  // from per-lane addresses), still in flight while the first pair's
-  // projection and LN2 run; LDS chunk (r, qp) holds global row
+  // from per-lane addresses), in flight while the first pair's projection and
+  // LN2 statistics run (registers and lane swaps only: no LDS access, which
+  // would wait for the transfer); LDS chunk (r, qp) holds global row
   // pair_row_inv(r), chunk qp ^ swizzle(r)
   {
     constexpr int NB = HID * (C / 8) / 64;   // 1 KB blocks per matrix
@@ -496,24 +516,14 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
                                        (lds_ptr_t)(W2s + 1024 * b), 16, 0, 0);
     }
   }
-  // fc1 yields u = 64 x + kGeluU0 for GELU's table: its operand (LN2's output)
-  // is scaled by 64 and its accumulator starts here
-  for (int c = tid; c < HID; c += nthr) b1s[c] = 64.0f * (b1 ? bf2f(b1[c]) : 0.f) + kGeluU0;
-  if constexpr (PROJ)
-    for (int c = tid; c < C; c += nthr) bps[c] = a.bp ? bf2f(a.bp[c]) : 0.f;
-  gelu_table_build_u(phi, tid, nthr);
-  for (int c = tid; c < 3 * (C / 8); c += nthr) {
-    const int which = c / (C / 8), q = c - which * (C / 8);
-    const bf16_t* src = which == 0 ? a.g2 : (which == 1 ? a.b2ln : a.bo);
-    *reinterpret_cast<u32x4_t*>(vecs + which * C + q * 8) =
-        src ? *reinterpret_cast<const u32x4_t*>(src + q * 8) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  __syncthreads();
 
   const int swz1 = (fr >> 2) & 3;   // W1 rows 32c + 16p + fr: ((row >> 2) & 3) = (fr >> 2) & 3
-  // front of a pair: (PROJ) z^ = x + o Wp^T + bp into z, then LN2 into af
+  // front of a pair, in two parts.  front1: (PROJ) z^ = x + o Wp^T + bp into
+  // z, and LN2's mean and 64 / std per token (registers and lane swaps only);
+  // front2: 64 LN2(z^) into af with gamma and beta from LDS.
   bf16x8_t af[2][3];
-  auto front = [&]() {
+  float mean[2], rstd[2];
+  auto front1 = [&]() {
     if constexpr (PROJ) {
       // 6 output tiles (pair order) of 16 tokens for each tile of the pair, the
       // accumulators starting at the bias
@@ -522,8 +532,10 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
         f32x4_t acc[6];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
-          acc[2 * j] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g);
-          acc[2 * j + 1] = *reinterpret_cast<const f32x4_t*>(bps + 32 * j + 8 * g + 4);
+          float bb[8];
+          unpack8(bpr[j], bb);
+          acc[2 * j] = f32x4_t{bb[0], bb[1], bb[2], bb[3]};
+          acc[2 * j + 1] = f32x4_t{bb[4], bb[5], bb[6], bb[7]};
         }
 #pragma unroll
         for (int kk = 0; kk < 3; ++kk)
@@ -543,44 +555,47 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
         }
       }
     }
-    // LN2 of the lane's token in each tile (4 lanes share a token: xor 16, 32)
+    // LN2 statistics of the lane's token in each tile (4 lanes share a token)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      float s = 0.f;
+      float sm = 0.f;
 #pragma unroll
       for (int j = 0; j < 3; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += z[u].z[j][e];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      const float mean = s * (1.0f / C);
+        for (int e = 0; e < 8; ++e) sm += z[u].z[j][e];
+      sm = row4_sum(sm);
+      mean[u] = sm * (1.0f / C);
       float q2 = 0.f;
 #pragma unroll
       for (int j = 0; j < 3; ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float dd = z[u].z[j][e] - mean;
+          const float dd = z[u].z[j][e] - mean[u];
           q2 += dd * dd;
         }
-      q2 += __shfl_xor(q2, 16);
-      q2 += __shfl_xor(q2, 32);
+      q2 = row4_sum(q2);
       // 64 LN2(z^): the power-of-two scale leaves every rounding unchanged
-      const float rstd = 64.0f / sqrtf(q2 * (1.0f / C) + eps);
+      rstd[u] = 64.0f / sqrtf(q2 * (1.0f / C) + eps);
+    }
+  };
+  auto front2 = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         float gg[8], bb[8], v[8];
         unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 32 * j + 8 * g), gg);
         unpack8(*reinterpret_cast<const u32x4_t*>(vecs + C + 32 * j + 8 * g), bb);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (z[u].z[j][e] - mean) * rstd * gg[e] + 64.0f * bb[e];
+        for (int e = 0; e < 8; ++e) v[e] = (z[u].z[j][e] - mean[u]) * rstd[u] * gg[e] + 64.0f * bb[e];
         af[u][j] = __builtin_bit_cast(bf16x8_t, pack8(v));
       }
-    }
   };
-  if (t2 < npairs) front();
+  if (t2 < npairs) front1();
   // every wave's weight blocks are in LDS (every wave reaches this barrier)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (t2 < npairs) front2();
 
   for (; t2 < npairs; t2 += nw) {
     // ---- fc1 -> GELU -> fc2 over 12 chunks of 32 hidden units, both tiles
@@ -656,7 +671,8 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
     if (t2 + nw < npairs) {
       load_inputs(t2 + nw);
       load_wp();
-      front();
+      front1();
+      front2();
     }
   }
 }

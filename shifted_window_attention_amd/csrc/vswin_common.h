@@ -299,6 +299,17 @@ __device__ __forceinline__ void warm_args_grid(const T&...) {
   kernarg_warm<kArgBytes<T...>() + 8>();
 }
 
+// Sum over the 4 lanes of a token row (lanes l, l^16, l^32, l^48) by lane
+// swaps in the VALU (v_permlane16_swap / v_permlane32_swap: with both
+// operands equal to v, the two results add up to v[l] + v[l ^ 16], resp.
+// v[l ^ 32]); the same sums as two xor-shuffle additions.
+__device__ __forceinline__ float row4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // entry x of head h's prepared table, from the (rows, heads) bf16 table T:
 // offsets outside the table give 0
 __device__ __forceinline__ f32x4_t t4_entry(const bf16_t* __restrict__ T, const Tab4Geo& tg, int h, int x) {
