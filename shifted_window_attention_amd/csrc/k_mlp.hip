@@ -597,72 +597,132 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
   __syncthreads();
   if (t2 < npairs) front2();
 
+  // chunk ch's LDS reads: W1 rows 32 ch .. + 31 (pair order) and the fc1
+  // accumulators' start (64 b1 + U0); W2 columns 32 ch .. + 31
+  auto load_w1 = [&](int ch, bf16x8_t (&w1f)[2][3], f32x4_t& bA, f32x4_t& bB) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const unsigned char* row = W1s + (32 * ch + 16 * p + fr) * (C * 2);
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk) w1f[p][kk] = *reinterpret_cast<const bf16x8_t*>(row + (((4 * kk + g) ^ swz1) << 4));
+    }
+    bA = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g);
+    bB = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g + 4);
+  };
+  auto load_w2 = [&](int ch, bf16x8_t (&w2f)[6]) {
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt) {
+      const int r = 16 * nt + fr;
+      w2f[nt] = *reinterpret_cast<const bf16x8_t*>(W2s + r * (HID * 2) + (((4 * ch + g) ^ (r & 15)) << 4));
+    }
+  };
+  // fc1 of one chunk for both tiles: u = 64 x + U0 of hidden units 8g .. + 7
+  auto fc1 = [&](const bf16x8_t (&w1f)[2][3], const f32x4_t& bA, const f32x4_t& bB, f32x4_t (&a1)[2][2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      a1[u][0] = bA;
+      a1[u][1] = bB;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          a1[u][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1f[p][kk], af[u][kk], a1[u][p], 0, 0, 0);
+  };
+  // GELU of one chunk's fc1 output (the fc2 operand of each tile)
+  auto gelu = [&](const f32x4_t (&a1)[2][2], bf16x8_t (&hf)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = gelu_tab_u(phi, i < 4 ? a1[u][0][i] : a1[u][1][i - 4]);
+      hf[u] = __builtin_bit_cast(bf16x8_t, pack8(h));
+    }
+  };
+  auto fc2 = [&](const bf16x8_t (&hf)[2], const bf16x8_t (&w2f)[6], f32x4_t (&acc2)[2][6]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int nt = 0; nt < 6; ++nt)
+        acc2[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[nt], hf[u], acc2[u][nt], 0, 0, 0);
+  };
+  auto gelu_fc2 = [&](const f32x4_t (&a1)[2][2], const bf16x8_t (&w2f)[6], f32x4_t (&acc2)[2][6]) {
+    bf16x8_t hf[2];
+    gelu(a1, hf);
+    fc2(hf, w2f, acc2);
+  };
+  // one pipelined step: the fc1 products of chunk ch + 1 (into nxt) are
+  // issued beside the GELU of chunk ch (from cur), whose table reads and VALU
+  // work do not depend on them; then chunk ch's W2 fragments and fc2
+  auto step = [&](int ch, const f32x4_t (&cur)[2][2], f32x4_t (&nxt)[2][2], f32x4_t (&acc2)[2][6]) {
+    bf16x8_t hf[2];
+    {
+      bf16x8_t w1f[2][3];
+      f32x4_t bA, bB;
+      load_w1(ch + 1, w1f, bA, bB);
+      __builtin_amdgcn_sched_barrier(0);
+      fc1(w1f, bA, bB, nxt);
+      gelu(cur, hf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t w2f[6];
+    load_w2(ch, w2f);
+    fc2(hf, w2f, acc2);
+  };
+
   for (; t2 < npairs; t2 += nw) {
-    // ---- fc1 -> GELU -> fc2 over 12 chunks of 32 hidden units, both tiles
+    // ---- fc1 -> GELU -> fc2 over 12 chunks of 32 hidden units, both tiles,
+    // software-pipelined by one chunk.  The fc2 accumulators start at
+    // z^ + b2, so the block output is their final value (z^ is not held).
     f32x4_t acc2[2][6];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 6; ++i) acc2[u][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int ch = 0; ch < HID / 32; ++ch) {
-      // every LDS read of the chunk (weights of both layers, fc1 bias as the
-      // fc1 accumulators' start) is in flight before the first MFMA
-      bf16x8_t w1f[2][3], w2f[6];
+      for (int j = 0; j < 3; ++j) {
+        float ob[8];
+        unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 2 * C + 32 * j + 8 * g), ob);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const unsigned char* row = W1s + (32 * ch + 16 * p + fr) * (C * 2);
-#pragma unroll
-        for (int kk = 0; kk < 3; ++kk) w1f[p][kk] = *reinterpret_cast<const bf16x8_t*>(row + (((4 * kk + g) ^ swz1) << 4));
-      }
-#pragma unroll
-      for (int nt = 0; nt < 6; ++nt) {
-        const int r = 16 * nt + fr;
-        w2f[nt] = *reinterpret_cast<const bf16x8_t*>(W2s + r * (HID * 2) + (((4 * ch + g) ^ (r & 15)) << 4));
-      }
-      const f32x4_t bA = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g);
-      const f32x4_t bB = *reinterpret_cast<const f32x4_t*>(b1s + 32 * ch + 8 * g + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4_t a1[2][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        a1[u][0] = bA;
-        a1[u][1] = bB;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 3; ++kk)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-            a1[u][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1f[p][kk], af[u][kk], a1[u][p], 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float uu = i < 4 ? a1[u][0][i] : a1[u][1][i - 4];
-          h[i] = gelu_tab_u(phi, uu);
+        for (int i = 0; i < 4; ++i) {
+          acc2[u][2 * j][i] = z[u].z[j][i] + ob[i];
+          acc2[u][2 * j + 1][i] = z[u].z[j][4 + i] + ob[4 + i];
         }
-        const bf16x8_t hf = __builtin_bit_cast(bf16x8_t, pack8(h));
+      }
+    static_assert(HID / 32 == 12, "chunk count");
+    f32x4_t a1A[2][2], a1B[2][2];
+    {
+      bf16x8_t w1f[2][3];
+      f32x4_t bA, bB;
+      load_w1(0, w1f, bA, bB);
+      fc1(w1f, bA, bB, a1A);
+    }
+#pragma unroll 1
+    for (int ch = 0; ch < 11; ++ch) {
+      step(ch, a1A, a1B, acc2);
 #pragma unroll
-        for (int nt = 0; nt < 6; ++nt)
-          acc2[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[nt], hf, acc2[u][nt], 0, 0, 0);
+      for (int u = 0; u < 2; ++u) {
+        a1A[u][0] = a1B[u][0];
+        a1A[u][1] = a1B[u][1];
       }
     }
-    // ---- y = z^ + fc2 + b2: lane holds columns 32j + 8g .. + 7 of token fr of each tile
+    {
+      bf16x8_t w2f[6];
+      load_w2(11, w2f);
+      gelu_fc2(a1A, w2f, acc2);
+    }
+    // ---- y = z^ + b2 + fc2: lane holds columns 32j + 8g .. + 7 of token fr of each tile
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int64_t tok = (2 * t2 + u) * 16 + fr;
       if (tok < L) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
-          float ob[8], o[8];
-          unpack8(*reinterpret_cast<const u32x4_t*>(vecs + 2 * C + 32 * j + 8 * g), ob);
+          float o[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            o[i] = z[u].z[j][i] + acc2[u][2 * j][i] + ob[i];
-            o[4 + i] = z[u].z[j][4 + i] + acc2[u][2 * j + 1][i] + ob[4 + i];
+            o[i] = acc2[u][2 * j][i];
+            o[4 + i] = acc2[u][2 * j + 1][i];
           }
           *reinterpret_cast<u32x4_t*>(a.y + tok * C + 32 * j + 8 * g) = pack8(o);
         }
