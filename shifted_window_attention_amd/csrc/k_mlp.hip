@@ -697,19 +697,18 @@ __global__ void __launch_bounds__(kMlpThreads) mlp_pair_kernel(const MlpArgs a) 
       load_w1(0, w1f, bA, bB);
       fc1(w1f, bA, bB, a1A);
     }
+    // two steps per iteration, so that the two fc1 outputs swap roles
+    // without register copies
 #pragma unroll 1
-    for (int ch = 0; ch < 11; ++ch) {
+    for (int ch = 0; ch < 10; ch += 2) {
       step(ch, a1A, a1B, acc2);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        a1A[u][0] = a1B[u][0];
-        a1A[u][1] = a1B[u][1];
-      }
+      step(ch + 1, a1B, a1A, acc2);
     }
+    step(10, a1A, a1B, acc2);
     {
       bf16x8_t w2f[6];
       load_w2(11, w2f);
-      gelu_fc2(a1A, w2f, acc2);
+      gelu_fc2(a1B, w2f, acc2);
     }
     // ---- y = z^ + b2 + fc2: lane holds columns 32j + 8g .. + 7 of token fr of each tile
 #pragma unroll
