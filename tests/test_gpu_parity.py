@@ -409,8 +409,8 @@ def test_workload4_bf16_pair_full(init):
 
 
 def test_block_c128_padded_stress_full():
-    """C = 128 (the fused MLP with the Abramowitz-Stegun erf) on a small padded
-    grid with B = 2, every output token, regular and shifted, stress init."""
+    """C = 128 (the fused MLP with its GELU table) on a small padded grid with
+    B = 2, every output token, regular and shifted, stress init."""
     C, heads, window = 128, 4, (8, 7, 7)
     p = _msa_params(C, heads, window, "bf16", "stress", seed=41)
     x = _rng_tokens((2, 16, 12, 13, C), "bf16", 14)
@@ -419,6 +419,24 @@ def test_block_c128_padded_stress_full():
         y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
         _, ref = oracle.block(x, p, heads, window, shift)
         check(host64(y), ref, "bf16", f"C=128 padded block shift {shift}")
+
+
+def test_block_c96_more_pairs_than_waves_stress_full():
+    """C = 96 with more 16-token tile pairs than the projection + MLP launch has
+    waves (grid (8, 93, 93) padded to (8, 98, 98): 69192 tokens, 4325 tiles,
+    the last one half full, 2163 pairs on 2048 waves), so some waves run the
+    per-pair loop (inputs, projection and LN2 of a further pair after the
+    pipelined chunk loop) and the last pair's second tile lies past the tokens;
+    every output token, regular and shifted (the temporal window covers T, so
+    only the spatial shift remains), stress init."""
+    C, heads, window = 96, 3, (8, 7, 7)
+    p = _msa_params(C, heads, window, "bf16", "stress", seed=43)
+    x = _rng_tokens((1, 8, 93, 93, C), "bf16", 17)
+    for shift in ((0, 0, 0), (4, 3, 3)):
+        say(f"C=96 block (1,8,93,93), stress, shift {shift}")
+        y = vs.vswin_block_fwd(dev(x, "bf16"), dev_params(p, "bf16"), heads, window, shift)
+        _, ref = oracle.block(x, p, heads, window, shift)
+        check(host64(y), ref, "bf16", f"C=96 multi-pair block shift {shift}")
 
 
 def _backbone_dev(params):
