@@ -327,6 +327,7 @@ unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 4096) {
 // dst (C x R) = src (R x C)^T, bf16, 32 x 32 tiles through LDS; up to 4
 // matrices in one launch, blockIdx.z picking the job
 __global__ void __launch_bounds__(256) transpose_jobs_kernel(const TransposeJobs jobs) {
+  warm_args(jobs);
   const TransposeJob& j = jobs.job[blockIdx.z];
   __shared__ bf16_t t[32][33];
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
@@ -416,6 +417,7 @@ hipError_t ln_bwd(int x_fp32, const void* x, const void* g, const void* dy, int 
 // dg = sum over workgroups of part[b][0:C], db of part[b][C:2C]; one
 // workgroup per output, blockIdx.y = job
 __global__ void __launch_bounds__(256) ln_reduce_kernel(const LnReds jobs) {
+  warm_args(jobs);
   const LnRed& j = jobs.job[blockIdx.y];
   const int i = blockIdx.x;
   if (i >= 2 * j.C) return;   // the whole workgroup
@@ -504,6 +506,7 @@ hipError_t wgrad_partials(const void* A, const void* B, float* dW, float* db, fl
 // partial row (so a long partial list is read 4 rows at a time) and one
 // wave adds the 4 sums (fixed order: the result does not depend on timing)
 __global__ void __launch_bounds__(256) wgrad_reduce_kernel(const WgradJobs jobs) {
+  warm_args_grid(jobs);
   const WgradJob& j = jobs.job[blockIdx.y];
   __shared__ float red[4][64];
   const int o = (int)threadIdx.x & 63, g = (int)threadIdx.x >> 6;

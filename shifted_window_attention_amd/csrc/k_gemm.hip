@@ -660,6 +660,7 @@ __global__ void __launch_bounds__(256) gemm_f32_mfma_kernel(const float* __restr
 template <class E>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
                                                        int64_t M, int N, int K, E epi) {
+  warm_args(A, W, M, N, K, epi);
   __shared__ float As[16][68];
   __shared__ float Ws[16][68];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;

@@ -36,6 +36,7 @@ __global__ void __launch_bounds__(256) ln_rows_kernel(const TIN* __restrict__ x,
                                                       const TOUT* __restrict__ b, TOUT* __restrict__ y,
                                                       int64_t rows, int C, float eps, int gather,
                                                       WinGeo geo, int apply_ln) {
+  warm_args(x, g, b, y, rows, C, eps, gather, geo, apply_ln);
   const int li = threadIdx.x % LPR;
   const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   if (row >= rows) return;
@@ -307,6 +308,7 @@ hipError_t ln_rows(vswin_dtype in_dt, vswin_dtype out_dt, const void* x, const v
 template <typename T>
 __global__ void __launch_bounds__(256) reverse_kernel(const T* __restrict__ win, const T* __restrict__ res,
                                                       T* __restrict__ y, int64_t slots, int C, WinGeo geo) {
+  warm_args(win, res, y, slots, C, geo);
   const int c4 = C >> 2;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= slots * c4) return;
@@ -390,6 +392,7 @@ hipError_t reverse_scatter(vswin_dtype dt, const void* win, const void* res, voi
 
 __global__ void __launch_bounds__(256) index_map_kernel(int32_t* __restrict__ map, uint8_t* __restrict__ region,
                                                         int64_t slots, WinGeo geo) {
+  warm_args(map, region, slots, geo);
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (s >= slots) return;
   int lab;
