@@ -69,6 +69,35 @@ def test_partition_and_reverse_bitexact(g, dtype):
     assert torch.equal(both, exp)
 
 
+@pytest.mark.parametrize("B,size,C,dtype", [
+    (2, (16, 48, 47), 128, "bf16"),   # 76832 padded slots
+    (2, (16, 48, 47), 128, "fp32"),
+    (2, (16, 91, 91), 96, "bf16"),    # 264992 padded slots
+])
+def test_partition_reverse_layernorm_many_rows(B, size, C, dtype):
+    """The gather, scatter + residual and LayerNorm kernels at large row counts
+    (tens of thousands of workgroups) with padded windows: permutations
+    bit-exact, LayerNorm against the oracle."""
+    window, shift = (8, 7, 7), (4, 3, 3)
+    say(f"many-row partition/reverse/LN {B} {size} C={C} {dtype}")
+    x = _rng_tokens((B, *size, C), dtype, 25)
+    xt = dev(x, dtype)
+    w = vs.vswin_partition_fwd(xt, window, shift)
+    o = ov.Geometry(B, size, window, shift)
+    ref = ov.partition(ov.roll3(ov.pad_end(x, o.padded), [-s for s in o.shift]), o.window)
+    assert np.array_equal(w.float().cpu().numpy(), ref.astype(np.float32))
+    r = _rng_tokens((B, *size, C), dtype, 26)
+    both = vs.vswin_reverse_fwd(w, x.shape, window, shift, residual=dev(r, dtype))
+    assert torch.equal(both, (xt.float() + dev(r, dtype).float()).to(xt.dtype))
+    rng = np.random.default_rng(C)
+    g = synth.round_bf16((1 + 0.1 * rng.standard_normal(C)).astype(np.float32))
+    b = synth.round_bf16((0.1 * rng.standard_normal(C)).astype(np.float32))
+    rows = x.reshape(-1, C)
+    y = vs.vswin_layernorm_fwd(dev(rows, dtype), dev(g, "bf16"), dev(b, "bf16"), out_dtype=tdt("bf16"))
+    ref = oracle.layer_norm(rows.astype(np.float64), g, b)
+    assert np.abs(host64(y) - ref).max() <= 2.0 ** -8 * np.abs(ref).max() + 1e-6
+
+
 @pytest.mark.parametrize("C", [32, 96, 128, 192, 384, 768, 1536, 3072])
 @pytest.mark.parametrize("io", [("fp32", "bf16"), ("bf16", "bf16"), ("fp32", "fp32")])
 def test_layernorm(C, io):
