@@ -130,10 +130,14 @@ vswin_status vswin_plan_query(const vswin_desc* desc, vswin_plan* plan);
 
 /* One Video Swin block (eq. 1):  y = z^ + MLP(LN2(z^)),
  * z^ = x + MSA(LN1(x)).  x, y: (B,T,H,W,C) of desc.dtype, must not alias.
- * MSA as in vswin_window_msa_fwd; MLP = Linear(C, hidden) -> exact erf GELU
+ * MSA as in vswin_window_msa_fwd; MLP = Linear(C, hidden) -> erf GELU
  * -> Linear(hidden, C); LayerNorm with biased variance and desc.ln_eps.
- * In the bf16 path z^ is kept in fp32 inside the workspace; softmax runs in
- * fp32 and the attention weights are rounded to bf16 for the AV product.
+ * In the bf16 path z^ is kept in fp32 (in registers of the fused projection +
+ * MLP kernel at C = 96 and 128, else in the workspace), and the fused MLP
+ * kernels take GELU from a piecewise linear table of the erf form (absolute
+ * error below 2.5e-5 before the bf16 rounding of the hidden activations);
+ * softmax runs in fp32 and the attention weights are rounded to bf16 for the
+ * AV product.
  * A regular/shifted pair (eq. 1) is two calls: shift 0, then window // 2.
  * workspace: >= plan.workspace_bytes bytes of device memory, 256-byte
  * aligned, used as scratch for the duration of the call on `stream`.        */
